@@ -1,0 +1,319 @@
+"""CPU oracle for the top-k-routed MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+This is the plain, slow, obviously-correct definition that the HIP path is
+checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path never
+does, and it imports nothing from the product package.  It shares no code with
+the HIP kernels or their host library.
+
+Arithmetic is fp64 throughout (numpy), with exactly the rounding points the
+method fixes:
+
+* router logits are formed in fp64 from the exact input values and rounded
+  once to fp32 -- the pages keep routing in fp32;
+* in bf16 workloads the expert's hidden activation ``Hm`` is rounded to bf16
+  (round-to-nearest-even) before the down projection, because the down
+  projection's left operand is a bf16 tensor;
+* the layer output is rounded once to its storage dtype.
+
+Sources (the pages' titles; the sections named in each docstring):
+
+* [OPS]  aicoding.csdn.net article on the ops-transformer MoE operators
+  (sections "原理：MoE的稀疏路由是怎么工作的" Steps 1-4, "坑1：负载均衡",
+  "实现：ops-transformer里面的MoE算子" with the ``MoEGatingForward`` sketch).
+* [CANN] "MoE 路由算子到底在做什么？一次拆透 ops-transformer 的核心机制"
+  (sections 2.1-2.3, 3).
+* [RTR]  "MoE Router：谁来决定 Token 去哪个 Expert" (router passage, the
+  ``MoERouter`` snippet, the load-balancing passage, the capacity-limit passage).
+* [MB]   "01 · MoE 为什么难算：变长专家输入" (MegaBlocks chapter 1; sections 1,
+  2, 3, 4.1-4.6, 5).
+* [CAI]  "在 Colossal-AI 中为你的模型集成混合专家（MoE）..." (SparseMLP forward
+  data flow, ``MoeLoss`` passage).
+
+Readings taken where the pages are silent or disagree are listed beside the
+function that takes them.  Every function here is pinned by ``tests/`` against
+worked examples, closed forms, brute force or library routines.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "bf16_to_f64", "round_to_bf16", "router_logits", "softmax", "select_topk",
+    "topk_weights", "expert_capacity", "histogram", "permute", "silu", "gelu",
+    "expert_ffn", "combine", "aux_loss", "layer_forward",
+]
+
+
+# ----------------------------------------------------------------------------
+# number formats
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp64 values (a bf16 is the top half of an fp32)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest bf16, ties to even, returned as uint16 bit patterns.
+
+    bf16 keeps 8 significant bits.  With v = m * 2**e (0.5 <= |m| < 1), the
+    spacing of bf16 values around v is q = 2**(e-8); rounding v/q to the
+    nearest integer with ties to even (numpy's ``rint``) and scaling back is an
+    exact, single rounding.  The result is representable in fp32, whose top 16
+    bits are the bf16 pattern.  Finite inputs in the normal range only.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    q = np.ldexp(1.0, e - 8)
+    r = np.rint(v / q) * q
+    r = np.where(v == 0.0, v, r)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_to_f64(a) if dtype == "bf16" else np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# routing: router linear, softmax, top-k, renormalisation
+
+def router_logits(x: np.ndarray, W_gate: np.ndarray, logit_bias, dtype: str) -> np.ndarray:
+    """``logits[t,e] = sum_i x[t,i] * W_gate[i,e] (+ logit_bias[e])`` as fp32 [T,E].
+
+    The router is one bias-free linear map from the hidden width to the expert
+    count ([RTR] ``MoERouter``: ``Linear(hidden_dim, num_experts, bias=False)``;
+    [OPS] Step 1; [MB] section 1, LearnedRouter).  Routing runs in fp32 ([CAI]
+    SparseMLP data flow, step 2: gate logits are cast to fp32 before the
+    router).  Reading: formed in fp64 from the exact inputs, rounded once to
+    fp32.  ``logit_bias`` is not a learned parameter of the method: it only
+    skews the synthetic workloads' expert popularity.
+    """
+    l = _as_f64(x, dtype) @ np.asarray(W_gate, dtype=np.float32).astype(np.float64)
+    if logit_bias is not None:
+        l = l + np.asarray(logit_bias, dtype=np.float32).astype(np.float64)[None, :]
+    return l.astype(np.float32)
+
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    """Row softmax over the E experts, fp64, with the row maximum subtracted
+    ([OPS] ``MoEGatingForward`` step 1; [RTR] ``F.softmax(logits, dim=-1)``)."""
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """The k experts with the largest scores per token, best first, as int32 [T,k].
+
+    [OPS] Step 2 and ``MoEGatingForward`` step 2 (a selection of the K best);
+    [RTR] ``torch.topk`` (sorted output).  Readings: the ranking is on the fp32
+    *logits* (softmax is monotone, so this is the same set, and it avoids ties
+    created by rounding of exp); equal logits rank the lower expert index
+    first; -0.0 equals +0.0 (IEEE comparison).  Slot j holds the j-th best.
+    """
+    l = np.asarray(logits, dtype=np.float32)
+    T, E = l.shape
+    expert = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort: the last key is the primary one -> (logit descending, expert ascending)
+    order = np.lexsort((expert, -l), axis=1)
+    return order[:, :k].astype(np.int32)
+
+
+def topk_weights(logits: np.ndarray, topk_idx: np.ndarray) -> np.ndarray:
+    """Renormalised gate weights of the selected experts, fp32 [T,k].
+
+    ``w[t,j] = p[t,S_j] / sum_j' p[t,S_j']`` with p the full softmax
+    ([OPS] ``MoEGatingForward`` step 3: the chosen weights are scaled to sum
+    to one; [RTR] ``topk_weights / topk_weights.sum(-1)``).  Always applied,
+    also for k = 1 (then w = 1).  fp64, rounded once to fp32.
+    """
+    p = softmax(logits)
+    sel = np.take_along_axis(p, np.asarray(topk_idx, dtype=np.int64), axis=1)
+    return (sel / sel.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# capacity, histogram, stable sort by expert
+
+def expert_capacity(T: int, E: int, k: int, capacity_factor: float):
+    """Per-expert capacity ``C = floor(cf * (k*T/E))``; ``None`` means unlimited.
+
+    [MB] section 3 (``C = capacity_factor * tokens * top_k / num_experts``)
+    and section 4.2 (``expert_capacity``: tokens-per-expert first, then the
+    factor, then truncation to int).  [RTR]'s capacity passage drops the k;
+    the MegaBlocks form with k is taken.  Section 4.6: a computed capacity of
+    zero means "never drop" -- taken here also for a factor <= 0.  The factor
+    enters as an fp32 value (that is how the library receives it) and the
+    product is formed in fp64.
+    """
+    cf = float(np.float32(capacity_factor))
+    if not math.isfinite(cf):
+        raise ValueError("capacity factor must be finite")
+    if cf <= 0.0:
+        return None
+    tokens_per_expert = (k * T) / E
+    C = int(math.floor(cf * tokens_per_expert))
+    return None if C == 0 else C
+
+
+def histogram(topk_idx: np.ndarray, E: int) -> np.ndarray:
+    """``tokens_per_expert``: how many (token, slot) assignments chose each expert, before
+    any capacity drop ([MB] section 4.1 table)."""
+    counts = np.zeros(E, dtype=np.int64)
+    for e in np.asarray(topk_idx).reshape(-1).tolist():
+        counts[e] += 1
+    return counts.astype(np.int32)
+
+
+def permute(topk_idx: np.ndarray, E: int, C):
+    """Sort the flattened assignments by expert id, stably, and apply the capacity.
+
+    Assignment ``s = t*k + j`` (token t, slot j).  [MB] section 4.1 sorts the
+    flattened expert ids and takes the running end positions of each expert
+    (``bins``); section 4.5: an expert keeps only its first C rows, later ones
+    are dropped silently and contribute zero.  Readings: the sort is stable,
+    so "first" means ascending s; offsets are exclusive starts over the
+    *kept* rows, ``offsets[E] = R`` the total kept.
+
+    Returns ``counts[E]`` (pre-drop), ``offsets[E+1]``, ``sorted_slot[T*k]``
+    (row r of the expert-sorted order -> its assignment s; rows >= R are -1) and
+    ``slot_pos[T*k]`` (assignment s -> its row, -1 if dropped).
+    """
+    flat = np.asarray(topk_idx).reshape(-1).tolist()
+    n = len(flat)
+    counts = [0] * E
+    for e in flat:
+        counts[e] += 1
+    kept = [c if C is None else min(c, C) for c in counts]
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + kept[e])
+    seen = [0] * E
+    sorted_slot = [-1] * n
+    slot_pos = [-1] * n
+    for s, e in enumerate(flat):
+        r = seen[e]
+        seen[e] += 1
+        if C is None or r < C:
+            slot_pos[s] = offsets[e] + r
+            sorted_slot[offsets[e] + r] = s
+    i32 = lambda a: np.asarray(a, dtype=np.int32)
+    return i32(counts), i32(offsets), i32(sorted_slot), i32(slot_pos)
+
+
+# ----------------------------------------------------------------------------
+# experts
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """``silu(z) = z / (1 + exp(-z))`` (the gate of SwiGLU, [CANN] section 7)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def gelu(z: np.ndarray) -> np.ndarray:
+    """GELU in its exact form ``z/2 * (1 + erf(z/sqrt(2)))`` ([MB] section 4.4 sketch names
+    gelu without a variant; the exact erf form is taken)."""
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def expert_ffn(a: np.ndarray, W1e, W3e, W2e, act: str, dtype: str) -> np.ndarray:
+    """One expert's MLP on fp64 rows ``a[n,h]``, returned in fp64 [n,h].
+
+    [MB] section 4.3: ``MLP.forward`` is matmul, activation, matmul on the
+    expert's ``[hs, ffn]`` weights.  SwiGLU experts gate the up projection:
+    ``(silu(a @ W1) * (a @ W3)) @ W2``; GELU experts: ``gelu(a @ W1) @ W2``.
+    In bf16 workloads the hidden activation is rounded to bf16 before the
+    down projection.
+    """
+    z1 = a @ _as_f64(W1e, dtype)
+    if act == "swiglu":
+        hm = silu(z1) * (a @ _as_f64(W3e, dtype))
+    elif act == "gelu":
+        hm = gelu(z1)
+    else:
+        raise ValueError(act)
+    if dtype == "bf16":
+        hm = bf16_to_f64(round_to_bf16(hm))
+    return hm @ _as_f64(W2e, dtype)
+
+
+def combine(x: np.ndarray, topk_idx, topk_w, slot_pos, W1, W3, W2, act: str, dtype: str,
+            tokens=None) -> np.ndarray:
+    """Layer output, token by token from the definition, fp64 [len(tokens), h].
+
+    ``y[t] = sum_j w[t,j] * FFN_{S_j}(x[t])`` over the slots that were kept
+    ([OPS] Step 4; [MB] section 4.3 ``binned_scatter``: scale by the routing
+    weight, then sum over the top-k slots).  A dropped slot adds nothing and the
+    surviving weights are *not* renormalised ([MB] section 3 item 2 and
+    section 4.5; [RTR] capacity passage: dropped tokens bypass the experts).
+    It does not use the permuted layout, so it checks the permutation rather
+    than trusting it.  Contributions are summed in ascending j.
+    """
+    T, k = np.asarray(topk_idx).shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    xs = _as_f64(np.asarray(x)[tokens], dtype)
+    h = xs.shape[1]
+    contrib = np.zeros((len(tokens), k, h), dtype=np.float64)
+    idx = np.asarray(topk_idx)[tokens]
+    w = np.asarray(topk_w, dtype=np.float32)[tokens].astype(np.float64)
+    kept = np.asarray(slot_pos).reshape(T, k)[tokens] >= 0
+    for e in np.unique(idx[kept]):
+        rows, slots = np.nonzero((idx == e) & kept)
+        out = expert_ffn(xs[rows], W1[e], None if W3 is None else W3[e], W2[e], act, dtype)
+        contrib[rows, slots] = w[rows, slots][:, None] * out
+    y = np.zeros((len(tokens), h), dtype=np.float64)
+    for j in range(k):
+        y += contrib[:, j]
+    return y
+
+
+def aux_loss(counts: np.ndarray, probs: np.ndarray, T: int, k: int, E: int) -> float:
+    """Switch-style load-balance loss ``E * sum_e f_e * P_e``, unscaled.
+
+    [OPS] "坑1：负载均衡" and the ``MoELoadBalance`` call, [RTR] load-balancing
+    passage (each expert should get about 1/E of the assignments), [CAI]
+    ``MoeLoss`` (the 0.01 weight is applied by the caller).  Readings:
+    ``f_e = counts_e / (T*k)`` with the pre-drop counts (the loss is a function
+    of the router alone), ``P_e`` = mean over tokens of the full softmax.
+    """
+    f = np.asarray(counts, dtype=np.float64) / float(T * k)
+    P = np.asarray(probs, dtype=np.float64).sum(axis=0) / float(T)
+    return float(E * np.sum(f * P))
+
+
+# ----------------------------------------------------------------------------
+# the whole layer
+
+def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float,
+                  act: str, dtype: str, logits=None, tokens=None, with_y: bool = True) -> dict:
+    """Router -> top-k -> permute (with capacity) -> experts -> weighted combine, plus aux.
+
+    ``logits`` may be given (fp32 [T,E]) to route on another implementation's
+    logits, so that integer routing results can be compared bit for bit.
+    ``tokens`` restricts the expensive output ``y`` to a subset of tokens
+    (routing, capacity and aux always cover all tokens).  ``y`` is returned in
+    the storage dtype: fp32 values, or bf16 bit patterns.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(W_gate).shape[1]
+    if logits is None:
+        logits = router_logits(x, W_gate, logit_bias, dtype)
+    logits = np.asarray(logits, dtype=np.float32)
+    idx = select_topk(logits, k)
+    w = topk_weights(logits, idx)
+    C = expert_capacity(T, E, k, capacity_factor)
+    counts, offsets, sorted_slot, slot_pos = permute(idx, E, C)
+    out = dict(logits=logits, topk_idx=idx, topk_w=w, C=C, counts=counts, offsets=offsets,
+               sorted_slot=sorted_slot, slot_pos=slot_pos,
+               aux=aux_loss(counts, softmax(logits), T, k, E))
+    if with_y:
+        tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+        y64 = combine(x, idx, w, slot_pos, W1, W3, W2, act, dtype, tokens=tok)
+        out["y_tokens"] = tok
+        out["y64"] = y64
+        out["y"] = round_to_bf16(y64) if dtype == "bf16" else y64.astype(np.float32)
+    return out

@@ -1,0 +1,95 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that its pins catch them.
+
+A pin is only worth something if a wrong oracle fails it.  Each case below
+replaces one oracle function with a subtly wrong variant and runs the pin
+tests that should notice; the test passes when at least one of them fails.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as o
+import oracle.moe_oracle as om
+from tests import test_oracle_pins as pins
+
+
+def _topk_ties_high(logits, k):
+    l = np.asarray(logits, dtype=np.float32)
+    T, E = l.shape
+    order = np.lexsort((-np.broadcast_to(np.arange(E), (T, E)), -l), axis=1)
+    return order[:, :k].astype(np.int32)
+
+
+def _weights_no_renorm(logits, idx):
+    p = om.softmax(logits)
+    return np.take_along_axis(p, np.asarray(idx, dtype=np.int64), 1).astype(np.float32)
+
+
+def _capacity_without_k(T, E, k, cf):
+    cf = float(np.float32(cf))
+    if cf <= 0:
+        return None
+    C = int(math.floor(cf * T / E))
+    return None if C == 0 else C
+
+
+def _gelu_tanh(z):
+    return 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _aux_counts_over_T(counts, probs, T, k, E):
+    return float(E * np.sum(np.asarray(counts, float) / T * np.asarray(probs).sum(0) / T))
+
+
+def _logits_no_bias(x, W_gate, logit_bias, dtype):
+    return _orig["router_logits"](x, W_gate, None, dtype)
+
+
+def _permute_unstable(topk_idx, E, C):
+    counts, offsets, sorted_slot, slot_pos = _orig["permute"](topk_idx, E, C)
+    # reverse the order inside each segment (a sort that is not stable)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        seg = sorted_slot[a:b][::-1].copy()
+        sorted_slot[a:b] = seg
+        slot_pos[seg] = np.arange(a, b)
+    return counts, offsets, sorted_slot, slot_pos
+
+
+def _silu_sign(z):
+    return z / (1.0 + np.exp(z))
+
+
+_orig = {n: getattr(om, n) for n in ("router_logits", "permute")}
+
+MUTANTS = [
+    ("select_topk", _topk_ties_high, ["test_topk_ties_and_signed_zero"]),
+    ("topk_weights", _weights_no_renorm, ["test_top2_worked_example", "test_topk_weights_invariants"]),
+    ("expert_capacity", _capacity_without_k, ["test_capacity_closed_forms"]),
+    ("gelu", _gelu_tanh, ["test_gelu_silu_vs_math"]),
+    ("aux_loss", _aux_counts_over_T, ["test_aux_uniform_counts_is_one_and_collapse_is_E"]),
+    ("router_logits", _logits_no_bias, ["test_k_equals_E_is_dense_softmax_mixture"]),
+    ("permute", _permute_unstable, ["test_histogram_worked_example_dropless"]),
+    ("silu", _silu_sign, ["test_gelu_silu_vs_math", "test_single_expert_is_plain_ffn"]),
+]
+
+
+def _run(test_name):
+    fn = getattr(pins, test_name)
+    if test_name == "test_k_equals_E_is_dense_softmax_mixture":
+        return fn("swiglu")
+    return fn()
+
+
+@pytest.mark.parametrize("target,mutant,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(monkeypatch, target, mutant, catchers):
+    monkeypatch.setattr(om, target, mutant)
+    monkeypatch.setattr(o, target, mutant, raising=False)
+    caught = False
+    for name in catchers:
+        try:
+            _run(name)
+        except AssertionError:
+            caught = True
+    assert caught, f"no pin caught the planted mistake in {target}"
