@@ -1,0 +1,249 @@
+"""Benchmark: one MoE layer forward per step on one MI355X.
+
+A step is one call of the whole hot path (router -> histogram -> scan ->
+stable scatter -> expert up-projection -> expert down-projection -> combine)
+over the Mixtral-shaped prefill batch (T = 4096 tokens, h = 4096, f = 14336,
+E = 8, k = 2, SwiGLU, bf16, fp32 router), inputs resident in HBM.  Prints one
+JSON line with tokens/s, a roofline entry for the dominant kernel (the
+SwiGLU up-projection GEMM, timed with HIP events recorded around it on the
+library's stream inside the timed loop), and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill-mixtral]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s at Mixtral shape (T=4096); % bf16 MFMA peak; route GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """Minimal HIP event API through ctypes (events on the library's stream)."""
+
+    def __init__(self):
+        self.l = ctypes.CDLL("libamdhip64.so")
+        self.l.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.l.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.l.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.l.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.l.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for ev in arr:
+            self.l.hipEventDestroy(ev)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(ROOT, "top_routing_expert_moe_amd", "csrc"))):
+        with open(os.path.join(ROOT, "top_routing_expert_moe_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(workload: str):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters, if they
+    were taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill-mixtral")
+    ap.add_argument("--cpu-sample", type=int, default=512, help="tokens in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the layer's sharding plan is design-only.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_workloads as mw
+    import top_routing_expert_moe_amd as moe
+
+    w = mw.by_name(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()  # fail loudly if the HIP library is missing
+
+    t = time.time()
+    host = mw.make_inputs(w)
+    bf = w.dtype == "bf16"
+
+    def to_dev(a, low):
+        if a is None:
+            return None
+        if low and bf:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = {k: to_dev(v, k in ("x", "W1", "W3", "W2")) for k, v in host.items()}
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: inputs drawn and resident in {time.time() - t:.1f}s")
+
+    T, h, f, E, k = w.T, w.h, w.f, w.E, w.k
+    act = moe.SWIGLU if w.act == "swiglu" else moe.GELU
+    dt = moe.BF16 if bf else moe.F32
+    ws = torch.empty(moe.workspace_bytes(T, h, f, E, k, w.cf, dt, act), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, h), dtype=d["x"].dtype, device=dev)
+    aux = torch.empty((), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+
+    def step(events=None):
+        moe.layer_forward(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
+                          capacity_factor=w.cf, act=w.act, ws=ws, y=y, aux=aux, counts=counts, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    nst = len(moe.LAYER_STAGES)
+    ev = [hip.events(nst + 1) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    stage_ms = {s: 0.0 for s in moe.LAYER_STAGES}
+    for i in range(args.steps):
+        for j, s in enumerate(moe.LAYER_STAGES):
+            stage_ms[s] += hip.elapsed_ms(ev[i][j], ev[i][j + 1]) / args.steps
+    for e_ in ev:
+        hip.destroy(e_)
+    log("[bench] stage ms: " + ", ".join(f"{s}={v:.4f}" for s, v in stage_ms.items()))
+
+    cnt = counts.cpu().numpy().astype(np.int64)
+    C = moe.capacity(T, E, k, w.cf)
+    kept = cnt if C is None else np.minimum(cnt, C)
+    R = int(kept.sum())
+    n_up = 2 if w.act == "swiglu" else 1
+    flops_up = 2.0 * n_up * R * h * f
+    flops_down = 2.0 * R * f * h
+    flops_router = 2.0 * T * h * E
+    up_s = stage_ms["expert_up"] / 1e3
+    achieved = flops_up / up_s / 1e12
+    ms_per_step = wall / args.steps * 1e3
+    es = 2 if bf else 4
+    # compulsory bytes of routing + permutation metadata: x and W_gate read once, logits written,
+    # topk idx/w, slot_pos and the sorted order (4 B each per assignment)
+    route_bytes = T * h * es + h * E * 4 + T * E * 4 + T * k * 16
+    route_ms = sum(stage_ms[s] for s in ("route", "hist", "scan", "scatter"))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry(w.name),
+                "kernel": "expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue)" if w.act == "swiglu"
+                else "expert up-projection (grouped GEMM, GELU epilogue)",
+                "flops_per_launch": flops_up, "avg_launch_ms": round(stage_ms["expert_up"], 5)}
+    extra = {
+        "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "rows_kept": R, "active_experts": int((cnt > 0).sum()),
+        "layer_mfma_frac": round((flops_up + flops_down) / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "expert_down_frac": round(flops_down / (stage_ms["expert_down"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "route_gbps": round(route_bytes / (route_ms / 1e3) / 1e9, 1),
+        "router_flops": flops_router,
+        "aux_loss": float(aux.cpu()),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as o
+        try:
+            import threadpoolctl
+            threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        ns = min(args.cpu_sample, T)
+        tokens = np.arange(ns) * (T // ns)
+        tc = time.perf_counter()
+        ref = o.layer_forward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"],
+                              k=k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, tokens=tokens)
+        el = time.perf_counter() - tc
+        cpu = {"value": round(ns / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"full routing of all {T} tokens + expert outputs of {ns} evenly spaced tokens "
+                         f"(fp64 numpy, {el:.1f} s)"}
+        # the bench's own output against the same oracle run, on tokens routed identically
+        _, gidx, _, _ = moe.route(d["x"], d["W_gate"], d["logit_bias"], k)
+        same = (np.sort(gidx.cpu().numpy()[tokens], 1) == np.sort(ref["topk_idx"][tokens], 1)).all(1)
+        gy = y.cpu()
+        gy = (gy.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32) \
+            if bf else gy.numpy()
+        got = gy[tokens][same].astype(np.float64)
+        ry = ref["y64"][same]
+        rms = float(np.sqrt(np.mean(ry ** 2)))
+        extra["parity_vs_oracle"] = {"tokens": int(same.sum()), "routing_differs": int((~same).sum()),
+                                     "max_abs_over_rms": round(float(np.abs(got - ry).max()) / rms, 5),
+                                     "aux_rel_err": abs(extra["aux_loss"] - ref["aux"]) / abs(ref["aux"])}
+
+    out = {
+        "metric": METRIC,
+        "value": round(T * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) random weights of the layer's shape)",
+        "config": {"workload": w.name, "T": T, "h": h, "f": f, "E": E, "k": k, "act": w.act,
+                   "capacity_factor": w.cf, "router": "fp32", "logit_bias": w.bias},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library
+ * (libmoe_mi355x.so).
+ *
+ * The layer: a router picks, for every token, the k best of E experts; the
+ * token is sent through those experts' MLPs and their outputs are summed with
+ * the renormalised gate weights.  Sources (page titles, with sections):
+ *   [OPS]  aicoding.csdn.net article on the ops-transformer MoE operators:
+ *          "原理：MoE的稀疏路由是怎么工作的" Steps 1-4; "坑1：负载均衡";
+ *          "实现" (MoEGatingForward); "使用" (MyMoELayer, MoEForward,
+ *          MoELoadBalance).
+ *   [RTR]  "MoE Router：谁来决定 Token 去哪个 Expert": MoERouter snippet,
+ *          load-balancing passage, capacity-limit passage.
+ *   [MB]   "01 · MoE 为什么难算：变长专家输入" (MegaBlocks chapter 1):
+ *          sections 3, 4.1-4.6.
+ *   [CAI]  "在 Colossal-AI 中为你的模型集成混合专家（MoE）...": SparseMLP data
+ *          flow, MoeLoss.
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are DEVICE pointers to row-major, contiguous arrays,
+ *     16-byte aligned.  The caller allocates and owns all memory, including
+ *     the workspace `ws`; the library never allocates, frees, synchronises,
+ *     prints or keeps state between calls.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns before it runs.  Concurrent calls on
+ *     different streams with different workspaces are independent.
+ *   - Arguments are checked on the host before any HIP call.  On an error
+ *     nothing is enqueued and no output is written.  T == 0 returns MOE_OK
+ *     and does nothing.
+ *   - Expert ids must lie in [0, E).  Logits must be finite (NaN/Inf give
+ *     unspecified routing).
+ *   - dtype MOE_BF16: x, W1, W3, W2, x_perm, out_perm and y are bf16 (raw
+ *     16-bit patterns); the router (W_gate, logit_bias, logits, weights) is
+ *     always fp32.  MOE_F32: everything fp32.
+ *   - Limits: 1 <= k <= E; E <= 256 (MOE_ERR_UNSUPPORTED beyond: one 8-bit
+ *     digit for the sort by expert id); k <= 16; h and f multiples of 64.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* null required pointer, bad size, k out of range, non-finite factor */
+  MOE_ERR_UNSUPPORTED = 2,  /* E > 256, k > 16, h or f not a multiple of 64, misaligned pointer */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the entry point needs */
+  MOE_ERR_DEVICE = 4        /* a kernel launch failed (hipGetLastError) */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
+
+/* moe_route flag: `logits` is an input (fp32 [T,E]); x, W_gate, logit_bias are ignored. */
+#define MOE_ROUTE_LOGITS_IN 1u
+
+/* Per-expert capacity C = floor(cf * (T*k/E)) ([MB] sections 3 and 4.2: tokens per
+ * expert first, then the factor, then truncation).  Returns INT32_MAX ("never drop")
+ * when cf <= 0 or the computed C is 0 ([MB] section 4.6), and -1 for invalid
+ * arguments (T < 0, E < 1, k < 1, cf not finite).  The factor is widened to double
+ * before the product.  Host only. */
+int32_t moe_capacity(int32_t T, int32_t E, int32_t k, float capacity_factor);
+
+/* Bytes of workspace that suffice for every entry point below at these sizes
+ * (the amount moe_layer_forward needs).  0 for invalid sizes. */
+size_t moe_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                           float capacity_factor, moe_dtype_t dt, moe_act_t act);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status_t s);
+
+/* Router: logits = x . W_gate (+ logit_bias), softmax, top-k selection, renormalised
+ * weights ([OPS] Steps 1-2 and MoEGatingForward; [RTR] MoERouter; routing in fp32 per
+ * [CAI] SparseMLP step 2).
+ *   x        [T,h] (dt)          W_gate [h,E] fp32        logit_bias [E] fp32 or NULL
+ *   logits   [T,E] fp32: output (input with MOE_ROUTE_LOGITS_IN)
+ *   topk_idx [T,k] int32: slot j = j-th best expert; order (logit desc, expert asc)
+ *   topk_w   [T,k] fp32: softmax of the selected logits (sums to 1 per token)
+ *   prob_sum [E] fp32 or NULL: sum over tokens of the full softmax (for the aux loss)
+ *   ws: needs 4*ceil(T/32)*E bytes (+256) when prob_sum is given, else may be NULL. */
+moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bias,
+                       int32_t T, int32_t h, int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags,
+                       float* logits, int32_t* topk_idx, float* topk_w, float* prob_sum,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permutation: histogram, capacity, prefix sum and a STABLE sort of the T*k assignments
+ * s = t*k+j by expert id, then the gather of token rows ([MB] sections 4.1, 4.2, 4.5, 4.6).
+ *   topk_idx [T,k] int32 (ids in [0,E)),  x [T,h] (dt) -- may be NULL when x_perm is NULL
+ *   counts   [E] int32: assignments per expert BEFORE any drop
+ *   offsets  [E+1] int32: exclusive starts over the KEPT rows; offsets[E] = R rows kept
+ *   sorted_slot [T*k] int32: row r -> assignment s (first R entries valid)
+ *   slot_pos [T*k] int32: assignment s -> row, -1 if dropped (rank >= C in ascending s)
+ *   x_perm   [T*k,h] (dt) or NULL: row r = x[sorted_slot[r]/k] for r < R
+ *   prob_sum [E] fp32 or NULL (from moe_route), aux_loss: device fp32 scalar or NULL --
+ *            when both are given, aux = E * sum_e (counts_e/(T*k)) * (prob_sum_e/T),
+ *            unscaled ([OPS] 坑1; [RTR] load-balancing passage; [CAI] MoeLoss).
+ *   ws: needs about 8*ceil(T*k/2048)*E + 4*T*k + 8*E bytes (see moe_workspace_bytes). */
+moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int32_t h, int32_t E,
+                         int32_t k, float capacity_factor, moe_dtype_t dt,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                         void* x_perm, const float* prob_sum, float* aux_loss,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Experts: for the rows r in segment e = [offsets[e], offsets[e+1]) of x_perm,
+ *   SwiGLU: out_perm[r] = (silu(x_perm[r] W1[e]) * (x_perm[r] W3[e])) W2[e]
+ *   GELU:   out_perm[r] = gelu(x_perm[r] W1[e]) W2[e]     (exact erf form)
+ * ([MB] section 4.3: matmul, activation, matmul per expert; SwiGLU per the
+ * ops-transformer operator list).  Offsets are read on the device; experts with no rows
+ * read no weights.  In bf16 the hidden activation is rounded to bf16 before W2.
+ *   x_perm [R_max,h], W1/W3 [E,h,f], W2 [E,f,h] (dt); W3 must be NULL iff GELU.
+ *   offsets [E+1] int32 (device), R_max >= offsets[E] (rows allocated in x_perm/out_perm)
+ *   out_perm [R_max,h] (dt): rows >= offsets[E] are not written.
+ *   ws: needs R_max*f*elem + 4*(E+1) bytes (+256). */
+moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t R_max,
+                            int32_t h, int32_t f, int32_t E, const void* W1, const void* W3,
+                            const void* W2, moe_act_t act, moe_dtype_t dt, void* out_perm,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine: y[t] = sum over j with slot_pos[t*k+j] >= 0 of topk_w[t,j] * out_perm[slot_pos[t*k+j]],
+ * fp32 accumulation in ascending j; a token whose slots were all dropped gets 0
+ * ([OPS] Step 4; [MB] sections 4.3 and 4.5).  No workspace.
+ *   out_perm [*,h] (dt), slot_pos [T*k] int32, topk_w [T,k] fp32, y [T,h] (dt). */
+moe_status_t moe_unpermute(const void* out_perm, const int32_t* slot_pos, const float* topk_w,
+                           int32_t T, int32_t h, int32_t k, moe_dtype_t dt, void* y,
+                           hipStream_t stream);
+
+/* The whole layer: route -> permute (with capacity) -> experts -> combine, plus the aux
+ * loss from the same histogram.  x [T,h]; W_gate [h,E] fp32; logit_bias [E] fp32 or NULL;
+ * W1/W3 [E,h,f], W2 [E,f,h] (dt; W3 NULL iff GELU); y [T,h] (dt).
+ * aux_loss: device fp32 scalar or NULL.  counts: device int32 [E] (pre-drop) or NULL.
+ * ws: at least moe_workspace_bytes(T,h,f,E,k,capacity_factor,dt,act) bytes. */
+moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* logit_bias,
+                               const void* W1, const void* W3, const void* W2,
+                               int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                               float capacity_factor, moe_act_t act, moe_dtype_t dt,
+                               void* y, float* aux_loss, int32_t* counts,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Measurement variant of moe_layer_forward: the same kernels on the same stream, with
+ * caller-created HIP events recorded between the stages, so a profiler-free caller can
+ * time each kernel: events[0] before the router, then one after each stage in order
+ * (router, histogram, scan, scatter, expert up-projection, expert down-projection,
+ * combine).  `events` holds MOE_LAYER_STAGES + 1 valid hipEvent_t (MOE_ERR_ARG otherwise). */
+#define MOE_LAYER_STAGES 7
+moe_status_t moe_layer_forward_timed(const void* x, const float* W_gate, const float* logit_bias,
+                                     const void* W1, const void* W3, const void* W2,
+                                     int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                     float capacity_factor, moe_act_t act, moe_dtype_t dt,
+                                     void* y, float* aux_loss, int32_t* counts,
+                                     void* ws, size_t ws_bytes, hipStream_t stream,
+                                     hipEvent_t* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

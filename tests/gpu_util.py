@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: moving the seeded numpy inputs to the device,
+caching full-size workloads, and the tolerances the parity checks use."""
+from __future__ import annotations
+
+import numpy as np
+
+import moe_workloads as mw
+
+_CACHE: dict = {}
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev():
+    t = torch()
+    if not t.cuda.is_available():
+        raise RuntimeError("GPU tests need a GPU")
+    return t.device("cuda:0")
+
+
+def to_dev(a, dtype: str):
+    """numpy fp32 array or bf16 bit pattern array -> device tensor (None passes through)."""
+    if a is None:
+        return None
+    t = torch()
+    if dtype == "bf16" and a.dtype == np.uint16:
+        return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(t.bfloat16).to(dev())
+    return t.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def from_dev(x) -> np.ndarray:
+    t = torch()
+    x = x.detach()
+    if x.dtype == t.bfloat16:
+        return x.view(t.int16).cpu().numpy().view(np.uint16)
+    return x.cpu().numpy()
+
+
+def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16" and a.dtype == np.uint16:
+        return mw.bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def workload(name: str):
+    """(Workload, host inputs, device inputs), cached for the test session."""
+    if name not in _CACHE:
+        w = mw.by_name(name)
+        host = mw.make_inputs(w)
+        devd = {}
+        for key in ("x", "W1", "W3", "W2"):
+            devd[key] = to_dev(host[key], w.dtype)
+        devd["W_gate"] = to_dev(host["W_gate"], "f32")
+        devd["logit_bias"] = to_dev(host["logit_bias"], "f32")
+        _CACHE.clear()  # keep at most one full-size workload resident
+        _CACHE[name] = (w, host, devd)
+        torch().cuda.synchronize()
+    return _CACHE[name]
+
+
+# ---------------------------------------------------------------- tolerances
+
+def check_rel_rms(got, ref, rel: float, what: str):
+    """|got - ref| <= rel * (|ref| + RMS(ref)) elementwise (relative error with an RMS floor)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    bound = rel * (np.abs(ref) + rms)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {ref.size} outside rel {rel}; worst "
+                           f"|d|={float(err.max()):.3e} at {np.unravel_index(int(np.argmax(err - bound)), err.shape)}, "
+                           f"rms={rms:.3e}")
+
+
+def check_bf16_out(got, ref, what: str, frac: float = 2e-2):
+    """max |got - ref| <= frac * RMS(ref) (the bf16 output bar)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    assert err <= frac * rms, f"{what}: max|d| = {err:.4e} > {frac} * RMS {rms:.4e} (ratio {err / rms:.4f})"
+    return err / rms if rms else 0.0

@@ -1,0 +1,108 @@
+"""GPU parity of the whole layer (moe_layer_forward) against the CPU oracle, at the
+workloads' full sizes, in the launch configuration the benchmark times.
+
+Mode A: the oracle routes on the GPU router's fp32 logits (obtained from
+moe_route, the same kernel the layer runs), so every integer decision is
+shared and must agree bit for bit (counts).  Mode B: the layer output y is
+compared with the oracle's y on that routing -- all tokens for the small
+workloads, a seeded sample of 256 tokens (each one exact, independent of the
+others) for the large ones.
+"""
+import numpy as np
+import pytest
+
+import moe_workloads as mw
+import oracle as o
+import top_routing_expert_moe_amd as moe
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 256
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run_layer(w, d_host, d_dev):
+    torch = gu.torch()
+    y, aux, counts = moe.layer_forward(d_dev["x"], d_dev["W_gate"], d_dev["logit_bias"], d_dev["W1"], d_dev["W3"],
+                                       d_dev["W2"], k=w.k, capacity_factor=w.cf, act=w.act)
+    logits, idx, _, _ = moe.route(d_dev["x"], d_dev["W_gate"], d_dev["logit_bias"], w.k)
+    torch.cuda.synchronize()
+    return y, aux, counts, logits
+
+
+def _check_layer(w, host, y, aux, counts, logits, tokens):
+    gl = gu.from_dev(logits)
+    ref = o.layer_forward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"],
+                          k=w.k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, logits=gl, tokens=tokens)
+    assert np.array_equal(gu.from_dev(counts), ref["counts"])
+    R = int(ref["offsets"][-1])
+    _say(f"  rows kept {R} of {w.T * w.k}; active experts {int((ref['counts'] > 0).sum())}; C={ref['C']}")
+    a = float(gu.from_dev(aux))
+    assert abs(a - ref["aux"]) <= 1e-5 * abs(ref["aux"]), (a, ref["aux"])
+    got = gu.as_f64(gu.from_dev(y)[tokens], w.dtype)
+    if w.dtype == "bf16":
+        ratio = gu.check_bf16_out(got, ref["y64"], "y")
+        _say(f"  y max|d|/RMS = {ratio:.4f}")
+    else:
+        gu.check_rel_rms(got, ref["y64"], 1e-5, "y")
+    return ref
+
+
+@pytest.mark.parametrize("name", [w.name for w in mw.WORKLOADS])
+def test_layer_forward_parity(name):
+    _say(f"layer {name}")
+    w, host, dd = gu.workload(name)
+    y, aux, counts, logits = _run_layer(w, host, dd)
+    if w.T <= 64:
+        tokens = np.arange(w.T)
+    else:
+        tokens = np.sort(np.random.default_rng(123).choice(w.T, SAMPLE, replace=False))
+        tokens[0], tokens[-1] = 0, w.T - 1  # include both ends of the batch
+    _check_layer(w, host, y, aux, counts, logits, tokens)
+
+
+def test_layer_forward_deterministic():
+    torch = gu.torch()
+    for name in ("tiny-fp32", "capacity-e64"):
+        w, host, dd = gu.workload(name)
+        outs = []
+        for _ in range(2):
+            y, aux, counts = moe.layer_forward(dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"],
+                                               k=w.k, capacity_factor=w.cf, act=w.act)
+            torch.cuda.synchronize()
+            outs.append((gu.from_dev(y).copy(), float(gu.from_dev(aux)), gu.from_dev(counts).copy()))
+        assert np.array_equal(outs[0][0], outs[1][0]) and outs[0][1] == outs[1][1]
+        assert np.array_equal(outs[0][2], outs[1][2])
+
+
+@pytest.mark.parametrize("T,h,f,E,k,cf,act,dtype", [
+    (1, 128, 256, 8, 2, 0.0, "swiglu", "bf16"),      # one token
+    (33, 256, 192, 6, 3, 0.0, "gelu", "bf16"),       # ragged against the 32-token router blocks
+    (300, 128, 128, 5, 5, 0.0, "swiglu", "bf16"),    # k = E: every expert, dense mixture
+    (200, 192, 256, 4, 1, 0.3, "gelu", "bf16"),      # heavy drops, k = 1
+    (130, 64, 64, 1, 1, 0.0, "swiglu", "f32"),       # a single expert: the plain FFN
+    (500, 128, 256, 16, 2, 0.25, "swiglu", "f32"),   # drops in fp32
+])
+def test_layer_edge_cases(T, h, f, E, k, cf, act, dtype):
+    import math
+    _say(f"layer edge T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")
+    rng = np.random.default_rng(T + E)
+    conv = (lambda a: mw.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32),
+                logit_bias=rng.standard_normal(E).astype(np.float32),
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)) if act == "swiglu" else None,
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("edge", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
+    y, aux, counts, logits = _run_layer(w, host, dd)
+    ref = _check_layer(w, host, y, aux, counts, logits, np.arange(T))
+    if cf > 0:
+        dropped = (ref["slot_pos"].reshape(T, k) < 0).all(1)
+        if dropped.any():
+            assert (gu.from_dev(y)[dropped] == 0).all()

@@ -1,0 +1,246 @@
+"""MI355X (gfx950) MoE layer forward: a thin ctypes binding over ``libmoe_mi355x.so``.
+
+Only argument marshalling happens here: every step of the layer runs in the
+library's HIP kernels.  PyTorch supplies device memory (tensors are passed by
+``data_ptr()``) and the stream (``torch.cuda.current_stream()``).  There is no
+fallback: if the library is missing or no GPU is present, calls raise.
+
+Entry points mirror the C ABI in ``include/moe.h``: ``route``, ``permute``,
+``expert_ffn``, ``unpermute``, ``layer_forward`` plus ``capacity`` and
+``workspace_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["MoEError", "lib", "lib_path", "capacity", "workspace_bytes", "status_string", "route",
+           "permute", "expert_ffn", "unpermute", "layer_forward", "LAYER_STAGES", "F32", "BF16", "GELU", "SWIGLU",
+           "ROUTE_LOGITS_IN"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libmoe_mi355x.so")
+
+F32, BF16 = 0, 1
+GELU, SWIGLU = 0, 1
+ROUTE_LOGITS_IN = 1
+_ACT = {"gelu": GELU, "swiglu": SWIGLU}
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "moe_capacity": (_i32, [_i32, _i32, _i32, _f32]),
+    "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_route": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                 ctypes.c_uint32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz,
+                                 _c_void_p]),
+    "moe_permute": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _f32, ctypes.c_int,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_expert_ffn": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                      _c_void_p, ctypes.c_int, ctypes.c_int, _c_void_p, _c_void_p, _sz,
+                                      _c_void_p]),
+    "moe_unpermute": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, ctypes.c_int,
+                                     _c_void_p, _c_void_p]),
+    "moe_layer_forward": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_layer_forward_timed": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                               _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
+                                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p,
+                                               _c_void_p]),
+}
+
+LAYER_STAGES = ("route", "hist", "scan", "scatter", "expert_up", "expert_down", "combine")
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is not built: run `python -m top_routing_expert_moe_amd.build`")
+        l = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoEError(status, where)
+
+
+def capacity(T: int, E: int, k: int, capacity_factor: float) -> int | None:
+    """Per-expert capacity as the library computes it; None = never drop."""
+    c = lib().moe_capacity(T, E, k, capacity_factor)
+    if c < 0:
+        raise ValueError("invalid capacity arguments")
+    return None if c == 2 ** 31 - 1 else c
+
+
+def workspace_bytes(T, h, f, E, k, capacity_factor, dtype: int, act: int) -> int:
+    return int(lib().moe_workspace_bytes(T, h, f, E, k, capacity_factor, dtype, act))
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev):
+    return _torch().cuda.current_stream(dev).cuda_stream
+
+
+def _ws(nbytes: int, dev):
+    return _torch().empty(max(int(nbytes), 1), dtype=_torch().uint8, device=dev)
+
+
+def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = False):
+    """Router on ``x[T,h]`` (or on given fp32 ``logits[T,E]``).
+
+    Returns ``(logits, topk_idx, topk_w, prob_sum)`` (prob_sum is None unless
+    requested)."""
+    torch = _torch()
+    ref = logits if logits is not None else x
+    dev = ref.device
+    T = ref.shape[0]
+    E = (logits if logits is not None else W_gate).shape[-1]
+    h = 0 if x is None else x.shape[1]
+    dt = F32 if x is None else _dt(x)
+    flags = ROUTE_LOGITS_IN if logits is not None else 0
+    out_logits = logits if logits is not None else torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ps = torch.empty(E, dtype=torch.float32, device=dev) if with_prob_sum else None
+    ws = _ws(4 * (-(-T // 32)) * E + 512, dev) if with_prob_sum else None
+    st = lib().moe_route(None if logits is not None else _p(x), None if logits is not None else _p(W_gate),
+                         None if (logits is not None or logit_bias is None) else _p(logit_bias),
+                         T, h, E, k, dt, flags, _p(out_logits), _p(idx), _p(w), _p(ps),
+                         _p(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st, "moe_route")
+    return out_logits, idx, w, ps
+
+
+def permute(topk_idx, x, E: int, capacity_factor: float, *, with_x_perm: bool = True, prob_sum=None):
+    """Histogram, capacity, stable sort by expert id and gather.
+
+    Returns a dict with ``counts``, ``offsets``, ``sorted_slot``, ``slot_pos``,
+    ``x_perm`` (or None) and ``aux`` (0-d tensor, or None without prob_sum)."""
+    torch = _torch()
+    dev = topk_idx.device
+    T, k = topk_idx.shape
+    h = 0 if x is None else x.shape[1]
+    dt = F32 if x is None else _dt(x)
+    n = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_slot = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    slot_pos = torch.empty(n, dtype=torch.int32, device=dev)
+    x_perm = torch.empty((n, h), dtype=x.dtype, device=dev) if (with_x_perm and x is not None) else None
+    aux = torch.empty((), dtype=torch.float32, device=dev) if prob_sum is not None else None
+    nhb = -(-n // 2048)
+    ws = _ws(8 * nhb * E + 4 * n + 4096, dev)
+    st = lib().moe_permute(_p(topk_idx), _p(x) if x_perm is not None else None, T, h, E, k,
+                           float(capacity_factor), dt, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_pos),
+                           _p(x_perm), _p(prob_sum), _p(aux), _p(ws), ws.numel(), _stream(dev))
+    _check(st, "moe_permute")
+    return dict(counts=counts, offsets=offsets, sorted_slot=sorted_slot, slot_pos=slot_pos, x_perm=x_perm,
+                aux=aux)
+
+
+def expert_ffn(x_perm, offsets, W1, W3, W2, act: str):
+    """Grouped expert MLP over the segments of ``x_perm``; returns ``out_perm[R_max,h]``."""
+    torch = _torch()
+    dev = x_perm.device
+    R_max, h = x_perm.shape
+    E, _, f = W1.shape
+    dt = _dt(x_perm)
+    out = torch.empty_like(x_perm)
+    ws = _ws(R_max * f * x_perm.element_size() + 4 * (E + 1) + 1024, dev)
+    st = lib().moe_expert_ffn(_p(x_perm), _p(offsets), R_max, h, f, E, _p(W1), _p(W3), _p(W2), _ACT[act], dt,
+                              _p(out), _p(ws), ws.numel(), _stream(dev))
+    _check(st, "moe_expert_ffn")
+    return out
+
+
+def unpermute(out_perm, slot_pos, topk_w):
+    """Weighted combine back to token order; returns ``y[T,h]``."""
+    torch = _torch()
+    T, k = topk_w.shape
+    h = out_perm.shape[1]
+    y = torch.empty((T, h), dtype=out_perm.dtype, device=out_perm.device)
+    st = lib().moe_unpermute(_p(out_perm), _p(slot_pos), _p(topk_w), T, h, k, _dt(out_perm), _p(y),
+                             _stream(out_perm.device))
+    _check(st, "moe_unpermute")
+    return y
+
+
+def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float, act: str,
+                  ws=None, y=None, aux=None, counts=None, events=None):
+    """The whole layer.  Returns ``(y, aux_loss, counts)``.  Pass preallocated
+    ``ws``/``y``/``aux``/``counts`` to avoid allocations in a timed loop.
+    ``events``: a ctypes array of ``len(LAYER_STAGES) + 1`` hipEvent_t handles to
+    record between the stages (the measurement variant of the entry point)."""
+    torch = _torch()
+    dev = x.device
+    T, h = x.shape
+    E, _, f = W1.shape
+    dt = _dt(x)
+    a = _ACT[act]
+    if ws is None:
+        ws = _ws(workspace_bytes(T, h, f, E, k, capacity_factor, dt, a), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    if aux is None:
+        aux = torch.empty((), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    args = (_p(x), _p(W_gate), _p(logit_bias), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor), a,
+            dt, _p(y), _p(aux), _p(counts), _p(ws), ws.numel(), _stream(dev))
+    if events is None:
+        _check(lib().moe_layer_forward(*args), "moe_layer_forward")
+    else:
+        _check(lib().moe_layer_forward_timed(*args, ctypes.cast(events, _c_void_p)), "moe_layer_forward_timed")
+    return y, aux, counts

@@ -1,0 +1,409 @@
+// C ABI of the MoE layer forward: argument checks, workspace carve-up and the
+// launch sequence.  Every check runs on the host before any HIP call; on an
+// error nothing is enqueued.
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <functional>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool dtype_ok(moe_dtype_t dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool act_ok(moe_act_t a) { return a == MOE_ACT_GELU || a == MOE_ACT_SWIGLU; }
+
+// Workspace carve-up from an (aligned-up) base.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* p) : base((char*)p) {
+    if (base) base = (char*)(((uintptr_t)base + kAlign - 1) & ~(uintptr_t)(kAlign - 1));
+  }
+  template <typename T> T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+  size_t bytes() const { return off + kAlign; }  // + slack for aligning the base
+};
+
+int64_t capacity_of(int32_t T, int32_t E, int32_t k, float cf) {
+  const double c = (double)cf;
+  if (!(c > 0.0)) return INT32_MAX;
+  const double tpe = (double)((int64_t)k * T) / (double)E;
+  const double C = floor(c * tpe);
+  if (C < 1.0) return INT32_MAX;
+  if (C >= (double)INT32_MAX) return INT32_MAX;
+  return (int64_t)C;
+}
+
+int rows_max(int32_t T, int32_t E, int32_t k, int64_t C) {
+  const int64_t n = (int64_t)T * k;
+  if (C == INT32_MAX) return (int)n;
+  const int64_t cap = C * E;
+  return (int)(cap < n ? cap : n);
+}
+
+moe_status_t common_sizes(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
+  if ((int64_t)T * k > (int64_t)INT32_MAX / 2) return MOE_ERR_ARG;
+  if (E > 256 || k > 16) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t dim_ok(int32_t d) {
+  if (d <= 0) return MOE_ERR_ARG;
+  if (d % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// --- workspace layouts (the same carve is used to size and to place)
+struct RouteWs { float* prob_part; };
+RouteWs carve_route(Carve& c, int32_t T, int32_t E) {
+  RouteWs w;
+  w.prob_part = c.take<float>((size_t)route_blocks(T) * E);
+  return w;
+}
+
+struct PermWs { int* blk_counts; int* blk_base; int* perm_token; };
+PermWs carve_perm(Carve& c, int32_t T, int32_t E, int32_t k) {
+  PermWs w;
+  const size_t nhb = (size_t)perm_blocks((int64_t)T * k);
+  w.blk_counts = c.take<int>(nhb * E);
+  w.blk_base = c.take<int>(nhb * E);
+  w.perm_token = c.take<int>((size_t)T * k);
+  return w;
+}
+
+struct FfnWs { int* tile_off; void* hm; };
+FfnWs carve_ffn(Carve& c, int R_max, int32_t f, int32_t E, moe_dtype_t dt) {
+  FfnWs w;
+  w.tile_off = c.take<int>((size_t)E + 1);
+  w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
+  return w;
+}
+
+struct LayerWs {
+  float* logits; int* topk_idx; float* topk_w; float* prob_part; int* blk_counts; int* blk_base;
+  int* counts; int* offsets; int* tile_off; float* aux; int* slot_pos; int* sorted_slot;
+  int* perm_token; void* hm; void* o;
+};
+LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int R_max,
+                    moe_dtype_t dt) {
+  LayerWs w;
+  const size_t n = (size_t)T * k;
+  const size_t nhb = (size_t)perm_blocks((int64_t)n);
+  w.logits = c.take<float>((size_t)T * E);
+  w.topk_idx = c.take<int>(n);
+  w.topk_w = c.take<float>(n);
+  w.prob_part = c.take<float>((size_t)route_blocks(T) * E);
+  w.blk_counts = c.take<int>(nhb * E);
+  w.blk_base = c.take<int>(nhb * E);
+  w.counts = c.take<int>(E);
+  w.offsets = c.take<int>((size_t)E + 1);
+  w.tile_off = c.take<int>((size_t)E + 1);
+  w.aux = c.take<float>(1);
+  w.slot_pos = c.take<int>(n);
+  w.sorted_slot = c.take<int>(n);
+  w.perm_token = c.take<int>(n);
+  w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
+  w.o = c.take<char>((size_t)R_max * h * elem_bytes(dt));
+  return w;
+}
+
+#define MOE_TRY(expr)                               \
+  do {                                              \
+    if ((expr) != hipSuccess) return MOE_ERR_DEVICE; \
+  } while (0)
+
+moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const int* tile_off, int R_max,
+                     int32_t h, int32_t f, int32_t E, const void* W1, const void* W3, const void* W2,
+                     moe_act_t act, moe_dtype_t dt, void* hm, void* out, hipStream_t st,
+                     const std::function<bool()>& mark = std::function<bool()>()) {
+  const bool bf = dt == MOE_BF16;
+  GemmArgs up{};
+  up.A = A;
+  up.a_rows = a_rows;
+  up.W = W1;
+  up.W3 = act == MOE_ACT_SWIGLU ? W3 : nullptr;
+  up.K = h;
+  up.N = f;
+  up.out = hm;
+  up.offsets = offsets;
+  up.tile_off = tile_off;
+  up.E = E;
+  up.R_max = R_max;
+  up.act = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
+  MOE_TRY(launch_gemm(up, bf, st));
+  if (mark && !mark()) return MOE_ERR_DEVICE;
+  GemmArgs down = up;
+  down.A = hm;
+  down.a_rows = nullptr;
+  down.W = W2;
+  down.W3 = nullptr;
+  down.K = f;
+  down.N = h;
+  down.out = out;
+  down.act = ACT_NONE;
+  MOE_TRY(launch_gemm(down, bf, st));
+  if (mark && !mark()) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int32_t T, int32_t E, int32_t k, float capacity_factor) {
+  if (T < 0 || E < 1 || k < 1 || !isfinite(capacity_factor)) return -1;
+  return (int32_t)capacity_of(T, E, k, capacity_factor);
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_ARG: return "MOE_ERR_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported size or alignment";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: kernel launch failed";
+  }
+  return "unknown moe_status_t";
+}
+
+size_t moe_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float capacity_factor,
+                           moe_dtype_t dt, moe_act_t act) {
+  if (common_sizes(T, E, k) != MOE_OK || h <= 0 || f <= 0 || !dtype_ok(dt) || !act_ok(act) ||
+      !isfinite(capacity_factor))
+    return 0;
+  const int64_t C = capacity_of(T, E, k, capacity_factor);
+  Carve c(nullptr);
+  carve_layer(c, T, h, f, E, k, rows_max(T, E, k, C), dt);
+  return c.bytes();
+}
+
+moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bias, int32_t T, int32_t h,
+                       int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags, float* logits,
+                       int32_t* topk_idx, float* topk_w, float* prob_sum, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status_t s = common_sizes(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt) || (flags & ~MOE_ROUTE_LOGITS_IN) != 0) return MOE_ERR_ARG;
+  const bool lin = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_ARG;
+  if (!lin) {
+    if (!x || !W_gate) return MOE_ERR_ARG;
+    if ((s = dim_ok(h)) != MOE_OK) return s;
+  }
+  if (T == 0) return MOE_OK;
+  Carve c(ws);
+  RouteWs w = carve_route(c, T, E);
+  if (prob_sum && (!ws || ws_bytes < c.bytes())) return MOE_ERR_WORKSPACE;
+  RouteArgs a{};
+  a.x = x;
+  a.W_gate = W_gate;
+  a.bias = logit_bias;
+  a.T = T;
+  a.h = h;
+  a.E = E;
+  a.k = k;
+  a.bf16 = dt == MOE_BF16;
+  a.logits_in = lin;
+  a.logits = logits;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.prob_part = prob_sum ? w.prob_part : nullptr;
+  MOE_TRY(launch_route(a, stream));
+  if (prob_sum) MOE_TRY(launch_reduce_prob(w.prob_part, route_blocks(T), E, prob_sum, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int32_t h, int32_t E, int32_t k,
+                         float capacity_factor, moe_dtype_t dt, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_slot, int32_t* slot_pos, void* x_perm, const float* prob_sum,
+                         float* aux_loss, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t s = common_sizes(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt) || !isfinite(capacity_factor)) return MOE_ERR_ARG;
+  if (!topk_idx || !counts || !offsets || !sorted_slot || !slot_pos) return MOE_ERR_ARG;
+  if (x_perm) {
+    if (!x) return MOE_ERR_ARG;
+    if ((s = dim_ok(h)) != MOE_OK) return s;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
+  }
+  if (T == 0) return MOE_OK;
+  Carve c(ws);
+  PermWs w = carve_perm(c, T, E, k);
+  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  const int64_t C = capacity_of(T, E, k, capacity_factor);
+  const int n = T * k;
+  MOE_TRY(launch_hist(topk_idx, n, E, w.blk_counts, stream));
+  ScanArgs sa{};
+  sa.blk_counts = w.blk_counts;
+  sa.nhb = perm_blocks(n);
+  sa.E = E;
+  sa.T = T;
+  sa.k = k;
+  sa.C = (int)C;
+  sa.BM = 0;
+  sa.prob_part = nullptr;
+  sa.nrb = 0;
+  sa.prob_sum = prob_sum;
+  sa.counts = counts;
+  sa.offsets = offsets;
+  sa.blk_base = w.blk_base;
+  sa.tile_off = nullptr;
+  sa.aux = (prob_sum && aux_loss) ? aux_loss : nullptr;
+  MOE_TRY(launch_scan(sa, stream));
+  MOE_TRY(launch_scatter(topk_idx, n, E, k, (int)C, offsets, w.blk_base, slot_pos, sorted_slot, w.perm_token,
+                         stream));
+  if (x_perm)
+    MOE_TRY(launch_gather(x, w.perm_token, offsets, E, rows_max(T, E, k, C), h, (int)elem_bytes(dt), x_perm,
+                          stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t R_max, int32_t h, int32_t f,
+                            int32_t E, const void* W1, const void* W3, const void* W2, moe_act_t act,
+                            moe_dtype_t dt, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (R_max < 0 || E < 1) return MOE_ERR_ARG;
+  if (E > 256) return MOE_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt) || !act_ok(act)) return MOE_ERR_ARG;
+  moe_status_t s;
+  if ((s = dim_ok(h)) != MOE_OK) return s;
+  if ((s = dim_ok(f)) != MOE_OK) return s;
+  if (!x_perm || !offsets || !W1 || !W2 || !out_perm) return MOE_ERR_ARG;
+  if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_ARG;
+  if (!aligned16(x_perm) || !aligned16(W1) || !aligned16(W2) || (W3 && !aligned16(W3)) || !aligned16(out_perm))
+    return MOE_ERR_UNSUPPORTED;
+  if (R_max == 0) return MOE_OK;
+  Carve c(ws);
+  FfnWs w = carve_ffn(c, R_max, f, E, dt);
+  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  const bool bf = dt == MOE_BF16;
+  MOE_TRY(launch_tiles(offsets, E, gemm_bm(bf), w.tile_off, stream));
+  return run_ffn(x_perm, nullptr, offsets, w.tile_off, R_max, h, f, E, W1, W3, W2, act, dt, w.hm, out_perm,
+                 stream);
+}
+
+moe_status_t moe_unpermute(const void* out_perm, const int32_t* slot_pos, const float* topk_w, int32_t T,
+                           int32_t h, int32_t k, moe_dtype_t dt, void* y, hipStream_t stream) {
+  if (T < 0 || k < 1) return MOE_ERR_ARG;
+  if (k > 16) return MOE_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt)) return MOE_ERR_ARG;
+  moe_status_t s;
+  if ((s = dim_ok(h)) != MOE_OK) return s;
+  if (!out_perm || !slot_pos || !topk_w || !y) return MOE_ERR_ARG;
+  if (!aligned16(out_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  MOE_TRY(launch_combine(out_perm, slot_pos, topk_w, T, h, k, dt == MOE_BF16, y, stream));
+  return MOE_OK;
+}
+
+static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const float* logit_bias,
+                                       const void* W1, const void* W3, const void* W2, int32_t T, int32_t h,
+                                       int32_t f, int32_t E, int32_t k, float capacity_factor, moe_act_t act,
+                                       moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, void* ws,
+                                       size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+  moe_status_t s = common_sizes(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor)) return MOE_ERR_ARG;
+  if ((s = dim_ok(h)) != MOE_OK) return s;
+  if ((s = dim_ok(f)) != MOE_OK) return s;
+  if (!x || !W_gate || !W1 || !W2 || !y) return MOE_ERR_ARG;
+  if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || (W3 && !aligned16(W3)) || !aligned16(y))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const int64_t C = capacity_of(T, E, k, capacity_factor);
+  const int R_max = rows_max(T, E, k, C);
+  Carve c(ws);
+  LayerWs w = carve_layer(c, T, h, f, E, k, R_max, dt);
+  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  const bool bf = dt == MOE_BF16;
+  const int n = T * k;
+  int stage = 0;
+  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
+  if (!mark()) return MOE_ERR_DEVICE;
+
+  RouteArgs ra{};
+  ra.x = x;
+  ra.W_gate = W_gate;
+  ra.bias = logit_bias;
+  ra.T = T;
+  ra.h = h;
+  ra.E = E;
+  ra.k = k;
+  ra.bf16 = bf;
+  ra.logits_in = false;
+  ra.logits = w.logits;
+  ra.topk_idx = w.topk_idx;
+  ra.topk_w = w.topk_w;
+  ra.prob_part = w.prob_part;
+  MOE_TRY(launch_route(ra, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
+  MOE_TRY(launch_hist(w.topk_idx, n, E, w.blk_counts, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
+  ScanArgs sa{};
+  sa.blk_counts = w.blk_counts;
+  sa.nhb = perm_blocks(n);
+  sa.E = E;
+  sa.T = T;
+  sa.k = k;
+  sa.C = (int)C;
+  sa.BM = gemm_bm(bf);
+  sa.prob_part = w.prob_part;
+  sa.nrb = route_blocks(T);
+  sa.prob_sum = nullptr;
+  sa.counts = counts ? counts : w.counts;
+  sa.offsets = w.offsets;
+  sa.blk_base = w.blk_base;
+  sa.tile_off = w.tile_off;
+  sa.aux = aux_loss ? aux_loss : w.aux;
+  MOE_TRY(launch_scan(sa, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
+  MOE_TRY(launch_scatter(w.topk_idx, n, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
+                         w.perm_token, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
+  moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
+                           w.o, stream, ev ? [&]() { return mark(); } : std::function<bool()>());
+  if (r != MOE_OK) return r;
+  MOE_TRY(launch_combine(w.o, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
+                               const void* W3, const void* W2, int32_t T, int32_t h, int32_t f, int32_t E,
+                               int32_t k, float capacity_factor, moe_act_t act, moe_dtype_t dt, void* y,
+                               float* aux_loss, int32_t* counts, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  return layer_forward_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, y,
+                            aux_loss, counts, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status_t moe_layer_forward_timed(const void* x, const float* W_gate, const float* logit_bias,
+                                     const void* W1, const void* W3, const void* W2, int32_t T, int32_t h,
+                                     int32_t f, int32_t E, int32_t k, float capacity_factor, moe_act_t act,
+                                     moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, void* ws,
+                                     size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  if (events == nullptr) return MOE_ERR_ARG;
+  for (int i = 0; i < MOE_LAYER_STAGES + 1; ++i)
+    if (events[i] == nullptr) return MOE_ERR_ARG;
+  return layer_forward_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, y,
+                            aux_loss, counts, ws, ws_bytes, stream, events);
+}
+
+}  // extern "C"

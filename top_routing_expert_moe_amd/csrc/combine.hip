@@ -1,0 +1,79 @@
+// Weighted combine back to token order.
+//
+// Method: a token's output is the sum over its k selected experts of the gate
+// weight times that expert's output (ops-transformer MoE article, "原理" Step
+// 4; MegaBlocks chapter 1, section 4.3, binned_scatter).  A dropped slot adds
+// nothing and the remaining weights are not rescaled (same chapter, sections
+// 3 and 4.5).
+//
+// gfx950 design: one thread per (token, 8 consecutive columns); it reads the
+// k expert-output rows through slot_pos with 16-byte (bf16) or 32-byte (fp32)
+// loads and sums w_j * O in fp32, j ascending, in registers -- the
+// [tokens, k, h] temporary of the page's scatter-then-sum is never formed.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, const int* __restrict__ slot_pos,
+                                                      const float* __restrict__ topk_w, int T, int h, int k,
+                                                      OT* __restrict__ y) {
+  const int groups = h >> 3;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)T * groups) return;
+  const int t = (int)(gid / groups);
+  const int c = (int)(gid % groups) * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int pos = slot_pos[(size_t)t * k + j];
+    if (pos < 0) continue;
+    const float wj = topk_w[(size_t)t * k + j];
+    const OT* src = O + (size_t)pos * h + c;
+    if constexpr (sizeof(OT) == 2) {
+      const u32x4 v = *(const u32x4*)src;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wj * __uint_as_float(v[i] << 16);
+        acc[2 * i + 1] += wj * __uint_as_float(v[i] & 0xFFFF0000u);
+      }
+    } else {
+      const floatx4 v0 = *(const floatx4*)src, v1 = *(const floatx4*)(src + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += wj * v0[i];
+        acc[4 + i] += wj * v1[i];
+      }
+    }
+  }
+  OT* dst = y + (size_t)t * h + c;
+  if constexpr (sizeof(OT) == 2) {
+    *(u32x4*)dst = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  } else {
+    *(floatx4*)dst = floatx4{acc[0], acc[1], acc[2], acc[3]};
+    *(floatx4*)(dst + 4) = floatx4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* O, const int* slot_pos, const float* topk_w, int T, int h, int k,
+                          bool bf16, void* y, hipStream_t st) {
+  const int64_t n = (int64_t)T * (h / 8);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (grid == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)O, slot_pos, topk_w,
+                       T, h, k, (bf16_t*)y);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)O, slot_pos, topk_w, T,
+                       h, k, (float*)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

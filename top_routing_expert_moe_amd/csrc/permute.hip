@@ -1,0 +1,235 @@
+// Token permutation: expert histogram, capacity + prefix sums, stable
+// scatter (the sort of assignments by expert id), gather of token rows.
+//
+// Method (MegaBlocks chapter "01 · MoE 为什么难算：变长专家输入", sections 4.1,
+// 4.2, 4.5, 4.6): the flattened expert ids (T*k of them) are sorted by expert
+// id, counted per expert (tokens_per_expert) and turned into per-expert end
+// positions by a running sum; with a capacity C an expert keeps its first C
+// assignments and later ones are dropped (they add nothing to the output).
+// C = floor(cf * T*k / E); a computed C of zero means "never drop".
+//
+// gfx950 design: no radix sort.  E <= 256 means one 8-bit digit, so a single
+// *stable counting scatter* does the sort:
+//   hist    : each block of 2048 consecutive assignments counts its experts in
+//             LDS (order-free atomics) -> blk_counts[b][e];
+//   scan    : one workgroup turns the counts into pre-drop ranks per block
+//             (blk_base), kept counts, exclusive offsets, the GEMM m-tile
+//             schedule and the aux loss (fixed summation order);
+//   scatter : each block ranks its assignments in order with wave ballots
+//             (a multisplit on the expert-id bits: lanes with the same expert
+//             in lower lanes are counted by popcount), then across its 4 waves
+//             and 8 rounds through LDS.  Rank = blk_base + in-block rank, so
+//             the result equals a stable sort for any number of blocks.
+#include <limits.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int PB = kPermBlock;
+constexpr int PR = PB / 256;  // rounds of 256 assignments per block
+
+__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ topk_idx, int n, int E,
+                                                   int* __restrict__ blk_counts) {
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * PB;
+#pragma unroll
+  for (int r = 0; r < PR; ++r) {
+    const int64_t s = base + r * 256 + tid;
+    if (s < n) {
+      const int e = topk_idx[s];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+// Inclusive Hillis-Steele scan over 256 threads (one value each).
+__device__ int block_inclusive_scan(int v, int* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int add = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  int r = sh[tid];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  __shared__ int sh[256];
+  __shared__ double dsh[256];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  int cnt = 0;
+  if (tid < E) {
+    for (int b = 0; b < a.nhb; ++b) {
+      const int c = a.blk_counts[(size_t)b * E + tid];
+      a.blk_base[(size_t)b * E + tid] = cnt;
+      cnt += c;
+    }
+  }
+  const int kept = tid < E ? min(cnt, a.C) : 0;
+  const int incl = block_inclusive_scan(kept, sh);
+  if (tid < E) {
+    a.counts[tid] = cnt;
+    a.offsets[tid] = incl - kept;
+    if (tid == E - 1) a.offsets[E] = incl;
+  }
+  if (a.BM > 0 && a.tile_off != nullptr) {
+    const int mt = tid < E ? (kept + a.BM - 1) / a.BM : 0;
+    const int tin = block_inclusive_scan(mt, sh);
+    if (tid < E) {
+      a.tile_off[tid] = tin - mt;
+      if (tid == E - 1) a.tile_off[E] = tin;
+    }
+  }
+  if (a.aux != nullptr && (a.prob_part != nullptr || a.prob_sum != nullptr)) {
+    double term = 0.0;
+    if (tid < E) {
+      double ps = 0.0;
+      if (a.prob_part != nullptr) {
+        for (int b = 0; b < a.nrb; ++b) ps += (double)a.prob_part[(size_t)b * E + tid];
+      } else {
+        ps = (double)a.prob_sum[tid];
+      }
+      const double n = (double)a.T * (double)a.k;
+      term = ((double)cnt / n) * (ps / (double)a.T);
+    }
+    dsh[tid] = term;
+    __syncthreads();
+    for (int o = 128; o >= 1; o >>= 1) {
+      if (tid < o) dsh[tid] += dsh[tid + o];
+      __syncthreads();
+    }
+    if (tid == 0) *a.aux = (float)((double)E * dsh[0]);
+  }
+}
+
+__global__ __launch_bounds__(256) void tiles_kernel(const int* __restrict__ offsets, int E, int BM,
+                                                    int* __restrict__ tile_off) {
+  __shared__ int sh[256];
+  const int tid = threadIdx.x;
+  const int rows = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
+  const int mt = (rows + BM - 1) / BM;
+  const int incl = block_inclusive_scan(mt, sh);
+  if (tid < E) {
+    tile_off[tid] = incl - mt;
+    if (tid == E - 1) tile_off[E] = incl;
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ topk_idx, int n, int E,
+                                                      int k, int nbits, int C,
+                                                      const int* __restrict__ offsets,
+                                                      const int* __restrict__ blk_base,
+                                                      int* __restrict__ slot_pos,
+                                                      int* __restrict__ sorted_slot,
+                                                      int* __restrict__ perm_token) {
+  __shared__ int run[256];
+  __shared__ int wcnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  run[tid] = 0;
+  const int64_t base = (int64_t)blockIdx.x * PB;
+  const int* bb = blk_base + (size_t)blockIdx.x * E;
+  for (int r = 0; r < PR; ++r) {
+    wcnt[0][tid] = 0;
+    wcnt[1][tid] = 0;
+    wcnt[2][tid] = 0;
+    wcnt[3][tid] = 0;
+    __syncthreads();
+    const int64_t s = base + r * 256 + tid;
+    int e = -1;
+    if (s < n) e = topk_idx[s];
+    const bool valid = (unsigned)e < (unsigned)E;
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = valid && ((e >> bit) & 1);
+      const uint64_t b = __ballot(on);
+      match &= on ? b : ~b;
+    }
+    const int rank_w = __popcll(match & lt_mask);
+    if (valid && rank_w == 0) wcnt[w][e] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int pre = run[e];
+      for (int q = 0; q < w; ++q) pre += wcnt[q][e];
+      const int g = bb[e] + pre + rank_w;  // rank among all earlier assignments to e
+      if (g < C) {
+        const int row = offsets[e] + g;
+        slot_pos[s] = row;
+        sorted_slot[row] = (int)s;
+        perm_token[row] = (int)(s / k);
+      } else {
+        slot_pos[s] = -1;
+      }
+    } else if (s < n) {
+      slot_pos[s] = -1;
+    }
+    __syncthreads();
+    run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    __syncthreads();
+  }
+}
+
+// x_perm[r] = x[perm_token[r]] for r < offsets[E]; one workgroup per row.
+__global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x,
+                                                     const int* __restrict__ perm_token,
+                                                     const int* __restrict__ offsets, int E,
+                                                     int vec_per_row, u32x4* __restrict__ x_perm) {
+  const int r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  const size_t src = (size_t)perm_token[r] * vec_per_row;
+  const size_t dst = (size_t)r * vec_per_row;
+  for (int i = threadIdx.x; i < vec_per_row; i += 256) x_perm[dst + i] = x[src + i];
+}
+
+}  // namespace
+
+hipError_t launch_hist(const int* topk_idx, int n, int E, int* blk_counts, hipStream_t st) {
+  hipLaunchKernelGGL(hist_kernel, dim3(perm_blocks(n)), dim3(256), 0, st, topk_idx, n, E, blk_counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles(const int* offsets, int E, int BM, int* tile_off, hipStream_t st) {
+  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(256), 0, st, offsets, E, BM, tile_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int* topk_idx, int n, int E, int k, int C, const int* offsets,
+                          const int* blk_base, int* slot_pos, int* sorted_slot, int* perm_token,
+                          hipStream_t st) {
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  hipLaunchKernelGGL(scatter_kernel, dim3(perm_blocks(n)), dim3(256), 0, st, topk_idx, n, E, k, nbits,
+                     C, offsets, blk_base, slot_pos, sorted_slot, perm_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* x, const int* perm_token, const int* offsets, int E, int R_max,
+                         int h, int elem_bytes, void* x_perm, hipStream_t st) {
+  if (R_max <= 0) return hipSuccess;
+  const int vec = h * elem_bytes / 16;
+  hipLaunchKernelGGL(gather_kernel, dim3(R_max), dim3(256), 0, st, (const u32x4*)x, perm_token, offsets,
+                     E, vec, (u32x4*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe
