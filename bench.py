@@ -177,7 +177,7 @@ def main():
     # compulsory bytes of routing + permutation metadata: x and W_gate read once, logits written,
     # topk idx/w, slot_pos and the sorted order (4 B each per assignment)
     route_bytes = T * h * es + h * E * 4 + T * E * 4 + T * k * 16
-    route_ms = sum(stage_ms[s] for s in ("route", "hist", "scan", "scatter"))
+    route_ms = sum(stage_ms[s] for s in ("logits", "select", "scan", "scatter"))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry(w.name),
                 "kernel": "expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue)" if w.act == "swiglu"

@@ -83,7 +83,9 @@ const char* moe_status_string(moe_status_t s);
  *   topk_idx [T,k] int32: slot j = j-th best expert; order (logit desc, expert asc)
  *   topk_w   [T,k] fp32: softmax of the selected logits (sums to 1 per token)
  *   prob_sum [E] fp32 or NULL: sum over tokens of the full softmax (for the aux loss)
- *   ws: needs 4*ceil(T/32)*E bytes (+256) when prob_sum is given, else may be NULL. */
+ *   ws: scratch for the split router weights (bf16 x: 6*ceil(E/16)*16*h bytes) and for
+ *       per-block softmax sums (prob_sum: 4*ceil(T/64)*E bytes), each rounded up to 256,
+ *       plus 256; may be NULL for fp32 x (or MOE_ROUTE_LOGITS_IN) without prob_sum. */
 moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bias,
                        int32_t T, int32_t h, int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags,
                        float* logits, int32_t* topk_idx, float* topk_w, float* prob_sum,
@@ -100,7 +102,7 @@ moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bi
  *   prob_sum [E] fp32 or NULL (from moe_route), aux_loss: device fp32 scalar or NULL --
  *            when both are given, aux = E * sum_e (counts_e/(T*k)) * (prob_sum_e/T),
  *            unscaled ([OPS] 坑1; [RTR] load-balancing passage; [CAI] MoeLoss).
- *   ws: needs about 8*ceil(T*k/2048)*E + 4*T*k + 8*E bytes (see moe_workspace_bytes). */
+ *   ws: needs about 8*ceil(T/64)*E + 4*T*k bytes (see moe_workspace_bytes). */
 moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int32_t h, int32_t E,
                          int32_t k, float capacity_factor, moe_dtype_t dt,
                          int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
@@ -145,8 +147,8 @@ moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* 
 /* Measurement variant of moe_layer_forward: the same kernels on the same stream, with
  * caller-created HIP events recorded between the stages, so a profiler-free caller can
  * time each kernel: events[0] before the router, then one after each stage in order
- * (router, histogram, scan, scatter, expert up-projection, expert down-projection,
- * combine).  `events` holds MOE_LAYER_STAGES + 1 valid hipEvent_t (MOE_ERR_ARG otherwise). */
+ * (router logits, selection + histogram, scan, scatter, expert up-projection, expert
+ * down-projection, combine).  `events` holds MOE_LAYER_STAGES + 1 valid hipEvent_t (MOE_ERR_ARG otherwise). */
 #define MOE_LAYER_STAGES 7
 moe_status_t moe_layer_forward_timed(const void* x, const float* W_gate, const float* logit_bias,
                                      const void* W1, const void* W3, const void* W2,

@@ -74,6 +74,26 @@ def test_route_ties_signed_zero_and_k_equals_E():
         assert np.abs(gu.from_dev(wt).astype(np.float64).sum(1) - 1).max() < 1e-6
 
 
+@pytest.mark.parametrize("T,h,E,k", [(65, 192, 8, 2), (100, 64, 40, 3), (1, 256, 256, 8), (130, 320, 96, 4),
+                                     (70, 128, 32, 1), (3, 192, 16, 16), (257, 512, 64, 2), (64, 1024, 200, 6)])
+def test_route_bf16_shapes(T, h, E, k):
+    """The MFMA router's code paths: k split across waves (h % 128), 1/2/4 expert blocks, ragged T and E."""
+    torch = gu.torch()
+    rng = np.random.default_rng(T * 7 + E)
+    x = mw.f32_to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    Wg = (rng.standard_normal((h, E)) / np.sqrt(h)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    logits, idx, wt, ps = moe.route(gu.to_dev(x, "bf16"), gu.to_dev(Wg, "f32"), gu.to_dev(b, "f32"), k,
+                                    with_prob_sum=True)
+    torch.cuda.synchronize()
+    gl = gu.from_dev(logits)
+    gu.check_rel_rms(gl, o.router_logits(x, Wg, b, "bf16"), 1e-5, "logits")
+    ridx = o.select_topk(gl, k)
+    assert np.array_equal(gu.from_dev(idx), ridx)
+    gu.check_rel_rms(gu.from_dev(wt), o.topk_weights(gl, ridx), 1e-5, "topk_w")
+    gu.check_rel_rms(gu.from_dev(ps), o.softmax(gl).sum(0), 1e-5, "prob_sum")
+
+
 def test_route_fp32_input_small_T():
     torch = gu.torch()
     rng = np.random.default_rng(8)

@@ -55,7 +55,7 @@ _SIGS = {
                                                _c_void_p]),
 }
 
-LAYER_STAGES = ("route", "hist", "scan", "scatter", "expert_up", "expert_down", "combine")
+LAYER_STAGES = ("logits", "select", "scan", "scatter", "expert_up", "expert_down", "combine")
 
 _lib = None
 
@@ -154,7 +154,9 @@ def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = F
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     ps = torch.empty(E, dtype=torch.float32, device=dev) if with_prob_sum else None
-    ws = _ws(4 * (-(-T // 32)) * E + 512, dev) if with_prob_sum else None
+    need = (4 * (-(-T // 64)) * E + 256 if with_prob_sum else 0) + \
+        (6 * (-(-E // 16)) * 16 * h + 256 if (logits is None and dt == BF16) else 0)
+    ws = _ws(need + 256, dev) if need else None
     st = lib().moe_route(None if logits is not None else _p(x), None if logits is not None else _p(W_gate),
                          None if (logits is not None or logit_bias is None) else _p(logit_bias),
                          T, h, E, k, dt, flags, _p(out_logits), _p(idx), _p(w), _p(ps),
@@ -180,7 +182,7 @@ def permute(topk_idx, x, E: int, capacity_factor: float, *, with_x_perm: bool = 
     slot_pos = torch.empty(n, dtype=torch.int32, device=dev)
     x_perm = torch.empty((n, h), dtype=x.dtype, device=dev) if (with_x_perm and x is not None) else None
     aux = torch.empty((), dtype=torch.float32, device=dev) if prob_sum is not None else None
-    nhb = -(-n // 2048)
+    nhb = -(-T // 64)
     ws = _ws(8 * nhb * E + 4 * n + 4096, dev)
     st = lib().moe_permute(_p(topk_idx), _p(x) if x_perm is not None else None, T, h, E, k,
                            float(capacity_factor), dt, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_pos),

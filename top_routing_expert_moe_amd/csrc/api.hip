@@ -71,17 +71,18 @@ moe_status_t dim_ok(int32_t d) {
 }
 
 // --- workspace layouts (the same carve is used to size and to place)
-struct RouteWs { float* prob_part; };
-RouteWs carve_route(Carve& c, int32_t T, int32_t E) {
+struct RouteWs { float* prob_part; uint16_t* planes; };
+RouteWs carve_route(Carve& c, int32_t T, int32_t h, int32_t E, bool prob, bool planes) {
   RouteWs w;
-  w.prob_part = c.take<float>((size_t)route_blocks(T) * E);
+  w.prob_part = prob ? c.take<float>((size_t)route_blocks(T) * E) : nullptr;
+  w.planes = planes ? c.take<uint16_t>((size_t)route_planes_elems(h, E)) : nullptr;
   return w;
 }
 
 struct PermWs { int* blk_counts; int* blk_base; int* perm_token; };
 PermWs carve_perm(Carve& c, int32_t T, int32_t E, int32_t k) {
   PermWs w;
-  const size_t nhb = (size_t)perm_blocks((int64_t)T * k);
+  const size_t nhb = (size_t)route_blocks(T);
   w.blk_counts = c.take<int>(nhb * E);
   w.blk_base = c.take<int>(nhb * E);
   w.perm_token = c.take<int>((size_t)T * k);
@@ -97,6 +98,7 @@ FfnWs carve_ffn(Carve& c, int R_max, int32_t f, int32_t E, moe_dtype_t dt) {
 }
 
 struct LayerWs {
+  uint16_t* planes;
   float* logits; int* topk_idx; float* topk_w; float* prob_part; int* blk_counts; int* blk_base;
   int* counts; int* offsets; int* tile_off; float* aux; int* slot_pos; int* sorted_slot;
   int* perm_token; void* hm; void* o;
@@ -105,7 +107,8 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
                     moe_dtype_t dt) {
   LayerWs w;
   const size_t n = (size_t)T * k;
-  const size_t nhb = (size_t)perm_blocks((int64_t)n);
+  const size_t nhb = (size_t)route_blocks(T);
+  w.planes = dt == MOE_BF16 ? c.take<uint16_t>((size_t)route_planes_elems(h, E)) : nullptr;
   w.logits = c.take<float>((size_t)T * E);
   w.topk_idx = c.take<int>(n);
   w.topk_w = c.take<float>(n);
@@ -120,7 +123,7 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
   w.sorted_slot = c.take<int>(n);
   w.perm_token = c.take<int>(n);
   w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
-  w.o = c.take<char>((size_t)R_max * h * elem_bytes(dt));
+  w.o = c.take<float>((size_t)R_max * h);  // expert outputs stay fp32 until the combine
   return w;
 }
 
@@ -131,7 +134,7 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
 
 moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const int* tile_off, int R_max,
                      int32_t h, int32_t f, int32_t E, const void* W1, const void* W3, const void* W2,
-                     moe_act_t act, moe_dtype_t dt, void* hm, void* out, hipStream_t st,
+                     moe_act_t act, moe_dtype_t dt, void* hm, void* out, bool out_f32, hipStream_t st,
                      const std::function<bool()>& mark = std::function<bool()>()) {
   const bool bf = dt == MOE_BF16;
   GemmArgs up{};
@@ -158,6 +161,7 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   down.N = h;
   down.out = out;
   down.act = ACT_NONE;
+  down.out_f32 = out_f32;
   MOE_TRY(launch_gemm(down, bf, st));
   if (mark && !mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
@@ -209,8 +213,9 @@ moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bi
   }
   if (T == 0) return MOE_OK;
   Carve c(ws);
-  RouteWs w = carve_route(c, T, E);
-  if (prob_sum && (!ws || ws_bytes < c.bytes())) return MOE_ERR_WORKSPACE;
+  const bool need_planes = !lin && dt == MOE_BF16;
+  RouteWs w = carve_route(c, T, h, E, prob_sum != nullptr, need_planes);
+  if ((prob_sum || need_planes) && (!ws || ws_bytes < c.bytes())) return MOE_ERR_WORKSPACE;
   RouteArgs a{};
   a.x = x;
   a.W_gate = W_gate;
@@ -225,6 +230,8 @@ moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bi
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.prob_part = prob_sum ? w.prob_part : nullptr;
+  a.blk_counts = nullptr;
+  a.planes = w.planes;
   MOE_TRY(launch_route(a, stream));
   if (prob_sum) MOE_TRY(launch_reduce_prob(w.prob_part, route_blocks(T), E, prob_sum, stream));
   return MOE_OK;
@@ -248,11 +255,10 @@ moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int3
   PermWs w = carve_perm(c, T, E, k);
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   const int64_t C = capacity_of(T, E, k, capacity_factor);
-  const int n = T * k;
-  MOE_TRY(launch_hist(topk_idx, n, E, w.blk_counts, stream));
+  MOE_TRY(launch_hist(topk_idx, T, k, E, w.blk_counts, stream));
   ScanArgs sa{};
   sa.blk_counts = w.blk_counts;
-  sa.nhb = perm_blocks(n);
+  sa.nhb = route_blocks(T);
   sa.E = E;
   sa.T = T;
   sa.k = k;
@@ -267,7 +273,7 @@ moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int3
   sa.tile_off = nullptr;
   sa.aux = (prob_sum && aux_loss) ? aux_loss : nullptr;
   MOE_TRY(launch_scan(sa, stream));
-  MOE_TRY(launch_scatter(topk_idx, n, E, k, (int)C, offsets, w.blk_base, slot_pos, sorted_slot, w.perm_token,
+  MOE_TRY(launch_scatter(topk_idx, T, E, k, (int)C, offsets, w.blk_base, slot_pos, sorted_slot, w.perm_token,
                          stream));
   if (x_perm)
     MOE_TRY(launch_gather(x, w.perm_token, offsets, E, rows_max(T, E, k, C), h, (int)elem_bytes(dt), x_perm,
@@ -295,7 +301,7 @@ moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t 
   const bool bf = dt == MOE_BF16;
   MOE_TRY(launch_tiles(offsets, E, gemm_bm(bf), w.tile_off, stream));
   return run_ffn(x_perm, nullptr, offsets, w.tile_off, R_max, h, f, E, W1, W3, W2, act, dt, w.hm, out_perm,
-                 stream);
+                 false, stream);
 }
 
 moe_status_t moe_unpermute(const void* out_perm, const int32_t* slot_pos, const float* topk_w, int32_t T,
@@ -308,7 +314,7 @@ moe_status_t moe_unpermute(const void* out_perm, const int32_t* slot_pos, const 
   if (!out_perm || !slot_pos || !topk_w || !y) return MOE_ERR_ARG;
   if (!aligned16(out_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  MOE_TRY(launch_combine(out_perm, slot_pos, topk_w, T, h, k, dt == MOE_BF16, y, stream));
+  MOE_TRY(launch_combine(out_perm, dt == MOE_F32, slot_pos, topk_w, T, h, k, dt == MOE_BF16, y, stream));
   return MOE_OK;
 }
 
@@ -333,7 +339,6 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   LayerWs w = carve_layer(c, T, h, f, E, k, R_max, dt);
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   const bool bf = dt == MOE_BF16;
-  const int n = T * k;
   int stage = 0;
   auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
   if (!mark()) return MOE_ERR_DEVICE;
@@ -352,13 +357,15 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   ra.topk_idx = w.topk_idx;
   ra.topk_w = w.topk_w;
   ra.prob_part = w.prob_part;
-  MOE_TRY(launch_route(ra, stream));
+  ra.blk_counts = w.blk_counts;  // the histogram is counted by the selection kernel
+  ra.planes = w.planes;
+  MOE_TRY(launch_logits(ra, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  MOE_TRY(launch_hist(w.topk_idx, n, E, w.blk_counts, stream));
+  MOE_TRY(launch_select(ra, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   ScanArgs sa{};
   sa.blk_counts = w.blk_counts;
-  sa.nhb = perm_blocks(n);
+  sa.nhb = route_blocks(T);
   sa.E = E;
   sa.T = T;
   sa.k = k;
@@ -374,13 +381,13 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.aux = aux_loss ? aux_loss : w.aux;
   MOE_TRY(launch_scan(sa, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  MOE_TRY(launch_scatter(w.topk_idx, n, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
+  MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
                          w.perm_token, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
-                           w.o, stream, ev ? [&]() { return mark(); } : std::function<bool()>());
+                           w.o, bf, stream, ev ? [&]() { return mark(); } : std::function<bool()>());
   if (r != MOE_OK) return r;
-  MOE_TRY(launch_combine(w.o, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
+  MOE_TRY(launch_combine(w.o, true, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
 }

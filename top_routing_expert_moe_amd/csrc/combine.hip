@@ -17,10 +17,10 @@ namespace moe {
 
 namespace {
 
-template <typename OT>
+template <typename OT, typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, const int* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w, int T, int h, int k,
-                                                      OT* __restrict__ y) {
+                                                      YT* __restrict__ y) {
   const int groups = h >> 3;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (int64_t)T * groups) return;
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, 
       }
     }
   }
-  OT* dst = y + (size_t)t * h + c;
-  if constexpr (sizeof(OT) == 2) {
+  YT* dst = y + (size_t)t * h + c;
+  if constexpr (sizeof(YT) == 2) {
     *(u32x4*)dst = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                          pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
   } else {
@@ -62,17 +62,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, 
 
 }  // namespace
 
-hipError_t launch_combine(const void* O, const int* slot_pos, const float* topk_w, int T, int h, int k,
-                          bool bf16, void* y, hipStream_t st) {
+hipError_t launch_combine(const void* O, bool o_f32, const int* slot_pos, const float* topk_w, int T, int h,
+                          int k, bool bf16, void* y, hipStream_t st) {
   const int64_t n = (int64_t)T * (h / 8);
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (grid == 0) return hipSuccess;
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)O, slot_pos, topk_w,
-                       T, h, k, (bf16_t*)y);
+  if (bf16 && o_f32)
+    hipLaunchKernelGGL((combine_kernel<float, bf16_t>), dim3(grid), dim3(256), 0, st, (const float*)O, slot_pos,
+                       topk_w, T, h, k, (bf16_t*)y);
+  else if (bf16)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), dim3(grid), dim3(256), 0, st, (const bf16_t*)O, slot_pos,
+                       topk_w, T, h, k, (bf16_t*)y);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)O, slot_pos, topk_w, T,
-                       h, k, (float*)y);
+    hipLaunchKernelGGL((combine_kernel<float, float>), dim3(grid), dim3(256), 0, st, (const float*)O, slot_pos,
+                       topk_w, T, h, k, (float*)y);
   return hipGetLastError();
 }
 

@@ -35,14 +35,19 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 
+__device__ __forceinline__ void store4(bf16_t* p, const float* v) {
+  *(u32x2*)p = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store4(float* p, const float* v) { *(floatx4*)p = floatx4{v[0], v[1], v[2], v[3]}; }
+
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // element offset of (row, 16-byte chunk) in a [256][64] bf16 LDS tile
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 3); }
 
-template <int ACT, bool GATHER>
+template <int ACT, bool GATHER, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
-    const bf16_t* __restrict__ W3, int K, int N, bf16_t* __restrict__ out,
+    const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out,
     const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, int NT) {
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
   __shared__ __attribute__((aligned(16))) bf16_t Wl[2][BN * BK];
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int jb = 0; jb < 4; ++jb) {
     const int r = row0 + wm * 128 + jb * 32 + (lane & 31);
     if (r >= row_end) continue;
-    bf16_t* orow = out + (size_t)r * N;
+    OT* orow = out + (size_t)r * N;
     if (ACT == ACT_SWIGLU) {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           float v[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) v[p] = silu(acc[ib][jb][4 * q + p]) * acc[ib + 2][jb][4 * q + p];
-          *(u32x2*)(orow + col) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          store4(orow + col, v);
         }
     } else {
 #pragma unroll
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const float z = acc[ib][jb][4 * q + p];
             v[p] = ACT == ACT_GELU ? gelu_erf(z) : z;
           }
-          *(u32x2*)(orow + col) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          store4(orow + col, v);
         }
     }
   }
@@ -295,16 +300,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   }
 }
 
-template <int ACT, bool G>
+template <int ACT, bool G, typename OT>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;
   const int NT = (a.N + NO - 1) / NO;
   const long long slots = ((long long)(a.R_max + BM - 1) / BM + a.E) * NT;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT>), dim3((unsigned)grid), dim3(256), 0, st,
                      (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                     (bf16_t*)a.out, a.offsets, a.tile_off, a.E, NT);
+                     (OT*)a.out, a.offsets, a.tile_off, a.E, NT);
   return hipGetLastError();
 }
 
@@ -321,10 +326,14 @@ hipError_t launch_f32_t(const GemmArgs& a, hipStream_t st) {
 
 template <bool BF, bool G>
 hipError_t dispatch_act(const GemmArgs& a, hipStream_t st) {
+  if (BF && a.out_f32) {
+    if (a.act != ACT_NONE) return hipErrorInvalidValue;
+    return launch_bf16_t<ACT_NONE, G, float>(a, st);
+  }
   switch (a.act) {
-    case ACT_NONE: return BF ? launch_bf16_t<ACT_NONE, G>(a, st) : launch_f32_t<ACT_NONE, G>(a, st);
-    case ACT_GELU: return BF ? launch_bf16_t<ACT_GELU, G>(a, st) : launch_f32_t<ACT_GELU, G>(a, st);
-    case ACT_SWIGLU: return BF ? launch_bf16_t<ACT_SWIGLU, G>(a, st) : launch_f32_t<ACT_SWIGLU, G>(a, st);
+    case ACT_NONE: return BF ? launch_bf16_t<ACT_NONE, G, bf16_t>(a, st) : launch_f32_t<ACT_NONE, G>(a, st);
+    case ACT_GELU: return BF ? launch_bf16_t<ACT_GELU, G, bf16_t>(a, st) : launch_f32_t<ACT_GELU, G>(a, st);
+    case ACT_SWIGLU: return BF ? launch_bf16_t<ACT_SWIGLU, G, bf16_t>(a, st) : launch_f32_t<ACT_SWIGLU, G>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -8,6 +8,8 @@
 namespace moe {
 
 // ---- router
+constexpr int kSelTokens = 64;  // tokens per selection / histogram / scatter block
+
 struct RouteArgs {
   const void* x;          // [T,h] fp32 or bf16
   const float* W_gate;    // [h,E]
@@ -19,17 +21,18 @@ struct RouteArgs {
   int* topk_idx;          // [T,k]
   float* topk_w;          // [T,k]
   float* prob_part;       // [route_blocks(T), E] or null
+  int* blk_counts;        // [route_blocks(T), E] or null: per-block expert histogram
+  uint16_t* planes;       // bf16 x: [3][E16][h] bf16 scratch for the split router weights
 };
-int expert_pad(int E);
+int route_planes_elems(int h, int E);
 int route_blocks(int T);
-hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_logits(const RouteArgs& a, hipStream_t st);  // logits only (ignores logits_in)
+hipError_t launch_select(const RouteArgs& a, hipStream_t st);  // softmax, top-k, weights, histogram
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);   // both (logits skipped when logits_in)
 hipError_t launch_reduce_prob(const float* prob_part, int nblk, int E, float* prob_sum, hipStream_t st);
 
-// ---- permutation
-constexpr int kPermBlock = 2048;  // assignments per histogram / scatter block
-inline int perm_blocks(int64_t n) { return (int)((n + kPermBlock - 1) / kPermBlock); }
-
-hipError_t launch_hist(const int* topk_idx, int n, int E, int* blk_counts, hipStream_t st);
+// ---- permutation (blocks of kSelTokens tokens = kSelTokens*k assignments)
+hipError_t launch_hist(const int* topk_idx, int T, int k, int E, int* blk_counts, hipStream_t st);
 
 struct ScanArgs {
   const int* blk_counts;   // [nhb,E]
@@ -47,7 +50,7 @@ struct ScanArgs {
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 
-hipError_t launch_scatter(const int* topk_idx, int n, int E, int k, int C, const int* offsets,
+hipError_t launch_scatter(const int* topk_idx, int T, int E, int k, int C, const int* offsets,
                           const int* blk_base, int* slot_pos, int* sorted_slot, int* perm_token,
                           hipStream_t st);
 hipError_t launch_gather(const void* x, const int* perm_token, const int* offsets, int E, int R_max,
@@ -69,12 +72,14 @@ struct GemmArgs {
   int E;
   int R_max;            // upper bound of rows
   int act;
+  bool out_f32;         // bf16 GEMM writing fp32 output (down projection inside the layer)
 };
 int gemm_bm(bool bf16);  // rows per m-tile of the expert GEMMs
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t st);
 
 // ---- combine
-hipError_t launch_combine(const void* O, const int* slot_pos, const float* topk_w, int T, int h, int k,
-                          bool bf16, void* y, hipStream_t st);
+// O is fp32 when o_f32, else the y dtype
+hipError_t launch_combine(const void* O, bool o_f32, const int* slot_pos, const float* topk_w, int T, int h,
+                          int k, bool bf16, void* y, hipStream_t st);
 
 }  // namespace moe

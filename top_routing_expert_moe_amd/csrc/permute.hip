@@ -10,15 +10,16 @@
 //
 // gfx950 design: no radix sort.  E <= 256 means one 8-bit digit, so a single
 // *stable counting scatter* does the sort:
-//   hist    : each block of 2048 consecutive assignments counts its experts in
-//             LDS (order-free atomics) -> blk_counts[b][e];
-//   scan    : one workgroup turns the counts into pre-drop ranks per block
+//   hist    : each block of 64 tokens (64*k consecutive assignments) counts its
+//             experts in LDS (order-free atomics) -> blk_counts[b][e]; inside the
+//             layer the router's selection kernel does this on the same blocks;
+//   scan    : one workgroup of 1024 turns the counts into pre-drop ranks per block
 //             (blk_base), kept counts, exclusive offsets, the GEMM m-tile
 //             schedule and the aux loss (fixed summation order);
 //   scatter : each block ranks its assignments in order with wave ballots
 //             (a multisplit on the expert-id bits: lanes with the same expert
 //             in lower lanes are counted by popcount), then across its 4 waves
-//             and 8 rounds through LDS.  Rank = blk_base + in-block rank, so
+//             and its rounds of 256 through LDS.  Rank = blk_base + in-block rank, so
 //             the result equals a stable sort for any number of blocks.
 #include <limits.h>
 
@@ -29,19 +30,17 @@ namespace moe {
 
 namespace {
 
-constexpr int PB = kPermBlock;
-constexpr int PR = PB / 256;  // rounds of 256 assignments per block
-
-__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ topk_idx, int n, int E,
+__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ topk_idx, int T, int k, int E,
                                                    int* __restrict__ blk_counts) {
   __shared__ int cnt[256];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * PB;
-#pragma unroll
-  for (int r = 0; r < PR; ++r) {
-    const int64_t s = base + r * 256 + tid;
+  const int64_t n = (int64_t)T * k;
+  const int pb = kSelTokens * k;
+  const int64_t base = (int64_t)blockIdx.x * pb;
+  for (int r = tid; r < pb; r += 256) {
+    const int64_t s = base + r;
     if (s < n) {
       const int e = topk_idx[s];
       if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
@@ -51,27 +50,33 @@ __global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ topk_
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
 }
 
-// Inclusive Hillis-Steele scan over 256 threads (one value each).
-__device__ int block_inclusive_scan(int v, int* sh) {
+// Inclusive Hillis-Steele scan of one value per thread over the first 256 threads of the
+// workgroup (all threads of the workgroup must call it).
+__device__ int block_inclusive_scan256(int v, int* sh) {
   const int tid = threadIdx.x;
-  sh[tid] = v;
+  if (tid < 256) sh[tid] = v;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    int add = tid >= o ? sh[tid - o] : 0;
+    int add = 0;
+    if (tid < 256 && tid >= o) add = sh[tid - o];
     __syncthreads();
-    sh[tid] += add;
+    if (tid < 256) sh[tid] += add;
     __syncthreads();
   }
-  int r = sh[tid];
+  int r = tid < 256 ? sh[tid] : 0;
   __syncthreads();
   return r;
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __shared__ int sh[256];
-  __shared__ double dsh[256];
+  __shared__ int cnt_sh[256];
+  __shared__ double dsh[kScanThreads];
   const int tid = threadIdx.x;
   const int E = a.E;
+  // per-expert running ranks over the blocks (blocks are few: T/64)
   int cnt = 0;
   if (tid < E) {
     for (int b = 0; b < a.nhb; ++b) {
@@ -79,9 +84,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       a.blk_base[(size_t)b * E + tid] = cnt;
       cnt += c;
     }
+    cnt_sh[tid] = cnt;
   }
   const int kept = tid < E ? min(cnt, a.C) : 0;
-  const int incl = block_inclusive_scan(kept, sh);
+  const int incl = block_inclusive_scan256(kept, sh);
   if (tid < E) {
     a.counts[tid] = cnt;
     a.offsets[tid] = incl - kept;
@@ -89,27 +95,41 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
   if (a.BM > 0 && a.tile_off != nullptr) {
     const int mt = tid < E ? (kept + a.BM - 1) / a.BM : 0;
-    const int tin = block_inclusive_scan(mt, sh);
+    const int tin = block_inclusive_scan256(mt, sh);
     if (tid < E) {
       a.tile_off[tid] = tin - mt;
       if (tid == E - 1) a.tile_off[E] = tin;
     }
   }
   if (a.aux != nullptr && (a.prob_part != nullptr || a.prob_sum != nullptr)) {
+    // sum_t p[t,e]: P threads per expert each sum a strided set of blocks, then a fixed-order tree
+    int ep = 1;
+    while (ep < E) ep <<= 1;
+    const int P = kScanThreads / ep;
+    const int e = tid % ep, part = tid / ep;
+    double ps = 0.0;
+    if (e < E) {
+      if (a.prob_part != nullptr) {
+        for (int b = part; b < a.nrb; b += P) ps += (double)a.prob_part[(size_t)b * E + e];
+      } else if (part == 0) {
+        ps = (double)a.prob_sum[e];
+      }
+    }
+    dsh[tid] = ps;
+    __syncthreads();
+    for (int o = P / 2; o >= 1; o >>= 1) {
+      if (part < o) dsh[tid] += dsh[tid + o * ep];
+      __syncthreads();
+    }
     double term = 0.0;
     if (tid < E) {
-      double ps = 0.0;
-      if (a.prob_part != nullptr) {
-        for (int b = 0; b < a.nrb; ++b) ps += (double)a.prob_part[(size_t)b * E + tid];
-      } else {
-        ps = (double)a.prob_sum[tid];
-      }
       const double n = (double)a.T * (double)a.k;
-      term = ((double)cnt / n) * (ps / (double)a.T);
+      term = ((double)cnt_sh[tid] / n) * (dsh[tid] / (double)a.T);
     }
+    __syncthreads();
     dsh[tid] = term;
     __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
+    for (int o = kScanThreads / 2; o >= 1; o >>= 1) {
       if (tid < o) dsh[tid] += dsh[tid + o];
       __syncthreads();
     }
@@ -123,14 +143,14 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int* __restrict__ offs
   const int tid = threadIdx.x;
   const int rows = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
   const int mt = (rows + BM - 1) / BM;
-  const int incl = block_inclusive_scan(mt, sh);
+  const int incl = block_inclusive_scan256(mt, sh);
   if (tid < E) {
     tile_off[tid] = incl - mt;
     if (tid == E - 1) tile_off[E] = incl;
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ topk_idx, int n, int E,
+__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ topk_idx, int T, int E,
                                                       int k, int nbits, int C,
                                                       const int* __restrict__ offsets,
                                                       const int* __restrict__ blk_base,
@@ -142,17 +162,20 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ to
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   run[tid] = 0;
-  const int64_t base = (int64_t)blockIdx.x * PB;
+  const int64_t n = (int64_t)T * k;
+  const int pb = kSelTokens * k;
+  const int64_t base = (int64_t)blockIdx.x * pb;
   const int* bb = blk_base + (size_t)blockIdx.x * E;
-  for (int r = 0; r < PR; ++r) {
+  for (int r0 = 0; r0 < pb; r0 += 256) {
     wcnt[0][tid] = 0;
     wcnt[1][tid] = 0;
     wcnt[2][tid] = 0;
     wcnt[3][tid] = 0;
     __syncthreads();
-    const int64_t s = base + r * 256 + tid;
+    const int64_t s = base + r0 + tid;
+    const bool in = (r0 + tid < pb) && s < n;
     int e = -1;
-    if (s < n) e = topk_idx[s];
+    if (in) e = topk_idx[s];
     const bool valid = (unsigned)e < (unsigned)E;
     uint64_t match = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -175,7 +198,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ to
       } else {
         slot_pos[s] = -1;
       }
-    } else if (s < n) {
+    } else if (in) {
       slot_pos[s] = -1;
     }
     __syncthreads();
@@ -198,13 +221,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
 
 }  // namespace
 
-hipError_t launch_hist(const int* topk_idx, int n, int E, int* blk_counts, hipStream_t st) {
-  hipLaunchKernelGGL(hist_kernel, dim3(perm_blocks(n)), dim3(256), 0, st, topk_idx, n, E, blk_counts);
+hipError_t launch_hist(const int* topk_idx, int T, int k, int E, int* blk_counts, hipStream_t st) {
+  hipLaunchKernelGGL(hist_kernel, dim3(route_blocks(T)), dim3(256), 0, st, topk_idx, T, k, E, blk_counts);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -213,13 +236,13 @@ hipError_t launch_tiles(const int* offsets, int E, int BM, int* tile_off, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const int* topk_idx, int n, int E, int k, int C, const int* offsets,
+hipError_t launch_scatter(const int* topk_idx, int T, int E, int k, int C, const int* offsets,
                           const int* blk_base, int* slot_pos, int* sorted_slot, int* perm_token,
                           hipStream_t st) {
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  hipLaunchKernelGGL(scatter_kernel, dim3(perm_blocks(n)), dim3(256), 0, st, topk_idx, n, E, k, nbits,
-                     C, offsets, blk_base, slot_pos, sorted_slot, perm_token);
+  hipLaunchKernelGGL(scatter_kernel, dim3(route_blocks(T)), dim3(256), 0, st, topk_idx, T, E, k, nbits, C,
+                     offsets, blk_base, slot_pos, sorted_slot, perm_token);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// Router: logits = x . W_gate (+ bias) in fp32, fused softmax statistics,
+// Router: logits = x . W_gate (+ bias) in fp32, then softmax statistics,
 // top-k selection and renormalised gate weights.
 //
 // Method: the router is one bias-free linear map followed by softmax and a
@@ -7,23 +7,26 @@
 // sketch; "MoE Router：谁来决定 Token 去哪个 Expert", MoERouter snippet).  The
 // logits stay in fp32 (Colossal-AI MoE tutorial, SparseMLP data flow step 2).
 //
-// Layout: one workgroup of 256 threads owns TT=32 tokens and all E experts.
-// The h-loop stages a 32-wide slice of x (converted to fp32, stored k-major so
-// that a thread's token values are one broadcast read) and of W_gate in LDS;
-// each thread accumulates a TM x TE register tile.  Then each wave takes 8
-// tokens: lane e holds the logits of experts e, e+64, ...; softmax sums and k
-// rounds of a 64-bit wave arg-max select the experts.  The key orders by
-// logit (IEEE order, -0 == +0) then by lower expert index, so ties are broken
-// deterministically.
+// gfx950 design, two kernels:
+//  * logits.  For bf16 activations the contraction runs on the matrix cores
+//    at fp32 accuracy: W_gate (fp32) is split exactly into three bf16 planes
+//    hi + mid + lo (each the bf16 rounding of what the previous ones left, 24
+//    significant bits in total), a bf16 x times a bf16 plane is exact in fp32,
+//    and v_mfma_f32_16x16x32_bf16 accumulates the three products in fp32.  Each
+//    wave streams 16 token rows straight from HBM into MFMA operands (no LDS);
+//    the planes ([3][E16][h], k-contiguous) are small and stay in L2.  For fp32
+//    activations a plain fp32 FMA kernel is used instead.
+//  * select.  One wave per token: lane e holds the logits of experts e, e+64,
+//    ...; softmax sums and k rounds of a 64-bit wave arg-max pick the experts.
+//    The key orders by logit (IEEE order, -0 == +0) then by the lower expert
+//    index, so ties are deterministic.  The same kernel counts its block's
+//    assignments per expert (the histogram) and sums the softmax per expert.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
-
-constexpr int TT = 32;   // tokens per workgroup
-constexpr int KC = 32;   // h-chunk staged per iteration
 
 __device__ __forceinline__ uint32_t ordered_bits(float l) {
   l = l + 0.0f;  // -0.0 -> +0.0
@@ -36,94 +39,184 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
   return __uint_as_float(u);
 }
 
-template <typename XT, int EP, bool LOGITS_IN>
-__global__ __launch_bounds__(256) void route_kernel(
-    const XT* __restrict__ x, const float* __restrict__ W_gate, const float* __restrict__ bias,
-    int T, int h, int E, int k, float* __restrict__ logits, int* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ prob_part) {
-  constexpr int TE = EP > 64 ? EP / 64 : 1;   // experts per thread
-  constexpr int NEG = EP / TE;                // expert groups (<= 64)
-  constexpr int TM = TT * NEG / 256;          // tokens per thread
-  constexpr int NV = EP >= 64 ? EP / 64 : 1;  // logits per lane in the selection phase
-  static_assert(TM >= 1 && TM * (256 / NEG) == TT, "tile");
+__device__ __forceinline__ float bf16_round(float v) { return __uint_as_float(f32_to_bf16_bits(v) << 16); }
 
+// ---------------------------------------------------------------------------
+// W_gate [h,E] fp32 -> planes [3][E16][h] bf16 with hi + mid + lo == W (to fp32 precision)
+__global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W_gate, int h, int E, int E16,
+                                                     bf16_t* __restrict__ planes) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)E16 * h) return;
+  const int e = (int)(idx / h), i = (int)(idx % h);
+  const float w = e < E ? W_gate[(size_t)i * E + e] : 0.f;
+  const float hi = bf16_round(w);
+  const float r1 = w - hi;  // exact
+  const float mid = bf16_round(r1);
+  const float lo = bf16_round(r1 - mid);
+  const size_t plane = (size_t)E16 * h;
+  planes[idx] = (bf16_t)(__float_as_uint(hi) >> 16);
+  planes[plane + idx] = (bf16_t)(__float_as_uint(mid) >> 16);
+  planes[2 * plane + idx] = (bf16_t)(__float_as_uint(lo) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// logits for bf16 x on MFMA.  Workgroup = 4 waves = TW token-waves x KS k-splits;
+// each wave: 16 tokens x NB*16 experts over h/KS.
+template <int NB, int TW>
+__global__ __launch_bounds__(256) void logits_mfma_kernel(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ planes,
+                                                          const float* __restrict__ bias, int T, int h, int E,
+                                                          int E16, float* __restrict__ logits) {
+  constexpr int KS = 4 / TW;
+  constexpr int U = NB >= 4 ? 2 : (NB == 2 ? 4 : 8);  // k-steps of 32 per batch of loads
+  __shared__ floatx4 red[KS > 1 ? KS - 1 : 1][TW][NB][64];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tw = wave % TW, ks = wave / TW;
+  const int t0 = blockIdx.x * (16 * TW) + tw * 16;
+  const int e0 = blockIdx.y * (16 * NB);
+  const int kspan = h / KS;
+  const int kb = ks * kspan, ke = kb + kspan;
+
+  const int tok = t0 + (lane & 15);
+  const bool tvalid = tok < T;
+  const bf16_t* xrow = x + (size_t)(tvalid ? tok : 0) * h + 8 * (lane >> 4);
+  const size_t plane = (size_t)E16 * h;
+  const bf16_t* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wrow[nb] = planes + (size_t)(e0 + nb * 16 + (lane & 15)) * h + 8 * (lane >> 4);
+
+  floatx4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = kb; k0 < ke; k0 += 32 * U) {
+    const int steps = min(U, (ke - k0) / 32);
+    bf16x8 xb[U], wa[U][NB][3];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < steps) {
+        const int kk = k0 + 32 * u;
+        xb[u] = tvalid ? *(const bf16x8*)(xrow + kk) : bf16x8{};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int p = 0; p < 3; ++p) wa[u][nb][p] = *(const bf16x8*)(wrow[nb] + p * plane + kk);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < steps) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[u][nb][p], xb[u], acc[nb], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds token (lane & 15), experts 4*(lane>>4) + 0..3 of each 16-block
+  if (KS > 1) {
+    if (ks > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[ks - 1][tw][nb][lane] = acc[nb];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < KS - 1; ++s) acc[nb] += red[s][tw][nb][lane];
+  }
+  if (!tvalid) return;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + nb * 16 + 4 * (lane >> 4) + r;
+      if (e < E) logits[(size_t)tok * E + e] = acc[nb][r] + (bias ? bias[e] : 0.f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// logits for fp32 x on the vector ALUs: 32 tokens x all experts per workgroup.
+template <int EP>
+__global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict__ x,
+                                                         const float* __restrict__ W_gate,
+                                                         const float* __restrict__ bias, int T, int h, int E,
+                                                         float* __restrict__ logits) {
+  constexpr int TT = 32, KC = 32;
+  constexpr int TE = EP > 64 ? EP / 64 : 1;
+  constexpr int NEG = EP / TE;
+  constexpr int TM = TT * NEG / 256;
   __shared__ float xs[KC][TT];
   __shared__ float ws[KC][EP];
-  __shared__ float lg[TT][EP + 1];
-  __shared__ float pp[4][EP];
-
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * TT;
-
-  if (!LOGITS_IN) {
-    const int eg = tid % NEG, tg = tid / NEG;
-    float acc[TM][TE];
+  const int eg = tid % NEG, tg = tid / NEG;
+  float acc[TM][TE];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TE; ++j) acc[i][j] = 0.f;
-
-    for (int k0 = 0; k0 < h; k0 += KC) {
-      {  // x slice: 32 tokens x 32 h, 4 consecutive h per thread
-        const int tt = tid >> 3, kk = (tid & 7) * 4;
-        const int t = t0 + tt;
+    for (int j = 0; j < TE; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < h; k0 += KC) {
+    {
+      const int tt = tid >> 3, kk = (tid & 7) * 4;
+      const int t = t0 + tt;
+      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (t < T) v = *(const floatx4*)(x + (size_t)t * h + k0 + kk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = 0.f;
-          if (t < T) v = Elem<XT>::load(x, (size_t)t * h + k0 + kk + i);
-          xs[kk + i][tt] = v;
-        }
-      }
-      for (int idx = tid; idx < KC * EP; idx += 256) {
-        const int kk = idx / EP, e = idx % EP;
-        ws[kk][e] = e < E ? W_gate[(size_t)(k0 + kk) * E + e] : 0.f;
-      }
-      __syncthreads();
-#pragma unroll 4
-      for (int kk = 0; kk < KC; ++kk) {
-        float xv[TM], wv[TE];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) xv[i] = xs[kk][tg * TM + i];
-#pragma unroll
-        for (int j = 0; j < TE; ++j) wv[j] = ws[kk][eg * TE + j];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TE; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
-      }
-      __syncthreads();
+      for (int i = 0; i < 4; ++i) xs[kk + i][tt] = v[i];
     }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TE; ++j) {
-        const int e = eg * TE + j;
-        float v = acc[i][j];
-        if (bias != nullptr && e < E) v += bias[e];
-        lg[tg * TM + i][e] = v;
-      }
+    for (int idx = tid; idx < KC * EP; idx += 256) {
+      const int kk = idx / EP, e = idx % EP;
+      ws[kk][e] = e < E ? W_gate[(size_t)(k0 + kk) * E + e] : 0.f;
+    }
     __syncthreads();
-    for (int idx = tid; idx < TT * E; idx += 256) {
-      const int tt = idx / E, e = idx % E;
-      if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = lg[tt][e];
-    }
-  } else {
-    for (int idx = tid; idx < TT * E; idx += 256) {
-      const int tt = idx / E, e = idx % E;
-      lg[tt][e] = (t0 + tt < T) ? logits[(size_t)(t0 + tt) * E + e] : 0.f;
+#pragma unroll 4
+    for (int kk = 0; kk < KC; ++kk) {
+      float xv[TM], wv[TE];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) xv[i] = xs[kk][tg * TM + i];
+#pragma unroll
+      for (int j = 0; j < TE; ++j) wv[j] = ws[kk][eg * TE + j];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TE; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
     }
     __syncthreads();
   }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int t = t0 + tg * TM + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int e = eg * TE + j;
+      if (e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+    }
+  }
+}
 
-  // ---- selection: wave w handles tokens w*8 .. w*8+7
-  const int lane = tid & 63, w = tid >> 6;
+// ---------------------------------------------------------------------------
+// selection: 64 tokens per workgroup, 16 per wave.
+template <int NV>
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                     int* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                     float* __restrict__ prob_part, int* __restrict__ blk_counts) {
+  __shared__ float pp[4][64 * NV];
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t0 = blockIdx.x * kSelTokens;
+  cnt[tid] = 0;
+  __syncthreads();
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.f;
 
-  for (int q = 0; q < TT / 4; ++q) {
-    const int tt = w * (TT / 4) + q;
-    const int t = t0 + tt;
+  for (int q = 0; q < kSelTokens / 4; ++q) {
+    const int t = t0 + w * (kSelTokens / 4) + q;
     if (t >= T) break;
     float v[NV];
     bool valid[NV];
@@ -132,7 +225,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
       valid[i] = e < E;
-      v[i] = valid[i] ? lg[tt][e] : -INFINITY;
+      v[i] = valid[i] ? logits[(size_t)t * E + e] : -INFINITY;
       m = fmaxf(m, v[i]);
     }
     m = wave_max(m);
@@ -150,8 +243,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     bool taken[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) taken[i] = false;
-    float lmax = 0.f, wsum = 0.f;
-    float my_l = 0.f;
+    float lmax = 0.f, wsum = 0.f, my_l = 0.f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
@@ -159,7 +251,7 @@ __global__ __launch_bounds__(256) void route_kernel(
       for (int i = 0; i < NV; ++i) {
         const int e = lane + 64 * i;
         if (valid[i] && !taken[i]) {
-          uint64_t key = ((uint64_t)ordered_bits(v[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+          const uint64_t key = ((uint64_t)ordered_bits(v[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
           best = key > best ? key : best;
         }
       }
@@ -176,20 +268,21 @@ __global__ __launch_bounds__(256) void route_kernel(
     if (lane < k) {
       topk_idx[(size_t)t * k + lane] = my_e;
       topk_w[(size_t)t * k + lane] = expf(my_l - lmax) / wsum;
+      if (blk_counts != nullptr) atomicAdd(&cnt[my_e], 1);
     }
   }
   if (prob_part != nullptr) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + 64 * i;
-      if (e < EP) pp[w][e] = psum[i];
-    }
-    __syncthreads();
+    for (int i = 0; i < NV; ++i) pp[w][lane + 64 * i] = psum[i];
+  }
+  __syncthreads();
+  if (prob_part != nullptr)
     for (int e = tid; e < E; e += 256)
       prob_part[(size_t)blockIdx.x * E + e] = ((pp[0][e] + pp[1][e]) + pp[2][e]) + pp[3][e];
-  }
+  if (blk_counts != nullptr && tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
 }
 
+// prob_sum[e] = sum over blocks of prob_part[b][e], in block order
 __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk, int E,
                                    float* __restrict__ prob_sum) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -199,49 +292,89 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
   prob_sum[e] = s;
 }
 
-template <typename XT, bool LIN>
-hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
-  const int nblk = route_blocks(a.T);
-  dim3 grid(nblk), block(256);
-  const void* xp = a.x;
-#define MOE_ROUTE_CASE(EPV)                                                                        \
-  case EPV:                                                                                        \
-    hipLaunchKernelGGL((route_kernel<XT, EPV, LIN>), grid, block, 0, st, (const XT*)xp, a.W_gate,  \
-                       a.bias, a.T, a.h, a.E, a.k, a.logits, a.topk_idx, a.topk_w, a.prob_part);   \
-    break;
-  switch (expert_pad(a.E)) {
-    MOE_ROUTE_CASE(8)
-    MOE_ROUTE_CASE(16)
-    MOE_ROUTE_CASE(32)
-    MOE_ROUTE_CASE(64)
-    MOE_ROUTE_CASE(128)
-    MOE_ROUTE_CASE(256)
-    default: return hipErrorInvalidValue;
-  }
-#undef MOE_ROUTE_CASE
-  return hipGetLastError();
+template <int NB, int TW>
+void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st) {
+  const dim3 grid((a.T + 16 * TW - 1) / (16 * TW), E16 / (16 * NB));
+  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW>), grid, dim3(256), 0, st, (const bf16_t*)a.x,
+                     (const bf16_t*)a.planes, a.bias,
+                     a.T, a.h, a.E, E16, a.logits);
 }
 
 }  // namespace
 
-int expert_pad(int E) {
-  int p = 8;
-  while (p < E) p <<= 1;
-  return p;
+int route_planes_elems(int h, int E) { return 3 * ((E + 15) / 16 * 16) * h; }
+
+int route_blocks(int T) { return (T + kSelTokens - 1) / kSelTokens; }
+
+hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
+  {
+    if (a.bf16) {
+      const int E16 = (a.E + 15) / 16 * 16;
+      const int64_t n = (int64_t)E16 * a.h;
+      hipLaunchKernelGGL(wsplit_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.W_gate, a.h, a.E,
+                         E16, (bf16_t*)a.planes);
+      // k split across waves needs h/KS to be a multiple of 32
+      if (E16 <= 16) {
+        if (a.h % 128 == 0) launch_logits_mfma<1, 1>(a, E16, st);
+        else launch_logits_mfma<1, 2>(a, E16, st);
+      } else if (E16 == 32) {
+        if (a.h % 128 == 0) launch_logits_mfma<2, 1>(a, E16, st);
+        else launch_logits_mfma<2, 2>(a, E16, st);
+      } else if (E16 % 64 == 0) {
+        launch_logits_mfma<4, 4>(a, E16, st);
+      } else if (E16 % 32 == 0) {
+        launch_logits_mfma<2, 4>(a, E16, st);
+      } else {
+        launch_logits_mfma<1, 4>(a, E16, st);
+      }
+    } else {
+      const dim3 grid((a.T + 31) / 32);
+      int p = 8;
+      while (p < a.E) p <<= 1;
+#define MOE_LOGITS_F32(EPV)                                                                                   \
+  case EPV:                                                                                                   \
+    hipLaunchKernelGGL(logits_f32_kernel<EPV>, grid, dim3(256), 0, st, (const float*)a.x, a.W_gate, a.bias, a.T, \
+                       a.h, a.E, a.logits);                                                                   \
+    break;
+      switch (p) {
+        MOE_LOGITS_F32(8)
+        MOE_LOGITS_F32(16)
+        MOE_LOGITS_F32(32)
+        MOE_LOGITS_F32(64)
+        MOE_LOGITS_F32(128)
+        MOE_LOGITS_F32(256)
+        default: return hipErrorInvalidValue;
+      }
+#undef MOE_LOGITS_F32
+    }
+  }
+  return hipGetLastError();
 }
 
-int route_blocks(int T) { return (T + TT - 1) / TT; }
+hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
+  const dim3 grid(route_blocks(a.T));
+  if (a.E <= 64)
+    hipLaunchKernelGGL(select_kernel<1>, grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w,
+                       a.prob_part, a.blk_counts);
+  else if (a.E <= 128)
+    hipLaunchKernelGGL(select_kernel<2>, grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w,
+                       a.prob_part, a.blk_counts);
+  else
+    hipLaunchKernelGGL(select_kernel<4>, grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w,
+                       a.prob_part, a.blk_counts);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
-  if (a.logits_in) {
-    return a.bf16 ? launch_route_t<bf16_t, true>(a, st) : launch_route_t<float, true>(a, st);
+  if (!a.logits_in) {
+    const hipError_t e = launch_logits(a, st);
+    if (e != hipSuccess) return e;
   }
-  return a.bf16 ? launch_route_t<bf16_t, false>(a, st) : launch_route_t<float, false>(a, st);
+  return launch_select(a, st);
 }
 
 hipError_t launch_reduce_prob(const float* prob_part, int nblk, int E, float* prob_sum, hipStream_t st) {
-  hipLaunchKernelGGL(reduce_prob_kernel, dim3((E + 255) / 256), dim3(256), 0, st, prob_part, nblk, E,
-                     prob_sum);
+  hipLaunchKernelGGL(reduce_prob_kernel, dim3((E + 255) / 256), dim3(256), 0, st, prob_part, nblk, E, prob_sum);
   return hipGetLastError();
 }
 
