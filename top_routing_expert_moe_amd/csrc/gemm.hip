@@ -24,8 +24,11 @@
 //  * the up projection reads its left operand straight from x through the
 //    row -> token map (the gather is fused into the A-load);
 //  * XCD-aware order: hardware workgroup i runs on XCD i%8; each XCD takes a
-//    contiguous range of the tile list, with m-tiles fastest, so the m-tiles of
-//    one expert that share a weight tile run together in one L2.
+//    contiguous range of the tile list, which is ordered in 4 x 8 groups of
+//    (m-tile, n-tile) inside each expert, so the workgroups running together in
+//    one XCD share activation and weight tiles in its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,16 +36,68 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256;
 
 __device__ __forceinline__ void store4(bf16_t* p, const float* v) {
   *(u32x2*)p = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 __device__ __forceinline__ void store4(float* p, const float* v) { *(floatx4*)p = floatx4{v[0], v[1], v[2], v[3]}; }
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-// element offset of (row, 16-byte chunk) in a [256][64] bf16 LDS tile
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 3); }
+
+// Tile order.  Tiles are listed expert by expert; inside an expert (me m-tiles x NT
+// n-tiles) they come in groups of GM m-tiles x GN n-tiles, m fastest inside a group,
+// then the next n-group, then the next m-group.  Consecutive tiles -- which run at the
+// same time on one XCD -- therefore share both their activation rows (across the GN
+// n-tiles) and their weight columns (across the GM m-tiles) in that XCD's L2.
+constexpr int GM = 4, GN = 8;
+
+__device__ __forceinline__ void tile_of(int L, const int* __restrict__ tile_off, int E, int NT, int& e,
+                                        int& mt_local, int& nt) {
+  // expert: tile_off[e]*NT <= L < tile_off[e+1]*NT
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_off[mid] * NT <= L) lo = mid; else hi = mid;
+  }
+  e = lo;
+  const int me = tile_off[e + 1] - tile_off[e];
+  const int l = L - tile_off[e] * NT;
+  const int mg = l / (GM * NT);
+  const int gm = min(GM, me - mg * GM);
+  const int r = l - mg * GM * NT;
+  const int ng = r / (gm * GN);
+  const int r2 = r - ng * gm * GN;
+  mt_local = mg * GM + r2 % gm;
+  nt = ng * GN + r2 / gm;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int KB = 32;      // k per LDS stage (one v_mfma_f32_16x16x32_bf16 step)
+constexpr int NSTAGE = 4;   // LDS stages: copies run NSTAGE-1 steps ahead
+constexpr int WST = KB * BN;  // weight stage, elements: [32 k][256 n], n contiguous
+constexpr int XST = BM * KB;  // activation stage, elements: [256 m][32 k], k contiguous
+
+// Swizzles (16-byte chunk index XOR a function of the row):
+//  * weight stage rows are 256 n = 32 chunks; a transposing read touches rows
+//    8g + 4h + t (g, t = 0..3) at one chunk pair, so f spreads t and g over 16
+//    distinct even values;
+//  * activation stage rows are 32 k = 4 chunks; 16 consecutive rows are read at one
+//    chunk, so f spreads (row >> 2) over the 4 chunks.
+// One 16-byte-per-lane copy from global memory straight into LDS (the wave's 1 KiB
+// block starts at the LDS byte address in m0).  Issued as a plain instruction so that
+// the compiler does not serialise later LDS reads behind it: the pipeline below waits
+// for these copies itself (s_waitcnt vmcnt + barrier) before any wave reads the stage.
+// It has no destination registers, so nothing is left in flight in a register.
+__device__ __forceinline__ void copy_to_lds16(const void* gptr, uint32_t lds_block) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_block) : "memory", "m0");
+}
+
+__device__ __forceinline__ int wswz(int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) << 1; }
+__device__ __forceinline__ int xswz(int r) { return (r >> 2) & 3; }
 
 template <int ACT, bool GATHER, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
@@ -50,8 +105,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out,
     const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, int NT) {
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
-  __shared__ __attribute__((aligned(16))) bf16_t Wl[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t Xl[2][BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t Ws[NSTAGE][WST];
+  __shared__ __attribute__((aligned(1024))) bf16_t Xs[NSTAGE][XST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -63,153 +118,144 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (slot >= per) return;
   const int L = xcd * per + slot;
   if (L >= n_real) return;
-  const int mt = L % MT, nt = L / MT;
-  const int e = find_expert(tile_off, E, mt);
-  const int row0 = offsets[e] + (mt - tile_off[e]) * BM;
+  int e, mt_local, nt;
+  tile_of(L, tile_off, E, NT, e, mt_local, nt);
+  const int row0 = offsets[e] + mt_local * BM;
   const int row_end = min(row0 + BM, offsets[e + 1]);
   const int n0 = nt * NO;
 
-  // ---- weight-tile loader: thread -> (8 LDS rows of group g, 8 k rows of group kg)
-  const int g = tid & 31, kg = tid >> 5;
-  const bf16_t* wsrc;
-  bool wvalid;
-  {
+  // ---- copy plan.  One wave instruction moves 1 KiB: lane l writes LDS bytes
+  // [16l, 16l+16) of the instruction's block, i.e. swizzle slot (l & 31) of weight
+  // row (l >> 5) or slot (l & 3) of activation row (l >> 2); it fetches the global
+  // chunk that the swizzle puts there.  Columns past N / rows past the segment fetch
+  // a valid neighbour instead (their results are never stored).
+  const bf16_t* wsrc[4];
+  uint32_t xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 2 * (4 * wave + i) + (lane >> 5);   // weight stage row (k)
+    const int c = (lane & 31) ^ wswz(r);              // 16-byte chunk of 8 columns
     int col;
     const bf16_t* Wm;
-    if (ACT == ACT_SWIGLU) {
-      const int wn = g >> 4, gg = g & 15;
-      col = n0 + wn * 64 + (gg & 7) * 8;
-      Wm = gg < 8 ? W : W3;
+    if (ACT == ACT_SWIGLU) {  // chunks 0-7 / 8-15: W1 / W3 of wave-half 0; 16-31: wave-half 1
+      const int wn = c >> 4, cc = c & 15;
+      col = n0 + wn * 64 + (cc & 7) * 8;
+      Wm = cc < 8 ? W : W3;
     } else {
-      col = n0 + g * 8;
+      col = n0 + c * 8;
       Wm = W;
     }
-    wvalid = col < N;
-    wsrc = Wm + (size_t)e * K * N + (size_t)(kg * 8) * N + (wvalid ? col : 0);
+    wsrc[i] = Wm + (size_t)e * K * N + (size_t)r * N + min(col, N - 8);
+    const int xr = 16 * (4 * wave + i) + (lane >> 2);  // activation stage row (m)
+    const int rr = min(row0 + xr, row_end - 1);
+    const int src_row = GATHER ? a_rows[rr] : rr;
+    xsrc[i] = (uint32_t)src_row * (uint32_t)K + (uint32_t)((((lane & 3) ^ xswz(xr))) << 3);
   }
-  // ---- activation-tile loader: thread -> chunk ch of rows (tid>>3) + 32*i
-  const int ch = tid & 7;
-  const bf16_t* xsrc[8];
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t ws_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Ws[0][0];
+  const uint32_t xs_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Xs[0][0];
+  auto issue = [&](int kt, int st) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = row0 + (tid >> 3) + 32 * i;
-    if (r < row_end) {
-      const int src_row = GATHER ? a_rows[r] : r;
-      xsrc[i] = A + (size_t)src_row * K + ch * 8;
-    } else {
-      xsrc[i] = nullptr;
-    }
-  }
-
-  u32x4 wreg[8], xreg[8];
-  auto load_tile = [&](int kt) {
-    const size_t koff = (size_t)kt * BK * N;
+    for (int i = 0; i < 4; ++i)
+      copy_to_lds16(wsrc[i] + (size_t)kt * KB * N,
+                    ws_lds + 2u * (uint32_t)(st * WST + (8 * uwave + 2 * i) * BN));
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (wvalid) wreg[r] = *(const u32x4*)(wsrc + koff + (size_t)r * N);
-      else wreg[r] = u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (xsrc[i] != nullptr) xreg[i] = *(const u32x4*)(xsrc[i] + kt * BK);
-      else xreg[i] = u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    // transpose the 8x8 weight block: column c gets k-pairs (2d, 2d+1), d = 0..3
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      u32x4 v;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = wreg[2 * d][c >> 1], hi = wreg[2 * d + 1][c >> 1];
-        v[d] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-      }
-      const int row = g * 8 + c;
-      *(u32x4*)&Wl[buf][lds_off(row, kg)] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      *(u32x4*)&Xl[buf][lds_off(row, ch)] = xreg[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      copy_to_lds16(A + xsrc[i] + kt * KB, xs_lds + 2u * (uint32_t)(st * XST + (64 * uwave + 16 * i) * KB));
   };
 
-  floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
+  // ---- fragment addressing.  Wave (wn, wm) owns weight columns wn*128 + [0,128) and
+  // activation rows wm*128 + [0,128) of the tile: 8 x 8 blocks of 16 x 16.
+  // Weights (MFMA rows): two transposing 8-byte reads per block; in lane group
+  // g = lane >> 4, lane s = lane & 15 points at row 8g + 4h + (s >> 2), columns
+  // 16*ib + 4*(s & 3) .. +3, and receives k = 8g + 4h + 0..3 of column 16*ib + s.
+  // Activations (MFMA columns): one 16-byte read, row 16*jb + (lane & 15), k-chunk g.
   const int wn = wave & 1, wm = wave >> 1;
-  const int nk = K / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
+  const int g = lane >> 4, s = lane & 15;
+  int aoff[2][8];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int chunk = 2 * ks + (lane >> 5);
-      bf16x8 a[4], b[4];
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * g + 4 * h + (s >> 2);
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int row = wn * 128 + ib * 32 + (lane & 31);
-        a[ib] = *(const bf16x8*)&Wl[cur][lds_off(row, chunk)];
-      }
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const int row = wm * 128 + jb * 32 + (lane & 31);
-        b[jb] = *(const bf16x8*)&Xl[cur][lds_off(row, chunk)];
-      }
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-          acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
+    for (int ib = 0; ib < 8; ++ib) {
+      const int col = wn * 128 + ib * 16 + 4 * (s & 3);
+      aoff[h][ib] = r * BN + ((((col >> 3) ^ wswz(r))) << 3) + (col & 7);
     }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
+  }
+  const int xrow = wm * 128 + s;
+  const int boff = xrow * KB + ((g ^ xswz(xrow)) << 3);  // + jb * 16 * KB
+
+  floatx4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st) {
+    const bf16_t* Wb = Ws[st];
+    const bf16_t* Xb = Xs[st];
+    bf16x8 b[8];
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) b[jb] = *(const bf16x8*)&Xb[boff + jb * 16 * KB];
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[0][ib]]);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[1][ib]]);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb)
+        acc[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[jb], acc[ib][jb], 0, 0, 0);
+    }
+  };
+
+  // ---- pipeline: stage kt lives in LDS buffer kt % NSTAGE; copies for stage
+  // kt + NSTAGE - 1 are issued right after the barrier that ends all reads of the
+  // buffer they overwrite.  Each thread waits for its own copies of stage kt (newer
+  // stages may stay in flight), then the barrier makes every thread's copies visible.
+  const int nk = K / KB;
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p)
+    if (p < nk) issue(p, p);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(nk - 1 - kt, NSTAGE - 2);  // stages newer than kt already issued
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
+    compute(kt % NSTAGE);
   }
 
-  // ---- epilogue: lane holds token row (lane&31) of block jb and, for acc
-  // element 4q+p, weight column 8q + 4*(lane>>5) + p of block ib.
-  const int half = lane >> 5;
+  // ---- epilogue: lane holds token row 16*jb + (lane & 15) and, for acc element p,
+  // weight column 16*ib + 4*g + p of its wave's columns.
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int r = row0 + wm * 128 + jb * 32 + (lane & 31);
+  for (int jb = 0; jb < 8; ++jb) {
+    const int r = row0 + wm * 128 + jb * 16 + s;
     if (r >= row_end) continue;
     OT* orow = out + (size_t)r * N;
     if (ACT == ACT_SWIGLU) {
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
+      for (int ib = 0; ib < 4; ++ib) {
+        const int col = n0 + wn * 64 + ib * 16 + 4 * g;
+        if (col >= N) continue;
+        float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 64 + ib * 32 + 8 * q + 4 * half;
-          if (col >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) v[p] = silu(acc[ib][jb][4 * q + p]) * acc[ib + 2][jb][4 * q + p];
-          store4(orow + col, v);
-        }
+        for (int p = 0; p < 4; ++p) v[p] = silu(acc[ib][jb][p]) * acc[ib + 4][jb][p];
+        store4(orow + col, v);
+      }
     } else {
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
+      for (int ib = 0; ib < 8; ++ib) {
+        const int col = n0 + wn * 128 + ib * 16 + 4 * g;
+        if (col >= N) continue;
+        float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 128 + ib * 32 + 8 * q + 4 * half;
-          if (col >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const float z = acc[ib][jb][4 * q + p];
-            v[p] = ACT == ACT_GELU ? gelu_erf(z) : z;
-          }
-          store4(orow + col, v);
+        for (int p = 0; p < 4; ++p) {
+          const float z = acc[ib][jb][p];
+          v[p] = ACT == ACT_GELU ? gelu_erf(z) : z;
         }
+        store4(orow + col, v);
+      }
     }
   }
 }
