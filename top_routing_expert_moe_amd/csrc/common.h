@@ -69,6 +69,11 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU for the bf16 GEMM epilogue: hardware exp2 and reciprocal (relative error ~1e-6,
+// far below the bf16 rounding that follows).
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
 // Binary search: the expert e with tile_off[e] <= mt < tile_off[e+1] (E >= 1).

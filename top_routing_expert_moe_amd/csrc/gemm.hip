@@ -76,10 +76,19 @@ typedef __attribute__((address_space(1))) void glob_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-constexpr int KB = 32;      // k per LDS stage (one v_mfma_f32_16x16x32_bf16 step)
-constexpr int NSTAGE = 4;   // LDS stages: copies run NSTAGE-1 steps ahead
-constexpr int WST = KB * BN;  // weight stage, elements: [32 k][256 n], n contiguous
-constexpr int XST = BM * KB;  // activation stage, elements: [256 m][32 k], k contiguous
+#ifndef MOE_GEMM_KB
+#define MOE_GEMM_KB 64
+#endif
+#ifndef MOE_GEMM_NSTAGE
+#define MOE_GEMM_NSTAGE 2
+#endif
+constexpr int KB = MOE_GEMM_KB;         // k per LDS stage (KB/16 MFMA k-steps)
+constexpr int NSTAGE = MOE_GEMM_NSTAGE; // LDS stages: copies run NSTAGE-1 stages ahead
+constexpr int WST = KB * BN;  // weight stage, elements: [KB k][256 n], n contiguous
+constexpr int XST = BM * KB;  // activation stage, elements: [256 m][KB k], k contiguous
+constexpr int XCH = KB / 8;   // 16-byte chunks per activation row
+constexpr int CPS = KB / 4;   // copies per thread per stage (KB/8 weight + KB/8 activation)
+static_assert(NSTAGE * (WST + XST) * 2 <= 160 * 1024, "LDS");
 
 // Swizzles (16-byte chunk index XOR a function of the row):
 //  * weight stage rows are 256 n = 32 chunks; a transposing read touches rows
@@ -129,11 +138,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // row (l >> 5) or slot (l & 3) of activation row (l >> 2); it fetches the global
   // chunk that the swizzle puts there.  Columns past N / rows past the segment fetch
   // a valid neighbour instead (their results are never stored).
-  const bf16_t* wsrc[4];
-  uint32_t xsrc[4];
+  constexpr int NI = KB / 8;  // copy instructions per wave per operand and stage
+  const bf16_t* wsrc[NI];
+  uint32_t xsrc[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 2 * (4 * wave + i) + (lane >> 5);   // weight stage row (k)
+  for (int i = 0; i < NI; ++i) {
+    const int r = 2 * (NI * wave + i) + (lane >> 5);  // weight stage row (k)
     const int c = (lane & 31) ^ wswz(r);              // 16-byte chunk of 8 columns
     int col;
     const bf16_t* Wm;
@@ -146,65 +156,100 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       Wm = W;
     }
     wsrc[i] = Wm + (size_t)e * K * N + (size_t)r * N + min(col, N - 8);
-    const int xr = 16 * (4 * wave + i) + (lane >> 2);  // activation stage row (m)
+    const int xr = (1024 / (2 * KB)) * (NI * wave + i) + lane / XCH;  // activation stage row (m)
     const int rr = min(row0 + xr, row_end - 1);
     const int src_row = GATHER ? a_rows[rr] : rr;
-    xsrc[i] = (uint32_t)src_row * (uint32_t)K + (uint32_t)((((lane & 3) ^ xswz(xr))) << 3);
+    xsrc[i] = (uint32_t)src_row * (uint32_t)K + (uint32_t)((((lane % XCH) ^ xswz(xr))) << 3);
   }
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ws_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Ws[0][0];
   const uint32_t xs_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Xs[0][0];
   auto issue = [&](int kt, int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
       copy_to_lds16(wsrc[i] + (size_t)kt * KB * N,
-                    ws_lds + 2u * (uint32_t)(st * WST + (8 * uwave + 2 * i) * BN));
+                    ws_lds + 2u * (uint32_t)(st * WST + (2 * (NI * uwave + i)) * BN));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      copy_to_lds16(A + xsrc[i] + kt * KB, xs_lds + 2u * (uint32_t)(st * XST + (64 * uwave + 16 * i) * KB));
+    for (int i = 0; i < NI; ++i)
+      copy_to_lds16(A + xsrc[i] + kt * KB,
+                    xs_lds + 2u * (uint32_t)(st * XST + (1024 / (2 * KB)) * (NI * uwave + i) * KB));
   };
 
-  // ---- fragment addressing.  Wave (wn, wm) owns weight columns wn*128 + [0,128) and
-  // activation rows wm*128 + [0,128) of the tile: 8 x 8 blocks of 16 x 16.
-  // Weights (MFMA rows): two transposing 8-byte reads per block; in lane group
-  // g = lane >> 4, lane s = lane & 15 points at row 8g + 4h + (s >> 2), columns
-  // 16*ib + 4*(s & 3) .. +3, and receives k = 8g + 4h + 0..3 of column 16*ib + s.
-  // Activations (MFMA columns): one 16-byte read, row 16*jb + (lane & 15), k-chunk g.
+  // ---- fragment addressing (v_mfma_f32_32x32x16_bf16).  Wave (wn, wm) owns weight
+  // columns wn*128 + [0,128) and activation rows wm*128 + [0,128): 4 x 4 blocks of
+  // 32 x 32, two 16-k halves (kh) per 32-k step.
+  // Weights (MFMA rows): two transposing 8-byte reads per block and half; in lane group
+  // g = lane >> 4, lane s = lane & 15 points at row 16*kh + 8*(g >> 1) + 4*h + (s >> 2),
+  // columns 32*ib + 16*(g & 1) + 4*(s & 3) .. +3, and receives k = 16*kh + 8*(g >> 1) +
+  // 4*h + 0..3 of column 32*ib + (lane & 31): the MFMA row layout.
+  // Activations (MFMA columns): one 16-byte read, row 32*jb + (lane & 31), k-chunk
+  // 2*kh + (lane >> 5).
   const int wn = wave & 1, wm = wave >> 1;
-  const int g = lane >> 4, s = lane & 15;
-  int aoff[2][8];
+  const int g = lane >> 4, s = lane & 15, l31 = lane & 31, hf = lane >> 5;
+  int aoff[KB / 16][2][4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 8 * g + 4 * h + (s >> 2);
+  for (int kh = 0; kh < KB / 16; ++kh)
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      const int col = wn * 128 + ib * 16 + 4 * (s & 3);
-      aoff[h][ib] = r * BN + ((((col >> 3) ^ wswz(r))) << 3) + (col & 7);
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * kh + 8 * (g >> 1) + 4 * h + (s >> 2);
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const int col = wn * 128 + ib * 32 + 16 * (g & 1) + 4 * (s & 3);
+        aoff[kh][h][ib] = r * BN + ((((col >> 3) ^ wswz(r))) << 3) + (col & 7);
+      }
     }
-  }
-  const int xrow = wm * 128 + s;
-  const int boff = xrow * KB + ((g ^ xswz(xrow)) << 3);  // + jb * 16 * KB
-
-  floatx4 acc[8][8];
+  const int xrow = wm * 128 + l31;
+  int boff[KB / 16];  // + jb * 32 * KB
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int kh = 0; kh < KB / 16; ++kh) boff[kh] = xrow * KB + (((2 * kh + hf) ^ xswz(xrow)) << 3);
 
-  auto compute = [&](int st) {
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#ifndef MOE_GEMM_INTERLEAVE
+#define MOE_GEMM_INTERLEAVE 1
+#endif
+  // copies of one stage, spread over the MFMA groups of the current stage (or all at once)
+  auto issue_part = [&](int kt, int st, int part, int parts) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (i % parts == part)
+        copy_to_lds16(wsrc[i] + (size_t)kt * KB * N,
+                      ws_lds + 2u * (uint32_t)(st * WST + (2 * (NI * uwave + i)) * BN));
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (i % parts == part)
+        copy_to_lds16(A + xsrc[i] + kt * KB,
+                      xs_lds + 2u * (uint32_t)(st * XST + (1024 / (2 * KB)) * (NI * uwave + i) * KB));
+  };
+  auto compute = [&](int st, int nkt, int nst) {
     const bf16_t* Wb = Ws[st];
     const bf16_t* Xb = Xs[st];
-    bf16x8 b[8];
+    constexpr int PARTS = MOE_GEMM_INTERLEAVE ? (KB / 16) * 4 : 1;
+    if (!MOE_GEMM_INTERLEAVE && nkt >= 0) issue_part(nkt, nst, 0, 1);
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) b[jb] = *(const bf16x8*)&Xb[boff + jb * 16 * KB];
+    for (int kh = 0; kh < KB / 16; ++kh) {
+      bf16x8 a[4], b[4];
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[0][ib]]);
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[1][ib]]);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int jb = 0; jb < 4; ++jb) b[jb] = *(const bf16x8*)&Xb[boff[kh] + jb * 32 * KB];
 #pragma unroll
-      for (int jb = 0; jb < 8; ++jb)
-        acc[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[jb], acc[ib][jb], 0, 0, 0);
+      for (int ib = 0; ib < 4; ++ib) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][0][ib]]);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][1][ib]]);
+        a[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+          acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
+        if (MOE_GEMM_INTERLEAVE && nkt >= 0) issue_part(nkt, nst, kh * 4 + ib, PARTS);
+      }
     }
   };
 
@@ -218,44 +263,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (p < nk) issue(p, p);
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = min(nk - 1 - kt, NSTAGE - 2);  // stages newer than kt already issued
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    static_assert(CPS == 8 || CPS == 16, "wait counts below assume 8 or 16 copies per stage");
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
-    compute(kt % NSTAGE);
+    const int nkt = kt + NSTAGE - 1 < nk ? kt + NSTAGE - 1 : -1;
+    compute(kt % NSTAGE, nkt, (kt + NSTAGE - 1) % NSTAGE);
   }
 
-  // ---- epilogue: lane holds token row 16*jb + (lane & 15) and, for acc element p,
-  // weight column 16*ib + 4*g + p of its wave's columns.
+  // ---- epilogue: lane holds token row 32*jb + (lane & 31) and, for acc element
+  // 4q+p, weight column 32*ib + 8q + 4*(lane >> 5) + p of its wave's columns.
 #pragma unroll
-  for (int jb = 0; jb < 8; ++jb) {
-    const int r = row0 + wm * 128 + jb * 16 + s;
+  for (int jb = 0; jb < 4; ++jb) {
+    const int r = row0 + wm * 128 + jb * 32 + l31;
     if (r >= row_end) continue;
     OT* orow = out + (size_t)r * N;
     if (ACT == ACT_SWIGLU) {
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int col = n0 + wn * 64 + ib * 16 + 4 * g;
-        if (col >= N) continue;
-        float v[4];
+      for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) v[p] = silu(acc[ib][jb][p]) * acc[ib + 4][jb][p];
-        store4(orow + col, v);
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * 64 + ib * 32 + 8 * q + 4 * hf;
+          if (col >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) v[p] = silu_fast(acc[ib][jb][4 * q + p]) * acc[ib + 2][jb][4 * q + p];
+          store4(orow + col, v);
+        }
     } else {
 #pragma unroll
-      for (int ib = 0; ib < 8; ++ib) {
-        const int col = n0 + wn * 128 + ib * 16 + 4 * g;
-        if (col >= N) continue;
-        float v[4];
+      for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float z = acc[ib][jb][p];
-          v[p] = ACT == ACT_GELU ? gelu_erf(z) : z;
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * 128 + ib * 32 + 8 * q + 4 * hf;
+          if (col >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const float z = acc[ib][jb][4 * q + p];
+            v[p] = ACT == ACT_GELU ? gelu_erf(z) : z;
+          }
+          store4(orow + col, v);
         }
-        store4(orow + col, v);
-      }
     }
   }
 }
