@@ -207,6 +207,9 @@ def _ffn_case(E, h, f, seg, act, dtype, seed):
     ("swiglu", "bf16", 5, 256, 512, [0, 1, 300, 257, 37]),       # empty, single row, >1 tile, ragged
     ("gelu", "bf16", 4, 192, 320, [256, 0, 513, 2]),              # N tails in both projections
     ("swiglu", "bf16", 3, 512, 384, [31, 64, 700]),
+    ("swiglu", "bf16", 8, 256, 512, [16, 0, 3, 40, 16, 1, 33, 17]),  # few rows per expert: 32-row tiles
+    ("gelu", "bf16", 2, 256, 320, [600, 700]),                     # many rows per expert: 256-row tiles
+    ("swiglu", "bf16", 2, 192, 320, [300, 530]),                   # 256-row tiles with k and N tails
     ("swiglu", "f32", 5, 128, 256, [0, 1, 70, 129, 37]),
     ("gelu", "f32", 3, 192, 320, [65, 0, 64]),
 ])

@@ -57,6 +57,14 @@ int rows_max(int32_t T, int32_t E, int32_t k, int64_t C) {
   return (int)(cap < n ? cap : n);
 }
 
+// Token-tile height of the expert GEMMs: from the rows an expert receives on average
+// (T k / E, at most the capacity).
+int layer_bm(bool bf, int32_t T, int32_t E, int32_t k, int64_t C) {
+  double rpe = (double)T * k / E;
+  if (C != INT32_MAX && (double)C < rpe) rpe = (double)C;
+  return gemm_bm(bf, rpe);
+}
+
 moe_status_t common_sizes(int32_t T, int32_t E, int32_t k) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
   if ((int64_t)T * k > (int64_t)INT32_MAX / 2) return MOE_ERR_ARG;
@@ -132,7 +140,7 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
     if ((expr) != hipSuccess) return MOE_ERR_DEVICE; \
   } while (0)
 
-moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const int* tile_off, int R_max,
+moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const int* tile_off, int bm, int R_max,
                      int32_t h, int32_t f, int32_t E, const void* W1, const void* W3, const void* W2,
                      moe_act_t act, moe_dtype_t dt, void* hm, void* out, bool out_f32, hipStream_t st,
                      const std::function<bool()>& mark = std::function<bool()>()) {
@@ -149,6 +157,7 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   up.tile_off = tile_off;
   up.E = E;
   up.R_max = R_max;
+  up.bm = bm;
   up.act = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
   MOE_TRY(launch_gemm(up, bf, st));
   if (mark && !mark()) return MOE_ERR_DEVICE;
@@ -299,8 +308,9 @@ moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t 
   FfnWs w = carve_ffn(c, R_max, f, E, dt);
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   const bool bf = dt == MOE_BF16;
-  MOE_TRY(launch_tiles(offsets, E, gemm_bm(bf), w.tile_off, stream));
-  return run_ffn(x_perm, nullptr, offsets, w.tile_off, R_max, h, f, E, W1, W3, W2, act, dt, w.hm, out_perm,
+  const int bm = gemm_bm(bf, (double)R_max / E);
+  MOE_TRY(launch_tiles(offsets, E, bm, w.tile_off, stream));
+  return run_ffn(x_perm, nullptr, offsets, w.tile_off, bm, R_max, h, f, E, W1, W3, W2, act, dt, w.hm, out_perm,
                  false, stream);
 }
 
@@ -370,7 +380,8 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.T = T;
   sa.k = k;
   sa.C = (int)C;
-  sa.BM = gemm_bm(bf);
+  const int bm = layer_bm(bf, T, E, k, C);
+  sa.BM = bm;
   sa.prob_part = w.prob_part;
   sa.nrb = route_blocks(T);
   sa.prob_sum = nullptr;
@@ -384,7 +395,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
                          w.perm_token, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
+  moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, bm, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
                            w.o, bf, stream, ev ? [&]() { return mark(); } : std::function<bool()>());
   if (r != MOE_OK) return r;
   MOE_TRY(launch_combine(w.o, true, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));

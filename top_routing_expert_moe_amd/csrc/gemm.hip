@@ -8,21 +8,25 @@
 //
 // gfx950 design (bf16):
 //  * one launch covers all experts: the m-tile -> expert map comes from the
-//    device-side tile_off[] (exclusive scan of ceil(rows_e / 256)), so there
-//    is no host synchronisation and experts with no rows cost nothing;
-//  * workgroup tile 256 rows x 256 weight columns x 64 k, 4 waves of 128x128,
-//    v_mfma_f32_32x32x16_bf16, fp32 accumulators (256 per lane);
-//  * the weights are stored [K, N] with N contiguous, while MFMA wants 8
-//    consecutive k per lane: each thread loads an 8x8 block (8 rows x 16 B)
-//    and transposes it in registers before one 16-byte LDS store per column;
-//  * LDS rows are 128 B (64 bf16) with the 16-byte chunk index XOR-swizzled by
-//    (row ^ row>>3) & 7, conflict-free for both the column stores and the
-//    MFMA fragment reads; two stages (128 KiB) double-buffer the k-loop;
-//  * SwiGLU: the 256 weight columns of a tile are 128 of W1 and the same 128
-//    of W3, arranged so each wave holds W1 and W3 accumulators of the same
-//    output column in the same lane; silu(a)*g is applied in registers;
+//    device-side tile_off[] (exclusive scan of ceil(rows_e / BM)), so there is
+//    no host synchronisation and experts with no rows cost nothing;
+//  * workgroup tile BM rows x 256 weight columns x 64 k per LDS stage, 4 waves,
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  BM follows the expected
+//    rows per expert: 256 (2 x 2 waves of 128 x 128, compute-bound prefill), 128
+//    or 32 (1 x 4 waves of BM x 64, where the weights dominate and a deeper
+//    pipeline keeps more of them in flight);
+//  * both operands go from global memory straight into LDS (global_load_lds,
+//    16 B per lane) with no register staging.  The weights stay [K, N] with N
+//    contiguous in LDS and the MFMA operand (8 consecutive k of one column) is
+//    read with ds_read_b64_tr_b16, the transposing LDS read;
+//  * the 16-byte chunk index of each LDS row is XOR-swizzled with a function of
+//    the row so that both the transposing reads and the activation reads are
+//    free of bank conflicts; the copies of the next stage are issued in small
+//    groups between the MFMAs of the current one;
+//  * SwiGLU: each wave's weight columns are half W1 and the same columns of W3,
+//    so silu(a) * g is applied in registers in the epilogue;
 //  * the up projection reads its left operand straight from x through the
-//    row -> token map (the gather is fused into the A-load);
+//    row -> token map (the gather is fused into the copy);
 //  * XCD-aware order: hardware workgroup i runs on XCD i%8; each XCD takes a
 //    contiguous range of the tile list, which is ordered in 4 x 8 groups of
 //    (m-tile, n-tile) inside each expert, so the workgroups running together in
@@ -36,7 +40,7 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 256, BN = 256;
+constexpr int BN = 256;  // weight columns staged per tile
 
 __device__ __forceinline__ void store4(bf16_t* p, const float* v) {
   *(u32x2*)p = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -76,44 +80,56 @@ typedef __attribute__((address_space(1))) void glob_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-#ifndef MOE_GEMM_KB
-#define MOE_GEMM_KB 64
-#endif
-#ifndef MOE_GEMM_NSTAGE
-#define MOE_GEMM_NSTAGE 2
-#endif
-constexpr int KB = MOE_GEMM_KB;         // k per LDS stage (KB/16 MFMA k-steps)
-constexpr int NSTAGE = MOE_GEMM_NSTAGE; // LDS stages: copies run NSTAGE-1 stages ahead
-constexpr int WST = KB * BN;  // weight stage, elements: [KB k][256 n], n contiguous
-constexpr int XST = BM * KB;  // activation stage, elements: [256 m][KB k], k contiguous
+constexpr int KB = 64;    // k per LDS stage (4 MFMA k-steps of 16)
+constexpr int WST = KB * BN;  // weight stage, elements: [64 k][256 n], n contiguous
 constexpr int XCH = KB / 8;   // 16-byte chunks per activation row
-constexpr int CPS = KB / 4;   // copies per thread per stage (KB/8 weight + KB/8 activation)
-static_assert(NSTAGE * (WST + XST) * 2 <= 160 * 1024, "LDS");
+constexpr int NIW = KB / 8;   // weight copies per thread per stage
+
+// Tile shapes by token-tile height: the wave grid (waves along m x along n) and the
+// number of LDS stages that fit.  256 rows: 2 x 2 waves of 128 x 128 (prefill);
+// 128 and 32 rows: 1 x 4 waves of BM x 64 (few rows per expert: the weights dominate,
+// so the deeper pipeline keeps more weight bytes in flight).
+// SPREAD: the next stage's copies are issued between the first SPREAD groups of MFMAs
+// of the current stage (issuing them early leaves them the most time to land; spreading
+// them keeps the MFMA issue from stalling behind a full memory queue).
+template <int BMT> struct TileCfg;
+template <> struct TileCfg<256> { static constexpr int WMW = 2, NSTAGE = 2, SPREAD = 8; };
+template <> struct TileCfg<128> { static constexpr int WMW = 1, NSTAGE = 3, SPREAD = 8; };
+template <> struct TileCfg<32> { static constexpr int WMW = 1, NSTAGE = 4, SPREAD = 8; };
 
 // Swizzles (16-byte chunk index XOR a function of the row):
 //  * weight stage rows are 256 n = 32 chunks; a transposing read touches rows
 //    8g + 4h + t (g, t = 0..3) at one chunk pair, so f spreads t and g over 16
 //    distinct even values;
-//  * activation stage rows are 32 k = 4 chunks; 16 consecutive rows are read at one
-//    chunk, so f spreads (row >> 2) over the 4 chunks.
+//  * activation stage rows are 64 k = 8 chunks; the 16 lanes read together touch 16
+//    consecutive rows at one chunk, so f spreads (row >> 1) over the 8 chunks.
+__device__ __forceinline__ int wswz(int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) << 1; }
+__device__ __forceinline__ int xswz(int r) { return (r >> 1) & 7; }
+
 // One 16-byte-per-lane copy from global memory straight into LDS (the wave's 1 KiB
 // block starts at the LDS byte address in m0).  Issued as a plain instruction so that
 // the compiler does not serialise later LDS reads behind it: the pipeline below waits
 // for these copies itself (s_waitcnt vmcnt + barrier) before any wave reads the stage.
-// It has no destination registers, so nothing is left in flight in a register.
+// It has no destination registers, so nothing is left in flight in a register, and
+// no other code in these kernels uses m0.
 __device__ __forceinline__ void copy_to_lds16(const void* gptr, uint32_t lds_block) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_block) : "memory", "m0");
 }
 
-__device__ __forceinline__ int wswz(int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) << 1; }
-__device__ __forceinline__ int xswz(int r) { return (r >> 2) & 3; }
-
-template <int ACT, bool GATHER, typename OT>
+template <int BMT, int ACT, bool GATHER, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out,
     const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, int NT) {
-  constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr int NSTAGE = TileCfg<BMT>::NSTAGE, SPREAD = TileCfg<BMT>::SPREAD;
+  constexpr int WMW = TileCfg<BMT>::WMW, WNW = 4 / WMW;  // waves along m / along n
+  constexpr int WTM = BMT / WMW, WTN = BN / WNW;          // wave tile
+  constexpr int IB = WTN / 32, JB = WTM / 32;             // 32 x 32 MFMA blocks per wave
+  constexpr int XST = BMT * KB;                           // activation stage elements
+  constexpr int NIX = BMT / 32;                           // activation copies per thread per stage
+  constexpr int CPS = NIW + NIX;                          // copies per thread per stage
+  constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;     // output columns per tile
+  static_assert(NSTAGE * (WST + XST) * 2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) bf16_t Ws[NSTAGE][WST];
   __shared__ __attribute__((aligned(1024))) bf16_t Xs[NSTAGE][XST];
 
@@ -129,34 +145,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (L >= n_real) return;
   int e, mt_local, nt;
   tile_of(L, tile_off, E, NT, e, mt_local, nt);
-  const int row0 = offsets[e] + mt_local * BM;
-  const int row_end = min(row0 + BM, offsets[e + 1]);
+  const int row0 = offsets[e] + mt_local * BMT;
+  const int row_end = min(row0 + BMT, offsets[e + 1]);
   const int n0 = nt * NO;
 
   // ---- copy plan.  One wave instruction moves 1 KiB: lane l writes LDS bytes
   // [16l, 16l+16) of the instruction's block, i.e. swizzle slot (l & 31) of weight
-  // row (l >> 5) or slot (l & 3) of activation row (l >> 2); it fetches the global
+  // row (l >> 5) or slot (l & 7) of activation row (l >> 3); it fetches the global
   // chunk that the swizzle puts there.  Columns past N / rows past the segment fetch
   // a valid neighbour instead (their results are never stored).
-  constexpr int NI = KB / 8;  // copy instructions per wave per operand and stage
-  const bf16_t* wsrc[NI];
-  uint32_t xsrc[NI];
+  // Weight columns: each wave's WTN LDS columns hold, for SwiGLU, WTN/2 columns of W1
+  // followed by the same WTN/2 columns of W3.
+  const bf16_t* wsrc[NIW];
+  uint32_t xsrc[NIX];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = 2 * (NI * wave + i) + (lane >> 5);  // weight stage row (k)
-    const int c = (lane & 31) ^ wswz(r);              // 16-byte chunk of 8 columns
+  for (int i = 0; i < NIW; ++i) {
+    const int r = 2 * (NIW * wave + i) + (lane >> 5);  // weight stage row (k)
+    const int c = (lane & 31) ^ wswz(r);               // 16-byte chunk of 8 columns
     int col;
     const bf16_t* Wm;
-    if (ACT == ACT_SWIGLU) {  // chunks 0-7 / 8-15: W1 / W3 of wave-half 0; 16-31: wave-half 1
-      const int wn = c >> 4, cc = c & 15;
-      col = n0 + wn * 64 + (cc & 7) * 8;
-      Wm = cc < 8 ? W : W3;
+    if (ACT == ACT_SWIGLU) {
+      constexpr int CPW = WTN / 8;  // chunks per wave's columns
+      const int wg = c / CPW, cc = c % CPW;
+      col = n0 + wg * (WTN / 2) + (cc % (CPW / 2)) * 8;
+      Wm = cc < CPW / 2 ? W : W3;
     } else {
       col = n0 + c * 8;
       Wm = W;
     }
     wsrc[i] = Wm + (size_t)e * K * N + (size_t)r * N + min(col, N - 8);
-    const int xr = (1024 / (2 * KB)) * (NI * wave + i) + lane / XCH;  // activation stage row (m)
+  }
+#pragma unroll
+  for (int i = 0; i < NIX; ++i) {
+    const int xr = 8 * (NIX * wave + i) + lane / XCH;  // activation stage row (m)
     const int rr = min(row0 + xr, row_end - 1);
     const int src_row = GATHER ? a_rows[rr] : rr;
     xsrc[i] = (uint32_t)src_row * (uint32_t)K + (uint32_t)((((lane % XCH) ^ xswz(xr))) << 3);
@@ -164,106 +185,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ws_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Ws[0][0];
   const uint32_t xs_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Xs[0][0];
-  auto issue = [&](int kt, int st) {
+  // the copies of one stage that belong to MFMA group `part` of `parts`: weight copy i
+  // and activation copy j go to groups i * sp / NIW and j * sp / NIX, sp = min(SPREAD,
+  // parts) (parts == 1: all of them)
+  auto issue_part = [&](int kt, int st, int part, int parts) {
+    const int sp = parts < SPREAD ? parts : SPREAD;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      copy_to_lds16(wsrc[i] + (size_t)kt * KB * N,
-                    ws_lds + 2u * (uint32_t)(st * WST + (2 * (NI * uwave + i)) * BN));
+    for (int i = 0; i < NIW; ++i)
+      if (i * sp / NIW == part)
+        copy_to_lds16(wsrc[i] + (size_t)kt * KB * N,
+                      ws_lds + 2u * (uint32_t)(st * WST + (2 * (NIW * uwave + i)) * BN));
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      copy_to_lds16(A + xsrc[i] + kt * KB,
-                    xs_lds + 2u * (uint32_t)(st * XST + (1024 / (2 * KB)) * (NI * uwave + i) * KB));
+    for (int i = 0; i < NIX; ++i)
+      if (i * sp / NIX == part)
+        copy_to_lds16(A + xsrc[i] + kt * KB, xs_lds + 2u * (uint32_t)(st * XST + 8 * (NIX * uwave + i) * KB));
   };
 
   // ---- fragment addressing (v_mfma_f32_32x32x16_bf16).  Wave (wn, wm) owns weight
-  // columns wn*128 + [0,128) and activation rows wm*128 + [0,128): 4 x 4 blocks of
-  // 32 x 32, two 16-k halves (kh) per 32-k step.
+  // columns wn*WTN + [0,WTN) and activation rows wm*WTM + [0,WTM): IB x JB blocks of
+  // 32 x 32, four 16-k halves (kh) per stage.
   // Weights (MFMA rows): two transposing 8-byte reads per block and half; in lane group
   // g = lane >> 4, lane s = lane & 15 points at row 16*kh + 8*(g >> 1) + 4*h + (s >> 2),
   // columns 32*ib + 16*(g & 1) + 4*(s & 3) .. +3, and receives k = 16*kh + 8*(g >> 1) +
   // 4*h + 0..3 of column 32*ib + (lane & 31): the MFMA row layout.
   // Activations (MFMA columns): one 16-byte read, row 32*jb + (lane & 31), k-chunk
   // 2*kh + (lane >> 5).
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WNW, wm = wave / WNW;
   const int g = lane >> 4, s = lane & 15, l31 = lane & 31, hf = lane >> 5;
-  int aoff[KB / 16][2][4];
+  int aoff[KB / 16][2][IB];
 #pragma unroll
   for (int kh = 0; kh < KB / 16; ++kh)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = 16 * kh + 8 * (g >> 1) + 4 * h + (s >> 2);
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int col = wn * 128 + ib * 32 + 16 * (g & 1) + 4 * (s & 3);
+      for (int ib = 0; ib < IB; ++ib) {
+        const int col = wn * WTN + ib * 32 + 16 * (g & 1) + 4 * (s & 3);
         aoff[kh][h][ib] = r * BN + ((((col >> 3) ^ wswz(r))) << 3) + (col & 7);
       }
     }
-  const int xrow = wm * 128 + l31;
+  const int xrow = wm * WTM + l31;
   int boff[KB / 16];  // + jb * 32 * KB
 #pragma unroll
   for (int kh = 0; kh < KB / 16; ++kh) boff[kh] = xrow * KB + (((2 * kh + hf) ^ xswz(xrow)) << 3);
 
-  floatx16 acc[4][4];
+  floatx16 acc[IB][JB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-#ifndef MOE_GEMM_INTERLEAVE
-#define MOE_GEMM_INTERLEAVE 1
-#endif
-  // copies of one stage, spread over the MFMA groups of the current stage (or all at once)
-  auto issue_part = [&](int kt, int st, int part, int parts) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if (i % parts == part)
-        copy_to_lds16(wsrc[i] + (size_t)kt * KB * N,
-                      ws_lds + 2u * (uint32_t)(st * WST + (2 * (NI * uwave + i)) * BN));
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if (i % parts == part)
-        copy_to_lds16(A + xsrc[i] + kt * KB,
-                      xs_lds + 2u * (uint32_t)(st * XST + (1024 / (2 * KB)) * (NI * uwave + i) * KB));
-  };
+  // MFMAs of stage `st`; the copies of stage `nkt` (if >= 0) into buffer `nst` are
+  // issued in between, one share after each group of JB MFMAs.
   auto compute = [&](int st, int nkt, int nst) {
     const bf16_t* Wb = Ws[st];
     const bf16_t* Xb = Xs[st];
-    constexpr int PARTS = MOE_GEMM_INTERLEAVE ? (KB / 16) * 4 : 1;
-    if (!MOE_GEMM_INTERLEAVE && nkt >= 0) issue_part(nkt, nst, 0, 1);
+    constexpr int PARTS = (KB / 16) * IB;
 #pragma unroll
     for (int kh = 0; kh < KB / 16; ++kh) {
-      bf16x8 a[4], b[4];
+      bf16x8 a[IB], b[JB];
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) b[jb] = *(const bf16x8*)&Xb[boff[kh] + jb * 32 * KB];
+      for (int jb = 0; jb < JB; ++jb) b[jb] = *(const bf16x8*)&Xb[boff[kh] + jb * 32 * KB];
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
+      for (int ib = 0; ib < IB; ++ib) {
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][0][ib]]);
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][1][ib]]);
         a[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
+      for (int ib = 0; ib < IB; ++ib) {
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
+        for (int jb = 0; jb < JB; ++jb)
           acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
-        if (MOE_GEMM_INTERLEAVE && nkt >= 0) issue_part(nkt, nst, kh * 4 + ib, PARTS);
+        if (nkt >= 0) issue_part(nkt, nst, kh * IB + ib, PARTS);
       }
     }
   };
 
-  // ---- pipeline: stage kt lives in LDS buffer kt % NSTAGE; copies for stage
-  // kt + NSTAGE - 1 are issued right after the barrier that ends all reads of the
-  // buffer they overwrite.  Each thread waits for its own copies of stage kt (newer
-  // stages may stay in flight), then the barrier makes every thread's copies visible.
+  // ---- pipeline: stage kt lives in LDS buffer kt % NSTAGE; the copies of stage
+  // kt + NSTAGE - 1 go into the buffer that the barrier of step kt has released.
+  // Each thread waits for its own copies of stage kt (newer stages may stay in
+  // flight), then the barrier makes every thread's copies visible.
   const int nk = K / KB;
 #pragma unroll
   for (int p = 0; p < NSTAGE - 1; ++p)
-    if (p < nk) issue(p, p);
+    if (p < nk) issue_part(p, p, 0, 1);
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = min(nk - 1 - kt, NSTAGE - 2);  // stages newer than kt already issued
-    static_assert(CPS == 8 || CPS == 16, "wait counts below assume 8 or 16 copies per stage");
     if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
     else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -275,28 +285,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- epilogue: lane holds token row 32*jb + (lane & 31) and, for acc element
   // 4q+p, weight column 32*ib + 8q + 4*(lane >> 5) + p of its wave's columns.
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int r = row0 + wm * 128 + jb * 32 + l31;
+  for (int jb = 0; jb < JB; ++jb) {
+    const int r = row0 + wm * WTM + jb * 32 + l31;
     if (r >= row_end) continue;
     OT* orow = out + (size_t)r * N;
     if (ACT == ACT_SWIGLU) {
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
+      for (int ib = 0; ib < IB / 2; ++ib)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 64 + ib * 32 + 8 * q + 4 * hf;
+          const int col = n0 + wn * (WTN / 2) + ib * 32 + 8 * q + 4 * hf;
           if (col >= N) continue;
           float v[4];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) v[p] = silu_fast(acc[ib][jb][4 * q + p]) * acc[ib + 2][jb][4 * q + p];
+          for (int p = 0; p < 4; ++p) v[p] = silu_fast(acc[ib][jb][4 * q + p]) * acc[ib + IB / 2][jb][4 * q + p];
           store4(orow + col, v);
         }
     } else {
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
+      for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 128 + ib * 32 + 8 * q + 4 * hf;
+          const int col = n0 + wn * WTN + ib * 32 + 8 * q + 4 * hf;
           if (col >= N) continue;
           float v[4];
 #pragma unroll
@@ -396,17 +406,27 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   }
 }
 
-template <int ACT, bool G, typename OT>
-hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
+template <int BMT, int ACT, bool G, typename OT>
+hipError_t launch_bf16_bm(const GemmArgs& a, hipStream_t st) {
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;
   const int NT = (a.N + NO - 1) / NO;
-  const long long slots = ((long long)(a.R_max + BM - 1) / BM + a.E) * NT;
+  const long long slots = ((long long)(a.R_max + BMT - 1) / BMT + a.E) * NT;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_kernel<BMT, ACT, G, OT>), dim3((unsigned)grid), dim3(256), 0, st,
                      (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
                      (OT*)a.out, a.offsets, a.tile_off, a.E, NT);
   return hipGetLastError();
+}
+
+template <int ACT, bool G, typename OT>
+hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
+  switch (a.bm) {
+    case 256: return launch_bf16_bm<256, ACT, G, OT>(a, st);
+    case 128: return launch_bf16_bm<128, ACT, G, OT>(a, st);
+    case 32: return launch_bf16_bm<32, ACT, G, OT>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int ACT, bool G>
@@ -436,7 +456,12 @@ hipError_t dispatch_act(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int gemm_bm(bool bf16) { return bf16 ? BM : FBM; }
+int gemm_bm(bool bf16, double rows_per_expert) {
+  if (!bf16) return FBM;
+  if (rows_per_expert <= 48.0) return 32;
+  if (rows_per_expert <= 320.0) return 128;
+  return 256;
+}
 
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t st) {
   if (bf16) return a.a_rows ? dispatch_act<true, true>(a, st) : dispatch_act<true, false>(a, st);

@@ -73,8 +73,10 @@ struct GemmArgs {
   int R_max;            // upper bound of rows
   int act;
   bool out_f32;         // bf16 GEMM writing fp32 output (down projection inside the layer)
+  int bm;               // rows per m-tile (gemm_bm); tile_off must be built with it
 };
-int gemm_bm(bool bf16);  // rows per m-tile of the expert GEMMs
+// rows per m-tile of the expert GEMMs, from the expected rows per expert
+int gemm_bm(bool bf16, double rows_per_expert);
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t st);
 
 // ---- combine
