@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 METRIC = "MoE layer tokens/s at Mixtral shape (T=4096); % bf16 MFMA peak; route GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -94,6 +95,9 @@ def main():
     ap.add_argument("--workload", default="prefill-mixtral")
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before warm-up, run a plain elementwise copy (y = x + 1, fp32) over this many MiB three "
+                         "times: a kernel of known traffic for calibrating rocprofv3's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -140,6 +144,16 @@ def main():
         moe.layer_forward(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
                           capacity_factor=w.cf, act=w.act, ws=ws, y=y, aux=aux, counts=counts, events=events)
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.zeros(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] copy probe: 3 x {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -171,23 +185,46 @@ def main():
     flops_down = 2.0 * R * f * h
     flops_router = 2.0 * T * h * E
     up_s = stage_ms["expert_up"] / 1e3
-    achieved = flops_up / up_s / 1e12
     ms_per_step = wall / args.steps * 1e3
     es = 2 if bf else 4
+    active = int((kept > 0).sum())
+    # algorithmic bytes of the up-projection: each active expert's W1 (and W3) once, the R
+    # gathered activation rows read, the R hidden rows written
+    bytes_up = active * n_up * h * f * es + R * h * es + R * f * es
+    bytes_down = active * f * h * es + R * f * es + R * h * 4
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    kname = ("expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue, gather fused)" if w.act == "swiglu"
+             else "expert up-projection (grouped bf16 MFMA GEMM, GELU epilogue, gather fused)")
+    if not bf:  # the fp32 GEMM runs on the vector ALUs
+        achieved = flops_up / up_s / 1e12
+        roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_FP32_TFLOPS, 5)}
+    elif flops_up / bytes_up >= ridge:
+        achieved = flops_up / up_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = bytes_up / up_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": traffic_entry(w.name), "kernel": kname, "flops_per_launch": flops_up,
+                     "algorithmic_bytes_per_launch": bytes_up, "avg_launch_ms": round(stage_ms["expert_up"], 5)})
     # compulsory bytes of routing + permutation metadata: x and W_gate read once, logits written,
     # topk idx/w, slot_pos and the sorted order (4 B each per assignment)
     route_bytes = T * h * es + h * E * 4 + T * E * 4 + T * k * 16
     route_ms = sum(stage_ms[s] for s in ("logits", "select", "scan", "scatter"))
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry(w.name),
-                "kernel": "expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue)" if w.act == "swiglu"
-                else "expert up-projection (grouped GEMM, GELU epilogue)",
-                "flops_per_launch": flops_up, "avg_launch_ms": round(stage_ms["expert_up"], 5)}
+    # the layer's own roof: compulsory bytes (x, W_gate, active weights, y, routing metadata) against
+    # its MFMA work
+    layer_bytes = T * h * es + h * E * 4 + active * (n_up + 1) * h * f * es + T * h * es + T * k * 12
+    t_roof = max((flops_up + flops_down) / (PEAK_BF16_TFLOPS * 1e12), layer_bytes / (PEAK_HBM_GBS * 1e9))
     extra = {
         "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
-        "rows_kept": R, "active_experts": int((cnt > 0).sum()),
+        "rows_kept": R, "active_experts": active,
         "layer_mfma_frac": round((flops_up + flops_down) / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "layer_roofline_frac": round(t_roof / (ms_per_step / 1e3), 4),
         "expert_down_frac": round(flops_down / (stage_ms["expert_down"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "expert_up_hbm_gbs": round(bytes_up / up_s / 1e9, 1),
+        "expert_down_hbm_gbs": round(bytes_down / (stage_ms["expert_down"] / 1e3) / 1e9, 1),
         "route_gbps": round(route_bytes / (route_ms / 1e3) / 1e9, 1),
         "router_flops": flops_router,
         "aux_loss": float(aux.cpu()),
