@@ -118,7 +118,11 @@ moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int3
  *   x_perm [R_max,h], W1/W3 [E,h,f], W2 [E,f,h] (dt); W3 must be NULL iff GELU.
  *   offsets [E+1] int32 (device), R_max >= offsets[E] (rows allocated in x_perm/out_perm)
  *   out_perm [R_max,h] (dt): rows >= offsets[E] are not written.
- *   ws: needs R_max*f*elem + 4*(E+1) bytes (+256). */
+ *   ws: at least moe_expert_ffn_workspace_bytes(R_max,h,f,E,dt,act) bytes (the hidden
+ *       activation, plus fp32 partial sums when few rows per expert make the library
+ *       split K to fill the GPU). */
+size_t moe_expert_ffn_workspace_bytes(int32_t R_max, int32_t h, int32_t f, int32_t E, moe_dtype_t dt,
+                                      moe_act_t act);  /* 0 for invalid sizes */
 moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t R_max,
                             int32_t h, int32_t f, int32_t E, const void* W1, const void* W3,
                             const void* W2, moe_act_t act, moe_dtype_t dt, void* out_perm,

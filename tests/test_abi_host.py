@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
     names = _declared()
     assert set(names) == {"moe_capacity", "moe_workspace_bytes", "moe_status_string", "moe_route",
                           "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_forward",
-                          "moe_layer_forward_timed"}
+                          "moe_layer_forward_timed", "moe_expert_ffn_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -80,6 +80,16 @@ def test_workspace_bytes(L):
     # a capacity below the mean load (E*C < T*k) shrinks the bound on kept rows
     assert moe.workspace_bytes(8192, 1024, 4096, 64, 2, 0.5, 1, 0) < moe.workspace_bytes(8192, 1024, 4096, 64, 2,
                                                                                            0.0, 1, 0)
+    # few rows per expert: the down projection splits K and keeps fp32 partial sums (8 parts
+    # of its h columns at decode shape)
+    b = moe.workspace_bytes(64, 4096, 14336, 8, 2, 0.0, 1, 1)
+    assert b >= 128 * 14336 * 2 + 8 * 128 * 4096 * 4
+    L = moe.lib()
+    fb = L.moe_expert_ffn_workspace_bytes(128, 4096, 14336, 8, 1, 1)
+    assert 128 * 14336 * 2 <= fb <= b
+    assert L.moe_expert_ffn_workspace_bytes(8192, 4096, 14336, 8, 1, 1) >= 8192 * 14336 * 2
+    assert L.moe_expert_ffn_workspace_bytes(-1, 64, 64, 8, 1, 1) == 0
+    assert L.moe_expert_ffn_workspace_bytes(8, 64, 64, 300, 1, 1) == 0
     assert moe.workspace_bytes(8, 64, 64, 300, 2, 0.0, 1, 0) == 0   # E > 256
     assert moe.workspace_bytes(8, 64, 64, 8, 9, 0.0, 1, 0) == 0     # k > E
     assert moe.workspace_bytes(8, 64, 64, 8, 2, float("nan"), 1, 0) == 0

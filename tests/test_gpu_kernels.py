@@ -210,6 +210,8 @@ def _ffn_case(E, h, f, seg, act, dtype, seed):
     ("swiglu", "bf16", 8, 256, 512, [16, 0, 3, 40, 16, 1, 33, 17]),  # few rows per expert: 32-row tiles
     ("gelu", "bf16", 2, 256, 320, [600, 700]),                     # many rows per expert: 256-row tiles
     ("swiglu", "bf16", 2, 192, 320, [300, 530]),                   # 256-row tiles with k and N tails
+    ("swiglu", "bf16", 4, 1024, 2048, [5, 20, 0, 9]),              # 32-row tiles, K split 2 (up) and 4 (down)
+    ("gelu", "bf16", 3, 2048, 1024, [12, 3, 30]),                  # K split 4 (up) and 2 (down), GELU parts
     ("swiglu", "f32", 5, 128, 256, [0, 1, 70, 129, 37]),
     ("gelu", "f32", 3, 192, 320, [65, 0, 64]),
 ])

@@ -87,6 +87,8 @@ def test_layer_forward_deterministic():
     (200, 192, 256, 4, 1, 0.3, "gelu", "bf16"),      # heavy drops, k = 1
     (130, 64, 64, 1, 1, 0.0, "swiglu", "f32"),       # a single expert: the plain FFN
     (500, 128, 256, 16, 2, 0.25, "swiglu", "f32"),   # drops in fp32
+    (20, 1024, 2048, 8, 2, 0.0, "swiglu", "bf16"),   # few rows per expert: K-split GEMMs, parts added in combine
+    (40, 2048, 1024, 6, 2, 0.5, "gelu", "bf16"),     # K-split GEMMs with drops
 ])
 def test_layer_edge_cases(T, h, f, E, k, cf, act, dtype):
     import math

@@ -34,6 +34,7 @@ _sz = ctypes.c_size_t
 _SIGS = {
     "moe_capacity": (_i32, [_i32, _i32, _i32, _f32]),
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int]),
+    "moe_expert_ffn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, ctypes.c_int,
                                  ctypes.c_uint32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz,
@@ -200,7 +201,7 @@ def expert_ffn(x_perm, offsets, W1, W3, W2, act: str):
     E, _, f = W1.shape
     dt = _dt(x_perm)
     out = torch.empty_like(x_perm)
-    ws = _ws(R_max * f * x_perm.element_size() + 4 * (E + 1) + 1024, dev)
+    ws = _ws(lib().moe_expert_ffn_workspace_bytes(R_max, h, f, E, dt, _ACT[act]), dev)
     st = lib().moe_expert_ffn(_p(x_perm), _p(offsets), R_max, h, f, E, _p(W1), _p(W3), _p(W2), _ACT[act], dt,
                               _p(out), _p(ws), ws.numel(), _stream(dev))
     _check(st, "moe_expert_ffn")

@@ -57,12 +57,12 @@ int rows_max(int32_t T, int32_t E, int32_t k, int64_t C) {
   return (int)(cap < n ? cap : n);
 }
 
-// Token-tile height of the expert GEMMs: from the rows an expert receives on average
-// (T k / E, at most the capacity).
-int layer_bm(bool bf, int32_t T, int32_t E, int32_t k, int64_t C) {
+// Tile height and K splits of the layer's expert GEMMs: from the rows an expert receives
+// on average (T k / E, at most the capacity).
+FfnPlan layer_plan(bool bf, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int64_t C) {
   double rpe = (double)T * k / E;
   if (C != INT32_MAX && (double)C < rpe) rpe = (double)C;
-  return gemm_bm(bf, rpe);
+  return plan_ffn(bf, rpe, E, rows_max(T, E, k, C), h, f);
 }
 
 moe_status_t common_sizes(int32_t T, int32_t E, int32_t k) {
@@ -97,11 +97,16 @@ PermWs carve_perm(Carve& c, int32_t T, int32_t E, int32_t k) {
   return w;
 }
 
-struct FfnWs { int* tile_off; void* hm; };
-FfnWs carve_ffn(Carve& c, int R_max, int32_t f, int32_t E, moe_dtype_t dt) {
+size_t up_cols(moe_act_t act, int32_t f) { return (size_t)(act == MOE_ACT_SWIGLU ? 2 : 1) * f; }
+
+struct FfnWs { int* tile_off; void* hm; float* part_up; float* part_down; };
+FfnWs carve_ffn(Carve& c, const FfnPlan& pl, int R_max, int32_t h, int32_t f, int32_t E, moe_dtype_t dt,
+                moe_act_t act) {
   FfnWs w;
   w.tile_off = c.take<int>((size_t)E + 1);
   w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
+  w.part_up = pl.s_up > 1 ? c.take<float>((size_t)pl.s_up * R_max * up_cols(act, f)) : nullptr;
+  w.part_down = pl.s_down > 1 ? c.take<float>((size_t)pl.s_down * R_max * h) : nullptr;
   return w;
 }
 
@@ -109,10 +114,10 @@ struct LayerWs {
   uint16_t* planes;
   float* logits; int* topk_idx; float* topk_w; float* prob_part; int* blk_counts; int* blk_base;
   int* counts; int* offsets; int* tile_off; float* aux; int* slot_pos; int* sorted_slot;
-  int* perm_token; void* hm; void* o;
+  int* perm_token; void* hm; float* part_up; float* o;
 };
 LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int R_max,
-                    moe_dtype_t dt) {
+                    const FfnPlan& pl, moe_dtype_t dt, moe_act_t act) {
   LayerWs w;
   const size_t n = (size_t)T * k;
   const size_t nhb = (size_t)route_blocks(T);
@@ -131,7 +136,10 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
   w.sorted_slot = c.take<int>(n);
   w.perm_token = c.take<int>(n);
   w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
-  w.o = c.take<float>((size_t)R_max * h);  // expert outputs stay fp32 until the combine
+  w.part_up = pl.s_up > 1 ? c.take<float>((size_t)pl.s_up * R_max * up_cols(act, f)) : nullptr;
+  // expert outputs stay fp32 until the combine (s_down K parts of them when the down
+  // projection is split; the combine adds the parts)
+  w.o = c.take<float>((size_t)pl.s_down * R_max * h);
   return w;
 }
 
@@ -140,11 +148,17 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
     if ((expr) != hipSuccess) return MOE_ERR_DEVICE; \
   } while (0)
 
-moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const int* tile_off, int bm, int R_max,
-                     int32_t h, int32_t f, int32_t E, const void* W1, const void* W3, const void* W2,
-                     moe_act_t act, moe_dtype_t dt, void* hm, void* out, bool out_f32, hipStream_t st,
+// The two expert GEMMs.  up: A (rows through a_rows) x W1 (and W3) -> act -> hm.
+// down: hm x W2 -> out (fp32 when out_f32, else dt).  With a K-split down projection and
+// out_parts set, the fp32 parts stay in part_down (== out) for the combine to add;
+// otherwise they are added into out here.
+moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const int* tile_off, const FfnPlan& pl,
+                     int R_max, int32_t h, int32_t f, int32_t E, const void* W1, const void* W3, const void* W2,
+                     moe_act_t act, moe_dtype_t dt, void* hm, float* part_up, void* out, bool out_f32,
+                     float* part_down, bool out_parts, hipStream_t st,
                      const std::function<bool()>& mark = std::function<bool()>()) {
   const bool bf = dt == MOE_BF16;
+  const int gact = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
   GemmArgs up{};
   up.A = A;
   up.a_rows = a_rows;
@@ -152,14 +166,16 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   up.W3 = act == MOE_ACT_SWIGLU ? W3 : nullptr;
   up.K = h;
   up.N = f;
-  up.out = hm;
+  up.out = pl.s_up > 1 ? (void*)part_up : hm;
   up.offsets = offsets;
   up.tile_off = tile_off;
   up.E = E;
   up.R_max = R_max;
-  up.bm = bm;
-  up.act = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
+  up.bm = pl.bm;
+  up.ksplit = pl.s_up;
+  up.act = gact;
   MOE_TRY(launch_gemm(up, bf, st));
+  if (pl.s_up > 1) MOE_TRY(launch_ffn_finish(part_up, pl.s_up, R_max, f, gact, offsets, E, bf, hm, st));
   if (mark && !mark()) return MOE_ERR_DEVICE;
   GemmArgs down = up;
   down.A = hm;
@@ -168,10 +184,13 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   down.W3 = nullptr;
   down.K = f;
   down.N = h;
-  down.out = out;
+  down.out = pl.s_down > 1 ? (void*)part_down : out;
   down.act = ACT_NONE;
   down.out_f32 = out_f32;
+  down.ksplit = pl.s_down;
   MOE_TRY(launch_gemm(down, bf, st));
+  if (pl.s_down > 1 && !out_parts)
+    MOE_TRY(launch_ffn_finish(part_down, pl.s_down, R_max, h, ACT_NONE, offsets, E, bf && !out_f32, out, st));
   if (mark && !mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
@@ -203,7 +222,7 @@ size_t moe_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k
     return 0;
   const int64_t C = capacity_of(T, E, k, capacity_factor);
   Carve c(nullptr);
-  carve_layer(c, T, h, f, E, k, rows_max(T, E, k, C), dt);
+  carve_layer(c, T, h, f, E, k, rows_max(T, E, k, C), layer_plan(dt == MOE_BF16, T, h, f, E, k, C), dt, act);
   return c.bytes();
 }
 
@@ -290,6 +309,15 @@ moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int3
   return MOE_OK;
 }
 
+size_t moe_expert_ffn_workspace_bytes(int32_t R_max, int32_t h, int32_t f, int32_t E, moe_dtype_t dt,
+                                      moe_act_t act) {
+  if (R_max < 0 || E < 1 || E > 256 || h <= 0 || f <= 0 || !dtype_ok(dt) || !act_ok(act)) return 0;
+  const FfnPlan pl = plan_ffn(dt == MOE_BF16, (double)R_max / E, E, R_max, h, f);
+  Carve c(nullptr);
+  carve_ffn(c, pl, R_max, h, f, E, dt, act);
+  return c.bytes();
+}
+
 moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t R_max, int32_t h, int32_t f,
                             int32_t E, const void* W1, const void* W3, const void* W2, moe_act_t act,
                             moe_dtype_t dt, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -304,14 +332,14 @@ moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t 
   if (!aligned16(x_perm) || !aligned16(W1) || !aligned16(W2) || (W3 && !aligned16(W3)) || !aligned16(out_perm))
     return MOE_ERR_UNSUPPORTED;
   if (R_max == 0) return MOE_OK;
-  Carve c(ws);
-  FfnWs w = carve_ffn(c, R_max, f, E, dt);
-  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   const bool bf = dt == MOE_BF16;
-  const int bm = gemm_bm(bf, (double)R_max / E);
-  MOE_TRY(launch_tiles(offsets, E, bm, w.tile_off, stream));
-  return run_ffn(x_perm, nullptr, offsets, w.tile_off, bm, R_max, h, f, E, W1, W3, W2, act, dt, w.hm, out_perm,
-                 false, stream);
+  const FfnPlan pl = plan_ffn(bf, (double)R_max / E, E, R_max, h, f);
+  Carve c(ws);
+  FfnWs w = carve_ffn(c, pl, R_max, h, f, E, dt, act);
+  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  MOE_TRY(launch_tiles(offsets, E, pl.bm, w.tile_off, stream));
+  return run_ffn(x_perm, nullptr, offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, W2, act, dt, w.hm, w.part_up,
+                 out_perm, false, w.part_down, false, stream);
 }
 
 moe_status_t moe_unpermute(const void* out_perm, const int32_t* slot_pos, const float* topk_w, int32_t T,
@@ -324,7 +352,7 @@ moe_status_t moe_unpermute(const void* out_perm, const int32_t* slot_pos, const 
   if (!out_perm || !slot_pos || !topk_w || !y) return MOE_ERR_ARG;
   if (!aligned16(out_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  MOE_TRY(launch_combine(out_perm, dt == MOE_F32, slot_pos, topk_w, T, h, k, dt == MOE_BF16, y, stream));
+  MOE_TRY(launch_combine(out_perm, dt == MOE_F32, 1, 0, slot_pos, topk_w, T, h, k, dt == MOE_BF16, y, stream));
   return MOE_OK;
 }
 
@@ -345,10 +373,11 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   if (T == 0) return MOE_OK;
   const int64_t C = capacity_of(T, E, k, capacity_factor);
   const int R_max = rows_max(T, E, k, C);
-  Carve c(ws);
-  LayerWs w = carve_layer(c, T, h, f, E, k, R_max, dt);
-  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   const bool bf = dt == MOE_BF16;
+  const FfnPlan pl = layer_plan(bf, T, h, f, E, k, C);
+  Carve c(ws);
+  LayerWs w = carve_layer(c, T, h, f, E, k, R_max, pl, dt, act);
+  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   int stage = 0;
   auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
   if (!mark()) return MOE_ERR_DEVICE;
@@ -380,8 +409,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.T = T;
   sa.k = k;
   sa.C = (int)C;
-  const int bm = layer_bm(bf, T, E, k, C);
-  sa.BM = bm;
+  sa.BM = pl.bm;
   sa.prob_part = w.prob_part;
   sa.nrb = route_blocks(T);
   sa.prob_sum = nullptr;
@@ -395,10 +423,11 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
                          w.perm_token, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, bm, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
-                           w.o, bf, stream, ev ? [&]() { return mark(); } : std::function<bool()>());
+  moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
+                           w.part_up, w.o, true, w.o, true, stream,
+                           ev ? [&]() { return mark(); } : std::function<bool()>());
   if (r != MOE_OK) return r;
-  MOE_TRY(launch_combine(w.o, true, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
+  MOE_TRY(launch_combine(w.o, true, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
 }

@@ -18,7 +18,8 @@ namespace moe {
 namespace {
 
 template <typename OT, typename YT>
-__global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, const int* __restrict__ slot_pos,
+__global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, int parts, size_t part_stride,
+                                                      const int* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w, int T, int h, int k,
                                                       YT* __restrict__ y) {
   const int groups = h >> 3;
@@ -42,7 +43,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, 
         acc[2 * i + 1] += wj * __uint_as_float(v[i] & 0xFFFF0000u);
       }
     } else {
-      const floatx4 v0 = *(const floatx4*)src, v1 = *(const floatx4*)(src + 4);
+      floatx4 v0 = *(const floatx4*)src, v1 = *(const floatx4*)(src + 4);
+      for (int s = 1; s < parts; ++s) {  // K parts of a split down projection, ascending
+        v0 += *(const floatx4*)(src + s * part_stride);
+        v1 += *(const floatx4*)(src + s * part_stride + 4);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i] += wj * v0[i];
@@ -62,19 +67,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, 
 
 }  // namespace
 
-hipError_t launch_combine(const void* O, bool o_f32, const int* slot_pos, const float* topk_w, int T, int h,
-                          int k, bool bf16, void* y, hipStream_t st) {
+hipError_t launch_combine(const void* O, bool o_f32, int o_parts, size_t o_part_stride, const int* slot_pos,
+                          const float* topk_w, int T, int h, int k, bool bf16, void* y, hipStream_t st) {
+  if (o_parts < 1 || (o_parts > 1 && !o_f32)) return hipErrorInvalidValue;
   const int64_t n = (int64_t)T * (h / 8);
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (grid == 0) return hipSuccess;
   if (bf16 && o_f32)
-    hipLaunchKernelGGL((combine_kernel<float, bf16_t>), dim3(grid), dim3(256), 0, st, (const float*)O, slot_pos,
+    hipLaunchKernelGGL((combine_kernel<float, bf16_t>), dim3(grid), dim3(256), 0, st, (const float*)O, o_parts, o_part_stride, slot_pos,
                        topk_w, T, h, k, (bf16_t*)y);
   else if (bf16)
-    hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), dim3(grid), dim3(256), 0, st, (const bf16_t*)O, slot_pos,
+    hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), dim3(grid), dim3(256), 0, st, (const bf16_t*)O, 1, (size_t)0, slot_pos,
                        topk_w, T, h, k, (bf16_t*)y);
   else
-    hipLaunchKernelGGL((combine_kernel<float, float>), dim3(grid), dim3(256), 0, st, (const float*)O, slot_pos,
+    hipLaunchKernelGGL((combine_kernel<float, float>), dim3(grid), dim3(256), 0, st, (const float*)O, o_parts, o_part_stride, slot_pos,
                        topk_w, T, h, k, (float*)y);
   return hipGetLastError();
 }

@@ -66,7 +66,7 @@ struct GemmArgs {
   const void* W;        // [E, K, N] row-major
   const void* W3;       // [E, K, N] (SwiGLU gate partner) or null
   int K, N;             // N = columns of W = columns of out
-  void* out;            // [R_max, N]
+  void* out;            // [R_max, N]; with ksplit > 1 the fp32 partial sums (see below)
   const int* offsets;   // [E+1] rows per expert (device)
   const int* tile_off;  // [E+1] m-tiles per expert, exclusive scan (device)
   int E;
@@ -74,14 +74,32 @@ struct GemmArgs {
   int act;
   bool out_f32;         // bf16 GEMM writing fp32 output (down projection inside the layer)
   int bm;               // rows per m-tile (gemm_bm); tile_off must be built with it
+  // K split into ksplit equal parts (K / ksplit a multiple of 64).  With ksplit > 1
+  // the kernel writes raw fp32 partial products, part s at out + s * R_max * NW
+  // (row stride NW = 2N for SwiGLU -- W1 columns then W3 columns -- else N), and
+  // launch_ffn_finish / the combine add the parts in ascending s.
+  int ksplit;
 };
+
+// Tile height and K splits of one expert FFN (both GEMMs), a pure function of the sizes.
+struct FfnPlan {
+  int bm;       // rows per m-tile
+  int s_up;     // K splits of the up projection (1 = none)
+  int s_down;   // K splits of the down projection
+};
+FfnPlan plan_ffn(bool bf16, double rows_per_expert, int E, int R_max, int h, int f);
 // rows per m-tile of the expert GEMMs, from the expected rows per expert
 int gemm_bm(bool bf16, double rows_per_expert);
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t st);
+// out[r, :] = act(sum_s part[s][r][:N] (, sum_s part[s][r][N:2N])) for r < offsets[E];
+// act: ACT_NONE, ACT_GELU or ACT_SWIGLU; out is bf16 when out_bf16 else fp32.
+hipError_t launch_ffn_finish(const float* part, int S, int R_max, int N, int act, const int* offsets, int E,
+                             bool out_bf16, void* out, hipStream_t st);
 
 // ---- combine
-// O is fp32 when o_f32, else the y dtype
-hipError_t launch_combine(const void* O, bool o_f32, const int* slot_pos, const float* topk_w, int T, int h,
-                          int k, bool bf16, void* y, hipStream_t st);
+// O is fp32 when o_f32, else the y dtype.  With o_parts > 1 (fp32 only), O holds o_parts
+// partial sums of the expert outputs, part s at O + s * o_part_stride elements.
+hipError_t launch_combine(const void* O, bool o_f32, int o_parts, size_t o_part_stride, const int* slot_pos,
+                          const float* topk_w, int T, int h, int k, bool bf16, void* y, hipStream_t st);
 
 }  // namespace moe

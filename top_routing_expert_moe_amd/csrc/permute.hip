@@ -74,18 +74,57 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __shared__ int sh[256];
   __shared__ int cnt_sh[256];
   __shared__ double dsh[kScanThreads];
+  __shared__ int part_sh[kScanThreads];
   const int tid = threadIdx.x;
   const int E = a.E;
-  // per-expert running ranks over the blocks (blocks are few: T/64)
-  int cnt = 0;
-  if (tid < E) {
-    for (int b = 0; b < a.nhb; ++b) {
-      const int c = a.blk_counts[(size_t)b * E + tid];
-      a.blk_base[(size_t)b * E + tid] = cnt;
-      cnt += c;
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int P = kScanThreads / ep;  // threads per expert
+  // Per-expert running ranks over the blocks: thread (part, e) owns a contiguous range of
+  // blocks; it sums its range (independent loads, kept in registers when the range is
+  // short), the ranges' sums are scanned across parts, then each thread writes its
+  // range's exclusive ranks.
+  {
+    constexpr int kCache = 16;
+    const int e = tid % ep, part = tid / ep;
+    const int per = (a.nhb + P - 1) / P;
+    const int b0 = min(part * per, a.nhb), b1 = min(b0 + per, a.nhb);
+    int c[kCache];
+    int sum = 0;
+    if (e < E) {
+      if (per <= kCache) {
+#pragma unroll
+        for (int i = 0; i < kCache; ++i) c[i] = b0 + i < b1 ? a.blk_counts[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < kCache; ++i) sum += c[i];
+      } else {
+        for (int b = b0; b < b1; ++b) sum += a.blk_counts[(size_t)b * E + e];
+      }
     }
-    cnt_sh[tid] = cnt;
+    part_sh[tid] = sum;
+    __syncthreads();
+    int pre = 0;
+    for (int q = 0; q < part; ++q) pre += part_sh[q * ep + e];
+    if (e < E) {
+      if (part == P - 1) cnt_sh[e] = pre + sum;
+      if (per <= kCache) {
+#pragma unroll
+        for (int i = 0; i < kCache; ++i)
+          if (b0 + i < b1) {
+            a.blk_base[(size_t)(b0 + i) * E + e] = pre;
+            pre += c[i];
+          }
+      } else {
+        for (int b = b0; b < b1; ++b) {
+          const int v = a.blk_counts[(size_t)b * E + e];
+          a.blk_base[(size_t)b * E + e] = pre;
+          pre += v;
+        }
+      }
+    }
+    __syncthreads();
   }
+  const int cnt = tid < E ? cnt_sh[tid] : 0;
   const int kept = tid < E ? min(cnt, a.C) : 0;
   const int incl = block_inclusive_scan256(kept, sh);
   if (tid < E) {
@@ -103,9 +142,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
   if (a.aux != nullptr && (a.prob_part != nullptr || a.prob_sum != nullptr)) {
     // sum_t p[t,e]: P threads per expert each sum a strided set of blocks, then a fixed-order tree
-    int ep = 1;
-    while (ep < E) ep <<= 1;
-    const int P = kScanThreads / ep;
     const int e = tid % ep, part = tid / ep;
     double ps = 0.0;
     if (e < E) {

@@ -16,8 +16,9 @@
 //    wave streams 16 token rows straight from HBM into MFMA operands (no LDS);
 //    the planes ([3][E16][h], k-contiguous) are small and stay in L2.  For fp32
 //    activations a plain fp32 FMA kernel is used instead.
-//  * select.  One wave per token: lane e holds the logits of experts e, e+64,
-//    ...; softmax sums and k rounds of a 64-bit wave arg-max pick the experts.
+//  * select.  A group of lanes per token (a whole wave from 64 experts up): lane
+//    e holds the logits of experts e, e+64, ...; softmax sums and k rounds of a
+//    64-bit group arg-max pick the experts.
 //    The key orders by logit (IEEE order, -0 == +0) then by the lower expert
 //    index, so ties are deterministic.  The same kernel counts its block's
 //    assignments per expert (the histogram) and sums the softmax per expert.
@@ -60,15 +61,18 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
 }
 
 // ---------------------------------------------------------------------------
-// logits for bf16 x on MFMA.  Workgroup = 4 waves = TW token-waves x KS k-splits;
-// each wave: 16 tokens x NB*16 experts over h/KS.
-template <int NB, int TW>
-__global__ __launch_bounds__(256) void logits_mfma_kernel(const bf16_t* __restrict__ x,
+// logits for bf16 x on MFMA.  Workgroup = NW waves = TW token-waves x KS k-splits;
+// each wave: 16 tokens x NB*16 experts over h/KS.  Few experts: 16 waves split h 16 ways,
+// so each wave has a single batch of loads in flight and the kernel costs about one
+// memory round trip.
+template <int NB, int TW, int NW>
+__global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ planes,
                                                           const float* __restrict__ bias, int T, int h, int E,
                                                           int E16, float* __restrict__ logits) {
-  constexpr int KS = 4 / TW;
-  constexpr int U = NB >= 4 ? 2 : (NB == 2 ? 4 : 8);  // k-steps of 32 per batch of loads
+  constexpr int KS = NW / TW;
+  // k-steps of 32 per batch of loads (bounded by registers: 128 per lane at 16 waves)
+  constexpr int U = NB >= 4 ? 2 : (NB == 2 ? 4 : (NW > 4 ? 4 : 8));
   __shared__ floatx4 red[KS > 1 ? KS - 1 : 1][TW][NB][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -200,45 +204,61 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// selection: 64 tokens per workgroup, 16 per wave.
-template <int NV>
+// selection: 64 tokens per workgroup, 16 per wave.  A token is handled by a group of G
+// lanes (G = E rounded up to a power of two, at most 64; lane gl of the group holds
+// experts gl, gl + 64, ...), so a wave works on 64/G tokens at once.  All of a wave's
+// logits are loaded before any is used: the kernel costs one memory round trip.
+template <int NV, int G>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                      int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                      float* __restrict__ prob_part, int* __restrict__ blk_counts) {
+  static_assert(G == 64 || NV == 1, "several values per lane only with whole-wave groups");
+  constexpr int TPW = 64 / G;                // tokens per wave and pass
+  constexpr int NQ = kSelTokens / 4 / TPW;   // passes per wave
   __shared__ float pp[4][64 * NV];
   __shared__ int cnt[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t0 = blockIdx.x * kSelTokens;
+  const int sub = lane / G, gl = lane % G;
+  const int t0 = blockIdx.x * kSelTokens + w * (kSelTokens / 4);
   cnt[tid] = 0;
   __syncthreads();
+
+  float v[NQ][NV];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int t = t0 + q * TPW + sub;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = gl + 64 * i;
+      v[q][i] = e < E ? (t < T ? logits[(size_t)t * E + e] : 0.f) : -INFINITY;
+    }
+  }
   float psum[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = 0.f;
 
-  for (int q = 0; q < kSelTokens / 4; ++q) {
-    const int t = t0 + w * (kSelTokens / 4) + q;
-    if (t >= T) break;
-    float v[NV];
-    bool valid[NV];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int t = t0 + q * TPW + sub;
+    const bool tv = t < T;
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + 64 * i;
-      valid[i] = e < E;
-      v[i] = valid[i] ? logits[(size_t)t * E + e] : -INFINITY;
-      m = fmaxf(m, v[i]);
-    }
-    m = wave_max(m);
+    for (int i = 0; i < NV; ++i) m = fmaxf(m, v[q][i]);
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
     float ex[NV], s = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      ex[i] = valid[i] ? expf(v[i] - m) : 0.f;
+      ex[i] = gl + 64 * i < E ? expf(v[q][i] - m) : 0.f;
       s += ex[i];
     }
-    s = wave_sum(s);
-    const float inv = 1.0f / s;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) psum[i] += ex[i] * inv;
+    for (int o = G / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+    const float inv = 1.0f / s;
+    if (tv) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) psum[i] += ex[i] * inv;
+    }
 
     bool taken[NV];
 #pragma unroll
@@ -249,31 +269,42 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ l
       uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        if (valid[i] && !taken[i]) {
-          const uint64_t key = ((uint64_t)ordered_bits(v[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+        const int e = gl + 64 * i;
+        if (e < E && !taken[i]) {
+          const uint64_t key = ((uint64_t)ordered_bits(v[q][i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
           best = key > best ? key : best;
         }
       }
-      best = wave_max_u64(best);
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)best, o, kWave);
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, kWave);
+        const uint64_t b2 = ((uint64_t)hi << 32) | lo;
+        best = b2 > best ? b2 : best;
+      }
       const int e_sel = (int)(0xFFFFFFFFu - (uint32_t)best);
       const float l_sel = from_ordered((uint32_t)(best >> 32));
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        if (lane + 64 * i == e_sel) taken[i] = true;
+        if (gl + 64 * i == e_sel) taken[i] = true;
       if (j == 0) lmax = l_sel;
       wsum += expf(l_sel - lmax);
-      if (lane == j) { my_l = l_sel; my_e = e_sel; }
+      if (gl == j) { my_l = l_sel; my_e = e_sel; }
     }
-    if (lane < k) {
-      topk_idx[(size_t)t * k + lane] = my_e;
-      topk_w[(size_t)t * k + lane] = expf(my_l - lmax) / wsum;
+    if (tv && gl < k) {
+      topk_idx[(size_t)t * k + gl] = my_e;
+      topk_w[(size_t)t * k + gl] = expf(my_l - lmax) / wsum;
       if (blk_counts != nullptr) atomicAdd(&cnt[my_e], 1);
     }
   }
-  if (prob_part != nullptr) {
+  // the token groups of a wave hold partial sums of the same experts: add them (fixed tree)
 #pragma unroll
-    for (int i = 0; i < NV; ++i) pp[w][lane + 64 * i] = psum[i];
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int o = G; o < 64; o <<= 1) psum[i] += __shfl_xor(psum[i], o, kWave);
+  if (prob_part != nullptr && sub == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) pp[w][gl + 64 * i] = psum[i];
   }
   __syncthreads();
   if (prob_part != nullptr)
@@ -292,10 +323,10 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
   prob_sum[e] = s;
 }
 
-template <int NB, int TW>
+template <int NB, int TW, int NW = 4>
 void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st) {
   const dim3 grid((a.T + 16 * TW - 1) / (16 * TW), E16 / (16 * NB));
-  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW>), grid, dim3(256), 0, st, (const bf16_t*)a.x,
+  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
                      (const bf16_t*)a.planes, a.bias,
                      a.T, a.h, a.E, E16, a.logits);
 }
@@ -315,7 +346,8 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
                          E16, (bf16_t*)a.planes);
       // k split across waves needs h/KS to be a multiple of 32
       if (E16 <= 16) {
-        if (a.h % 128 == 0) launch_logits_mfma<1, 1>(a, E16, st);
+        if (a.h % 512 == 0) launch_logits_mfma<1, 1, 16>(a, E16, st);
+        else if (a.h % 128 == 0) launch_logits_mfma<1, 1>(a, E16, st);
         else launch_logits_mfma<1, 2>(a, E16, st);
       } else if (E16 == 32) {
         if (a.h % 128 == 0) launch_logits_mfma<2, 1>(a, E16, st);
@@ -353,15 +385,17 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
 
 hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
   const dim3 grid(route_blocks(a.T));
-  if (a.E <= 64)
-    hipLaunchKernelGGL(select_kernel<1>, grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w,
-                       a.prob_part, a.blk_counts);
-  else if (a.E <= 128)
-    hipLaunchKernelGGL(select_kernel<2>, grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w,
-                       a.prob_part, a.blk_counts);
-  else
-    hipLaunchKernelGGL(select_kernel<4>, grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w,
-                       a.prob_part, a.blk_counts);
+#define MOE_SELECT(NV, G)                                                                                      \
+  hipLaunchKernelGGL((select_kernel<NV, G>), grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w, \
+                     a.prob_part, a.blk_counts)
+  if (a.E <= 4) MOE_SELECT(1, 4);
+  else if (a.E <= 8) MOE_SELECT(1, 8);
+  else if (a.E <= 16) MOE_SELECT(1, 16);
+  else if (a.E <= 32) MOE_SELECT(1, 32);
+  else if (a.E <= 64) MOE_SELECT(1, 64);
+  else if (a.E <= 128) MOE_SELECT(2, 64);
+  else MOE_SELECT(4, 64);
+#undef MOE_SELECT
   return hipGetLastError();
 }
 
