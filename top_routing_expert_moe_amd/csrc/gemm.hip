@@ -93,9 +93,14 @@ constexpr int NIW = KB / 8;   // weight copies per thread per stage
 // of the current stage (issuing them early leaves them the most time to land; spreading
 // them keeps the MFMA issue from stalling behind a full memory queue).
 template <int BMT> struct TileCfg;
-template <> struct TileCfg<256> { static constexpr int WMW = 2, NSTAGE = 2, SPREAD = 8; };
-template <> struct TileCfg<128> { static constexpr int WMW = 1, NSTAGE = 3, SPREAD = 8; };
-template <> struct TileCfg<32> { static constexpr int WMW = 1, NSTAGE = 4, SPREAD = 8; };
+// NSTAGE counts activation stages; NSW weight stages (NSW = NSTAGE, or NSTAGE + 1 when a
+// third weight stage fits: the weights, streamed from HBM, then run two stages ahead).
+#ifndef MOE_NSW256
+#define MOE_NSW256 3
+#endif
+template <> struct TileCfg<256> { static constexpr int WMW = 2, NSTAGE = 2, NSW = MOE_NSW256, SPREAD = 8; };
+template <> struct TileCfg<128> { static constexpr int WMW = 1, NSTAGE = 3, NSW = 3, SPREAD = 8; };
+template <> struct TileCfg<32> { static constexpr int WMW = 1, NSTAGE = 4, NSW = 4, SPREAD = 8; };
 
 // Swizzles (16-byte chunk index XOR a function of the row):
 //  * weight stage rows are 256 n = 32 chunks; a transposing read touches rows
@@ -125,7 +130,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out,
     const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, int NT, int S, int R_max) {
   static_assert(!SPLIT || std::is_same<OT, float>::value, "K-split parts are fp32");
-  constexpr int NSTAGE = TileCfg<BMT>::NSTAGE, SPREAD = TileCfg<BMT>::SPREAD;
+  constexpr int NSTAGE = TileCfg<BMT>::NSTAGE, NSW = TileCfg<BMT>::NSW, SPREAD = TileCfg<BMT>::SPREAD;
+  static_assert(NSW == NSTAGE || (NSW == 3 && NSTAGE == 2), "stage counts");
   constexpr int WMW = TileCfg<BMT>::WMW, WNW = 4 / WMW;  // waves along m / along n
   constexpr int WTM = BMT / WMW, WTN = BN / WNW;          // wave tile
   constexpr int IB = WTN / 32, JB = WTM / 32;             // 32 x 32 MFMA blocks per wave
@@ -133,8 +139,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NIX = BMT / 32;                           // activation copies per thread per stage
   constexpr int CPS = NIW + NIX;                          // copies per thread per stage
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;     // output columns per tile
-  static_assert(NSTAGE * (WST + XST) * 2 <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) bf16_t Ws[NSTAGE][WST];
+  static_assert((NSW * WST + NSTAGE * XST) * 2 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) bf16_t Ws[NSW][WST];
   __shared__ __attribute__((aligned(1024))) bf16_t Xs[NSTAGE][XST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -197,20 +203,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ws_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Ws[0][0];
   const uint32_t xs_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Xs[0][0];
-  // the copies of one stage that belong to MFMA group `part` of `parts`: weight copy i
-  // and activation copy j go to groups i * sp / NIW and j * sp / NIX, sp = min(SPREAD,
-  // parts) (parts == 1: all of them)
-  auto issue_part = [&](int kt, int st, int part, int parts) {
+  // The copies that belong to MFMA group `part` of `parts` (parts == 1: all of them):
+  // activation copies of stage xkt into buffer xst (if xkt >= 0), then weight copies of
+  // stage wkt into buffer wst (if wkt >= 0).  With equal stage counts, weight copy i and
+  // activation copy j go to groups i * sp / NIW and j * sp / NIX, sp = min(SPREAD, parts);
+  // with a deeper weight pipeline the activation copies (needed first) take the first
+  // sp/2 groups and the weight copies the next sp.
+  auto issue_part = [&](int xkt, int xst, int wkt, int wst, int part, int parts) {
     const int sp = parts < SPREAD ? parts : SPREAD;
-#pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      if (i * sp / NIW == part)
-        copy_to_lds16(wsrc[i] + (size_t)kt * KB * N,
-                      ws_lds + 2u * (uint32_t)(st * WST + (2 * (NIW * uwave + i)) * BN));
+    const bool split = NSW != NSTAGE && parts > 1;
 #pragma unroll
     for (int i = 0; i < NIX; ++i)
-      if (i * sp / NIX == part)
-        copy_to_lds16(A + xsrc[i] + kt * KB, xs_lds + 2u * (uint32_t)(st * XST + 8 * (NIX * uwave + i) * KB));
+      if (xkt >= 0 && (split ? i * (sp / 2) / NIX : i * sp / NIX) == part)
+        copy_to_lds16(A + xsrc[i] + xkt * KB, xs_lds + 2u * (uint32_t)(xst * XST + 8 * (NIX * uwave + i) * KB));
+#pragma unroll
+    for (int i = 0; i < NIW; ++i)
+      if (wkt >= 0 && (split ? sp / 2 + i * sp / NIW : i * sp / NIW) == part)
+        copy_to_lds16(wsrc[i] + (size_t)wkt * KB * N,
+                      ws_lds + 2u * (uint32_t)(wst * WST + (2 * (NIW * uwave + i)) * BN));
   };
 
   // ---- fragment addressing (v_mfma_f32_32x32x16_bf16).  Wave (wn, wm) owns weight
@@ -249,11 +259,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // MFMAs of stage `st`; the copies of stage `nkt` (if >= 0) into buffer `nst` are
-  // issued in between, one share after each group of JB MFMAs.
-  auto compute = [&](int st, int nkt, int nst) {
-    const bf16_t* Wb = Ws[st];
-    const bf16_t* Xb = Xs[st];
+  // MFMAs of stage kt; the copies of later stages (see issue_part) are issued in
+  // between, one share after each group of JB MFMAs.
+  auto compute = [&](int kt, int xkt, int wkt) {
+    const bf16_t* Wb = Ws[kt % NSW];
+    const bf16_t* Xb = Xs[kt % NSTAGE];
     constexpr int PARTS = (KB / 16) * IB;
 #pragma unroll
     for (int kh = 0; kh < KB / 16; ++kh) {
@@ -271,27 +281,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb)
           acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
-        if (nkt >= 0) issue_part(nkt, nst, kh * IB + ib, PARTS);
+        issue_part(xkt, xkt % NSTAGE, wkt, wkt % NSW, kh * IB + ib, PARTS);
       }
     }
   };
 
-  // ---- pipeline: stage kt lives in LDS buffer kt % NSTAGE; the copies of stage
-  // kt + NSTAGE - 1 go into the buffer that the barrier of step kt has released.
-  // Each thread waits for its own copies of stage kt (newer stages may stay in
-  // flight), then the barrier makes every thread's copies visible.
+  // ---- pipeline: stage kt lives in activation buffer kt % NSTAGE and weight buffer
+  // kt % NSW.  During stage kt the activations of stage kt + NSTAGE - 1 and the weights of
+  // stage kt + NSW - 1 are copied, into the buffers that the barrier of step kt has
+  // released.  Each thread waits for its own copies of stage kt -- newer copies, issued
+  // after them, may stay in flight -- then the barrier makes every thread's copies visible.
   const int nk = Kc / KB;
 #pragma unroll
-  for (int p = 0; p < NSTAGE - 1; ++p)
-    if (p < nk) issue_part(p, p, 0, 1);
+  for (int p = 0; p < NSW - 1; ++p)
+    if (p < nk) issue_part(p < NSTAGE - 1 ? p : -1, p, p, p, 0, 1);
   for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = min(nk - 1 - kt, NSTAGE - 2);  // stages newer than kt already issued
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (NSW == NSTAGE) {
+      const int ahead = min(nk - 1 - kt, NSTAGE - 2);  // stages newer than kt already issued
+      if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
+      else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      // the newest copies are the weights of stage kt + 1 (issued after the activations
+      // of stage kt during step kt - 1, or in the prologue)
+      if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    const int nkt = kt + NSTAGE - 1 < nk ? kt + NSTAGE - 1 : -1;
-    compute(kt % NSTAGE, nkt, (kt + NSTAGE - 1) % NSTAGE);
+    const int xkt = kt + NSTAGE - 1 < nk ? kt + NSTAGE - 1 : -1;
+    const int wkt = kt + NSW - 1 < nk ? kt + NSW - 1 : -1;
+    compute(kt, xkt, wkt);
   }
 
   // ---- epilogue: lane holds token row 32*jb + (lane & 31) and, for acc element
