@@ -102,14 +102,17 @@ template <> struct TileCfg<256> { static constexpr int WMW = 2, NSTAGE = 2, NSW 
 template <> struct TileCfg<128> { static constexpr int WMW = 1, NSTAGE = 3, NSW = 3, SPREAD = 8; };
 template <> struct TileCfg<32> { static constexpr int WMW = 1, NSTAGE = 4, NSW = 4, SPREAD = 8; };
 
-// Swizzles (16-byte chunk index XOR a function of the row):
-//  * weight stage rows are 256 n = 32 chunks; a transposing read touches rows
-//    8g + 4h + t (g, t = 0..3) at one chunk pair, so f spreads t and g over 16
-//    distinct even values;
-//  * activation stage rows are 64 k = 8 chunks; the 16 lanes read together touch 16
-//    consecutive rows at one chunk, so f spreads (row >> 1) over the 8 chunks.
-__device__ __forceinline__ int wswz(int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) << 1; }
-__device__ __forceinline__ int xswz(int r) { return (r >> 1) & 7; }
+// Swizzles (16-byte chunk index XOR a function of the row).  The LDS serves 256 bytes
+// (64 banks) per cycle, i.e. 32 lanes of an 8-byte read or 16 lanes of a 16-byte read:
+//  * weight stage rows are 256 n = 32 chunks.  The 32 lanes of a transposing read
+//    served together touch rows r0 .. r0+3 (r0 a multiple of 4) at chunks 4b .. 4b+3;
+//    XOR-ing with 2*(r & 3) ^ 4*(r & 3) gives each row a distinct 64-byte bank group;
+//  * activation stage rows are 64 k = 8 chunks (128 B).  The 16 lanes read together touch
+//    16 consecutive rows at one chunk; rows of equal parity share banks, so the XOR value
+//    (r & 7) ^ ((r >> 3) & 1) is distinct across the 8 rows of either parity.
+// (Measured with rocprofv3: no LDS bank-conflict cycles in either GEMM.)
+__device__ __forceinline__ int wswz(int r) { return ((r & 3) << 1) ^ ((r & 3) << 2); }
+__device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // One 16-byte-per-lane copy from global memory straight into LDS (the wave's 1 KiB
 // block starts at the LDS byte address in m0).  Issued as a plain instruction so that
