@@ -124,14 +124,17 @@ __device__ __forceinline__ void copy_to_lds16(const void* gptr, uint32_t lds_blo
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_block) : "memory", "m0");
 }
 
-// SPLIT: the workgroup covers one of S equal parts of K and writes its raw fp32
-// accumulators to part s of `out` (row stride NW = 2N for SwiGLU, else N; parts
-// R_max rows apart); the activation is applied when the parts are added.
+constexpr int kSmemBytes = 160 * 1024;  // LDS of the largest tile shape
+
+// One tile of BMT rows (row0 .. row_end-1 of expert e) x 256 weight columns from n0, over
+// k in [ks * Kc, ks * Kc + Kc).  SPLIT: the raw fp32 accumulators go to K part ks of
+// `out` (row stride NW = 2N for SwiGLU, else N; parts R_max rows apart) and the
+// activation is applied when the parts are added.
 template <int BMT, int ACT, bool GATHER, typename OT, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
-    const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out,
-    const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, int NT, int S, int R_max) {
+__device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__ A, const int* __restrict__ a_rows,
+                                          const bf16_t* __restrict__ W, const bf16_t* __restrict__ W3, int K,
+                                          int N, OT* __restrict__ out, int R_max, int e, int row0, int row_end,
+                                          int n0, int ks, int Kc) {
   static_assert(!SPLIT || std::is_same<OT, float>::value, "K-split parts are fp32");
   constexpr int NSTAGE = TileCfg<BMT>::NSTAGE, NSW = TileCfg<BMT>::NSW, SPREAD = TileCfg<BMT>::SPREAD;
   static_assert(NSW == NSTAGE || (NSW == 3 && NSTAGE == 2), "stage counts");
@@ -142,33 +145,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NIX = BMT / 32;                           // activation copies per thread per stage
   constexpr int CPS = NIW + NIX;                          // copies per thread per stage
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;     // output columns per tile
-  static_assert((NSW * WST + NSTAGE * XST) * 2 <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) bf16_t Ws[NSW][WST];
-  __shared__ __attribute__((aligned(1024))) bf16_t Xs[NSTAGE][XST];
+  static_assert((NSW * WST + NSTAGE * XST) * 2 <= kSmemBytes, "LDS");
+  bf16_t(*Ws)[WST] = reinterpret_cast<bf16_t(*)[WST]>(smem);
+  bf16_t(*Xs)[XST] = reinterpret_cast<bf16_t(*)[XST]>(smem + NSW * WST * 2);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // ---- tile schedule (XCD-aware), exits for surplus workgroups
-  const int MT = tile_off[E];
-  const int n_tiles = MT * NT;
-  const int n_real = n_tiles * (SPLIT ? S : 1);
-  const int per = (n_real + 7) >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  if (slot >= per) return;
-  const int L = xcd * per + slot;
-  if (L >= n_real) return;
-  int e, mt_local, nt;
-  int ks = 0;  // K part
-  int Lt = L;
-  if (SPLIT) {
-    ks = L / n_tiles;
-    Lt = L - ks * n_tiles;
-  }
-  tile_of(Lt, tile_off, E, NT, e, mt_local, nt);
-  const int Kc = SPLIT ? K / S : K;  // this workgroup's k range: [ks * Kc, ks * Kc + Kc)
-  const int row0 = offsets[e] + mt_local * BMT;
-  const int row_end = min(row0 + BMT, offsets[e + 1]);
-  const int n0 = nt * NO;
 
   // ---- copy plan.  One wave instruction moves 1 KiB: lane l writes LDS bytes
   // [16l, 16l+16) of the instruction's block, i.e. swizzle slot (l & 31) of weight
@@ -375,6 +356,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// The grouped GEMM over all experts in one launch.  The tile list (device-side
+// tile_off, built with fh rows per m-tile) and the XCD-aware order give each workgroup
+// an (expert, m-tile, n-tile[, K part]); the tile's code path is chosen by the rows it
+// really has: an expert's last m-tile with few rows runs the 128- or 32-row shape
+// instead of computing on padding.
+template <int ACT, bool GATHER, typename OT, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
+    const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
+    const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
+    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
+  // ---- tile schedule (XCD-aware), exits for surplus workgroups
+  const int MT = tile_off[E];
+  const int n_tiles = MT * NT;
+  const int n_real = n_tiles * (SPLIT ? S : 1);
+  const int per = (n_real + 7) >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  if (slot >= per) return;
+  const int L = xcd * per + slot;
+  if (L >= n_real) return;
+  int e, mt_local, nt;
+  int ks = 0;  // K part
+  int Lt = L;
+  if (SPLIT) {
+    ks = L / n_tiles;
+    Lt = L - ks * n_tiles;
+  }
+  tile_of(Lt, tile_off, E, NT, e, mt_local, nt);
+  const int Kc = SPLIT ? K / S : K;  // this workgroup's k range: [ks * Kc, ks * Kc + Kc)
+  const int row0 = offsets[e] + mt_local * fh;
+  const int rows = min(fh, offsets[e + 1] - row0);
+  const int n0 = nt * NO;
+  if (rows > 128)
+    gemm_tile<256, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc);
+  else if (rows > 32)
+    gemm_tile<128, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc);
+  else
+    gemm_tile<32, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 grouped GEMM on the vector ALUs (fp32 workloads: exact fp32 products,
 // fp32 accumulation).  Tile 64 rows x 64 columns x 16 k, 4x4 per thread.
@@ -461,38 +483,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   }
 }
 
-template <int BMT, int ACT, bool G, typename OT, bool SPLIT>
-hipError_t launch_bf16_bm(const GemmArgs& a, hipStream_t st) {
+template <int ACT, bool G, typename OT, bool SPLIT>
+hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;
   const int NT = (a.N + NO - 1) / NO;
   const int S = SPLIT ? a.ksplit : 1;
-  const long long slots = ((long long)(a.R_max + BMT - 1) / BMT + a.E) * NT * S;
+  const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BMT, ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(256), 0, st,
                      (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                     (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max);
+                     (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm);
   return hipGetLastError();
 }
 
 template <int ACT, bool G, typename OT>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
+  if (a.bm != 256 && a.bm != 128 && a.bm != 32) return hipErrorInvalidValue;
   if (a.ksplit > 1) {
-    // K parts: only for the small tiles, where there are too few tiles to fill the chip
+    // K parts: for few rows per expert, where there are too few tiles to fill the chip
     if (a.K % (a.ksplit * KB) != 0) return hipErrorInvalidValue;
     constexpr int PA = ACT == ACT_SWIGLU ? ACT_SWIGLU : ACT_NONE;  // part layout
-    switch (a.bm) {
-      case 128: return launch_bf16_bm<128, PA, G, float, true>(a, st);
-      case 32: return launch_bf16_bm<32, PA, G, float, true>(a, st);
-    }
-    return hipErrorInvalidValue;
+    return launch_bf16_k<PA, G, float, true>(a, st);
   }
-  switch (a.bm) {
-    case 256: return launch_bf16_bm<256, ACT, G, OT, false>(a, st);
-    case 128: return launch_bf16_bm<128, ACT, G, OT, false>(a, st);
-    case 32: return launch_bf16_bm<32, ACT, G, OT, false>(a, st);
-  }
-  return hipErrorInvalidValue;
+  return launch_bf16_k<ACT, G, OT, false>(a, st);
 }
 
 // Adds the K parts of a split GEMM in ascending order and applies the activation.
