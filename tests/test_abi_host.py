@@ -76,7 +76,8 @@ def test_workspace_bytes(L):
         R = T * k if C is None else min(T * k, E * C)
         need = R * f * es + R * h * 4  # hidden activation + fp32 expert outputs
         assert b >= need
-        assert b < need + 64 * T * k + 16 * T * E + 8 * h * E + 2 ** 20
+        # the down projection may keep two fp32 K parts of the expert outputs
+        assert b < need + R * h * 4 + 64 * T * k + 16 * T * E + 8 * h * E + 2 ** 20
     # a capacity below the mean load (E*C < T*k) shrinks the bound on kept rows
     assert moe.workspace_bytes(8192, 1024, 4096, 64, 2, 0.5, 1, 0) < moe.workspace_bytes(8192, 1024, 4096, 64, 2,
                                                                                            0.0, 1, 0)

@@ -31,6 +31,7 @@
 //    contiguous range of the tile list, which is ordered in 4 x 8 groups of
 //    (m-tile, n-tile) inside each expert, so the workgroups running together in
 //    one XCD share activation and weight tiles in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -584,24 +585,38 @@ hipError_t launch_ffn_finish(const float* part, int S, int R_max, int N, int act
 
 FfnPlan plan_ffn(bool bf16, double rows_per_expert, int E, int R_max, int h, int f) {
   FfnPlan p{gemm_bm(bf16, rows_per_expert), 1, 1};
-  if (!bf16 || p.bm != 32) return p;
-  // Few rows per expert: the GEMMs stream weights.  When there are fewer tiles than two
-  // per CU (one 256-column tile per expert and column block: the down projection at
-  // decode shapes), split K until there are about four per CU.  (Measured at T = 64,
-  // h = 4096, f = 14336, E = 8: the down projection gains ~10 %; splitting the
-  // up projection's 896 tiles further only adds partial-sum traffic.)
-  double mt = (double)E * ceil(rows_per_expert / p.bm);  // expected m-tiles
+  if (!bf16) return p;
+  constexpr double kCUs = 256.0;
   const double mt_max = ceil((double)R_max / p.bm) + E;
-  if (mt > mt_max) mt = mt_max;
-  auto split = [&](int K, int N, int no) {
-    const double tiles = mt * ceil((double)N / no);
-    int S = 1;
-    if (tiles >= 512.0) return S;
-    while (S < 16 && tiles * S < 1024.0 && K % (2 * S * KB) == 0 && K / (2 * S) >= 8 * KB) S *= 2;
-    return S;
+  if (p.bm == 32) {
+    // Few rows per expert: the GEMMs stream weights.  When there are fewer tiles than two
+    // per CU (one 256-column tile per expert and column block: the down projection at
+    // decode shapes), split K until there are about four per CU.  (Measured at T = 64,
+    // h = 4096, f = 14336, E = 8: the down projection gains ~10 %; splitting the
+    // up projection's 896 tiles further only adds partial-sum traffic.)
+    const double mt = std::min((double)E * ceil(rows_per_expert / p.bm), mt_max);  // expected m-tiles
+    auto split = [&](int K, int N, int no) {
+      const double tiles = mt * ceil((double)N / no);
+      int S = 1;
+      if (tiles >= 2 * kCUs) return S;
+      while (S < 16 && tiles * S < 4 * kCUs && K % (2 * S * KB) == 0 && K / (2 * S) >= 8 * KB) S *= 2;
+      return S;
+    };
+    p.s_up = split(h, f, BN / 2);
+    p.s_down = split(f, h, BN);
+    return p;
+  }
+  // Larger tiles: the last round of tiles may leave many CUs idle (the down projection
+  // has only h/256 column blocks per m-tile).  Expected m-tiles: half a tile of padding
+  // per expert on top of the rows.  Split the down projection's K in two when that
+  // fills the last round markedly better; its two fp32 parts are added by the combine.
+  const double mt = std::min((double)E * (rows_per_expert / p.bm + 0.5), mt_max);
+  auto fill = [&](double tiles) {
+    const double r = tiles / kCUs;
+    return r / ceil(r);
   };
-  p.s_up = split(h, f, BN / 2);
-  p.s_down = split(f, h, BN);
+  const double tiles_down = mt * ceil((double)h / BN);
+  if (f % (2 * KB) == 0 && f / 2 >= 16 * KB && fill(2 * tiles_down) > fill(tiles_down) + 0.08) p.s_down = 2;
   return p;
 }
 
