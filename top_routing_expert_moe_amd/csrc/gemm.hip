@@ -84,12 +84,18 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 constexpr int KB = 64;    // k per LDS stage (4 MFMA k-steps of 16)
 constexpr int WST = KB * BN;  // weight stage, elements: [64 k][256 n], n contiguous
 constexpr int XCH = KB / 8;   // 16-byte chunks per activation row
-constexpr int NIW = KB / 8;   // weight copies per thread per stage
+#ifndef MOE_WAVES
+#define MOE_WAVES 8
+#endif
+constexpr int kWaves = MOE_WAVES;  // waves per workgroup: two per SIMD
+constexpr int NIW = 32 / kWaves;   // weight copies (1 KiB each, 32 per stage) per wave and stage
 
 // Tile shapes by token-tile height: the wave grid (waves along m x along n) and the
-// number of LDS stages that fit.  256 rows: 2 x 2 waves of 128 x 128 (prefill);
-// 128 and 32 rows: 1 x 4 waves of BM x 64 (few rows per expert: the weights dominate,
-// so the deeper pipeline keeps more weight bytes in flight).
+// number of LDS stages that fit.  Eight waves, two per SIMD: while one waits on a barrier,
+// an LDS read or a copy, the other issues MFMAs.  256 rows: 4 x 2 waves of 64 x 128
+// (prefill); 128 rows: 2 x 4 waves of 64 x 64; 32 rows: 1 x 4 waves of 32 x 64 compute
+// (the other four only copy: these tiles stream weights, and the deeper pipeline keeps
+// more weight bytes in flight).
 // SPREAD: the next stage's copies are issued between the first SPREAD groups of MFMAs
 // of the current stage (issuing them early leaves them the most time to land; spreading
 // them keeps the MFMA issue from stalling behind a full memory queue).
@@ -99,9 +105,13 @@ template <int BMT> struct TileCfg;
 #ifndef MOE_NSW256
 #define MOE_NSW256 3
 #endif
-template <> struct TileCfg<256> { static constexpr int WMW = 2, NSTAGE = 2, NSW = MOE_NSW256, SPREAD = 8; };
-template <> struct TileCfg<128> { static constexpr int WMW = 1, NSTAGE = 3, NSW = 3, SPREAD = 8; };
-template <> struct TileCfg<32> { static constexpr int WMW = 1, NSTAGE = 4, NSW = 4, SPREAD = 8; };
+template <> struct TileCfg<256> {
+  static constexpr int WMW = kWaves == 8 ? 4 : 2, WNW = 2, NSTAGE = 2, NSW = MOE_NSW256, SPREAD = 8;
+};
+template <> struct TileCfg<128> {
+  static constexpr int WMW = kWaves == 8 ? 2 : 1, WNW = 4, NSTAGE = 3, NSW = 3, SPREAD = 8;
+};
+template <> struct TileCfg<32> { static constexpr int WMW = 1, WNW = 4, NSTAGE = 4, NSW = 4, SPREAD = 8; };
 
 // Swizzles (16-byte chunk index XOR a function of the row).  The LDS serves 256 bytes
 // (64 banks) per cycle, i.e. 32 lanes of an 8-byte read or 16 lanes of a 16-byte read:
@@ -139,18 +149,23 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   static_assert(!SPLIT || std::is_same<OT, float>::value, "K-split parts are fp32");
   constexpr int NSTAGE = TileCfg<BMT>::NSTAGE, NSW = TileCfg<BMT>::NSW, SPREAD = TileCfg<BMT>::SPREAD;
   static_assert(NSW == NSTAGE || (NSW == 3 && NSTAGE == 2), "stage counts");
-  constexpr int WMW = TileCfg<BMT>::WMW, WNW = 4 / WMW;  // waves along m / along n
-  constexpr int WTM = BMT / WMW, WTN = BN / WNW;          // wave tile
-  constexpr int IB = WTN / 32, JB = WTM / 32;             // 32 x 32 MFMA blocks per wave
-  constexpr int XST = BMT * KB;                           // activation stage elements
-  constexpr int NIX = BMT / 32;                           // activation copies per thread per stage
-  constexpr int CPS = NIW + NIX;                          // copies per thread per stage
+  constexpr int WMW = TileCfg<BMT>::WMW, WNW = TileCfg<BMT>::WNW;  // waves along m / along n
+  constexpr int NCW = WMW * WNW;                                   // waves with MFMA work
+  static_assert(NCW <= kWaves, "wave grid");
+  constexpr int WTM = BMT / WMW, WTN = BN / WNW;  // wave tile
+  constexpr int IB = WTN / 32, JB = WTM / 32;     // 32 x 32 MFMA blocks per wave
+  constexpr int XST = BMT * KB;                   // activation stage elements
+  constexpr int XI = BMT / 8;                     // activation copies (1 KiB each) per stage
+  constexpr int NIX = (XI + kWaves - 1) / kWaves; // ... per wave (waves past XI / NIX have none)
+  static_assert(XI % NIX == 0, "activation copies");
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;     // output columns per tile
   static_assert((NSW * WST + NSTAGE * XST) * 2 <= kSmemBytes, "LDS");
   bf16_t(*Ws)[WST] = reinterpret_cast<bf16_t(*)[WST]>(smem);
   bf16_t(*Xs)[XST] = reinterpret_cast<bf16_t(*)[XST]>(smem + NSW * WST * 2);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+  const bool has_x = NIX * uwave < XI;  // this wave copies activations
 
   // ---- copy plan.  One wave instruction moves 1 KiB: lane l writes LDS bytes
   // [16l, 16l+16) of the instruction's block, i.e. swizzle slot (l & 31) of weight
@@ -185,7 +200,6 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     const int src_row = GATHER ? a_rows[rr] : rr;
     xsrc[i] = (uint32_t)src_row * (uint32_t)K + (uint32_t)(ks * Kc) + (uint32_t)((((lane % XCH) ^ xswz(xr))) << 3);
   }
-  const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ws_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Ws[0][0];
   const uint32_t xs_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Xs[0][0];
   // The copies that belong to MFMA group `part` of `parts` (parts == 1: all of them):
@@ -199,7 +213,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     const bool split = NSW != NSTAGE && parts > 1;
 #pragma unroll
     for (int i = 0; i < NIX; ++i)
-      if (xkt >= 0 && (split ? i * (sp / 2) / NIX : i * sp / NIX) == part)
+      if (xkt >= 0 && has_x && (split ? i * (sp / 2) / NIX : i * sp / NIX) == part)
         copy_to_lds16(A + xsrc[i] + xkt * KB, xs_lds + 2u * (uint32_t)(xst * XST + 8 * (NIX * uwave + i) * KB));
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
@@ -250,22 +264,27 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     const bf16_t* Wb = Ws[kt % NSW];
     const bf16_t* Xb = Xs[kt % NSTAGE];
     constexpr int PARTS = (KB / 16) * IB;
+    const bool mf = NCW == kWaves || uwave < NCW;  // waves past the grid only copy
 #pragma unroll
     for (int kh = 0; kh < KB / 16; ++kh) {
       bf16x8 a[IB], b[JB];
+      if (mf) {
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) b[jb] = *(const bf16x8*)&Xb[boff[kh] + jb * 32 * KB];
+        for (int jb = 0; jb < JB; ++jb) b[jb] = *(const bf16x8*)&Xb[boff[kh] + jb * 32 * KB];
 #pragma unroll
-      for (int ib = 0; ib < IB; ++ib) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][0][ib]]);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][1][ib]]);
-        a[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int ib = 0; ib < IB; ++ib) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][0][ib]]);
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)&Wb[aoff[kh][1][ib]]);
+          a[ib] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
 #pragma unroll
       for (int ib = 0; ib < IB; ++ib) {
+        if (mf) {
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
-          acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
+          for (int jb = 0; jb < JB; ++jb)
+            acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
+        }
         issue_part(xkt, xkt % NSTAGE, wkt, wkt % NSW, kh * IB + ib, PARTS);
       }
     }
@@ -282,10 +301,17 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     if (p < nk) issue_part(p < NSTAGE - 1 ? p : -1, p, p, p, 0, 1);
   for (int kt = 0; kt < nk; ++kt) {
     if (NSW == NSTAGE) {
-      const int ahead = min(nk - 1 - kt, NSTAGE - 2);  // stages newer than kt already issued
-      if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
-      else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // stages newer than kt already issued, NIW (+ NIX) copies each
+      const int ahead = min(nk - 1 - kt, NSTAGE - 2);
+      if (has_x) {
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIW + NIX)) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW + NIX) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIW) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
     } else {
       // the newest copies are the weights of stage kt + 1 (issued after the activations
       // of stage kt during step kt - 1, or in the prologue)
@@ -300,6 +326,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 
   // ---- epilogue: lane holds token row 32*jb + (lane & 31) and, for acc element
   // 4q+p, weight column 32*ib + 8q + 4*(lane >> 5) + p of its wave's columns.
+  if (NCW < kWaves && uwave >= NCW) return;
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb) {
     const int r = row0 + wm * WTM + jb * 32 + l31;
@@ -363,7 +390,8 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 // really has: an expert's last m-tile with few rows runs the 128- or 32-row shape
 // instead of computing on padding.
 template <int ACT, bool GATHER, typename OT, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void
+gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
     const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh) {
@@ -492,7 +520,7 @@ hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                      (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
                      (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm);
   return hipGetLastError();
