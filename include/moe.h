@@ -83,9 +83,12 @@ const char* moe_status_string(moe_status_t s);
  *   topk_idx [T,k] int32: slot j = j-th best expert; order (logit desc, expert asc)
  *   topk_w   [T,k] fp32: softmax of the selected logits (sums to 1 per token)
  *   prob_sum [E] fp32 or NULL: sum over tokens of the full softmax (for the aux loss)
- *   ws: scratch for the split router weights (bf16 x: 6*ceil(E/16)*16*h bytes) and for
- *       per-block softmax sums (prob_sum: 4*ceil(T/64)*E bytes), each rounded up to 256,
- *       plus 256; may be NULL for fp32 x (or MOE_ROUTE_LOGITS_IN) without prob_sum. */
+ *   ws: at least moe_route_workspace_bytes(T,h,E,dt,flags,prob_sum != NULL) bytes: the
+ *       split router weights and, for few tokens, partial logits (bf16 x), and per-block
+ *       softmax sums (prob_sum); may be NULL when that is 0 (fp32 x or MOE_ROUTE_LOGITS_IN,
+ *       without prob_sum). */
+size_t moe_route_workspace_bytes(int32_t T, int32_t h, int32_t E, moe_dtype_t dt, uint32_t flags,
+                                 int32_t with_prob_sum);  /* 0 for invalid sizes */
 moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bias,
                        int32_t T, int32_t h, int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags,
                        float* logits, int32_t* topk_idx, float* topk_w, float* prob_sum,

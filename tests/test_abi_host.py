@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol(L):
     names = _declared()
     assert set(names) == {"moe_capacity", "moe_workspace_bytes", "moe_status_string", "moe_route",
                           "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_forward",
-                          "moe_layer_forward_timed", "moe_expert_ffn_workspace_bytes"}
+                          "moe_layer_forward_timed", "moe_expert_ffn_workspace_bytes",
+                          "moe_route_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -90,6 +91,13 @@ def test_workspace_bytes(L):
     assert 128 * 14336 * 2 <= fb <= b
     assert L.moe_expert_ffn_workspace_bytes(8192, 4096, 14336, 8, 1, 1) >= 8192 * 14336 * 2
     assert L.moe_expert_ffn_workspace_bytes(-1, 64, 64, 8, 1, 1) == 0
+    # router: split weights (bf16 x) plus, for few tokens, partial logits; nothing for fp32 x
+    rb = L.moe_route_workspace_bytes(64, 4096, 8, 1, 0, 0)
+    assert rb >= 6 * 16 * 4096 + 32 * 64 * 8 * 4
+    assert L.moe_route_workspace_bytes(4096, 4096, 8, 1, 0, 0) < rb + 2 ** 12
+    assert L.moe_route_workspace_bytes(64, 4096, 8, 0, 0, 0) <= 256
+    assert L.moe_route_workspace_bytes(64, 4096, 8, 1, 1, 0) <= 256     # logits given
+    assert L.moe_route_workspace_bytes(64, 4096, 300, 1, 0, 0) == 0
     assert L.moe_expert_ffn_workspace_bytes(8, 64, 64, 300, 1, 1) == 0
     assert moe.workspace_bytes(8, 64, 64, 300, 2, 0.0, 1, 0) == 0   # E > 256
     assert moe.workspace_bytes(8, 64, 64, 8, 9, 0.0, 1, 0) == 0     # k > E

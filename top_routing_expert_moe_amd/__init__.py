@@ -35,6 +35,7 @@ _SIGS = {
     "moe_capacity": (_i32, [_i32, _i32, _i32, _f32]),
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int]),
+    "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32, ctypes.c_int, ctypes.c_uint32, _i32]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, ctypes.c_int,
                                  ctypes.c_uint32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz,
@@ -155,9 +156,8 @@ def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = F
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     ps = torch.empty(E, dtype=torch.float32, device=dev) if with_prob_sum else None
-    need = (4 * (-(-T // 64)) * E + 256 if with_prob_sum else 0) + \
-        (6 * (-(-E // 16)) * 16 * h + 256 if (logits is None and dt == BF16) else 0)
-    ws = _ws(need + 256, dev) if need else None
+    need = lib().moe_route_workspace_bytes(T, h, E, dt, flags, 1 if with_prob_sum else 0)
+    ws = _ws(need, dev) if need else None
     st = lib().moe_route(None if logits is not None else _p(x), None if logits is not None else _p(W_gate),
                          None if (logits is not None or logit_bias is None) else _p(logit_bias),
                          T, h, E, k, dt, flags, _p(out_logits), _p(idx), _p(w), _p(ps),

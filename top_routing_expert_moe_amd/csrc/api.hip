@@ -83,7 +83,7 @@ struct RouteWs { float* prob_part; uint16_t* planes; };
 RouteWs carve_route(Carve& c, int32_t T, int32_t h, int32_t E, bool prob, bool planes) {
   RouteWs w;
   w.prob_part = prob ? c.take<float>((size_t)route_blocks(T) * E) : nullptr;
-  w.planes = planes ? c.take<uint16_t>((size_t)route_planes_elems(h, E)) : nullptr;
+  w.planes = planes ? (uint16_t*)c.take<char>(route_scratch_bytes(T, h, E, true)) : nullptr;
   return w;
 }
 
@@ -121,7 +121,7 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
   LayerWs w;
   const size_t n = (size_t)T * k;
   const size_t nhb = (size_t)route_blocks(T);
-  w.planes = dt == MOE_BF16 ? c.take<uint16_t>((size_t)route_planes_elems(h, E)) : nullptr;
+  w.planes = dt == MOE_BF16 ? (uint16_t*)c.take<char>(route_scratch_bytes(T, h, E, true)) : nullptr;
   w.logits = c.take<float>((size_t)T * E);
   w.topk_idx = c.take<int>(n);
   w.topk_w = c.take<float>(n);
@@ -223,6 +223,15 @@ size_t moe_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k
   const int64_t C = capacity_of(T, E, k, capacity_factor);
   Carve c(nullptr);
   carve_layer(c, T, h, f, E, k, rows_max(T, E, k, C), layer_plan(dt == MOE_BF16, T, h, f, E, k, C), dt, act);
+  return c.bytes();
+}
+
+size_t moe_route_workspace_bytes(int32_t T, int32_t h, int32_t E, moe_dtype_t dt, uint32_t flags,
+                                 int32_t with_prob_sum) {
+  if (T < 0 || E < 1 || E > 256 || h < 0 || !dtype_ok(dt)) return 0;
+  const bool lin = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+  Carve c(nullptr);
+  carve_route(c, T, h, E, with_prob_sum != 0, !lin && dt == MOE_BF16);
   return c.bytes();
 }
 

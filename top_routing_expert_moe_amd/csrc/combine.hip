@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, 
       }
     } else {
       floatx4 v0 = *(const floatx4*)src, v1 = *(const floatx4*)(src + 4);
+#pragma unroll 8
       for (int s = 1; s < parts; ++s) {  // K parts of a split down projection, ascending
         v0 += *(const floatx4*)(src + s * part_stride);
         v1 += *(const floatx4*)(src + s * part_stride + 4);

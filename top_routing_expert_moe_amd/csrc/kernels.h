@@ -22,9 +22,12 @@ struct RouteArgs {
   float* topk_w;          // [T,k]
   float* prob_part;       // [route_blocks(T), E] or null
   int* blk_counts;        // [route_blocks(T), E] or null: per-block expert histogram
-  uint16_t* planes;       // bf16 x: [3][E16][h] bf16 scratch for the split router weights
+  uint16_t* planes;       // bf16 x: route_scratch_bytes of scratch -- [3][E16][h] bf16 split router
+                          // weights, then (few tokens) [SH][T][E] fp32 partial logits
 };
 int route_planes_elems(int h, int E);
+int route_hsplit(int T, int h, int E, bool bf16);              // h-split of the logits (1 = none)
+size_t route_scratch_bytes(int T, int h, int E, bool bf16);   // bytes behind RouteArgs::planes
 int route_blocks(int T);
 hipError_t launch_logits(const RouteArgs& a, hipStream_t st);  // logits only (ignores logits_in)
 hipError_t launch_select(const RouteArgs& a, hipStream_t st);  // softmax, top-k, weights, histogram

@@ -70,28 +70,46 @@ __device__ int block_inclusive_scan256(int v, int* sh) {
 
 constexpr int kScanThreads = 1024;
 
+__device__ __forceinline__ int wave_incl_scan(int v, int lane, int width) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (o < width && (lane % width) >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// One workgroup: per-(block, expert) rank origins, pre-drop counts, capacity-clamped
+// offsets, the m-tile list and the aux loss.  Every sum has a fixed order (wave shuffles
+// and LDS in index order), so the results do not vary from run to run.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
-  __shared__ int sh[256];
   __shared__ int cnt_sh[256];
-  __shared__ double dsh[kScanThreads];
-  __shared__ int part_sh[kScanThreads];
-  const int tid = threadIdx.x;
+  __shared__ int wsum[2][4];
+  __shared__ double dterm[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
   int ep = 1;
   while (ep < E) ep <<= 1;
-  const int P = kScanThreads / ep;  // threads per expert
-  // Per-expert running ranks over the blocks: thread (part, e) owns a contiguous range of
-  // blocks; it sums its range (independent loads, kept in registers when the range is
-  // short), the ranges' sums are scanned across parts, then each thread writes its
-  // range's exclusive ranks.
+  // Per-expert running ranks over the blocks: P consecutive lanes of one wave per expert;
+  // each owns a contiguous range of blocks, sums it (independent loads, kept in registers
+  // when the range is short), the lanes scan their sums, then each writes its range's
+  // exclusive ranks.
   {
     constexpr int kCache = 16;
-    const int e = tid % ep, part = tid / ep;
+    const int P = min(64, kScanThreads / ep);
+    const int e = tid / P, part = tid % P;
+    const bool act = e < E;
     const int per = (a.nhb + P - 1) / P;
     const int b0 = min(part * per, a.nhb), b1 = min(b0 + per, a.nhb);
     int c[kCache];
     int sum = 0;
-    if (e < E) {
+    if (act) {
       if (per <= kCache) {
 #pragma unroll
         for (int i = 0; i < kCache; ++i) c[i] = b0 + i < b1 ? a.blk_counts[(size_t)(b0 + i) * E + e] : 0;
@@ -101,12 +119,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
         for (int b = b0; b < b1; ++b) sum += a.blk_counts[(size_t)b * E + e];
       }
     }
-    part_sh[tid] = sum;
-    __syncthreads();
-    int pre = 0;
-    for (int q = 0; q < part; ++q) pre += part_sh[q * ep + e];
-    if (e < E) {
-      if (part == P - 1) cnt_sh[e] = pre + sum;
+    const int incl = wave_incl_scan(sum, lane, P);
+    int pre = incl - sum;
+    if (act) {
+      if (part == P - 1) cnt_sh[e] = incl;
       if (per <= kCache) {
 #pragma unroll
         for (int i = 0; i < kCache; ++i)
@@ -122,54 +138,75 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
         }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
+  // kept counts -> offsets, m-tiles -> tile list: exclusive scans over the experts (4 waves)
   const int cnt = tid < E ? cnt_sh[tid] : 0;
   const int kept = tid < E ? min(cnt, a.C) : 0;
-  const int incl = block_inclusive_scan256(kept, sh);
+  const int mt = (tid < E && a.BM > 0) ? (kept + a.BM - 1) / a.BM : 0;
+  int ik = wave_incl_scan(kept, lane, 64), im = wave_incl_scan(mt, lane, 64);
+  if (wave < 4 && lane == 63) {
+    wsum[0][wave] = ik;
+    wsum[1][wave] = im;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    for (int w = 0; w < wave; ++w) {
+      ik += wsum[0][w];
+      im += wsum[1][w];
+    }
+  }
   if (tid < E) {
     a.counts[tid] = cnt;
-    a.offsets[tid] = incl - kept;
-    if (tid == E - 1) a.offsets[E] = incl;
-  }
-  if (a.BM > 0 && a.tile_off != nullptr) {
-    const int mt = tid < E ? (kept + a.BM - 1) / a.BM : 0;
-    const int tin = block_inclusive_scan256(mt, sh);
-    if (tid < E) {
-      a.tile_off[tid] = tin - mt;
-      if (tid == E - 1) a.tile_off[E] = tin;
+    a.offsets[tid] = ik - kept;
+    if (tid == E - 1) a.offsets[E] = ik;
+    if (a.BM > 0 && a.tile_off != nullptr) {
+      a.tile_off[tid] = im - mt;
+      if (tid == E - 1) a.tile_off[E] = im;
     }
   }
   if (a.aux != nullptr && (a.prob_part != nullptr || a.prob_sum != nullptr)) {
-    // sum_t p[t,e]: P threads per expert each sum a strided set of blocks, then a fixed-order tree
-    const int e = tid % ep, part = tid / ep;
-    double ps = 0.0;
-    if (e < E) {
-      if (a.prob_part != nullptr) {
-        for (int b = part; b < a.nrb; b += P) ps += (double)a.prob_part[(size_t)b * E + e];
-      } else if (part == 0) {
-        ps = (double)a.prob_sum[e];
+    // sum_t p[t,e]: few experts -- a wave per expert, lanes stride the blocks; many experts --
+    // P = 1024/ep threads per expert stride the blocks, then a fixed tree over the P sums
+    const double n = (double)a.T * (double)a.k;
+    if (E <= 16) {
+      for (int e = wave; e < E; e += kScanThreads / 64) {
+        double ps = 0.0;
+        if (a.prob_part != nullptr) {
+          for (int b = lane; b < a.nrb; b += 64) ps += (double)a.prob_part[(size_t)b * E + e];
+        } else if (lane == 0) {
+          ps = (double)a.prob_sum[e];
+        }
+        ps = wave_sum_f64(ps);
+        if (lane == 0) dterm[e] = ((double)cnt_sh[e] / n) * (ps / (double)a.T);
       }
-    }
-    dsh[tid] = ps;
-    __syncthreads();
-    for (int o = P / 2; o >= 1; o >>= 1) {
-      if (part < o) dsh[tid] += dsh[tid + o * ep];
+    } else {
+      __shared__ double dsh[kScanThreads];
+      const int P = kScanThreads / ep;
+      const int e = tid % ep, part = tid / ep;
+      double ps = 0.0;
+      if (e < E) {
+        if (a.prob_part != nullptr) {
+          for (int b = part; b < a.nrb; b += P) ps += (double)a.prob_part[(size_t)b * E + e];
+        } else if (part == 0) {
+          ps = (double)a.prob_sum[e];
+        }
+      }
+      dsh[tid] = ps;
       __syncthreads();
-    }
-    double term = 0.0;
-    if (tid < E) {
-      const double n = (double)a.T * (double)a.k;
-      term = ((double)cnt_sh[tid] / n) * (dsh[tid] / (double)a.T);
+      for (int o = P / 2; o >= 1; o >>= 1) {
+        if (part < o) dsh[tid] += dsh[tid + o * ep];
+        __syncthreads();
+      }
+      if (tid < E) dterm[tid] = ((double)cnt_sh[tid] / n) * (dsh[tid] / (double)a.T);
     }
     __syncthreads();
-    dsh[tid] = term;
-    __syncthreads();
-    for (int o = kScanThreads / 2; o >= 1; o >>= 1) {
-      if (tid < o) dsh[tid] += dsh[tid + o];
-      __syncthreads();
+    if (wave == 0) {
+      double t = 0.0;
+      for (int e = lane; e < E; e += 64) t += dterm[e];
+      t = wave_sum_f64(t);
+      if (lane == 0) *a.aux = (float)((double)E * t);
     }
-    if (tid == 0) *a.aux = (float)((double)E * dsh[0]);
   }
 }
 

@@ -65,6 +65,8 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
 // each wave: 16 tokens x NB*16 experts over h/KS.  Few experts: 16 waves split h 16 ways,
 // so each wave has a single batch of loads in flight and the kernel costs about one
 // memory round trip.
+// With gridDim.z = SH > 1 (few tokens), workgroup z covers h / SH of the contraction and
+// writes partial sums to logits + z * T * E (the selection kernel adds them).
 template <int NB, int TW, int NW>
 __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ planes,
@@ -79,8 +81,12 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
   const int tw = wave % TW, ks = wave / TW;
   const int t0 = blockIdx.x * (16 * TW) + tw * 16;
   const int e0 = blockIdx.y * (16 * NB);
-  const int kspan = h / KS;
-  const int kb = ks * kspan, ke = kb + kspan;
+  const int kspan = h / (KS * gridDim.z);
+  const int kb = (blockIdx.z * KS + ks) * kspan, ke = kb + kspan;
+  if (gridDim.z > 1) {
+    logits += (size_t)blockIdx.z * T * E;
+    if (blockIdx.z > 0) bias = nullptr;
+  }
 
   const int tok = t0 + (lane & 15);
   const bool tvalid = tok < T;
@@ -208,8 +214,11 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // lanes (G = E rounded up to a power of two, at most 64; lane gl of the group holds
 // experts gl, gl + 64, ...), so a wave works on 64/G tokens at once.  All of a wave's
 // logits are loaded before any is used: the kernel costs one memory round trip.
-template <int NV, int G>
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ logits, int T, int E, int k,
+// With SH > 1 the logits arrive as SH partial sums (lpart[z][t][e]); they are added in
+// ascending z and the sums written to `logits`.
+template <int NV, int G, bool HSPLIT>
+__global__ __launch_bounds__(256) void select_kernel(float* __restrict__ logits, const float* __restrict__ lpart,
+                                                     int SH, int T, int E, int k,
                                                      int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                      float* __restrict__ prob_part, int* __restrict__ blk_counts) {
   static_assert(G == 64 || NV == 1, "several values per lane only with whole-wave groups");
@@ -230,7 +239,21 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ l
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = gl + 64 * i;
-      v[q][i] = e < E ? (t < T ? logits[(size_t)t * E + e] : 0.f) : -INFINITY;
+      float l = 0.f;
+      if (e < E && t < T) {
+        if (HSPLIT) {
+          // SH <= 32 and a power of two: issue all the loads, then add in ascending z
+          float pz[32];
+#pragma unroll
+          for (int z = 0; z < 32; ++z) pz[z] = z < SH ? lpart[((size_t)z * T + t) * E + e] : 0.f;
+#pragma unroll
+          for (int z = 0; z < 32; ++z) l += pz[z];
+          logits[(size_t)t * E + e] = l;
+        } else {
+          l = logits[(size_t)t * E + e];
+        }
+      }
+      v[q][i] = e < E ? l : -INFINITY;
     }
   }
   float psum[NV];
@@ -324,16 +347,38 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
 }
 
 template <int NB, int TW, int NW = 4>
-void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st) {
-  const dim3 grid((a.T + 16 * TW - 1) / (16 * TW), E16 / (16 * NB));
+void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr) {
+  const dim3 grid((a.T + 16 * TW - 1) / (16 * TW), E16 / (16 * NB), SH);
   hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
-                     (const bf16_t*)a.planes, a.bias,
-                     a.T, a.h, a.E, E16, a.logits);
+                     (const bf16_t*)a.planes, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits);
 }
 
 }  // namespace
 
 int route_planes_elems(int h, int E) { return 3 * ((E + 15) / 16 * 16) * h; }
+
+int route_hsplit(int T, int h, int E, bool bf16) {
+  // few tokens: too few workgroups to stream the router weights and x at full rate, so the
+  // contraction over h is split across workgroups (partial logits added in the selection)
+  const int E16 = (E + 15) / 16 * 16;
+  if (!bf16 || E16 > 16 || T > 1024) return 1;
+  const int nwg = (T + 15) / 16;
+  int SH = 1;
+  while (SH < 32 && nwg * SH * 2 <= 512 && h % (SH * 2 * 4 * 32) == 0) SH *= 2;
+  return SH;
+}
+
+size_t route_scratch_bytes(int T, int h, int E, bool bf16) {
+  if (!bf16) return 0;
+  const size_t planes = ((size_t)route_planes_elems(h, E) * 2 + 255) / 256 * 256;
+  const int SH = route_hsplit(T, h, E, bf16);
+  return planes + (SH > 1 ? (size_t)SH * T * E * 4 : 0);
+}
+
+float* route_lpart(const RouteArgs& a) {
+  const size_t planes = ((size_t)route_planes_elems(a.h, a.E) * 2 + 255) / 256 * 256;
+  return (float*)((char*)a.planes + planes);
+}
 
 int route_blocks(int T) { return (T + kSelTokens - 1) / kSelTokens; }
 
@@ -345,7 +390,10 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(wsplit_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.W_gate, a.h, a.E,
                          E16, (bf16_t*)a.planes);
       // k split across waves needs h/KS to be a multiple of 32
-      if (E16 <= 16) {
+      const int SH = route_hsplit(a.T, a.h, a.E, true);
+      if (SH > 1) {
+        launch_logits_mfma<1, 1>(a, E16, st, SH, route_lpart(a));
+      } else if (E16 <= 16) {
         if (a.h % 512 == 0) launch_logits_mfma<1, 1, 16>(a, E16, st);
         else if (a.h % 128 == 0) launch_logits_mfma<1, 1>(a, E16, st);
         else launch_logits_mfma<1, 2>(a, E16, st);
@@ -385,16 +433,20 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
 
 hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
   const dim3 grid(route_blocks(a.T));
-#define MOE_SELECT(NV, G)                                                                                      \
-  hipLaunchKernelGGL((select_kernel<NV, G>), grid, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.topk_idx, a.topk_w, \
-                     a.prob_part, a.blk_counts)
-  if (a.E <= 4) MOE_SELECT(1, 4);
-  else if (a.E <= 8) MOE_SELECT(1, 8);
-  else if (a.E <= 16) MOE_SELECT(1, 16);
-  else if (a.E <= 32) MOE_SELECT(1, 32);
-  else if (a.E <= 64) MOE_SELECT(1, 64);
-  else if (a.E <= 128) MOE_SELECT(2, 64);
-  else MOE_SELECT(4, 64);
+  // partial logits from a split contraction (never with logits given as input)
+  const int SH = a.logits_in ? 1 : route_hsplit(a.T, a.h, a.E, a.bf16);
+  const float* lpart = SH > 1 ? route_lpart(a) : nullptr;
+#define MOE_SELECT(NV, G, HS)                                                                               \
+  hipLaunchKernelGGL((select_kernel<NV, G, HS>), grid, dim3(256), 0, st, a.logits, lpart, SH, a.T, a.E, a.k,  \
+                     a.topk_idx, a.topk_w, a.prob_part, a.blk_counts)
+  if (SH > 1 && a.E > 16) return hipErrorInvalidValue;  // the h split is for few experts only
+  if (a.E <= 4) { if (SH > 1) MOE_SELECT(1, 4, true); else MOE_SELECT(1, 4, false); }
+  else if (a.E <= 8) { if (SH > 1) MOE_SELECT(1, 8, true); else MOE_SELECT(1, 8, false); }
+  else if (a.E <= 16) { if (SH > 1) MOE_SELECT(1, 16, true); else MOE_SELECT(1, 16, false); }
+  else if (a.E <= 32) MOE_SELECT(1, 32, false);
+  else if (a.E <= 64) MOE_SELECT(1, 64, false);
+  else if (a.E <= 128) MOE_SELECT(2, 64, false);
+  else MOE_SELECT(4, 64, false);
 #undef MOE_SELECT
   return hipGetLastError();
 }
