@@ -619,15 +619,15 @@ FfnPlan plan_ffn(bool bf16, double rows_per_expert, int E, int R_max, int h, int
   if (p.bm == 32) {
     // Few rows per expert: the GEMMs stream weights.  When there are fewer tiles than two
     // per CU (one 256-column tile per expert and column block: the down projection at
-    // decode shapes), split K until there are about four per CU.  (Measured at T = 64,
-    // h = 4096, f = 14336, E = 8: the down projection gains ~10 %; splitting the
-    // up projection's 896 tiles further only adds partial-sum traffic.)
+    // decode shapes), split K until there are about two per CU.  (Measured at T = 64,
+    // h = 4096, f = 14336, E = 8: the down projection gains ~12 % with 4 parts; more
+    // parts, or splitting the up projection's 896 tiles, only add partial-sum traffic.)
     const double mt = std::min((double)E * ceil(rows_per_expert / p.bm), mt_max);  // expected m-tiles
     auto split = [&](int K, int N, int no) {
       const double tiles = mt * ceil((double)N / no);
       int S = 1;
       if (tiles >= 2 * kCUs) return S;
-      while (S < 16 && tiles * S < 4 * kCUs && K % (2 * S * KB) == 0 && K / (2 * S) >= 8 * KB) S *= 2;
+      while (S < 16 && tiles * S < 2 * kCUs && K % (2 * S * KB) == 0 && K / (2 * S) >= 8 * KB) S *= 2;
       return S;
     };
     p.s_up = split(h, f, BN / 2);
