@@ -62,12 +62,14 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
 
 // ---------------------------------------------------------------------------
 // logits for bf16 x on MFMA.  Workgroup = NW waves = TW token-waves x KS k-splits;
-// each wave: 16 tokens x NB*16 experts over h/KS.  Few experts: 16 waves split h 16 ways,
-// so each wave has a single batch of loads in flight and the kernel costs about one
-// memory round trip.
+// each wave: TG groups of 16 tokens x NB*16 experts over h/KS (the weight fragments
+// loaded for one k-step serve all TG token groups).  Few experts: 16 waves split h 16
+// ways, so each wave has a single batch of loads in flight and the kernel costs about
+// one memory round trip.  Many experts: each wave takes 64 tokens, so the router
+// weights are read once per 64 tokens instead of once per 16.
 // With gridDim.z = SH > 1 (few tokens), workgroup z covers h / SH of the contraction and
 // writes partial sums to logits + z * T * E (the selection kernel adds them).
-template <int NB, int TW, int NW>
+template <int NB, int TW, int NW, int TG = 1>
 __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ planes,
                                                           const float* __restrict__ bias, int T, int h, int E,
@@ -75,11 +77,11 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
   constexpr int KS = NW / TW;
   // k-steps of 32 per batch of loads (bounded by registers: 128 per lane at 16 waves)
   constexpr int U = NB >= 4 ? 2 : (NB == 2 ? 4 : (NW > 4 ? 4 : 8));
-  __shared__ floatx4 red[KS > 1 ? KS - 1 : 1][TW][NB][64];
+  __shared__ floatx4 red[KS > 1 ? KS - 1 : 1][TW][TG][NB][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tw = wave % TW, ks = wave / TW;
-  const int t0 = blockIdx.x * (16 * TW) + tw * 16;
+  const int t0 = blockIdx.x * (16 * TW * TG) + tw * 16 * TG;
   const int e0 = blockIdx.y * (16 * NB);
   const int kspan = h / (KS * gridDim.z);
   const int kb = (blockIdx.z * KS + ks) * kspan, ke = kb + kspan;
@@ -88,26 +90,35 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
     if (blockIdx.z > 0) bias = nullptr;
   }
 
-  const int tok = t0 + (lane & 15);
-  const bool tvalid = tok < T;
-  const bf16_t* xrow = x + (size_t)(tvalid ? tok : 0) * h + 8 * (lane >> 4);
+  bool tvalid[TG];
+  const bf16_t* xrow[TG];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    const int tok = t0 + 16 * tg + (lane & 15);
+    tvalid[tg] = tok < T;
+    xrow[tg] = x + (size_t)(tvalid[tg] ? tok : 0) * h + 8 * (lane >> 4);
+  }
   const size_t plane = (size_t)E16 * h;
   const bf16_t* wrow[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) wrow[nb] = planes + (size_t)(e0 + nb * 16 + (lane & 15)) * h + 8 * (lane >> 4);
 
-  floatx4 acc[NB];
+  floatx4 acc[TG][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[tg][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = kb; k0 < ke; k0 += 32 * U) {
-    const int steps = min(U, (ke - k0) / 32);
-    bf16x8 xb[U], wa[U][NB][3];
+  constexpr int UU = TG > 1 ? 1 : U;
+  for (int k0 = kb; k0 < ke; k0 += 32 * UU) {
+    const int steps = min(UU, (ke - k0) / 32);
+    bf16x8 xb[UU][TG], wa[UU][NB][3];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UU; ++u) {
       if (u < steps) {
         const int kk = k0 + 32 * u;
-        xb[u] = tvalid ? *(const bf16x8*)(xrow + kk) : bf16x8{};
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) xb[u][tg] = tvalid[tg] ? *(const bf16x8*)(xrow[tg] + kk) : bf16x8{};
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -115,37 +126,47 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UU; ++u) {
       if (u < steps) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-          for (int p = 0; p < 3; ++p)
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[u][nb][p], xb[u], acc[nb], 0, 0, 0);
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              acc[tg][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[u][nb][p], xb[u][tg], acc[tg][nb], 0, 0, 0);
       }
     }
   }
-  // lane holds token (lane & 15), experts 4*(lane>>4) + 0..3 of each 16-block
+  // lane holds token (lane & 15) of each group, experts 4*(lane>>4) + 0..3 of each 16-block
   if (KS > 1) {
     if (ks > 0) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) red[ks - 1][tw][nb][lane] = acc[nb];
+      for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) red[ks - 1][tw][tg][nb][lane] = acc[tg][nb];
     }
     __syncthreads();
     if (ks > 0) return;
 #pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int s = 0; s < KS - 1; ++s) acc[tg][nb] += red[s][tw][tg][nb][lane];
+  }
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    if (!tvalid[tg]) continue;
+    const int tok = t0 + 16 * tg + (lane & 15);
+#pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int s = 0; s < KS - 1; ++s) acc[nb] += red[s][tw][nb][lane];
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + nb * 16 + 4 * (lane >> 4) + r;
+        if (e < E) logits[(size_t)tok * E + e] = acc[tg][nb][r] + (bias ? bias[e] : 0.f);
+      }
   }
-  if (!tvalid) return;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = e0 + nb * 16 + 4 * (lane >> 4) + r;
-      if (e < E) logits[(size_t)tok * E + e] = acc[nb][r] + (bias ? bias[e] : 0.f);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -216,20 +237,21 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // logits are loaded before any is used: the kernel costs one memory round trip.
 // With SH > 1 the logits arrive as SH partial sums (lpart[z][t][e]); they are added in
 // ascending z and the sums written to `logits`.
-template <int NV, int G, bool HSPLIT>
-__global__ __launch_bounds__(256) void select_kernel(float* __restrict__ logits, const float* __restrict__ lpart,
+template <int NV, int G, bool HSPLIT, int NWS = 4>
+__global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ logits, const float* __restrict__ lpart,
                                                      int SH, int T, int E, int k,
                                                      int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                      float* __restrict__ prob_part, int* __restrict__ blk_counts) {
   static_assert(G == 64 || NV == 1, "several values per lane only with whole-wave groups");
-  constexpr int TPW = 64 / G;                // tokens per wave and pass
-  constexpr int NQ = kSelTokens / 4 / TPW;   // passes per wave
-  __shared__ float pp[4][64 * NV];
+  constexpr int TPW = 64 / G;                  // tokens per wave and pass
+  constexpr int NQ = kSelTokens / NWS / TPW;   // passes per wave
+  static_assert(NQ >= 1, "tokens per wave");
+  __shared__ float pp[NWS][64 * NV];
   __shared__ int cnt[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int sub = lane / G, gl = lane % G;
-  const int t0 = blockIdx.x * kSelTokens + w * (kSelTokens / 4);
-  cnt[tid] = 0;
+  const int t0 = blockIdx.x * kSelTokens + w * (kSelTokens / NWS);
+  if (tid < 256) cnt[tid] = 0;
   __syncthreads();
 
   float v[NQ][NV];
@@ -331,8 +353,12 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ logits,
   }
   __syncthreads();
   if (prob_part != nullptr)
-    for (int e = tid; e < E; e += 256)
-      prob_part[(size_t)blockIdx.x * E + e] = ((pp[0][e] + pp[1][e]) + pp[2][e]) + pp[3][e];
+    for (int e = tid; e < E; e += NWS * 64) {
+      float sum = pp[0][e];
+#pragma unroll
+      for (int q = 1; q < NWS; ++q) sum += pp[q][e];
+      prob_part[(size_t)blockIdx.x * E + e] = sum;
+    }
   if (blk_counts != nullptr && tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
 }
 
@@ -346,10 +372,10 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
   prob_sum[e] = s;
 }
 
-template <int NB, int TW, int NW = 4>
+template <int NB, int TW, int NW = 4, int TG = 1>
 void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr) {
-  const dim3 grid((a.T + 16 * TW - 1) / (16 * TW), E16 / (16 * NB), SH);
-  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
+  const dim3 grid((a.T + 16 * TW * TG - 1) / (16 * TW * TG), E16 / (16 * NB), SH);
+  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
                      (const bf16_t*)a.planes, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits);
 }
 
@@ -402,7 +428,10 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
         if (a.h % 128 == 0) launch_logits_mfma<2, 1>(a, E16, st);
         else launch_logits_mfma<2, 2>(a, E16, st);
       } else if (E16 % 64 == 0) {
-        launch_logits_mfma<4, 4>(a, E16, st);
+        // 64 tokens per wave and a 4-way k split: the router weights are read once per 64
+        // tokens (h / 4 must be a multiple of 32)
+        if (a.h % 128 == 0 && a.T >= 1024) launch_logits_mfma<4, 1, 4, 4>(a, E16, st);
+        else launch_logits_mfma<4, 4>(a, E16, st);
       } else if (E16 % 32 == 0) {
         launch_logits_mfma<2, 4>(a, E16, st);
       } else {
@@ -437,18 +466,21 @@ hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
   // partial logits from a split contraction (never with logits given as input)
   const int SH = a.logits_in ? 1 : route_hsplit(a.T, a.h, a.E, a.bf16);
   const float* lpart = SH > 1 ? route_lpart(a) : nullptr;
-#define MOE_SELECT(NV, G, HS)                                                                               \
-  hipLaunchKernelGGL((select_kernel<NV, G, HS>), grid, dim3(256), 0, st, a.logits, lpart, SH, a.T, a.E, a.k,  \
-                     a.topk_idx, a.topk_w, a.prob_part, a.blk_counts)
+#define MOE_SELECT_W(NV, G, HS, NWS)                                                                       \
+  hipLaunchKernelGGL((select_kernel<NV, G, HS, NWS>), grid, dim3(NWS * 64), 0, st, a.logits, lpart, SH, a.T, \
+                     a.E, a.k, a.topk_idx, a.topk_w, a.prob_part, a.blk_counts)
+#define MOE_SELECT(NV, G, HS) MOE_SELECT_W(NV, G, HS, 4)
   if (SH > 1 && a.E > 16) return hipErrorInvalidValue;  // the h split is for few experts only
   if (a.E <= 4) { if (SH > 1) MOE_SELECT(1, 4, true); else MOE_SELECT(1, 4, false); }
   else if (a.E <= 8) { if (SH > 1) MOE_SELECT(1, 8, true); else MOE_SELECT(1, 8, false); }
   else if (a.E <= 16) { if (SH > 1) MOE_SELECT(1, 16, true); else MOE_SELECT(1, 16, false); }
   else if (a.E <= 32) MOE_SELECT(1, 32, false);
-  else if (a.E <= 64) MOE_SELECT(1, 64, false);
-  else if (a.E <= 128) MOE_SELECT(2, 64, false);
-  else MOE_SELECT(4, 64, false);
+  // a whole wave per token: 16 waves, 4 tokens each, to keep enough selections in flight
+  else if (a.E <= 64) MOE_SELECT_W(1, 64, false, 16);
+  else if (a.E <= 128) MOE_SELECT_W(2, 64, false, 16);
+  else MOE_SELECT_W(4, 64, false, 16);
 #undef MOE_SELECT
+#undef MOE_SELECT_W
   return hipGetLastError();
 }
 
