@@ -169,9 +169,11 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
     stage_ms = {s: 0.0 for s in moe.LAYER_STAGES}
+    step_ms = []  # per step, from the first to the last event (GPU time of the whole layer)
     for i in range(args.steps):
         for j, s in enumerate(moe.LAYER_STAGES):
             stage_ms[s] += hip.elapsed_ms(ev[i][j], ev[i][j + 1]) / args.steps
+        step_ms.append(hip.elapsed_ms(ev[i][0], ev[i][nst]))
     for e_ in ev:
         hip.destroy(e_)
     log("[bench] stage ms: " + ", ".join(f"{s}={v:.4f}" for s, v in stage_ms.items()))
@@ -217,7 +219,13 @@ def main():
     # its MFMA work
     layer_bytes = T * h * es + h * E * 4 + active * (n_up + 1) * h * f * es + T * h * es + T * k * 12
     t_roof = max((flops_up + flops_down) / (PEAK_BF16_TFLOPS * 1e12), layer_bytes / (PEAK_HBM_GBS * 1e9))
+    # combine: one fp32 expert-output row per kept assignment and the routing weights read,
+    # y written (a lower bound: a K-split down projection leaves two or four parts to add)
+    combine_bytes = R * h * 4 + T * h * es + T * k * 8
+    q = np.percentile(np.array(step_ms), [10, 50, 90])
     extra = {
+        "layer_ms_p10_p50_p90": [round(float(v), 5) for v in q],
+        "combine_gbps_min": round(combine_bytes / (stage_ms["combine"] / 1e3) / 1e9, 1),
         "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
         "rows_kept": R, "active_experts": active,
         "layer_mfma_frac": round((flops_up + flops_down) / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
