@@ -165,7 +165,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
-  const bool has_x = NIX * uwave < XI;  // this wave copies activations
+  const bool has_x = XI % kWaves == 0 || NIX * uwave < XI;  // this wave copies activations
 
   // ---- copy plan.  One wave instruction moves 1 KiB: lane l writes LDS bytes
   // [16l, 16l+16) of the instruction's block, i.e. swizzle slot (l & 31) of weight
@@ -208,16 +208,17 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   // activation copy j go to groups i * sp / NIW and j * sp / NIX, sp = min(SPREAD, parts);
   // with a deeper weight pipeline the activation copies (needed first) take the first
   // sp/2 groups and the weight copies the next sp.
-  auto issue_part = [&](int xkt, int xst, int wkt, int wst, int part, int parts) {
+  // (ALL: both stages are known to exist, no checks)
+  auto issue_part = [&](int xkt, int xst, int wkt, int wst, int part, int parts, bool all = false) {
     const int sp = parts < SPREAD ? parts : SPREAD;
     const bool split = NSW != NSTAGE && parts > 1;
 #pragma unroll
     for (int i = 0; i < NIX; ++i)
-      if (xkt >= 0 && has_x && (split ? i * (sp / 2) / NIX : i * sp / NIX) == part)
+      if ((all || xkt >= 0) && has_x && (split ? i * (sp / 2) / NIX : i * sp / NIX) == part)
         copy_to_lds16(A + xsrc[i] + xkt * KB, xs_lds + 2u * (uint32_t)(xst * XST + 8 * (NIX * uwave + i) * KB));
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
-      if (wkt >= 0 && (split ? sp / 2 + i * sp / NIW : i * sp / NIW) == part)
+      if ((all || wkt >= 0) && (split ? sp / 2 + i * sp / NIW : i * sp / NIW) == part)
         copy_to_lds16(wsrc[i] + (size_t)wkt * KB * N,
                       ws_lds + 2u * (uint32_t)(wst * WST + (2 * (NIW * uwave + i)) * BN));
   };
@@ -260,9 +261,10 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 
   // MFMAs of stage kt; the copies of later stages (see issue_part) are issued in
   // between, one share after each group of JB MFMAs.
-  auto compute = [&](int kt, int xkt, int wkt) {
-    const bf16_t* Wb = Ws[kt % NSW];
-    const bf16_t* Xb = Xs[kt % NSTAGE];
+  // (xkt, xnb) / (wkt, wnb): the stage whose copies are issued, and its buffer
+  auto compute = [&](int xbuf, int wbuf, int xkt, int xnb, int wkt, int wnb, bool all) {
+    const bf16_t* Wb = Ws[wbuf];
+    const bf16_t* Xb = Xs[xbuf];
     constexpr int PARTS = (KB / 16) * IB;
     const bool mf = NCW == kWaves || uwave < NCW;  // waves past the grid only copy
 #pragma unroll
@@ -285,7 +287,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
           for (int jb = 0; jb < JB; ++jb)
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
         }
-        issue_part(xkt, xkt % NSTAGE, wkt, wkt % NSW, kh * IB + ib, PARTS);
+        issue_part(xkt, xnb, wkt, wnb, kh * IB + ib, PARTS, all);
       }
     }
   };
@@ -299,7 +301,33 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 #pragma unroll
   for (int p = 0; p < NSW - 1; ++p)
     if (p < nk) issue_part(p < NSTAGE - 1 ? p : -1, p, p, p, 0, 1);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Steady state: U = lcm(NSTAGE, NSW) stages per iteration, so every buffer index is a
+  // constant, and every copy of these stages exists.
+  constexpr int U = NSW == NSTAGE ? NSW : NSW * NSTAGE;
+  int kt = 0;
+  for (; kt + U + NSW - 2 < nk; kt += U) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (NSW == NSTAGE) {
+        if (NSTAGE >= 4) {
+          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIW + NIX)) : "memory");
+          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIW) : "memory");
+        } else if (NSTAGE == 3) {
+          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW + NIX) : "memory");
+          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+      } else {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+      }
+      __syncthreads();
+      compute(j % NSTAGE, j % NSW, kt + j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE, kt + j + NSW - 1,
+              (j + NSW - 1) % NSW, true);
+    }
+  }
+  // the remaining stages (the pipeline drains)
+  for (; kt < nk; ++kt) {
     if (NSW == NSTAGE) {
       // stages newer than kt already issued, NIW (+ NIX) copies each
       const int ahead = min(nk - 1 - kt, NSTAGE - 2);
@@ -321,7 +349,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     __syncthreads();
     const int xkt = kt + NSTAGE - 1 < nk ? kt + NSTAGE - 1 : -1;
     const int wkt = kt + NSW - 1 < nk ? kt + NSW - 1 : -1;
-    compute(kt, xkt, wkt);
+    compute(kt % NSTAGE, kt % NSW, xkt, xkt % NSTAGE, wkt, wkt % NSW, false);
   }
 
   // ---- epilogue: lane holds token row 32*jb + (lane & 31) and, for acc element
