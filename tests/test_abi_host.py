@@ -203,3 +203,14 @@ def test_binding_refuses_cpu_tensors(L):
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         moe.unpermute(torch.zeros(4, 64), torch.zeros(8, dtype=torch.int32), torch.zeros(4, 2))
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py runs on one GPU only and says so before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout

@@ -109,3 +109,54 @@ def test_layer_edge_cases(T, h, f, E, k, cf, act, dtype):
         dropped = (ref["slot_pos"].reshape(T, k) < 0).all(1)
         if dropped.any():
             assert (gu.from_dev(y)[dropped] == 0).all()
+
+
+def test_layer_forward_timed_matches_untimed():
+    """The measurement entry point runs the same kernels: identical outputs, and the
+    stage events are ordered and add up to the whole layer."""
+    import bench
+    torch = gu.torch()
+    w, host, dd = gu.workload("tiny-fp32")
+    args = (dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"])
+    kw = dict(k=w.k, capacity_factor=w.cf, act=w.act)
+    y0, aux0, c0 = moe.layer_forward(*args, **kw)
+    hip = bench.Hip()
+    ev = hip.events(len(moe.LAYER_STAGES) + 1)
+    y1, aux1, c1 = moe.layer_forward(*args, **kw, events=ev)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.from_dev(y0), gu.from_dev(y1))
+    assert float(gu.from_dev(aux0)) == float(gu.from_dev(aux1))
+    assert np.array_equal(gu.from_dev(c0), gu.from_dev(c1))
+    stages = [hip.elapsed_ms(ev[i], ev[i + 1]) for i in range(len(moe.LAYER_STAGES))]
+    total = hip.elapsed_ms(ev[0], ev[len(moe.LAYER_STAGES)])
+    hip.destroy(ev)
+    assert all(s >= 0 for s in stages)
+    assert abs(sum(stages) - total) <= 1e-3 * max(total, 1e-3) + 1e-3
+
+
+def test_bench_json_contract():
+    """bench.py on the small fp32 workload prints one JSON line with the fields the
+    benchmark contract names."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--steps", "3", "--warmup", "1",
+                        "--workload", "tiny-fp32", "--cpu-sample", "64"], capture_output=True, text=True,
+                       timeout=300, cwd=root)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
+    assert d["config"]["workload"] == "tiny-fp32" and d["dtype"] == "f32"
+    rf = d["roofline"]
+    assert rf["bound"] in ("hbm", "mfma", "alu") and rf["peak"] > 0 and rf["achieved"] > 0
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert d["extra"]["parity_vs_oracle"]["routing_differs"] <= 1  # a near-tie may route differently
