@@ -45,6 +45,7 @@ __all__ = [
     "bf16_to_f64", "round_to_bf16", "router_logits", "softmax", "select_topk",
     "topk_weights", "expert_capacity", "histogram", "permute", "silu", "gelu",
     "expert_ffn", "combine", "aux_loss", "layer_forward",
+    "binned_capacity", "binned_layout", "layer_forward_binned",
 ]
 
 
@@ -317,3 +318,78 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
         out["y64"] = y64
         out["y"] = round_to_bf16(y64) if dtype == "bf16" else y64.astype(np.float32)
     return out
+
+
+# ----------------------------------------------------------------------------
+# fixed-capacity ("binned") layout
+
+def binned_capacity(T: int, E: int, k: int, capacity_factor: float, min_capacity: int, counts) -> int:
+    """Bucket size C of the fixed-capacity layout.
+
+    [MB] section 3: every expert gets C = capacity_factor * tokens * top_k / num_experts
+    rows; section 4.2 truncates to int; section 4.6: a computed capacity of zero means
+    "the largest expert count of this step" (nothing dropped, buckets padded to the worst
+    case).  [CAI] SparseMLP parameters: a minimum capacity (router_min_capacity) applies
+    on top of the formula.  Readings: the minimum is applied to the formula's value
+    (cf > 0); a factor <= 0, or a capacity that is still zero, takes the largest count.
+    """
+    cf = float(np.float32(capacity_factor))
+    if not math.isfinite(cf) or min_capacity < 0:
+        raise ValueError("capacity factor must be finite, minimum capacity >= 0")
+    cmax = int(max(np.asarray(counts).tolist() or [0]))
+    if cf <= 0.0:
+        return cmax
+    C = max(int(math.floor(cf * ((k * T) / E))), int(min_capacity))
+    return cmax if C == 0 else C
+
+
+def binned_layout(topk_idx: np.ndarray, E: int, C: int):
+    """The [E, C] buckets of the fixed-capacity layout, from the page's slot semantics.
+
+    [MB] section 4.5: slot i of expert e holds the i-th assignment routed to e when e has
+    more than i of them; otherwise it stays zero (padding); assignments past the C-th are
+    not read by any slot (dropped).  Assignments are taken in ascending s = t*k + j (the
+    stable order).  Returns ``bins[E, C]`` (assignment s, or -1 for padding) and
+    ``slot_pos[T*k]`` (assignment -> bucket row e*C + i, or -1 if dropped).
+    """
+    flat = np.asarray(topk_idx).reshape(-1).tolist()
+    bins = [[-1] * C for _ in range(E)]
+    seen = [0] * E
+    slot_pos = [-1] * len(flat)
+    for s, e in enumerate(flat):
+        i = seen[e]
+        seen[e] += 1
+        if i < C:
+            bins[e][i] = s
+            slot_pos[s] = e * C + i
+    return np.asarray(bins, dtype=np.int32).reshape(E, C), np.asarray(slot_pos, dtype=np.int32)
+
+
+def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float,
+                         min_capacity: int, act: str, dtype: str, logits=None, tokens=None) -> dict:
+    """The layer with fixed-capacity buckets ([MB] sections 3 and 4.3: gather into
+    [E, C, h], the expert MLPs on every bucket row, weighted scatter back; [CAI] SparseMLP
+    data flow step 4).  Padding rows are zero and are never read back, so the output is
+    the compact layer's output for the same capacity; the bucket tensor ``x_bins`` is
+    returned as well (bf16 bit patterns or fp32, zero rows for padding)."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(W_gate).shape[1]
+    if logits is None:
+        logits = router_logits(x, W_gate, logit_bias, dtype)
+    logits = np.asarray(logits, dtype=np.float32)
+    idx = select_topk(logits, k)
+    w = topk_weights(logits, idx)
+    counts = histogram(idx, E)
+    C = binned_capacity(T, E, k, capacity_factor, min_capacity, counts)
+    bins, slot_pos = binned_layout(idx, E, C)
+    x_bins = np.zeros((E, C) + x.shape[1:], dtype=x.dtype)
+    for e in range(E):
+        for i in range(C):
+            if bins[e, i] >= 0:
+                x_bins[e, i] = x[bins[e, i] // k]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y64 = combine(x, idx, w, slot_pos, W1, W3, W2, act, dtype, tokens=tok)
+    return dict(logits=logits, topk_idx=idx, topk_w=w, C=C, counts=counts, bins=bins, slot_pos=slot_pos,
+                x_bins=x_bins, aux=aux_loss(counts, softmax(logits), T, k, E), y_tokens=tok, y64=y64,
+                y=round_to_bf16(y64) if dtype == "bf16" else y64.astype(np.float32))

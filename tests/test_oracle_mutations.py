@@ -61,7 +61,21 @@ def _silu_sign(z):
     return z / (1.0 + np.exp(z))
 
 
-_orig = {n: getattr(om, n) for n in ("router_logits", "permute")}
+def _binned_keep_last(topk_idx, E, C):
+    # fills the buckets with the last C assignments of each expert instead of the first C
+    flat = np.asarray(topk_idx).reshape(-1)
+    rev = flat[::-1].reshape(-1, 1)
+    bins, sp = _orig["binned_layout"](rev, E, C)
+    n = flat.size
+    bins = np.where(bins >= 0, n - 1 - bins, -1).astype(np.int32)
+    return bins, sp[::-1].copy()
+
+
+def _binned_capacity_no_minimum(T, E, k, cf, min_capacity, counts):
+    return _orig["binned_capacity"](T, E, k, cf, 0, counts)
+
+
+_orig = {n: getattr(om, n) for n in ("router_logits", "permute", "binned_layout", "binned_capacity")}
 
 MUTANTS = [
     ("select_topk", _topk_ties_high, ["test_topk_ties_and_signed_zero"]),
@@ -72,6 +86,8 @@ MUTANTS = [
     ("router_logits", _logits_no_bias, ["test_k_equals_E_is_dense_softmax_mixture"]),
     ("permute", _permute_unstable, ["test_histogram_worked_example_dropless"]),
     ("silu", _silu_sign, ["test_gelu_silu_vs_math", "test_single_expert_is_plain_ffn"]),
+    ("binned_layout", _binned_keep_last, ["test_binned_worked_example"]),
+    ("binned_capacity", _binned_capacity_no_minimum, ["test_binned_capacity_rules", "test_binned_worked_example"]),
 ]
 
 

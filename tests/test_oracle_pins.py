@@ -398,3 +398,67 @@ def test_generator_is_seeded_and_sliceable():
     assert a["W3"] is None and a["logit_bias"] is None
     # distributions: N(0,1) x, N(0,1/h) gate
     assert abs(a["x"].std() - 1) < 0.05 and abs(a["W_gate"].std() * math.sqrt(w.h) - 1) < 0.1
+
+
+# ----------------------------------------------------------------------------
+# fixed-capacity ("binned") layout
+
+def test_binned_worked_example():
+    g = _gold("mb_histogram_example.json")
+    idx = np.array(g["topk_idx"], dtype=np.int32).reshape(-1, 1)
+    counts = o.histogram(idx, g["E"])
+    for key, cf, mn in (("cf_1", 1.0, 0), ("cf_0", 0.0, 0), ("cf_0.5_min_3", 0.5, 3)):
+        ref = g["binned"][key]
+        C = o.binned_capacity(idx.shape[0], g["E"], 1, cf, mn, counts)
+        assert C == ref["C"], key
+        bins, slot_pos = o.binned_layout(idx, g["E"], C)
+        assert bins.tolist() == ref["bins"], key
+        assert slot_pos.tolist() == ref["slot_pos"], key
+
+
+def test_binned_capacity_rules():
+    counts = [5, 1, 0, 9]
+    assert o.binned_capacity(8, 4, 2, 0.0, 4, counts) == 9          # factor 0: the largest count
+    assert o.binned_capacity(8, 4, 2, -1.0, 0, counts) == 9
+    assert o.binned_capacity(8, 4, 2, 1.25, 0, counts) == 5         # floor(1.25 * 16 / 4)
+    assert o.binned_capacity(8, 4, 2, 0.1, 4, counts) == 4          # the minimum capacity
+    assert o.binned_capacity(8, 4, 2, 0.1, 0, counts) == 9          # computed zero: the largest count
+    with pytest.raises(ValueError):
+        o.binned_capacity(8, 4, 2, float("nan"), 0, counts)
+
+
+def test_binned_keeps_what_the_compact_layout_keeps():
+    # the same stable ranks decide both layouts: row e*C + i holds the assignment that the
+    # compact layout puts at offsets[e] + i
+    rng = np.random.default_rng(21)
+    for E, k, T, C in [(5, 2, 40, 7), (8, 3, 33, 2), (3, 1, 50, 30)]:
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        counts, offsets, sorted_slot, _ = o.permute(idx, E, C)
+        bins, slot_pos = o.binned_layout(idx, E, C)
+        for e in range(E):
+            kept = sorted_slot[offsets[e]:offsets[e + 1]].tolist()
+            assert bins[e, :len(kept)].tolist() == kept
+            assert (bins[e, len(kept):] == -1).all()
+        assert ((slot_pos >= 0) == (o.permute(idx, E, C)[3] >= 0)).all()
+
+
+@pytest.mark.parametrize("T,h,f,E,k,cf,act,dtype", [
+    (7, 4, 6, 6, 3, 0.0, "swiglu", "bf16"),   # factor 0: buckets of the largest count, nothing dropped
+    (10, 6, 3, 3, 2, 0.7, "swiglu", "bf16"),  # drops
+    (9, 3, 4, 5, 1, 1.0, "gelu", "f32"),
+])
+def test_binned_layer_vs_brute_force(T, h, f, E, k, cf, act, dtype):
+    x, Wg, b, W1, W3, W2 = _tiny(T, h, f, E, seed=T * 17 + E, act=act, dtype=dtype, bias=True)
+    r = o.layer_forward_binned(x, Wg, b, W1, W3, W2, k=k, capacity_factor=cf, min_capacity=0, act=act,
+                               dtype=dtype)
+    ref = brute.layer(_to_list(x, dtype), Wg.astype(np.float64).tolist(), b.astype(np.float64).tolist(),
+                      _to_list(W1, dtype), _to_list(W3, dtype), _to_list(W2, dtype), k, cf, act, dtype)
+    np.testing.assert_allclose(r["y64"], ref["y64"], rtol=1e-10, atol=1e-12)
+    assert abs(r["aux"] - ref["aux"]) < 1e-12
+    # the buckets: token rows where a slot is filled, zero rows elsewhere
+    C = r["C"]
+    for e in range(E):
+        for i in range(C):
+            s = r["bins"][e, i]
+            want = x[s // k] if s >= 0 else np.zeros_like(x[0])
+            assert np.array_equal(r["x_bins"][e, i], want)
