@@ -151,6 +151,32 @@ moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* 
                                void* y, float* aux_loss, int32_t* counts,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The layer with fixed-capacity buckets ("binned" layout: [MB] sections 3, 4.3 and 4.5;
+ * [CAI] SparseMLP data flow step 4 and its capacity parameters).  Every expert gets a
+ * bucket of C rows: C = max(floor(cf * T*k/E), min_capacity) when cf > 0, else (or if that
+ * is 0) the largest expert count of this call ([MB] section 4.6).  An expert's first C
+ * assignments, in ascending t*k + j, fill its bucket; later ones are dropped (they add
+ * nothing to y); the bucket rows past its count are zero and still go through the
+ * expert MLP -- the padding cost of the layout.  y equals moe_layer_forward's output for
+ * the same capacity.
+ *   capacity: device int32 scalar or NULL: the C used.
+ *   x_bins: [E*Cmax, h] (dt) or NULL (then kept in ws), Cmax = moe_binned_capacity_max(...):
+ *           bucket e occupies rows [e*C, e*C + C); rows >= E*C are not written.
+ *   ws: at least moe_binned_workspace_bytes(...) bytes.  Other arguments as in
+ *   moe_layer_forward.  MOE_ERR_UNSUPPORTED when E*Cmax*max(h,f) >= 2^32. */
+int32_t moe_binned_capacity_max(int32_t T, int32_t E, int32_t k, float capacity_factor,
+                                int32_t min_capacity);  /* -1 for invalid sizes */
+size_t moe_binned_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                  float capacity_factor, int32_t min_capacity, moe_dtype_t dt,
+                                  moe_act_t act);
+moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const float* logit_bias,
+                                      const void* W1, const void* W3, const void* W2,
+                                      int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                      float capacity_factor, int32_t min_capacity, moe_act_t act,
+                                      moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts,
+                                      int32_t* capacity, void* x_bins, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* Measurement variant of moe_layer_forward: the same kernels on the same stream, with
  * caller-created HIP events recorded between the stages, so a profiler-free caller can
  * time each kernel: events[0] before the router, then one after each stage in order

@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"moe_capacity", "moe_workspace_bytes", "moe_status_string", "moe_route",
                           "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_forward",
                           "moe_layer_forward_timed", "moe_expert_ffn_workspace_bytes",
-                          "moe_route_workspace_bytes"}
+                          "moe_route_workspace_bytes", "moe_binned_capacity_max", "moe_binned_workspace_bytes",
+                          "moe_layer_forward_binned"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -197,6 +198,67 @@ def test_ffn_and_unpermute_host_errors(L):
     assert u(FAKE, FAKE, FAKE, 4, 64, 17, 1, FAKE, None) == UNSUP
     assert u(FAKE, FAKE, FAKE, 4, 64, 2, 1, MIS, None) == UNSUP
     assert u(FAKE, FAKE, FAKE, 0, 64, 2, 1, FAKE, None) == OK
+
+
+@pytest.mark.parametrize("T,E,k,cf,mc", [(8192, 64, 2, 1.25, 0), (8, 4, 1, 1.0, 0), (10, 4, 2, 0.3, 0),
+                                         (10, 4, 2, 0.3, 3), (8, 64, 1, 0.5, 0), (8, 64, 1, 0.5, 2),
+                                         (4096, 256, 8, 1.1, 4), (100, 7, 3, 2.0, 0), (1, 1, 1, 1.0, 0),
+                                         (4096, 8, 2, 1e-9, 5)])
+def test_binned_capacity_max_matches_oracle(L, T, E, k, cf, mc):
+    """With a positive factor the bucket size does not depend on the routing: the oracle's
+    value for any counts (all zero here, so a zero capacity would show up as 0)."""
+    C = o.binned_capacity(T, E, k, cf, mc, [0] * E)
+    assert moe.binned_capacity_max(T, E, k, cf, mc) == (C if C > 0 else T)
+
+
+def test_binned_capacity_max_dynamic_and_invalid(L):
+    # no factor, or a zero capacity: the bucket is the largest count, at most T
+    assert moe.binned_capacity_max(4096, 8, 2, 0.0, 0) == 4096
+    assert moe.binned_capacity_max(4096, 8, 2, -1.0, 7) == 4096
+    assert moe.binned_capacity_max(8, 64, 1, 0.5, 0) == 8          # floor(0.125) = 0
+    assert L.moe_binned_capacity_max(8, 8, 2, 1.0, -1) == -1
+    assert L.moe_binned_capacity_max(8, 8, 2, float("nan"), 0) == -1
+    assert L.moe_binned_capacity_max(8, 8, 9, 1.0, 0) == -1
+
+
+def test_binned_workspace_bytes(L):
+    T, h, f, E, k = 4096, 1024, 4096, 64, 2
+    C = o.binned_capacity(T, E, k, 1.25, 0, [0] * E)
+    b = moe.binned_workspace_bytes(T, h, f, E, k, 1.25, 0, 1, 0)
+    R = E * C
+    need = R * h * 2 + R * f * 2 + R * h * 4  # buckets + hidden activation + fp32 expert outputs
+    assert need <= b < need + R * h * 4 + 64 * T * k + 16 * T * E + 8 * h * E + 2 ** 20
+    # no factor: buffers for the worst case, every token on one expert
+    assert moe.binned_workspace_bytes(T, h, f, E, k, 0.0, 0, 1, 0) >= E * T * (h * 2 + f * 2 + h * 4)
+    assert moe.binned_workspace_bytes(T, h, f, E, k, float("nan"), 0, 1, 0) == 0
+    assert moe.binned_workspace_bytes(T, h, f, E, k, 1.0, -2, 1, 0) == 0
+    assert moe.binned_workspace_bytes(1 << 20, 4096, 4096, 256, 2, 0.0, 0, 1, 0) == 0  # rows overflow int32
+
+
+def _binned(L, **kw):
+    a = dict(x=FAKE, W_gate=FAKE, bias=None, W1=FAKE, W3=FAKE, W2=FAKE, T=64, h=128, f=256, E=8, k=2, cf=1.0, mc=0,
+             act=1, dt=1, y=FAKE, aux=None, counts=None, cap=None, xb=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.moe_layer_forward_binned(a["x"], a["W_gate"], a["bias"], a["W1"], a["W3"], a["W2"], a["T"], a["h"],
+                                      a["f"], a["E"], a["k"], a["cf"], a["mc"], a["act"], a["dt"], a["y"], a["aux"],
+                                      a["counts"], a["cap"], a["xb"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=0), ARG), (dict(k=9), ARG), (dict(T=-1), ARG), (dict(h=0), ARG), (dict(mc=-1), ARG),
+    (dict(cf=float("nan")), ARG), (dict(x=None), ARG), (dict(W3=None), ARG), (dict(act=0), ARG), (dict(dt=3), ARG),
+    (dict(h=96), UNSUP), (dict(E=300, k=2), UNSUP), (dict(xb=MIS), UNSUP), (dict(y=MIS), UNSUP),
+    (dict(T=1 << 20, h=4096, f=4096, E=256, cf=0.0), UNSUP),      # E * T bucket rows of 4096: 32-bit offsets
+    (dict(ws_bytes=1000), WS), (dict(ws=None), WS),
+    (dict(T=0), OK),
+])
+def test_layer_forward_binned_host_errors(L, kw, expect):
+    assert _binned(L, **kw) == expect
+
+
+def test_layer_forward_binned_workspace_boundary(L):
+    need = moe.binned_workspace_bytes(64, 128, 256, 8, 2, 1.0, 0, 1, 1)
+    assert _binned(L, ws_bytes=need - 1) == WS
 
 
 def test_binding_refuses_cpu_tensors(L):

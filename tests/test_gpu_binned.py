@@ -1,0 +1,130 @@
+"""GPU parity of the fixed-capacity (binned) layer, moe_layer_forward_binned, against
+the oracle's layer_forward_binned.
+
+The oracle routes on the GPU router's fp32 logits (from moe_route, the kernel the
+layer runs), so the integer results -- expert counts, the bucket size C and the
+bucket contents x_bins (copies of rows of x, zero padding) -- must agree bit for
+bit; y is compared with the oracle's fp64 y within the floating-point bar, on all
+tokens for small cases and a seeded sample of 256 tokens for the full-size ones.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+
+import moe_workloads as mw
+import oracle as o
+import top_routing_expert_moe_amd as moe
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 256
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run_and_check(w, host, dd, min_capacity, tokens, check_all_bins=True):
+    torch = gu.torch()
+    y, aux, counts, cap, x_bins = moe.layer_forward_binned(
+        dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"], k=w.k, capacity_factor=w.cf,
+        min_capacity=min_capacity, act=w.act)
+    logits, _, _, _ = moe.route(dd["x"], dd["W_gate"], dd["logit_bias"], w.k)
+    torch.cuda.synchronize()
+    ref = o.layer_forward_binned(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"],
+                                 k=w.k, capacity_factor=w.cf, min_capacity=min_capacity, act=w.act, dtype=w.dtype,
+                                 logits=gu.from_dev(logits), tokens=tokens)
+    C = int(gu.from_dev(cap))
+    E = ref["counts"].shape[0]
+    _say(f"  C={C} (oracle {ref['C']}); padded rows {E * C - int(np.minimum(ref['counts'], C).sum())} of {E * C}")
+    assert np.array_equal(gu.from_dev(counts), ref["counts"])
+    assert C == ref["C"]
+    assert x_bins.shape[0] == E * moe.binned_capacity_max(w.T, E, w.k, w.cf, min_capacity)
+    gb = gu.from_dev(x_bins[:E * C]).reshape(ref["x_bins"].shape)
+    if check_all_bins:
+        assert np.array_equal(gb, ref["x_bins"])
+    else:  # every bucket's first, last-filled and first-padding rows, plus a seeded sample
+        rows = set(np.random.default_rng(7).choice(E * C, min(E * C, 4096), replace=False).tolist())
+        for e in range(E):
+            n = min(int(ref["counts"][e]), C)
+            rows.update(r for r in (e * C, e * C + n - 1, e * C + n) if e * C <= r < (e + 1) * C)
+        rows = np.array(sorted(rows))
+        assert np.array_equal(gb.reshape(E * C, -1)[rows], ref["x_bins"].reshape(E * C, -1)[rows])
+    a = float(gu.from_dev(aux))
+    assert abs(a - ref["aux"]) <= 1e-5 * abs(ref["aux"]), (a, ref["aux"])
+    got = gu.as_f64(gu.from_dev(y)[tokens], w.dtype)
+    if w.dtype == "bf16":
+        raw, beyond = gu.check_bf16_out(got, ref["y64"], "y")
+        _say(f"  y max|d|/RMS = {raw:.4f} (beyond the output's own bf16 rounding: {beyond:.4f})")
+    else:
+        gu.check_rel_rms(got, ref["y64"], 1e-5, "y")
+    dropped = (ref["slot_pos"].reshape(w.T, w.k) < 0).all(1)[tokens]
+    if dropped.any():
+        assert (gu.from_dev(y)[tokens][dropped] == 0).all()
+    return ref
+
+
+@pytest.mark.parametrize("name,cf,min_capacity", [
+    ("decode-mixtral", 0.0, 0),       # no factor: buckets of the largest count
+    ("prefill-mixtral", 1.0, 0),      # GShard-style capacity with drops
+    ("capacity-e64", 1.25, 0),        # C = 320
+    ("capacity-e64", 1.25, 400),      # the minimum capacity wins: every bucket padded
+    ("capacity-e64", 0.0, 0),         # no factor under zipf-skewed routing: padding to the busiest expert
+    ("finegrained-e256", 1.0, 0),     # C = 128 of 256 experts under skewed routing
+])
+def test_binned_layer_parity(name, cf, min_capacity):
+    _say(f"binned {name} cf={cf} min_capacity={min_capacity}")
+    w0, host, dd = gu.workload(name)
+    w = dataclasses.replace(w0, cf=cf)
+    if w.T <= 64:
+        tokens = np.arange(w.T)
+    else:
+        tokens = np.sort(np.random.default_rng(321).choice(w.T, SAMPLE, replace=False))
+        tokens[0], tokens[-1] = 0, w.T - 1
+    _run_and_check(w, host, dd, min_capacity, tokens, check_all_bins=w.T * w.h <= 4096 * 4096 and w.E <= 64)
+
+
+@pytest.mark.parametrize("T,h,f,E,k,cf,mc,act,dtype", [
+    (1, 128, 256, 8, 2, 1.0, 0, "swiglu", "bf16"),      # floor(cf T k / E) = 0: buckets of the largest count (1)
+    (33, 256, 192, 6, 3, 0.5, 12, "gelu", "bf16"),      # minimum capacity above the formula's 8
+    (65, 192, 320, 40, 3, 1.0, 0, "swiglu", "bf16"),    # C = 4 of 40 experts: drops and padding together
+    (300, 128, 128, 5, 5, 0.0, 0, "swiglu", "bf16"),    # k = E: every bucket holds every token
+    (200, 192, 256, 4, 1, 0.3, 0, "gelu", "bf16"),      # heavy drops, k = 1
+    (130, 64, 64, 1, 1, 0.0, 0, "swiglu", "f32"),       # a single expert
+    (500, 128, 256, 16, 2, 2.0, 200, "swiglu", "f32"),  # fp32, minimum capacity pads every bucket
+    (20, 1024, 2048, 8, 2, 0.0, 0, "swiglu", "bf16"),   # few rows per expert: K-split GEMMs
+    (40, 2048, 1024, 6, 2, 0.5, 3, "gelu", "bf16"),     # K splits with drops
+])
+def test_binned_edge_cases(T, h, f, E, k, cf, mc, act, dtype):
+    _say(f"binned edge T={T} h={h} f={f} E={E} k={k} cf={cf} min_capacity={mc} {act} {dtype}")
+    rng = np.random.default_rng(T + 7 * E)
+    conv = (lambda a: mw.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32),
+                logit_bias=rng.standard_normal(E).astype(np.float32),
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)) if act == "swiglu" else None,
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("edge", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
+    _run_and_check(w, host, dd, mc, np.arange(T))
+
+
+def test_binned_matches_compact_layer():
+    """Same capacity, same routing: the binned layer keeps the assignments the compact
+    layer keeps, so both give the same counts and aux and y within the output bar."""
+    torch = gu.torch()
+    w, host, dd = gu.workload("capacity-e64")
+    args = (dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"])
+    y0, aux0, c0 = moe.layer_forward(*args, k=w.k, capacity_factor=w.cf, act=w.act)
+    y1, aux1, c1, cap, _ = moe.layer_forward_binned(*args, k=w.k, capacity_factor=w.cf, act=w.act)
+    torch.cuda.synchronize()
+    assert int(gu.from_dev(cap)) == moe.capacity(w.T, w.E, w.k, w.cf)
+    assert np.array_equal(gu.from_dev(c0), gu.from_dev(c1))
+    assert float(gu.from_dev(aux0)) == float(gu.from_dev(aux1))
+    y0h, y1h = gu.as_f64(gu.from_dev(y0), "bf16"), gu.as_f64(gu.from_dev(y1), "bf16")
+    assert np.array_equal(y0h == 0, y1h == 0)  # the same tokens dropped
+    gu.check_bf16_out(y1h, y0h, "binned vs compact", frac=2e-2)

@@ -55,6 +55,12 @@ _SIGS = {
                                                _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
                                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p,
                                                _c_void_p]),
+    "moe_binned_capacity_max": (_i32, [_i32, _i32, _i32, _f32, _i32]),
+    "moe_binned_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, ctypes.c_int]),
+    "moe_layer_forward_binned": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                _i32, _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
+                                                ctypes.c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                _c_void_p, _c_void_p, _sz, _c_void_p]),
 }
 
 LAYER_STAGES = ("logits", "select", "scan", "scatter", "expert_up", "expert_down", "combine")
@@ -102,6 +108,14 @@ def capacity(T: int, E: int, k: int, capacity_factor: float) -> int | None:
 
 def workspace_bytes(T, h, f, E, k, capacity_factor, dtype: int, act: int) -> int:
     return int(lib().moe_workspace_bytes(T, h, f, E, k, capacity_factor, dtype, act))
+
+
+def binned_capacity_max(T, E, k, capacity_factor, min_capacity) -> int:
+    return int(lib().moe_binned_capacity_max(T, E, k, capacity_factor, min_capacity))
+
+
+def binned_workspace_bytes(T, h, f, E, k, capacity_factor, min_capacity, dtype: int, act: int) -> int:
+    return int(lib().moe_binned_workspace_bytes(T, h, f, E, k, capacity_factor, min_capacity, dtype, act))
 
 
 # ----------------------------------------------------------------------------
@@ -247,3 +261,37 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
     else:
         _check(lib().moe_layer_forward_timed(*args, ctypes.cast(events, _c_void_p)), "moe_layer_forward_timed")
     return y, aux, counts
+
+
+def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float,
+                         min_capacity: int = 0, act: str, ws=None, y=None, aux=None, counts=None,
+                         capacity=None, x_bins=None):
+    """The layer with fixed-capacity buckets of C rows per expert.  Returns
+    ``(y, aux_loss, counts, capacity, x_bins)``; ``x_bins`` is ``[E * Cmax, h]`` with
+    bucket e in rows ``[e*C, (e+1)*C)``, C = ``capacity`` (a device scalar)."""
+    torch = _torch()
+    dev = x.device
+    T, h = x.shape
+    E, _, f = W1.shape
+    dt = _dt(x)
+    a = _ACT[act]
+    cmax = binned_capacity_max(T, E, k, capacity_factor, min_capacity)
+    if cmax < 0:
+        raise MoEError(1, "moe_binned_capacity_max")
+    if ws is None:
+        ws = _ws(binned_workspace_bytes(T, h, f, E, k, capacity_factor, min_capacity, dt, a), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    if aux is None:
+        aux = torch.empty((), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if capacity is None:
+        capacity = torch.empty((), dtype=torch.int32, device=dev)
+    if x_bins is None:
+        x_bins = torch.empty((E * cmax, h), dtype=x.dtype, device=dev)
+    _check(lib().moe_layer_forward_binned(_p(x), _p(W_gate), _p(logit_bias), _p(W1), _p(W3), _p(W2), T, h, f, E, k,
+                                          float(capacity_factor), int(min_capacity), a, dt, _p(y), _p(aux),
+                                          _p(counts), _p(capacity), _p(x_bins), _p(ws), ws.numel(), _stream(dev)),
+           "moe_layer_forward_binned")
+    return y, aux, counts, capacity, x_bins

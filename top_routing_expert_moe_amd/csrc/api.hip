@@ -65,6 +65,24 @@ FfnPlan layer_plan(bool bf, int32_t T, int32_t h, int32_t f, int32_t E, int32_t 
   return plan_ffn(bf, rpe, E, rows_max(T, E, k, C), h, f);
 }
 
+// Fixed-capacity buckets: the bucket size when it is known on the host (cf > 0:
+// max(floor(cf * T * k / E), min_capacity)), INT32_MAX when it is the largest count of
+// the step (cf <= 0 or a computed zero); and the bound the buffers are sized for.
+int64_t binned_cfixed(int32_t T, int32_t E, int32_t k, float cf, int32_t min_capacity) {
+  const double c = (double)cf;
+  if (!(c > 0.0)) return INT32_MAX;
+  double C = floor(c * ((double)((int64_t)k * T) / (double)E));
+  if (C < (double)min_capacity) C = (double)min_capacity;
+  if (C < 1.0) return INT32_MAX;
+  if (C >= (double)INT32_MAX) return INT32_MAX - 1;
+  return (int64_t)C;
+}
+
+int64_t binned_cmax(int32_t T, int32_t E, int32_t k, float cf, int32_t min_capacity) {
+  const int64_t C = binned_cfixed(T, E, k, cf, min_capacity);
+  return C == INT32_MAX ? (int64_t)T : C;  // an expert gets at most one assignment per token
+}
+
 moe_status_t common_sizes(int32_t T, int32_t E, int32_t k) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
   if ((int64_t)T * k > (int64_t)INT32_MAX / 2) return MOE_ERR_ARG;
@@ -133,8 +151,10 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
   w.tile_off = c.take<int>((size_t)E + 1);
   w.aux = c.take<float>(1);
   w.slot_pos = c.take<int>(n);
-  w.sorted_slot = c.take<int>(n);
-  w.perm_token = c.take<int>(n);
+  // indexed by row: the fixed-capacity layout may have more rows than assignments
+  const size_t rows = (size_t)R_max > n ? (size_t)R_max : n;
+  w.sorted_slot = c.take<int>(rows);
+  w.perm_token = c.take<int>(rows);
   w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
   w.part_up = pl.s_up > 1 ? c.take<float>((size_t)pl.s_up * R_max * up_cols(act, f)) : nullptr;
   // expert outputs stay fp32 until the combine (s_down K parts of them when the down
@@ -147,6 +167,16 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
   do {                                              \
     if ((expr) != hipSuccess) return MOE_ERR_DEVICE; \
   } while (0)
+
+struct BinnedWs { LayerWs l; int* cap; void* x_bins; };
+BinnedWs carve_binned(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int R_max, const FfnPlan& pl,
+                      moe_dtype_t dt, moe_act_t act, bool own_bins) {
+  BinnedWs w;
+  w.l = carve_layer(c, T, h, f, E, k, R_max, pl, dt, act);
+  w.cap = c.take<int>(1);
+  w.x_bins = own_bins ? c.take<char>((size_t)R_max * h * elem_bytes(dt)) : nullptr;
+  return w;
+}
 
 // The two expert GEMMs.  up: A (rows through a_rows) x W1 (and W3) -> act -> hm.
 // down: hm x W2 -> out (fp32 when out_f32, else dt).  With a K-split down projection and
@@ -438,6 +468,111 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   if (r != MOE_OK) return r;
   MOE_TRY(launch_combine(w.o, true, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
   if (!mark()) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+int32_t moe_binned_capacity_max(int32_t T, int32_t E, int32_t k, float capacity_factor, int32_t min_capacity) {
+  if (common_sizes(T, E, k) != MOE_OK || !isfinite(capacity_factor) || min_capacity < 0) return -1;
+  return (int32_t)binned_cmax(T, E, k, capacity_factor, min_capacity);
+}
+
+static moe_status_t binned_sizes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float cf,
+                                 int32_t min_capacity, int64_t* cmax) {
+  moe_status_t s = common_sizes(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!isfinite(cf) || min_capacity < 0) return MOE_ERR_ARG;
+  if ((s = dim_ok(h)) != MOE_OK) return s;
+  if ((s = dim_ok(f)) != MOE_OK) return s;
+  *cmax = binned_cmax(T, E, k, cf, min_capacity);
+  // bucket rows are int32 and the GEMMs address their operands with 32-bit element offsets
+  const int64_t rows = (int64_t)E * *cmax;
+  if (rows > INT32_MAX / 2 || rows * (int64_t)(h > f ? h : f) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_binned_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float capacity_factor,
+                                  int32_t min_capacity, moe_dtype_t dt, moe_act_t act) {
+  int64_t cmax = 0;
+  if (!dtype_ok(dt) || !act_ok(act) || binned_sizes(T, h, f, E, k, capacity_factor, min_capacity, &cmax) != MOE_OK)
+    return 0;
+  const int64_t cfix = binned_cfixed(T, E, k, capacity_factor, min_capacity);
+  const double rpe = cfix == INT32_MAX ? (double)T * k / E : (double)cfix;
+  const int R_max = (int)(E * cmax);
+  const FfnPlan pl = plan_ffn(dt == MOE_BF16, rpe, E, R_max, h, f);
+  Carve c(nullptr);
+  carve_binned(c, T, h, f, E, k, R_max, pl, dt, act, true);
+  return c.bytes();
+}
+
+moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
+                                      const void* W3, const void* W2, int32_t T, int32_t h, int32_t f, int32_t E,
+                                      int32_t k, float capacity_factor, int32_t min_capacity, moe_act_t act,
+                                      moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, int32_t* capacity,
+                                      void* x_bins, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t cmax = 0;
+  moe_status_t s = binned_sizes(T, h, f, E, k, capacity_factor, min_capacity, &cmax);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt) || !act_ok(act)) return MOE_ERR_ARG;
+  if (!x || !W_gate || !W1 || !W2 || !y) return MOE_ERR_ARG;
+  if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || (W3 && !aligned16(W3)) || !aligned16(y) ||
+      (x_bins && !aligned16(x_bins)))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const int64_t cfix = binned_cfixed(T, E, k, capacity_factor, min_capacity);
+  const double rpe = cfix == INT32_MAX ? (double)T * k / E : (double)cfix;
+  const int R_max = (int)(E * cmax);
+  const bool bf = dt == MOE_BF16;
+  const FfnPlan pl = plan_ffn(bf, rpe, E, R_max, h, f);
+  Carve c(ws);
+  BinnedWs bw = carve_binned(c, T, h, f, E, k, R_max, pl, dt, act, x_bins == nullptr);
+  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  LayerWs& w = bw.l;
+  void* xb = x_bins ? x_bins : bw.x_bins;
+
+  RouteArgs ra{};
+  ra.x = x;
+  ra.W_gate = W_gate;
+  ra.bias = logit_bias;
+  ra.T = T;
+  ra.h = h;
+  ra.E = E;
+  ra.k = k;
+  ra.bf16 = bf;
+  ra.logits = w.logits;
+  ra.topk_idx = w.topk_idx;
+  ra.topk_w = w.topk_w;
+  ra.prob_part = w.prob_part;
+  ra.blk_counts = w.blk_counts;
+  ra.planes = w.planes;
+  MOE_TRY(launch_logits(ra, stream));
+  MOE_TRY(launch_select(ra, stream));
+  ScanArgs sa{};
+  sa.blk_counts = w.blk_counts;
+  sa.nhb = route_blocks(T);
+  sa.E = E;
+  sa.T = T;
+  sa.k = k;
+  sa.C = (int)cfix;
+  sa.BM = pl.bm;
+  sa.prob_part = w.prob_part;
+  sa.nrb = route_blocks(T);
+  sa.counts = counts ? counts : w.counts;
+  sa.offsets = w.offsets;
+  sa.blk_base = w.blk_base;
+  sa.tile_off = w.tile_off;
+  sa.aux = aux_loss ? aux_loss : w.aux;
+  sa.binned = true;
+  sa.cap_out = capacity ? capacity : bw.cap;
+  MOE_TRY(launch_scan(sa, stream));
+  MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)cfix, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
+                         w.perm_token, stream));
+  MOE_TRY(launch_binned_gather(x, w.perm_token, w.offsets, sa.counts, E, R_max, h, (int)elem_bytes(dt), xb,
+                               stream));
+  moe_status_t r = run_ffn(xb, nullptr, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, W2, act, dt,
+                           w.hm, w.part_up, w.o, true, w.o, true, stream);
+  if (r != MOE_OK) return r;
+  MOE_TRY(launch_combine(w.o, true, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
   return MOE_OK;
 }
 

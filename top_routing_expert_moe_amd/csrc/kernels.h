@@ -50,8 +50,16 @@ struct ScanArgs {
   int* blk_base;           // [nhb,E]
   int* tile_off;           // [E+1] or null
   float* aux;              // scalar or null
+  // fixed-capacity buckets: every expert gets C rows (offsets[e] = e * C), C = the
+  // capacity, or the largest count when C == INT32_MAX; the bucket size goes to *cap_out
+  bool binned;
+  int* cap_out;            // scalar or null
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+// x_bins[r] = x[perm_token[r]] for filled bucket rows, zero for the rest of the E buckets
+// (bucket size offsets[1] - offsets[0], fill min(counts[e], size)); rows >= offsets[E] untouched
+hipError_t launch_binned_gather(const void* x, const int* perm_token, const int* offsets, const int* counts, int E,
+                                int R_max, int h, int elem_bytes, void* x_bins, hipStream_t st);
 
 hipError_t launch_scatter(const int* topk_idx, int T, int E, int k, int C, const int* offsets,
                           const int* blk_base, int* slot_pos, int* sorted_slot, int* perm_token,

@@ -142,7 +142,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __syncthreads();
   // kept counts -> offsets, m-tiles -> tile list: exclusive scans over the experts (4 waves)
   const int cnt = tid < E ? cnt_sh[tid] : 0;
-  const int kept = tid < E ? min(cnt, a.C) : 0;
+  int kept = tid < E ? min(cnt, a.C) : 0;
+  if (a.binned) {
+    // fixed buckets: C rows each (the largest count when no capacity is given)
+    __shared__ int cmax_sh;
+    if (tid == 0) cmax_sh = 0;
+    __syncthreads();
+    if (tid < E) atomicMax(&cmax_sh, cnt);
+    __syncthreads();
+    const int cb = a.C == INT_MAX ? cmax_sh : a.C;
+    kept = tid < E ? cb : 0;
+    if (tid == 0 && a.cap_out != nullptr) *a.cap_out = cb;
+  }
   const int mt = (tid < E && a.BM > 0) ? (kept + a.BM - 1) / a.BM : 0;
   int ik = wave_incl_scan(kept, lane, 64), im = wave_incl_scan(mt, lane, 64);
   if (wave < 4 && lane == 63) {
@@ -292,7 +303,36 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
   for (int i = threadIdx.x; i < vec_per_row; i += 256) x_perm[dst + i] = x[src + i];
 }
 
+// Fixed-capacity buckets: one workgroup per bucket row; filled rows copy their token's
+// row of x, the others are zero ([MB] section 4.5: slots past an expert's count stay zero).
+__global__ __launch_bounds__(256) void binned_gather_kernel(const u32x4* __restrict__ x,
+                                                            const int* __restrict__ perm_token,
+                                                            const int* __restrict__ offsets,
+                                                            const int* __restrict__ counts, int E,
+                                                            int vec_per_row, u32x4* __restrict__ x_bins) {
+  const int r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  const int C = offsets[1] - offsets[0];
+  const int e = r / C, i = r - e * C;
+  const size_t dst = (size_t)r * vec_per_row;
+  if (i < min(counts[e], C)) {
+    const size_t src = (size_t)perm_token[r] * vec_per_row;
+    for (int v = threadIdx.x; v < vec_per_row; v += 256) x_bins[dst + v] = x[src + v];
+  } else {
+    for (int v = threadIdx.x; v < vec_per_row; v += 256) x_bins[dst + v] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_binned_gather(const void* x, const int* perm_token, const int* offsets, const int* counts, int E,
+                                int R_max, int h, int elem_bytes, void* x_bins, hipStream_t st) {
+  if (R_max <= 0) return hipSuccess;
+  const int vec = h * elem_bytes / 16;
+  hipLaunchKernelGGL(binned_gather_kernel, dim3(R_max), dim3(256), 0, st, (const u32x4*)x, perm_token, offsets,
+                     counts, E, vec, (u32x4*)x_bins);
+  return hipGetLastError();
+}
 
 hipError_t launch_hist(const int* topk_idx, int T, int k, int E, int* blk_counts, hipStream_t st) {
   hipLaunchKernelGGL(hist_kernel, dim3(route_blocks(T)), dim3(256), 0, st, topk_idx, T, k, E, blk_counts);
