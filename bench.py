@@ -10,6 +10,11 @@ library's stream inside the timed loop), and the CPU oracle timed on a
 bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill-mixtral]
+                    [--layout compact|binned] [--capacity-factor CF] [--min-capacity N]
+
+``--layout binned`` times the fixed-capacity variant instead: every expert gets a
+bucket of C rows (zero padding past its count), the expert GEMMs run over all E*C
+bucket rows, so the padding cost shows against the compact layout.
 """
 from __future__ import annotations
 
@@ -95,6 +100,9 @@ def main():
     ap.add_argument("--workload", default="prefill-mixtral")
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("compact", "binned"), default="compact")
+    ap.add_argument("--capacity-factor", type=float, default=None, help="override the workload's factor")
+    ap.add_argument("--min-capacity", type=int, default=0, help="binned layout: the smallest bucket size")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run a plain elementwise copy (y = x + 1, fp32) over this many MiB three "
                          "times: a kernel of known traffic for calibrating rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -113,6 +121,10 @@ def main():
     import top_routing_expert_moe_amd as moe
 
     w = mw.by_name(args.workload)
+    if args.capacity_factor is not None:
+        import dataclasses
+        w = dataclasses.replace(w, cf=args.capacity_factor)
+    binned = args.layout == "binned"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.lib()  # fail loudly if the HIP library is missing
@@ -135,14 +147,28 @@ def main():
     T, h, f, E, k = w.T, w.h, w.f, w.E, w.k
     act = moe.SWIGLU if w.act == "swiglu" else moe.GELU
     dt = moe.BF16 if bf else moe.F32
-    ws = torch.empty(moe.workspace_bytes(T, h, f, E, k, w.cf, dt, act), dtype=torch.uint8, device=dev)
     y = torch.empty((T, h), dtype=d["x"].dtype, device=dev)
     aux = torch.empty((), dtype=torch.float32, device=dev)
     counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if binned:
+        mc = args.min_capacity
+        ws = torch.empty(moe.binned_workspace_bytes(T, h, f, E, k, w.cf, mc, dt, act), dtype=torch.uint8,
+                         device=dev)
+        cap = torch.empty((), dtype=torch.int32, device=dev)
+        x_bins = torch.empty((E * moe.binned_capacity_max(T, E, k, w.cf, mc), h), dtype=d["x"].dtype, device=dev)
+        stages = moe.BINNED_STAGES
 
-    def step(events=None):
-        moe.layer_forward(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
-                          capacity_factor=w.cf, act=w.act, ws=ws, y=y, aux=aux, counts=counts, events=events)
+        def step(events=None):
+            moe.layer_forward_binned(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
+                                     capacity_factor=w.cf, min_capacity=mc, act=w.act, ws=ws, y=y, aux=aux,
+                                     counts=counts, capacity=cap, x_bins=x_bins, events=events)
+    else:
+        ws = torch.empty(moe.workspace_bytes(T, h, f, E, k, w.cf, dt, act), dtype=torch.uint8, device=dev)
+        stages = moe.LAYER_STAGES
+
+        def step(events=None):
+            moe.layer_forward(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
+                              capacity_factor=w.cf, act=w.act, ws=ws, y=y, aux=aux, counts=counts, events=events)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -159,7 +185,7 @@ def main():
     torch.cuda.synchronize()
 
     hip = Hip()
-    nst = len(moe.LAYER_STAGES)
+    nst = len(stages)
     ev = [hip.events(nst + 1) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -168,10 +194,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    stage_ms = {s: 0.0 for s in moe.LAYER_STAGES}
+    stage_ms = {s: 0.0 for s in stages}
     step_ms = []  # per step, from the first to the last event (GPU time of the whole layer)
     for i in range(args.steps):
-        for j, s in enumerate(moe.LAYER_STAGES):
+        for j, s in enumerate(stages):
             stage_ms[s] += hip.elapsed_ms(ev[i][j], ev[i][j + 1]) / args.steps
         step_ms.append(hip.elapsed_ms(ev[i][0], ev[i][nst]))
     for e_ in ev:
@@ -179,9 +205,14 @@ def main():
     log("[bench] stage ms: " + ", ".join(f"{s}={v:.4f}" for s, v in stage_ms.items()))
 
     cnt = counts.cpu().numpy().astype(np.int64)
-    C = moe.capacity(T, E, k, w.cf)
-    kept = cnt if C is None else np.minimum(cnt, C)
-    R = int(kept.sum())
+    if binned:
+        C = int(cap.cpu())
+        kept = np.minimum(cnt, C)
+        R = E * C  # the GEMMs run over every bucket row, padding included
+    else:
+        C = moe.capacity(T, E, k, w.cf)
+        kept = cnt if C is None else np.minimum(cnt, C)
+        R = int(kept.sum())
     n_up = 2 if w.act == "swiglu" else 1
     flops_up = 2.0 * n_up * R * h * f
     flops_down = 2.0 * R * f * h
@@ -189,14 +220,15 @@ def main():
     up_s = stage_ms["expert_up"] / 1e3
     ms_per_step = wall / args.steps * 1e3
     es = 2 if bf else 4
-    active = int((kept > 0).sum())
+    active = E if binned else int((kept > 0).sum())
     # algorithmic bytes of the up-projection: each active expert's W1 (and W3) once, the R
     # gathered activation rows read, the R hidden rows written
     bytes_up = active * n_up * h * f * es + R * h * es + R * f * es
     bytes_down = active * f * h * es + R * f * es + R * h * 4
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    kname = ("expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue, gather fused)" if w.act == "swiglu"
-             else "expert up-projection (grouped bf16 MFMA GEMM, GELU epilogue, gather fused)")
+    kname = ("expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue, " if w.act == "swiglu"
+             else "expert up-projection (grouped bf16 MFMA GEMM, GELU epilogue, ")
+    kname += "over the E x C buckets)" if binned else "gather fused)"
     if not bf:  # the fp32 GEMM runs on the vector ALUs
         achieved = flops_up / up_s / 1e12
         roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
@@ -209,7 +241,8 @@ def main():
         achieved = bytes_up / up_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roofline.update({"traffic": traffic_entry(w.name), "kernel": kname, "flops_per_launch": flops_up,
+    roofline.update({"traffic": None if binned else traffic_entry(w.name), "kernel": kname,
+                     "flops_per_launch": flops_up,
                      "algorithmic_bytes_per_launch": bytes_up, "avg_launch_ms": round(stage_ms["expert_up"], 5)})
     # compulsory bytes of routing + permutation metadata: x and W_gate read once, logits written,
     # topk idx/w, slot_pos and the sorted order (4 B each per assignment)
@@ -218,17 +251,19 @@ def main():
     # the layer's own roof: compulsory bytes (x, W_gate, active weights, y, routing metadata) against
     # its MFMA work
     layer_bytes = T * h * es + h * E * 4 + active * (n_up + 1) * h * f * es + T * h * es + T * k * 12
-    t_roof = max((flops_up + flops_down) / (PEAK_BF16_TFLOPS * 1e12), layer_bytes / (PEAK_HBM_GBS * 1e9))
+    # (on the kept rows only: bucket padding is work the layer's own roof does not count)
+    flops_kept = 2.0 * (n_up + 1) * int(kept.sum()) * h * f
+    t_roof = max(flops_kept / (PEAK_BF16_TFLOPS * 1e12), layer_bytes / (PEAK_HBM_GBS * 1e9))
     # combine: one fp32 expert-output row per kept assignment and the routing weights read,
     # y written (a lower bound: a K-split down projection leaves two or four parts to add)
-    combine_bytes = R * h * 4 + T * h * es + T * k * 8
+    combine_bytes = int(kept.sum()) * h * 4 + T * h * es + T * k * 8
     q = np.percentile(np.array(step_ms), [10, 50, 90])
     extra = {
         "layer_ms_p10_p50_p90": [round(float(v), 5) for v in q],
         "combine_gbps_min": round(combine_bytes / (stage_ms["combine"] / 1e3) / 1e9, 1),
         "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
-        "rows_kept": R, "active_experts": active,
-        "layer_mfma_frac": round((flops_up + flops_down) / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "rows_kept": int(kept.sum()), "gemm_rows": R, "active_experts": active,
+        "layer_mfma_frac": round(flops_kept / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "layer_roofline_frac": round(t_roof / (ms_per_step / 1e3), 4),
         "expert_down_frac": round(flops_down / (stage_ms["expert_down"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "expert_up_hbm_gbs": round(bytes_up / up_s / 1e9, 1),
@@ -249,8 +284,13 @@ def main():
         ns = min(args.cpu_sample, T)
         tokens = np.arange(ns) * (T // ns)
         tc = time.perf_counter()
-        ref = o.layer_forward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"],
-                              k=k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, tokens=tokens)
+        if binned:
+            ref = o.layer_forward_binned(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"],
+                                         host["W2"], k=k, capacity_factor=w.cf, min_capacity=args.min_capacity,
+                                         act=w.act, dtype=w.dtype, tokens=tokens)
+        else:
+            ref = o.layer_forward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"],
+                                  host["W2"], k=k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, tokens=tokens)
         el = time.perf_counter() - tc
         cpu = {"value": round(ns / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
                "sample": f"full routing of all {T} tokens + expert outputs of {ns} evenly spaced tokens "
@@ -282,7 +322,7 @@ def main():
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) random weights of the layer's shape)",
         "config": {"workload": w.name, "T": T, "h": h, "f": f, "E": E, "k": k, "act": w.act,
-                   "capacity_factor": w.cf, "router": "fp32", "logit_bias": w.bias},
+                   "capacity_factor": w.cf, "router": "fp32", "logit_bias": w.bias, "layout": args.layout},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -177,6 +177,19 @@ moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const 
                                       int32_t* capacity, void* x_bins, void* ws, size_t ws_bytes,
                                       hipStream_t stream);
 
+/* Measurement variant of moe_layer_forward_binned, as moe_layer_forward_timed: events[0]
+ * before the router, then one after each stage (router logits, selection + histogram,
+ * scan, scatter, bucket gather, expert up-projection, expert down-projection, combine).
+ * `events` holds MOE_BINNED_STAGES + 1 valid hipEvent_t (MOE_ERR_ARG otherwise). */
+#define MOE_BINNED_STAGES 8
+moe_status_t moe_layer_forward_binned_timed(const void* x, const float* W_gate, const float* logit_bias,
+                                            const void* W1, const void* W3, const void* W2,
+                                            int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                            float capacity_factor, int32_t min_capacity, moe_act_t act,
+                                            moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts,
+                                            int32_t* capacity, void* x_bins, void* ws, size_t ws_bytes,
+                                            hipStream_t stream, hipEvent_t* events);
+
 /* Measurement variant of moe_layer_forward: the same kernels on the same stream, with
  * caller-created HIP events recorded between the stages, so a profiler-free caller can
  * time each kernel: events[0] before the router, then one after each stage in order

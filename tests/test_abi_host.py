@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
                           "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_forward",
                           "moe_layer_forward_timed", "moe_expert_ffn_workspace_bytes",
                           "moe_route_workspace_bytes", "moe_binned_capacity_max", "moe_binned_workspace_bytes",
-                          "moe_layer_forward_binned"}
+                          "moe_layer_forward_binned", "moe_layer_forward_binned_timed"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -221,6 +221,21 @@ def test_binned_capacity_max_dynamic_and_invalid(L):
     assert L.moe_binned_capacity_max(8, 8, 9, 1.0, 0) == -1
 
 
+def test_capacity_config_defaults(L):
+    """The Colossal-AI SparseMLP defaults: factor 1.25 in training, 2.0 in evaluation,
+    minimum capacity 4; without dropping the factor is 0 (buckets of the largest count)."""
+    cfg = moe.CapacityConfig()
+    assert (cfg.train, cfg.eval, cfg.min_capacity, cfg.drop_tokens) == (1.25, 2.0, 4, True)
+    assert cfg.factor(True) == 1.25 and cfg.factor(False) == 2.0
+    assert moe.CapacityConfig(drop_tokens=False).factor(True) == 0.0
+    # Mixtral prefill shape (T = 4096, E = 8, k = 2): 1024 assignments per expert on average
+    assert moe.binned_capacity_max(4096, 8, 2, cfg.factor(True), cfg.min_capacity) == 1280
+    assert moe.binned_capacity_max(4096, 8, 2, cfg.factor(False), cfg.min_capacity) == 2048
+    # decode: floor(1.25 * 64 * 2 / 8) = 20, floor(2.0 * 16) = 32; a tiny batch takes the minimum
+    assert moe.binned_capacity_max(64, 8, 2, cfg.factor(True), cfg.min_capacity) == 20
+    assert moe.binned_capacity_max(4, 64, 2, cfg.factor(False), cfg.min_capacity) == 4
+
+
 def test_binned_workspace_bytes(L):
     T, h, f, E, k = 4096, 1024, 4096, 64, 2
     C = o.binned_capacity(T, E, k, 1.25, 0, [0] * E)
@@ -254,6 +269,18 @@ def _binned(L, **kw):
 ])
 def test_layer_forward_binned_host_errors(L, kw, expect):
     assert _binned(L, **kw) == expect
+
+
+def test_layer_forward_binned_timed_needs_events(L):
+    a = [FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, 128, 256, 8, 2, 1.0, 0, 1, 1, FAKE, None, None, None, None, FAKE,
+         1 << 40, None]
+    assert L.moe_layer_forward_binned_timed(*a, None) == ARG
+    ev = (ctypes.c_void_p * 9)(*([FAKE] * 8 + [0]))
+    assert L.moe_layer_forward_binned_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == ARG
+    ev = (ctypes.c_void_p * 9)(*([FAKE] * 9))
+    a[12] = -1  # negative minimum capacity: rejected before any event is recorded
+    assert L.moe_layer_forward_binned_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == ARG
+    assert len(moe.BINNED_STAGES) == 8
 
 
 def test_layer_forward_binned_workspace_boundary(L):

@@ -72,6 +72,7 @@ def _run_and_check(w, host, dd, min_capacity, tokens, check_all_bins=True):
     ("prefill-mixtral", 1.0, 0),      # GShard-style capacity with drops
     ("capacity-e64", 1.25, 0),        # C = 320
     ("capacity-e64", 1.25, 400),      # the minimum capacity wins: every bucket padded
+    ("capacity-e64", 2.0, 4),         # the evaluation-time factor and minimum of the SparseMLP defaults
     ("capacity-e64", 0.0, 0),         # no factor under zipf-skewed routing: padding to the busiest expert
     ("finegrained-e256", 1.0, 0),     # C = 128 of 256 experts under skewed routing
 ])

@@ -134,7 +134,8 @@ def test_layer_forward_timed_matches_untimed():
     assert abs(sum(stages) - total) <= 1e-3 * max(total, 1e-3) + 1e-3
 
 
-def test_bench_json_contract():
+@pytest.mark.parametrize("layout", ["compact", "binned"])
+def test_bench_json_contract(layout):
     """bench.py on the small fp32 workload prints one JSON line with the fields the
     benchmark contract names."""
     import json
@@ -143,7 +144,8 @@ def test_bench_json_contract():
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--steps", "3", "--warmup", "1",
-                        "--workload", "tiny-fp32", "--cpu-sample", "64"], capture_output=True, text=True,
+                        "--workload", "tiny-fp32", "--cpu-sample", "64", "--layout", layout,
+                        "--min-capacity", "3"], capture_output=True, text=True,
                        timeout=300, cwd=root)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
@@ -153,7 +155,8 @@ def test_bench_json_contract():
                 "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
-    assert d["config"]["workload"] == "tiny-fp32" and d["dtype"] == "f32"
+    assert d["config"]["workload"] == "tiny-fp32" and d["dtype"] == "f32" and d["config"]["layout"] == layout
+    assert d["extra"]["gemm_rows"] >= d["extra"]["rows_kept"]
     rf = d["roofline"]
     assert rf["bound"] in ("hbm", "mfma", "alu") and rf["peak"] > 0 and rf["achieved"] > 0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3

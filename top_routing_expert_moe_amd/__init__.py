@@ -12,6 +12,7 @@ Entry points mirror the C ABI in ``include/moe.h``: ``route``, ``permute``,
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 
 __all__ = ["MoEError", "lib", "lib_path", "capacity", "workspace_bytes", "status_string", "route",
@@ -61,9 +62,14 @@ _SIGS = {
                                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
                                                 ctypes.c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                 _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_layer_forward_binned_timed": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                      _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                                      ctypes.c_int, ctypes.c_int, _c_void_p, _c_void_p, _c_void_p,
+                                                      _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p, _c_void_p]),
 }
 
 LAYER_STAGES = ("logits", "select", "scan", "scatter", "expert_up", "expert_down", "combine")
+BINNED_STAGES = ("logits", "select", "scan", "scatter", "gather", "expert_up", "expert_down", "combine")
 
 _lib = None
 
@@ -108,6 +114,23 @@ def capacity(T: int, E: int, k: int, capacity_factor: float) -> int | None:
 
 def workspace_bytes(T, h, f, E, k, capacity_factor, dtype: int, act: int) -> int:
     return int(lib().moe_workspace_bytes(T, h, f, E, k, capacity_factor, dtype, act))
+
+
+@dataclasses.dataclass(frozen=True)
+class CapacityConfig:
+    """Capacity settings of a fixed-capacity layer, after the SparseMLP parameters of the
+    Colossal-AI MoE page: one factor for training and one for evaluation, a minimum bucket
+    size, and whether assignments past the capacity are dropped.  Without dropping, the
+    bucket is the largest expert count of the call (factor 0), so nothing is dropped."""
+    train: float = 1.25
+    eval: float = 2.0
+    min_capacity: int = 4
+    drop_tokens: bool = True
+
+    def factor(self, training: bool) -> float:
+        if not self.drop_tokens:
+            return 0.0
+        return float(self.train if training else self.eval)
 
 
 def binned_capacity_max(T, E, k, capacity_factor, min_capacity) -> int:
@@ -265,10 +288,11 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
 
 def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float,
                          min_capacity: int = 0, act: str, ws=None, y=None, aux=None, counts=None,
-                         capacity=None, x_bins=None):
+                         capacity=None, x_bins=None, events=None):
     """The layer with fixed-capacity buckets of C rows per expert.  Returns
     ``(y, aux_loss, counts, capacity, x_bins)``; ``x_bins`` is ``[E * Cmax, h]`` with
-    bucket e in rows ``[e*C, (e+1)*C)``, C = ``capacity`` (a device scalar)."""
+    bucket e in rows ``[e*C, (e+1)*C)``, C = ``capacity`` (a device scalar).
+    ``events``: ``len(BINNED_STAGES) + 1`` hipEvent_t handles recorded between the stages."""
     torch = _torch()
     dev = x.device
     T, h = x.shape
@@ -290,8 +314,12 @@ def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_
         capacity = torch.empty((), dtype=torch.int32, device=dev)
     if x_bins is None:
         x_bins = torch.empty((E * cmax, h), dtype=x.dtype, device=dev)
-    _check(lib().moe_layer_forward_binned(_p(x), _p(W_gate), _p(logit_bias), _p(W1), _p(W3), _p(W2), T, h, f, E, k,
-                                          float(capacity_factor), int(min_capacity), a, dt, _p(y), _p(aux),
-                                          _p(counts), _p(capacity), _p(x_bins), _p(ws), ws.numel(), _stream(dev)),
-           "moe_layer_forward_binned")
+    args = (_p(x), _p(W_gate), _p(logit_bias), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor),
+            int(min_capacity), a, dt, _p(y), _p(aux), _p(counts), _p(capacity), _p(x_bins), _p(ws), ws.numel(),
+            _stream(dev))
+    if events is None:
+        _check(lib().moe_layer_forward_binned(*args), "moe_layer_forward_binned")
+    else:
+        _check(lib().moe_layer_forward_binned_timed(*args, ctypes.cast(events, _c_void_p)),
+               "moe_layer_forward_binned_timed")
     return y, aux, counts, capacity, x_bins

@@ -504,11 +504,12 @@ size_t moe_binned_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, in
   return c.bytes();
 }
 
-moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
-                                      const void* W3, const void* W2, int32_t T, int32_t h, int32_t f, int32_t E,
-                                      int32_t k, float capacity_factor, int32_t min_capacity, moe_act_t act,
-                                      moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, int32_t* capacity,
-                                      void* x_bins, void* ws, size_t ws_bytes, hipStream_t stream) {
+static moe_status_t layer_forward_binned_impl(const void* x, const float* W_gate, const float* logit_bias,
+                                              const void* W1, const void* W3, const void* W2, int32_t T, int32_t h,
+                                              int32_t f, int32_t E, int32_t k, float capacity_factor,
+                                              int32_t min_capacity, moe_act_t act, moe_dtype_t dt, void* y,
+                                              float* aux_loss, int32_t* counts, int32_t* capacity, void* x_bins,
+                                              void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
   int64_t cmax = 0;
   moe_status_t s = binned_sizes(T, h, f, E, k, capacity_factor, min_capacity, &cmax);
   if (s != MOE_OK) return s;
@@ -529,6 +530,9 @@ moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const 
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   LayerWs& w = bw.l;
   void* xb = x_bins ? x_bins : bw.x_bins;
+  int stage = 0;
+  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
+  if (!mark()) return MOE_ERR_DEVICE;
 
   RouteArgs ra{};
   ra.x = x;
@@ -546,7 +550,9 @@ moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const 
   ra.blk_counts = w.blk_counts;
   ra.planes = w.planes;
   MOE_TRY(launch_logits(ra, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   MOE_TRY(launch_select(ra, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   ScanArgs sa{};
   sa.blk_counts = w.blk_counts;
   sa.nhb = route_blocks(T);
@@ -565,15 +571,42 @@ moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const 
   sa.binned = true;
   sa.cap_out = capacity ? capacity : bw.cap;
   MOE_TRY(launch_scan(sa, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)cfix, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
                          w.perm_token, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   MOE_TRY(launch_binned_gather(x, w.perm_token, w.offsets, sa.counts, E, R_max, h, (int)elem_bytes(dt), xb,
                                stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   moe_status_t r = run_ffn(xb, nullptr, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, W2, act, dt,
-                           w.hm, w.part_up, w.o, true, w.o, true, stream);
+                           w.hm, w.part_up, w.o, true, w.o, true, stream,
+                           ev ? [&]() { return mark(); } : std::function<bool()>());
   if (r != MOE_OK) return r;
   MOE_TRY(launch_combine(w.o, true, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
+}
+
+moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
+                                      const void* W3, const void* W2, int32_t T, int32_t h, int32_t f, int32_t E,
+                                      int32_t k, float capacity_factor, int32_t min_capacity, moe_act_t act,
+                                      moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, int32_t* capacity,
+                                      void* x_bins, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_forward_binned_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, min_capacity,
+                                   act, dt, y, aux_loss, counts, capacity, x_bins, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status_t moe_layer_forward_binned_timed(const void* x, const float* W_gate, const float* logit_bias,
+                                            const void* W1, const void* W3, const void* W2, int32_t T, int32_t h,
+                                            int32_t f, int32_t E, int32_t k, float capacity_factor,
+                                            int32_t min_capacity, moe_act_t act, moe_dtype_t dt, void* y,
+                                            float* aux_loss, int32_t* counts, int32_t* capacity, void* x_bins,
+                                            void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  if (events == nullptr) return MOE_ERR_ARG;
+  for (int i = 0; i < MOE_BINNED_STAGES + 1; ++i)
+    if (events[i] == nullptr) return MOE_ERR_ARG;
+  return layer_forward_binned_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, min_capacity,
+                                   act, dt, y, aux_loss, counts, capacity, x_bins, ws, ws_bytes, stream, events);
 }
 
 moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
