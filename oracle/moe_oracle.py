@@ -46,6 +46,7 @@ __all__ = [
     "topk_weights", "expert_capacity", "histogram", "permute", "silu", "gelu",
     "expert_ffn", "combine", "aux_loss", "layer_forward",
     "binned_capacity", "binned_layout", "layer_forward_binned",
+    "jitter_input", "noisy_logits", "softmax_t", "topk_weights_t", "uniform_assignment", "route",
 ]
 
 
@@ -135,6 +136,78 @@ def topk_weights(logits: np.ndarray, topk_idx: np.ndarray) -> np.ndarray:
     p = softmax(logits)
     sel = np.take_along_axis(p, np.asarray(topk_idx, dtype=np.int64), axis=1)
     return (sel / sel.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# router variants: jitter, gate noise, softmax temperature, uniform assignment
+
+def jitter_input(x: np.ndarray, u: np.ndarray, dtype: str) -> np.ndarray:
+    """The router's input under multiplicative jitter: ``x * u`` elementwise, stored in
+    the input's dtype ([MB] section 5: during training the router input may be
+    multiplied by uniform noise in [1 - eps, 1 + eps], an exploration aid from Switch).
+    Readings: the noise ``u`` is drawn by the caller in x's dtype (it is an input
+    here); the product is rounded once to that dtype (bf16: round to nearest even);
+    only the router sees the jittered input -- the experts get x.  Returns bf16 bit
+    patterns or fp32 values."""
+    prod = _as_f64(x, dtype) * _as_f64(u, dtype)
+    return round_to_bf16(prod) if dtype == "bf16" else prod.astype(np.float32)
+
+
+def noisy_logits(logits: np.ndarray, noise) -> np.ndarray:
+    """Gate logits with additive noise ([CAI] Top2Router with a NormalNoiseGenerator:
+    Gaussian noise scaled by the expert count is added to the router scores during
+    training).  Readings: the noise [T,E] is an input (the caller draws it); it is
+    added in fp32, so selection sees exactly the fp32 sum; every later step (softmax,
+    top-k, weights, aux loss) uses the noisy logits."""
+    l = np.asarray(logits, dtype=np.float32)
+    if noise is None:
+        return l
+    return (l + np.asarray(noise, dtype=np.float32)).astype(np.float32)
+
+
+def softmax_t(logits: np.ndarray, temperature: float) -> np.ndarray:
+    """Row softmax of ``logits / temperature`` in fp64 ([OPS] "坑3：数值稳定性": a
+    softmax with a temperature, so that experts that are not selected keep some
+    probability).  temperature = 1 is :func:`softmax`."""
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    z = np.exp((l - l.max(axis=1, keepdims=True)) / float(temperature))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def topk_weights_t(logits: np.ndarray, topk_idx: np.ndarray, temperature: float) -> np.ndarray:
+    """Renormalised weights of the selected experts under the temperature softmax:
+    ``w[t,j] = p[t,S_j] / sum_j' p[t,S_j']``, ``p = softmax(l / temperature)``.
+    Readings ([OPS] "坑3"): the page names a temperature softmax without fixing where it
+    enters; here it shapes the probabilities (weights and aux loss) while the
+    selection still ranks the logits (the same order for any temperature > 0), and
+    the weights are still renormalised over the k selected experts."""
+    p = softmax_t(logits, temperature)
+    sel = np.take_along_axis(p, np.asarray(topk_idx, dtype=np.int64), axis=1)
+    return (sel / sel.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def uniform_assignment(T: int, k: int, E: int) -> np.ndarray:
+    """Benchmark mode of [MB] section 5: the expert ids are replaced by
+    ``arange(T*k) % E`` laid out as [T,k] (slot j of token t gets ``(t*k + j) % E``),
+    a perfectly balanced assignment for measuring speed without a trained router.
+    Reading: only the ids are replaced; the weights stay those of the real top-k."""
+    return (np.arange(T * k, dtype=np.int64) % E).astype(np.int32).reshape(T, k)
+
+
+def route(logits: np.ndarray, k: int, *, noise=None, temperature: float = 1.0,
+          uniform: bool = False) -> dict:
+    """Selection with the router variants applied in the pages' order: noise on the
+    logits, top-k on the (noisy) logits, temperature-softmax weights renormalised over
+    the selection, ids optionally replaced by the uniform assignment.  Returns
+    ``topk_idx``, ``topk_w``, ``probs`` (for the aux loss) and the logits used."""
+    if not (float(temperature) > 0.0 and math.isfinite(float(temperature))):
+        raise ValueError("temperature must be finite and > 0")
+    l = noisy_logits(logits, noise)
+    idx = select_topk(l, k)
+    w = topk_weights_t(l, idx, temperature)
+    if uniform:
+        idx = uniform_assignment(l.shape[0], k, l.shape[1])
+    return dict(logits=l, topk_idx=idx, topk_w=w, probs=softmax_t(l, temperature))
 
 
 # ----------------------------------------------------------------------------
@@ -289,28 +362,32 @@ def aux_loss(counts: np.ndarray, probs: np.ndarray, T: int, k: int, E: int) -> f
 # the whole layer
 
 def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float,
-                  act: str, dtype: str, logits=None, tokens=None, with_y: bool = True) -> dict:
+                  act: str, dtype: str, logits=None, tokens=None, with_y: bool = True,
+                  jitter=None, noise=None, temperature: float = 1.0, uniform: bool = False) -> dict:
     """Router -> top-k -> permute (with capacity) -> experts -> weighted combine, plus aux.
 
     ``logits`` may be given (fp32 [T,E]) to route on another implementation's
     logits, so that integer routing results can be compared bit for bit.
     ``tokens`` restricts the expensive output ``y`` to a subset of tokens
     (routing, capacity and aux always cover all tokens).  ``y`` is returned in
-    the storage dtype: fp32 values, or bf16 bit patterns.
+    the storage dtype: fp32 values, or bf16 bit patterns.  ``jitter``, ``noise``,
+    ``temperature`` and ``uniform`` are the router variants (:func:`jitter_input`,
+    :func:`route`); the experts always read the unjittered x.
     """
     x = np.asarray(x)
     T = x.shape[0]
     E = np.asarray(W_gate).shape[1]
     if logits is None:
-        logits = router_logits(x, W_gate, logit_bias, dtype)
+        xr = x if jitter is None else jitter_input(x, jitter, dtype)
+        logits = router_logits(xr, W_gate, logit_bias, dtype)
     logits = np.asarray(logits, dtype=np.float32)
-    idx = select_topk(logits, k)
-    w = topk_weights(logits, idx)
+    r = route(logits, k, noise=noise, temperature=temperature, uniform=uniform)
+    idx, w = r["topk_idx"], r["topk_w"]
     C = expert_capacity(T, E, k, capacity_factor)
     counts, offsets, sorted_slot, slot_pos = permute(idx, E, C)
     out = dict(logits=logits, topk_idx=idx, topk_w=w, C=C, counts=counts, offsets=offsets,
                sorted_slot=sorted_slot, slot_pos=slot_pos,
-               aux=aux_loss(counts, softmax(logits), T, k, E))
+               aux=aux_loss(counts, r["probs"], T, k, E))
     if with_y:
         tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
         y64 = combine(x, idx, w, slot_pos, W1, W3, W2, act, dtype, tokens=tok)

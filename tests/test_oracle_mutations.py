@@ -75,7 +75,20 @@ def _binned_capacity_no_minimum(T, E, k, cf, min_capacity, counts):
     return _orig["binned_capacity"](T, E, k, cf, 0, counts)
 
 
-_orig = {n: getattr(om, n) for n in ("router_logits", "permute", "binned_layout", "binned_capacity")}
+def _softmax_t_times(logits, temperature):
+    # multiplies by the temperature instead of dividing
+    return _orig["softmax_t"](logits, 1.0 / float(temperature))
+
+
+def _uniform_transposed(T, k, E):
+    return ((np.arange(k)[None, :] * T + np.arange(T)[:, None]) % E).astype(np.int32)
+
+
+def _noise_ignored(logits, noise):
+    return np.asarray(logits, dtype=np.float32)
+
+
+_orig = {n: getattr(om, n) for n in ("router_logits", "permute", "binned_layout", "binned_capacity", "softmax_t")}
 
 MUTANTS = [
     ("select_topk", _topk_ties_high, ["test_topk_ties_and_signed_zero"]),
@@ -88,6 +101,9 @@ MUTANTS = [
     ("silu", _silu_sign, ["test_gelu_silu_vs_math", "test_single_expert_is_plain_ffn"]),
     ("binned_layout", _binned_keep_last, ["test_binned_worked_example"]),
     ("binned_capacity", _binned_capacity_no_minimum, ["test_binned_capacity_rules", "test_binned_worked_example"]),
+    ("softmax_t", _softmax_t_times, ["test_temperature_closed_form_on_the_worked_example"]),
+    ("uniform_assignment", _uniform_transposed, ["test_uniform_assignment_ids_counts_and_aux"]),
+    ("noisy_logits", _noise_ignored, ["test_noise_decides_the_selection"]),
 ]
 
 

@@ -462,3 +462,140 @@ def test_binned_layer_vs_brute_force(T, h, f, E, k, cf, act, dtype):
             s = r["bins"][e, i]
             want = x[s // k] if s >= 0 else np.zeros_like(x[0])
             assert np.array_equal(r["x_bins"][e, i], want)
+
+
+# ----------------------------------------------------------------------------
+# router variants: temperature, gate noise, uniform assignment, jitter
+
+def test_temperature_one_is_the_plain_router():
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((40, 16)).astype(np.float32)
+    r = o.route(l, 4)
+    idx = o.select_topk(l, 4)
+    assert np.array_equal(r["topk_idx"], idx)
+    assert np.array_equal(r["topk_w"], o.topk_weights(l, idx))
+    assert np.array_equal(r["probs"], o.softmax(l))
+
+
+def test_temperature_closed_form_on_the_worked_example():
+    """k = 2 on the [OPS] worked example (experts 0 and 6, scores 0.9 and 0.7): the
+    renormalised pair is a logistic of the score gap over the temperature,
+    w0 = 1 / (1 + exp(-(0.9 - 0.7) / tau))."""
+    g = _gold("ops_top2_example.json")
+    l = np.array([g["scores"]], dtype=np.float32)
+    for tau in (0.5, 2.0, 0.1):
+        r = o.route(l, 2, temperature=tau)
+        assert r["topk_idx"].tolist() == [g["topk_idx"]]   # selection does not move with tau
+        gap = float(np.float32(0.9)) - float(np.float32(0.7))
+        w0 = 1.0 / (1.0 + math.exp(-gap / tau))
+        np.testing.assert_allclose(r["topk_w"][0], [w0, 1.0 - w0], rtol=3e-7)
+        # the full probabilities are the plain softmax of the scores over tau
+        z = np.exp((np.array(g["scores"], np.float32).astype(np.float64) - 0.9) / tau)
+        np.testing.assert_allclose(r["probs"][0], z / z.sum(), rtol=1e-6)
+
+
+def test_temperature_limits():
+    rng = np.random.default_rng(6)
+    l = (rng.permutation(64).reshape(8, 8) / 8.0).astype(np.float32)  # distinct logits, gaps >= 1/8
+    hot = o.route(l, 3, temperature=1e9)["topk_w"]
+    np.testing.assert_allclose(hot, 1.0 / 3.0, rtol=1e-6)               # flat: uniform weights
+    cold = o.route(l, 3, temperature=1e-3)["topk_w"]
+    np.testing.assert_allclose(cold[:, 0], 1.0, atol=1e-30)             # sharp: all weight on the best
+    with pytest.raises(ValueError):
+        o.route(l, 3, temperature=0.0)
+
+
+def test_noise_shift_per_token_changes_nothing():
+    """Softmax and top-k are invariant to adding one constant to all logits of a token.
+    Logits on a 2^-10 grid plus whole-number shifts are exact in fp32, so the noisy
+    selection is bit-identical and the weights equal to fp64 rounding."""
+    rng = np.random.default_rng(7)
+    l = (rng.integers(-2048, 2048, size=(32, 12)) / 1024.0).astype(np.float32)
+    shift = rng.integers(-8, 9, size=(32, 1)).astype(np.float32) * np.ones((1, 12), np.float32)
+    a, b = o.route(l, 3), o.route(l, 3, noise=shift)
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    np.testing.assert_allclose(b["topk_w"], a["topk_w"], rtol=1e-6)
+    np.testing.assert_allclose(b["probs"], a["probs"], rtol=1e-12)
+
+
+def test_noise_decides_the_selection():
+    l = np.zeros((6, 5), np.float32)
+    noise = np.zeros((6, 5), np.float32)
+    for t in range(6):
+        noise[t, (t * 2) % 5] = 4.0
+    r = o.route(l, 2, noise=noise)
+    assert r["topk_idx"][:, 0].tolist() == [(t * 2) % 5 for t in range(6)]
+    # second place: the equal zeros, lowest expert first
+    assert r["topk_idx"][:, 1].tolist() == [1 if (t * 2) % 5 == 0 else 0 for t in range(6)]
+    # noise equal to minus the logits leaves all-equal scores: experts 0..k-1, equal weights
+    l2 = np.random.default_rng(8).standard_normal((4, 6)).astype(np.float32)
+    r2 = o.route(l2, 3, noise=-l2)
+    assert r2["topk_idx"].tolist() == [[0, 1, 2]] * 4
+    np.testing.assert_allclose(r2["topk_w"], 1.0 / 3.0, rtol=1e-7)
+
+
+def test_uniform_assignment_ids_counts_and_aux():
+    # ids of slot j of token t: (t*k + j) % E, written out for T = 3, k = 2, E = 4
+    assert o.uniform_assignment(3, 2, 4).tolist() == [[0, 1], [2, 3], [0, 1]]
+    rng = np.random.default_rng(9)
+    l = rng.standard_normal((48, 8)).astype(np.float32)
+    r = o.route(l, 2, uniform=True)
+    counts = o.histogram(r["topk_idx"], 8)
+    assert (counts == 12).all()
+    # the weights are those of the real top-k
+    assert np.array_equal(r["topk_w"], o.topk_weights(l, o.select_topk(l, 2)))
+    # perfectly balanced counts: the aux loss is sum_e P_e = 1 whatever the router says
+    assert abs(o.aux_loss(counts, r["probs"], 48, 2, 8) - 1.0) < 1e-12
+
+
+def test_jitter_input_vs_torch_and_identity():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(10)
+    x = mw.f32_to_bf16_bits(rng.standard_normal((16, 64)).astype(np.float32))
+    u = mw.f32_to_bf16_bits(rng.uniform(0.99, 1.01, size=(16, 64)).astype(np.float32))
+    got = o.jitter_input(x, u, "bf16")
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    tu = torch.from_numpy(u.view(np.int16)).view(torch.bfloat16)
+    want = (tx * tu).view(torch.int16).numpy().view(np.uint16)   # torch: fp32 product, RNE to bf16
+    assert np.array_equal(got, want)
+    one = mw.f32_to_bf16_bits(np.ones((16, 64), np.float32))
+    assert np.array_equal(o.jitter_input(x, one, "bf16"), x)
+    xf = rng.standard_normal((4, 8)).astype(np.float32)
+    uf = rng.uniform(0.9, 1.1, (4, 8)).astype(np.float32)
+    assert np.array_equal(o.jitter_input(xf, uf, "f32"), xf * uf)   # fp32: one rounding of the product
+
+
+def test_layer_router_variants_vs_brute_force():
+    """The layer with jitter, noise, a temperature and the uniform assignment against the
+    pure-Python brute force fed the same variant routing."""
+    rng = np.random.default_rng(11)
+    T, h, f, E, k = 12, 16, 24, 5, 2
+    x = rng.standard_normal((T, h)).astype(np.float32)
+    Wg = (rng.standard_normal((h, E)) / 4).astype(np.float32)
+    W1 = (rng.standard_normal((E, h, f)) / 4).astype(np.float32)
+    W2 = (rng.standard_normal((E, f, h)) / 5).astype(np.float32)
+    u = rng.uniform(0.9, 1.1, (T, h)).astype(np.float32)
+    noise = (rng.standard_normal((T, E)) / E).astype(np.float32)
+    for uniform in (False, True):
+        ref = o.layer_forward(x, Wg, None, W1, None, W2, k=k, capacity_factor=0.0, act="gelu", dtype="f32",
+                              jitter=u, noise=noise, temperature=0.7, uniform=uniform)
+        # routing of the variant, recomputed step by step from its definitions
+        xr = x * u
+        lg = (xr.astype(np.float64) @ Wg.astype(np.float64)).astype(np.float32)
+        ln = (lg + noise).astype(np.float32)
+        idx = np.argsort(-ln.astype(np.float64), axis=1, kind="stable")[:, :k]
+        p = np.exp((ln.astype(np.float64) - ln.max(1, keepdims=True)) / 0.7)
+        ps = np.take_along_axis(p, idx, 1)
+        w = ps / ps.sum(1, keepdims=True)
+        if uniform:
+            idx = (np.arange(T * k) % E).reshape(T, k)
+        y = np.zeros((T, h))
+        for t in range(T):
+            for j in range(k):
+                e = idx[t, j]
+                a = np.array([math.fsum(float(x[t, i]) * float(W1[e, i, c]) for i in range(h)) for c in range(f)])
+                hm = 0.5 * a * (1 + np.array([math.erf(v / math.sqrt(2)) for v in a]))
+                y[t] += w[t, j] * np.array([math.fsum(hm[c] * float(W2[e, c, i]) for c in range(f))
+                                            for i in range(h)])
+        assert np.array_equal(ref["topk_idx"], idx)
+        np.testing.assert_allclose(ref["y64"], y, rtol=1e-5, atol=1e-6)
