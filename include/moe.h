@@ -94,6 +94,37 @@ moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bi
                        float* logits, int32_t* topk_idx, float* topk_w, float* prob_sum,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Router variants, for training and benchmarking (all optional; NULL options = the plain
+ * router).  Random numbers are inputs: the caller draws them.
+ *   jitter      [T,h] in x's dtype or NULL: the router sees x * jitter, rounded to the
+ *               dtype (bf16: to nearest even); the experts still read x.  Multiplicative
+ *               noise in [1-eps, 1+eps] on the router input ([MB] section 5, jitter).
+ *   logit_noise [T,E] fp32 or NULL: added (in fp32) to the logits before the softmax and
+ *               the top-k ([CAI] Top2Router with a NormalNoiseGenerator); the logits
+ *               returned by moe_route_ex are the router's own, without the noise.
+ *   temperature > 0: probabilities = softmax(logits / temperature), used for the weights
+ *               and the aux loss; the selection still ranks the (noisy) logits ([OPS]
+ *               "坑3": a softmax with a temperature as the soft top-K remedy).  1 = plain.
+ *   uniform_assignment nonzero: the expert id of slot j of token t is replaced by
+ *               (t*k + j) % E; the weights stay those of the real top-k ([MB] section 5,
+ *               the benchmark-only uniform assignment).
+ * Errors: MOE_ERR_ARG for a temperature that is not finite and > 0, or jitter together
+ * with MOE_ROUTE_LOGITS_IN; MOE_ERR_UNSUPPORTED for a jitter buffer or x not 16-byte
+ * aligned.  With jitter the entry points need moe_router_opts_workspace_bytes(...) bytes
+ * of workspace beyond their usual amount (the jittered router input). */
+typedef struct {
+  const void* jitter;
+  const float* logit_noise;
+  float temperature;
+  int32_t uniform_assignment;
+} moe_router_opts_t;
+size_t moe_router_opts_workspace_bytes(int32_t T, int32_t h, moe_dtype_t dt, const moe_router_opts_t* opts);
+moe_status_t moe_route_ex(const void* x, const float* W_gate, const float* logit_bias,
+                          int32_t T, int32_t h, int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags,
+                          const moe_router_opts_t* opts, float* logits, int32_t* topk_idx,
+                          float* topk_w, float* prob_sum, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* Permutation: histogram, capacity, prefix sum and a STABLE sort of the T*k assignments
  * s = t*k+j by expert id, then the gather of token rows ([MB] sections 4.1, 4.2, 4.5, 4.6).
  *   topk_idx [T,k] int32 (ids in [0,E)),  x [T,h] (dt) -- may be NULL when x_perm is NULL
@@ -150,6 +181,15 @@ moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* 
                                float capacity_factor, moe_act_t act, moe_dtype_t dt,
                                void* y, float* aux_loss, int32_t* counts,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward with the router variants of moe_router_opts_t (NULL = plain).  ws:
+ * moe_workspace_bytes(...) + moe_router_opts_workspace_bytes(T,h,dt,opts) bytes. */
+moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const float* logit_bias,
+                                  const void* W1, const void* W3, const void* W2,
+                                  int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                  float capacity_factor, moe_act_t act, moe_dtype_t dt,
+                                  const moe_router_opts_t* opts, void* y, float* aux_loss,
+                                  int32_t* counts, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The layer with fixed-capacity buckets ("binned" layout: [MB] sections 3, 4.3 and 4.5;
  * [CAI] SparseMLP data flow step 4 and its capacity parameters).  Every expert gets a

@@ -36,7 +36,7 @@ import os
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "by_name", "make_inputs", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "uniform_assignment"]
+           "bf16_bits_to_f32", "uniform_assignment", "router_variant_inputs"]
 
 
 @dataclass(frozen=True)
@@ -93,7 +93,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # generators
 
-_TENSOR_ID = {"x": 1, "W_gate": 2, "logit_bias": 3, "W1": 4, "W3": 5, "W2": 6}
+_TENSOR_ID = {"x": 1, "W_gate": 2, "logit_bias": 3, "W1": 4, "W3": 5, "W2": 6, "jitter": 7, "noise": 8}
 
 
 def _stream(seed: int, name: str, e: int = 0) -> np.random.Generator:
@@ -179,3 +179,14 @@ def uniform_assignment(T: int, E: int, k: int) -> np.ndarray:
     """Benchmark-mode expert ids ``(t*k + j) % E`` as int32 [T,k] (every expert equally loaded
     when E divides T*k).  The MegaBlocks chapter describes this mode for its router."""
     return (np.arange(T * k, dtype=np.int64) % E).astype(np.int32).reshape(T, k)
+
+
+def router_variant_inputs(w: Workload, eps: float = 0.01, noise_std: float | None = None, seed: int = 0) -> dict:
+    """Random draws of the router variants, seeded like the other inputs:
+    ``jitter`` [T,h] ~ U[1 - eps, 1 + eps] in the workload's dtype (bf16 bit patterns or
+    fp32), and gate ``noise`` [T,E] fp32 ~ N(0, noise_std^2), noise_std = 1/E by default
+    (noise scaled by the expert count)."""
+    std = 1.0 / w.E if noise_std is None else noise_std
+    u = _stream(seed, "jitter").uniform(1.0 - eps, 1.0 + eps, size=(w.T, w.h)).astype(np.float32)
+    noise = _normal(seed, "noise", 0, (w.T, w.E), std)
+    return dict(jitter=f32_to_bf16_bits(u) if w.dtype == "bf16" else u, noise=noise)

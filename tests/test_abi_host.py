@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(L):
                           "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_forward",
                           "moe_layer_forward_timed", "moe_expert_ffn_workspace_bytes",
                           "moe_route_workspace_bytes", "moe_binned_capacity_max", "moe_binned_workspace_bytes",
-                          "moe_layer_forward_binned", "moe_layer_forward_binned_timed"}
+                          "moe_layer_forward_binned", "moe_layer_forward_binned_timed",
+                          "moe_router_opts_workspace_bytes", "moe_route_ex", "moe_layer_forward_ex"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -286,6 +287,59 @@ def test_layer_forward_binned_timed_needs_events(L):
 def test_layer_forward_binned_workspace_boundary(L):
     need = moe.binned_workspace_bytes(64, 128, 256, 8, 2, 1.0, 0, 1, 1)
     assert _binned(L, ws_bytes=need - 1) == WS
+
+
+def _ropts(jitter=None, noise=None, temperature=1.0, uniform=0):
+    return ctypes.byref(moe.RouterOpts(jitter, noise, temperature, uniform))
+
+
+def test_router_opts_workspace_bytes(L):
+    assert L.moe_router_opts_workspace_bytes(4096, 4096, 1, None) == 0
+    assert L.moe_router_opts_workspace_bytes(4096, 4096, 1, _ropts(noise=FAKE, temperature=0.5)) == 0
+    assert L.moe_router_opts_workspace_bytes(4096, 4096, 1, _ropts(jitter=FAKE)) == 4096 * 4096 * 2
+    assert L.moe_router_opts_workspace_bytes(3, 64, 1, _ropts(jitter=FAKE)) == 512   # 384 rounded up to 256
+    assert L.moe_router_opts_workspace_bytes(-1, 64, 0, _ropts(jitter=FAKE)) == 0
+
+
+def test_route_ex_host_errors(L):
+    r = L.moe_route_ex
+    # (x, Wg, bias, T, h, E, k, dt, flags, opts, logits, idx, w, prob_sum, ws, ws_bytes, stream)
+    base = [FAKE, FAKE, None, 8, 64, 8, 2, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None]
+
+    def call(opts, **ch):
+        a = list(base)
+        a[9] = opts
+        names = {"x": 0, "T": 3, "flags": 8, "ws": 14, "wsb": 15}
+        for kk, v in ch.items():
+            a[names[kk]] = v
+        return r(*a)
+
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(_ropts(temperature=bad)) == ARG
+    assert call(_ropts(jitter=FAKE), flags=1) == ARG            # jitter needs the router input
+    assert call(_ropts(jitter=MIS)) == UNSUP
+    assert call(_ropts(jitter=FAKE), x=MIS) == UNSUP
+    need = L.moe_route_workspace_bytes(8, 64, 8, 1, 0, 0) + L.moe_router_opts_workspace_bytes(8, 64, 1, _ropts(FAKE))
+    assert call(_ropts(jitter=FAKE), wsb=need - 1) == WS
+    assert call(_ropts(jitter=FAKE), ws=None, wsb=0) == WS
+    assert call(_ropts(temperature=0.0), T=0) == ARG             # options are checked before the empty-batch exit
+    assert call(_ropts(temperature=2.0), T=0) == OK
+
+
+def test_layer_forward_ex_host_errors(L):
+    def call(opts, ws_bytes=1 << 40, **kw):
+        a = dict(x=FAKE, T=64, h=128, f=256, E=8, k=2)
+        a.update(kw)
+        return L.moe_layer_forward_ex(a["x"], FAKE, None, FAKE, FAKE, FAKE, a["T"], a["h"], a["f"], a["E"], a["k"],
+                                      0.0, 1, 1, opts, FAKE, None, None, FAKE, ws_bytes, None)
+    assert call(_ropts(temperature=0.0)) == ARG
+    assert call(_ropts(jitter=MIS)) == UNSUP
+    assert call(_ropts(), h=96) == UNSUP
+    need = moe.workspace_bytes(64, 128, 256, 8, 2, 0.0, 1, 1)
+    extra = L.moe_router_opts_workspace_bytes(64, 128, 1, _ropts(FAKE))
+    assert extra == 64 * 128 * 2
+    assert call(_ropts(jitter=FAKE), ws_bytes=need + extra - 1) == WS
+    assert call(_ropts(jitter=FAKE), T=0) == OK
 
 
 def test_binding_refuses_cpu_tensors(L):

@@ -32,6 +32,15 @@ _i32 = ctypes.c_int32
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 
+class RouterOpts(ctypes.Structure):
+    """moe_router_opts_t: router-input jitter, gate noise, softmax temperature, uniform
+    expert assignment (device pointers as integers, or None)."""
+    _fields_ = [("jitter", ctypes.c_void_p), ("logit_noise", ctypes.c_void_p), ("temperature", ctypes.c_float),
+                ("uniform_assignment", ctypes.c_int32)]
+
+
+_opts_p = ctypes.POINTER(RouterOpts)
+
 _SIGS = {
     "moe_capacity": (_i32, [_i32, _i32, _i32, _f32]),
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int]),
@@ -56,6 +65,14 @@ _SIGS = {
                                                _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
                                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p,
                                                _c_void_p]),
+    "moe_router_opts_workspace_bytes": (_sz, [_i32, _i32, ctypes.c_int, _opts_p]),
+    "moe_route_ex": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                    ctypes.c_uint32, _opts_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_void_p, _sz, _c_void_p]),
+    "moe_layer_forward_ex": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                            _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
+                                            _opts_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz,
+                                            _c_void_p]),
     "moe_binned_capacity_max": (_i32, [_i32, _i32, _i32, _f32, _i32]),
     "moe_binned_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, ctypes.c_int]),
     "moe_layer_forward_binned": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -176,8 +193,23 @@ def _ws(nbytes: int, dev):
     return _torch().empty(max(int(nbytes), 1), dtype=_torch().uint8, device=dev)
 
 
-def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = False):
-    """Router on ``x[T,h]`` (or on given fp32 ``logits[T,E]``).
+def _opts(jitter, noise, temperature, uniform, x=None, T=None, E=None):
+    """A RouterOpts for the given variants, or None when all are at their defaults."""
+    if jitter is None and noise is None and float(temperature) == 1.0 and not uniform:
+        return None
+    torch = _torch()
+    if jitter is not None and (x is None or jitter.shape != x.shape or jitter.dtype != x.dtype):
+        raise ValueError("jitter must have x's shape and dtype")
+    if noise is not None and (tuple(noise.shape) != (T, E) or noise.dtype != torch.float32):
+        raise ValueError("noise must be fp32 [T, E]")
+    return RouterOpts(_p(jitter), _p(noise), float(temperature), 1 if uniform else 0)
+
+
+def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = False, jitter=None, noise=None,
+          temperature: float = 1.0, uniform: bool = False):
+    """Router on ``x[T,h]`` (or on given fp32 ``logits[T,E]``), optionally with the
+    router variants (``jitter`` [T,h] in x's dtype, gate ``noise`` [T,E] fp32, softmax
+    ``temperature``, ``uniform`` expert assignment).
 
     Returns ``(logits, topk_idx, topk_w, prob_sum)`` (prob_sum is None unless
     requested)."""
@@ -186,6 +218,7 @@ def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = F
     dev = ref.device
     T = ref.shape[0]
     E = (logits if logits is not None else W_gate).shape[-1]
+    opts = _opts(jitter, noise, temperature, uniform, x, T, E)
     h = 0 if x is None else x.shape[1]
     dt = F32 if x is None else _dt(x)
     flags = ROUTE_LOGITS_IN if logits is not None else 0
@@ -194,12 +227,16 @@ def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = F
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     ps = torch.empty(E, dtype=torch.float32, device=dev) if with_prob_sum else None
     need = lib().moe_route_workspace_bytes(T, h, E, dt, flags, 1 if with_prob_sum else 0)
+    if opts is not None:
+        need += lib().moe_router_opts_workspace_bytes(T, h, dt, ctypes.byref(opts))
     ws = _ws(need, dev) if need else None
-    st = lib().moe_route(None if logits is not None else _p(x), None if logits is not None else _p(W_gate),
-                         None if (logits is not None or logit_bias is None) else _p(logit_bias),
-                         T, h, E, k, dt, flags, _p(out_logits), _p(idx), _p(w), _p(ps),
-                         _p(ws), 0 if ws is None else ws.numel(), _stream(dev))
-    _check(st, "moe_route")
+    args = (None if logits is not None else _p(x), None if logits is not None else _p(W_gate),
+            None if (logits is not None or logit_bias is None) else _p(logit_bias), T, h, E, k, dt, flags)
+    tail = (_p(out_logits), _p(idx), _p(w), _p(ps), _p(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    if opts is None:
+        _check(lib().moe_route(*args, *tail), "moe_route")
+    else:
+        _check(lib().moe_route_ex(*args, ctypes.byref(opts), *tail), "moe_route_ex")
     return out_logits, idx, w, ps
 
 
@@ -258,25 +295,36 @@ def unpermute(out_perm, slot_pos, topk_w):
 
 
 def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float, act: str,
-                  ws=None, y=None, aux=None, counts=None, events=None):
+                  ws=None, y=None, aux=None, counts=None, events=None, jitter=None, noise=None,
+                  temperature: float = 1.0, uniform: bool = False):
     """The whole layer.  Returns ``(y, aux_loss, counts)``.  Pass preallocated
     ``ws``/``y``/``aux``/``counts`` to avoid allocations in a timed loop.
     ``events``: a ctypes array of ``len(LAYER_STAGES) + 1`` hipEvent_t handles to
-    record between the stages (the measurement variant of the entry point)."""
+    record between the stages (the measurement variant of the entry point).
+    ``jitter``/``noise``/``temperature``/``uniform``: the router variants (see route)."""
     torch = _torch()
     dev = x.device
     T, h = x.shape
     E, _, f = W1.shape
+    opts = _opts(jitter, noise, temperature, uniform, x, T, E)
+    if opts is not None and events is not None:
+        raise ValueError("the measurement entry point takes no router variants")
     dt = _dt(x)
     a = _ACT[act]
     if ws is None:
-        ws = _ws(workspace_bytes(T, h, f, E, k, capacity_factor, dt, a), dev)
+        extra = 0 if opts is None else lib().moe_router_opts_workspace_bytes(T, h, dt, ctypes.byref(opts))
+        ws = _ws(workspace_bytes(T, h, f, E, k, capacity_factor, dt, a) + extra, dev)
     if y is None:
         y = torch.empty_like(x)
     if aux is None:
         aux = torch.empty((), dtype=torch.float32, device=dev)
     if counts is None:
         counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if opts is not None:
+        _check(lib().moe_layer_forward_ex(_p(x), _p(W_gate), _p(logit_bias), _p(W1), _p(W3), _p(W2), T, h, f, E, k,
+                                          float(capacity_factor), a, dt, ctypes.byref(opts), _p(y), _p(aux),
+                                          _p(counts), _p(ws), ws.numel(), _stream(dev)), "moe_layer_forward_ex")
+        return y, aux, counts
     args = (_p(x), _p(W_gate), _p(logit_bias), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor), a,
             dt, _p(y), _p(aux), _p(counts), _p(ws), ws.numel(), _stream(dev))
     if events is None:

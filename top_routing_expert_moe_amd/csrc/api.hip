@@ -265,10 +265,28 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t h, int32_t E, moe_dtype_t dt
   return c.bytes();
 }
 
-moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bias, int32_t T, int32_t h,
-                       int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags, float* logits,
-                       int32_t* topk_idx, float* topk_w, float* prob_sum, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+// ---- router variants (moe_router_opts_t)
+static moe_status_t opts_ok(const moe_router_opts_t* o, const void* x, bool logits_in) {
+  if (o == nullptr) return MOE_OK;
+  if (!isfinite(o->temperature) || !(o->temperature > 0.f)) return MOE_ERR_ARG;
+  if (o->jitter != nullptr) {
+    if (logits_in) return MOE_ERR_ARG;  // the jitter acts on the router input
+    if (!aligned16(o->jitter) || !aligned16(x)) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+static bool has_jitter(const moe_router_opts_t* o) { return o != nullptr && o->jitter != nullptr; }
+static void apply_opts(RouteArgs& a, const moe_router_opts_t* o) {
+  if (o == nullptr) return;
+  a.noise = o->logit_noise;
+  a.inv_temp = 1.0f / o->temperature;
+  a.uniform = o->uniform_assignment != 0;
+}
+
+static moe_status_t route_impl(const void* x, const float* W_gate, const float* logit_bias, int32_t T, int32_t h,
+                               int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags,
+                               const moe_router_opts_t* opts, float* logits, int32_t* topk_idx, float* topk_w,
+                               float* prob_sum, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status_t s = common_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (!dtype_ok(dt) || (flags & ~MOE_ROUTE_LOGITS_IN) != 0) return MOE_ERR_ARG;
@@ -278,11 +296,13 @@ moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bi
     if (!x || !W_gate) return MOE_ERR_ARG;
     if ((s = dim_ok(h)) != MOE_OK) return s;
   }
+  if ((s = opts_ok(opts, x, lin)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   Carve c(ws);
   const bool need_planes = !lin && dt == MOE_BF16;
   RouteWs w = carve_route(c, T, h, E, prob_sum != nullptr, need_planes);
-  if ((prob_sum || need_planes) && (!ws || ws_bytes < c.bytes())) return MOE_ERR_WORKSPACE;
+  void* xj = has_jitter(opts) ? c.take<char>((size_t)T * h * elem_bytes(dt)) : nullptr;
+  if ((prob_sum || need_planes || has_jitter(opts)) && (!ws || ws_bytes < c.bytes())) return MOE_ERR_WORKSPACE;
   RouteArgs a{};
   a.x = x;
   a.W_gate = W_gate;
@@ -299,9 +319,35 @@ moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bi
   a.prob_part = prob_sum ? w.prob_part : nullptr;
   a.blk_counts = nullptr;
   a.planes = w.planes;
+  apply_opts(a, opts);
+  if (xj != nullptr) {
+    MOE_TRY(launch_jitter(x, opts->jitter, (int64_t)T * h, a.bf16, xj, stream));
+    a.x = xj;
+  }
   MOE_TRY(launch_route(a, stream));
   if (prob_sum) MOE_TRY(launch_reduce_prob(w.prob_part, route_blocks(T), E, prob_sum, stream));
   return MOE_OK;
+}
+
+moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bias, int32_t T, int32_t h,
+                       int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags, float* logits,
+                       int32_t* topk_idx, float* topk_w, float* prob_sum, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  return route_impl(x, W_gate, logit_bias, T, h, E, k, dt, flags, nullptr, logits, topk_idx, topk_w, prob_sum, ws,
+                    ws_bytes, stream);
+}
+
+moe_status_t moe_route_ex(const void* x, const float* W_gate, const float* logit_bias, int32_t T, int32_t h,
+                          int32_t E, int32_t k, moe_dtype_t dt, uint32_t flags, const moe_router_opts_t* opts,
+                          float* logits, int32_t* topk_idx, float* topk_w, float* prob_sum, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return route_impl(x, W_gate, logit_bias, T, h, E, k, dt, flags, opts, logits, topk_idx, topk_w, prob_sum, ws,
+                    ws_bytes, stream);
+}
+
+size_t moe_router_opts_workspace_bytes(int32_t T, int32_t h, moe_dtype_t dt, const moe_router_opts_t* opts) {
+  if (T < 0 || h < 0 || !dtype_ok(dt) || !has_jitter(opts)) return 0;
+  return align_up((size_t)T * h * elem_bytes(dt));
 }
 
 moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int32_t h, int32_t E, int32_t k,
@@ -399,7 +445,8 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
                                        const void* W1, const void* W3, const void* W2, int32_t T, int32_t h,
                                        int32_t f, int32_t E, int32_t k, float capacity_factor, moe_act_t act,
                                        moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, void* ws,
-                                       size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+                                       size_t ws_bytes, hipStream_t stream, hipEvent_t* ev,
+                                       const moe_router_opts_t* opts = nullptr) {
   moe_status_t s = common_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor)) return MOE_ERR_ARG;
@@ -409,6 +456,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_ARG;
   if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || (W3 && !aligned16(W3)) || !aligned16(y))
     return MOE_ERR_UNSUPPORTED;
+  if ((s = opts_ok(opts, x, false)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   const int64_t C = capacity_of(T, E, k, capacity_factor);
   const int R_max = rows_max(T, E, k, C);
@@ -416,6 +464,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   const FfnPlan pl = layer_plan(bf, T, h, f, E, k, C);
   Carve c(ws);
   LayerWs w = carve_layer(c, T, h, f, E, k, R_max, pl, dt, act);
+  void* xj = has_jitter(opts) ? c.take<char>((size_t)T * h * elem_bytes(dt)) : nullptr;
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   int stage = 0;
   auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
@@ -437,6 +486,11 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   ra.prob_part = w.prob_part;
   ra.blk_counts = w.blk_counts;  // the histogram is counted by the selection kernel
   ra.planes = w.planes;
+  apply_opts(ra, opts);
+  if (xj != nullptr) {  // only the router sees the jittered input
+    MOE_TRY(launch_jitter(x, opts->jitter, (int64_t)T * h, bf, xj, stream));
+    ra.x = xj;
+  }
   MOE_TRY(launch_logits(ra, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   MOE_TRY(launch_select(ra, stream));
@@ -616,6 +670,15 @@ moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* 
                                hipStream_t stream) {
   return layer_forward_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, y,
                             aux_loss, counts, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
+                                  const void* W3, const void* W2, int32_t T, int32_t h, int32_t f, int32_t E,
+                                  int32_t k, float capacity_factor, moe_act_t act, moe_dtype_t dt,
+                                  const moe_router_opts_t* opts, void* y, float* aux_loss, int32_t* counts,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_forward_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, y,
+                            aux_loss, counts, ws, ws_bytes, stream, nullptr, opts);
 }
 
 moe_status_t moe_layer_forward_timed(const void* x, const float* W_gate, const float* logit_bias,

@@ -24,7 +24,14 @@ struct RouteArgs {
   int* blk_counts;        // [route_blocks(T), E] or null: per-block expert histogram
   uint16_t* planes;       // bf16 x: route_scratch_bytes of scratch -- [3][E16][h] bf16 split router
                           // weights, then (few tokens) [SH][T][E] fp32 partial logits
+  // router variants (selection kernel): gate noise [T,E] added to the logits, softmax of
+  // logits * inv_temp, ids replaced by (t*k + j) % E
+  const float* noise = nullptr;
+  float inv_temp = 1.0f;
+  bool uniform = false;
 };
+// router-input jitter: out = x * u elementwise in the storage dtype (n_elems * elem size % 16 == 0)
+hipError_t launch_jitter(const void* x, const void* u, int64_t n_elems, bool bf16, void* out, hipStream_t st);
 int route_planes_elems(int h, int E);
 int route_hsplit(int T, int h, int E, bool bf16);              // h-split of the logits (1 = none)
 size_t route_scratch_bytes(int T, int h, int E, bool bf16);   // bytes behind RouteArgs::planes

@@ -237,11 +237,17 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // logits are loaded before any is used: the kernel costs one memory round trip.
 // With SH > 1 the logits arrive as SH partial sums (lpart[z][t][e]); they are added in
 // ascending z and the sums written to `logits`.
+// Router variants: `noise` [T,E] (or null) is added to the logits before anything else
+// uses them (the stored logits stay the router's own); the softmax and the weights use
+// logits * inv_temp (selection ranks the logits themselves, the same order for any
+// positive temperature); with `uniform` the ids written (and counted) are (t*k + j) % E
+// while the weights stay those of the real top-k.
 template <int NV, int G, bool HSPLIT, int NWS = 4>
 __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ logits, const float* __restrict__ lpart,
                                                      int SH, int T, int E, int k,
                                                      int* __restrict__ topk_idx, float* __restrict__ topk_w,
-                                                     float* __restrict__ prob_part, int* __restrict__ blk_counts) {
+                                                     float* __restrict__ prob_part, int* __restrict__ blk_counts,
+                                                     const float* __restrict__ noise, float inv_temp, int uniform) {
   static_assert(G == 64 || NV == 1, "several values per lane only with whole-wave groups");
   constexpr int TPW = 64 / G;                  // tokens per wave and pass
   constexpr int NQ = kSelTokens / NWS / TPW;   // passes per wave
@@ -274,6 +280,7 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
         } else {
           l = logits[(size_t)t * E + e];
         }
+        if (noise != nullptr) l += noise[(size_t)t * E + e];
       }
       v[q][i] = e < E ? l : -INFINITY;
     }
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
     float ex[NV], s = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      ex[i] = gl + 64 * i < E ? expf(v[q][i] - m) : 0.f;
+      ex[i] = gl + 64 * i < E ? expf((v[q][i] - m) * inv_temp) : 0.f;
       s += ex[i];
     }
 #pragma unroll
@@ -333,13 +340,14 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
       for (int i = 0; i < NV; ++i)
         if (gl + 64 * i == e_sel) taken[i] = true;
       if (j == 0) lmax = l_sel;
-      wsum += expf(l_sel - lmax);
+      wsum += expf((l_sel - lmax) * inv_temp);
       if (gl == j) { my_l = l_sel; my_e = e_sel; }
     }
     if (tv && gl < k) {
-      topk_idx[(size_t)t * k + gl] = my_e;
-      topk_w[(size_t)t * k + gl] = expf(my_l - lmax) / wsum;
-      if (blk_counts != nullptr) atomicAdd(&cnt[my_e], 1);
+      const int e_out = uniform ? (int)(((int64_t)t * k + gl) % E) : my_e;
+      topk_idx[(size_t)t * k + gl] = e_out;
+      topk_w[(size_t)t * k + gl] = expf((my_l - lmax) * inv_temp) / wsum;
+      if (blk_counts != nullptr) atomicAdd(&cnt[e_out], 1);
     }
   }
   // the token groups of a wave hold partial sums of the same experts: add them (fixed tree)
@@ -468,7 +476,8 @@ hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
   const float* lpart = SH > 1 ? route_lpart(a) : nullptr;
 #define MOE_SELECT_W(NV, G, HS, NWS)                                                                       \
   hipLaunchKernelGGL((select_kernel<NV, G, HS, NWS>), grid, dim3(NWS * 64), 0, st, a.logits, lpart, SH, a.T, \
-                     a.E, a.k, a.topk_idx, a.topk_w, a.prob_part, a.blk_counts)
+                     a.E, a.k, a.topk_idx, a.topk_w, a.prob_part, a.blk_counts, a.noise, a.inv_temp,  \
+                     a.uniform ? 1 : 0)
 #define MOE_SELECT(NV, G, HS) MOE_SELECT_W(NV, G, HS, 4)
   if (SH > 1 && a.E > 16) return hipErrorInvalidValue;  // the h split is for few experts only
   if (a.E <= 4) { if (SH > 1) MOE_SELECT(1, 4, true); else MOE_SELECT(1, 4, false); }
@@ -490,6 +499,36 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   return launch_select(a, st);
+}
+
+// Jitter of the router input: out = x * u elementwise, rounded to the storage dtype
+// (bf16: the exact fp32 product rounded to nearest even).  8 elements per thread.
+__global__ __launch_bounds__(256) void jitter_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ u,
+                                                     int64_t n_vec, int bf16, u32x4* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_vec) return;
+  const u32x4 a = x[i], b = u[i];
+  u32x4 r;
+  if (bf16) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float lo = __uint_as_float(a[c] << 16) * __uint_as_float(b[c] << 16);
+      const float hi = __uint_as_float(a[c] & 0xFFFF0000u) * __uint_as_float(b[c] & 0xFFFF0000u);
+      r[c] = pack_bf16x2(lo, hi);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r[c] = __float_as_uint(__uint_as_float(a[c]) * __uint_as_float(b[c]));
+  }
+  out[i] = r;
+}
+
+hipError_t launch_jitter(const void* x, const void* u, int64_t n_elems, bool bf16, void* out, hipStream_t st) {
+  const int64_t n_vec = n_elems * (bf16 ? 2 : 4) / 16;
+  if (n_vec <= 0) return hipSuccess;
+  hipLaunchKernelGGL(jitter_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256), 0, st, (const u32x4*)x,
+                     (const u32x4*)u, n_vec, bf16 ? 1 : 0, (u32x4*)out);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_prob(const float* prob_part, int nblk, int E, float* prob_sum, hipStream_t st) {
