@@ -47,6 +47,7 @@ __all__ = [
     "expert_ffn", "combine", "aux_loss", "layer_forward",
     "binned_capacity", "binned_layout", "layer_forward_binned",
     "jitter_input", "noisy_logits", "softmax_t", "topk_weights_t", "uniform_assignment", "route",
+    "silu_grad", "gelu_grad", "layer_backward",
 ]
 
 
@@ -395,6 +396,130 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
         out["y64"] = y64
         out["y"] = round_to_bf16(y64) if dtype == "bf16" else y64.astype(np.float32)
     return out
+
+
+# ----------------------------------------------------------------------------
+# backward pass: the adjoint of layer_forward
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d silu / dz = s (1 + z (1 - s)), s = 1 / (1 + exp(-z))."""
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def gelu_grad(z: np.ndarray) -> np.ndarray:
+    """d gelu / dz for the exact form: Phi(z) + z phi(z)."""
+    return 0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: int, capacity_factor: float,
+                   act: str, dtype: str, logits=None, tokens=None, experts=None,
+                   with_w_gate: bool = True) -> dict:
+    """Gradients of ``L = <dy, y> + d_aux * aux`` for the layer of :func:`layer_forward`,
+    fp64, as the adjoint of each forward step in reverse order (chain rule).
+
+    The pages name a backward pass for the gating operator ([OPS] operator list:
+    moe_gating holds the router's forward and backward) and autograd wrappers around
+    the gather / scatter of the permutation ([MB] section 5 file map) without writing
+    them out, so this is the plain derivative of the forward as defined here:
+
+    * combine: ``dw[t,j] = <dy[t], O[r]>`` and ``dO[r] = w[t,j] dy[t]`` for kept slots
+      ``r = slot_pos[t*k+j]``; dropped slots get ``dw = 0`` (they do not reach y);
+    * expert e on its rows X: ``dHm = dO W2^T``, ``dW2 = Hm^T dO``; SwiGLU
+      ``da = dHm * g * silu'(a)``, ``dg = dHm * silu(a)``; GELU ``da = dHm * gelu'(a)``;
+      ``dW1 = X^T da``, ``dW3 = X^T dg``, ``dX = da W1^T (+ dg W3^T)``;
+    * the permutation's adjoint: ``dx[t] += sum_j dX[slot_pos[t*k+j]]``;
+    * the router: the weights are the softmax over the selected logits, so
+      ``dl[t,S_j] = w_j (dw_j - sum_j' w_j' dw_j')`` and 0 for unselected experts; the aux
+      loss adds ``d_aux (E/T) p[t,i] (f_i - sum_e f_e p[t,e])`` (the counts f are
+      piecewise constant in the logits: no gradient through them);
+    * ``dW_gate = x^T dl``, ``dx += dl W_gate^T``.
+
+    Readings: top-k selection and the capacity drop are piecewise constant (no
+    gradient); in bf16 workloads the rounding of Hm passes gradients unchanged while
+    ``dW2`` uses the rounded Hm that the forward multiplied; ``logit_bias`` gets no
+    gradient (it is not a parameter of the method).  ``tokens`` limits ``dx`` to those
+    tokens, ``experts`` limits the weight gradients (and the expert work) to those
+    experts, and ``with_w_gate=False`` skips ``dW_gate`` (which needs every token);
+    the returned arrays are full-sized, with zeros where nothing was computed.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(W_gate).shape[1]
+    x64 = _as_f64(x, dtype)
+    h = x64.shape[1]
+    f = np.asarray(W1).shape[2]
+    Wg = np.asarray(W_gate, dtype=np.float32).astype(np.float64)
+    if logits is None:
+        logits = router_logits(x, W_gate, logit_bias, dtype)
+    l = np.asarray(logits, dtype=np.float32)
+    idx = select_topk(l, k)
+    w = topk_weights(l, idx)
+    C = expert_capacity(T, E, k, capacity_factor)
+    counts, offsets, sorted_slot, slot_pos = permute(idx, E, C)
+    dy64 = _as_f64(dy, dtype)
+    kept = slot_pos.reshape(T, k) >= 0
+    wk = w.astype(np.float64)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    need_tok = np.zeros(T, dtype=bool)
+    need_tok[tok] = True
+    if with_w_gate:
+        need_tok[:] = True           # dl of every token enters dW_gate
+    want_e = set(range(E)) if experts is None else set(int(e) for e in experts)
+
+    dx = np.zeros((T, h))
+    dW1 = np.zeros((E, h, f))
+    dW3 = np.zeros((E, h, f)) if act == "swiglu" else None
+    dW2 = np.zeros((E, f, h))
+    dw = np.zeros((T, k))
+    for e in range(E):
+        rows, slots = np.nonzero((idx == e) & kept)
+        if e in want_e:
+            sel = np.ones(rows.shape, dtype=bool)      # all rows of e: the weight gradients need them
+        else:
+            sel = need_tok[rows]                       # only the rows whose token is asked for
+        rows, slots = rows[sel], slots[sel]
+        if rows.size == 0:
+            continue
+        X = x64[rows]
+        W1e = _as_f64(W1[e], dtype)
+        W2e = _as_f64(W2[e], dtype)
+        a = X @ W1e
+        if act == "swiglu":
+            W3e = _as_f64(W3[e], dtype)
+            g = X @ W3e
+            hm = silu(a) * g
+        else:
+            hm = gelu(a)
+        hm_r = bf16_to_f64(round_to_bf16(hm)) if dtype == "bf16" else hm
+        O = hm_r @ W2e
+        dw[rows, slots] = np.sum(dy64[rows] * O, axis=1)
+        dO = wk[rows, slots][:, None] * dy64[rows]
+        dHm = dO @ W2e.T
+        if act == "swiglu":
+            da = dHm * g * silu_grad(a)
+            dg = dHm * silu(a)
+            dX = da @ W1e.T + dg @ W3e.T
+        else:
+            da = dHm * gelu_grad(a)
+            dX = da @ W1e.T
+        if e in want_e:
+            dW2[e] = hm_r.T @ dO
+            dW1[e] = X.T @ da
+            if act == "swiglu":
+                dW3[e] = X.T @ dg
+        np.add.at(dx, rows, dX)
+    # router: the renormalised softmax over the selection, and the aux loss
+    p = softmax(l)
+    dl = np.zeros((T, E))
+    s_dw = np.sum(wk * dw, axis=1, keepdims=True)
+    np.add.at(dl, (np.repeat(np.arange(T), k), idx.reshape(-1)), (wk * (dw - s_dw)).reshape(-1))
+    fe = counts.astype(np.float64) / float(T * k)
+    dl += float(d_aux) * (E / float(T)) * p * (fe[None, :] - np.sum(p * fe[None, :], axis=1, keepdims=True))
+    dx += dl @ Wg.T
+    dWg = x64.T @ dl if with_w_gate else None
+    return dict(dx=dx, dW_gate=dWg, dW1=dW1, dW3=dW3, dW2=dW2, dlogits=dl, dw=dw, topk_idx=idx, topk_w=w,
+                counts=counts, slot_pos=slot_pos, logits=l)
 
 
 # ----------------------------------------------------------------------------

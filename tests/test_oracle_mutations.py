@@ -11,6 +11,7 @@ import pytest
 
 import oracle as o
 import oracle.moe_oracle as om
+from tests import test_oracle_backward as bpins
 from tests import test_oracle_pins as pins
 
 
@@ -88,6 +89,14 @@ def _noise_ignored(logits, noise):
     return np.asarray(logits, dtype=np.float32)
 
 
+def _silu_grad_first_term(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _gelu_grad_cdf_only(z):
+    return 0.5 * (1.0 + om._erf(z / math.sqrt(2.0)))
+
+
 _orig = {n: getattr(om, n) for n in ("router_logits", "permute", "binned_layout", "binned_capacity", "softmax_t")}
 
 MUTANTS = [
@@ -104,10 +113,15 @@ MUTANTS = [
     ("softmax_t", _softmax_t_times, ["test_temperature_closed_form_on_the_worked_example"]),
     ("uniform_assignment", _uniform_transposed, ["test_uniform_assignment_ids_counts_and_aux"]),
     ("noisy_logits", _noise_ignored, ["test_noise_decides_the_selection"]),
+    ("silu_grad", _silu_grad_first_term, ["backward:swiglu"]),
+    ("gelu_grad", _gelu_grad_cdf_only, ["backward:gelu"]),
 ]
 
 
 def _run(test_name):
+    if test_name.startswith("backward:"):
+        act = test_name.split(":")[1]
+        return bpins.test_backward_vs_torch_autograd(act, 0.0, 0.5, 2, 5)
     fn = getattr(pins, test_name)
     if test_name == "test_k_equals_E_is_dense_softmax_mixture":
         return fn("swiglu")
