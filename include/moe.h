@@ -191,6 +191,36 @@ moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const floa
                                   const moe_router_opts_t* opts, void* y, float* aux_loss,
                                   int32_t* counts, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Backward pass of moe_layer_forward: the gradients of L = <dy, y> + d_aux * aux_loss.
+ * The pages name a backward pass for the gating operator ([OPS] operator list) and
+ * autograd wrappers for the permutation ([MB] section 5) without writing them out; this
+ * is the exact adjoint of the forward as the library defines it:
+ *   dw[t,j] = <dy[t], O[r]>, dO[r] = w[t,j] dy[t] (kept slots; dropped ones get nothing);
+ *   dHm = dO W2[e]^T; SwiGLU da = dHm g silu'(a), dg = dHm silu(a); GELU da = dHm gelu'(a);
+ *   dW2[e] = Hm^T dO, dW1[e] = X^T da, dW3[e] = X^T dg, dX = da W1^T (+ dg W3^T);
+ *   dx[t] = sum_j dX[slot of (t,j)] + dl[t] W_gate^T, dW_gate = x^T dl, with
+ *   dl[t,S_j] = w_j (dw_j - sum_j' w_j' dw_j') + d_aux (E/T) p (f - <f, p>) (p the full
+ *   softmax, f_e = counts_e / (T k)).
+ * Selection and capacity are piecewise constant (no gradient); in bf16 the rounding of
+ * Hm passes gradients unchanged, while dW2 uses the rounded Hm.  The plain router only:
+ * not the variants of moe_router_opts_t.
+ *   fwd_ws / fwd_ws_bytes: the workspace of the moe_layer_forward call being
+ *     differentiated, untouched since (it holds the routing, Hm and the expert outputs);
+ *     the other inputs must be that call's.
+ *   dy [T,h] (dt); d_aux: host scalar.
+ *   dx [T,h] (dt); dW_gate [h,E] fp32 or NULL (skipped); dW1, dW3 [E,h,f], dW2 [E,f,h]
+ *     fp32 (dW3 NULL iff GELU).  The weight gradients are overwritten, not accumulated.
+ *   ws: at least moe_layer_backward_workspace_bytes(...) bytes.
+ * The pre-activations a (| g) are recomputed with the up projection's GEMM. */
+size_t moe_layer_backward_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                          float capacity_factor, moe_dtype_t dt, moe_act_t act);
+moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* W1, const void* W3,
+                                const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
+                                float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                                float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 /* The layer with fixed-capacity buckets ("binned" layout: [MB] sections 3, 4.3 and 4.5;
  * [CAI] SparseMLP data flow step 4 and its capacity parameters).  Every expert gets a
  * bucket of C rows: C = max(floor(cf * T*k/E), min_capacity) when cf > 0, else (or if that

@@ -414,7 +414,7 @@ def gelu_grad(z: np.ndarray) -> np.ndarray:
 
 def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: int, capacity_factor: float,
                    act: str, dtype: str, logits=None, tokens=None, experts=None,
-                   with_w_gate: bool = True) -> dict:
+                   with_w_gate: bool = True, with_scale: bool = False) -> dict:
     """Gradients of ``L = <dy, y> + d_aux * aux`` for the layer of :func:`layer_forward`,
     fp64, as the adjoint of each forward step in reverse order (chain rule).
 
@@ -442,6 +442,13 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
     tokens, ``experts`` limits the weight gradients (and the expert work) to those
     experts, and ``with_w_gate=False`` skips ``dW_gate`` (which needs every token);
     the returned arrays are full-sized, with zeros where nothing was computed.
+
+    ``with_scale`` also returns, for each gradient, its magnitude scale: the same chain
+    of products taken over absolute values, carried from ``|dO| = |w| |dy|`` through
+    ``|dO| |W2|^T`` to the bound on ``|da|`` (and ``|dg|``), then ``|X|^T`` of that for
+    ``dW1``, and so on, with the router path carried from ``sum |dy| |O|``.  An
+    implementation that rounds intermediate operands with relative error u moves each
+    gradient, to first order, by at most a small multiple of u times its scale.
     """
     x = np.asarray(x)
     T = x.shape[0]
@@ -472,6 +479,11 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
     dW3 = np.zeros((E, h, f)) if act == "swiglu" else None
     dW2 = np.zeros((E, f, h))
     dw = np.zeros((T, k))
+    sc = {}
+    if with_scale:
+        sc = dict(dx=np.zeros((T, h)), dW1=np.zeros((E, h, f)), dW2=np.zeros((E, f, h)),
+                  dW3=np.zeros((E, h, f)) if act == "swiglu" else None)
+        dw_m = np.zeros((T, k))
     for e in range(E):
         rows, slots = np.nonzero((idx == e) & kept)
         if e in want_e:
@@ -508,6 +520,24 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
             dW1[e] = X.T @ da
             if act == "swiglu":
                 dW3[e] = X.T @ dg
+        if with_scale:
+            dO_m = np.abs(dO)
+            dHm_m = dO_m @ np.abs(W2e).T
+            if act == "swiglu":
+                da_m = dHm_m * np.abs(g * silu_grad(a))
+                dg_m = dHm_m * np.abs(silu(a))
+            else:
+                da_m = dHm_m * np.abs(gelu_grad(a))
+            dw_m[rows, slots] = np.sum(np.abs(dy64[rows]) * np.abs(O), axis=1)
+            if e in want_e:
+                sc["dW2"][e] = np.abs(hm_r).T @ dO_m
+                sc["dW1"][e] = np.abs(X).T @ da_m
+                if act == "swiglu":
+                    sc["dW3"][e] = np.abs(X).T @ dg_m
+            mag = da_m @ np.abs(W1e).T
+            if act == "swiglu":
+                mag = mag + dg_m @ np.abs(W3e).T
+            np.add.at(sc["dx"], rows, mag)
         np.add.at(dx, rows, dX)
     # router: the renormalised softmax over the selection, and the aux loss
     p = softmax(l)
@@ -518,8 +548,17 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
     dl += float(d_aux) * (E / float(T)) * p * (fe[None, :] - np.sum(p * fe[None, :], axis=1, keepdims=True))
     dx += dl @ Wg.T
     dWg = x64.T @ dl if with_w_gate else None
-    return dict(dx=dx, dW_gate=dWg, dW1=dW1, dW3=dW3, dW2=dW2, dlogits=dl, dw=dw, topk_idx=idx, topk_w=w,
-                counts=counts, slot_pos=slot_pos, logits=l)
+    out = dict(dx=dx, dW_gate=dWg, dW1=dW1, dW3=dW3, dW2=dW2, dlogits=dl, dw=dw, topk_idx=idx, topk_w=w,
+               counts=counts, slot_pos=slot_pos, logits=l)
+    if with_scale:
+        dl_m = np.zeros((T, E))
+        s_m = np.sum(wk * dw_m, axis=1, keepdims=True)
+        np.add.at(dl_m, (np.repeat(np.arange(T), k), idx.reshape(-1)), (wk * (dw_m + s_m)).reshape(-1))
+        dl_m += abs(float(d_aux)) * (E / float(T)) * p * (fe[None, :] + np.sum(p * fe[None, :], axis=1, keepdims=True))
+        sc["dx"] += dl_m @ np.abs(Wg).T
+        sc["dW_gate"] = np.abs(x64).T @ dl_m if with_w_gate else None
+        out["scale"] = sc
+    return out
 
 
 # ----------------------------------------------------------------------------

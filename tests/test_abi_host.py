@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(L):
                           "moe_layer_forward_timed", "moe_expert_ffn_workspace_bytes",
                           "moe_route_workspace_bytes", "moe_binned_capacity_max", "moe_binned_workspace_bytes",
                           "moe_layer_forward_binned", "moe_layer_forward_binned_timed",
-                          "moe_router_opts_workspace_bytes", "moe_route_ex", "moe_layer_forward_ex"}
+                          "moe_router_opts_workspace_bytes", "moe_route_ex", "moe_layer_forward_ex",
+                          "moe_layer_backward_workspace_bytes", "moe_layer_backward"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -340,6 +341,32 @@ def test_layer_forward_ex_host_errors(L):
     assert extra == 64 * 128 * 2
     assert call(_ropts(jitter=FAKE), ws_bytes=need + extra - 1) == WS
     assert call(_ropts(jitter=FAKE), T=0) == OK
+
+
+def test_layer_backward_host_errors(L):
+    T, h, f, E, k = 64, 128, 256, 8, 2
+    fwd = moe.workspace_bytes(T, h, f, E, k, 0.0, 1, 1)
+    bws = L.moe_layer_backward_workspace_bytes(T, h, f, E, k, 0.0, 1, 1)
+    # dHm/da|dg, dO, dX and the recomputed pre-activations, at R = T*k rows
+    assert bws >= T * k * (h * 2 + 2 * f * 4 + 2 * f * 2 + h * 4)
+    assert L.moe_layer_backward_workspace_bytes(T, h, f, E, 9, 0.0, 1, 1) == 0
+
+    def call(**kw):
+        a = dict(x=FAKE, Wg=FAKE, W1=FAKE, W3=FAKE, W2=FAKE, T=T, h=h, f=f, E=E, k=k, cf=0.0, act=1, dt=1, dy=FAKE,
+                 d_aux=0.0, fws=FAKE, fwsb=fwd, dx=FAKE, dWg=None, dW1=FAKE, dW3=FAKE, dW2=FAKE, ws=FAKE, wsb=bws)
+        a.update(kw)
+        return L.moe_layer_backward(a["x"], a["Wg"], a["W1"], a["W3"], a["W2"], a["T"], a["h"], a["f"], a["E"],
+                                    a["k"], a["cf"], a["act"], a["dt"], a["dy"], a["d_aux"], a["fws"], a["fwsb"],
+                                    a["dx"], a["dWg"], a["dW1"], a["dW3"], a["dW2"], a["ws"], a["wsb"], None)
+    assert call(d_aux=float("nan")) == ARG
+    assert call(dW3=None) == ARG                 # SwiGLU has a W3 gradient
+    assert call(act=0, W3=None) == ARG           # GELU has none
+    assert call(dy=None) == ARG
+    assert call(k=0) == ARG
+    assert call(h=96) == UNSUP
+    assert call(fwsb=fwd - 1) == WS              # the forward's workspace is the saved context
+    assert call(wsb=bws - 1) == WS
+    assert call(T=0) == OK
 
 
 def test_binding_refuses_cpu_tensors(L):

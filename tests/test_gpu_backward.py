@@ -1,0 +1,150 @@
+"""GPU parity of the layer's backward pass (moe_layer_backward) against the oracle's
+layer_backward.
+
+The oracle routes on the GPU router's fp32 logits (Mode A), so the selection, the
+capacity drops and the counts that enter the aux gradient are shared.  Gradients are
+compared elementwise: fp32 workloads within 1e-4 (|ref| + RMS) -- the GPU chains five
+fp32-accumulated products; bf16 workloads within 2^-5 of the oracle's magnitude scale
+(the gradient's chain of products over absolute values, see layer_backward), plus half
+a bf16 ulp for the bf16 dx.  The GPU rounds dO and da | dg to bf16 (2^-9 each, relative
+to the scale), its forward's bf16 Hm may round one ulp away from the oracle's where the
+fp32 pre-activation sits on a rounding boundary (up to 2^-7), and it accumulates
+K <= 2f terms in fp32: at most about 2^-6.5 together, so 2^-5 leaves twice that.
+Full-size prefill and fine-grained layers compare dx on sampled tokens and the weight
+gradients of the expert with the fewest rows (the oracle's fp64 work is bounded to
+those).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import moe_workloads as mw
+import oracle as o
+import top_routing_expert_moe_amd as moe
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+D_AUX = 0.5
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _dy(T, h, dtype, seed=17):
+    a = np.random.default_rng(seed).standard_normal((T, h)).astype(np.float32)
+    return mw.f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def _run(w, dd, dy_host):
+    torch = gu.torch()
+    dt = moe.BF16 if w.dtype == "bf16" else moe.F32
+    a = moe.SWIGLU if w.act == "swiglu" else moe.GELU
+    fws = moe._ws(moe.workspace_bytes(w.T, w.h, w.f, w.E, w.k, w.cf, dt, a), dd["x"].device)
+    args = (dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"])
+    moe.layer_forward(*args, k=w.k, capacity_factor=w.cf, act=w.act, ws=fws)
+    logits, _, _, _ = moe.route(dd["x"], dd["W_gate"], dd["logit_bias"], w.k)
+    dy = gu.to_dev(dy_host, w.dtype)
+    g = moe.layer_backward(dd["x"], dd["W_gate"], dd["W1"], dd["W3"], dd["W2"], dy, k=w.k, capacity_factor=w.cf,
+                           act=w.act, fwd_ws=fws, d_aux=D_AUX)
+    torch.cuda.synchronize()
+    return g, gu.from_dev(logits)
+
+
+def _cmp(got, ref, dtype, what, scale=None, bf16_out=False):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if dtype == "bf16":
+        d = np.abs(got - ref)
+        bound = 2.0 ** -5 * np.asarray(scale, np.float64)
+        if bf16_out:
+            bound = bound + gu.half_ulp_bf16(ref)
+        bound = bound + 1e-30
+        bad = d > bound
+        rms = float(np.sqrt(np.mean(ref ** 2))) or 1.0
+        assert not bad.any(), (f"{what}: {int(bad.sum())} of {d.size} beyond 2^-5 scale; worst ratio "
+                               f"{float((d / bound).max()):.2f}")
+        _say(f"  {what}: max|d|/RMS {d.max() / rms:.4f}, max |d| / bound {float((d / bound).max()):.3f}")
+    else:
+        gu.check_rel_rms(got, ref, 1e-4, what)
+
+
+def _check_all(w, host, g, gl, dy_host, tokens=None, experts=None, with_w_gate=True):
+    ref = o.layer_backward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"],
+                           dy_host, D_AUX, k=w.k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, logits=gl,
+                           tokens=tokens, experts=experts, with_w_gate=with_w_gate, with_scale=True)
+    sc = ref["scale"]
+    tok = np.arange(w.T) if tokens is None else np.asarray(tokens)
+    dx = gu.as_f64(gu.from_dev(g["dx"])[tok], w.dtype)
+    _cmp(dx, ref["dx"][tok], w.dtype, "dx", sc["dx"][tok], bf16_out=True)
+    exps = list(range(w.E)) if experts is None else list(experts)
+    for name in ("dW1", "dW3", "dW2"):
+        if ref[name] is None:
+            continue
+        got = np.stack([gu.from_dev(g[name][e]) for e in exps])
+        _cmp(got, ref[name][exps], w.dtype, name, sc[name][exps])
+    if with_w_gate:
+        _cmp(gu.from_dev(g["dW_gate"]), ref["dW_gate"], w.dtype, "dW_gate", sc["dW_gate"])
+
+
+@pytest.mark.parametrize("T,h,f,E,k,cf,act,dtype", [
+    (64, 128, 256, 8, 2, 0.0, "swiglu", "f32"),
+    (33, 256, 192, 6, 3, 0.0, "gelu", "bf16"),       # ragged T
+    (65, 192, 320, 40, 3, 1.0, "swiglu", "bf16"),    # drops, many experts, some empty
+    (200, 192, 256, 4, 1, 0.3, "gelu", "bf16"),      # heavy drops, k = 1
+    (130, 64, 64, 1, 1, 0.0, "swiglu", "f32"),       # a single expert
+    (300, 128, 128, 5, 5, 0.0, "swiglu", "bf16"),    # k = E
+    (20, 1024, 2048, 8, 2, 0.0, "swiglu", "bf16"),   # K-split down projection: O in parts
+    (500, 128, 256, 16, 2, 0.25, "gelu", "f32"),     # fp32 with drops
+])
+def test_backward_edge_cases(T, h, f, E, k, cf, act, dtype):
+    _say(f"backward edge T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")
+    rng = np.random.default_rng(T + 3 * E)
+    conv = (lambda a: mw.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32),
+                logit_bias=rng.standard_normal(E).astype(np.float32),
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)) if act == "swiglu" else None,
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("edge", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
+    dy = _dy(T, h, dtype)
+    g, gl = _run(w, dd, dy)
+    _check_all(w, host, g, gl, dy)
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "decode-mixtral", "capacity-e64"])
+def test_backward_full_size(name):
+    _say(f"backward {name}")
+    w, host, dd = gu.workload(name)
+    dy = _dy(w.T, w.h, w.dtype)
+    g, gl = _run(w, dd, dy)
+    _check_all(w, host, g, gl, dy)
+
+
+@pytest.mark.parametrize("name", ["prefill-mixtral", "finegrained-e256"])
+def test_backward_full_size_sampled(name):
+    _say(f"backward {name} (sampled)")
+    w, host, dd = gu.workload(name)
+    dy = _dy(w.T, w.h, w.dtype)
+    g, gl = _run(w, dd, dy)
+    counts = o.histogram(o.select_topk(gl, w.k), w.E)
+    live = np.nonzero(counts > 0)[0]
+    e_small = int(live[np.argmin(counts[live])])
+    tokens = np.sort(np.random.default_rng(5).choice(w.T, 48, replace=False))
+    _say(f"  experts checked: {e_small} ({int(counts[e_small])} rows); tokens: {len(tokens)}")
+    _check_all(w, host, g, gl, dy, tokens=tokens, experts=[e_small], with_w_gate=False)
+
+
+def test_backward_deterministic():
+    torch = gu.torch()
+    w, host, dd = gu.workload("capacity-e64")
+    dy = _dy(w.T, w.h, w.dtype)
+    g1, _ = _run(w, dd, dy)
+    first = {kk: gu.from_dev(v).copy() for kk, v in g1.items() if v is not None}
+    g2, _ = _run(w, dd, dy)
+    for kk, v in first.items():
+        assert np.array_equal(v, gu.from_dev(g2[kk])), kk

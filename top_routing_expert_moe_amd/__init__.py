@@ -73,6 +73,11 @@ _SIGS = {
                                             _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
                                             _opts_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz,
                                             _c_void_p]),
+    "moe_layer_backward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int]),
+    "moe_layer_backward": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                          _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _c_void_p, _f32, _c_void_p,
+                                          _sz, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                          _sz, _c_void_p]),
     "moe_binned_capacity_max": (_i32, [_i32, _i32, _i32, _f32, _i32]),
     "moe_binned_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, ctypes.c_int]),
     "moe_layer_forward_binned": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -371,3 +376,30 @@ def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_
         _check(lib().moe_layer_forward_binned_timed(*args, ctypes.cast(events, _c_void_p)),
                "moe_layer_forward_binned_timed")
     return y, aux, counts, capacity, x_bins
+
+
+def layer_backward(x, W_gate, W1, W3, W2, dy, *, k: int, capacity_factor: float, act: str, fwd_ws,
+                   d_aux: float = 0.0, with_w_gate: bool = True, ws=None, out=None):
+    """Gradients of ``<dy, y> + d_aux * aux`` for the layer_forward call that used the
+    workspace ``fwd_ws`` (pass the same inputs).  Returns a dict with ``dx`` (x's dtype)
+    and fp32 ``dW_gate`` (or None), ``dW1``, ``dW3`` (None for GELU), ``dW2``.  ``out``:
+    preallocated tensors under those names."""
+    torch = _torch()
+    dev = x.device
+    T, h = x.shape
+    E, _, f = W1.shape
+    dt = _dt(x)
+    a = _ACT[act]
+    if ws is None:
+        ws = _ws(lib().moe_layer_backward_workspace_bytes(T, h, f, E, k, float(capacity_factor), dt, a), dev)
+    o = dict(out or {})
+    o.setdefault("dx", torch.empty_like(x))
+    o.setdefault("dW_gate", torch.empty((h, E), dtype=torch.float32, device=dev) if with_w_gate else None)
+    o.setdefault("dW1", torch.empty((E, h, f), dtype=torch.float32, device=dev))
+    o.setdefault("dW3", torch.empty((E, h, f), dtype=torch.float32, device=dev) if act == "swiglu" else None)
+    o.setdefault("dW2", torch.empty((E, f, h), dtype=torch.float32, device=dev))
+    _check(lib().moe_layer_backward(_p(x), _p(W_gate), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor),
+                                    a, dt, _p(dy), float(d_aux), _p(fwd_ws), fwd_ws.numel(), _p(o["dx"]),
+                                    _p(o["dW_gate"]), _p(o["dW1"]), _p(o["dW3"]), _p(o["dW2"]), _p(ws), ws.numel(),
+                                    _stream(dev)), "moe_layer_backward")
+    return o

@@ -672,6 +672,245 @@ moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* 
                             aux_loss, counts, ws, ws_bytes, stream, nullptr);
 }
 
+// ---- backward pass
+struct BwdWs {
+  int* counts;
+  int* tile64;
+  int* seg;
+  float* dw;
+  float* dl;
+  void* dO;
+  float* ag;
+  void* dag;
+  float* dXp;
+  float* dx_r;
+};
+static BwdWs carve_bwd(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int R_max, moe_dtype_t dt,
+                       moe_act_t act) {
+  const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
+  const size_t es = elem_bytes(dt);
+  BwdWs b;
+  b.counts = c.take<int>(E);
+  b.tile64 = c.take<int>((size_t)E + 1);
+  b.seg = c.take<int>(4);
+  b.dw = c.take<float>((size_t)T * k);
+  b.dl = c.take<float>((size_t)T * E);
+  b.dO = c.take<char>((size_t)R_max * h * es);
+  b.ag = c.take<float>((size_t)R_max * n_up * f);
+  b.dag = c.take<char>((size_t)R_max * n_up * f * es);
+  b.dXp = c.take<float>((size_t)R_max * h);
+  b.dx_r = c.take<float>((size_t)T * h);
+  return b;
+}
+
+size_t moe_layer_backward_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                          float capacity_factor, moe_dtype_t dt, moe_act_t act) {
+  if (common_sizes(T, E, k) != MOE_OK || !dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor)) return 0;
+  if (dim_ok(h) != MOE_OK || dim_ok(f) != MOE_OK) return 0;
+  const int R_max = rows_max(T, E, k, capacity_of(T, E, k, capacity_factor));
+  Carve c(nullptr);
+  carve_bwd(c, T, h, f, E, k, R_max, dt, act);
+  return c.bytes();
+}
+
+moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* W1, const void* W3, const void* W2,
+                                int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float capacity_factor,
+                                moe_act_t act, moe_dtype_t dt, const void* dy, float d_aux, const void* fwd_ws,
+                                size_t fwd_ws_bytes, void* dx, float* dW_gate, float* dW1, float* dW3, float* dW2,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t s = common_sizes(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor) || !isfinite(d_aux)) return MOE_ERR_ARG;
+  if ((s = dim_ok(h)) != MOE_OK) return s;
+  if ((s = dim_ok(f)) != MOE_OK) return s;
+  if (!x || !W_gate || !W1 || !W2 || !dy || !dx || !dW1 || !dW2) return MOE_ERR_ARG;
+  if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr) || (act == MOE_ACT_SWIGLU) != (dW3 != nullptr)) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  const int64_t C = capacity_of(T, E, k, capacity_factor);
+  const int R_max = rows_max(T, E, k, C);
+  const bool bf = dt == MOE_BF16;
+  const FfnPlan pl = layer_plan(bf, T, h, f, E, k, C);
+  // the forward's workspace, carved as the forward carved it
+  Carve cf(const_cast<void*>(fwd_ws));
+  LayerWs w = carve_layer(cf, T, h, f, E, k, R_max, pl, dt, act);
+  if (!fwd_ws || fwd_ws_bytes < cf.bytes()) return MOE_ERR_WORKSPACE;
+  Carve c(ws);
+  BwdWs b = carve_bwd(c, T, h, f, E, k, R_max, dt, act);
+  if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
+  const int gact = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
+
+  MOE_TRY(launch_counts(w.blk_counts, route_blocks(T), E, b.counts, stream));
+  MOE_TRY(launch_tile_scan(w.offsets, E, 64, b.tile64, stream));
+  MOE_TRY(launch_seg_init(b.seg, T, stream));
+  // combine: dw and dO
+  MOE_TRY(launch_combine_bwd(dy, w.o, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, b.dw, b.dO,
+                             stream));
+  // router: logit gradient of the renormalised selection and of the aux loss
+  MOE_TRY(launch_router_bwd(w.logits, w.topk_idx, w.topk_w, b.dw, b.counts, T, E, k, d_aux, b.dl, stream));
+  // the up projection's pre-activations a (| g), recomputed
+  const float* pa = b.ag;
+  const float* pg = nullptr;
+  int ld_ag = n_up * f;
+  {
+    GemmArgs up{};
+    up.A = x;
+    up.a_rows = w.perm_token;
+    up.K = h;
+    up.N = f;
+    up.offsets = w.offsets;
+    up.tile_off = w.tile_off;
+    up.E = E;
+    up.R_max = R_max;
+    up.bm = pl.bm;
+    up.ksplit = 1;
+    if (bf) {
+      up.W = W1;
+      up.W3 = act == MOE_ACT_SWIGLU ? W3 : nullptr;
+      up.out = b.ag;
+      up.act = gact;
+      up.raw = true;
+      MOE_TRY(launch_gemm(up, true, stream));
+      pg = b.ag + f;
+    } else {
+      up.act = ACT_NONE;
+      up.W = W1;
+      up.out = b.ag;
+      MOE_TRY(launch_gemm(up, false, stream));
+      if (act == MOE_ACT_SWIGLU) {
+        up.W = W3;
+        up.out = b.ag + (size_t)R_max * f;
+        MOE_TRY(launch_gemm(up, false, stream));
+      }
+      pg = b.ag + (size_t)R_max * f;
+      ld_ag = f;
+    }
+  }
+  // down projection: dHm = dO W2^T, folded into da (| dg) by the activation's derivative
+  BwdNT nt{};
+  nt.A = b.dO;
+  nt.lda = h;
+  nt.a_bf16 = bf;
+  nt.B1 = W2;
+  nt.B2 = W2;
+  nt.K1 = h;
+  nt.sbe = (long long)f * h;
+  nt.ldb = h;
+  nt.b_bf16 = bf;
+  nt.K = h;
+  nt.N = f;
+  nt.offsets = w.offsets;
+  nt.tile_off = b.tile64;
+  nt.E = E;
+  nt.R_max = R_max;
+  nt.epi = gact;
+  nt.pa = pa;
+  nt.pg = pg;
+  nt.ld_ag = ld_ag;
+  nt.DAG = b.dag;
+  MOE_TRY(launch_gemm_nt(nt, stream));
+  // dW2[e] = Hm^T dO
+  BwdTN tn{};
+  tn.A = w.hm;
+  tn.lda = f;
+  tn.a_bf16 = bf;
+  tn.B = b.dO;
+  tn.ldb = h;
+  tn.b_bf16 = bf;
+  tn.M = f;
+  tn.N = h;
+  tn.offsets = w.offsets;
+  tn.E = E;
+  tn.C1 = dW2;
+  tn.C2 = dW2;
+  tn.N1 = h;
+  tn.sce = (long long)f * h;
+  tn.ldc = h;
+  MOE_TRY(launch_gemm_tn(tn, stream));
+  // up projection: dX = da W1^T (+ dg W3^T)
+  nt = BwdNT{};
+  nt.A = b.dag;
+  nt.lda = n_up * f;
+  nt.a_bf16 = bf;
+  nt.B1 = W1;
+  nt.B2 = act == MOE_ACT_SWIGLU ? W3 : W1;
+  nt.K1 = f;
+  nt.sbe = (long long)h * f;
+  nt.ldb = f;
+  nt.b_bf16 = bf;
+  nt.K = n_up * f;
+  nt.N = h;
+  nt.offsets = w.offsets;
+  nt.tile_off = b.tile64;
+  nt.E = E;
+  nt.R_max = R_max;
+  nt.C = b.dXp;
+  nt.ldc = h;
+  nt.epi = ACT_NONE;
+  MOE_TRY(launch_gemm_nt(nt, stream));
+  // dW1[e] = X^T da, dW3[e] = X^T dg (X rows gathered from x)
+  tn = BwdTN{};
+  tn.A = x;
+  tn.lda = h;
+  tn.a_rows = w.perm_token;
+  tn.a_bf16 = bf;
+  tn.B = b.dag;
+  tn.ldb = n_up * f;
+  tn.b_bf16 = bf;
+  tn.M = h;
+  tn.N = n_up * f;
+  tn.offsets = w.offsets;
+  tn.E = E;
+  tn.C1 = dW1;
+  tn.C2 = act == MOE_ACT_SWIGLU ? dW3 : dW1;
+  tn.N1 = f;
+  tn.sce = (long long)h * f;
+  tn.ldc = f;
+  MOE_TRY(launch_gemm_tn(tn, stream));
+  // router: dx += dl W_gate^T (one segment of T rows), dW_gate = x^T dl
+  nt = BwdNT{};
+  nt.A = b.dl;
+  nt.lda = E;
+  nt.a_bf16 = false;
+  nt.B1 = W_gate;
+  nt.B2 = W_gate;
+  nt.K1 = E;
+  nt.sbe = 0;
+  nt.ldb = E;
+  nt.b_bf16 = false;
+  nt.K = E;
+  nt.N = h;
+  nt.offsets = b.seg;
+  nt.tile_off = b.seg + 2;
+  nt.E = 1;
+  nt.R_max = T;
+  nt.C = b.dx_r;
+  nt.ldc = h;
+  nt.epi = ACT_NONE;
+  MOE_TRY(launch_gemm_nt(nt, stream));
+  if (dW_gate) {
+    tn = BwdTN{};
+    tn.A = x;
+    tn.lda = h;
+    tn.a_bf16 = bf;
+    tn.B = b.dl;
+    tn.ldb = E;
+    tn.b_bf16 = false;
+    tn.M = h;
+    tn.N = E;
+    tn.offsets = b.seg;
+    tn.E = 1;
+    tn.C1 = dW_gate;
+    tn.C2 = dW_gate;
+    tn.N1 = E;
+    tn.sce = 0;
+    tn.ldc = E;
+    MOE_TRY(launch_gemm_tn(tn, stream));
+  }
+  MOE_TRY(launch_dx_final(b.dx_r, b.dXp, w.slot_pos, T, h, k, bf, dx, stream));
+  return MOE_OK;
+}
+
 moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
                                   const void* W3, const void* W2, int32_t T, int32_t h, int32_t f, int32_t E,
                                   int32_t k, float capacity_factor, moe_act_t act, moe_dtype_t dt,

@@ -1,0 +1,423 @@
+// Backward pass of the layer: the adjoint of each forward step, in reverse order.
+//
+// The pages name a backward pass for the gating operator (ops-transformer MoE article,
+// operator list: moe_gating holds the router's forward and backward) and autograd
+// wrappers around the permutation's gather and scatter (MegaBlocks chapter "01 · MoE
+// 为什么难算", section 5 file map) without writing them out; what is computed here is
+// the plain derivative of the forward:
+//  * combine:   dw[t,j] = <dy[t], O[r]>,  dO[r] = w[t,j] dy[t]   (r = slot of (t, j));
+//  * experts:   dHm = dO W2[e]^T; SwiGLU da = dHm g silu'(a), dg = dHm silu(a) (GELU:
+//               da = dHm gelu'(a)); dX = da W1[e]^T (+ dg W3[e]^T);
+//               dW2[e] = Hm^T dO, dW1[e] = X^T da, dW3[e] = X^T dg over the expert's rows;
+//  * permutation adjoint: dx[t] += sum_j dX[slot of (t, j)];
+//  * router:    softmax over the selected logits, dl[t,S_j] = w_j (dw_j - sum w dw); aux
+//               loss d_aux (E/T) p_i (f_i - sum_e f_e p_e) with the full softmax p;
+//               dW_gate = x^T dl, dx += dl W_gate^T.
+//
+// The GEMMs here run on the vector ALUs in fp32 (64 x 64 tiles, 4 x 4 per thread),
+// reading bf16 or fp32 operands: grouped "NT" products C[r, n] = sum_k A[r, k] B_e[n, k]
+// over the expert segments (the data-gradient GEMMs; B is the weight read along its
+// contiguous dimension) and grouped "TN" products C_e[m, n] = sum_r A[row(r), m] B[r, n]
+// over each expert's rows (the weight-gradient GEMMs).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+template <typename T> __device__ __forceinline__ float ld(const T* p, size_t i);
+template <> __device__ __forceinline__ float ld<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+template <typename T> __device__ __forceinline__ void st(T* p, size_t i, float v);
+template <> __device__ __forceinline__ void st<float>(float* p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, size_t i, float v) {
+  p[i] = (bf16_t)f32_to_bf16_bits(v);
+}
+
+__device__ __forceinline__ float silu_grad(float z) {
+  const float s = 1.0f / (1.0f + expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
+__device__ __forceinline__ float gelu_grad(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * expf(-0.5f * z * z) * 0.39894228040143268f;
+}
+
+// counts[e] = sum over the 64-token blocks of the selection kernel's histogram
+__global__ void counts_kernel(const int* __restrict__ blk_counts, int nblk, int E, int* __restrict__ counts) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  int s = 0;
+  for (int b = 0; b < nblk; ++b) s += blk_counts[(size_t)b * E + e];
+  counts[e] = s;
+}
+
+// tile_off[e] = exclusive scan of ceil(rows_e / BM) over the segments (one workgroup)
+__global__ void tile_scan_kernel(const int* __restrict__ offsets, int E, int BM, int* __restrict__ tile_off) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int e = 0; e < E; ++e) {
+    tile_off[e] = acc;
+    acc += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+  }
+  tile_off[E] = acc;
+}
+
+// One workgroup per token: dw[t,j] = <dy[t], O[r]> (O = sum of the down projection's
+// K parts) and dO[r] = w[t,j] dy[t]; dropped slots get dw = 0 and write nothing.
+template <typename TD>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const TD* __restrict__ dy, const float* __restrict__ O,
+                                                          int n_parts, size_t part_stride,
+                                                          const int* __restrict__ slot_pos,
+                                                          const float* __restrict__ topk_w, int T, int h, int k,
+                                                          float* __restrict__ dw, TD* __restrict__ dO) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int j = 0; j < k; ++j) {
+    const int r = slot_pos[(size_t)t * k + j];
+    if (r < 0) {
+      if (tid == 0) dw[(size_t)t * k + j] = 0.f;
+      continue;
+    }
+    const float wj = topk_w[(size_t)t * k + j];
+    float part = 0.f;
+    for (int i = tid; i < h; i += 256) {
+      const float g = ld(dy, (size_t)t * h + i);
+      float o = 0.f;
+      for (int p = 0; p < n_parts; ++p) o += O[p * part_stride + (size_t)r * h + i];
+      part += g * o;
+      st(dO, (size_t)r * h + i, wj * g);
+    }
+    part = wave_sum(part);
+    if ((tid & 63) == 0) red[tid >> 6] = part;
+    __syncthreads();
+    if (tid == 0) dw[(size_t)t * k + j] = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+  }
+}
+
+// One wave per token: the logit gradient of the renormalised selection and of the aux
+// loss.  Lane l holds experts l, l + 64, ...
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ logits,
+                                                         const int* __restrict__ topk_idx,
+                                                         const float* __restrict__ topk_w,
+                                                         const float* __restrict__ dw,
+                                                         const int* __restrict__ counts, int T, int E, int k,
+                                                         float d_aux, float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  constexpr int NQ = 4;  // E <= 256
+  float l[NQ], p[NQ], fe[NQ];
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    l[q] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    m = fmaxf(m, l[q]);
+  }
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    p[q] = e < E ? expf(l[q] - m) : 0.f;
+    s += p[q];
+  }
+  s = wave_sum(s);
+  const float inv = 1.0f / s;
+  const float scale = 1.0f / (float)((int64_t)T * k);
+  float fp = 0.f;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    p[q] *= inv;
+    fe[q] = e < E ? (float)counts[e] * scale : 0.f;
+    fp += fe[q] * p[q];
+  }
+  fp = wave_sum(fp);
+  const float ca = d_aux * (float)E / (float)T;
+  float g[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) g[q] = ca * p[q] * (fe[q] - fp);
+  // the renormalised softmax over the selection
+  float swd = 0.f;
+  for (int j = 0; j < k; ++j) swd += topk_w[(size_t)t * k + j] * dw[(size_t)t * k + j];
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(size_t)t * k + j];
+    const float v = topk_w[(size_t)t * k + j] * (dw[(size_t)t * k + j] - swd);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (lane + 64 * q == e) g[q] += v;
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E) dl[(size_t)t * E + e] = g[q];
+  }
+}
+
+constexpr int VT = 64, VK = 16;  // VALU GEMM tile and k step
+
+// C[r, n] = sum_k A[r, k] B(e, k, n) over the 64-row tiles of the segments, with
+// B(e, k, n) = B1[e*sbe + n*ldb + k] for k < K1, else B2[e*sbe + n*ldb + k - K1].
+// EPI = ACT_NONE: C fp32 [R, ldc].  EPI = ACT_SWIGLU / ACT_GELU: C is dHm; the epilogue
+// forms the activation's input gradients from the pre-activations (a at pa[r*ld_ag + n],
+// g at pg[r*ld_ag + n]) and writes da (and dg) to DAG [R, n_up*N] in TA.
+template <typename TA, typename TB, int EPI>
+__global__ __launch_bounds__(256) void gemm_nt_valu_kernel(const TA* __restrict__ A, int lda,
+                                                           const TB* __restrict__ B1, const TB* __restrict__ B2,
+                                                           int K1, long long sbe, int ldb, int K, int N,
+                                                           const int* __restrict__ offsets,
+                                                           const int* __restrict__ tile_off, int E,
+                                                           float* __restrict__ C, int ldc,
+                                                           const float* __restrict__ pa, const float* __restrict__ pg,
+                                                           int ld_ag, TA* __restrict__ DAG) {
+  __shared__ float As[VK][VT + 4];
+  __shared__ float Bs[VK][VT + 4];
+  const int tid = threadIdx.x;
+  const int mt = blockIdx.y;
+  if (mt >= tile_off[E]) return;
+  const int e = find_expert(tile_off, E, mt);
+  const int row0 = offsets[e] + (mt - tile_off[e]) * VT;
+  const int row_end = offsets[e + 1];
+  const int n0 = blockIdx.x * VT;
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  const int lr = tid / 4, lk = (tid % 4) * 4;  // loader: row / column lr, k lk .. lk+3
+  for (int k0 = 0; k0 < K; k0 += VK) {
+    {
+      const int r = row0 + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kk = k0 + lk + q;
+        As[lk + q][lr] = (r < row_end && kk < K) ? ld(A, (size_t)r * lda + kk) : 0.f;
+      }
+      const int n = n0 + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kk = k0 + lk + q;
+        float v = 0.f;
+        if (n < N && kk < K)
+          v = kk < K1 ? ld(B1, (size_t)e * sbe + (size_t)n * ldb + kk)
+                      : ld(B2, (size_t)e * sbe + (size_t)n * ldb + (kk - K1));
+        Bs[lk + q][lr] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < VK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = row0 + ty * 4 + i;
+    if (r >= row_end) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      const float v = acc[i][j];
+      if (EPI == ACT_NONE) {
+        C[(size_t)r * ldc + n] = v;
+      } else if (EPI == ACT_SWIGLU) {
+        const float a = pa[(size_t)r * ld_ag + n], g = pg[(size_t)r * ld_ag + n];
+        const float sa = a / (1.0f + expf(-a));
+        st(DAG, (size_t)r * 2 * N + n, v * g * silu_grad(a));
+        st(DAG, (size_t)r * 2 * N + N + n, v * sa);
+      } else {
+        const float a = pa[(size_t)r * ld_ag + n];
+        st(DAG, (size_t)r * N + n, v * gelu_grad(a));
+      }
+    }
+  }
+}
+
+// C_e[m, n] = sum over the rows r of segment e of A[row(r), m] B[r, n]; written to
+// C1[e*sce + m*ldc + n] for n < N1, else C2[e*sce + m*ldc + n - N1].  Rows past the
+// segment read as zero; an empty segment writes zeros.
+template <typename TA, typename TB, bool GATHER>
+__global__ __launch_bounds__(256) void gemm_tn_valu_kernel(const TA* __restrict__ A, int lda,
+                                                           const int* __restrict__ a_rows,
+                                                           const TB* __restrict__ B, int ldb, int M, int N,
+                                                           const int* __restrict__ offsets,
+                                                           float* __restrict__ C1, float* __restrict__ C2, int N1,
+                                                           long long sce, int ldc) {
+  __shared__ float As[VK][VT + 4];
+  __shared__ float Bs[VK][VT + 4];
+  const int tid = threadIdx.x;
+  const int e = blockIdx.z;
+  const int m0 = blockIdx.y * VT, n0 = blockIdx.x * VT;
+  const int rb = offsets[e], re = offsets[e + 1];
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  const int lk = tid / 16, lc = (tid % 16) * 4;  // loader: k row lk, columns lc .. lc+3
+  for (int r0 = rb; r0 < re; r0 += VK) {
+    const int r = r0 + lk;
+    const bool rv = r < re;
+    const size_t arow = rv ? (size_t)(GATHER ? a_rows[r] : r) : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = m0 + lc + q, n = n0 + lc + q;
+      As[lk][lc + q] = (rv && m < M) ? ld(A, arow * lda + m) : 0.f;
+      Bs[lk][lc + q] = (rv && n < N) ? ld(B, (size_t)r * ldb + n) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < VK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      if (n < N1) C1[(size_t)e * sce + (size_t)m * ldc + n] = acc[i][j];
+      else C2[(size_t)e * sce + (size_t)m * ldc + (n - N1)] = acc[i][j];
+    }
+  }
+}
+
+// dx[t] = dx_router[t] + sum over kept slots j (ascending) of dXp[slot of (t, j)]
+template <typename TD>
+__global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__ dx_router,
+                                                       const float* __restrict__ dXp,
+                                                       const int* __restrict__ slot_pos, int T, int h, int k,
+                                                       TD* __restrict__ dx) {
+  const int t = blockIdx.x;
+  for (int i = threadIdx.x; i < h; i += 256) {
+    float v = dx_router[(size_t)t * h + i];
+    for (int j = 0; j < k; ++j) {
+      const int r = slot_pos[(size_t)t * k + j];
+      if (r >= 0) v += dXp[(size_t)r * h + i];
+    }
+    st(dx, (size_t)t * h + i, v);
+  }
+}
+
+}  // namespace
+
+// one segment of T rows and its 64-row tile list: seg = {0, T}, seg + 2 = {0, ceil(T / 64)}
+__global__ void seg_init_kernel(int* seg, int T) {
+  if (threadIdx.x == 0) {
+    seg[0] = 0;
+    seg[1] = T;
+    seg[2] = 0;
+    seg[3] = (T + VT - 1) / VT;
+  }
+}
+
+hipError_t launch_seg_init(int* seg, int T, hipStream_t st) {
+  hipLaunchKernelGGL(seg_init_kernel, dim3(1), dim3(64), 0, st, seg, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_counts(const int* blk_counts, int nblk, int E, int* counts, hipStream_t st) {
+  hipLaunchKernelGGL(counts_kernel, dim3((E + 255) / 256), dim3(256), 0, st, blk_counts, nblk, E, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_scan(const int* offsets, int E, int BM, int* tile_off, hipStream_t st) {
+  hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(64), 0, st, offsets, E, BM, tile_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dy, const float* O, int n_parts, size_t part_stride, const int* slot_pos,
+                              const float* topk_w, int T, int h, int k, bool bf16, float* dw, void* dO,
+                              hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)dy, O, n_parts,
+                       part_stride, slot_pos, topk_w, T, h, k, dw, (bf16_t*)dO);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)dy, O, n_parts,
+                       part_stride, slot_pos, topk_w, T, h, k, dw, (float*)dO);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const float* topk_w, const float* dw,
+                             const int* counts, int T, int E, int k, float d_aux, float* dl, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (E > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, topk_idx, topk_w, dw, counts,
+                     T, E, k, d_aux, dl);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st) {
+  const dim3 grid((a.N + VT - 1) / VT, (a.R_max + VT - 1) / VT + a.E);
+#define MOE_NT(TA, TB, EPI)                                                                                    \
+  hipLaunchKernelGGL((gemm_nt_valu_kernel<TA, TB, EPI>), grid, dim3(256), 0, st, (const TA*)a.A, a.lda,        \
+                     (const TB*)a.B1, (const TB*)a.B2, a.K1, a.sbe, a.ldb, a.K, a.N, a.offsets, a.tile_off, a.E, \
+                     a.C, a.ldc, a.pa, a.pg, a.ld_ag, (TA*)a.DAG)
+  if (a.a_bf16 && a.b_bf16) {
+    if (a.epi == ACT_SWIGLU) MOE_NT(bf16_t, bf16_t, ACT_SWIGLU);
+    else if (a.epi == ACT_GELU) MOE_NT(bf16_t, bf16_t, ACT_GELU);
+    else MOE_NT(bf16_t, bf16_t, ACT_NONE);
+  } else if (!a.a_bf16 && !a.b_bf16) {
+    if (a.epi == ACT_SWIGLU) MOE_NT(float, float, ACT_SWIGLU);
+    else if (a.epi == ACT_GELU) MOE_NT(float, float, ACT_GELU);
+    else MOE_NT(float, float, ACT_NONE);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MOE_NT
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
+  const dim3 grid((a.N + VT - 1) / VT, (a.M + VT - 1) / VT, a.E);
+#define MOE_TN(TA, TB, G)                                                                                      \
+  hipLaunchKernelGGL((gemm_tn_valu_kernel<TA, TB, G>), grid, dim3(256), 0, st, (const TA*)a.A, a.lda, a.a_rows, \
+                     (const TB*)a.B, a.ldb, a.M, a.N, a.offsets, a.C1, a.C2, a.N1, a.sce, a.ldc)
+  const bool g = a.a_rows != nullptr;
+  if (a.a_bf16 && a.b_bf16) {
+    if (g) MOE_TN(bf16_t, bf16_t, true); else MOE_TN(bf16_t, bf16_t, false);
+  } else if (a.a_bf16 && !a.b_bf16) {
+    if (g) MOE_TN(bf16_t, float, true); else MOE_TN(bf16_t, float, false);
+  } else if (!a.a_bf16 && !a.b_bf16) {
+    if (g) MOE_TN(float, float, true); else MOE_TN(float, float, false);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MOE_TN
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_final(const float* dx_router, const float* dXp, const int* slot_pos, int T, int h, int k,
+                           bool bf16, void* dx, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(dx_final_kernel<bf16_t>, dim3(T), dim3(256), 0, st, dx_router, dXp, slot_pos, T, h, k,
+                       (bf16_t*)dx);
+  else
+    hipLaunchKernelGGL(dx_final_kernel<float>, dim3(T), dim3(256), 0, st, dx_router, dXp, slot_pos, T, h, k,
+                       (float*)dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

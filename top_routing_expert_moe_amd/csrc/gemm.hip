@@ -544,7 +544,7 @@ template <int ACT, bool G, typename OT, bool SPLIT>
 hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;
   const int NT = (a.N + NO - 1) / NO;
-  const int S = SPLIT ? a.ksplit : 1;
+  const int S = SPLIT ? std::max(a.ksplit, 1) : 1;
   const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
@@ -557,9 +557,10 @@ hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
 template <int ACT, bool G, typename OT>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
   if (a.bm != 256 && a.bm != 128 && a.bm != 32) return hipErrorInvalidValue;
-  if (a.ksplit > 1) {
+  if (a.ksplit > 1 || a.raw) {
     // K parts: for few rows per expert, where there are too few tiles to fill the chip
-    if (a.K % (a.ksplit * KB) != 0) return hipErrorInvalidValue;
+    // (or one part of raw accumulators)
+    if (a.K % (std::max(a.ksplit, 1) * KB) != 0) return hipErrorInvalidValue;
     constexpr int PA = ACT == ACT_SWIGLU ? ACT_SWIGLU : ACT_NONE;  // part layout
     return launch_bf16_k<PA, G, float, true>(a, st);
   }

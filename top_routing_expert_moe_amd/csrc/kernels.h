@@ -97,6 +97,9 @@ struct GemmArgs {
   // (row stride NW = 2N for SwiGLU -- W1 columns then W3 columns -- else N), and
   // launch_ffn_finish / the combine add the parts in ascending s.
   int ksplit;
+  // raw: write the raw fp32 accumulators in the K-part layout (one part when ksplit <= 1),
+  // no activation: the pre-activations [a | g] for the backward pass
+  bool raw;
 };
 
 // Tile height and K splits of one expert FFN (both GEMMs), a pure function of the sizes.
@@ -119,5 +122,38 @@ hipError_t launch_ffn_finish(const float* part, int S, int R_max, int N, int act
 // partial sums of the expert outputs, part s at O + s * o_part_stride elements.
 hipError_t launch_combine(const void* O, bool o_f32, int o_parts, size_t o_part_stride, const int* slot_pos,
                           const float* topk_w, int T, int h, int k, bool bf16, void* y, hipStream_t st);
+
+// ---- backward pass (backward.hip)
+// grouped NT product over the 64-row tiles of the segments (tile_off built with BM = 64):
+// C[r, n] = sum_k A[r, k] B(e, k, n), B(e, k, n) = B1[e*sbe + n*ldb + k] (k < K1) or
+// B2[e*sbe + n*ldb + k - K1]; epi = ACT_SWIGLU / ACT_GELU turns dHm into da (| dg) in DAG
+struct BwdNT {
+  const void* A; int lda; bool a_bf16;
+  const void* B1; const void* B2; int K1; long long sbe; int ldb; bool b_bf16;
+  int K, N;
+  const int* offsets; const int* tile_off; int E; int R_max;
+  float* C; int ldc;
+  int epi; const float* pa; const float* pg; int ld_ag; void* DAG;
+};
+// grouped TN product over each segment's rows: C_e[m, n] = sum_r A[row(r), m] B[r, n]
+struct BwdTN {
+  const void* A; int lda; const int* a_rows; bool a_bf16;
+  const void* B; int ldb; bool b_bf16;
+  int M, N;
+  const int* offsets; int E;
+  float* C1; float* C2; int N1; long long sce; int ldc;
+};
+hipError_t launch_seg_init(int* seg, int T, hipStream_t st);
+hipError_t launch_counts(const int* blk_counts, int nblk, int E, int* counts, hipStream_t st);
+hipError_t launch_tile_scan(const int* offsets, int E, int BM, int* tile_off, hipStream_t st);
+hipError_t launch_combine_bwd(const void* dy, const float* O, int n_parts, size_t part_stride, const int* slot_pos,
+                              const float* topk_w, int T, int h, int k, bool bf16, float* dw, void* dO,
+                              hipStream_t st);
+hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const float* topk_w, const float* dw,
+                             const int* counts, int T, int E, int k, float d_aux, float* dl, hipStream_t st);
+hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st);
+hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st);
+hipError_t launch_dx_final(const float* dx_router, const float* dXp, const int* slot_pos, int T, int h, int k,
+                           bool bf16, void* dx, hipStream_t st);
 
 }  // namespace moe
