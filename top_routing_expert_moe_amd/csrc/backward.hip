@@ -302,6 +302,172 @@ __global__ __launch_bounds__(256) void gemm_tn_valu_kernel(const TA* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same grouped NT / TN products for bf16 operands on MFMA (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation).  Workgroup tile 128 x 128, four waves of 64 x 64 (2 x 2 blocks of
+// 32 x 32), k in stages of 64, two LDS buffers: the next stage's 16-byte global loads
+// are in flight while the current stage's MFMAs run, then go to the other buffer.
+// Operand layouts in LDS:
+//  * K-contiguous (NT: both operands) -- [128 rows][64 k], rows padded to 72 elements
+//    (144 B) so that the 16 rows of one 16-byte read phase hit distinct banks; the MFMA
+//    fragment (8 consecutive k of one row) is one 16-byte read;
+//  * M/N-contiguous (TN: both operands) -- [64 k][128 cols], rows padded to 144
+//    elements (288 B); the fragment (8 consecutive k of one column) is two transposing
+//    8-byte reads (ds_read_b64_tr_b16: in a 16-lane group, lane j receives element j & 3
+//    of the 8-byte block addressed by lane 4i + (j >> 2)).
+constexpr int MT = 128, MKB = 64;
+constexpr int LDK = MKB + 8;    // K-contiguous row stride (elements)
+constexpr int LDM = MT + 16;    // M/N-contiguous row stride (elements)
+constexpr int KC_ELEMS = MT * LDK, MC_ELEMS = MKB * LDM;
+typedef short v4i16b __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16b v4i16_lds;
+
+template <bool MC>
+__device__ __forceinline__ bf16x8 frag(const bf16_t* buf, int rc0, int kh, int lane) {
+  if (!MC) {
+    return *(const bf16x8*)&buf[(rc0 + (lane & 31)) * LDK + 16 * kh + 8 * (lane >> 5)];
+  } else {
+    const int g = lane >> 4, s = lane & 15;
+    const int col = rc0 + 16 * (g & 1) + 4 * (s & 3);
+    const int r = 16 * kh + 8 * (g >> 1) + (s >> 2);
+    const v4i16b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16_lds*)&buf[r * LDM + col]);
+    const v4i16b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16_lds*)&buf[(r + 4) * LDM + col]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+// MODE 0 = NT over the 128-row tiles of the segments, MODE 1 = TN over each segment's rows.
+template <int MODE, int EPI, bool GATHER>
+__global__ __launch_bounds__(256) void gemm_bwd_mfma_kernel(
+    const bf16_t* __restrict__ A, int lda, const int* __restrict__ a_rows, const bf16_t* __restrict__ B1,
+    const bf16_t* __restrict__ B2, int K1, long long sbe, int ldb, int K, int M, int N,
+    const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, float* __restrict__ C1,
+    float* __restrict__ C2, int N1, long long sce, int ldc, const float* __restrict__ pa,
+    const float* __restrict__ pg, int ld_ag, bf16_t* __restrict__ DAG) {
+  constexpr bool MC = MODE == 1;
+  constexpr int SZ = MC ? MC_ELEMS : KC_ELEMS;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][SZ];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][SZ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int e, m0, row_end, kb, ke;
+  const int n0 = blockIdx.x * MT;
+  if (MODE == 0) {
+    const int mt = blockIdx.y;
+    if (mt >= tile_off[E]) return;
+    e = find_expert(tile_off, E, mt);
+    m0 = offsets[e] + (mt - tile_off[e]) * MT;  // segment rows
+    row_end = offsets[e + 1];
+    kb = 0;
+    ke = K;
+  } else {
+    e = blockIdx.z;
+    m0 = blockIdx.y * MT;                       // output rows (columns of A)
+    row_end = M;
+    kb = offsets[e];                            // k runs over the segment's rows
+    ke = offsets[e + 1];
+  }
+  const bf16_t* Be1 = B1 + (size_t)e * sbe;
+  const bf16_t* Be2 = B2 + (size_t)e * sbe;
+
+  u32x4 ra[4], rb[4];
+  // global -> registers for the stage starting at k0 (zero outside the operands)
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * q;
+      if (MODE == 0) {
+        const int row = c >> 3, kc = (c & 7) * 8;   // 128 rows x 8 chunks
+        const int r = m0 + row;
+        ra[q] = r < row_end ? *(const u32x4*)&A[(size_t)r * lda + k0 + kc] : u32x4{0u, 0u, 0u, 0u};
+        const int n = n0 + row;
+        const bf16_t* bp = k0 < K1 ? Be1 + (size_t)n * ldb + k0 + kc : Be2 + (size_t)n * ldb + (k0 - K1) + kc;
+        rb[q] = n < N ? *(const u32x4*)bp : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const int kr = c >> 4, cc = (c & 15) * 8;   // 64 k-rows x 16 chunks
+        const int r = k0 + kr;
+        const bool rv = r < ke;
+        const int arow = rv ? (GATHER ? a_rows[r] : r) : 0;
+        ra[q] = (rv && m0 + cc < M) ? *(const u32x4*)&A[(size_t)arow * lda + m0 + cc] : u32x4{0u, 0u, 0u, 0u};
+        rb[q] = (rv && n0 + cc < N) ? *(const u32x4*)&B1[(size_t)r * ldb + n0 + cc] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * q;
+      int off;
+      if (MODE == 0) off = (c >> 3) * LDK + (c & 7) * 8;
+      else off = (c >> 4) * LDM + (c & 15) * 8;
+      *(u32x4*)&As[buf][off] = ra[q];
+      *(u32x4*)&Bs[buf][off] = rb[q];
+    }
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (ke - kb + MKB - 1) / MKB;
+  if (nk > 0) {
+    gload(kb);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kb + (kt + 1) * MKB);
+#pragma unroll
+    for (int kh = 0; kh < MKB / 16; ++kh) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = frag<MC>(As[cur], wm * 64 + 32 * i, kh, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = frag<MC>(Bs[cur], wn * 64 + 32 * j, kh, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+  // lane holds, for acc element 4q + p of block (i, j): row wm*64 + 32i + 8q + 4*(lane >> 5) + p,
+  // column wn*64 + 32j + (lane & 31)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int m = m0 + wm * 64 + 32 * i + 8 * q + 4 * (lane >> 5) + p;
+          const int n = n0 + wn * 64 + 32 * j + (lane & 31);
+          if (m >= row_end || n >= N) continue;
+          const float v = acc[i][j][4 * q + p];
+          if (MODE == 1) {
+            if (n < N1) C1[(size_t)e * sce + (size_t)m * ldc + n] = v;
+            else C2[(size_t)e * sce + (size_t)m * ldc + (n - N1)] = v;
+          } else if (EPI == ACT_NONE) {
+            C1[(size_t)m * ldc + n] = v;
+          } else if (EPI == ACT_SWIGLU) {
+            const float a = pa[(size_t)m * ld_ag + n], g = pg[(size_t)m * ld_ag + n];
+            const float sa = a / (1.0f + expf(-a));
+            DAG[(size_t)m * 2 * N + n] = (bf16_t)f32_to_bf16_bits(v * g * silu_grad(a));
+            DAG[(size_t)m * 2 * N + N + n] = (bf16_t)f32_to_bf16_bits(v * sa);
+          } else {
+            const float a = pa[(size_t)m * ld_ag + n];
+            DAG[(size_t)m * N + n] = (bf16_t)f32_to_bf16_bits(v * gelu_grad(a));
+          }
+        }
+}
+
 // dx[t] = dx_router[t] + sum over kept slots j (ascending) of dXp[slot of (t, j)]
 template <typename TD>
 __global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__ dx_router,
@@ -369,6 +535,19 @@ hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const flo
 }
 
 hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st) {
+  if (a.a_bf16 && a.b_bf16 && a.tile_off128 != nullptr && a.K % MKB == 0 && a.K1 % MKB == 0 && a.lda % 8 == 0 &&
+      a.ldb % 8 == 0) {
+    const dim3 g((a.N + MT - 1) / MT, (a.R_max + MT - 1) / MT + a.E);
+#define MOE_NTM(EPI)                                                                                               \
+  hipLaunchKernelGGL((gemm_bwd_mfma_kernel<0, EPI, false>), g, dim3(256), 0, st, (const bf16_t*)a.A, a.lda, nullptr, \
+                     (const bf16_t*)a.B1, (const bf16_t*)a.B2, a.K1, a.sbe, a.ldb, a.K, 0, a.N, a.offsets,           \
+                     a.tile_off128, a.E, a.C, a.C, a.N, 0LL, a.ldc, a.pa, a.pg, a.ld_ag, (bf16_t*)a.DAG)
+    if (a.epi == ACT_SWIGLU) MOE_NTM(ACT_SWIGLU);
+    else if (a.epi == ACT_GELU) MOE_NTM(ACT_GELU);
+    else MOE_NTM(ACT_NONE);
+#undef MOE_NTM
+    return hipGetLastError();
+  }
   const dim3 grid((a.N + VT - 1) / VT, (a.R_max + VT - 1) / VT + a.E);
 #define MOE_NT(TA, TB, EPI)                                                                                    \
   hipLaunchKernelGGL((gemm_nt_valu_kernel<TA, TB, EPI>), grid, dim3(256), 0, st, (const TA*)a.A, a.lda,        \
@@ -390,6 +569,18 @@ hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
+  if (a.a_bf16 && a.b_bf16 && a.M % 8 == 0 && a.N % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0) {
+    const dim3 g((a.N + MT - 1) / MT, (a.M + MT - 1) / MT, a.E);
+    if (a.a_rows)
+      hipLaunchKernelGGL((gemm_bwd_mfma_kernel<1, ACT_NONE, true>), g, dim3(256), 0, st, (const bf16_t*)a.A, a.lda,
+                         a.a_rows, (const bf16_t*)a.B, (const bf16_t*)a.B, 0, 0LL, a.ldb, 0, a.M, a.N, a.offsets,
+                         nullptr, a.E, a.C1, a.C2, a.N1, a.sce, a.ldc, nullptr, nullptr, 0, nullptr);
+    else
+      hipLaunchKernelGGL((gemm_bwd_mfma_kernel<1, ACT_NONE, false>), g, dim3(256), 0, st, (const bf16_t*)a.A, a.lda,
+                         nullptr, (const bf16_t*)a.B, (const bf16_t*)a.B, 0, 0LL, a.ldb, 0, a.M, a.N, a.offsets,
+                         nullptr, a.E, a.C1, a.C2, a.N1, a.sce, a.ldc, nullptr, nullptr, 0, nullptr);
+    return hipGetLastError();
+  }
   const dim3 grid((a.N + VT - 1) / VT, (a.M + VT - 1) / VT, a.E);
 #define MOE_TN(TA, TB, G)                                                                                      \
   hipLaunchKernelGGL((gemm_tn_valu_kernel<TA, TB, G>), grid, dim3(256), 0, st, (const TA*)a.A, a.lda, a.a_rows, \

@@ -132,6 +132,7 @@ struct BwdNT {
   const void* B1; const void* B2; int K1; long long sbe; int ldb; bool b_bf16;
   int K, N;
   const int* offsets; const int* tile_off; int E; int R_max;
+  const int* tile_off128;  // 128-row tile list of the same segments: bf16 operands run on MFMA
   float* C; int ldc;
   int epi; const float* pa; const float* pg; int ld_ag; void* DAG;
 };
