@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--layout", choices=("compact", "binned"), default="compact")
     ap.add_argument("--capacity-factor", type=float, default=None, help="override the workload's factor")
     ap.add_argument("--min-capacity", type=int, default=0, help="binned layout: the smallest bucket size")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step: the layer forward, then its backward pass (dy ~ N(0,1), aux weight "
+                         "0.01), with per-stage times of both")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run a plain elementwise copy (y = x + 1, fp32) over this many MiB three "
                          "times: a kernel of known traffic for calibrating rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -125,6 +128,9 @@ def main():
         import dataclasses
         w = dataclasses.replace(w, cf=args.capacity_factor)
     binned = args.layout == "binned"
+    if args.backward and binned:
+        print("bench.py: the backward pass is built for the compact layout only", flush=True)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.lib()  # fail loudly if the HIP library is missing
@@ -169,6 +175,25 @@ def main():
         def step(events=None):
             moe.layer_forward(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
                               capacity_factor=w.cf, act=w.act, ws=ws, y=y, aux=aux, counts=counts, events=events)
+    if args.backward:
+        g = torch.Generator(device="cpu").manual_seed(1)
+        dy = torch.randn((T, h), generator=g, dtype=torch.float32).to(d["x"].dtype).to(dev)
+        bws = torch.empty(moe.lib().moe_layer_backward_workspace_bytes(T, h, f, E, k, w.cf, dt, act), dtype=torch.uint8,
+                          device=dev)
+        grads = {}
+        fwd_step = step
+        nf = len(moe.LAYER_STAGES)
+        stages = tuple(moe.LAYER_STAGES) + ("forward_to_backward",) + tuple("bwd_" + s for s in moe.BACKWARD_STAGES)
+
+        def step(events=None):
+            evf = evb = None
+            if events is not None:
+                evf = (ctypes.c_void_p * (nf + 1))(*events[:nf + 1])
+                evb = (ctypes.c_void_p * (len(moe.BACKWARD_STAGES) + 1))(*events[nf + 1:])
+            fwd_step(evf)
+            out = moe.layer_backward(d["x"], d["W_gate"], d["W1"], d["W3"], d["W2"], dy, k=k, capacity_factor=w.cf,
+                                     act=w.act, fwd_ws=ws, d_aux=0.01, ws=bws, out=grads or None, events=evb)
+            grads.update(out)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -273,8 +298,62 @@ def main():
         "aux_loss": float(aux.cpu()),
     }
 
+    if args.backward:
+        # the backward GEMMs: FLOPs and algorithmic bytes (operands read once, outputs written once;
+        # the weight gradients are fp32)
+        bw = {s_: stage_ms["bwd_" + s_] for s_ in moe.BACKWARD_STAGES}
+        Rk = int(kept.sum())
+        fl = {"recompute_up": 2.0 * n_up * Rk * h * f, "down_dgrad": 2.0 * Rk * h * f, "down_wgrad": 2.0 * Rk * f * h,
+              "up_dgrad": 2.0 * n_up * Rk * f * h, "up_wgrad": 2.0 * n_up * Rk * h * f}
+        by = {"recompute_up": active * n_up * h * f * es + Rk * h * es + Rk * n_up * f * 4,
+              "down_dgrad": active * f * h * es + Rk * h * es + Rk * n_up * f * 4 + Rk * n_up * f * es,
+              "down_wgrad": Rk * f * es + Rk * h * es + active * f * h * 4,
+              "up_dgrad": active * n_up * h * f * es + Rk * n_up * f * es + Rk * h * 4,
+              "up_wgrad": Rk * h * es + Rk * n_up * f * es + active * n_up * h * f * 4}
+        dom = max(fl, key=lambda s_: bw[s_])
+        t_dom = bw[dom] / 1e3
+        if not bf:
+            ach = fl[dom] / t_dom / 1e12
+            roofline = {"bound": "alu", "achieved": round(ach, 3), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_FP32_TFLOPS, 5)}
+        elif fl[dom] / by[dom] >= ridge:
+            ach = fl[dom] / t_dom / 1e12
+            roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = by[dom] / t_dom / 1e9
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(ach / PEAK_HBM_GBS, 4)}
+        roofline.update({"traffic": None, "kernel": f"backward {dom} (grouped GEMM)", "flops_per_launch": fl[dom],
+                         "algorithmic_bytes_per_launch": by[dom], "avg_launch_ms": round(bw[dom], 5)})
+        bwd_ms = sum(bw.values())
+        extra["backward_stage_ms"] = {s_: round(v, 5) for s_, v in bw.items()}
+        extra["backward_ms"] = round(bwd_ms, 5)
+        extra["backward_gemm_tflops"] = round(sum(fl.values()) / (sum(bw[s_] for s_ in fl) / 1e3) / 1e12, 2)
+        extra["train_step_mfma_frac"] = round((flops_up + flops_down + sum(fl.values())) / (ms_per_step / 1e3) / 1e12
+                                              / PEAK_BF16_TFLOPS, 4)
+
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.backward:
+        import oracle as o
+        try:
+            import threadpoolctl
+            threads = max(p_["num_threads"] for p_ in threadpoolctl.threadpool_info()) or 1
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        ns = min(args.cpu_sample, T)
+        tokens = np.arange(ns) * (T // ns)
+        dyh = dy.cpu()
+        dyh = dyh.view(torch.int16).numpy().view(np.uint16) if bf else dyh.numpy()
+        tc = time.perf_counter()
+        o.layer_backward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"], dyh, 0.01,
+                         k=k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, tokens=tokens, experts=[],
+                         with_w_gate=False)
+        el = time.perf_counter() - tc
+        cpu = {"value": round(ns / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"backward: full routing of all {T} tokens + dx of {ns} evenly spaced tokens through their "
+                         f"experts, no weight gradients (fp64 numpy, {el:.1f} s)"}
+    elif not args.no_cpu_baseline:
         import oracle as o
         try:
             import threadpoolctl
@@ -309,7 +388,7 @@ def main():
                                      "aux_rel_err": abs(extra["aux_loss"] - ref["aux"]) / abs(ref["aux"])}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not args.backward else "MoE layer training step (forward + backward) tokens/s",
         "value": round(T * args.steps / wall, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -322,7 +401,8 @@ def main():
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) random weights of the layer's shape)",
         "config": {"workload": w.name, "T": T, "h": h, "f": f, "E": E, "k": k, "act": w.act,
-                   "capacity_factor": w.cf, "router": "fp32", "logit_bias": w.bias, "layout": args.layout},
+                   "capacity_factor": w.cf, "router": "fp32", "logit_bias": w.bias, "layout": args.layout,
+                   "step": "forward + backward" if args.backward else "forward"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -221,6 +221,20 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
                                 float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* Measurement variant of moe_layer_backward: events[0] before the first kernel, then one
+ * after each stage (combine adjoint with the counts and tile lists, router adjoint,
+ * pre-activation recompute, down-projection data gradient with the activation's
+ * derivative, down-projection weight gradient, up-projection data gradient, up-projection
+ * weight gradients, router GEMMs, dx).  `events` holds MOE_BACKWARD_STAGES + 1 valid
+ * hipEvent_t (MOE_ERR_ARG otherwise). */
+#define MOE_BACKWARD_STAGES 9
+moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const void* W1, const void* W3,
+                                      const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                      float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
+                                      float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                                      float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
+                                      size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
 /* The layer with fixed-capacity buckets ("binned" layout: [MB] sections 3, 4.3 and 4.5;
  * [CAI] SparseMLP data flow step 4 and its capacity parameters).  Every expert gets a
  * bucket of C rows: C = max(floor(cf * T*k/E), min_capacity) when cf > 0, else (or if that

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(L):
                           "moe_route_workspace_bytes", "moe_binned_capacity_max", "moe_binned_workspace_bytes",
                           "moe_layer_forward_binned", "moe_layer_forward_binned_timed",
                           "moe_router_opts_workspace_bytes", "moe_route_ex", "moe_layer_forward_ex",
-                          "moe_layer_backward_workspace_bytes", "moe_layer_backward"}
+                          "moe_layer_backward_workspace_bytes", "moe_layer_backward", "moe_layer_backward_timed"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -367,6 +367,12 @@ def test_layer_backward_host_errors(L):
     assert call(fwsb=fwd - 1) == WS              # the forward's workspace is the saved context
     assert call(wsb=bws - 1) == WS
     assert call(T=0) == OK
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, T, h, f, E, k, 0.0, 1, 1, FAKE, 0.0, FAKE, fwd, FAKE, None, FAKE, FAKE, FAKE,
+         FAKE, bws, None]
+    assert L.moe_layer_backward_timed(*a, None) == ARG
+    ev = (ctypes.c_void_p * 10)(*([FAKE] * 9 + [0]))
+    assert L.moe_layer_backward_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == ARG
+    assert len(moe.BACKWARD_STAGES) == 9
 
 
 def test_binding_refuses_cpu_tensors(L):

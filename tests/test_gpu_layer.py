@@ -134,8 +134,8 @@ def test_layer_forward_timed_matches_untimed():
     assert abs(sum(stages) - total) <= 1e-3 * max(total, 1e-3) + 1e-3
 
 
-@pytest.mark.parametrize("layout", ["compact", "binned"])
-def test_bench_json_contract(layout):
+@pytest.mark.parametrize("layout,backward", [("compact", False), ("binned", False), ("compact", True)])
+def test_bench_json_contract(layout, backward):
     """bench.py on the small fp32 workload prints one JSON line with the fields the
     benchmark contract names."""
     import json
@@ -145,7 +145,7 @@ def test_bench_json_contract(layout):
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--steps", "3", "--warmup", "1",
                         "--workload", "tiny-fp32", "--cpu-sample", "64", "--layout", layout,
-                        "--min-capacity", "3"], capture_output=True, text=True,
+                        "--min-capacity", "3"] + (["--backward"] if backward else []), capture_output=True, text=True,
                        timeout=300, cwd=root)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
@@ -162,4 +162,8 @@ def test_bench_json_contract(layout):
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
-    assert d["extra"]["parity_vs_oracle"]["routing_differs"] <= 1  # a near-tie may route differently
+    if backward:
+        assert d["config"]["step"] == "forward + backward" and d["extra"]["backward_ms"] > 0
+        assert set(d["extra"]["backward_stage_ms"]) == set(moe.BACKWARD_STAGES)
+    else:
+        assert d["extra"]["parity_vs_oracle"]["routing_differs"] <= 1  # a near-tie may route differently

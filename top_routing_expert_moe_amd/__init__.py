@@ -78,6 +78,10 @@ _SIGS = {
                                           _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _c_void_p, _f32, _c_void_p,
                                           _sz, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                           _sz, _c_void_p]),
+    "moe_layer_backward_timed": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                                                _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _c_void_p, _f32,
+                                                _c_void_p, _sz, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                _c_void_p, _c_void_p, _sz, _c_void_p, _c_void_p]),
     "moe_binned_capacity_max": (_i32, [_i32, _i32, _i32, _f32, _i32]),
     "moe_binned_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, ctypes.c_int]),
     "moe_layer_forward_binned": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -91,6 +95,8 @@ _SIGS = {
 }
 
 LAYER_STAGES = ("logits", "select", "scan", "scatter", "expert_up", "expert_down", "combine")
+BACKWARD_STAGES = ("combine_bwd", "router_bwd", "recompute_up", "down_dgrad", "down_wgrad", "up_dgrad", "up_wgrad",
+                   "router_gemms", "dx")
 BINNED_STAGES = ("logits", "select", "scan", "scatter", "gather", "expert_up", "expert_down", "combine")
 
 _lib = None
@@ -379,11 +385,12 @@ def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_
 
 
 def layer_backward(x, W_gate, W1, W3, W2, dy, *, k: int, capacity_factor: float, act: str, fwd_ws,
-                   d_aux: float = 0.0, with_w_gate: bool = True, ws=None, out=None):
+                   d_aux: float = 0.0, with_w_gate: bool = True, ws=None, out=None, events=None):
     """Gradients of ``<dy, y> + d_aux * aux`` for the layer_forward call that used the
     workspace ``fwd_ws`` (pass the same inputs).  Returns a dict with ``dx`` (x's dtype)
     and fp32 ``dW_gate`` (or None), ``dW1``, ``dW3`` (None for GELU), ``dW2``.  ``out``:
-    preallocated tensors under those names."""
+    preallocated tensors under those names.  ``events``: ``len(BACKWARD_STAGES) + 1``
+    hipEvent_t handles recorded between the stages."""
     torch = _torch()
     dev = x.device
     T, h = x.shape
@@ -398,8 +405,11 @@ def layer_backward(x, W_gate, W1, W3, W2, dy, *, k: int, capacity_factor: float,
     o.setdefault("dW1", torch.empty((E, h, f), dtype=torch.float32, device=dev))
     o.setdefault("dW3", torch.empty((E, h, f), dtype=torch.float32, device=dev) if act == "swiglu" else None)
     o.setdefault("dW2", torch.empty((E, f, h), dtype=torch.float32, device=dev))
-    _check(lib().moe_layer_backward(_p(x), _p(W_gate), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor),
-                                    a, dt, _p(dy), float(d_aux), _p(fwd_ws), fwd_ws.numel(), _p(o["dx"]),
-                                    _p(o["dW_gate"]), _p(o["dW1"]), _p(o["dW3"]), _p(o["dW2"]), _p(ws), ws.numel(),
-                                    _stream(dev)), "moe_layer_backward")
+    args = (_p(x), _p(W_gate), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor), a, dt, _p(dy),
+            float(d_aux), _p(fwd_ws), fwd_ws.numel(), _p(o["dx"]), _p(o["dW_gate"]), _p(o["dW1"]), _p(o["dW3"]),
+            _p(o["dW2"]), _p(ws), ws.numel(), _stream(dev))
+    if events is None:
+        _check(lib().moe_layer_backward(*args), "moe_layer_backward")
+    else:
+        _check(lib().moe_layer_backward_timed(*args, ctypes.cast(events, _c_void_p)), "moe_layer_backward_timed")
     return o

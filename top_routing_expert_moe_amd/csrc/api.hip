@@ -715,11 +715,12 @@ size_t moe_layer_backward_workspace_bytes(int32_t T, int32_t h, int32_t f, int32
   return c.bytes();
 }
 
-moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* W1, const void* W3, const void* W2,
-                                int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float capacity_factor,
-                                moe_act_t act, moe_dtype_t dt, const void* dy, float d_aux, const void* fwd_ws,
-                                size_t fwd_ws_bytes, void* dx, float* dW_gate, float* dW1, float* dW3, float* dW2,
-                                void* ws, size_t ws_bytes, hipStream_t stream) {
+static moe_status_t layer_backward_impl(const void* x, const float* W_gate, const void* W1, const void* W3,
+                                        const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                        float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
+                                        float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                                        float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
+                                        size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
   moe_status_t s = common_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor) || !isfinite(d_aux)) return MOE_ERR_ARG;
@@ -741,6 +742,9 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
   const int gact = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
+  int stage = 0;
+  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
+  if (!mark()) return MOE_ERR_DEVICE;
 
   MOE_TRY(launch_counts(w.blk_counts, route_blocks(T), E, b.counts, stream));
   MOE_TRY(launch_tile_scan(w.offsets, E, 64, b.tile64, stream));
@@ -749,8 +753,10 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
   // combine: dw and dO
   MOE_TRY(launch_combine_bwd(dy, w.o, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, b.dw, b.dO,
                              stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   // router: logit gradient of the renormalised selection and of the aux loss
   MOE_TRY(launch_router_bwd(w.logits, w.topk_idx, w.topk_w, b.dw, b.counts, T, E, k, d_aux, b.dl, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   // the up projection's pre-activations a (| g), recomputed
   const float* pa = b.ag;
   const float* pg = nullptr;
@@ -789,6 +795,7 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
       ld_ag = f;
     }
   }
+  if (!mark()) return MOE_ERR_DEVICE;
   // down projection: dHm = dO W2^T, folded into da (| dg) by the activation's derivative
   BwdNT nt{};
   nt.A = b.dO;
@@ -813,6 +820,7 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
   nt.ld_ag = ld_ag;
   nt.DAG = b.dag;
   MOE_TRY(launch_gemm_nt(nt, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   // dW2[e] = Hm^T dO
   BwdTN tn{};
   tn.A = w.hm;
@@ -831,6 +839,7 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
   tn.sce = (long long)f * h;
   tn.ldc = h;
   MOE_TRY(launch_gemm_tn(tn, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   // up projection: dX = da W1^T (+ dg W3^T)
   nt = BwdNT{};
   nt.A = b.dag;
@@ -853,6 +862,7 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
   nt.ldc = h;
   nt.epi = ACT_NONE;
   MOE_TRY(launch_gemm_nt(nt, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   // dW1[e] = X^T da, dW3[e] = X^T dg (X rows gathered from x)
   tn = BwdTN{};
   tn.A = x;
@@ -872,6 +882,7 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
   tn.sce = (long long)h * f;
   tn.ldc = f;
   MOE_TRY(launch_gemm_tn(tn, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   // router: dx += dl W_gate^T (one segment of T rows), dW_gate = x^T dl
   nt = BwdNT{};
   nt.A = b.dl;
@@ -912,8 +923,32 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
     tn.ldc = E;
     MOE_TRY(launch_gemm_tn(tn, stream));
   }
+  if (!mark()) return MOE_ERR_DEVICE;
   MOE_TRY(launch_dx_final(b.dx_r, b.dXp, w.slot_pos, T, h, k, bf, dx, stream));
+  if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
+}
+
+moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* W1, const void* W3, const void* W2,
+                                int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float capacity_factor,
+                                moe_act_t act, moe_dtype_t dt, const void* dy, float d_aux, const void* fwd_ws,
+                                size_t fwd_ws_bytes, void* dx, float* dW_gate, float* dW1, float* dW3, float* dW2,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_backward_impl(x, W_gate, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, dy, d_aux, fwd_ws,
+                             fwd_ws_bytes, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const void* W1, const void* W3,
+                                      const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                      float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
+                                      float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                                      float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                                      hipStream_t stream, hipEvent_t* events) {
+  if (events == nullptr) return MOE_ERR_ARG;
+  for (int i = 0; i < MOE_BACKWARD_STAGES + 1; ++i)
+    if (events[i] == nullptr) return MOE_ERR_ARG;
+  return layer_backward_impl(x, W_gate, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, dy, d_aux, fwd_ws,
+                             fwd_ws_bytes, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream, events);
 }
 
 moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
