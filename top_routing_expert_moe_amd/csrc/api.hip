@@ -685,7 +685,10 @@ struct BwdWs {
   void* dag;
   float* dXp;
   float* dx_r;
+  float* wg_part;  // partial sums of dW_gate over token slices
 };
+// token slices of dW_gate = x^T dl: about 512 tokens each, at most 64
+static int wgate_splits(int32_t T) { return std::max(1, std::min(64, (T + 511) / 512)); }
 static BwdWs carve_bwd(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int R_max, moe_dtype_t dt,
                        moe_act_t act) {
   const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
@@ -702,6 +705,8 @@ static BwdWs carve_bwd(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int
   b.dag = c.take<char>((size_t)R_max * n_up * f * es);
   b.dXp = c.take<float>((size_t)R_max * h);
   b.dx_r = c.take<float>((size_t)T * h);
+  const int S = wgate_splits(T);
+  b.wg_part = S > 1 ? c.take<float>((size_t)S * h * E) : nullptr;
   return b;
 }
 
@@ -921,6 +926,9 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
     tn.N1 = E;
     tn.sce = 0;
     tn.ldc = E;
+    tn.ksplit = wgate_splits(T);
+    tn.rows = T;
+    tn.part = b.wg_part;
     MOE_TRY(launch_gemm_tn(tn, stream));
   }
   if (!mark()) return MOE_ERR_DEVICE;

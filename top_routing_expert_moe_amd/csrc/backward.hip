@@ -247,19 +247,27 @@ __global__ __launch_bounds__(256) void gemm_nt_valu_kernel(const TA* __restrict_
 // C_e[m, n] = sum over the rows r of segment e of A[row(r), m] B[r, n]; written to
 // C1[e*sce + m*ldc + n] for n < N1, else C2[e*sce + m*ldc + n - N1].  Rows past the
 // segment read as zero; an empty segment writes zeros.
+// With rows_per_split > 0 (one segment only): blockIdx.z takes rows_per_split rows of it
+// and writes its partial sums to C1 + z * sce (added by reduce_parts_kernel).
 template <typename TA, typename TB, bool GATHER>
 __global__ __launch_bounds__(256) void gemm_tn_valu_kernel(const TA* __restrict__ A, int lda,
                                                            const int* __restrict__ a_rows,
                                                            const TB* __restrict__ B, int ldb, int M, int N,
                                                            const int* __restrict__ offsets,
                                                            float* __restrict__ C1, float* __restrict__ C2, int N1,
-                                                           long long sce, int ldc) {
+                                                           long long sce, int ldc, int rows_per_split) {
   __shared__ float As[VK][VT + 4];
   __shared__ float Bs[VK][VT + 4];
   const int tid = threadIdx.x;
-  const int e = blockIdx.z;
+  const int e = rows_per_split > 0 ? 0 : blockIdx.z;
   const int m0 = blockIdx.y * VT, n0 = blockIdx.x * VT;
-  const int rb = offsets[e], re = offsets[e + 1];
+  int rb = offsets[e], re = offsets[e + 1];
+  if (rows_per_split > 0) {
+    rb += blockIdx.z * rows_per_split;
+    re = min(re, rb + rows_per_split);
+    C1 += (size_t)blockIdx.z * sce;
+    C2 = C1;
+  }
   const int ty = tid / 16, tx = tid % 16;
   float acc[4][4] = {};
   const int lk = tid / 16, lc = (tid % 16) * 4;  // loader: k row lk, columns lc .. lc+3
@@ -296,10 +304,21 @@ __global__ __launch_bounds__(256) void gemm_tn_valu_kernel(const TA* __restrict_
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
       if (n >= N) continue;
-      if (n < N1) C1[(size_t)e * sce + (size_t)m * ldc + n] = acc[i][j];
+      if (rows_per_split > 0) C1[(size_t)m * ldc + n] = acc[i][j];
+      else if (n < N1) C1[(size_t)e * sce + (size_t)m * ldc + n] = acc[i][j];
       else C2[(size_t)e * sce + (size_t)m * ldc + (n - N1)] = acc[i][j];
     }
   }
+}
+
+// out[i] = sum over s = 0 .. S-1 (ascending) of part[s * n + i]
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ part, int S, int64_t n,
+                                                           float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.f;
+  for (int p = 0; p < S; ++p) v += part[(size_t)p * n + i];
+  out[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -569,6 +588,23 @@ hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
+  if (a.ksplit > 1) {
+    // one segment of rows split in a.ksplit slices: partial sums in a.part, added in order
+    if (a.E != 1 || a.part == nullptr || a.a_rows != nullptr) return hipErrorInvalidValue;
+    const int per = (a.rows + a.ksplit - 1) / a.ksplit;
+    const dim3 g((a.N + VT - 1) / VT, (a.M + VT - 1) / VT, a.ksplit);
+    const long long sz = (long long)a.M * a.ldc;
+#define MOE_TNS(TA, TB)                                                                                         \
+  hipLaunchKernelGGL((gemm_tn_valu_kernel<TA, TB, false>), g, dim3(256), 0, st, (const TA*)a.A, a.lda, nullptr, \
+                     (const TB*)a.B, a.ldb, a.M, a.N, a.offsets, a.part, a.part, a.N, sz, a.ldc, per)
+    if (a.a_bf16 && !a.b_bf16) MOE_TNS(bf16_t, float);
+    else if (!a.a_bf16 && !a.b_bf16) MOE_TNS(float, float);
+    else return hipErrorInvalidValue;
+#undef MOE_TNS
+    hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)((sz + 255) / 256)), dim3(256), 0, st, a.part, a.ksplit,
+                       (int64_t)sz, a.C1);
+    return hipGetLastError();
+  }
   if (a.a_bf16 && a.b_bf16 && a.M % 8 == 0 && a.N % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0) {
     const dim3 g((a.N + MT - 1) / MT, (a.M + MT - 1) / MT, a.E);
     if (a.a_rows)
@@ -584,7 +620,7 @@ hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
   const dim3 grid((a.N + VT - 1) / VT, (a.M + VT - 1) / VT, a.E);
 #define MOE_TN(TA, TB, G)                                                                                      \
   hipLaunchKernelGGL((gemm_tn_valu_kernel<TA, TB, G>), grid, dim3(256), 0, st, (const TA*)a.A, a.lda, a.a_rows, \
-                     (const TB*)a.B, a.ldb, a.M, a.N, a.offsets, a.C1, a.C2, a.N1, a.sce, a.ldc)
+                     (const TB*)a.B, a.ldb, a.M, a.N, a.offsets, a.C1, a.C2, a.N1, a.sce, a.ldc, 0)
   const bool g = a.a_rows != nullptr;
   if (a.a_bf16 && a.b_bf16) {
     if (g) MOE_TN(bf16_t, bf16_t, true); else MOE_TN(bf16_t, bf16_t, false);

@@ -143,6 +143,9 @@ struct BwdTN {
   int M, N;
   const int* offsets; int E;
   float* C1; float* C2; int N1; long long sce; int ldc;
+  // one segment (E == 1, no gather) of `rows` rows in ksplit slices: fp32 partial sums
+  // [ksplit][M][ldc] in `part`, then added in slice order
+  int ksplit; int rows; float* part;
 };
 hipError_t launch_seg_init(int* seg, int T, hipStream_t st);
 hipError_t launch_counts(const int* blk_counts, int nblk, int E, int* counts, hipStream_t st);
