@@ -676,7 +676,7 @@ moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* 
 struct BwdWs {
   int* counts;
   int* tile64;
-  int* tile128;
+  int* tile_ts;  // data-gradient tile list (ts rows per tile)
   int* seg;
   float* dw;
   float* dl;
@@ -696,7 +696,7 @@ static BwdWs carve_bwd(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int
   BwdWs b;
   b.counts = c.take<int>(E);
   b.tile64 = c.take<int>((size_t)E + 1);
-  b.tile128 = c.take<int>((size_t)E + 1);
+  b.tile_ts = c.take<int>((size_t)E + 1);
   b.seg = c.take<int>(4);
   b.dw = c.take<float>((size_t)T * k);
   b.dl = c.take<float>((size_t)T * E);
@@ -753,7 +753,9 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
 
   MOE_TRY(launch_counts(w.blk_counts, route_blocks(T), E, b.counts, stream));
   MOE_TRY(launch_tile_scan(w.offsets, E, 64, b.tile64, stream));
-  if (bf) MOE_TRY(launch_tile_scan(w.offsets, E, 128, b.tile128, stream));
+  // data-gradient tile height: 256 rows when the forward's GEMMs take 256-row tiles
+  const int ts = pl.bm == 256 ? 256 : 128;
+  if (bf) MOE_TRY(launch_tile_scan(w.offsets, E, ts, b.tile_ts, stream));
   MOE_TRY(launch_seg_init(b.seg, T, stream));
   // combine: dw and dO
   MOE_TRY(launch_combine_bwd(dy, w.o, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, b.dw, b.dO,
@@ -816,7 +818,8 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   nt.N = f;
   nt.offsets = w.offsets;
   nt.tile_off = b.tile64;
-  nt.tile_off128 = bf ? b.tile128 : nullptr;
+  nt.ts = ts;
+  nt.tile_off_ts = bf ? b.tile_ts : nullptr;
   nt.E = E;
   nt.R_max = R_max;
   nt.epi = gact;
@@ -860,7 +863,8 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   nt.N = h;
   nt.offsets = w.offsets;
   nt.tile_off = b.tile64;
-  nt.tile_off128 = bf ? b.tile128 : nullptr;
+  nt.ts = ts;
+  nt.tile_off_ts = bf ? b.tile_ts : nullptr;
   nt.E = E;
   nt.R_max = R_max;
   nt.C = b.dXp;

@@ -327,21 +327,22 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restri
 // 32 x 32), k in stages of 64, two LDS buffers: the next stage's 16-byte global loads
 // are in flight while the current stage's MFMAs run, then go to the other buffer.
 // Operand layouts in LDS:
-//  * K-contiguous (NT: both operands) -- [128 rows][64 k], rows padded to 72 elements
+//  * K-contiguous (NT: both operands) -- [TS rows][64 k], rows padded to 72 elements
 //    (144 B) so that the 16 rows of one 16-byte read phase hit distinct banks; the MFMA
 //    fragment (8 consecutive k of one row) is one 16-byte read;
-//  * M/N-contiguous (TN: both operands) -- [64 k][128 cols], rows padded to 144
-//    elements (288 B); the fragment (8 consecutive k of one column) is two transposing
+//  * M/N-contiguous (TN: both operands) -- [64 k][TS cols], rows padded by 16 elements
+//    (rows 8 banks apart); the fragment (8 consecutive k of one column) is two transposing
 //    8-byte reads (ds_read_b64_tr_b16: in a 16-lane group, lane j receives element j & 3
 //    of the 8-byte block addressed by lane 4i + (j >> 2)).
-constexpr int MT = 128, MKB = 64;
+// Tile sizes: TS = 128 (four waves of 64 x 64, two workgroups per CU) or TS = 256 (eight
+// waves of 64 x 128, one workgroup per CU): the larger tile reads each operand half as
+// often, which is what bounds these products when both operands stream from HBM.
+constexpr int MKB = 64;
 constexpr int LDK = MKB + 8;    // K-contiguous row stride (elements)
-constexpr int LDM = MT + 16;    // M/N-contiguous row stride (elements)
-constexpr int KC_ELEMS = MT * LDK, MC_ELEMS = MKB * LDM;
 typedef short v4i16b __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16b v4i16_lds;
 
-template <bool MC>
+template <bool MC, int LDM>
 __device__ __forceinline__ bf16x8 frag(const bf16_t* buf, int rc0, int kh, int lane) {
   if (!MC) {
     return *(const bf16x8*)&buf[(rc0 + (lane & 31)) * LDK + 16 * kh + 8 * (lane >> 5)];
@@ -355,33 +356,46 @@ __device__ __forceinline__ bf16x8 frag(const bf16_t* buf, int rc0, int kh, int l
   }
 }
 
-// MODE 0 = NT over the 128-row tiles of the segments, MODE 1 = TN over each segment's rows.
-template <int MODE, int EPI, bool GATHER>
-__global__ __launch_bounds__(256) void gemm_bwd_mfma_kernel(
-    const bf16_t* __restrict__ A, int lda, const int* __restrict__ a_rows, const bf16_t* __restrict__ B1,
-    const bf16_t* __restrict__ B2, int K1, long long sbe, int ldb, int K, int M, int N,
-    const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, float* __restrict__ C1,
-    float* __restrict__ C2, int N1, long long sce, int ldc, const float* __restrict__ pa,
-    const float* __restrict__ pg, int ld_ag, bf16_t* __restrict__ DAG) {
+template <int TS> struct BwdTile {
+  static constexpr int NW = TS == 256 ? 8 : 4;           // waves
+  static constexpr int WMW = TS == 256 ? 4 : 2, WNW = 2;  // waves along m / along n
+  static constexpr int WTM = TS / WMW, WTN = TS / WNW;    // wave tile
+  static constexpr int IB = WTM / 32, JB = WTN / 32;
+  static constexpr int LDM = TS + 16;
+  static constexpr int KC_ELEMS = TS * LDK, MC_ELEMS = MKB * LDM;
+  static constexpr int NQ = TS * 8 / (NW * 64);           // 16-byte chunks per thread and operand
+};
+
+// MODE 0 = NT over the TS-row tiles of the segments, MODE 1 = TN over each segment's rows.
+template <int MODE, int EPI, bool GATHER, int TS>
+__global__ __launch_bounds__(BwdTile<TS>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+gemm_bwd_mfma_kernel(const bf16_t* __restrict__ A, int lda, const int* __restrict__ a_rows,
+                     const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B2, int K1, long long sbe, int ldb,
+                     int K, int M, int N, const int* __restrict__ offsets, const int* __restrict__ tile_off, int E,
+                     float* __restrict__ C1, float* __restrict__ C2, int N1, long long sce, int ldc,
+                     const float* __restrict__ pa, const float* __restrict__ pg, int ld_ag, bf16_t* __restrict__ DAG) {
+  using TC = BwdTile<TS>;
+  constexpr int NT_ = TC::NW * 64;
   constexpr bool MC = MODE == 1;
-  constexpr int SZ = MC ? MC_ELEMS : KC_ELEMS;
+  constexpr int SZ = MC ? TC::MC_ELEMS : TC::KC_ELEMS;
+  constexpr int IB = TC::IB, JB = TC::JB, NQ = TC::NQ, CPR = TS / 8;  // chunks per M/N-contiguous row
   __shared__ __attribute__((aligned(16))) bf16_t As[2][SZ];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][SZ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TC::WNW, wn = wave % TC::WNW;
   int e, m0, row_end, kb, ke;
-  const int n0 = blockIdx.x * MT;
+  const int n0 = blockIdx.x * TS;
   if (MODE == 0) {
     const int mt = blockIdx.y;
     if (mt >= tile_off[E]) return;
     e = find_expert(tile_off, E, mt);
-    m0 = offsets[e] + (mt - tile_off[e]) * MT;  // segment rows
+    m0 = offsets[e] + (mt - tile_off[e]) * TS;  // segment rows
     row_end = offsets[e + 1];
     kb = 0;
     ke = K;
   } else {
     e = blockIdx.z;
-    m0 = blockIdx.y * MT;                       // output rows (columns of A)
+    m0 = blockIdx.y * TS;                       // output rows (columns of A)
     row_end = M;
     kb = offsets[e];                            // k runs over the segment's rows
     ke = offsets[e + 1];
@@ -389,21 +403,21 @@ __global__ __launch_bounds__(256) void gemm_bwd_mfma_kernel(
   const bf16_t* Be1 = B1 + (size_t)e * sbe;
   const bf16_t* Be2 = B2 + (size_t)e * sbe;
 
-  u32x4 ra[4], rb[4];
+  u32x4 ra[NQ], rb[NQ];
   // global -> registers for the stage starting at k0 (zero outside the operands)
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + 256 * q;
+    for (int q = 0; q < NQ; ++q) {
+      const int c = tid + NT_ * q;
       if (MODE == 0) {
-        const int row = c >> 3, kc = (c & 7) * 8;   // 128 rows x 8 chunks
+        const int row = c >> 3, kc = (c & 7) * 8;   // TS rows x 8 chunks
         const int r = m0 + row;
         ra[q] = r < row_end ? *(const u32x4*)&A[(size_t)r * lda + k0 + kc] : u32x4{0u, 0u, 0u, 0u};
         const int n = n0 + row;
         const bf16_t* bp = k0 < K1 ? Be1 + (size_t)n * ldb + k0 + kc : Be2 + (size_t)n * ldb + (k0 - K1) + kc;
         rb[q] = n < N ? *(const u32x4*)bp : u32x4{0u, 0u, 0u, 0u};
       } else {
-        const int kr = c >> 4, cc = (c & 15) * 8;   // 64 k-rows x 16 chunks
+        const int kr = c / CPR, cc = (c % CPR) * 8;  // 64 k-rows x TS/8 chunks
         const int r = k0 + kr;
         const bool rv = r < ke;
         const int arow = rv ? (GATHER ? a_rows[r] : r) : 0;
@@ -414,21 +428,21 @@ __global__ __launch_bounds__(256) void gemm_bwd_mfma_kernel(
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + 256 * q;
+    for (int q = 0; q < NQ; ++q) {
+      const int c = tid + NT_ * q;
       int off;
       if (MODE == 0) off = (c >> 3) * LDK + (c & 7) * 8;
-      else off = (c >> 4) * LDM + (c & 15) * 8;
+      else off = (c / CPR) * TC::LDM + (c % CPR) * 8;
       *(u32x4*)&As[buf][off] = ra[q];
       *(u32x4*)&Bs[buf][off] = rb[q];
     }
   };
 
-  floatx16 acc[2][2];
+  floatx16 acc[IB][JB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -443,31 +457,32 @@ __global__ __launch_bounds__(256) void gemm_bwd_mfma_kernel(
     if (kt + 1 < nk) gload(kb + (kt + 1) * MKB);
 #pragma unroll
     for (int kh = 0; kh < MKB / 16; ++kh) {
-      bf16x8 fa[2], fb[2];
+      bf16x8 fa[IB], fb[JB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = frag<MC>(As[cur], wm * 64 + 32 * i, kh, lane);
+      for (int i = 0; i < IB; ++i) fa[i] = frag<MC, TC::LDM>(As[cur], wm * TC::WTM + 32 * i, kh, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = frag<MC>(Bs[cur], wn * 64 + 32 * j, kh, lane);
+      for (int j = 0; j < JB; ++j) fb[j] = frag<MC, TC::LDM>(Bs[cur], wn * TC::WTN + 32 * j, kh, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < JB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) lstore(cur ^ 1);
     __syncthreads();
   }
-  // lane holds, for acc element 4q + p of block (i, j): row wm*64 + 32i + 8q + 4*(lane >> 5) + p,
-  // column wn*64 + 32j + (lane & 31)
+  // lane holds, for acc element 4q + p of block (i, j): row wm*WTM + 32i + 8q + 4*(lane >> 5) + p,
+  // column wn*WTN + 32j + (lane & 31)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const int m = m0 + wm * 64 + 32 * i + 8 * q + 4 * (lane >> 5) + p;
-          const int n = n0 + wn * 64 + 32 * j + (lane & 31);
+          const int m = m0 + wm * TC::WTM + 32 * i + 8 * q + 4 * (lane >> 5) + p;
+          const int n = n0 + wn * TC::WTN + 32 * j + (lane & 31);
           if (m >= row_end || n >= N) continue;
           const float v = acc[i][j][4 * q + p];
           if (MODE == 1) {
@@ -554,16 +569,23 @@ hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const flo
 }
 
 hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st) {
-  if (a.a_bf16 && a.b_bf16 && a.tile_off128 != nullptr && a.K % MKB == 0 && a.K1 % MKB == 0 && a.lda % 8 == 0 &&
-      a.ldb % 8 == 0) {
-    const dim3 g((a.N + MT - 1) / MT, (a.R_max + MT - 1) / MT + a.E);
-#define MOE_NTM(EPI)                                                                                               \
-  hipLaunchKernelGGL((gemm_bwd_mfma_kernel<0, EPI, false>), g, dim3(256), 0, st, (const bf16_t*)a.A, a.lda, nullptr, \
-                     (const bf16_t*)a.B1, (const bf16_t*)a.B2, a.K1, a.sbe, a.ldb, a.K, 0, a.N, a.offsets,           \
-                     a.tile_off128, a.E, a.C, a.C, a.N, 0LL, a.ldc, a.pa, a.pg, a.ld_ag, (bf16_t*)a.DAG)
-    if (a.epi == ACT_SWIGLU) MOE_NTM(ACT_SWIGLU);
-    else if (a.epi == ACT_GELU) MOE_NTM(ACT_GELU);
-    else MOE_NTM(ACT_NONE);
+  if (a.a_bf16 && a.b_bf16 && a.tile_off_ts != nullptr && a.K % MKB == 0 && a.K1 % MKB == 0 && a.lda % 8 == 0 &&
+      a.ldb % 8 == 0 && (a.ts == 128 || a.ts == 256)) {
+#define MOE_NTM(EPI, TS)                                                                                           \
+  hipLaunchKernelGGL((gemm_bwd_mfma_kernel<0, EPI, false, TS>),                                                    \
+                     dim3((a.N + TS - 1) / TS, (a.R_max + TS - 1) / TS + a.E), dim3(BwdTile<TS>::NW * 64), 0, st,  \
+                     (const bf16_t*)a.A, a.lda, nullptr, (const bf16_t*)a.B1, (const bf16_t*)a.B2, a.K1, a.sbe,     \
+                     a.ldb, a.K, 0, a.N, a.offsets, a.tile_off_ts, a.E, a.C, a.C, a.N, 0LL, a.ldc, a.pa, a.pg,     \
+                     a.ld_ag, (bf16_t*)a.DAG)
+    if (a.ts == 256) {
+      if (a.epi == ACT_SWIGLU) MOE_NTM(ACT_SWIGLU, 256);
+      else if (a.epi == ACT_GELU) MOE_NTM(ACT_GELU, 256);
+      else MOE_NTM(ACT_NONE, 256);
+    } else {
+      if (a.epi == ACT_SWIGLU) MOE_NTM(ACT_SWIGLU, 128);
+      else if (a.epi == ACT_GELU) MOE_NTM(ACT_GELU, 128);
+      else MOE_NTM(ACT_NONE, 128);
+    }
 #undef MOE_NTM
     return hipGetLastError();
   }
@@ -606,15 +628,19 @@ hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
     return hipGetLastError();
   }
   if (a.a_bf16 && a.b_bf16 && a.M % 8 == 0 && a.N % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0) {
-    const dim3 g((a.N + MT - 1) / MT, (a.M + MT - 1) / MT, a.E);
-    if (a.a_rows)
-      hipLaunchKernelGGL((gemm_bwd_mfma_kernel<1, ACT_NONE, true>), g, dim3(256), 0, st, (const bf16_t*)a.A, a.lda,
-                         a.a_rows, (const bf16_t*)a.B, (const bf16_t*)a.B, 0, 0LL, a.ldb, 0, a.M, a.N, a.offsets,
-                         nullptr, a.E, a.C1, a.C2, a.N1, a.sce, a.ldc, nullptr, nullptr, 0, nullptr);
-    else
-      hipLaunchKernelGGL((gemm_bwd_mfma_kernel<1, ACT_NONE, false>), g, dim3(256), 0, st, (const bf16_t*)a.A, a.lda,
-                         nullptr, (const bf16_t*)a.B, (const bf16_t*)a.B, 0, 0LL, a.ldb, 0, a.M, a.N, a.offsets,
-                         nullptr, a.E, a.C1, a.C2, a.N1, a.sce, a.ldc, nullptr, nullptr, 0, nullptr);
+    // weight gradients: M and N are weight dimensions (large), so the 256 tile when both fill it
+    const bool big = a.M >= 256 && a.N >= 256;
+#define MOE_TNM(G, TS)                                                                                             \
+  hipLaunchKernelGGL((gemm_bwd_mfma_kernel<1, ACT_NONE, G, TS>), dim3((a.N + TS - 1) / TS, (a.M + TS - 1) / TS, a.E), \
+                     dim3(BwdTile<TS>::NW * 64), 0, st, (const bf16_t*)a.A, a.lda, a.a_rows, (const bf16_t*)a.B,     \
+                     (const bf16_t*)a.B, 0, 0LL, a.ldb, 0, a.M, a.N, a.offsets, nullptr, a.E, a.C1, a.C2, a.N1,     \
+                     a.sce, a.ldc, nullptr, nullptr, 0, nullptr)
+    if (big) {
+      if (a.a_rows) MOE_TNM(true, 256); else MOE_TNM(false, 256);
+    } else {
+      if (a.a_rows) MOE_TNM(true, 128); else MOE_TNM(false, 128);
+    }
+#undef MOE_TNM
     return hipGetLastError();
   }
   const dim3 grid((a.N + VT - 1) / VT, (a.M + VT - 1) / VT, a.E);

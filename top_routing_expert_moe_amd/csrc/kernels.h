@@ -132,7 +132,9 @@ struct BwdNT {
   const void* B1; const void* B2; int K1; long long sbe; int ldb; bool b_bf16;
   int K, N;
   const int* offsets; const int* tile_off; int E; int R_max;
-  const int* tile_off128;  // 128-row tile list of the same segments: bf16 operands run on MFMA
+  // bf16 operands run on MFMA with ts x ts tiles (128 or 256) over tile_off_ts, the ts-row
+  // tile list of the same segments
+  int ts; const int* tile_off_ts;
   float* C; int ldc;
   int epi; const float* pa; const float* pg; int ld_ag; void* DAG;
 };
