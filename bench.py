@@ -70,9 +70,14 @@ class Hip:
             self.l.hipEventDestroy(ev)
 
 
+# the sources the expert GEMM kernels (the dominant forward kernel) are compiled from
+GEMM_SOURCES = ("common.h", "gemm.hip", "kernels.h")
+
+
 def kernel_source_hash() -> str:
+    """sha256 prefix over the expert GEMM's sources: counters taken on other sources are stale."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.join(ROOT, "top_routing_expert_moe_amd", "csrc"))):
+    for name in GEMM_SOURCES:
         with open(os.path.join(ROOT, "top_routing_expert_moe_amd", "csrc", name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
