@@ -83,10 +83,9 @@ const char* moe_status_string(moe_status_t s);
  *   topk_idx [T,k] int32: slot j = j-th best expert; order (logit desc, expert asc)
  *   topk_w   [T,k] fp32: softmax of the selected logits (sums to 1 per token)
  *   prob_sum [E] fp32 or NULL: sum over tokens of the full softmax (for the aux loss)
- *   ws: at least moe_route_workspace_bytes(T,h,E,dt,flags,prob_sum != NULL) bytes: the
- *       split router weights and, for few tokens, partial logits (bf16 x), and per-block
- *       softmax sums (prob_sum); may be NULL when that is 0 (fp32 x or MOE_ROUTE_LOGITS_IN,
- *       without prob_sum). */
+ *   ws: at least moe_route_workspace_bytes(T,h,E,dt,flags,prob_sum != NULL) bytes: for
+ *       bf16 x the split router weights (from 32 experts up) and, for few tokens, partial
+ *       logits; per-block softmax sums (prob_sum); may be NULL when that is 0. */
 size_t moe_route_workspace_bytes(int32_t T, int32_t h, int32_t E, moe_dtype_t dt, uint32_t flags,
                                  int32_t with_prob_sum);  /* 0 for invalid sizes */
 moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bias,
@@ -225,8 +224,8 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
  * after each stage (combine adjoint with the counts and tile lists, router adjoint,
  * pre-activation recompute, down-projection data gradient with the activation's
  * derivative, down-projection weight gradient, up-projection data gradient, up-projection
- * weight gradients, router GEMMs, dx).  `events` holds MOE_BACKWARD_STAGES + 1 valid
- * hipEvent_t (MOE_ERR_ARG otherwise). */
+ * weight gradients, router GEMMs, dx).  `events` (not null: MOE_ERR_ARG) holds
+ * MOE_BACKWARD_STAGES + 1 entries, each a hipEvent_t or null (nothing recorded there). */
 #define MOE_BACKWARD_STAGES 9
 moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const void* W1, const void* W3,
                                       const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
@@ -264,7 +263,8 @@ moe_status_t moe_layer_forward_binned(const void* x, const float* W_gate, const 
 /* Measurement variant of moe_layer_forward_binned, as moe_layer_forward_timed: events[0]
  * before the router, then one after each stage (router logits, selection + histogram,
  * scan, scatter, bucket gather, expert up-projection, expert down-projection, combine).
- * `events` holds MOE_BINNED_STAGES + 1 valid hipEvent_t (MOE_ERR_ARG otherwise). */
+ * `events` (not null: MOE_ERR_ARG) holds MOE_BINNED_STAGES + 1 entries, each a hipEvent_t or
+ * null (nothing recorded there). */
 #define MOE_BINNED_STAGES 8
 moe_status_t moe_layer_forward_binned_timed(const void* x, const float* W_gate, const float* logit_bias,
                                             const void* W1, const void* W3, const void* W2,
@@ -278,7 +278,9 @@ moe_status_t moe_layer_forward_binned_timed(const void* x, const float* W_gate, 
  * caller-created HIP events recorded between the stages, so a profiler-free caller can
  * time each kernel: events[0] before the router, then one after each stage in order
  * (router logits, selection + histogram, scan, scatter, expert up-projection, expert
- * down-projection, combine).  `events` holds MOE_LAYER_STAGES + 1 valid hipEvent_t (MOE_ERR_ARG otherwise). */
+ * down-projection, combine).  `events` (not null: MOE_ERR_ARG) holds MOE_LAYER_STAGES + 1
+ * entries, each a hipEvent_t or null: nothing is recorded there, so a caller can time one
+ * kernel without the idle gaps that every event record adds between kernels. */
 #define MOE_LAYER_STAGES 7
 moe_status_t moe_layer_forward_timed(const void* x, const float* W_gate, const float* logit_bias,
                                      const void* W1, const void* W3, const void* W2,

@@ -94,10 +94,12 @@ def test_workspace_bytes(L):
     assert 128 * 14336 * 2 <= fb <= b
     assert L.moe_expert_ffn_workspace_bytes(8192, 4096, 14336, 8, 1, 1) >= 8192 * 14336 * 2
     assert L.moe_expert_ffn_workspace_bytes(-1, 64, 64, 8, 1, 1) == 0
-    # router: split weights (bf16 x) plus, for few tokens, partial logits; nothing for fp32 x
+    # router (bf16 x): the split weights from 32 experts up (fewer are split in registers)
+    # plus, for few tokens, partial logits; nothing for fp32 x
     rb = L.moe_route_workspace_bytes(64, 4096, 8, 1, 0, 0)
-    assert rb >= 6 * 16 * 4096 + 8 * 64 * 8 * 4
-    assert L.moe_route_workspace_bytes(4096, 4096, 8, 1, 0, 0) < rb + 2 ** 12
+    assert 8 * 64 * 8 * 4 <= rb <= 8 * 64 * 8 * 4 + 512
+    assert L.moe_route_workspace_bytes(4096, 4096, 8, 1, 0, 0) <= 256
+    assert L.moe_route_workspace_bytes(4096, 4096, 64, 1, 0, 0) >= 6 * 64 * 4096
     assert L.moe_route_workspace_bytes(64, 4096, 8, 0, 0, 0) <= 256
     assert L.moe_route_workspace_bytes(64, 4096, 8, 1, 1, 0) <= 256     # logits given
     assert L.moe_route_workspace_bytes(64, 4096, 300, 1, 0, 0) == 0
@@ -134,9 +136,9 @@ def test_layer_forward_host_errors(L, kw, expect):
 def test_layer_forward_timed_needs_events(L):
     a = [FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, 128, 256, 8, 2, 0.0, 1, 1, FAKE, None, None, FAKE, 1 << 40, None]
     assert L.moe_layer_forward_timed(*a, None) == ARG
-    ev = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [0]))
-    assert L.moe_layer_forward_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == ARG
-    ev = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    # null entries are allowed (nothing is recorded there): the call gets past the event
+    # check to the shape check
+    ev = (ctypes.c_void_p * 8)(*([0] * 4 + [FAKE, FAKE] + [0] * 2))
     a[7] = 96  # h not a multiple of 64: rejected before any event is recorded
     assert L.moe_layer_forward_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == UNSUP
     assert len(moe.LAYER_STAGES) == 7
@@ -278,8 +280,6 @@ def test_layer_forward_binned_timed_needs_events(L):
          1 << 40, None]
     assert L.moe_layer_forward_binned_timed(*a, None) == ARG
     ev = (ctypes.c_void_p * 9)(*([FAKE] * 8 + [0]))
-    assert L.moe_layer_forward_binned_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == ARG
-    ev = (ctypes.c_void_p * 9)(*([FAKE] * 9))
     a[12] = -1  # negative minimum capacity: rejected before any event is recorded
     assert L.moe_layer_forward_binned_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == ARG
     assert len(moe.BINNED_STAGES) == 8
@@ -370,8 +370,9 @@ def test_layer_backward_host_errors(L):
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, T, h, f, E, k, 0.0, 1, 1, FAKE, 0.0, FAKE, fwd, FAKE, None, FAKE, FAKE, FAKE,
          FAKE, bws, None]
     assert L.moe_layer_backward_timed(*a, None) == ARG
-    ev = (ctypes.c_void_p * 10)(*([FAKE] * 9 + [0]))
-    assert L.moe_layer_backward_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == ARG
+    ev = (ctypes.c_void_p * 10)(*([FAKE] * 9 + [0]))  # null entries: nothing recorded there
+    a[6] = 96  # h not a multiple of 64: rejected before any event is recorded
+    assert L.moe_layer_backward_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == UNSUP
     assert len(moe.BACKWARD_STAGES) == 9
 
 

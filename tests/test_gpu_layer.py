@@ -132,6 +132,18 @@ def test_layer_forward_timed_matches_untimed():
     hip.destroy(ev)
     assert all(s >= 0 for s in stages)
     assert abs(sum(stages) - total) <= 1e-3 * max(total, 1e-3) + 1e-3
+    # null entries record nothing: two events around the up-projection only
+    import ctypes
+    pair = hip.events(2)
+    j = moe.LAYER_STAGES.index("expert_up")
+    part = (ctypes.c_void_p * (len(moe.LAYER_STAGES) + 1))()
+    part[j], part[j + 1] = pair[0], pair[1]
+    y2, aux2, c2 = moe.layer_forward(*args, **kw, events=part)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.from_dev(y0), gu.from_dev(y2))
+    assert np.array_equal(gu.from_dev(c0), gu.from_dev(c2))
+    assert hip.elapsed_ms(pair[0], pair[1]) > 0
+    hip.destroy(pair)
 
 
 @pytest.mark.parametrize("layout,backward", [("compact", False), ("binned", False), ("compact", True)])

@@ -299,7 +299,7 @@ static moe_status_t route_impl(const void* x, const float* W_gate, const float* 
   if ((s = opts_ok(opts, x, lin)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   Carve c(ws);
-  const bool need_planes = !lin && dt == MOE_BF16;
+  const bool need_planes = !lin && dt == MOE_BF16 && route_scratch_bytes(T, h, E, true) > 0;
   RouteWs w = carve_route(c, T, h, E, prob_sum != nullptr, need_planes);
   void* xj = has_jitter(opts) ? c.take<char>((size_t)T * h * elem_bytes(dt)) : nullptr;
   if ((prob_sum || need_planes || has_jitter(opts)) && (!ws || ws_bytes < c.bytes())) return MOE_ERR_WORKSPACE;
@@ -467,7 +467,11 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   void* xj = has_jitter(opts) ? c.take<char>((size_t)T * h * elem_bytes(dt)) : nullptr;
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   int stage = 0;
-  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
+  // a null array or a null entry records nothing at that point
+  auto mark = [&]() -> bool {
+    const hipEvent_t e = ev == nullptr ? nullptr : ev[stage++];
+    return e == nullptr || hipEventRecord(e, stream) == hipSuccess;
+  };
   if (!mark()) return MOE_ERR_DEVICE;
 
   RouteArgs ra{};
@@ -585,7 +589,11 @@ static moe_status_t layer_forward_binned_impl(const void* x, const float* W_gate
   LayerWs& w = bw.l;
   void* xb = x_bins ? x_bins : bw.x_bins;
   int stage = 0;
-  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
+  // a null array or a null entry records nothing at that point
+  auto mark = [&]() -> bool {
+    const hipEvent_t e = ev == nullptr ? nullptr : ev[stage++];
+    return e == nullptr || hipEventRecord(e, stream) == hipSuccess;
+  };
   if (!mark()) return MOE_ERR_DEVICE;
 
   RouteArgs ra{};
@@ -657,8 +665,6 @@ moe_status_t moe_layer_forward_binned_timed(const void* x, const float* W_gate, 
                                             float* aux_loss, int32_t* counts, int32_t* capacity, void* x_bins,
                                             void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
   if (events == nullptr) return MOE_ERR_ARG;
-  for (int i = 0; i < MOE_BINNED_STAGES + 1; ++i)
-    if (events[i] == nullptr) return MOE_ERR_ARG;
   return layer_forward_binned_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, min_capacity,
                                    act, dt, y, aux_loss, counts, capacity, x_bins, ws, ws_bytes, stream, events);
 }
@@ -748,7 +754,11 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
   const int gact = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
   int stage = 0;
-  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[stage++], stream) == hipSuccess; };
+  // a null array or a null entry records nothing at that point
+  auto mark = [&]() -> bool {
+    const hipEvent_t e = ev == nullptr ? nullptr : ev[stage++];
+    return e == nullptr || hipEventRecord(e, stream) == hipSuccess;
+  };
   if (!mark()) return MOE_ERR_DEVICE;
 
   MOE_TRY(launch_counts(w.blk_counts, route_blocks(T), E, b.counts, stream));
@@ -957,8 +967,6 @@ moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const 
                                       float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
                                       hipStream_t stream, hipEvent_t* events) {
   if (events == nullptr) return MOE_ERR_ARG;
-  for (int i = 0; i < MOE_BACKWARD_STAGES + 1; ++i)
-    if (events[i] == nullptr) return MOE_ERR_ARG;
   return layer_backward_impl(x, W_gate, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, dy, d_aux, fwd_ws,
                              fwd_ws_bytes, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream, events);
 }
@@ -978,8 +986,6 @@ moe_status_t moe_layer_forward_timed(const void* x, const float* W_gate, const f
                                      moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, void* ws,
                                      size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
   if (events == nullptr) return MOE_ERR_ARG;
-  for (int i = 0; i < MOE_LAYER_STAGES + 1; ++i)
-    if (events[i] == nullptr) return MOE_ERR_ARG;
   return layer_forward_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, y,
                             aux_loss, counts, ws, ws_bytes, stream, events);
 }

@@ -112,6 +112,20 @@ template <> struct TileCfg<128> {
   static constexpr int WMW = kWaves == 8 ? 2 : 1, WNW = 4, NSTAGE = 3, NSW = 3, SPREAD = 8;
 };
 template <> struct TileCfg<32> { static constexpr int WMW = 1, WNW = 4, NSTAGE = 4, NSW = 4, SPREAD = 8; };
+// Weight-streaming launches (every m-tile at most 32 rows) use wide tiles: 512 weight
+// columns (SwiGLU: 256 of W1 and the same 256 of W3), so every k row of a weight stage is
+// a 512-byte run of each matrix instead of 256 bytes (measured on this chip: the decode
+// up projection's weights stream at 6.3 TB/s in 512-byte runs, 5.8 in 256-byte runs).
+// All eight waves compute (32 x 64 each); two 64 KiB weight stages, one workgroup per CU.
+// Without K parts (the up projection) the next stage's copies are all issued right after
+// the barrier (SPREAD 0) and tiles go to workgroups in launch order; with K parts (the
+// down projection) the copies are spread and the order is XCD-aware as above.  (Measured
+// at 16 rows per expert, h = 4096, f = 14336, E = 8: each choice is 2-4 % faster on the
+// GEMM it is used for than the other.)
+constexpr int BNW = 512;
+template <bool SPLIT> struct TileCfgWide32 {
+  static constexpr int WMW = 1, WNW = 8, NSTAGE = 2, NSW = 2, SPREAD = SPLIT ? 8 : 0;
+};
 
 // Swizzles (16-byte chunk index XOR a function of the row).  The LDS serves 256 bytes
 // (64 banks) per cycle, i.e. 32 lanes of an 8-byte read or 16 lanes of a 16-byte read:
@@ -137,49 +151,52 @@ __device__ __forceinline__ void copy_to_lds16(const void* gptr, uint32_t lds_blo
 
 constexpr int kSmemBytes = 160 * 1024;  // LDS of the largest tile shape
 
-// One tile of BMT rows (row0 .. row_end-1 of expert e) x 256 weight columns from n0, over
+// One tile of BMT rows (row0 .. row_end-1 of expert e) x BNT weight columns from n0, over
 // k in [ks * Kc, ks * Kc + Kc).  SPLIT: the raw fp32 accumulators go to K part ks of
 // `out` (row stride NW = 2N for SwiGLU, else N; parts R_max rows apart) and the
 // activation is applied when the parts are added.
-template <int BMT, int ACT, bool GATHER, typename OT, bool SPLIT>
+template <int BMT, int ACT, bool GATHER, typename OT, bool SPLIT, int BNT = BN, typename CFG = TileCfg<BMT>>
 __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__ A, const int* __restrict__ a_rows,
                                           const bf16_t* __restrict__ W, const bf16_t* __restrict__ W3, int K,
                                           int N, OT* __restrict__ out, int R_max, int e, int row0, int row_end,
                                           int n0, int ks, int Kc) {
   static_assert(!SPLIT || std::is_same<OT, float>::value, "K-split parts are fp32");
-  constexpr int NSTAGE = TileCfg<BMT>::NSTAGE, NSW = TileCfg<BMT>::NSW, SPREAD = TileCfg<BMT>::SPREAD;
+  constexpr int NSTAGE = CFG::NSTAGE, NSW = CFG::NSW, SPREAD = CFG::SPREAD;
   static_assert(NSW == NSTAGE || (NSW == 3 && NSTAGE == 2), "stage counts");
-  constexpr int WMW = TileCfg<BMT>::WMW, WNW = TileCfg<BMT>::WNW;  // waves along m / along n
+  constexpr int WMW = CFG::WMW, WNW = CFG::WNW;  // waves along m / along n
   constexpr int NCW = WMW * WNW;                                   // waves with MFMA work
   static_assert(NCW <= kWaves, "wave grid");
-  constexpr int WTM = BMT / WMW, WTN = BN / WNW;  // wave tile
+  constexpr int WTM = BMT / WMW, WTN = BNT / WNW;  // wave tile
+  constexpr int WSTT = KB * BNT;                   // weight stage elements: [64 k][BNT n]
+  constexpr int CPR = BNT / 8;                     // 16-byte chunks per weight stage row
+  constexpr int RPI = 64 / CPR;                    // weight rows per 1 KiB copy (2 or 1)
+  constexpr int NIWT = KB / RPI / kWaves;          // weight copies per wave and stage
   constexpr int IB = WTN / 32, JB = WTM / 32;     // 32 x 32 MFMA blocks per wave
   constexpr int XST = BMT * KB;                   // activation stage elements
   constexpr int XI = BMT / 8;                     // activation copies (1 KiB each) per stage
   constexpr int NIX = (XI + kWaves - 1) / kWaves; // ... per wave (waves past XI / NIX have none)
   static_assert(XI % NIX == 0, "activation copies");
-  constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;     // output columns per tile
-  static_assert((NSW * WST + NSTAGE * XST) * 2 <= kSmemBytes, "LDS");
-  bf16_t(*Ws)[WST] = reinterpret_cast<bf16_t(*)[WST]>(smem);
-  bf16_t(*Xs)[XST] = reinterpret_cast<bf16_t(*)[XST]>(smem + NSW * WST * 2);
+  static_assert((NSW * WSTT + NSTAGE * XST) * 2 <= kSmemBytes, "LDS");
+  bf16_t(*Ws)[WSTT] = reinterpret_cast<bf16_t(*)[WSTT]>(smem);
+  bf16_t(*Xs)[XST] = reinterpret_cast<bf16_t(*)[XST]>(smem + NSW * WSTT * 2);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const bool has_x = XI % kWaves == 0 || NIX * uwave < XI;  // this wave copies activations
 
   // ---- copy plan.  One wave instruction moves 1 KiB: lane l writes LDS bytes
-  // [16l, 16l+16) of the instruction's block, i.e. swizzle slot (l & 31) of weight
-  // row (l >> 5) or slot (l & 7) of activation row (l >> 3); it fetches the global
+  // [16l, 16l+16) of the instruction's block, i.e. swizzle slot (l % CPR) of weight
+  // row (l / CPR) or slot (l & 7) of activation row (l >> 3); it fetches the global
   // chunk that the swizzle puts there.  Columns past N / rows past the segment fetch
   // a valid neighbour instead (their results are never stored).
   // Weight columns: each wave's WTN LDS columns hold, for SwiGLU, WTN/2 columns of W1
   // followed by the same WTN/2 columns of W3.
-  const bf16_t* wsrc[NIW];
+  const bf16_t* wsrc[NIWT];
   uint32_t xsrc[NIX];
 #pragma unroll
-  for (int i = 0; i < NIW; ++i) {
-    const int r = 2 * (NIW * wave + i) + (lane >> 5);  // weight stage row (k)
-    const int c = (lane & 31) ^ wswz(r);               // 16-byte chunk of 8 columns
+  for (int i = 0; i < NIWT; ++i) {
+    const int r = RPI * (NIWT * wave + i) + lane / CPR;  // weight stage row (k)
+    const int c = (lane % CPR) ^ wswz(r);                // 16-byte chunk of 8 columns
     int col;
     const bf16_t* Wm;
     if (ACT == ACT_SWIGLU) {
@@ -205,22 +222,22 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   // The copies that belong to MFMA group `part` of `parts` (parts == 1: all of them):
   // activation copies of stage xkt into buffer xst (if xkt >= 0), then weight copies of
   // stage wkt into buffer wst (if wkt >= 0).  With equal stage counts, weight copy i and
-  // activation copy j go to groups i * sp / NIW and j * sp / NIX, sp = min(SPREAD, parts);
+  // activation copy j go to groups i * sp / NIWT and j * sp / NIX, sp = min(SPREAD, parts);
   // with a deeper weight pipeline the activation copies (needed first) take the first
   // sp/2 groups and the weight copies the next sp.
   // (ALL: both stages are known to exist, no checks)
   auto issue_part = [&](int xkt, int xst, int wkt, int wst, int part, int parts, bool all = false) {
-    const int sp = parts < SPREAD ? parts : SPREAD;
+    const int sp = parts < SPREAD ? parts : (SPREAD > 0 ? SPREAD : 1);
     const bool split = NSW != NSTAGE && parts > 1;
 #pragma unroll
     for (int i = 0; i < NIX; ++i)
       if ((all || xkt >= 0) && has_x && (split ? i * (sp / 2) / NIX : i * sp / NIX) == part)
         copy_to_lds16(A + xsrc[i] + xkt * KB, xs_lds + 2u * (uint32_t)(xst * XST + 8 * (NIX * uwave + i) * KB));
 #pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      if ((all || wkt >= 0) && (split ? sp / 2 + i * sp / NIW : i * sp / NIW) == part)
+    for (int i = 0; i < NIWT; ++i)
+      if ((all || wkt >= 0) && (split ? sp / 2 + i * sp / NIWT : i * sp / NIWT) == part)
         copy_to_lds16(wsrc[i] + (size_t)wkt * KB * N,
-                      ws_lds + 2u * (uint32_t)(wst * WST + (2 * (NIW * uwave + i)) * BN));
+                      ws_lds + 2u * (uint32_t)(wst * WSTT + RPI * (NIWT * uwave + i) * BNT));
   };
 
   // ---- fragment addressing (v_mfma_f32_32x32x16_bf16).  Wave (wn, wm) owns weight
@@ -243,7 +260,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 #pragma unroll
       for (int ib = 0; ib < IB; ++ib) {
         const int col = wn * WTN + ib * 32 + 16 * (g & 1) + 4 * (s & 3);
-        aoff[kh][h][ib] = r * BN + ((((col >> 3) ^ wswz(r))) << 3) + (col & 7);
+        aoff[kh][h][ib] = r * BNT + ((((col >> 3) ^ wswz(r))) << 3) + (col & 7);
       }
     }
   const int xrow = wm * WTM + l31;
@@ -267,6 +284,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     const bf16_t* Xb = Xs[xbuf];
     constexpr int PARTS = (KB / 16) * IB;
     const bool mf = NCW == kWaves || uwave < NCW;  // waves past the grid only copy
+    if (SPREAD == 0) issue_part(xkt, xnb, wkt, wnb, 0, 1, all);  // all copies before the first LDS read
 #pragma unroll
     for (int kh = 0; kh < KB / 16; ++kh) {
       bf16x8 a[IB], b[JB];
@@ -287,7 +305,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
           for (int jb = 0; jb < JB; ++jb)
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
         }
-        issue_part(xkt, xnb, wkt, wnb, kh * IB + ib, PARTS, all);
+        if (SPREAD > 0) issue_part(xkt, xnb, wkt, wnb, kh * IB + ib, PARTS, all);
       }
     }
   };
@@ -310,16 +328,16 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     for (int j = 0; j < U; ++j) {
       if (NSW == NSTAGE) {
         if (NSTAGE >= 4) {
-          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIW + NIX)) : "memory");
-          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIW) : "memory");
+          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIWT + NIX)) : "memory");
+          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIWT) : "memory");
         } else if (NSTAGE == 3) {
-          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW + NIX) : "memory");
-          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT + NIX) : "memory");
+          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
       } else {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
       }
       __syncthreads();
       compute(j % NSTAGE, j % NSW, kt + j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE, kt + j + NSW - 1,
@@ -329,21 +347,21 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   // the remaining stages (the pipeline drains)
   for (; kt < nk; ++kt) {
     if (NSW == NSTAGE) {
-      // stages newer than kt already issued, NIW (+ NIX) copies each
+      // stages newer than kt already issued, NIWT (+ NIX) copies each
       const int ahead = min(nk - 1 - kt, NSTAGE - 2);
       if (has_x) {
-        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIW + NIX)) : "memory");
-        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW + NIX) : "memory");
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIWT + NIX)) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT + NIX) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       } else {
-        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIW) : "memory");
-        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIWT) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
     } else {
       // the newest copies are the weights of stage kt + 1 (issued after the activations
       // of stage kt during step kt - 1, or in the prologue)
-      if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+      if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
@@ -454,6 +472,43 @@ gemm_bf16_kernel(
     gemm_tile<32, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc);
 }
 
+// The same grouped GEMM when every m-tile has at most 32 rows (fh = 32): wide tiles.
+template <int ACT, bool GATHER, typename OT, bool SPLIT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void
+gemm_bf16_wide_kernel(
+    const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
+    const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
+    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh) {
+  using CFG = TileCfgWide32<SPLIT>;
+  constexpr int LDS = (CFG::NSW * KB * BNW + CFG::NSTAGE * 32 * KB) * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  constexpr int NO = ACT == ACT_SWIGLU ? BNW / 2 : BNW;  // output columns per tile
+  const int MT = tile_off[E];
+  const int n_tiles = MT * NT;
+  const int n_real = n_tiles * (SPLIT ? S : 1);
+  int L = blockIdx.x;
+  if (SPLIT) {
+    const int per = (n_real + 7) >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    if (slot >= per) return;
+    L = xcd * per + slot;
+  }
+  if (L >= n_real) return;
+  int e, mt_local, nt;
+  int ks = 0;
+  int Lt = L;
+  if (SPLIT) {
+    ks = L / n_tiles;
+    Lt = L - ks * n_tiles;
+  }
+  tile_of(Lt, tile_off, E, NT, e, mt_local, nt);
+  const int Kc = SPLIT ? K / S : K;
+  const int row0 = offsets[e] + mt_local * fh;
+  const int rows = min(fh, offsets[e + 1] - row0);
+  gemm_tile<32, ACT, GATHER, OT, SPLIT, BNW, CFG>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows,
+                                                  nt * NO, ks, Kc);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 grouped GEMM on the vector ALUs (fp32 workloads: exact fp32 products,
 // fp32 accumulation).  Tile 64 rows x 64 columns x 16 k, 4x4 per thread.
@@ -542,15 +597,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
 
 template <int ACT, bool G, typename OT, bool SPLIT>
 hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
-  constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;
+  const bool wide = a.bm == 32;
+  const int NO = ACT == ACT_SWIGLU ? (wide ? BNW : BN) / 2 : (wide ? BNW : BN);
   const int NT = (a.N + NO - 1) / NO;
   const int S = SPLIT ? std::max(a.ksplit, 1) : 1;
   const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
-                     (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                     (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm);
+  if (wide)
+    hipLaunchKernelGGL((gemm_bf16_wide_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
+                       (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
+                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
+                       (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
+                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm);
   return hipGetLastError();
 }
 
@@ -646,21 +707,20 @@ FfnPlan plan_ffn(bool bf16, double rows_per_expert, int E, int R_max, int h, int
   constexpr double kCUs = 256.0;
   const double mt_max = ceil((double)R_max / p.bm) + E;
   if (p.bm == 32) {
-    // Few rows per expert: the GEMMs stream weights.  When there are fewer tiles than two
-    // per CU (one 256-column tile per expert and column block: the down projection at
-    // decode shapes), split K until there are about two per CU.  (Measured at T = 64,
-    // h = 4096, f = 14336, E = 8: the down projection gains ~12 % with 4 parts; more
-    // parts, or splitting the up projection's 896 tiles, only add partial-sum traffic.)
+    // Few rows per expert: the GEMMs stream weights, in wide tiles with one workgroup per
+    // CU.  When there are fewer tiles than CUs (one 512-column tile per expert and column
+    // block: the down projection at decode shapes), split K until there is about one per
+    // CU; the fp32 parts are added by the combine.
     const double mt = std::min((double)E * ceil(rows_per_expert / p.bm), mt_max);  // expected m-tiles
     auto split = [&](int K, int N, int no) {
       const double tiles = mt * ceil((double)N / no);
       int S = 1;
-      if (tiles >= 2 * kCUs) return S;
-      while (S < 16 && tiles * S < 2 * kCUs && K % (2 * S * KB) == 0 && K / (2 * S) >= 8 * KB) S *= 2;
+      if (tiles >= kCUs) return S;
+      while (S < 16 && tiles * S < kCUs && K % (2 * S * KB) == 0 && K / (2 * S) >= 8 * KB) S *= 2;
       return S;
     };
-    p.s_up = split(h, f, BN / 2);
-    p.s_down = split(f, h, BN);
+    p.s_up = split(h, f, BNW / 2);
+    p.s_down = split(f, h, BNW);
     return p;
   }
   // Larger tiles: the last round of tiles may leave many CUs idle (the down projection

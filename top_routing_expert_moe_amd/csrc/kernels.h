@@ -22,8 +22,9 @@ struct RouteArgs {
   float* topk_w;          // [T,k]
   float* prob_part;       // [route_blocks(T), E] or null
   int* blk_counts;        // [route_blocks(T), E] or null: per-block expert histogram
-  uint16_t* planes;       // bf16 x: route_scratch_bytes of scratch -- [3][E16][h] bf16 split router
-                          // weights, then (few tokens) [SH][T][E] fp32 partial logits
+  uint16_t* planes;       // bf16 x: route_scratch_bytes of scratch -- from 32 experts up [3][E16][h]
+                          // bf16 split router weights, then (few tokens) [SH][T][E] fp32 partial
+                          // logits
   // router variants (selection kernel): gate noise [T,E] added to the logits, softmax of
   // logits * inv_temp, ids replaced by (t*k + j) % E
   const float* noise = nullptr;

@@ -13,9 +13,11 @@
 //    hi + mid + lo (each the bf16 rounding of what the previous ones left, 24
 //    significant bits in total), a bf16 x times a bf16 plane is exact in fp32,
 //    and v_mfma_f32_16x16x32_bf16 accumulates the three products in fp32.  Each
-//    wave streams 16 token rows straight from HBM into MFMA operands (no LDS);
-//    the planes ([3][E16][h], k-contiguous) are small and stay in L2.  For fp32
-//    activations a plain fp32 FMA kernel is used instead.
+//    wave streams 16 token rows straight from HBM into MFMA operands (no LDS).
+//    Up to 16 experts each wave splits the fp32 weights it loads in registers;
+//    from 32 experts up (where that split would cost as much as the MFMAs) a
+//    first kernel writes the planes ([3][E16][h], k-contiguous; small, they stay
+//    in L2).  For fp32 activations a plain fp32 FMA kernel is used instead.
 //  * select.  A group of lanes per token (a whole wave from 64 experts up): lane
 //    e holds the logits of experts e, e+64, ...; softmax sums and k rounds of a
 //    64-bit group arg-max pick the experts.
@@ -42,6 +44,15 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
 
 __device__ __forceinline__ float bf16_round(float v) { return __uint_as_float(f32_to_bf16_bits(v) << 16); }
 
+// w == hi + mid + lo exactly (fp32 w: 24 significant bits, 8 per bf16 part), each part
+// the bf16 rounding of what the previous parts leave
+__device__ __forceinline__ void split3(float w, float& hi, float& mid, float& lo) {
+  hi = bf16_round(w);
+  const float r1 = w - hi;  // exact
+  mid = bf16_round(r1);
+  lo = bf16_round(r1 - mid);
+}
+
 // ---------------------------------------------------------------------------
 // W_gate [h,E] fp32 -> planes [3][E16][h] bf16 with hi + mid + lo == W (to fp32 precision)
 __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W_gate, int h, int E, int E16,
@@ -50,10 +61,8 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
   if (idx >= (int64_t)E16 * h) return;
   const int e = (int)(idx / h), i = (int)(idx % h);
   const float w = e < E ? W_gate[(size_t)i * E + e] : 0.f;
-  const float hi = bf16_round(w);
-  const float r1 = w - hi;  // exact
-  const float mid = bf16_round(r1);
-  const float lo = bf16_round(r1 - mid);
+  float hi, mid, lo;
+  split3(w, hi, mid, lo);
   const size_t plane = (size_t)E16 * h;
   planes[idx] = (bf16_t)(__float_as_uint(hi) >> 16);
   planes[plane + idx] = (bf16_t)(__float_as_uint(mid) >> 16);
@@ -69,9 +78,13 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
 // weights are read once per 64 tokens instead of once per 16.
 // With gridDim.z = SH > 1 (few tokens), workgroup z covers h / SH of the contraction and
 // writes partial sums to logits + z * T * E (the selection kernel adds them).
-template <int NB, int TW, int NW, int TG = 1>
+// WF32: the weights come as W_gate itself ([h][E] fp32) and each lane splits the eight
+// k-values of its expert column that it loads (exactly what the split kernel writes);
+// otherwise they come as the bf16 planes.
+template <int NB, int TW, int NW, int TG = 1, bool WF32 = false>
 __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ planes,
+                                                          const float* __restrict__ W_gate,
                                                           const float* __restrict__ bias, int T, int h, int E,
                                                           int E16, float* __restrict__ logits) {
   constexpr int KS = NW / TW;
@@ -100,8 +113,13 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
   }
   const size_t plane = (size_t)E16 * h;
   const bf16_t* wrow[NB];
+  const float* wcol[NB];  // WF32: W_gate[8 * (lane >> 4)][e], or null past E
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wrow[nb] = planes + (size_t)(e0 + nb * 16 + (lane & 15)) * h + 8 * (lane >> 4);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int e = e0 + nb * 16 + (lane & 15);
+    if (WF32) wcol[nb] = e < E ? W_gate + (size_t)(8 * (lane >> 4)) * E + e : nullptr;
+    else wrow[nb] = planes + (size_t)e * h + 8 * (lane >> 4);
+  }
 
   floatx4 acc[TG][NB];
 #pragma unroll
@@ -120,9 +138,29 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg) xb[u][tg] = tvalid[tg] ? *(const bf16x8*)(xrow[tg] + kk) : bf16x8{};
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb) {
+          if (WF32) {
+            float wv[8];
 #pragma unroll
-          for (int p = 0; p < 3; ++p) wa[u][nb][p] = *(const bf16x8*)(wrow[nb] + p * plane + kk);
+            for (int j = 0; j < 8; ++j) wv[j] = wcol[nb] ? wcol[nb][(size_t)(kk + j) * E] : 0.f;
+            uint32_t pk[3][4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+              float p0[3], p1[3];
+              split3(wv[j], p0[0], p0[1], p0[2]);
+              split3(wv[j + 1], p1[0], p1[1], p1[2]);
+#pragma unroll
+              for (int p = 0; p < 3; ++p)
+                pk[p][j / 2] = (__float_as_uint(p0[p]) >> 16) | (__float_as_uint(p1[p]) & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              wa[u][nb][p] = __builtin_bit_cast(bf16x8, u32x4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]});
+          } else {
+#pragma unroll
+            for (int p = 0; p < 3; ++p) wa[u][nb][p] = *(const bf16x8*)(wrow[nb] + p * plane + kk);
+          }
+        }
       }
     }
 #pragma unroll
@@ -383,13 +421,24 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
 template <int NB, int TW, int NW = 4, int TG = 1>
 void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr) {
   const dim3 grid((a.T + 16 * TW * TG - 1) / (16 * TW * TG), E16 / (16 * NB), SH);
-  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
-                     (const bf16_t*)a.planes, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits);
+  if constexpr (NB == 1) {
+    if (E16 <= 16) {  // weights split in registers
+      hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true>), grid, dim3(NW * 64), 0, st,
+                         (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
+                     (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits);
 }
 
 }  // namespace
 
-int route_planes_elems(int h, int E) { return 3 * ((E + 15) / 16 * 16) * h; }
+// the bf16 planes of the router weights (from 32 experts up; fewer are split in registers)
+int route_planes_elems(int h, int E) {
+  const int E16 = (E + 15) / 16 * 16;
+  return E16 > 16 ? 3 * E16 * h : 0;
+}
 
 int route_hsplit(int T, int h, int E, bool bf16) {
   // few tokens: too few workgroups to stream the router weights and x at full rate, so the
@@ -422,8 +471,9 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
     if (a.bf16) {
       const int E16 = (a.E + 15) / 16 * 16;
       const int64_t n = (int64_t)E16 * a.h;
-      hipLaunchKernelGGL(wsplit_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.W_gate, a.h, a.E,
-                         E16, (bf16_t*)a.planes);
+      if (E16 > 16)
+        hipLaunchKernelGGL(wsplit_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.W_gate, a.h, a.E,
+                           E16, (bf16_t*)a.planes);
       // k split across waves needs h/KS to be a multiple of 32
       const int SH = route_hsplit(a.T, a.h, a.E, true);
       if (SH > 1) {
