@@ -689,14 +689,32 @@ struct BwdWs {
   void* dO;
   float* ag;
   void* dag;
-  float* dXp;
+  float* dXp;      // [dx_parts][R_max][h]: K parts of the up projection's data gradient
   float* dx_r;
   float* wg_part;  // partial sums of dW_gate over token slices
+  void* xp;        // bf16: the gathered rows of x for the up projection's weight gradients
 };
 // token slices of dW_gate = x^T dl: about 512 tokens each, at most 64
 static int wgate_splits(int32_t T) { return std::max(1, std::min(64, (T + 511) / 512)); }
+// K parts of the up projection's data gradient (bf16, 256-row tiles): two when that fills
+// the last round of tiles on the 256 CUs markedly better (expected m-tiles: half a tile of
+// padding per expert on top of the rows)
+static int dx_parts(bool bf, const FfnPlan& pl, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int64_t C,
+                    int n_up) {
+  if (!bf || pl.bm != 256) return 1;
+  double rpe = (double)T * k / E;
+  if (C != INT32_MAX && (double)C < rpe) rpe = (double)C;
+  const double tiles = E * (rpe / 256.0 + 0.5) * ceil(h / 256.0);
+  auto fill = [](double t) {
+    const double r = t / 256.0;
+    return r / ceil(r);
+  };
+  const int K = n_up * f;
+  if (K % (2 * 64) == 0 && K / 2 >= 16 * 64 && fill(2 * tiles) > fill(tiles) + 0.08) return 2;
+  return 1;
+}
 static BwdWs carve_bwd(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, int R_max, moe_dtype_t dt,
-                       moe_act_t act) {
+                       moe_act_t act, int parts) {
   const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
   const size_t es = elem_bytes(dt);
   BwdWs b;
@@ -709,10 +727,11 @@ static BwdWs carve_bwd(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int
   b.dO = c.take<char>((size_t)R_max * h * es);
   b.ag = c.take<float>((size_t)R_max * n_up * f);
   b.dag = c.take<char>((size_t)R_max * n_up * f * es);
-  b.dXp = c.take<float>((size_t)R_max * h);
+  b.dXp = c.take<float>((size_t)parts * R_max * h);
   b.dx_r = c.take<float>((size_t)T * h);
   const int S = wgate_splits(T);
   b.wg_part = S > 1 ? c.take<float>((size_t)S * h * E) : nullptr;
+  b.xp = dt == MOE_BF16 ? c.take<char>((size_t)R_max * h * es) : nullptr;
   return b;
 }
 
@@ -720,9 +739,12 @@ size_t moe_layer_backward_workspace_bytes(int32_t T, int32_t h, int32_t f, int32
                                           float capacity_factor, moe_dtype_t dt, moe_act_t act) {
   if (common_sizes(T, E, k) != MOE_OK || !dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor)) return 0;
   if (dim_ok(h) != MOE_OK || dim_ok(f) != MOE_OK) return 0;
-  const int R_max = rows_max(T, E, k, capacity_of(T, E, k, capacity_factor));
+  const int64_t C = capacity_of(T, E, k, capacity_factor);
+  const int R_max = rows_max(T, E, k, C);
+  const bool bf = dt == MOE_BF16;
+  const int parts = dx_parts(bf, layer_plan(bf, T, h, f, E, k, C), T, h, f, E, k, C, act == MOE_ACT_SWIGLU ? 2 : 1);
   Carve c(nullptr);
-  carve_bwd(c, T, h, f, E, k, R_max, dt, act);
+  carve_bwd(c, T, h, f, E, k, R_max, dt, act, parts);
   return c.bytes();
 }
 
@@ -749,7 +771,8 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   LayerWs w = carve_layer(cf, T, h, f, E, k, R_max, pl, dt, act);
   if (!fwd_ws || fwd_ws_bytes < cf.bytes()) return MOE_ERR_WORKSPACE;
   Carve c(ws);
-  BwdWs b = carve_bwd(c, T, h, f, E, k, R_max, dt, act);
+  const int parts = dx_parts(bf, pl, T, h, f, E, k, C, act == MOE_ACT_SWIGLU ? 2 : 1);
+  BwdWs b = carve_bwd(c, T, h, f, E, k, R_max, dt, act, parts);
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
   const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
   const int gact = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
@@ -880,13 +903,20 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   nt.C = b.dXp;
   nt.ldc = h;
   nt.epi = ACT_NONE;
+  nt.ksplit = parts;
   MOE_TRY(launch_gemm_nt(nt, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  // dW1[e] = X^T da, dW3[e] = X^T dg (X rows gathered from x)
+  // dW1[e] = X^T da, dW3[e] = X^T dg (X rows gathered from x; bf16: into xp first, so
+  // that the product reads whole rows)
   tn = BwdTN{};
   tn.A = x;
   tn.lda = h;
   tn.a_rows = w.perm_token;
+  if (bf) {
+    MOE_TRY(launch_gather_rows(x, w.perm_token, w.offsets, E, R_max, h * 2, b.xp, stream));
+    tn.A = b.xp;
+    tn.a_rows = nullptr;
+  }
   tn.a_bf16 = bf;
   tn.B = b.dag;
   tn.ldb = n_up * f;
@@ -946,7 +976,7 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
     MOE_TRY(launch_gemm_tn(tn, stream));
   }
   if (!mark()) return MOE_ERR_DEVICE;
-  MOE_TRY(launch_dx_final(b.dx_r, b.dXp, w.slot_pos, T, h, k, bf, dx, stream));
+  MOE_TRY(launch_dx_final(b.dx_r, b.dXp, parts, (size_t)R_max * h, w.slot_pos, T, h, k, bf, dx, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
 }

@@ -502,10 +502,364 @@ gemm_bwd_mfma_kernel(const bf16_t* __restrict__ A, int lda, const int* __restric
         }
 }
 
-// dx[t] = dx_router[t] + sum over kept slots j (ascending) of dXp[slot of (t, j)]
+// ---------------------------------------------------------------------------
+// The large products (both tile extents 256, bf16 operands) with the expert GEMM's
+// pipeline: operands go from global memory straight into LDS (global_load_lds_dwordx4,
+// no register staging), the P operand three stages ahead and the Q operand two, and
+// each wave waits only for its own copies of the stage it is about to read.
+// P is the MFMA row operand: a lane's accumulators hold four consecutive P indices
+// (8q + 4(lane >> 5) + 0..3 of a 32-block), stored as one vector; Q is the column
+// operand (index lane & 31).
+//  * NT (data gradients): C[r, n] = sum_k A[r, k] B(e, n, k); P = n (rows of B), Q = r
+//    (rows of A).  Both are staged [256 rows][64 k], k contiguous, 16-byte chunks XOR-ed
+//    by kswz(row); a fragment (8 consecutive k of one row) is one 16-byte read.
+//  * TN (weight gradients): C_e[m, n] = sum_{r in segment e} A[r, m] B[r, n]; P = n,
+//    Q = m.  Both are staged [64 r][256 columns], chunks XOR-ed by cswz(r); a fragment is
+//    two transposing 8-byte reads.  A segment's last stage is partial: the copies read a
+//    valid row in place of the missing ones and the fragments' k-values past the segment
+//    are set to zero before the MFMAs.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+namespace bt {
+constexpr int TS = 256, KB = 64, WAVES = 8;
+constexpr int WQ = 4, WP = 2;                // waves along Q / along P
+constexpr int WTQ = TS / WQ, WTP = TS / WP;  // wave tile: 64 (Q) x 128 (P)
+constexpr int IB = WTP / 32, JB = WTQ / 32;  // 32 x 32 blocks per wave
+constexpr int NSP = 3, NSQ = 2;              // LDS stages of P and Q
+constexpr int ST = TS * KB;                  // elements per stage of either operand
+constexpr int NI = 32 / WAVES;               // 1 KiB copies per wave, operand and stage
+constexpr int BLK = 512;                     // elements per 1 KiB copy
+constexpr int GM = 4, GN = 8;                // tile groups, as in the forward GEMM
+}  // namespace bt
+
+__device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int cswz(int r) { return ((r & 3) << 1) ^ ((r & 3) << 2); }
+
+// one 16-byte-per-lane copy from global memory into the wave's 1 KiB LDS block at the
+// byte address in m0 (no destination registers: nothing stays in flight in a register)
+__device__ __forceinline__ void bt_copy16(const void* gptr, uint32_t lds_block) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_block) : "memory", "m0");
+}
+
+// tile l of an expert's me x NT tiles, in groups of GM m-tiles x GN n-tiles (m fastest)
+__device__ __forceinline__ void bt_group(int l, int me, int NT, int& mt, int& nt) {
+  const int mg = l / (bt::GM * NT);
+  const int gm = min(bt::GM, me - mg * bt::GM);
+  const int r = l - mg * bt::GM * NT;
+  const int ng = r / (gm * bt::GN);
+  const int r2 = r - ng * gm * bt::GN;
+  mt = mg * bt::GM + r2 % gm;
+  nt = ng * bt::GN + r2 / gm;
+}
+
+// zero the k-values k0 + t (t = 0..7) of a fragment that lie at or past `valid`
+__device__ __forceinline__ bf16x8 bt_mask(bf16x8 v, int k0, int valid) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 s = __builtin_bit_cast(s16x8, v);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    if (k0 + t >= valid) s[t] = 0;
+  return __builtin_bit_cast(bf16x8, s);
+}
+
+// MODE 0 = NT over the 256-row tiles of the segments (tile_off: their list), in S K parts
+// (part s of C at C1 + s * R_max * ldc); MODE 1 = TN over each segment's rows.
+template <int MODE, int EPI, bool SPLIT>
+__global__ __launch_bounds__(bt::WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B1,
+                const bf16_t* __restrict__ B2, int K1, long long sbe, int ldb, int K, int M, int N,
+                const int* __restrict__ offsets, const int* __restrict__ tile_off, int E, int NT, int MT, int S,
+                int R_max, float* __restrict__ C1, float* __restrict__ C2, int N1, long long sce, int ldc,
+                const float* __restrict__ pa, const float* __restrict__ pg, int ld_ag, bf16_t* __restrict__ DAG) {
+  using namespace bt;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[(NSP + NSQ) * ST];
+  bf16_t(*Ps)[ST] = reinterpret_cast<bf16_t(*)[ST]>(smem);
+  bf16_t(*Qs)[ST] = reinterpret_cast<bf16_t(*)[ST]>(smem + NSP * ST);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+
+  // ---- tile.  NT tiles all do the same work: each XCD takes a contiguous range of the
+  // tile list, so tiles that share operands share its L2.  TN tiles do work in proportion
+  // to their expert's rows, so they are dealt round-robin over the XCDs (launch order),
+  // which spreads every expert over the whole chip.
+  int e, p0, q0, kb, ke, row_end = 0, ks = 0;
+  {
+    const int n_tiles = MODE == 0 ? tile_off[E] * NT : E * MT * NT;
+    const int n_real = n_tiles * (SPLIT ? S : 1);
+    int L = blockIdx.x;
+    if (MODE == 0) {
+      const int per = (n_real + 7) >> 3;
+      const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+      if (slot >= per) return;
+      L = xcd * per + slot;
+    }
+    if (L >= n_real) return;
+    if (SPLIT) {
+      ks = L / n_tiles;
+      L -= ks * n_tiles;
+    }
+    int mt, nt;
+    if (MODE == 0) {
+      int lo = 0, hi = E;  // expert: tile_off[e] * NT <= L < tile_off[e + 1] * NT
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_off[mid] * NT <= L) lo = mid; else hi = mid;
+      }
+      e = lo;
+      bt_group(L - tile_off[e] * NT, tile_off[e + 1] - tile_off[e], NT, mt, nt);
+      q0 = offsets[e] + mt * TS;
+      row_end = offsets[e + 1];
+      const int Kc = SPLIT ? K / S : K;
+      kb = ks * Kc;
+      ke = kb + Kc;
+    } else {
+      e = L / (MT * NT);
+      bt_group(L - e * MT * NT, MT, NT, mt, nt);
+      q0 = mt * TS;
+      kb = offsets[e];
+      ke = offsets[e + 1];
+    }
+    p0 = nt * TS;
+  }
+  const int nk = (ke - kb + KB - 1) / KB;
+
+  // ---- copy plan: copy i of wave w fills 1 KiB block NI * w + i of a stage
+  const bf16_t* pb1[NI];
+  const bf16_t* pb2[NI];
+  const bf16_t* qa[NI];
+  int rl[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (MODE == 0) {
+      const int r = 8 * (NI * wave + i) + (lane >> 3);  // stage row
+      const int ch = ((lane & 7) ^ kswz(r)) << 3;
+      const size_t n = (size_t)min(p0 + r, N - 1);
+      pb1[i] = B1 + (size_t)e * sbe + n * ldb + ch;
+      pb2[i] = B2 + (size_t)e * sbe + n * ldb + ch;
+      qa[i] = A + (size_t)min(q0 + r, row_end - 1) * lda + ch;
+    } else {
+      rl[i] = 2 * (NI * wave + i) + (lane >> 5);  // stage row (k)
+      const int ch = ((lane & 31) ^ cswz(rl[i])) << 3;
+      pb1[i] = B1 + min(p0 + ch, N - 8);
+      qa[i] = A + min(q0 + ch, M - 8);
+    }
+  }
+  const uint32_t ps_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Ps[0][0];
+  const uint32_t qs_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Qs[0][0];
+  auto copy_q = [&](int i, int kt, int buf) {
+    const bf16_t* src;
+    if (MODE == 0) src = qa[i] + kb + kt * KB;
+    else src = qa[i] + (size_t)min(kb + kt * KB + rl[i], ke - 1) * lda;
+    bt_copy16(src, qs_lds + 2u * (uint32_t)(buf * ST + BLK * (NI * uwave + i)));
+  };
+  auto copy_p = [&](int i, int kt, int buf) {
+    const bf16_t* src;
+    if (MODE == 0) {
+      const int k0 = kb + kt * KB;
+      src = k0 < K1 ? pb1[i] + k0 : pb2[i] + (k0 - K1);
+    } else {
+      src = pb1[i] + (size_t)min(kb + kt * KB + rl[i], ke - 1) * ldb;
+    }
+    bt_copy16(src, ps_lds + 2u * (uint32_t)(buf * ST + BLK * (NI * uwave + i)));
+  };
+  // copies of MFMA group `part` of `parts`: the Q copies of stage qkt take the first
+  // four groups, the P copies of stage pkt every other group after them (parts == 1:
+  // all at once); ALL: both stages are known to exist
+  auto issue_part = [&](int qkt, int qnb, int pkt, int pnb, int part, int parts, bool all = false) {
+    const int sp = parts < 8 ? parts : 8;
+    const bool split = parts > 1;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if ((all || qkt >= 0) && (split ? i * (sp / 2) / NI : 0) == part) copy_q(i, qkt, qnb);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if ((all || pkt >= 0) && (split ? sp / 2 + i * sp / NI : 0) == part) copy_p(i, pkt, pnb);
+  };
+
+  // ---- fragment offsets (elements within a stage) for 16-k step kh and half h
+  const int wn = wave % WP, wm = wave / WP;
+  const int g = lane >> 4, s = lane & 15, l31 = lane & 31, hf = lane >> 5;
+  int poff[KB / 16][2][IB], qoff[KB / 16][2][JB];
+#pragma unroll
+  for (int kh = 0; kh < KB / 16; ++kh)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (MODE == 0) {  // one 16-byte read (h = 0 only)
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib) {
+          const int r = wn * WTP + 32 * ib + l31;
+          poff[kh][h][ib] = r * KB + (((2 * kh + hf) ^ kswz(r)) << 3);
+        }
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const int r = wm * WTQ + 32 * jb + l31;
+          qoff[kh][h][jb] = r * KB + (((2 * kh + hf) ^ kswz(r)) << 3);
+        }
+      } else {  // transposing reads: lane s of group g reads row 16kh + 8(g>>1) + 4h + (s>>2)
+        const int r = 16 * kh + 8 * (g >> 1) + 4 * h + (s >> 2);
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib) {
+          const int col = wn * WTP + 32 * ib + 16 * (g & 1) + 4 * (s & 3);
+          poff[kh][h][ib] = r * TS + (((col >> 3) ^ cswz(r)) << 3) + (col & 7);
+        }
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const int col = wm * WTQ + 32 * jb + 16 * (g & 1) + 4 * (s & 3);
+          qoff[kh][h][jb] = r * TS + (((col >> 3) ^ cswz(r)) << 3) + (col & 7);
+        }
+      }
+    }
+  auto frag = [&](const bf16_t* buf, int off0, int off1) -> bf16x8 {
+    if (MODE == 0) return *(const bf16x8*)&buf[off0];
+    const v4i16b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16_lds*)&buf[off0]);
+    const v4i16b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16_lds*)&buf[off1]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  floatx16 acc[IB][JB];
+#pragma unroll
+  for (int i = 0; i < IB; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // MFMAs of one stage (`valid` k-values of it are real), with the copies of later
+  // stages issued between the MFMA groups
+  auto compute = [&](int qbuf, int pbuf, int qkt, int qnb, int pkt, int pnb, bool all, int valid) {
+    const bf16_t* Pb = Ps[pbuf];
+    const bf16_t* Qb = Qs[qbuf];
+    constexpr int PARTS = (KB / 16) * IB;
+#pragma unroll
+    for (int kh = 0; kh < KB / 16; ++kh) {
+      bf16x8 a[IB], b[JB];
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) b[jb] = frag(Qb, qoff[kh][0][jb], qoff[kh][1][jb]);
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) a[ib] = frag(Pb, poff[kh][0][ib], poff[kh][1][ib]);
+      if (MODE == 1 && valid < KB) {
+        const int k0 = 16 * kh + 8 * hf;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) b[jb] = bt_mask(b[jb], k0, valid);
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib) a[ib] = bt_mask(a[ib], k0, valid);
+      }
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) {
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+          acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
+        issue_part(qkt, qnb, pkt, pnb, kh * IB + ib, PARTS, all);
+      }
+    }
+  };
+
+  // ---- pipeline: stage kt in Q buffer kt % NSQ and P buffer kt % NSP.  During stage kt
+  // the Q copies of stage kt + 1 and the P copies of stage kt + 2 are issued (in that
+  // order), so at the top of stage kt + 1 only the newest NI copies may still be in
+  // flight; the barrier then makes every wave's copies visible and releases the buffers
+  // the new copies go to.
+#pragma unroll
+  for (int p = 0; p < NSP - 1; ++p)
+    if (p < nk) issue_part(p < NSQ - 1 ? p : -1, p, p, p, 0, 1);
+  constexpr int U = NSP * NSQ;  // stages per unrolled step: every buffer index is a constant
+  int kt = 0;
+  for (; kt + U + NSP - 2 < nk; kt += U) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+      __syncthreads();
+      compute(j % NSQ, j % NSP, kt + j + NSQ - 1, (j + NSQ - 1) % NSQ, kt + j + NSP - 1, (j + NSP - 1) % NSP, true,
+              KB);
+    }
+  }
+  for (; kt < nk; ++kt) {
+    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int qkt = kt + NSQ - 1 < nk ? kt + NSQ - 1 : -1;
+    const int pkt = kt + NSP - 1 < nk ? kt + NSP - 1 : -1;
+    compute(kt % NSQ, kt % NSP, qkt, qkt % NSQ, pkt, pkt % NSP, false, min(KB, ke - kb - kt * KB));
+  }
+
+  // ---- epilogue: acc[ib][jb][4q + i] is P index wn*WTP + 32ib + 8q + 4hf + i and Q index
+  // wm*WTQ + 32jb + l31.  The tile goes through LDS (fp32, half of its Q rows at a time) so
+  // that each output row is written by one wave, 16 contiguous bytes per lane: written
+  // straight from the accumulators, every store instruction would touch 32 rows.
+  constexpr int LDR = TS + 4;  // staged row stride (floats)
+  constexpr int HQ = TS / 2;   // Q rows per half
+  static_assert(HQ * LDR * 4 <= (NSP + NSQ) * ST * 2, "staging fits in LDS");
+  float* stg = reinterpret_cast<float*>(smem);
+  const int qend = MODE == 0 ? row_end : M;
+  __syncthreads();  // every wave is done reading the last stage
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((wm >> 1) == half) {
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = (wm & 1) * WTQ + 32 * jb + l31;
+            const int col = wn * WTP + 32 * ib + 8 * q + 4 * hf;
+            *(floatx4*)&stg[row * LDR + col] = floatx4{acc[ib][jb][4 * q], acc[ib][jb][4 * q + 1],
+                                                       acc[ib][jb][4 * q + 2], acc[ib][jb][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    const int n = p0 + 4 * lane;
+    for (int rr = 0; rr < HQ / WAVES; ++rr) {
+      const int row = uwave * (HQ / WAVES) + rr;
+      const int qi = q0 + half * HQ + row;
+      if (qi >= qend || n >= N) continue;
+      const floatx4 v = *(const floatx4*)&stg[row * LDR + 4 * lane];
+      if (MODE == 1) {
+        float* dst = n < N1 ? C1 + (size_t)e * sce + (size_t)qi * ldc + n
+                            : C2 + (size_t)e * sce + (size_t)qi * ldc + (n - N1);
+        *(floatx4*)dst = v;
+      } else if (EPI == ACT_NONE) {
+        *(floatx4*)&C1[((size_t)(SPLIT ? ks * R_max : 0) + qi) * ldc + n] = v;
+      } else if (EPI == ACT_SWIGLU) {
+        const floatx4 a4 = *(const floatx4*)&pa[(size_t)qi * ld_ag + n];
+        const floatx4 g4 = *(const floatx4*)&pg[(size_t)qi * ld_ag + n];
+        float da[4], dg[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = a4[i];
+          da[i] = v[i] * g4[i] * silu_grad(a);
+          dg[i] = v[i] * (a / (1.0f + expf(-a)));
+        }
+        bf16_t* orow = DAG + (size_t)qi * 2 * N;
+        *(u32x2*)&orow[n] = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+        *(u32x2*)&orow[N + n] = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+      } else {
+        const floatx4 a4 = *(const floatx4*)&pa[(size_t)qi * ld_ag + n];
+        float da[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) da[i] = v[i] * gelu_grad(a4[i]);
+        *(u32x2*)&DAG[(size_t)qi * N + n] = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// xp[r] = x[rows[r]] for the rows of the segments (r < offsets[E]), 16 bytes per lane
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x, const int* __restrict__ rows,
+                                                          const int* __restrict__ offsets, int E, int cpr,
+                                                          u32x4* __restrict__ xp) {
+  const int r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  const u32x4* src = x + (size_t)rows[r] * cpr;
+  for (int c = threadIdx.x; c < cpr; c += 256) xp[(size_t)r * cpr + c] = src[c];
+}
+
+// dx[t] = dx_router[t] + sum over kept slots j (ascending) of dX[slot of (t, j)], where
+// dX is the sum of the `parts` K parts of dXp (part p at dXp + p * part_stride), in order
 template <typename TD>
 __global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__ dx_router,
-                                                       const float* __restrict__ dXp,
+                                                       const float* __restrict__ dXp, int parts, size_t part_stride,
                                                        const int* __restrict__ slot_pos, int T, int h, int k,
                                                        TD* __restrict__ dx) {
   const int t = blockIdx.x;
@@ -513,7 +867,10 @@ __global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__
     float v = dx_router[(size_t)t * h + i];
     for (int j = 0; j < k; ++j) {
       const int r = slot_pos[(size_t)t * k + j];
-      if (r >= 0) v += dXp[(size_t)r * h + i];
+      if (r < 0) continue;
+      float d = dXp[(size_t)r * h + i];
+      for (int p = 1; p < parts; ++p) d += dXp[p * part_stride + (size_t)r * h + i];
+      v += d;
     }
     st(dx, (size_t)t * h + i, v);
   }
@@ -568,7 +925,61 @@ hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const flo
   return hipGetLastError();
 }
 
+namespace {
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// the pipelined 256 x 256 kernel for an NT product, when its layout allows it
+bool bt_nt_ok(const BwdNT& a) {
+  const int S = std::max(a.ksplit, 1);
+  if (!(a.a_bf16 && a.b_bf16 && a.ts == 256 && a.tile_off_ts != nullptr)) return false;
+  if (a.K % (S * bt::KB) != 0 || a.K1 % bt::KB != 0 || a.lda % 8 || a.ldb % 8 || a.N % 4 || a.sbe % 8) return false;
+  if (!al16(a.A) || !al16(a.B1) || !al16(a.B2)) return false;
+  if (a.epi == ACT_NONE) return a.ldc % 4 == 0 && al16(a.C);
+  return S == 1 && a.ld_ag % 4 == 0 && al16(a.pa) && (a.pg == nullptr || al16(a.pg)) &&
+         ((uintptr_t)a.DAG & 7) == 0;
+}
+
+hipError_t launch_bt_nt(const BwdNT& a, hipStream_t st) {
+  const int NT = (a.N + bt::TS - 1) / bt::TS;
+  const int S = std::max(a.ksplit, 1);
+  const long long slots = ((long long)(a.R_max + bt::TS - 1) / bt::TS + a.E) * NT * S;
+  const long long grid = (slots + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+#define MOE_BTN(EPI, SP)                                                                                         \
+  hipLaunchKernelGGL((bwd_tile_kernel<0, EPI, SP>), dim3((unsigned)grid), dim3(bt::WAVES * 64), 0, st,          \
+                     (const bf16_t*)a.A, a.lda, (const bf16_t*)a.B1, (const bf16_t*)a.B2, a.K1, a.sbe, a.ldb,    \
+                     a.K, 0, a.N, a.offsets, a.tile_off_ts, a.E, NT, 0, S, a.R_max, a.C, a.C, a.N, 0LL, a.ldc, \
+                     a.pa, a.pg, a.ld_ag, (bf16_t*)a.DAG)
+  if (a.epi == ACT_SWIGLU) MOE_BTN(ACT_SWIGLU, false);
+  else if (a.epi == ACT_GELU) MOE_BTN(ACT_GELU, false);
+  else if (S > 1) MOE_BTN(ACT_NONE, true);
+  else MOE_BTN(ACT_NONE, false);
+#undef MOE_BTN
+  return hipGetLastError();
+}
+
+// ... for a TN product (rows not gathered, both weight dimensions at least one tile)
+bool bt_tn_ok(const BwdTN& a) {
+  return a.a_bf16 && a.b_bf16 && a.a_rows == nullptr && a.ksplit <= 1 && a.M >= bt::TS && a.N >= bt::TS &&
+         a.M % 8 == 0 && a.N % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.ldc % 4 == 0 && a.N1 % 4 == 0 &&
+         a.sce % 4 == 0 && al16(a.A) && al16(a.B) && al16(a.C1) && al16(a.C2);
+}
+
+hipError_t launch_bt_tn(const BwdTN& a, hipStream_t st) {
+  const int MT = (a.M + bt::TS - 1) / bt::TS, NT = (a.N + bt::TS - 1) / bt::TS;
+  const long long grid = ((long long)a.E * MT * NT + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_tile_kernel<1, ACT_NONE, false>), dim3((unsigned)grid), dim3(bt::WAVES * 64), 0, st,
+                     (const bf16_t*)a.A, a.lda, (const bf16_t*)a.B, (const bf16_t*)a.B, 0, 0LL, a.ldb, 0, a.M, a.N,
+                     a.offsets, nullptr, a.E, NT, MT, 1, 0, a.C1, a.C2, a.N1, a.sce, a.ldc, nullptr, nullptr, 0,
+                     nullptr);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st) {
+  if (bt_nt_ok(a)) return launch_bt_nt(a, st);
+  if (a.ksplit > 1) return hipErrorInvalidValue;  // K parts only on the pipelined kernel
   if (a.a_bf16 && a.b_bf16 && a.tile_off_ts != nullptr && a.K % MKB == 0 && a.K1 % MKB == 0 && a.lda % 8 == 0 &&
       a.ldb % 8 == 0 && (a.ts == 128 || a.ts == 256)) {
 #define MOE_NTM(EPI, TS)                                                                                           \
@@ -610,6 +1021,7 @@ hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
+  if (bt_tn_ok(a)) return launch_bt_tn(a, st);
   if (a.ksplit > 1) {
     // one segment of rows split in a.ksplit slices: partial sums in a.part, added in order
     if (a.E != 1 || a.part == nullptr || a.a_rows != nullptr) return hipErrorInvalidValue;
@@ -661,15 +1073,25 @@ hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_dx_final(const float* dx_router, const float* dXp, const int* slot_pos, int T, int h, int k,
-                           bool bf16, void* dx, hipStream_t st) {
+hipError_t launch_dx_final(const float* dx_router, const float* dXp, int parts, size_t part_stride,
+                           const int* slot_pos, int T, int h, int k, bool bf16, void* dx, hipStream_t st) {
   if (T <= 0) return hipSuccess;
+  if (parts < 1) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(dx_final_kernel<bf16_t>, dim3(T), dim3(256), 0, st, dx_router, dXp, slot_pos, T, h, k,
-                       (bf16_t*)dx);
+    hipLaunchKernelGGL(dx_final_kernel<bf16_t>, dim3(T), dim3(256), 0, st, dx_router, dXp, parts, part_stride,
+                       slot_pos, T, h, k, (bf16_t*)dx);
   else
-    hipLaunchKernelGGL(dx_final_kernel<float>, dim3(T), dim3(256), 0, st, dx_router, dXp, slot_pos, T, h, k,
-                       (float*)dx);
+    hipLaunchKernelGGL(dx_final_kernel<float>, dim3(T), dim3(256), 0, st, dx_router, dXp, parts, part_stride,
+                       slot_pos, T, h, k, (float*)dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int* rows, const int* offsets, int E, int R_max, int row_bytes,
+                              void* xp, hipStream_t st) {
+  if (R_max <= 0) return hipSuccess;
+  if (row_bytes % 16 != 0 || ((uintptr_t)x | (uintptr_t)xp) % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)R_max), dim3(256), 0, st, (const u32x4*)x, rows, offsets, E,
+                     row_bytes / 16, (u32x4*)xp);
   return hipGetLastError();
 }
 

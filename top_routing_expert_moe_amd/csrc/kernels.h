@@ -138,6 +138,8 @@ struct BwdNT {
   int ts; const int* tile_off_ts;
   float* C; int ldc;
   int epi; const float* pa; const float* pg; int ld_ag; void* DAG;
+  // K parts (epi == ACT_NONE, 256-row tiles only): part p of C at C + p * R_max * ldc
+  int ksplit;
 };
 // grouped TN product over each segment's rows: C_e[m, n] = sum_r A[row(r), m] B[r, n]
 struct BwdTN {
@@ -160,7 +162,10 @@ hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const flo
                              const int* counts, int T, int E, int k, float d_aux, float* dl, hipStream_t st);
 hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st);
 hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st);
-hipError_t launch_dx_final(const float* dx_router, const float* dXp, const int* slot_pos, int T, int h, int k,
-                           bool bf16, void* dx, hipStream_t st);
+hipError_t launch_dx_final(const float* dx_router, const float* dXp, int parts, size_t part_stride,
+                           const int* slot_pos, int T, int h, int k, bool bf16, void* dx, hipStream_t st);
+// xp[r] = x[rows[r]] (row_bytes each) for r < offsets[E]
+hipError_t launch_gather_rows(const void* x, const int* rows, const int* offsets, int E, int R_max, int row_bytes,
+                              void* xp, hipStream_t st);
 
 }  // namespace moe
