@@ -521,13 +521,10 @@ gemm_bwd_mfma_kernel(const bf16_t* __restrict__ A, int lda, const int* __restric
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 namespace bt {
-constexpr int TS = 256, KB = 64, WAVES = 8;
-constexpr int WQ = 4, WP = 2;                // waves along Q / along P
-constexpr int WTQ = TS / WQ, WTP = TS / WP;  // wave tile: 64 (Q) x 128 (P)
-constexpr int IB = WTP / 32, JB = WTQ / 32;  // 32 x 32 blocks per wave
+constexpr int TS = 256, KB = 64, WAVES = 8;  // P extent of a tile, k per stage, waves
 constexpr int NSP = 3, NSQ = 2;              // LDS stages of P and Q
-constexpr int ST = TS * KB;                  // elements per stage of either operand
-constexpr int NI = 32 / WAVES;               // 1 KiB copies per wave, operand and stage
+constexpr int STP = TS * KB;                 // elements per P stage
+constexpr int NIP = STP / 512 / WAVES;       // 1 KiB copies per wave and P stage
 constexpr int BLK = 512;                     // elements per 1 KiB copy
 constexpr int GM = 4, GN = 8;                // tile groups, as in the forward GEMM
 }  // namespace bt
@@ -562,9 +559,10 @@ __device__ __forceinline__ bf16x8 bt_mask(bf16x8 v, int k0, int valid) {
   return __builtin_bit_cast(bf16x8, s);
 }
 
-// MODE 0 = NT over the 256-row tiles of the segments (tile_off: their list), in S K parts
-// (part s of C at C1 + s * R_max * ldc); MODE 1 = TN over each segment's rows.
-template <int MODE, int EPI, bool SPLIT>
+// MODE 0 = NT over the TQ-row tiles of the segments (tile_off: their list), in S K parts
+// (part s of C at C1 + s * R_max * ldc); MODE 1 = TN over each segment's rows (TQ = 256).
+// The Q extent TQ of a tile is 256 (4 x 2 waves of 64 x 128) or 128 (2 x 4 waves of 64 x 64).
+template <int MODE, int EPI, bool SPLIT, int TQ = 256>
 __global__ __launch_bounds__(bt::WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B1,
                 const bf16_t* __restrict__ B2, int K1, long long sbe, int ldb, int K, int M, int N,
@@ -572,9 +570,15 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
                 int R_max, float* __restrict__ C1, float* __restrict__ C2, int N1, long long sce, int ldc,
                 const float* __restrict__ pa, const float* __restrict__ pg, int ld_ag, bf16_t* __restrict__ DAG) {
   using namespace bt;
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[(NSP + NSQ) * ST];
-  bf16_t(*Ps)[ST] = reinterpret_cast<bf16_t(*)[ST]>(smem);
-  bf16_t(*Qs)[ST] = reinterpret_cast<bf16_t(*)[ST]>(smem + NSP * ST);
+  static_assert(TQ == 256 || (TQ == 128 && MODE == 0), "tile shapes");
+  constexpr int WQ = TQ / 64, WP = WAVES / WQ;  // waves along Q / along P
+  constexpr int WTQ = 64, WTP = TS / WP;         // wave tile
+  constexpr int IB = WTP / 32, JB = WTQ / 32;    // 32 x 32 blocks per wave
+  constexpr int STQ = TQ * KB;                   // elements per Q stage
+  constexpr int NIQ = STQ / BLK / WAVES;         // 1 KiB copies per wave and Q stage
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NSP * STP + NSQ * STQ];
+  bf16_t(*Ps)[STP] = reinterpret_cast<bf16_t(*)[STP]>(smem);
+  bf16_t(*Qs)[STQ] = reinterpret_cast<bf16_t(*)[STQ]>(smem + NSP * STP);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
 
@@ -607,7 +611,7 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
       }
       e = lo;
       bt_group(L - tile_off[e] * NT, tile_off[e + 1] - tile_off[e], NT, mt, nt);
-      q0 = offsets[e] + mt * TS;
+      q0 = offsets[e] + mt * TQ;
       row_end = offsets[e + 1];
       const int Kc = SPLIT ? K / S : K;
       kb = ks * Kc;
@@ -615,7 +619,7 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
     } else {
       e = L / (MT * NT);
       bt_group(L - e * MT * NT, MT, NT, mt, nt);
-      q0 = mt * TS;
+      q0 = mt * TQ;
       kb = offsets[e];
       ke = offsets[e + 1];
     }
@@ -623,24 +627,34 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
   }
   const int nk = (ke - kb + KB - 1) / KB;
 
-  // ---- copy plan: copy i of wave w fills 1 KiB block NI * w + i of a stage
-  const bf16_t* pb1[NI];
-  const bf16_t* pb2[NI];
-  const bf16_t* qa[NI];
-  int rl[NI];
+  // ---- copy plan: P copy i of wave w fills 1 KiB block NIP * w + i of a P stage, Q copy
+  // i block NIQ * w + i of a Q stage
+  const bf16_t* pb1[NIP];
+  const bf16_t* pb2[NIP];
+  const bf16_t* qa[NIQ];
+  int rl[NIP];  // TN: the stage row (k) of each copy (the same for both operands)
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  for (int i = 0; i < NIP; ++i) {
     if (MODE == 0) {
-      const int r = 8 * (NI * wave + i) + (lane >> 3);  // stage row
+      const int r = 8 * (NIP * wave + i) + (lane >> 3);  // stage row (n)
       const int ch = ((lane & 7) ^ kswz(r)) << 3;
       const size_t n = (size_t)min(p0 + r, N - 1);
       pb1[i] = B1 + (size_t)e * sbe + n * ldb + ch;
       pb2[i] = B2 + (size_t)e * sbe + n * ldb + ch;
-      qa[i] = A + (size_t)min(q0 + r, row_end - 1) * lda + ch;
     } else {
-      rl[i] = 2 * (NI * wave + i) + (lane >> 5);  // stage row (k)
+      rl[i] = 2 * (NIP * wave + i) + (lane >> 5);
       const int ch = ((lane & 31) ^ cswz(rl[i])) << 3;
       pb1[i] = B1 + min(p0 + ch, N - 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NIQ; ++i) {
+    if (MODE == 0) {
+      const int r = 8 * (NIQ * wave + i) + (lane >> 3);  // stage row (r)
+      const int ch = ((lane & 7) ^ kswz(r)) << 3;
+      qa[i] = A + (size_t)min(q0 + r, row_end - 1) * lda + ch;
+    } else {
+      const int ch = ((lane & 31) ^ cswz(rl[i])) << 3;  // TQ = 256: the same rows as P
       qa[i] = A + min(q0 + ch, M - 8);
     }
   }
@@ -650,7 +664,7 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
     const bf16_t* src;
     if (MODE == 0) src = qa[i] + kb + kt * KB;
     else src = qa[i] + (size_t)min(kb + kt * KB + rl[i], ke - 1) * lda;
-    bt_copy16(src, qs_lds + 2u * (uint32_t)(buf * ST + BLK * (NI * uwave + i)));
+    bt_copy16(src, qs_lds + 2u * (uint32_t)(buf * STQ + BLK * (NIQ * uwave + i)));
   };
   auto copy_p = [&](int i, int kt, int buf) {
     const bf16_t* src;
@@ -660,20 +674,22 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
     } else {
       src = pb1[i] + (size_t)min(kb + kt * KB + rl[i], ke - 1) * ldb;
     }
-    bt_copy16(src, ps_lds + 2u * (uint32_t)(buf * ST + BLK * (NI * uwave + i)));
+    bt_copy16(src, ps_lds + 2u * (uint32_t)(buf * STP + BLK * (NIP * uwave + i)));
   };
   // copies of MFMA group `part` of `parts`: the Q copies of stage qkt take the first
-  // four groups, the P copies of stage pkt every other group after them (parts == 1:
-  // all at once); ALL: both stages are known to exist
+  // four groups, the P copies of stage pkt every other group after them when there are
+  // 16 groups, the next four when there are 8 (parts == 1: all at once); ALL: both
+  // stages are known to exist
   auto issue_part = [&](int qkt, int qnb, int pkt, int pnb, int part, int parts, bool all = false) {
     const int sp = parts < 8 ? parts : 8;
     const bool split = parts > 1;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if ((all || qkt >= 0) && (split ? i * (sp / 2) / NI : 0) == part) copy_q(i, qkt, qnb);
+    for (int i = 0; i < NIQ; ++i)
+      if ((all || qkt >= 0) && (split ? i * (sp / 2) / NIQ : 0) == part) copy_q(i, qkt, qnb);
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if ((all || pkt >= 0) && (split ? sp / 2 + i * sp / NI : 0) == part) copy_p(i, pkt, pnb);
+    for (int i = 0; i < NIP; ++i)
+      if ((all || pkt >= 0) && (split ? sp / 2 + i * (parts >= 2 * sp ? sp : sp / 2) / NIP : 0) == part)
+        copy_p(i, pkt, pnb);
   };
 
   // ---- fragment offsets (elements within a stage) for 16-k step kh and half h
@@ -756,7 +772,7 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
 
   // ---- pipeline: stage kt in Q buffer kt % NSQ and P buffer kt % NSP.  During stage kt
   // the Q copies of stage kt + 1 and the P copies of stage kt + 2 are issued (in that
-  // order), so at the top of stage kt + 1 only the newest NI copies may still be in
+  // order), so at the top of stage kt + 1 only the newest NIP copies may still be in
   // flight; the barrier then makes every wave's copies visible and releases the buffers
   // the new copies go to.
 #pragma unroll
@@ -767,14 +783,14 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
   for (; kt + U + NSP - 2 < nk; kt += U) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIP) : "memory");
       __syncthreads();
       compute(j % NSQ, j % NSP, kt + j + NSQ - 1, (j + NSQ - 1) % NSQ, kt + j + NSP - 1, (j + NSP - 1) % NSP, true,
               KB);
     }
   }
   for (; kt < nk; ++kt) {
-    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIP) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int qkt = kt + NSQ - 1 < nk ? kt + NSQ - 1 : -1;
@@ -787,21 +803,21 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
   // that each output row is written by one wave, 16 contiguous bytes per lane: written
   // straight from the accumulators, every store instruction would touch 32 rows.
   constexpr int LDR = TS + 4;  // staged row stride (floats)
-  constexpr int HQ = TS / 2;   // Q rows per half
-  static_assert(HQ * LDR * 4 <= (NSP + NSQ) * ST * 2, "staging fits in LDS");
+  constexpr int HQ = TQ / 2;   // Q rows per half
+  static_assert(HQ * LDR * 4 <= (NSP * STP + NSQ * STQ) * 2, "staging fits in LDS");
   float* stg = reinterpret_cast<float*>(smem);
   const int qend = MODE == 0 ? row_end : M;
   __syncthreads();  // every wave is done reading the last stage
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if ((wm >> 1) == half) {
+    if (wm / (WQ / 2) == half) {
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int row = (wm & 1) * WTQ + 32 * jb + l31;
+            const int row = (wm % (WQ / 2)) * WTQ + 32 * jb + l31;
             const int col = wn * WTP + 32 * ib + 8 * q + 4 * hf;
             *(floatx4*)&stg[row * LDR + col] = floatx4{acc[ib][jb][4 * q], acc[ib][jb][4 * q + 1],
                                                        acc[ib][jb][4 * q + 2], acc[ib][jb][4 * q + 3]};
@@ -931,7 +947,7 @@ bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // the pipelined 256 x 256 kernel for an NT product, when its layout allows it
 bool bt_nt_ok(const BwdNT& a) {
   const int S = std::max(a.ksplit, 1);
-  if (!(a.a_bf16 && a.b_bf16 && a.ts == 256 && a.tile_off_ts != nullptr)) return false;
+  if (!(a.a_bf16 && a.b_bf16 && (a.ts == 256 || a.ts == 128) && a.tile_off_ts != nullptr)) return false;
   if (a.K % (S * bt::KB) != 0 || a.K1 % bt::KB != 0 || a.lda % 8 || a.ldb % 8 || a.N % 4 || a.sbe % 8) return false;
   if (!al16(a.A) || !al16(a.B1) || !al16(a.B2)) return false;
   if (a.epi == ACT_NONE) return a.ldc % 4 == 0 && al16(a.C);
@@ -939,14 +955,15 @@ bool bt_nt_ok(const BwdNT& a) {
          ((uintptr_t)a.DAG & 7) == 0;
 }
 
-hipError_t launch_bt_nt(const BwdNT& a, hipStream_t st) {
+template <int TQ>
+hipError_t launch_bt_nt_t(const BwdNT& a, hipStream_t st) {
   const int NT = (a.N + bt::TS - 1) / bt::TS;
   const int S = std::max(a.ksplit, 1);
-  const long long slots = ((long long)(a.R_max + bt::TS - 1) / bt::TS + a.E) * NT * S;
+  const long long slots = ((long long)(a.R_max + TQ - 1) / TQ + a.E) * NT * S;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
 #define MOE_BTN(EPI, SP)                                                                                         \
-  hipLaunchKernelGGL((bwd_tile_kernel<0, EPI, SP>), dim3((unsigned)grid), dim3(bt::WAVES * 64), 0, st,          \
+  hipLaunchKernelGGL((bwd_tile_kernel<0, EPI, SP, TQ>), dim3((unsigned)grid), dim3(bt::WAVES * 64), 0, st,      \
                      (const bf16_t*)a.A, a.lda, (const bf16_t*)a.B1, (const bf16_t*)a.B2, a.K1, a.sbe, a.ldb,    \
                      a.K, 0, a.N, a.offsets, a.tile_off_ts, a.E, NT, 0, S, a.R_max, a.C, a.C, a.N, 0LL, a.ldc, \
                      a.pa, a.pg, a.ld_ag, (bf16_t*)a.DAG)
@@ -956,6 +973,10 @@ hipError_t launch_bt_nt(const BwdNT& a, hipStream_t st) {
   else MOE_BTN(ACT_NONE, false);
 #undef MOE_BTN
   return hipGetLastError();
+}
+
+hipError_t launch_bt_nt(const BwdNT& a, hipStream_t st) {
+  return a.ts == 256 ? launch_bt_nt_t<256>(a, st) : launch_bt_nt_t<128>(a, st);
 }
 
 // ... for a TN product (rows not gathered, both weight dimensions at least one tile)
