@@ -114,8 +114,9 @@ def main():
     ap.add_argument("--capacity-factor", type=float, default=None, help="override the workload's factor")
     ap.add_argument("--min-capacity", type=int, default=0, help="binned layout: the smallest bucket size")
     ap.add_argument("--backward", action="store_true",
-                    help="time a training step: the layer forward, then its backward pass (dy ~ N(0,1), aux weight "
-                         "0.01), with per-stage times of both")
+                    help="time a training step: the training forward (which saves the up projection's "
+                         "pre-activations), then the backward pass (dy ~ N(0,1), aux weight 0.01), with per-stage "
+                         "times of both")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run a plain elementwise copy (y = x + 1, fp32) over this many MiB three "
                          "times: a kernel of known traffic for calibrating rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -191,18 +192,22 @@ def main():
         bws = torch.empty(moe.lib().moe_layer_backward_workspace_bytes(T, h, f, E, k, w.cf, dt, act), dtype=torch.uint8,
                           device=dev)
         grads = {}
-        fwd_step = step
         nf = len(moe.LAYER_STAGES)
         stages = tuple(moe.LAYER_STAGES) + ("forward_to_backward",) + tuple("bwd_" + s for s in moe.BACKWARD_STAGES)
+        # the training forward saves the up projection's pre-activations for the backward
+        pre = torch.empty(moe.preact_bytes(T, h, f, E, k, w.cf, w.act), dtype=torch.uint8, device=dev)
 
         def step(events=None):
             evf = evb = None
             if events is not None:
                 evf = (ctypes.c_void_p * (nf + 1))(*events[:nf + 1])
                 evb = (ctypes.c_void_p * (len(moe.BACKWARD_STAGES) + 1))(*events[nf + 1:])
-            fwd_step(evf)
+            moe.layer_forward(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
+                              capacity_factor=w.cf, act=w.act, ws=ws, y=y, aux=aux, counts=counts, events=evf,
+                              preact=pre)
             out = moe.layer_backward(d["x"], d["W_gate"], d["W1"], d["W3"], d["W2"], dy, k=k, capacity_factor=w.cf,
-                                     act=w.act, fwd_ws=ws, d_aux=0.01, ws=bws, out=grads or None, events=evb)
+                                     act=w.act, fwd_ws=ws, d_aux=0.01, ws=bws, out=grads or None, events=evb,
+                                     preact=pre)
             grads.update(out)
 
     if args.copy_probe_mib > 0:
@@ -340,9 +345,10 @@ def main():
         # the weight gradients are fp32)
         bw = {s_: stage_ms["bwd_" + s_] for s_ in moe.BACKWARD_STAGES}
         Rk = int(kept.sum())
-        fl = {"recompute_up": 2.0 * n_up * Rk * h * f, "down_dgrad": 2.0 * Rk * h * f, "down_wgrad": 2.0 * Rk * f * h,
+        # (the pre-activations are saved by the training forward: no recompute)
+        fl = {"recompute_up": 0.0, "down_dgrad": 2.0 * Rk * h * f, "down_wgrad": 2.0 * Rk * f * h,
               "up_dgrad": 2.0 * n_up * Rk * f * h, "up_wgrad": 2.0 * n_up * Rk * h * f}
-        by = {"recompute_up": active * n_up * h * f * es + Rk * h * es + Rk * n_up * f * 4,
+        by = {"recompute_up": 0,
               "down_dgrad": active * f * h * es + Rk * h * es + Rk * n_up * f * 4 + Rk * n_up * f * es,
               "down_wgrad": Rk * f * es + Rk * h * es + active * f * h * 4,
               "up_dgrad": active * n_up * h * f * es + Rk * n_up * f * es + Rk * h * 4,

@@ -203,26 +203,48 @@ moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const floa
  * Selection and capacity are piecewise constant (no gradient); in bf16 the rounding of
  * Hm passes gradients unchanged, while dW2 uses the rounded Hm.  The plain router only:
  * not the variants of moe_router_opts_t.
- *   fwd_ws / fwd_ws_bytes: the workspace of the moe_layer_forward call being
- *     differentiated, untouched since (it holds the routing, Hm and the expert outputs);
- *     the other inputs must be that call's.
+ *   fwd_ws / fwd_ws_bytes: the workspace of the moe_layer_forward (or
+ *     moe_layer_forward_train) call being differentiated, untouched since (it holds the
+ *     routing, Hm and the expert outputs); the other inputs must be that call's.
+ *   preact / preact_bytes: NULL, or the pre-activations that moe_layer_forward_train wrote
+ *     in that call (at least moe_layer_preact_bytes(...) bytes, else MOE_ERR_WORKSPACE).
+ *     With NULL the pre-activations a (| g) are recomputed with the up projection's GEMM.
  *   dy [T,h] (dt); d_aux: host scalar.
  *   dx [T,h] (dt); dW_gate [h,E] fp32 or NULL (skipped); dW1, dW3 [E,h,f], dW2 [E,f,h]
  *     fp32 (dW3 NULL iff GELU).  The weight gradients are overwritten, not accumulated.
- *   ws: at least moe_layer_backward_workspace_bytes(...) bytes.
- * The pre-activations a (| g) are recomputed with the up projection's GEMM. */
+ *   ws: at least moe_layer_backward_workspace_bytes(...) bytes (the same with or without
+ *     preact). */
 size_t moe_layer_backward_workspace_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
                                           float capacity_factor, moe_dtype_t dt, moe_act_t act);
 moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* W1, const void* W3,
                                 const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
                                 float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
-                                float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                                float d_aux, const void* fwd_ws, size_t fwd_ws_bytes,
+                                const float* preact, size_t preact_bytes, void* dx,
                                 float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* Training forward: moe_layer_forward (same arguments and results) that also writes the
+ * up projection's fp32 pre-activations a (| g) of every kept assignment to `preact`, so
+ * that moe_layer_backward can read them instead of recomputing them.  The buffer is an
+ * opaque context of moe_layer_preact_bytes(...) bytes (R_max * f * 4, twice that for
+ * SwiGLU, R_max the bound on kept assignments), 16-byte aligned (MOE_ERR_UNSUPPORTED
+ * otherwise), caller-owned.  Its values equal the recomputed ones when the up projection
+ * runs without K parts, and agree to fp32 rounding otherwise.  `events`: NULL, or as for
+ * moe_layer_forward_timed.  preact NULL: MOE_ERR_ARG; too small: MOE_ERR_WORKSPACE. */
+size_t moe_layer_preact_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                              float capacity_factor, moe_act_t act);  /* 0 for invalid sizes */
+moe_status_t moe_layer_forward_train(const void* x, const float* W_gate, const float* logit_bias,
+                                     const void* W1, const void* W3, const void* W2,
+                                     int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                     float capacity_factor, moe_act_t act, moe_dtype_t dt,
+                                     void* y, float* aux_loss, int32_t* counts,
+                                     void* ws, size_t ws_bytes, float* preact, size_t preact_bytes,
+                                     hipStream_t stream, hipEvent_t* events);
+
 /* Measurement variant of moe_layer_backward: events[0] before the first kernel, then one
  * after each stage (combine adjoint with the counts and tile lists, router adjoint,
- * pre-activation recompute, down-projection data gradient with the activation's
+ * pre-activation recompute (empty with preact), down-projection data gradient with the activation's
  * derivative, down-projection weight gradient, up-projection data gradient, up-projection
  * weight gradients, router GEMMs, dx).  `events` (not null: MOE_ERR_ARG) holds
  * MOE_BACKWARD_STAGES + 1 entries, each a hipEvent_t or null (nothing recorded there). */
@@ -230,7 +252,8 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
 moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const void* W1, const void* W3,
                                       const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
                                       float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
-                                      float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                                      float d_aux, const void* fwd_ws, size_t fwd_ws_bytes,
+                                      const float* preact, size_t preact_bytes, void* dx,
                                       float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
                                       size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
 

@@ -41,7 +41,8 @@ def test_exports_every_declared_symbol(L):
                           "moe_route_workspace_bytes", "moe_binned_capacity_max", "moe_binned_workspace_bytes",
                           "moe_layer_forward_binned", "moe_layer_forward_binned_timed",
                           "moe_router_opts_workspace_bytes", "moe_route_ex", "moe_layer_forward_ex",
-                          "moe_layer_backward_workspace_bytes", "moe_layer_backward", "moe_layer_backward_timed"}
+                          "moe_layer_backward_workspace_bytes", "moe_layer_backward", "moe_layer_backward_timed",
+                          "moe_layer_preact_bytes", "moe_layer_forward_train"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -353,11 +354,13 @@ def test_layer_backward_host_errors(L):
 
     def call(**kw):
         a = dict(x=FAKE, Wg=FAKE, W1=FAKE, W3=FAKE, W2=FAKE, T=T, h=h, f=f, E=E, k=k, cf=0.0, act=1, dt=1, dy=FAKE,
-                 d_aux=0.0, fws=FAKE, fwsb=fwd, dx=FAKE, dWg=None, dW1=FAKE, dW3=FAKE, dW2=FAKE, ws=FAKE, wsb=bws)
+                 d_aux=0.0, fws=FAKE, fwsb=fwd, pre=None, preb=0, dx=FAKE, dWg=None, dW1=FAKE, dW3=FAKE, dW2=FAKE,
+                 ws=FAKE, wsb=bws)
         a.update(kw)
         return L.moe_layer_backward(a["x"], a["Wg"], a["W1"], a["W3"], a["W2"], a["T"], a["h"], a["f"], a["E"],
                                     a["k"], a["cf"], a["act"], a["dt"], a["dy"], a["d_aux"], a["fws"], a["fwsb"],
-                                    a["dx"], a["dWg"], a["dW1"], a["dW3"], a["dW2"], a["ws"], a["wsb"], None)
+                                    a["pre"], a["preb"], a["dx"], a["dWg"], a["dW1"], a["dW3"], a["dW2"], a["ws"],
+                                    a["wsb"], None)
     assert call(d_aux=float("nan")) == ARG
     assert call(dW3=None) == ARG                 # SwiGLU has a W3 gradient
     assert call(act=0, W3=None) == ARG           # GELU has none
@@ -366,14 +369,39 @@ def test_layer_backward_host_errors(L):
     assert call(h=96) == UNSUP
     assert call(fwsb=fwd - 1) == WS              # the forward's workspace is the saved context
     assert call(wsb=bws - 1) == WS
+    # saved pre-activations: R_max * 2f fp32 for SwiGLU; the backward's workspace is the same
+    pb = L.moe_layer_preact_bytes(T, h, f, E, k, 0.0, 1)
+    assert pb == T * k * 2 * f * 4 and L.moe_layer_preact_bytes(T, h, f, E, k, 0.0, 0) == pb // 2
+    assert L.moe_layer_preact_bytes(T, 96, f, E, k, 0.0, 1) == 0
+    assert call(pre=FAKE, preb=pb - 1) == WS
     assert call(T=0) == OK
-    a = [FAKE, FAKE, FAKE, FAKE, FAKE, T, h, f, E, k, 0.0, 1, 1, FAKE, 0.0, FAKE, fwd, FAKE, None, FAKE, FAKE, FAKE,
-         FAKE, bws, None]
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, T, h, f, E, k, 0.0, 1, 1, FAKE, 0.0, FAKE, fwd, None, 0, FAKE, None, FAKE,
+         FAKE, FAKE, FAKE, bws, None]
     assert L.moe_layer_backward_timed(*a, None) == ARG
     ev = (ctypes.c_void_p * 10)(*([FAKE] * 9 + [0]))  # null entries: nothing recorded there
     a[6] = 96  # h not a multiple of 64: rejected before any event is recorded
     assert L.moe_layer_backward_timed(*a, ctypes.cast(ev, ctypes.c_void_p)) == UNSUP
     assert len(moe.BACKWARD_STAGES) == 9
+
+
+def test_layer_forward_train_host_errors(L):
+    T, h, f, E, k = 64, 128, 256, 8, 2
+    ws = moe.workspace_bytes(T, h, f, E, k, 0.0, 1, 1)
+    pb = L.moe_layer_preact_bytes(T, h, f, E, k, 0.0, 1)
+
+    def call(pre=FAKE, preb=pb, **kw):
+        a = dict(x=FAKE, Wg=FAKE, b=None, W1=FAKE, W3=FAKE, W2=FAKE, T=T, h=h, f=f, E=E, k=k, cf=0.0, act=1, dt=1,
+                 y=FAKE, aux=None, counts=None, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return L.moe_layer_forward_train(a["x"], a["Wg"], a["b"], a["W1"], a["W3"], a["W2"], a["T"], a["h"], a["f"],
+                                         a["E"], a["k"], a["cf"], a["act"], a["dt"], a["y"], a["aux"], a["counts"],
+                                         a["ws"], a["wsb"], pre, preb, None, None)
+    assert call(pre=None) == ARG
+    assert call(pre=FAKE + 8) == UNSUP         # 16-byte alignment
+    assert call(preb=pb - 1) == WS
+    assert call(wsb=ws - 1) == WS
+    assert call(h=96) == UNSUP
+    assert call(T=0) == OK
 
 
 def test_binding_refuses_cpu_tensors(L):

@@ -151,3 +151,69 @@ def test_backward_deterministic():
     g2, _ = _run(w, dd, dy)
     for kk, v in first.items():
         assert np.array_equal(v, gu.from_dev(g2[kk])), kk
+
+
+def _fwd_bwd(w, dd, dy_host, saved):
+    """Forward then backward; with `saved`, the training forward and the backward that reads
+    its pre-activations."""
+    torch = gu.torch()
+    dev = dd["x"].device
+    dt = moe.BF16 if w.dtype == "bf16" else moe.F32
+    a = moe.SWIGLU if w.act == "swiglu" else moe.GELU
+    fws = moe._ws(moe.workspace_bytes(w.T, w.h, w.f, w.E, w.k, w.cf, dt, a), dev)
+    pre = moe._ws(moe.preact_bytes(w.T, w.h, w.f, w.E, w.k, w.cf, w.act), dev) if saved else None
+    args = (dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"])
+    fwd = moe.layer_forward(*args, k=w.k, capacity_factor=w.cf, act=w.act, ws=fws, preact=pre)
+    g = moe.layer_backward(dd["x"], dd["W_gate"], dd["W1"], dd["W3"], dd["W2"], gu.to_dev(dy_host, w.dtype), k=w.k,
+                           capacity_factor=w.cf, act=w.act, fwd_ws=fws, d_aux=D_AUX, preact=pre)
+    torch.cuda.synchronize()
+    return [gu.from_dev(t).copy() for t in fwd], {kk: gu.from_dev(v).copy() for kk, v in g.items() if v is not None}
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "decode-mixtral", "capacity-e64"])
+def test_saved_preactivations_give_the_recomputed_gradients(name):
+    """The training forward returns what the forward returns, and its saved a (| g) are the
+    accumulators the recomputing backward would form (the same products, summed in the same
+    order), so the gradients agree bit for bit."""
+    _say(f"saved pre-activations {name}")
+    w, host, dd = gu.workload(name)
+    dy = _dy(w.T, w.h, w.dtype)
+    f0, g0 = _fwd_bwd(w, dd, dy, saved=False)
+    f1, g1 = _fwd_bwd(w, dd, dy, saved=True)
+    for a, b in zip(f0, f1):
+        assert np.array_equal(a, b)
+    assert set(g0) == set(g1)
+    for kk in g0:
+        assert np.array_equal(g0[kk], g1[kk]), kk
+
+
+@pytest.mark.parametrize("T,h,f,E,k,cf,act,dtype", [
+    (20, 1024, 2048, 8, 2, 0.0, "swiglu", "bf16"),   # up projection in K parts: saved by the parts' sum
+    (33, 256, 192, 6, 3, 0.0, "gelu", "bf16"),
+    (500, 128, 256, 16, 2, 0.25, "gelu", "f32"),
+])
+def test_saved_preactivations_parity(T, h, f, E, k, cf, act, dtype):
+    _say(f"saved pre-activations T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")
+    rng = np.random.default_rng(T + 3 * E)
+    conv = (lambda a: mw.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32),
+                logit_bias=rng.standard_normal(E).astype(np.float32),
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)) if act == "swiglu" else None,
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("edge", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
+    dy = _dy(T, h, dtype)
+    torch = gu.torch()
+    dev = dd["x"].device
+    dt = moe.BF16 if dtype == "bf16" else moe.F32
+    fws = moe._ws(moe.workspace_bytes(T, h, f, E, k, cf, dt, moe.SWIGLU if act == "swiglu" else moe.GELU), dev)
+    pre = moe._ws(moe.preact_bytes(T, h, f, E, k, cf, act), dev)
+    args = (dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"])
+    moe.layer_forward(*args, k=k, capacity_factor=cf, act=act, ws=fws, preact=pre)
+    logits, _, _, _ = moe.route(dd["x"], dd["W_gate"], dd["logit_bias"], k)
+    g = moe.layer_backward(dd["x"], dd["W_gate"], dd["W1"], dd["W3"], dd["W2"], gu.to_dev(dy, dtype), k=k,
+                           capacity_factor=cf, act=act, fwd_ws=fws, d_aux=D_AUX, preact=pre)
+    torch.cuda.synchronize()
+    _check_all(w, host, g, gu.from_dev(logits), dy)

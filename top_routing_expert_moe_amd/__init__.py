@@ -17,7 +17,8 @@ import os
 
 __all__ = ["MoEError", "lib", "lib_path", "capacity", "workspace_bytes", "status_string", "route",
            "permute", "expert_ffn", "unpermute", "layer_forward", "LAYER_STAGES", "F32", "BF16", "GELU", "SWIGLU",
-           "ROUTE_LOGITS_IN"]
+           "ROUTE_LOGITS_IN", "layer_backward", "layer_forward_binned", "preact_bytes", "BACKWARD_STAGES",
+           "BINNED_STAGES", "binned_capacity_max", "binned_workspace_bytes", "CapacityConfig", "RouterOpts"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoe_mi355x.so")
@@ -76,12 +77,17 @@ _SIGS = {
     "moe_layer_backward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int]),
     "moe_layer_backward": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                           _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _c_void_p, _f32, _c_void_p,
-                                          _sz, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                          _sz, _c_void_p]),
+                                          _sz, _c_void_p, _sz, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                          _c_void_p, _c_void_p, _sz, _c_void_p]),
     "moe_layer_backward_timed": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                                 _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _c_void_p, _f32,
-                                                _c_void_p, _sz, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                                _c_void_p, _c_void_p, _sz, _c_void_p, _c_void_p]),
+                                                _c_void_p, _sz, _c_void_p, _sz, _c_void_p, _c_void_p, _c_void_p,
+                                                _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p, _c_void_p]),
+    "moe_layer_preact_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int]),
+    "moe_layer_forward_train": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                               _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
+                                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p, _sz,
+                                               _c_void_p, _c_void_p]),
     "moe_binned_capacity_max": (_i32, [_i32, _i32, _i32, _f32, _i32]),
     "moe_binned_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, ctypes.c_int]),
     "moe_layer_forward_binned": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -200,6 +206,10 @@ def _stream(dev):
     return _torch().cuda.current_stream(dev).cuda_stream
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def _ws(nbytes: int, dev):
     return _torch().empty(max(int(nbytes), 1), dtype=_torch().uint8, device=dev)
 
@@ -305,14 +315,21 @@ def unpermute(out_perm, slot_pos, topk_w):
     return y
 
 
+def preact_bytes(T: int, h: int, f: int, E: int, k: int, capacity_factor: float, act: str) -> int:
+    """Bytes of the pre-activation context that the training forward writes."""
+    return lib().moe_layer_preact_bytes(T, h, f, E, k, float(capacity_factor), _ACT[act])
+
+
 def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float, act: str,
                   ws=None, y=None, aux=None, counts=None, events=None, jitter=None, noise=None,
-                  temperature: float = 1.0, uniform: bool = False):
+                  temperature: float = 1.0, uniform: bool = False, preact=None):
     """The whole layer.  Returns ``(y, aux_loss, counts)``.  Pass preallocated
     ``ws``/``y``/``aux``/``counts`` to avoid allocations in a timed loop.
     ``events``: a ctypes array of ``len(LAYER_STAGES) + 1`` hipEvent_t handles to
     record between the stages (the measurement variant of the entry point).
-    ``jitter``/``noise``/``temperature``/``uniform``: the router variants (see route)."""
+    ``jitter``/``noise``/``temperature``/``uniform``: the router variants (see route).
+    ``preact``: a uint8 device tensor of ``preact_bytes(...)`` bytes: the training forward,
+    which also saves the up projection's pre-activations there for layer_backward."""
     torch = _torch()
     dev = x.device
     T, h = x.shape
@@ -320,6 +337,8 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
     opts = _opts(jitter, noise, temperature, uniform, x, T, E)
     if opts is not None and events is not None:
         raise ValueError("the measurement entry point takes no router variants")
+    if opts is not None and preact is not None:
+        raise ValueError("the training forward takes no router variants")
     dt = _dt(x)
     a = _ACT[act]
     if ws is None:
@@ -338,7 +357,11 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
         return y, aux, counts
     args = (_p(x), _p(W_gate), _p(logit_bias), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor), a,
             dt, _p(y), _p(aux), _p(counts), _p(ws), ws.numel(), _stream(dev))
-    if events is None:
+    if preact is not None:
+        _check(lib().moe_layer_forward_train(*args[:-1], _p(preact), _nbytes(preact), _stream(dev),
+                                             None if events is None else ctypes.cast(events, _c_void_p)),
+               "moe_layer_forward_train")
+    elif events is None:
         _check(lib().moe_layer_forward(*args), "moe_layer_forward")
     else:
         _check(lib().moe_layer_forward_timed(*args, ctypes.cast(events, _c_void_p)), "moe_layer_forward_timed")
@@ -385,12 +408,13 @@ def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_
 
 
 def layer_backward(x, W_gate, W1, W3, W2, dy, *, k: int, capacity_factor: float, act: str, fwd_ws,
-                   d_aux: float = 0.0, with_w_gate: bool = True, ws=None, out=None, events=None):
+                   d_aux: float = 0.0, with_w_gate: bool = True, ws=None, out=None, events=None, preact=None):
     """Gradients of ``<dy, y> + d_aux * aux`` for the layer_forward call that used the
     workspace ``fwd_ws`` (pass the same inputs).  Returns a dict with ``dx`` (x's dtype)
     and fp32 ``dW_gate`` (or None), ``dW1``, ``dW3`` (None for GELU), ``dW2``.  ``out``:
     preallocated tensors under those names.  ``events``: ``len(BACKWARD_STAGES) + 1``
-    hipEvent_t handles recorded between the stages."""
+    hipEvent_t handles recorded between the stages.  ``preact``: the pre-activations that
+    the training forward (layer_forward with ``preact``) saved; None = recompute them."""
     torch = _torch()
     dev = x.device
     T, h = x.shape
@@ -406,8 +430,9 @@ def layer_backward(x, W_gate, W1, W3, W2, dy, *, k: int, capacity_factor: float,
     o.setdefault("dW3", torch.empty((E, h, f), dtype=torch.float32, device=dev) if act == "swiglu" else None)
     o.setdefault("dW2", torch.empty((E, f, h), dtype=torch.float32, device=dev))
     args = (_p(x), _p(W_gate), _p(W1), _p(W3), _p(W2), T, h, f, E, k, float(capacity_factor), a, dt, _p(dy),
-            float(d_aux), _p(fwd_ws), fwd_ws.numel(), _p(o["dx"]), _p(o["dW_gate"]), _p(o["dW1"]), _p(o["dW3"]),
-            _p(o["dW2"]), _p(ws), ws.numel(), _stream(dev))
+            float(d_aux), _p(fwd_ws), fwd_ws.numel(), _p(preact), 0 if preact is None else _nbytes(preact),
+            _p(o["dx"]), _p(o["dW_gate"]), _p(o["dW1"]), _p(o["dW3"]), _p(o["dW2"]), _p(ws), ws.numel(),
+            _stream(dev))
     if events is None:
         _check(lib().moe_layer_backward(*args), "moe_layer_backward")
     else:

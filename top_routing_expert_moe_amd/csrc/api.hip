@@ -186,7 +186,7 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
                      int R_max, int32_t h, int32_t f, int32_t E, const void* W1, const void* W3, const void* W2,
                      moe_act_t act, moe_dtype_t dt, void* hm, float* part_up, void* out, bool out_f32,
                      float* part_down, bool out_parts, hipStream_t st,
-                     const std::function<bool()>& mark = std::function<bool()>()) {
+                     const std::function<bool()>& mark = std::function<bool()>(), float* save = nullptr) {
   const bool bf = dt == MOE_BF16;
   const int gact = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
   GemmArgs up{};
@@ -204,10 +204,13 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   up.bm = pl.bm;
   up.ksplit = pl.s_up;
   up.act = gact;
+  up.save = bf && pl.s_up <= 1 ? save : nullptr;  // bf16 only (fp32: the caller runs preact_gemms)
   MOE_TRY(launch_gemm(up, bf, st));
-  if (pl.s_up > 1) MOE_TRY(launch_ffn_finish(part_up, pl.s_up, R_max, f, gact, offsets, E, bf, hm, st));
+  if (pl.s_up > 1)
+    MOE_TRY(launch_ffn_finish(part_up, pl.s_up, R_max, f, gact, offsets, E, bf, hm, st, bf ? save : nullptr));
   if (mark && !mark()) return MOE_ERR_DEVICE;
   GemmArgs down = up;
+  down.save = nullptr;
   down.A = hm;
   down.a_rows = nullptr;
   down.W = W2;
@@ -223,6 +226,45 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
     MOE_TRY(launch_ffn_finish(part_down, pl.s_down, R_max, h, ACT_NONE, offsets, E, bf && !out_f32, out, st));
   if (mark && !mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
+}
+
+// The up projection's pre-activations a (| g) as raw fp32 GEMM outputs, into `ag`:
+// bf16 [R_max][n_up * f] (a then g in each row), fp32 [n_up][R_max][f].
+moe_status_t preact_gemms(const void* A, const int* a_rows, const int* offsets, const int* tile_off,
+                          const FfnPlan& pl, int R_max, int32_t h, int32_t f, int32_t E, const void* W1,
+                          const void* W3, moe_act_t act, bool bf, float* ag, hipStream_t st) {
+  GemmArgs up{};
+  up.A = A;
+  up.a_rows = a_rows;
+  up.K = h;
+  up.N = f;
+  up.offsets = offsets;
+  up.tile_off = tile_off;
+  up.E = E;
+  up.R_max = R_max;
+  up.bm = pl.bm;
+  up.ksplit = 1;
+  up.W = W1;
+  up.out = ag;
+  if (bf) {
+    up.W3 = act == MOE_ACT_SWIGLU ? W3 : nullptr;
+    up.act = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
+    up.raw = true;
+    MOE_TRY(launch_gemm(up, true, st));
+  } else {
+    up.act = ACT_NONE;
+    MOE_TRY(launch_gemm(up, false, st));
+    if (act == MOE_ACT_SWIGLU) {
+      up.W = W3;
+      up.out = ag + (size_t)R_max * f;
+      MOE_TRY(launch_gemm(up, false, st));
+    }
+  }
+  return MOE_OK;
+}
+
+size_t preact_bytes(int R_max, int32_t f, moe_act_t act) {
+  return (size_t)R_max * (act == MOE_ACT_SWIGLU ? 2 : 1) * f * 4;
 }
 
 }  // namespace
@@ -446,7 +488,8 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
                                        int32_t f, int32_t E, int32_t k, float capacity_factor, moe_act_t act,
                                        moe_dtype_t dt, void* y, float* aux_loss, int32_t* counts, void* ws,
                                        size_t ws_bytes, hipStream_t stream, hipEvent_t* ev,
-                                       const moe_router_opts_t* opts = nullptr) {
+                                       const moe_router_opts_t* opts = nullptr, float* preact = nullptr,
+                                       size_t preact_len = 0) {
   moe_status_t s = common_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor)) return MOE_ERR_ARG;
@@ -466,6 +509,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   LayerWs w = carve_layer(c, T, h, f, E, k, R_max, pl, dt, act);
   void* xj = has_jitter(opts) ? c.take<char>((size_t)T * h * elem_bytes(dt)) : nullptr;
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  if (preact != nullptr && preact_len < preact_bytes(R_max, f, act)) return MOE_ERR_WORKSPACE;
   int stage = 0;
   // a null array or a null entry records nothing at that point
   auto mark = [&]() -> bool {
@@ -522,8 +566,11 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   if (!mark()) return MOE_ERR_DEVICE;
   moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
                            w.part_up, w.o, true, w.o, true, stream,
-                           ev ? [&]() { return mark(); } : std::function<bool()>());
+                           ev ? [&]() { return mark(); } : std::function<bool()>(), preact);
   if (r != MOE_OK) return r;
+  if (preact != nullptr && !bf)  // fp32: the pre-activations from their own GEMMs
+    MOE_TRY(preact_gemms(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, act, false, preact,
+                         stream));
   MOE_TRY(launch_combine(w.o, true, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
@@ -758,9 +805,10 @@ size_t moe_layer_backward_workspace_bytes(int32_t T, int32_t h, int32_t f, int32
 static moe_status_t layer_backward_impl(const void* x, const float* W_gate, const void* W1, const void* W3,
                                         const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
                                         float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
-                                        float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
-                                        float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
-                                        size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+                                        float d_aux, const void* fwd_ws, size_t fwd_ws_bytes,
+                                        const float* preact, size_t preact_len, void* dx, float* dW_gate,
+                                        float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                                        hipStream_t stream, hipEvent_t* ev) {
   moe_status_t s = common_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor) || !isfinite(d_aux)) return MOE_ERR_ARG;
@@ -781,6 +829,7 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   const int parts = dx_parts(bf, pl, T, h, f, E, k, C, act == MOE_ACT_SWIGLU ? 2 : 1);
   BwdWs b = carve_bwd(c, T, h, f, E, k, R_max, dt, act, parts);
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  if (preact != nullptr && preact_len < preact_bytes(R_max, f, act)) return MOE_ERR_WORKSPACE;
   const int n_up = act == MOE_ACT_SWIGLU ? 2 : 1;
   const int gact = act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
   int stage = 0;
@@ -804,44 +853,16 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   // router: logit gradient of the renormalised selection and of the aux loss
   MOE_TRY(launch_router_bwd(w.logits, w.topk_idx, w.topk_w, b.dw, b.counts, T, E, k, d_aux, b.dl, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  // the up projection's pre-activations a (| g), recomputed
-  const float* pa = b.ag;
-  const float* pg = nullptr;
-  int ld_ag = n_up * f;
-  {
-    GemmArgs up{};
-    up.A = x;
-    up.a_rows = w.perm_token;
-    up.K = h;
-    up.N = f;
-    up.offsets = w.offsets;
-    up.tile_off = w.tile_off;
-    up.E = E;
-    up.R_max = R_max;
-    up.bm = pl.bm;
-    up.ksplit = 1;
-    if (bf) {
-      up.W = W1;
-      up.W3 = act == MOE_ACT_SWIGLU ? W3 : nullptr;
-      up.out = b.ag;
-      up.act = gact;
-      up.raw = true;
-      MOE_TRY(launch_gemm(up, true, stream));
-      pg = b.ag + f;
-    } else {
-      up.act = ACT_NONE;
-      up.W = W1;
-      up.out = b.ag;
-      MOE_TRY(launch_gemm(up, false, stream));
-      if (act == MOE_ACT_SWIGLU) {
-        up.W = W3;
-        up.out = b.ag + (size_t)R_max * f;
-        MOE_TRY(launch_gemm(up, false, stream));
-      }
-      pg = b.ag + (size_t)R_max * f;
-      ld_ag = f;
-    }
+  // the up projection's pre-activations a (| g): saved by the training forward, else
+  // recomputed with the same GEMM
+  const float* ag = preact;
+  if (ag == nullptr) {
+    MOE_TRY(preact_gemms(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, act, bf, b.ag, stream));
+    ag = b.ag;
   }
+  const float* pa = ag;
+  const float* pg = bf ? ag + f : ag + (size_t)R_max * f;
+  const int ld_ag = bf ? n_up * f : f;
   if (!mark()) return MOE_ERR_DEVICE;
   // down projection: dHm = dO W2^T, folded into da (| dg) by the activation's derivative
   BwdNT nt{};
@@ -991,21 +1012,43 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
 moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* W1, const void* W3, const void* W2,
                                 int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float capacity_factor,
                                 moe_act_t act, moe_dtype_t dt, const void* dy, float d_aux, const void* fwd_ws,
-                                size_t fwd_ws_bytes, void* dx, float* dW_gate, float* dW1, float* dW3, float* dW2,
-                                void* ws, size_t ws_bytes, hipStream_t stream) {
+                                size_t fwd_ws_bytes, const float* preact, size_t preact_bytes_, void* dx,
+                                float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
   return layer_backward_impl(x, W_gate, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, dy, d_aux, fwd_ws,
-                             fwd_ws_bytes, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream, nullptr);
+                             fwd_ws_bytes, preact, preact_bytes_, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream,
+                             nullptr);
 }
 
 moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const void* W1, const void* W3,
                                       const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
                                       float capacity_factor, moe_act_t act, moe_dtype_t dt, const void* dy,
-                                      float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
-                                      float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
-                                      hipStream_t stream, hipEvent_t* events) {
+                                      float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, const float* preact,
+                                      size_t preact_bytes_, void* dx, float* dW_gate, float* dW1, float* dW3,
+                                      float* dW2, void* ws, size_t ws_bytes, hipStream_t stream,
+                                      hipEvent_t* events) {
   if (events == nullptr) return MOE_ERR_ARG;
   return layer_backward_impl(x, W_gate, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, dy, d_aux, fwd_ws,
-                             fwd_ws_bytes, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream, events);
+                             fwd_ws_bytes, preact, preact_bytes_, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream,
+                             events);
+}
+
+size_t moe_layer_preact_bytes(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float capacity_factor,
+                              moe_act_t act) {
+  if (common_sizes(T, E, k) != MOE_OK || !act_ok(act) || !isfinite(capacity_factor)) return 0;
+  if (dim_ok(h) != MOE_OK || dim_ok(f) != MOE_OK) return 0;
+  return preact_bytes(rows_max(T, E, k, capacity_of(T, E, k, capacity_factor)), f, act);
+}
+
+moe_status_t moe_layer_forward_train(const void* x, const float* W_gate, const float* logit_bias, const void* W1,
+                                     const void* W3, const void* W2, int32_t T, int32_t h, int32_t f, int32_t E,
+                                     int32_t k, float capacity_factor, moe_act_t act, moe_dtype_t dt, void* y,
+                                     float* aux_loss, int32_t* counts, void* ws, size_t ws_bytes, float* preact,
+                                     size_t preact_bytes_, hipStream_t stream, hipEvent_t* events) {
+  if (preact == nullptr) return MOE_ERR_ARG;
+  if (!aligned16(preact)) return MOE_ERR_UNSUPPORTED;
+  return layer_forward_impl(x, W_gate, logit_bias, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, y,
+                            aux_loss, counts, ws, ws_bytes, stream, events, nullptr, preact, preact_bytes_);
 }
 
 moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const float* logit_bias, const void* W1,

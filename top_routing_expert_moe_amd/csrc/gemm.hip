@@ -159,7 +159,7 @@ template <int BMT, int ACT, bool GATHER, typename OT, bool SPLIT, int BNT = BN, 
 __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__ A, const int* __restrict__ a_rows,
                                           const bf16_t* __restrict__ W, const bf16_t* __restrict__ W3, int K,
                                           int N, OT* __restrict__ out, int R_max, int e, int row0, int row_end,
-                                          int n0, int ks, int Kc) {
+                                          int n0, int ks, int Kc, float* __restrict__ save) {
   static_assert(!SPLIT || std::is_same<OT, float>::value, "K-split parts are fp32");
   constexpr int NSTAGE = CFG::NSTAGE, NSW = CFG::NSW, SPREAD = CFG::SPREAD;
   static_assert(NSW == NSTAGE || (NSW == 3 && NSTAGE == 2), "stage counts");
@@ -410,6 +410,17 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 #pragma unroll
           for (int p = 0; p < 4; ++p) v[p] = silu_fast(acc[ib][jb][4 * q + p]) * acc[ib + IB / 2][jb][4 * q + p];
           store4(orow + col, v);
+          if (save != nullptr) {  // the pre-activations a | g, as the raw layout holds them
+            float* srow = save + (size_t)r * 2 * N;
+            float a4[4], g4[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              a4[p] = acc[ib][jb][4 * q + p];
+              g4[p] = acc[ib + IB / 2][jb][4 * q + p];
+            }
+            store4(srow + col, a4);
+            store4(srow + N + col, g4);
+          }
         }
     } else {
 #pragma unroll
@@ -425,6 +436,12 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
             v[p] = ACT == ACT_GELU ? gelu_erf(z) : z;
           }
           store4(orow + col, v);
+          if (ACT == ACT_GELU && save != nullptr) {
+            float a4[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) a4[p] = acc[ib][jb][4 * q + p];
+            store4(save + (size_t)r * N + col, a4);
+          }
         }
     }
   }
@@ -440,7 +457,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
-    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh) {
+    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, float* __restrict__ save) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
   // ---- tile schedule (XCD-aware), exits for surplus workgroups
@@ -465,11 +482,14 @@ gemm_bf16_kernel(
   const int rows = min(fh, offsets[e + 1] - row0);
   const int n0 = nt * NO;
   if (rows > 128)
-    gemm_tile<256, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc);
+    gemm_tile<256, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc,
+                                           save);
   else if (rows > 32)
-    gemm_tile<128, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc);
+    gemm_tile<128, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc,
+                                           save);
   else
-    gemm_tile<32, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc);
+    gemm_tile<32, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc,
+                                          save);
 }
 
 // The same grouped GEMM when every m-tile has at most 32 rows (fh = 32): wide tiles.
@@ -478,7 +498,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 gemm_bf16_wide_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
-    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh) {
+    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, float* __restrict__ save) {
   using CFG = TileCfgWide32<SPLIT>;
   constexpr int LDS = (CFG::NSW * KB * BNW + CFG::NSTAGE * 32 * KB) * 2;
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
@@ -506,7 +526,7 @@ gemm_bf16_wide_kernel(
   const int row0 = offsets[e] + mt_local * fh;
   const int rows = min(fh, offsets[e + 1] - row0);
   gemm_tile<32, ACT, GATHER, OT, SPLIT, BNW, CFG>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows,
-                                                  nt * NO, ks, Kc);
+                                                  nt * NO, ks, Kc, save);
 }
 
 // ---------------------------------------------------------------------------
@@ -604,20 +624,23 @@ hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
   const long long grid = (slots + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
+  float* save = SPLIT ? nullptr : a.save;
   if (wide)
     hipLaunchKernelGGL((gemm_bf16_wide_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                        (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm);
+                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, save);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                        (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm);
+                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, save);
   return hipGetLastError();
 }
 
 template <int ACT, bool G, typename OT>
 hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
   if (a.bm != 256 && a.bm != 128 && a.bm != 32) return hipErrorInvalidValue;
+  // pre-activations are saved by the epilogue of a one-part up projection only
+  if (a.save != nullptr && (a.ksplit > 1 || a.raw || ACT == ACT_NONE)) return hipErrorInvalidValue;
   if (a.ksplit > 1 || a.raw) {
     // K parts: for few rows per expert, where there are too few tiles to fill the chip
     // (or one part of raw accumulators)
@@ -632,7 +655,7 @@ hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
 template <int ACT, typename OT>
 __global__ __launch_bounds__(256) void ffn_finish_kernel(const float* __restrict__ part, int S, int R_max, int N,
                                                          const int* __restrict__ offsets, int E,
-                                                         OT* __restrict__ out) {
+                                                         OT* __restrict__ out, float* __restrict__ save) {
   const int R = offsets[E];
   const int groups = N >> 2;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -653,6 +676,10 @@ __global__ __launch_bounds__(256) void ffn_finish_kernel(const float* __restrict
   for (int i = 0; i < 4; ++i)
     v[i] = ACT == ACT_SWIGLU ? silu_fast(a[i]) * g[i] : (ACT == ACT_GELU ? gelu_erf(a[i]) : a[i]);
   store4(out + (size_t)r * N + c, v);
+  if (ACT != ACT_NONE && save != nullptr) {  // the summed pre-activations, in the raw layout
+    *(floatx4*)(save + (size_t)r * NWM * N + c) = a;
+    if (NWM == 2) *(floatx4*)(save + (size_t)r * NWM * N + N + c) = g;
+  }
 }
 
 template <int ACT, bool G>
@@ -683,14 +710,14 @@ hipError_t dispatch_act(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_ffn_finish(const float* part, int S, int R_max, int N, int act, const int* offsets, int E,
-                             bool out_bf16, void* out, hipStream_t st) {
+                             bool out_bf16, void* out, hipStream_t st, float* save) {
   // grid over the row bound; rows past offsets[E] exit
   const int64_t n = (int64_t)R_max * (N / 4);
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (grid == 0) return hipSuccess;
 #define MOE_FIN(A, OT)                                                                              \
   hipLaunchKernelGGL((ffn_finish_kernel<A, OT>), dim3(grid), dim3(256), 0, st, part, S, R_max, N, offsets, E, \
-                     (OT*)out)
+                     (OT*)out, save)
   switch (act) {
     case ACT_NONE: if (out_bf16) MOE_FIN(ACT_NONE, bf16_t); else MOE_FIN(ACT_NONE, float); break;
     case ACT_GELU: if (out_bf16) MOE_FIN(ACT_GELU, bf16_t); else MOE_FIN(ACT_GELU, float); break;

@@ -101,6 +101,9 @@ struct GemmArgs {
   // raw: write the raw fp32 accumulators in the K-part layout (one part when ksplit <= 1),
   // no activation: the pre-activations [a | g] for the backward pass
   bool raw;
+  // bf16 up projection (act SwiGLU or GELU) without K parts: not null = also write the
+  // fp32 pre-activations here, in the raw layout ([R_max][2N] a | g, or [R_max][N])
+  float* save;
 };
 
 // Tile height and K splits of one expert FFN (both GEMMs), a pure function of the sizes.
@@ -115,8 +118,10 @@ int gemm_bm(bool bf16, double rows_per_expert);
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t st);
 // out[r, :] = act(sum_s part[s][r][:N] (, sum_s part[s][r][N:2N])) for r < offsets[E];
 // act: ACT_NONE, ACT_GELU or ACT_SWIGLU; out is bf16 when out_bf16 else fp32.
+// (save, act SwiGLU or GELU: the summed pre-activations are also written there, in the
+// raw layout)
 hipError_t launch_ffn_finish(const float* part, int S, int R_max, int N, int act, const int* offsets, int E,
-                             bool out_bf16, void* out, hipStream_t st);
+                             bool out_bf16, void* out, hipStream_t st, float* save = nullptr);
 
 // ---- combine
 // O is fp32 when o_f32, else the y dtype.  With o_parts > 1 (fp32 only), O holds o_parts
