@@ -244,9 +244,9 @@ moe_status_t moe_layer_forward_train(const void* x, const float* W_gate, const f
 
 /* Measurement variant of moe_layer_backward: events[0] before the first kernel, then one
  * after each stage (combine adjoint with the counts and tile lists, router adjoint,
- * pre-activation recompute (empty with preact), down-projection data gradient with the activation's
- * derivative, down-projection weight gradient, up-projection data gradient, up-projection
- * weight gradients, router GEMMs, dx).  `events` (not null: MOE_ERR_ARG) holds
+ * pre-activation recompute (empty with preact), down-projection data gradient with the
+ * activation's derivative, down-projection weight gradient, up-projection data gradient,
+ * up-projection weight gradients, router GEMMs, dx).  `events` (not null: MOE_ERR_ARG) holds
  * MOE_BACKWARD_STAGES + 1 entries, each a hipEvent_t or null (nothing recorded there). */
 #define MOE_BACKWARD_STAGES 9
 moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const void* W1, const void* W3,
