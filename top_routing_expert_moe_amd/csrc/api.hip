@@ -568,9 +568,10 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
                            w.part_up, w.o, true, w.o, true, stream,
                            ev ? [&]() { return mark(); } : std::function<bool()>(), preact);
   if (r != MOE_OK) return r;
-  if (preact != nullptr && !bf)  // fp32: the pre-activations from their own GEMMs
-    MOE_TRY(preact_gemms(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, act, false, preact,
-                         stream));
+  if (preact != nullptr && !bf) {  // fp32: the pre-activations from their own GEMMs
+    r = preact_gemms(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, act, false, preact, stream);
+    if (r != MOE_OK) return r;
+  }
   MOE_TRY(launch_combine(w.o, true, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
@@ -857,7 +858,9 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   // recomputed with the same GEMM
   const float* ag = preact;
   if (ag == nullptr) {
-    MOE_TRY(preact_gemms(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, act, bf, b.ag, stream));
+    const moe_status_t r =
+        preact_gemms(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, act, bf, b.ag, stream);
+    if (r != MOE_OK) return r;
     ag = b.ag;
   }
   const float* pa = ag;
