@@ -101,6 +101,7 @@ def _check_all(w, host, g, gl, dy_host, tokens=None, experts=None, with_w_gate=T
     (800, 768, 1024, 4, 2, 0.0, "swiglu", "bf16"),   # 256-row tiles: pipelined NT in two K parts, ragged segments
     (700, 512, 1024, 2, 1, 0.0, "gelu", "bf16"),     # 256-row tiles, GELU derivative in the pipelined NT
     (40, 256, 256, 16, 1, 0.0, "swiglu", "bf16"),    # pipelined TN with empty experts (zero gradients)
+    (64, 128, 128, 256, 16, 0.0, "swiglu", "bf16"),  # the largest E and k the library takes
 ])
 def test_backward_edge_cases(T, h, f, E, k, cf, act, dtype):
     _say(f"backward edge T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")

@@ -115,6 +115,7 @@ def _perm_cases():
     cases = []
     cases.append(("uniform", mw.uniform_assignment(4096, 8, 2), 8, 0.0))
     cases.append(("uniform-e256", mw.uniform_assignment(4096, 256, 8), 256, 0.0))
+    cases.append(("e256-k16-cap", mw.uniform_assignment(1000, 256, 16), 256, 0.5))  # largest E and k
     one = np.zeros((3000, 1), dtype=np.int32)
     cases.append(("all-to-one", one, 16, 0.0))
     cases.append(("all-to-one-cap", one, 16, 1.0))          # C = 187: almost all dropped

@@ -89,6 +89,8 @@ def test_layer_forward_deterministic():
     (500, 128, 256, 16, 2, 0.25, "swiglu", "f32"),   # drops in fp32
     (20, 1024, 2048, 8, 2, 0.0, "swiglu", "bf16"),   # few rows per expert: K-split GEMMs, parts added in combine
     (40, 2048, 1024, 6, 2, 0.5, "gelu", "bf16"),     # K-split GEMMs with drops
+    (64, 128, 128, 256, 16, 0.0, "swiglu", "bf16"),  # the largest E and k the library takes
+    (96, 64, 128, 256, 16, 1.0, "gelu", "f32"),      # ... in fp32, with drops
 ])
 def test_layer_edge_cases(T, h, f, E, k, cf, act, dtype):
     import math
