@@ -14,11 +14,13 @@
 //               loss d_aux (E/T) p_i (f_i - sum_e f_e p_e) with the full softmax p;
 //               dW_gate = x^T dl, dx += dl W_gate^T.
 //
-// The GEMMs here run on the vector ALUs in fp32 (64 x 64 tiles, 4 x 4 per thread),
-// reading bf16 or fp32 operands: grouped "NT" products C[r, n] = sum_k A[r, k] B_e[n, k]
-// over the expert segments (the data-gradient GEMMs; B is the weight read along its
-// contiguous dimension) and grouped "TN" products C_e[m, n] = sum_r A[row(r), m] B[r, n]
-// over each expert's rows (the weight-gradient GEMMs).
+// The GEMMs are grouped "NT" products C[r, n] = sum_k A[r, k] B_e[n, k] over the expert
+// segments (the data gradients; B is the weight read along its contiguous dimension) and
+// grouped "TN" products C_e[m, n] = sum_r A[row(r), m] B[r, n] over each expert's rows
+// (the weight gradients).  bf16 operands run on the matrix cores: the large products on
+// bwd_tile_kernel (the expert GEMM's direct-to-LDS pipeline), the others on
+// gemm_bwd_mfma_kernel (register-staged); fp32 operands, and the router's small products,
+// on the vector ALUs in fp32 (64 x 64 tiles, 4 x 4 per thread).
 #include "common.h"
 #include "kernels.h"
 
@@ -503,7 +505,7 @@ gemm_bwd_mfma_kernel(const bf16_t* __restrict__ A, int lda, const int* __restric
 }
 
 // ---------------------------------------------------------------------------
-// The large products (both tile extents 256, bf16 operands) with the expert GEMM's
+// The large products (bf16 operands; tiles of 256 P x 256 or 128 Q) with the expert GEMM's
 // pipeline: operands go from global memory straight into LDS (global_load_lds_dwordx4,
 // no register staging), the P operand three stages ahead and the Q operand two, and
 // each wave waits only for its own copies of the stage it is about to read.
