@@ -559,10 +559,20 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.blk_base = w.blk_base;
   sa.tile_off = w.tile_off;
   sa.aux = aux_loss ? aux_loss : w.aux;
+  // one block of tokens (decode): the scatter runs inside the scan's workgroup
+  sa.scatter = route_blocks(T) == 1;
+  if (sa.scatter) {
+    sa.topk_idx = w.topk_idx;
+    sa.nbits = expert_bits(E);
+    sa.slot_pos = w.slot_pos;
+    sa.sorted_slot = w.sorted_slot;
+    sa.perm_token = w.perm_token;
+  }
   MOE_TRY(launch_scan(sa, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
-                         w.perm_token, stream));
+  if (!sa.scatter)
+    MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
+                           w.perm_token, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   moe_status_t r = run_ffn(x, w.perm_token, w.offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, W2, act, dt, w.hm,
                            w.part_up, w.o, true, w.o, true, stream,

@@ -62,8 +62,22 @@ struct ScanArgs {
   // capacity, or the largest count when C == INT32_MAX; the bucket size goes to *cap_out
   bool binned;
   int* cap_out;            // scalar or null
+  // one block of tokens (nhb == 1, not binned): the stable scatter runs in the same
+  // workgroup once the offsets are known (the arguments of launch_scatter)
+  bool scatter;
+  const int* topk_idx;
+  int nbits;               // bits of an expert id
+  int* slot_pos;
+  int* sorted_slot;
+  int* perm_token;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+// bits of an expert id (at least 1): the scatter's match by ballots
+inline int expert_bits(int E) {
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  return nbits;
+}
 // x_bins[r] = x[perm_token[r]] for filled bucket rows, zero for the rest of the E buckets
 // (bucket size offsets[1] - offsets[0], fill min(counts[e], size)); rows >= offsets[E] untouched
 hipError_t launch_binned_gather(const void* x, const int* perm_token, const int* offsets, const int* counts, int E,
