@@ -539,6 +539,22 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
     MOE_TRY(launch_jitter(x, opts->jitter, (int64_t)T * h, bf, xj, stream));
     ra.x = xj;
   }
+  // one block of tokens (decode): the selection kernel also does the scan and the scatter
+  const bool one_block = route_blocks(T) == 1;
+  SmallPermute sp{};
+  if (one_block) {
+    sp.C = (int)C;
+    sp.BM = pl.bm;
+    sp.nbits = expert_bits(E);
+    sp.counts = counts ? counts : w.counts;
+    sp.offsets = w.offsets;
+    sp.tile_off = w.tile_off;
+    sp.aux = aux_loss ? aux_loss : w.aux;
+    sp.slot_pos = w.slot_pos;
+    sp.sorted_slot = w.sorted_slot;
+    sp.perm_token = w.perm_token;
+    ra.permute = &sp;
+  }
   MOE_TRY(launch_logits(ra, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   MOE_TRY(launch_select(ra, stream));
@@ -559,18 +575,9 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.blk_base = w.blk_base;
   sa.tile_off = w.tile_off;
   sa.aux = aux_loss ? aux_loss : w.aux;
-  // one block of tokens (decode): the scatter runs inside the scan's workgroup
-  sa.scatter = route_blocks(T) == 1;
-  if (sa.scatter) {
-    sa.topk_idx = w.topk_idx;
-    sa.nbits = expert_bits(E);
-    sa.slot_pos = w.slot_pos;
-    sa.sorted_slot = w.sorted_slot;
-    sa.perm_token = w.perm_token;
-  }
-  MOE_TRY(launch_scan(sa, stream));
+  if (!one_block) MOE_TRY(launch_scan(sa, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  if (!sa.scatter)
+  if (!one_block)
     MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
                            w.perm_token, stream));
   if (!mark()) return MOE_ERR_DEVICE;

@@ -10,6 +10,21 @@ namespace moe {
 // ---- router
 constexpr int kSelTokens = 64;  // tokens per selection / histogram / scatter block
 
+// The outputs of the scan and the scatter, for a selection kernel that produces them itself
+// when the tokens are one block (T <= kSelTokens): see launch_select.
+struct SmallPermute {
+  int C;                   // capacity, INT32_MAX = none
+  int BM;                  // rows per GEMM tile for tile_off; 0 = no tile list
+  int nbits;               // bits of an expert id (expert_bits)
+  int* counts;             // [E] pre-drop
+  int* offsets;            // [E+1] over kept
+  int* tile_off;           // [E+1] or null
+  float* aux;              // scalar or null
+  int* slot_pos;           // [T*k]
+  int* sorted_slot;        // [T*k]
+  int* perm_token;         // [T*k]
+};
+
 struct RouteArgs {
   const void* x;          // [T,h] fp32 or bf16
   const float* W_gate;    // [h,E]
@@ -30,6 +45,8 @@ struct RouteArgs {
   const float* noise = nullptr;
   float inv_temp = 1.0f;
   bool uniform = false;
+  // not null and T <= kSelTokens: the selection kernel also does the scan and the scatter
+  const SmallPermute* permute = nullptr;
 };
 // router-input jitter: out = x * u elementwise in the storage dtype (n_elems * elem size % 16 == 0)
 hipError_t launch_jitter(const void* x, const void* u, int64_t n_elems, bool bf16, void* out, hipStream_t st);
@@ -62,14 +79,6 @@ struct ScanArgs {
   // capacity, or the largest count when C == INT32_MAX; the bucket size goes to *cap_out
   bool binned;
   int* cap_out;            // scalar or null
-  // one block of tokens (nhb == 1, not binned): the stable scatter runs in the same
-  // workgroup once the offsets are known (the arguments of launch_scatter)
-  bool scatter;
-  const int* topk_idx;
-  int nbits;               // bits of an expert id
-  int* slot_pos;
-  int* sorted_slot;
-  int* perm_token;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 // bits of an expert id (at least 1): the scatter's match by ballots

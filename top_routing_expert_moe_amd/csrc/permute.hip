@@ -25,6 +25,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "permute_dev.h"
 
 namespace moe {
 
@@ -69,84 +70,6 @@ __device__ int block_inclusive_scan256(int v, int* sh) {
 }
 
 constexpr int kScanThreads = 1024;
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane, int width) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (o < width && (lane % width) >= o) v += t;
-  }
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-// The stable scatter of token block `blk` (assignments blk * pb .. blk * pb + pb - 1, pb =
-// kSelTokens * k), by the first 256 threads of the workgroup; every thread of the workgroup
-// reaches the barriers.  bb[e]: the rank origin of expert e's assignments in this block
-// (null: zero, the first block); offsets may point to LDS.
-__device__ __forceinline__ void scatter_block(int blk, const int* __restrict__ topk_idx, int T, int E, int k,
-                                              int nbits, int C, const int* offsets, const int* __restrict__ bb,
-                                              int* __restrict__ slot_pos, int* __restrict__ sorted_slot,
-                                              int* __restrict__ perm_token) {
-  __shared__ int run[256];
-  __shared__ int wcnt[4][256];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool act = tid < 256;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  if (act) run[tid] = 0;
-  const int64_t n = (int64_t)T * k;
-  const int pb = kSelTokens * k;
-  const int64_t base = (int64_t)blk * pb;
-  for (int r0 = 0; r0 < pb; r0 += 256) {
-    if (act) {
-      wcnt[0][tid] = 0;
-      wcnt[1][tid] = 0;
-      wcnt[2][tid] = 0;
-      wcnt[3][tid] = 0;
-    }
-    __syncthreads();
-    const int64_t s = base + r0 + tid;
-    const bool in = act && (r0 + tid < pb) && s < n;
-    int e = -1;
-    if (in) e = topk_idx[s];
-    const bool valid = (unsigned)e < (unsigned)E;
-    int rank_w = 0;
-    if (act) {  // whole waves: the ballots see only this block's lanes
-      uint64_t match = __ballot(valid);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const bool on = valid && ((e >> bit) & 1);
-        const uint64_t b = __ballot(on);
-        match &= on ? b : ~b;
-      }
-      rank_w = __popcll(match & lt_mask);
-      if (valid && rank_w == 0) wcnt[w][e] = __popcll(match);
-    }
-    __syncthreads();
-    if (valid) {
-      int pre = run[e];
-      for (int q = 0; q < w; ++q) pre += wcnt[q][e];
-      const int g = (bb != nullptr ? bb[e] : 0) + pre + rank_w;  // rank among all earlier assignments to e
-      if (g < C) {
-        const int row = offsets[e] + g;
-        slot_pos[s] = row;
-        sorted_slot[row] = (int)s;
-        perm_token[row] = (int)(s / k);
-      } else {
-        slot_pos[s] = -1;
-      }
-    } else if (in) {
-      slot_pos[s] = -1;
-    }
-    __syncthreads();
-    if (act) run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
-    __syncthreads();
-  }
-}
 
 // One workgroup: per-(block, expert) rank origins, pre-drop counts, capacity-clamped
 // offsets, the m-tile list and the aux loss.  Every sum has a fixed order (wave shuffles
@@ -229,14 +152,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       ik += wsum[0][w];
       im += wsum[1][w];
     }
-  }
-  if (a.scatter) {
-    // one block of tokens: its scatter here, with the offsets from LDS (its ranks start at 0)
-    __shared__ int off_sh[256];
-    if (tid < E) off_sh[tid] = ik - kept;
-    __syncthreads();
-    scatter_block(0, a.topk_idx, a.T, E, a.k, a.nbits, a.C, off_sh, nullptr, a.slot_pos, a.sorted_slot,
-                  a.perm_token);
   }
   if (tid < E) {
     a.counts[tid] = cnt;
@@ -365,7 +280,6 @@ hipError_t launch_hist(const int* topk_idx, int T, int k, int E, int* blk_counts
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
-  if (a.scatter && (a.nhb != 1 || a.binned)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -26,6 +26,7 @@
 //    assignments per expert (the histogram) and sums the softmax per expert.
 #include "common.h"
 #include "kernels.h"
+#include "permute_dev.h"
 
 namespace moe {
 
@@ -280,12 +281,15 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // logits * inv_temp (selection ranks the logits themselves, the same order for any
 // positive temperature); with `uniform` the ids written (and counted) are (t*k + j) % E
 // while the weights stay those of the real top-k.
-template <int NV, int G, bool HSPLIT, int NWS = 4>
+// FUSE (T <= kSelTokens, one workgroup): the workgroup then also does the scan and the
+// scatter (single_block_permute) into the outputs named by sp.
+template <int NV, int G, bool HSPLIT, int NWS = 4, bool FUSE = false>
 __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ logits, const float* __restrict__ lpart,
                                                      int SH, int T, int E, int k,
                                                      int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                      float* __restrict__ prob_part, int* __restrict__ blk_counts,
-                                                     const float* __restrict__ noise, float inv_temp, int uniform) {
+                                                     const float* __restrict__ noise, float inv_temp, int uniform,
+                                                     SmallPermute sp) {
   static_assert(G == 64 || NV == 1, "several values per lane only with whole-wave groups");
   constexpr int TPW = 64 / G;                  // tokens per wave and pass
   constexpr int NQ = kSelTokens / NWS / TPW;   // passes per wave
@@ -406,6 +410,17 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
       prob_part[(size_t)blockIdx.x * E + e] = sum;
     }
   if (blk_counts != nullptr && tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
+  if (FUSE) {
+    __shared__ float psum_sh[256];  // this block's softmax sums, as prob_part holds them
+    for (int e = tid; e < E; e += NWS * 64) {
+      float sum = pp[0][e];
+#pragma unroll
+      for (int q = 1; q < NWS; ++q) sum += pp[q][e];
+      psum_sh[e] = sum;
+    }
+    __syncthreads();  // also makes this block's topk_idx visible to the whole workgroup
+    single_block_permute(cnt, psum_sh, T, E, k, topk_idx, sp);
+  }
 }
 
 // prob_sum[e] = sum over blocks of prob_part[b][e], in block order
@@ -524,10 +539,18 @@ hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
   // partial logits from a split contraction (never with logits given as input)
   const int SH = a.logits_in ? 1 : route_hsplit(a.T, a.h, a.E, a.bf16);
   const float* lpart = SH > 1 ? route_lpart(a) : nullptr;
-#define MOE_SELECT_W(NV, G, HS, NWS)                                                                       \
-  hipLaunchKernelGGL((select_kernel<NV, G, HS, NWS>), grid, dim3(NWS * 64), 0, st, a.logits, lpart, SH, a.T, \
-                     a.E, a.k, a.topk_idx, a.topk_w, a.prob_part, a.blk_counts, a.noise, a.inv_temp,  \
-                     a.uniform ? 1 : 0)
+  const bool fuse = a.permute != nullptr;
+  if (fuse && (route_blocks(a.T) != 1 || a.blk_counts == nullptr)) return hipErrorInvalidValue;
+  const SmallPermute sp = fuse ? *a.permute : SmallPermute{};
+#define MOE_SELECT_F(NV, G, HS, NWS, F)                                                                          \
+  hipLaunchKernelGGL((select_kernel<NV, G, HS, NWS, F>), grid, dim3(NWS * 64), 0, st, a.logits, lpart, SH, a.T, \
+                     a.E, a.k, a.topk_idx, a.topk_w, a.prob_part, a.blk_counts, a.noise, a.inv_temp,       \
+                     a.uniform ? 1 : 0, sp)
+#define MOE_SELECT_W(NV, G, HS, NWS)              \
+  do {                                            \
+    if (fuse) MOE_SELECT_F(NV, G, HS, NWS, true); \
+    else MOE_SELECT_F(NV, G, HS, NWS, false);     \
+  } while (0)
 #define MOE_SELECT(NV, G, HS) MOE_SELECT_W(NV, G, HS, 4)
   if (SH > 1 && a.E > 16) return hipErrorInvalidValue;  // the h split is for few experts only
   if (a.E <= 4) { if (SH > 1) MOE_SELECT(1, 4, true); else MOE_SELECT(1, 4, false); }
@@ -540,6 +563,7 @@ hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
   else MOE_SELECT_W(4, 64, false, 16);
 #undef MOE_SELECT
 #undef MOE_SELECT_W
+#undef MOE_SELECT_F
   return hipGetLastError();
 }
 
