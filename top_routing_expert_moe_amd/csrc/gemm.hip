@@ -10,11 +10,13 @@
 //  * one launch covers all experts: the m-tile -> expert map comes from the
 //    device-side tile_off[] (exclusive scan of ceil(rows_e / BM)), so there is
 //    no host synchronisation and experts with no rows cost nothing;
-//  * workgroup tile BM rows x 256 weight columns x 64 k per LDS stage, 4 waves,
+//  * workgroup tile BM rows x 256 weight columns x 64 k per LDS stage, 8 waves,
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  BM follows the expected
-//    rows per expert: 256 (2 x 2 waves of 128 x 128, compute-bound prefill), 128
-//    or 32 (1 x 4 waves of BM x 64, where the weights dominate and a deeper
-//    pipeline keeps more of them in flight);
+//    rows per expert: 256 (4 x 2 waves of 64 x 128, compute-bound prefill) or 128
+//    (2 x 4 waves of 64 x 64); an expert's last m-tile runs the shape its rows
+//    need.  When every m-tile has at most 32 rows (decode) the launch only
+//    streams weights, and its tiles are 32 rows x 512 weight columns (1 x 8 waves
+//    of 32 x 64), so that each k row of a weight stage is a longer contiguous run;
 //  * both operands go from global memory straight into LDS (global_load_lds,
 //    16 B per lane) with no register staging.  The weights stay [K, N] with N
 //    contiguous in LDS and the MFMA operand (8 consecutive k of one column) is
@@ -93,9 +95,9 @@ constexpr int NIW = 32 / kWaves;   // weight copies (1 KiB each, 32 per stage) p
 // Tile shapes by token-tile height: the wave grid (waves along m x along n) and the
 // number of LDS stages that fit.  Eight waves, two per SIMD: while one waits on a barrier,
 // an LDS read or a copy, the other issues MFMAs.  256 rows: 4 x 2 waves of 64 x 128
-// (prefill); 128 rows: 2 x 4 waves of 64 x 64; 32 rows: 1 x 4 waves of 32 x 64 compute
-// (the other four only copy: these tiles stream weights, and the deeper pipeline keeps
-// more weight bytes in flight).
+// (prefill); 128 rows: 2 x 4 waves of 64 x 64; 32 rows (an expert's last m-tile in a
+// launch of 128- or 256-row tiles): 1 x 4 waves of 32 x 64 compute, the other four only
+// copy (such tiles stream weights, and the deeper pipeline keeps more bytes in flight).
 // SPREAD: the next stage's copies are issued between the first SPREAD groups of MFMAs
 // of the current stage (issuing them early leaves them the most time to land; spreading
 // them keeps the MFMA issue from stalling behind a full memory queue).
