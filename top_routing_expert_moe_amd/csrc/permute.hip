@@ -21,6 +21,8 @@
 //             in lower lanes are counted by popcount), then across its 4 waves
 //             and its rounds of 256 through LDS.  Rank = blk_base + in-block rank, so
 //             the result equals a stable sort for any number of blocks.
+// With a single block of tokens the layer's selection kernel runs the scan and the
+// scatter itself (single_block_permute in permute_dev.h).
 #include <limits.h>
 
 #include "common.h"

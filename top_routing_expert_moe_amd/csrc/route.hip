@@ -24,6 +24,9 @@
 //    The key orders by logit (IEEE order, -0 == +0) then by the lower expert
 //    index, so ties are deterministic.  The same kernel counts its block's
 //    assignments per expert (the histogram) and sums the softmax per expert.
+//    Inside the layer, when all tokens are one block (decode), it then also
+//    does the permutation's scan and stable scatter (permute_dev.h), which saves
+//    two launches.
 #include "common.h"
 #include "kernels.h"
 #include "permute_dev.h"
