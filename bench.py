@@ -133,7 +133,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}); the layer's sharding plan is design-only.", flush=True)
         sys.exit(2)
 
