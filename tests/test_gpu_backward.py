@@ -102,6 +102,9 @@ def _check_all(w, host, g, gl, dy_host, tokens=None, experts=None, with_w_gate=T
     (700, 512, 1024, 2, 1, 0.0, "gelu", "bf16"),     # 256-row tiles, GELU derivative in the pipelined NT
     (40, 256, 256, 16, 1, 0.0, "swiglu", "bf16"),    # pipelined TN with empty experts (zero gradients)
     (64, 128, 128, 256, 16, 0.0, "swiglu", "bf16"),  # the largest E and k the library takes
+    (150, 320, 448, 4, 2, 0.0, "swiglu", "bf16"),    # pipelined TN with partial tiles in both weight dimensions
+    (600, 320, 576, 3, 2, 0.5, "gelu", "bf16"),      # ... GELU with drops; 128-row NT tiles, partial in N
+    (1400, 320, 576, 2, 1, 0.9, "gelu", "bf16"),     # 256-row NT tiles, partial in N, with drops
 ])
 def test_backward_edge_cases(T, h, f, E, k, cf, act, dtype):
     _say(f"backward edge T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")
