@@ -748,6 +748,11 @@ bwd_tile_kernel(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict_
     const bf16_t* Pb = Ps[pbuf];
     const bf16_t* Qb = Qs[qbuf];
     constexpr int PARTS = (KB / 16) * IB;
+    // every copy must fall in one of the PARTS groups (issue_part's mapping)
+    constexpr int SP = PARTS < 8 ? PARTS : 8;
+    static_assert((NIQ - 1) * (SP / 2) / NIQ < SP / 2 &&
+                      SP / 2 + (NIP - 1) * (PARTS >= 2 * SP ? SP : SP / 2) / NIP < PARTS,
+                  "copy groups");
 #pragma unroll
     for (int kh = 0; kh < KB / 16; ++kh) {
       bf16x8 a[IB], b[JB];

@@ -285,6 +285,12 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     const bf16_t* Wb = Ws[wbuf];
     const bf16_t* Xb = Xs[xbuf];
     constexpr int PARTS = (KB / 16) * IB;
+    // every copy must fall in one of the PARTS groups (issue_part's mapping)
+    constexpr int SP = PARTS < SPREAD ? PARTS : (SPREAD > 0 ? SPREAD : 1);
+    static_assert(SPREAD == 0 || (NSW != NSTAGE
+                                      ? SP / 2 + (NIWT - 1) * SP / NIWT < PARTS && (NIX - 1) * (SP / 2) / NIX < SP / 2
+                                      : (NIWT - 1) * SP / NIWT < PARTS && (NIX - 1) * SP / NIX < PARTS),
+                  "copy groups");
     const bool mf = NCW == kWaves || uwave < NCW;  // waves past the grid only copy
     if (SPREAD == 0) issue_part(xkt, xnb, wkt, wnb, 0, 1, all);  // all copies before the first LDS read
 #pragma unroll
