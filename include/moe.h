@@ -226,7 +226,9 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
 
 /* Training forward: moe_layer_forward (same arguments and results) that also writes the
  * up projection's fp32 pre-activations a (| g) of every kept assignment to `preact`, so
- * that moe_layer_backward can read them instead of recomputing them.  The buffer is an
+ * that moe_layer_backward can read them instead of recomputing them.  (They are the
+ * inputs of the expert's activation: x W1[e] and, for SwiGLU, x W3[e], [CANN] section 7
+ * and [MB] section 4.3.)  The buffer is an
  * opaque context of moe_layer_preact_bytes(...) bytes (R_max * f * 4, twice that for
  * SwiGLU, R_max the bound on kept assignments), 16-byte aligned (MOE_ERR_UNSUPPORTED
  * otherwise), caller-owned.  Its values equal the recomputed ones when the up projection
