@@ -1,6 +1,7 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library
- * (libmoe_mi355x.so).
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer library (libmoe_mi355x.so):
+ * the forward pass, its fixed-capacity variant and router variants, and the
+ * backward pass.
  *
  * The layer: a router picks, for every token, the k best of E experts; the
  * token is sent through those experts' MLPs and their outputs are summed with
@@ -15,6 +16,8 @@
  *          sections 3, 4.1-4.6.
  *   [CAI]  "在 Colossal-AI 中为你的模型集成混合专家（MoE）...": SparseMLP data
  *          flow, MoeLoss.
+ *   [CANN] "MoE 路由算子到底在做什么？一次拆透 ops-transformer 的核心机制":
+ *          sections 2-3, 7 (SwiGLU experts).
  *
  * Conventions for every entry point
  *   - Tensor arguments are DEVICE pointers to row-major, contiguous arrays,
