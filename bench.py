@@ -301,8 +301,20 @@ def main():
     bytes_up = active * n_up * h * f * es + R * h * es + R * f * es
     bytes_down = active * f * h * es + R * f * es + R * h * 4
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    kname = ("expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue, " if w.act == "swiglu"
-             else "expert up-projection (grouped bf16 MFMA GEMM, GELU epilogue, ")
+    # the library's tile choice: 32-row tiles when the planned rows per expert are <= 48
+    # (T*k/E, at most C; the bucket size in the binned layout with a positive factor); with
+    # SwiGLU those write the raw a and g (512-column tiles of W1 or W3 alone) and a second
+    # pass applies the activation
+    rpe = T * k / E
+    if binned and w.cf > 0:
+        rpe = float(moe.binned_capacity_max(T, E, k, w.cf, args.min_capacity))
+    elif not binned and moe.capacity(T, E, k, w.cf) is not None:
+        rpe = min(rpe, float(moe.capacity(T, E, k, w.cf)))
+    if bf and w.act == "swiglu" and rpe <= 48:
+        kname = "expert up-projection (grouped bf16 MFMA GEMM writing raw a and g, then the SwiGLU pass, "
+    else:
+        kname = ("expert up-projection (grouped bf16 MFMA GEMM, SwiGLU epilogue, " if w.act == "swiglu"
+                 else "expert up-projection (grouped bf16 MFMA GEMM, GELU epilogue, ")
     kname += "over the E x C buckets)" if binned else "gather fused)"
     if not bf:  # the fp32 GEMM runs on the vector ALUs
         achieved = flops_up / up_s / 1e12

@@ -117,13 +117,27 @@ PermWs carve_perm(Carve& c, int32_t T, int32_t E, int32_t k) {
 
 size_t up_cols(moe_act_t act, int32_t f) { return (size_t)(act == MOE_ACT_SWIGLU ? 2 : 1) * f; }
 
+// Few rows per expert (32-row tiles, the weight-streaming case), bf16 SwiGLU, one K part:
+// the up projection writes its raw accumulators [a | g] from tiles of 512 columns of W1
+// alone or W3 alone -- 1 KiB weight runs instead of two 512-byte runs -- and
+// launch_ffn_finish applies the activation.  (Measured at 16 rows per expert, h = 4096,
+// f = 14336, E = 8: the up projection with its finishing pass takes 0.314 ms instead of
+// 0.324 ms, the layer 0.484 instead of 0.491 ms.)
+bool sep_up(const FfnPlan& pl, moe_act_t act, moe_dtype_t dt) {
+  return dt == MOE_BF16 && act == MOE_ACT_SWIGLU && pl.bm == 32 && pl.s_up <= 1;
+}
+// fp32 parts of the up projection in the workspace (0: it writes Hm directly)
+int up_parts(const FfnPlan& pl, moe_act_t act, moe_dtype_t dt) {
+  return pl.s_up > 1 ? pl.s_up : (sep_up(pl, act, dt) ? 1 : 0);
+}
+
 struct FfnWs { int* tile_off; void* hm; float* part_up; float* part_down; };
 FfnWs carve_ffn(Carve& c, const FfnPlan& pl, int R_max, int32_t h, int32_t f, int32_t E, moe_dtype_t dt,
                 moe_act_t act) {
   FfnWs w;
   w.tile_off = c.take<int>((size_t)E + 1);
   w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
-  w.part_up = pl.s_up > 1 ? c.take<float>((size_t)pl.s_up * R_max * up_cols(act, f)) : nullptr;
+  w.part_up = up_parts(pl, act, dt) ? c.take<float>((size_t)up_parts(pl, act, dt) * R_max * up_cols(act, f)) : nullptr;
   w.part_down = pl.s_down > 1 ? c.take<float>((size_t)pl.s_down * R_max * h) : nullptr;
   return w;
 }
@@ -156,7 +170,7 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
   w.sorted_slot = c.take<int>(rows);
   w.perm_token = c.take<int>(rows);
   w.hm = c.take<char>((size_t)R_max * f * elem_bytes(dt));
-  w.part_up = pl.s_up > 1 ? c.take<float>((size_t)pl.s_up * R_max * up_cols(act, f)) : nullptr;
+  w.part_up = up_parts(pl, act, dt) ? c.take<float>((size_t)up_parts(pl, act, dt) * R_max * up_cols(act, f)) : nullptr;
   // expert outputs stay fp32 until the combine (s_down K parts of them when the down
   // projection is split; the combine adds the parts)
   w.o = c.take<float>((size_t)pl.s_down * R_max * h);
@@ -196,7 +210,8 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   up.W3 = act == MOE_ACT_SWIGLU ? W3 : nullptr;
   up.K = h;
   up.N = f;
-  up.out = pl.s_up > 1 ? (void*)part_up : hm;
+  const bool sep = sep_up(pl, act, dt);
+  up.out = pl.s_up > 1 || sep ? (void*)part_up : hm;
   up.offsets = offsets;
   up.tile_off = tile_off;
   up.E = E;
@@ -204,13 +219,18 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   up.bm = pl.bm;
   up.ksplit = pl.s_up;
   up.act = gact;
-  up.save = bf && pl.s_up <= 1 ? save : nullptr;  // bf16 only (fp32: the caller runs preact_gemms)
+  up.save = bf && pl.s_up <= 1 && !sep ? save : nullptr;  // bf16 only (fp32: the caller runs preact_gemms)
+  up.raw = sep;
+  up.sep = sep;
   MOE_TRY(launch_gemm(up, bf, st));
-  if (pl.s_up > 1)
-    MOE_TRY(launch_ffn_finish(part_up, pl.s_up, R_max, f, gact, offsets, E, bf, hm, st, bf ? save : nullptr));
+  if (pl.s_up > 1 || sep)
+    MOE_TRY(launch_ffn_finish(part_up, pl.s_up > 1 ? pl.s_up : 1, R_max, f, gact, offsets, E, bf, hm, st,
+                              bf ? save : nullptr));
   if (mark && !mark()) return MOE_ERR_DEVICE;
   GemmArgs down = up;
   down.save = nullptr;
+  down.raw = false;
+  down.sep = false;
   down.A = hm;
   down.a_rows = nullptr;
   down.W = W2;

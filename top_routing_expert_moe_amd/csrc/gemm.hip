@@ -206,6 +206,11 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
       const int wg = c / CPW, cc = c % CPW;
       col = n0 + wg * (WTN / 2) + (cc % (CPW / 2)) * 8;
       Wm = cc < CPW / 2 ? W : W3;
+    } else if (ACT == ACT_SWIGLU_SEP) {
+      // column n0 + 8c of [W1 | W3] (N a multiple of 8: no chunk straddles the two)
+      const int gc = n0 + c * 8;
+      col = gc < N ? gc : gc - N;
+      Wm = gc < N ? W : W3;
     } else {
       col = n0 + c * 8;
       Wm = W;
@@ -386,14 +391,16 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
     const int r = row0 + wm * WTM + jb * 32 + l31;
     if (r >= row_end) continue;
     if (SPLIT) {
-      constexpr int NWM = ACT == ACT_SWIGLU ? 2 : 1;
-      OT* prow = out + ((size_t)ks * R_max + r) * (size_t)(NWM * N);
+      constexpr int NWM = ACT == ACT_SWIGLU ? 2 : 1;               // W1 | W3 halves in a tile
+      constexpr int RW = ACT == ACT_SWIGLU || ACT == ACT_SWIGLU_SEP ? 2 : 1;  // row width / N
+      constexpr int NC = ACT == ACT_SWIGLU_SEP ? 2 : 1;            // column bound / N
+      OT* prow = out + ((size_t)ks * R_max + r) * (size_t)(RW * N);
 #pragma unroll
       for (int ib = 0; ib < IB / NWM; ++ib)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = n0 + wn * (WTN / NWM) + ib * 32 + 8 * q + 4 * hf;
-          if (col >= N) continue;
+          if (col >= NC * N) continue;
           float v[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) v[p] = acc[ib][jb][4 * q + p];
@@ -507,7 +514,10 @@ gemm_bf16_wide_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
     const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, float* __restrict__ save) {
-  using CFG = TileCfgWide32<SPLIT>;
+  // K parts: spread copies and the XCD-aware order; one part (the up projection, also
+  // its separated raw form): copies after the barrier and launch order
+  constexpr bool KP = SPLIT && ACT != ACT_SWIGLU_SEP;
+  using CFG = TileCfgWide32<KP>;
   constexpr int LDS = (CFG::NSW * KB * BNW + CFG::NSTAGE * 32 * KB) * 2;
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   constexpr int NO = ACT == ACT_SWIGLU ? BNW / 2 : BNW;  // output columns per tile
@@ -515,7 +525,7 @@ gemm_bf16_wide_kernel(
   const int n_tiles = MT * NT;
   const int n_real = n_tiles * (SPLIT ? S : 1);
   int L = blockIdx.x;
-  if (SPLIT) {
+  if (KP) {
     const int per = (n_real + 7) >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     if (slot >= per) return;
@@ -627,7 +637,7 @@ template <int ACT, bool G, typename OT, bool SPLIT>
 hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   const bool wide = a.bm == 32;
   const int NO = ACT == ACT_SWIGLU ? (wide ? BNW : BN) / 2 : (wide ? BNW : BN);
-  const int NT = (a.N + NO - 1) / NO;
+  const int NT = ((ACT == ACT_SWIGLU_SEP ? 2 * a.N : a.N) + NO - 1) / NO;
   const int S = SPLIT ? std::max(a.ksplit, 1) : 1;
   const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
   const long long grid = (slots + 7) / 8 * 8;
@@ -637,6 +647,8 @@ hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_bf16_wide_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                        (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
                        (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, save);
+  else if constexpr (ACT == ACT_SWIGLU_SEP)
+    return hipErrorInvalidValue;  // wide tiles only
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                        (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
@@ -649,6 +661,10 @@ hipError_t launch_bf16_t(const GemmArgs& a, hipStream_t st) {
   if (a.bm != 256 && a.bm != 128 && a.bm != 32) return hipErrorInvalidValue;
   // pre-activations are saved by the epilogue of a one-part up projection only
   if (a.save != nullptr && (a.ksplit > 1 || a.raw || ACT == ACT_NONE)) return hipErrorInvalidValue;
+  if (a.sep) {  // raw SwiGLU pre-activations in 512-column tiles of W1 or W3 alone
+    if (ACT != ACT_SWIGLU || !a.raw || a.ksplit > 1 || a.bm != 32 || a.N % 8 != 0) return hipErrorInvalidValue;
+    return launch_bf16_k<ACT_SWIGLU_SEP, G, float, true>(a, st);
+  }
   if (a.ksplit > 1 || a.raw) {
     // K parts: for few rows per expert, where there are too few tiles to fill the chip
     // (or one part of raw accumulators)

@@ -100,7 +100,9 @@ hipError_t launch_gather(const void* x, const int* perm_token, const int* offset
 hipError_t launch_tiles(const int* offsets, int E, int BM, int* tile_off, hipStream_t st);
 
 // ---- expert GEMMs
-enum Act { ACT_NONE = 0, ACT_GELU = 1, ACT_SWIGLU = 2 };
+// ACT_SWIGLU_SEP is a kernel mode, not an activation: the raw SwiGLU pre-activations
+// [a | g] in tiles that each take their weight columns from W1 alone or W3 alone.
+enum Act { ACT_NONE = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_SWIGLU_SEP = 3 };
 
 struct GemmArgs {
   const void* A;        // rows of the left operand ([*, K], row-major)
@@ -124,6 +126,10 @@ struct GemmArgs {
   // raw: write the raw fp32 accumulators in the K-part layout (one part when ksplit <= 1),
   // no activation: the pre-activations [a | g] for the backward pass
   bool raw;
+  // with raw, SwiGLU and 32-row tiles (bm 32, no K parts): each 512-column tile takes its
+  // columns from W1 alone or W3 alone, so every k row of a weight stage is one 1 KiB run
+  // (the layout of the output is the same)
+  bool sep;
   // bf16 up projection (act SwiGLU or GELU) without K parts: not null = also write the
   // fp32 pre-activations here, in the raw layout ([R_max][2N] a | g, or [R_max][N])
   float* save;
