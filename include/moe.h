@@ -156,7 +156,8 @@ moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int3
  *   out_perm [R_max,h] (dt): rows >= offsets[E] are not written.
  *   ws: at least moe_expert_ffn_workspace_bytes(R_max,h,f,E,dt,act) bytes (the hidden
  *       activation, plus fp32 partial sums when few rows per expert make the library
- *       split K to fill the GPU). */
+ *       split K to fill the GPU, or the raw SwiGLU pre-activations [R_max, 2f] fp32
+ *       that the up projection writes when few rows per expert make it stream weights). */
 size_t moe_expert_ffn_workspace_bytes(int32_t R_max, int32_t h, int32_t f, int32_t E, moe_dtype_t dt,
                                       moe_act_t act);  /* 0 for invalid sizes */
 moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t R_max,
