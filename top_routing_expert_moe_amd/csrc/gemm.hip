@@ -16,7 +16,9 @@
 //    (2 x 4 waves of 64 x 64); an expert's last m-tile runs the shape its rows
 //    need.  When every m-tile has at most 32 rows (decode) the launch only
 //    streams weights, and its tiles are 32 rows x 512 weight columns (1 x 8 waves
-//    of 32 x 64), so that each k row of a weight stage is a longer contiguous run;
+//    of 32 x 64), so that each k row of a weight stage is a longer contiguous run
+//    (SwiGLU: 512 columns of W1 alone or W3 alone, written as raw a and g for a
+//    second pass that applies the activation -- ACT_SWIGLU_SEP);
 //  * both operands go from global memory straight into LDS (global_load_lds,
 //    16 B per lane) with no register staging.  The weights stay [K, N] with N
 //    contiguous in LDS and the MFMA operand (8 consecutive k of one column) is
