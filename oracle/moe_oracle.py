@@ -47,7 +47,8 @@ __all__ = [
     "expert_ffn", "combine", "aux_loss", "layer_forward",
     "binned_capacity", "binned_layout", "layer_forward_binned",
     "jitter_input", "noisy_logits", "softmax_t", "topk_weights_t", "uniform_assignment", "route",
-    "silu_grad", "gelu_grad", "layer_backward",
+    "silu_grad", "gelu_grad", "router_logit_grad", "router_logit_grad_scale", "expert_grad_scale",
+    "layer_backward",
 ]
 
 
@@ -167,23 +168,37 @@ def noisy_logits(logits: np.ndarray, noise) -> np.ndarray:
 
 
 def softmax_t(logits: np.ndarray, temperature: float) -> np.ndarray:
-    """Row softmax of ``logits / temperature`` in fp64 ([OPS] "坑3：数值稳定性": a
-    softmax with a temperature, so that experts that are not selected keep some
-    probability).  temperature = 1 is :func:`softmax`."""
+    """Row softmax of ``logits / temperature`` in fp64, with the row maximum subtracted
+    ([OPS] "坑3：数值稳定性": the soft top-K remedy uses a softmax with a temperature).
+    temperature = 1 is :func:`softmax`."""
     l = np.asarray(logits, dtype=np.float32).astype(np.float64)
     z = np.exp((l - l.max(axis=1, keepdims=True)) / float(temperature))
     return z / z.sum(axis=1, keepdims=True)
 
 
-def topk_weights_t(logits: np.ndarray, topk_idx: np.ndarray, temperature: float) -> np.ndarray:
-    """Renormalised weights of the selected experts under the temperature softmax:
-    ``w[t,j] = p[t,S_j] / sum_j' p[t,S_j']``, ``p = softmax(l / temperature)``.
-    Readings ([OPS] "坑3"): the page names a temperature softmax without fixing where it
-    enters; here it shapes the probabilities (weights and aux loss) while the
-    selection still ranks the logits (the same order for any temperature > 0), and
-    the weights are still renormalised over the k selected experts."""
+def topk_weights_t(logits: np.ndarray, topk_idx: np.ndarray, temperature: float,
+                   soft: bool = False) -> np.ndarray:
+    """Gate weights of the selected experts under ``p = softmax(l / temperature)``, fp32 [T,k].
+
+    ``soft=False``: renormalised over the k selected experts, ``w[t,j] = p[t,S_j] /
+    sum_j' p[t,S_j']`` -- the plain router's weights ([OPS] Step 4) with a temperature.
+
+    ``soft=True``: the soft top-K of [OPS] "坑3：数值稳定性".  The page contrasts it with
+    a hard top-K: a softmax with a temperature over all experts, so that experts that
+    are not selected keep a little probability (and with it a gradient).  Reading: the
+    k best experts are still the ones that run (the selection is unchanged), and their
+    weights are the temperature softmax over all E experts taken at the selection,
+    ``w[t,j] = p[t,S_j]``, *without* renormalising over the k.  The weights then sum to
+    less than one; the rest of the mass, ``sum over unselected e of p[t,e]``, belongs to
+    the experts that did not run.  Each weight depends on every expert's logit through
+    the softmax's denominator, so unselected experts receive gradient (see
+    :func:`layer_backward`).  The temperature sets how much mass they keep: a small one
+    concentrates it on the best expert, a large one spreads it towards 1/E each.
+    """
     p = softmax_t(logits, temperature)
     sel = np.take_along_axis(p, np.asarray(topk_idx, dtype=np.int64), axis=1)
+    if soft:
+        return sel.astype(np.float32)
     return (sel / sel.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
@@ -196,16 +211,17 @@ def uniform_assignment(T: int, k: int, E: int) -> np.ndarray:
 
 
 def route(logits: np.ndarray, k: int, *, noise=None, temperature: float = 1.0,
-          uniform: bool = False) -> dict:
+          uniform: bool = False, soft: bool = False) -> dict:
     """Selection with the router variants applied in the pages' order: noise on the
-    logits, top-k on the (noisy) logits, temperature-softmax weights renormalised over
-    the selection, ids optionally replaced by the uniform assignment.  Returns
-    ``topk_idx``, ``topk_w``, ``probs`` (for the aux loss) and the logits used."""
+    logits, top-k on the (noisy) logits, temperature-softmax weights (renormalised over
+    the selection, or not with the soft top-K), ids optionally replaced by the uniform
+    assignment.  Returns ``topk_idx``, ``topk_w``, ``probs`` (the temperature softmax
+    over all experts, for the aux loss) and the logits used."""
     if not (float(temperature) > 0.0 and math.isfinite(float(temperature))):
         raise ValueError("temperature must be finite and > 0")
     l = noisy_logits(logits, noise)
     idx = select_topk(l, k)
-    w = topk_weights_t(l, idx, temperature)
+    w = topk_weights_t(l, idx, temperature, soft)
     if uniform:
         idx = uniform_assignment(l.shape[0], k, l.shape[1])
     return dict(logits=l, topk_idx=idx, topk_w=w, probs=softmax_t(l, temperature))
@@ -364,7 +380,8 @@ def aux_loss(counts: np.ndarray, probs: np.ndarray, T: int, k: int, E: int) -> f
 
 def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float,
                   act: str, dtype: str, logits=None, tokens=None, with_y: bool = True,
-                  jitter=None, noise=None, temperature: float = 1.0, uniform: bool = False) -> dict:
+                  jitter=None, noise=None, temperature: float = 1.0, uniform: bool = False,
+                  soft: bool = False) -> dict:
     """Router -> top-k -> permute (with capacity) -> experts -> weighted combine, plus aux.
 
     ``logits`` may be given (fp32 [T,E]) to route on another implementation's
@@ -372,8 +389,8 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
     ``tokens`` restricts the expensive output ``y`` to a subset of tokens
     (routing, capacity and aux always cover all tokens).  ``y`` is returned in
     the storage dtype: fp32 values, or bf16 bit patterns.  ``jitter``, ``noise``,
-    ``temperature`` and ``uniform`` are the router variants (:func:`jitter_input`,
-    :func:`route`); the experts always read the unjittered x.
+    ``temperature``, ``uniform`` and ``soft`` are the router variants
+    (:func:`jitter_input`, :func:`route`); the experts always read the unjittered x.
     """
     x = np.asarray(x)
     T = x.shape[0]
@@ -382,7 +399,7 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
         xr = x if jitter is None else jitter_input(x, jitter, dtype)
         logits = router_logits(xr, W_gate, logit_bias, dtype)
     logits = np.asarray(logits, dtype=np.float32)
-    r = route(logits, k, noise=noise, temperature=temperature, uniform=uniform)
+    r = route(logits, k, noise=noise, temperature=temperature, uniform=uniform, soft=soft)
     idx, w = r["topk_idx"], r["topk_w"]
     C = expert_capacity(T, E, k, capacity_factor)
     counts, offsets, sorted_slot, slot_pos = permute(idx, E, C)
@@ -412,9 +429,104 @@ def gelu_grad(z: np.ndarray) -> np.ndarray:
     return 0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
 
 
+def router_logit_grad(l: np.ndarray, idx: np.ndarray, w: np.ndarray, dw: np.ndarray, counts: np.ndarray,
+                      d_aux: float, k: int, temperature: float = 1.0, soft: bool = False) -> np.ndarray:
+    """Gradient of ``L`` with respect to the (noisy) logits ``l`` [T,E], fp64, given the
+    gradient ``dw`` [T,k] of the selected experts' weights.
+
+    With ``p = softmax(l / tau)`` the softmax's Jacobian is ``dp_a/dl_b = p_a (delta_ab -
+    p_b) / tau``:
+
+    * renormalised weights (the plain router; ``w = softmax(l_S / tau)`` over the k
+      selected): ``dl[t,S_j] = w_j (dw_j - sum_j' w_j' dw_j') / tau``, zero for experts
+      that were not selected;
+    * soft top-K (``w_j = p[S_j]``, no renormalisation, [OPS] "坑3"): ``dl[t,b] = p_b
+      (dw_b - sum_j w_j dw_j) / tau`` for every expert b, with ``dw_b`` the weight
+      gradient of b's slot if b was selected and 0 otherwise -- experts that did not run
+      still get ``-p_b sum_j w_j dw_j / tau``;
+    * the aux loss ``E sum_e f_e P_e`` with ``P_e`` the mean of p adds ``d_aux (E/T) p_b
+      (f_b - sum_e f_e p_e) / tau``; the counts ``f = counts / (T k)`` are piecewise
+      constant in the logits (no gradient).
+
+    The stored fp32 weights ``w`` are used where the weights appear.
+    """
+    T, E = l.shape
+    tau = float(temperature)
+    p = softmax_t(l, tau)
+    wk = np.asarray(w, dtype=np.float32).astype(np.float64)
+    s_dw = np.sum(wk * dw, axis=1, keepdims=True)
+    rows = np.repeat(np.arange(T), k)
+    dl = np.zeros((T, E))
+    if soft:
+        g = np.zeros((T, E))
+        np.add.at(g, (rows, np.asarray(idx).reshape(-1)), dw.reshape(-1))
+        dl += p * (g - s_dw) / tau
+    else:
+        np.add.at(dl, (rows, np.asarray(idx).reshape(-1)), (wk * (dw - s_dw) / tau).reshape(-1))
+    fe = np.asarray(counts, dtype=np.float64) / float(T * k)
+    dl += float(d_aux) * (E / float(T)) * p * (fe[None, :] - np.sum(p * fe[None, :], axis=1, keepdims=True)) / tau
+    return dl
+
+
+def router_logit_grad_scale(l: np.ndarray, idx: np.ndarray, w: np.ndarray, dw_m: np.ndarray, counts: np.ndarray,
+                            d_aux: float, k: int, temperature: float = 1.0, soft: bool = False) -> np.ndarray:
+    """Magnitude scale of :func:`router_logit_grad`: the same sums with every term taken
+    by absolute value (differences become sums of the absolute terms), from the
+    magnitude ``dw_m`` of the weight gradients.  ``|router_logit_grad| <= this`` for
+    ``|dw| <= dw_m``; equality when no two terms cancel."""
+    T, E = l.shape
+    tau = float(temperature)
+    p = softmax_t(l, tau)
+    wk = np.abs(np.asarray(w, dtype=np.float32).astype(np.float64))
+    s_m = np.sum(wk * dw_m, axis=1, keepdims=True)
+    rows = np.repeat(np.arange(T), k)
+    dl_m = np.zeros((T, E))
+    if soft:
+        g = np.zeros((T, E))
+        np.add.at(g, (rows, np.asarray(idx).reshape(-1)), dw_m.reshape(-1))
+        dl_m += p * (g + s_m) / tau
+    else:
+        np.add.at(dl_m, (rows, np.asarray(idx).reshape(-1)), (wk * (dw_m + s_m) / tau).reshape(-1))
+    fe = np.asarray(counts, dtype=np.float64) / float(T * k)
+    dl_m += abs(float(d_aux)) * (E / float(T)) * p * (fe[None, :] + np.sum(p * fe[None, :], axis=1,
+                                                                            keepdims=True)) / tau
+    return dl_m
+
+
+def expert_grad_scale(X: np.ndarray, dy_rows: np.ndarray, w_rows: np.ndarray, a: np.ndarray, g, hm_r: np.ndarray,
+                      O: np.ndarray, W1e: np.ndarray, W3e, W2e: np.ndarray, act: str) -> dict:
+    """Magnitude scales of one expert's gradients (rows X of that expert, fp64): the
+    chain of products of :func:`layer_backward` taken over absolute values,
+
+      ``|dO| = |w| |dy|``, ``dHm_m = |dO| |W2|^T``; SwiGLU ``da_m = dHm_m |g silu'(a)|``,
+      ``dg_m = dHm_m |silu(a)|``; GELU ``da_m = dHm_m |gelu'(a)|``;
+      ``dW2_m = |Hm|^T |dO|``, ``dW1_m = |X|^T da_m``, ``dW3_m = |X|^T dg_m``,
+      ``dX_m = da_m |W1|^T (+ dg_m |W3|^T)``, ``dw_m = sum |dy| |O|`` per row.
+
+    Each is at least the magnitude of the matching gradient (triangle inequality), and
+    equals it when no sum has terms of both signs.  A computation that rounds its
+    operands with relative error u moves the gradient, to first order, by at most a
+    small multiple of u times this scale -- which is what makes it a bound for a
+    reduced-precision implementation."""
+    dO_m = np.abs(w_rows)[:, None] * np.abs(dy_rows)
+    dHm_m = dO_m @ np.abs(W2e).T
+    out = dict(dw=np.sum(np.abs(dy_rows) * np.abs(O), axis=1), dW2=np.abs(hm_r).T @ dO_m)
+    if act == "swiglu":
+        da_m = dHm_m * np.abs(g * silu_grad(a))
+        dg_m = dHm_m * np.abs(silu(a))
+        out["dW3"] = np.abs(X).T @ dg_m
+        out["dX"] = da_m @ np.abs(W1e).T + dg_m @ np.abs(W3e).T
+    else:
+        da_m = dHm_m * np.abs(gelu_grad(a))
+        out["dX"] = da_m @ np.abs(W1e).T
+    out["dW1"] = np.abs(X).T @ da_m
+    return out
+
+
 def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: int, capacity_factor: float,
                    act: str, dtype: str, logits=None, tokens=None, experts=None,
-                   with_w_gate: bool = True, with_scale: bool = False) -> dict:
+                   with_w_gate: bool = True, with_scale: bool = False, jitter=None, noise=None,
+                   temperature: float = 1.0, soft: bool = False) -> dict:
     """Gradients of ``L = <dy, y> + d_aux * aux`` for the layer of :func:`layer_forward`,
     fp64, as the adjoint of each forward step in reverse order (chain rule).
 
@@ -429,11 +541,15 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
       ``da = dHm * g * silu'(a)``, ``dg = dHm * silu(a)``; GELU ``da = dHm * gelu'(a)``;
       ``dW1 = X^T da``, ``dW3 = X^T dg``, ``dX = da W1^T (+ dg W3^T)``;
     * the permutation's adjoint: ``dx[t] += sum_j dX[slot_pos[t*k+j]]``;
-    * the router: the weights are the softmax over the selected logits, so
-      ``dl[t,S_j] = w_j (dw_j - sum_j' w_j' dw_j')`` and 0 for unselected experts; the aux
-      loss adds ``d_aux (E/T) p[t,i] (f_i - sum_e f_e p[t,e])`` (the counts f are
-      piecewise constant in the logits: no gradient through them);
-    * ``dW_gate = x^T dl``, ``dx += dl W_gate^T``.
+    * the router: :func:`router_logit_grad` (the weights and the aux loss);
+    * ``dW_gate = xr^T dl``, ``dx += (dl W_gate^T) * u`` where ``xr`` is the router's
+      input: x, or with jitter ``u`` the rounded product ``x * u``.
+
+    Router variants: ``noise`` (added to the logits: the gradient with respect to the
+    noisy logits is the one with respect to the logits), ``temperature`` and ``soft``
+    (:func:`topk_weights_t`), ``jitter`` (:func:`jitter_input`; the rounding of the
+    product passes gradients unchanged).  The uniform assignment is a benchmarking
+    mode with no gradient of its own and is not differentiated here.
 
     Readings: top-k selection and the capacity drop are piecewise constant (no
     gradient); in bf16 workloads the rounding of Hm passes gradients unchanged while
@@ -444,11 +560,9 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
     the returned arrays are full-sized, with zeros where nothing was computed.
 
     ``with_scale`` also returns, for each gradient, its magnitude scale: the same chain
-    of products taken over absolute values, carried from ``|dO| = |w| |dy|`` through
-    ``|dO| |W2|^T`` to the bound on ``|da|`` (and ``|dg|``), then ``|X|^T`` of that for
-    ``dW1``, and so on, with the router path carried from ``sum |dy| |O|``.  An
-    implementation that rounds intermediate operands with relative error u moves each
-    gradient, to first order, by at most a small multiple of u times its scale.
+    of products taken over absolute values (:func:`expert_grad_scale`,
+    :func:`router_logit_grad_scale`), carried through ``|dl| |W_gate|^T |u|`` and
+    ``|xr|^T |dl|`` for the router's share of dx and for dW_gate.
     """
     x = np.asarray(x)
     T = x.shape[0]
@@ -457,11 +571,13 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
     h = x64.shape[1]
     f = np.asarray(W1).shape[2]
     Wg = np.asarray(W_gate, dtype=np.float32).astype(np.float64)
+    xr = x if jitter is None else jitter_input(x, jitter, dtype)
+    xr64 = _as_f64(xr, dtype)
+    u64 = None if jitter is None else _as_f64(jitter, dtype)
     if logits is None:
-        logits = router_logits(x, W_gate, logit_bias, dtype)
-    l = np.asarray(logits, dtype=np.float32)
-    idx = select_topk(l, k)
-    w = topk_weights(l, idx)
+        logits = router_logits(xr, W_gate, logit_bias, dtype)
+    r = route(np.asarray(logits, dtype=np.float32), k, noise=noise, temperature=temperature, soft=soft)
+    l, idx, w = r["logits"], r["topk_idx"], r["topk_w"]
     C = expert_capacity(T, E, k, capacity_factor)
     counts, offsets, sorted_slot, slot_pos = permute(idx, E, C)
     dy64 = _as_f64(dy, dtype)
@@ -496,12 +612,13 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
         X = x64[rows]
         W1e = _as_f64(W1[e], dtype)
         W2e = _as_f64(W2[e], dtype)
+        W3e = _as_f64(W3[e], dtype) if act == "swiglu" else None
         a = X @ W1e
         if act == "swiglu":
-            W3e = _as_f64(W3[e], dtype)
             g = X @ W3e
             hm = silu(a) * g
         else:
+            g = None
             hm = gelu(a)
         hm_r = bf16_to_f64(round_to_bf16(hm)) if dtype == "bf16" else hm
         O = hm_r @ W2e
@@ -521,42 +638,26 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
             if act == "swiglu":
                 dW3[e] = X.T @ dg
         if with_scale:
-            dO_m = np.abs(dO)
-            dHm_m = dO_m @ np.abs(W2e).T
-            if act == "swiglu":
-                da_m = dHm_m * np.abs(g * silu_grad(a))
-                dg_m = dHm_m * np.abs(silu(a))
-            else:
-                da_m = dHm_m * np.abs(gelu_grad(a))
-            dw_m[rows, slots] = np.sum(np.abs(dy64[rows]) * np.abs(O), axis=1)
+            m = expert_grad_scale(X, dy64[rows], wk[rows, slots], a, g, hm_r, O, W1e, W3e, W2e, act)
+            dw_m[rows, slots] = m["dw"]
             if e in want_e:
-                sc["dW2"][e] = np.abs(hm_r).T @ dO_m
-                sc["dW1"][e] = np.abs(X).T @ da_m
+                sc["dW2"][e] = m["dW2"]
+                sc["dW1"][e] = m["dW1"]
                 if act == "swiglu":
-                    sc["dW3"][e] = np.abs(X).T @ dg_m
-            mag = da_m @ np.abs(W1e).T
-            if act == "swiglu":
-                mag = mag + dg_m @ np.abs(W3e).T
-            np.add.at(sc["dx"], rows, mag)
+                    sc["dW3"][e] = m["dW3"]
+            np.add.at(sc["dx"], rows, m["dX"])
         np.add.at(dx, rows, dX)
-    # router: the renormalised softmax over the selection, and the aux loss
-    p = softmax(l)
-    dl = np.zeros((T, E))
-    s_dw = np.sum(wk * dw, axis=1, keepdims=True)
-    np.add.at(dl, (np.repeat(np.arange(T), k), idx.reshape(-1)), (wk * (dw - s_dw)).reshape(-1))
-    fe = counts.astype(np.float64) / float(T * k)
-    dl += float(d_aux) * (E / float(T)) * p * (fe[None, :] - np.sum(p * fe[None, :], axis=1, keepdims=True))
-    dx += dl @ Wg.T
-    dWg = x64.T @ dl if with_w_gate else None
+    dl = router_logit_grad(l, idx, w, dw, counts, d_aux, k, temperature, soft)
+    dxr = dl @ Wg.T
+    dx += dxr if u64 is None else dxr * u64
+    dWg = xr64.T @ dl if with_w_gate else None
     out = dict(dx=dx, dW_gate=dWg, dW1=dW1, dW3=dW3, dW2=dW2, dlogits=dl, dw=dw, topk_idx=idx, topk_w=w,
                counts=counts, slot_pos=slot_pos, logits=l)
     if with_scale:
-        dl_m = np.zeros((T, E))
-        s_m = np.sum(wk * dw_m, axis=1, keepdims=True)
-        np.add.at(dl_m, (np.repeat(np.arange(T), k), idx.reshape(-1)), (wk * (dw_m + s_m)).reshape(-1))
-        dl_m += abs(float(d_aux)) * (E / float(T)) * p * (fe[None, :] + np.sum(p * fe[None, :], axis=1, keepdims=True))
-        sc["dx"] += dl_m @ np.abs(Wg).T
-        sc["dW_gate"] = np.abs(x64).T @ dl_m if with_w_gate else None
+        dl_m = router_logit_grad_scale(l, idx, w, dw_m, counts, d_aux, k, temperature, soft)
+        dxr_m = dl_m @ np.abs(Wg).T
+        sc["dx"] += dxr_m if u64 is None else dxr_m * np.abs(u64)
+        sc["dW_gate"] = np.abs(xr64).T @ dl_m if with_w_gate else None
         out["scale"] = sc
     return out
 

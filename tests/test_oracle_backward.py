@@ -26,24 +26,32 @@ def _case(T=24, h=16, f=20, E=5, k=2, act="swiglu", seed=0, bias=True):
     return x, Wg, b, W1, W3, W2, dy
 
 
-def _torch_grads(x, Wg, b, W1, W3, W2, dy, d_aux, k, cf, act):
+def _torch_grads(x, Wg, b, W1, W3, W2, dy, d_aux, k, cf, act, *, temperature=1.0, soft=False, noise=None,
+                 jitter=None):
     """The layer in torch float64 with autograd; the selection and the capacity mask
-    are taken from the oracle (they are piecewise constant)."""
+    are taken from the oracle (they are piecewise constant).  Router variants: gate
+    noise added to the logits, a softmax temperature, soft top-K weights (the
+    temperature softmax over all experts at the selection, not renormalised), and a
+    multiplicative jitter of the router's input."""
     torch = pytest.importorskip("torch")
     T, h = x.shape
     E = Wg.shape[1]
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
     X, G, A1, A2 = t(x), t(Wg), t(W1), t(W2)
     A3 = t(W3) if W3 is not None else None
-    logits = X @ G + (torch.tensor(b, dtype=torch.float64) if b is not None else 0.0)
-    lf = o.router_logits(x, Wg, b, "f32")
+    XR = X if jitter is None else X * torch.tensor(np.asarray(jitter, np.float64))
+    logits = XR @ G + (torch.tensor(b, dtype=torch.float64) if b is not None else 0.0)
+    if noise is not None:
+        logits = logits + torch.tensor(np.asarray(noise, np.float64))
+    xr = x if jitter is None else o.jitter_input(x, jitter, "f32")
+    lf = o.noisy_logits(o.router_logits(xr, Wg, b, "f32"), noise)
     idx = o.select_topk(lf, k)
     C = o.expert_capacity(T, E, k, cf)
     counts, _, _, slot_pos = o.permute(idx, E, C)
     kept = torch.tensor(slot_pos.reshape(T, k) >= 0)
     I = torch.tensor(idx.astype(np.int64))
-    wsel = torch.softmax(torch.gather(logits, 1, I), dim=1)
-    p = torch.softmax(logits, dim=1)
+    p = torch.softmax(logits / temperature, dim=1)
+    wsel = torch.gather(p, 1, I) if soft else torch.softmax(torch.gather(logits, 1, I) / temperature, dim=1)
     fe = torch.tensor(counts / (T * k), dtype=torch.float64)
     aux = E * torch.sum(fe * p.mean(0))
     y = torch.zeros((T, h), dtype=torch.float64)
@@ -164,3 +172,177 @@ def test_backward_bf16_uses_rounded_hidden_activation():
     np.testing.assert_allclose(gb["dW3"], gf["dW3"], rtol=0, atol=1e-12)
     _close(gb["dW2"], gf["dW2"], 2e-2, "dW2 with rounded Hm")
     assert np.abs(gb["dW2"] - gf["dW2"]).max() > 0
+
+
+VARIANT_CASES = {
+    "temperature": dict(temperature=0.6),
+    "soft": dict(soft=True),
+    "soft-temperature-noise": dict(soft=True, temperature=0.5, noise=True),
+    "all": dict(soft=True, temperature=1.5, noise=True, jitter=True),
+    "jitter-noise": dict(noise=True, jitter=True, temperature=0.8),
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANT_CASES))
+@pytest.mark.parametrize("act,cf,d_aux", [("swiglu", 0.6, 0.8), ("gelu", 0.0, 0.0)])
+def test_backward_router_variants_vs_torch_autograd(variant, act, cf, d_aux):
+    spec = VARIANT_CASES[variant]
+    T, E, k = 24, 6, 2
+    x, Wg, b, W1, W3, W2, dy = _case(T=T, E=E, k=k, act=act, seed=31)
+    rng = np.random.default_rng(32)
+    noise = (rng.standard_normal((T, E)) / E).astype(np.float32) if spec.get("noise") else None
+    jit = rng.uniform(0.9, 1.1, x.shape).astype(np.float32) if spec.get("jitter") else None
+    kw = dict(temperature=spec.get("temperature", 1.0), soft=spec.get("soft", False), noise=noise, jitter=jit)
+    ref = _torch_grads(x, Wg, b, W1, W3, W2, dy, d_aux, k, cf, act, **kw)
+    fwd = o.layer_forward(x, Wg, b, W1, W3, W2, k=k, capacity_factor=cf, act=act, dtype="f32", **kw)
+    _close(fwd["y64"], ref["y"], 1e-6, "torch forward = oracle forward")
+    assert abs(fwd["aux"] - ref["aux"]) <= 1e-6 * abs(ref["aux"])
+    g = o.layer_backward(x, Wg, b, W1, W3, W2, dy, d_aux, k=k, capacity_factor=cf, act=act, dtype="f32", **kw)
+    for key in ("dx", "dW_gate", "dW1", "dW2") + (("dW3",) if act == "swiglu" else ()):
+        _close(g[key], ref[key], 2e-6, key)
+
+
+def test_soft_topk_reaches_unselected_experts():
+    """The reason for the soft top-K ([OPS] "坑3"): with hard, renormalised weights an
+    expert that was not selected gets no logit gradient (without the aux term); with
+    soft weights it gets -p_b * sum_j w_j dw_j / tau, and every token's logit gradient
+    still sums to zero (the softmax ignores a shift of all logits)."""
+    T, E, k, tau = 32, 8, 2, 0.7
+    x, Wg, b, W1, W3, W2, dy = _case(T=T, E=E, k=k, seed=33)
+    kw = dict(k=k, capacity_factor=0.0, act="swiglu", dtype="f32", temperature=tau)
+    hard = o.layer_backward(x, Wg, b, W1, W3, W2, dy, 0.0, **kw)
+    soft = o.layer_backward(x, Wg, b, W1, W3, W2, dy, 0.0, soft=True, **kw)
+    sel = np.zeros((T, E), bool)
+    np.put_along_axis(sel, soft["topk_idx"].astype(np.int64), True, axis=1)
+    assert (hard["dlogits"][~sel] == 0).all()
+    assert (np.abs(soft["dlogits"][~sel]) > 0).all()
+    p = o.softmax_t(soft["logits"], tau)
+    s_wdw = np.sum(soft["topk_w"].astype(np.float64) * soft["dw"], axis=1, keepdims=True)
+    want = -p * s_wdw / tau
+    np.testing.assert_allclose(soft["dlogits"][~sel], want[~sel], rtol=1e-12)
+    # (to the rounding of the stored fp32 weights against the fp64 probabilities)
+    assert np.abs(soft["dlogits"].sum(1)).max() <= 1e-6 * np.abs(soft["dlogits"]).sum(1).max()
+    # the soft weights are smaller than the renormalised ones, by the selected mass
+    ratio = soft["topk_w"].astype(np.float64) / hard["topk_w"].astype(np.float64)
+    mass = np.take_along_axis(p, soft["topk_idx"].astype(np.int64), 1).sum(1, keepdims=True)
+    np.testing.assert_allclose(ratio, np.broadcast_to(mass, ratio.shape), rtol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# the magnitude scale (with_scale=True) that sets the bar for reduced-precision gradients
+
+SCALE_KEYS = ("dx", "dW_gate", "dW1", "dW2", "dW3")
+
+
+@pytest.mark.parametrize("act,cf,d_aux,k,variant", [("swiglu", 0.0, 0.0, 2, None), ("gelu", 0.5, 1.1, 2, None),
+                                                    ("swiglu", 0.6, 0.7, 3, "soft"), ("gelu", 0.0, 0.4, 1, None),
+                                                    ("swiglu", 0.0, 0.9, 2, "all")])
+def test_grad_scale_bounds_every_gradient(act, cf, d_aux, k, variant):
+    """Triangle inequality: the chain taken over absolute values bounds each gradient
+    element, on random inputs of both signs."""
+    T, E = 30, 6
+    x, Wg, b, W1, W3, W2, dy = _case(T=T, E=E, k=k, act=act, seed=40 + k)
+    kw = {}
+    if variant:
+        rng = np.random.default_rng(41)
+        spec = VARIANT_CASES[variant]
+        kw = dict(temperature=spec.get("temperature", 1.0), soft=spec.get("soft", False),
+                  noise=(rng.standard_normal((T, E)) / E).astype(np.float32) if spec.get("noise") else None,
+                  jitter=rng.uniform(0.9, 1.1, x.shape).astype(np.float32) if spec.get("jitter") else None)
+    g = o.layer_backward(x, Wg, b, W1, W3, W2, dy, d_aux, k=k, capacity_factor=cf, act=act, dtype="f32",
+                         with_scale=True, **kw)
+    for key in SCALE_KEYS:
+        if g[key] is None:
+            continue
+        sc = g["scale"][key]
+        assert np.isfinite(sc).all() and (sc >= 0).all(), key
+        assert (np.abs(g[key]) <= sc * (1 + 1e-12) + 1e-300).all(), key
+        assert (sc > 0).any(), key
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_grad_scale_equals_gradient_without_cancellation(act):
+    """With every operand non-negative no sum has terms of both signs, so the scale of
+    each expert-side gradient is its magnitude exactly.  (k = 1 gives w = 1 and no
+    renormalisation gradient; W_gate = 0 -- routing by the bias alone -- takes the
+    router's share out of dx.)"""
+    T, h, f, E = 20, 12, 10, 4
+    rng = np.random.default_rng(42)
+    x = rng.uniform(0.0, 1.0, (T, h)).astype(np.float32)
+    W1 = rng.uniform(0.0, 0.3, (E, h, f)).astype(np.float32)
+    W3 = rng.uniform(0.0, 0.3, (E, h, f)).astype(np.float32) if act == "swiglu" else None
+    W2 = rng.uniform(0.0, 0.3, (E, f, h)).astype(np.float32)
+    dy = rng.uniform(0.0, 1.0, (T, h)).astype(np.float32)
+    Wg = np.zeros((h, E), np.float32)
+    b = np.array([0.3, 0.1, -0.2, 0.0], np.float32)
+    # the bias routes every token to expert 0; give each token its own top expert instead
+    logits = rng.permutation(np.tile(np.arange(E, dtype=np.float32), (T, 1)).T).T.copy()
+    g = o.layer_backward(x, Wg, b, W1, W3, W2, dy, 0.0, k=1, capacity_factor=0.0, act=act, dtype="f32",
+                         logits=logits, with_scale=True)
+    for key in ("dx", "dW1", "dW2") + (("dW3",) if act == "swiglu" else ()):
+        np.testing.assert_allclose(g["scale"][key], np.abs(g[key]), rtol=1e-12, atol=0, err_msg=key)
+
+
+def test_grad_scale_vs_brute_force_chain():
+    """Every scale element recomputed with Python loops and math.fsum from the
+    definition of the magnitude chain, on a tiny case with drops, the aux term and a
+    soft router."""
+    T, h, f, E, k, tau, d_aux = 7, 4, 3, 3, 2, 0.8, 0.6
+    x, Wg, b, W1, W3, W2, dy = _case(T=T, h=h, f=f, E=E, k=k, seed=43)
+    cf = 0.8
+    g = o.layer_backward(x, Wg, b, W1, W3, W2, dy, d_aux, k=k, capacity_factor=cf, act="swiglu", dtype="f32",
+                         with_scale=True, temperature=tau, soft=True)
+    idx, w, sp = g["topk_idx"], g["topk_w"], g["slot_pos"].reshape(T, k)
+    F = lambda v: float(v)
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z))
+    dw_m = [[0.0] * k for _ in range(T)]
+    sx = [[0.0] * h for _ in range(T)]
+    s1 = [[[0.0] * f for _ in range(h)] for _ in range(E)]
+    s3 = [[[0.0] * f for _ in range(h)] for _ in range(E)]
+    s2 = [[[0.0] * h for _ in range(f)] for _ in range(E)]
+    for t in range(T):
+        for j in range(k):
+            if sp[t, j] < 0:
+                continue
+            e = int(idx[t, j])
+            a = [math.fsum(F(x[t, i]) * F(W1[e, i, c]) for i in range(h)) for c in range(f)]
+            gg = [math.fsum(F(x[t, i]) * F(W3[e, i, c]) for i in range(h)) for c in range(f)]
+            hm = [a[c] * sig(a[c]) * gg[c] for c in range(f)]
+            O = [math.fsum(hm[c] * F(W2[e, c, i]) for c in range(f)) for i in range(h)]
+            dw_m[t][j] = math.fsum(abs(F(dy[t, i])) * abs(O[i]) for i in range(h))
+            dO = [abs(F(w[t, j])) * abs(F(dy[t, i])) for i in range(h)]
+            dHm = [math.fsum(dO[i] * abs(F(W2[e, c, i])) for i in range(h)) for c in range(f)]
+            sgrad = [sig(a[c]) * (1 + a[c] * (1 - sig(a[c]))) for c in range(f)]
+            da = [dHm[c] * abs(gg[c] * sgrad[c]) for c in range(f)]
+            dg = [dHm[c] * abs(a[c] * sig(a[c])) for c in range(f)]
+            for i in range(h):
+                sx[t][i] += math.fsum([da[c] * abs(F(W1[e, i, c])) for c in range(f)] +
+                                      [dg[c] * abs(F(W3[e, i, c])) for c in range(f)])
+                for c in range(f):
+                    s1[e][i][c] += abs(F(x[t, i])) * da[c]
+                    s3[e][i][c] += abs(F(x[t, i])) * dg[c]
+            for c in range(f):
+                for i in range(h):
+                    s2[e][c][i] += abs(hm[c]) * dO[i]
+    # router: soft weights p_b at the selection; |d/dl_b| <= p_b (dw_m_b + sum_j |w_j| dw_m_j) / tau
+    # + |d_aux| (E/T) p_b (f_b + sum_e f_e p_e) / tau
+    counts = [sum(1 for t in range(T) for j in range(k) if idx[t, j] == e) for e in range(E)]
+    fe = [c / (T * k) for c in counts]
+    l = g["logits"]
+    dl_m = [[0.0] * E for _ in range(T)]
+    for t in range(T):
+        m = max(F(v) for v in l[t])
+        ex = [math.exp((F(l[t, e]) - m) / tau) for e in range(E)]
+        den = math.fsum(ex)
+        p = [v / den for v in ex]
+        s_m = math.fsum(abs(F(w[t, j])) * dw_m[t][j] for j in range(k))
+        fp = math.fsum(fe[e] * p[e] for e in range(E))
+        for e in range(E):
+            own = math.fsum(dw_m[t][j] for j in range(k) if idx[t, j] == e)
+            dl_m[t][e] = p[e] * (own + s_m) / tau + abs(d_aux) * (E / T) * p[e] * (fe[e] + fp) / tau
+    for t in range(T):
+        for i in range(h):
+            sx[t][i] += math.fsum(dl_m[t][e] * abs(F(Wg[i, e])) for e in range(E))
+    sg = [[math.fsum(abs(F(x[t, i])) * dl_m[t][e] for t in range(T)) for e in range(E)] for i in range(h)]
+    for key, want in (("dx", sx), ("dW1", s1), ("dW3", s3), ("dW2", s2), ("dW_gate", sg)):
+        np.testing.assert_allclose(g["scale"][key], np.array(want), rtol=1e-10, atol=1e-300, err_msg=key)

@@ -97,7 +97,63 @@ def _gelu_grad_cdf_only(z):
     return 0.5 * (1.0 + om._erf(z / math.sqrt(2.0)))
 
 
-_orig = {n: getattr(om, n) for n in ("router_logits", "permute", "binned_layout", "binned_capacity", "softmax_t")}
+def _scale_no_abs_on_W2(X, dy_rows, w_rows, a, g, hm_r, O, W1e, W3e, W2e, act):
+    # the magnitude chain with |W2| replaced by W2 (a dropped abs)
+    return _orig["expert_grad_scale"](X, dy_rows, w_rows, a, g, hm_r, O, W1e, W3e, W2e, act) | dict(
+        dX=_scale_chain_dx(X, dy_rows, w_rows, a, g, W1e, W3e, W2e, act, abs_w2=False))
+
+
+def _scale_chain_dx(X, dy_rows, w_rows, a, g, W1e, W3e, W2e, act, abs_w2):
+    dO_m = np.abs(w_rows)[:, None] * np.abs(dy_rows)
+    dHm_m = dO_m @ (np.abs(W2e) if abs_w2 else W2e).T
+    if act == "swiglu":
+        return (dHm_m * np.abs(g * om.silu_grad(a))) @ np.abs(W1e).T + (dHm_m * np.abs(om.silu(a))) @ np.abs(W3e).T
+    return (dHm_m * np.abs(om.gelu_grad(a))) @ np.abs(W1e).T
+
+
+def _scale_dg_term_doubled(X, dy_rows, w_rows, a, g, hm_r, O, W1e, W3e, W2e, act):
+    # |W3| enters only the dX chain's dg term: doubling it doubles that term
+    return _orig["expert_grad_scale"](X, dy_rows, w_rows, a, g, hm_r, O, W1e, None if W3e is None else 2 * W3e,
+                                      W2e, act)
+
+
+def _router_scale_difference(l, idx, w, dw_m, counts, d_aux, k, temperature=1.0, soft=False):
+    # the renormalisation's two terms subtracted instead of added in the magnitude
+    T, E = l.shape
+    p = om.softmax_t(l, temperature)
+    wk = np.abs(np.asarray(w, np.float64))
+    s_m = np.sum(wk * dw_m, axis=1, keepdims=True)
+    rows = np.repeat(np.arange(T), k)
+    out = np.zeros((T, E))
+    if soft:
+        gm = np.zeros((T, E))
+        np.add.at(gm, (rows, np.asarray(idx).reshape(-1)), dw_m.reshape(-1))
+        out += p * np.abs(gm - s_m) / temperature
+    else:
+        np.add.at(out, (rows, np.asarray(idx).reshape(-1)), (wk * np.abs(dw_m - s_m) / temperature).reshape(-1))
+    fe = np.asarray(counts, np.float64) / (T * k)
+    out += abs(d_aux) * (E / T) * p * (fe[None, :] + np.sum(p * fe[None, :], 1, keepdims=True)) / temperature
+    return out
+
+
+def _soft_renormalised(logits, topk_idx, temperature, soft=False):
+    # the earlier reading: a temperature on the hard top-k, renormalised over the k
+    return _orig["topk_weights_t"](logits, topk_idx, temperature, False)
+
+
+def _soft_grad_selected_only(l, idx, w, dw, counts, d_aux, k, temperature=1.0, soft=False):
+    # the soft router's gradient kept only at the selected experts
+    dl = _orig["router_logit_grad"](l, idx, w, dw, counts, d_aux, k, temperature, soft)
+    if soft:
+        aux_only = _orig["router_logit_grad"](l, idx, w, np.zeros_like(dw), counts, d_aux, k, temperature, soft)
+        sel = np.zeros(dl.shape, bool)
+        np.put_along_axis(sel, np.asarray(idx, np.int64), True, axis=1)
+        dl = np.where(sel, dl, aux_only)
+    return dl
+
+
+_orig = {n: getattr(om, n) for n in ("router_logits", "permute", "binned_layout", "binned_capacity", "softmax_t",
+                                     "expert_grad_scale", "topk_weights_t", "router_logit_grad")}
 
 MUTANTS = [
     ("select_topk", _topk_ties_high, ["test_topk_ties_and_signed_zero"]),
@@ -115,20 +171,37 @@ MUTANTS = [
     ("noisy_logits", _noise_ignored, ["test_noise_decides_the_selection"]),
     ("silu_grad", _silu_grad_first_term, ["backward:swiglu"]),
     ("gelu_grad", _gelu_grad_cdf_only, ["backward:gelu"]),
+    ("expert_grad_scale", _scale_no_abs_on_W2, ["scale:bounds", "scale:brute"]),
+    ("expert_grad_scale", _scale_dg_term_doubled, ["scale:equal", "scale:brute"]),
+    ("router_logit_grad_scale", _router_scale_difference, ["scale:bounds", "scale:brute"]),
+    ("topk_weights_t", _soft_renormalised, ["test_soft_topk_closed_form_on_the_worked_example"]),
+    ("router_logit_grad", _soft_grad_selected_only, ["backward:soft", "backward:soft-unselected"]),
 ]
 
 
 def _run(test_name):
+    if test_name == "backward:soft":
+        return bpins.test_backward_router_variants_vs_torch_autograd("soft-temperature-noise", "swiglu", 0.6, 0.8)
+    if test_name == "backward:soft-unselected":
+        return bpins.test_soft_topk_reaches_unselected_experts()
     if test_name.startswith("backward:"):
         act = test_name.split(":")[1]
         return bpins.test_backward_vs_torch_autograd(act, 0.0, 0.5, 2, 5)
+    if test_name == "scale:bounds":
+        for args in (("swiglu", 0.0, 0.0, 2, None), ("swiglu", 0.6, 0.7, 3, "soft"), ("gelu", 0.5, 1.1, 2, None)):
+            bpins.test_grad_scale_bounds_every_gradient(*args)
+        return None
+    if test_name == "scale:equal":
+        return bpins.test_grad_scale_equals_gradient_without_cancellation("swiglu")
+    if test_name == "scale:brute":
+        return bpins.test_grad_scale_vs_brute_force_chain()
     fn = getattr(pins, test_name)
     if test_name == "test_k_equals_E_is_dense_softmax_mixture":
         return fn("swiglu")
     return fn()
 
 
-@pytest.mark.parametrize("target,mutant,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
+@pytest.mark.parametrize("target,mutant,catchers", MUTANTS, ids=[m[1].__name__.lstrip("_") for m in MUTANTS])
 def test_pins_catch_planted_mistake(monkeypatch, target, mutant, catchers):
     monkeypatch.setattr(om, target, mutant)
     monkeypatch.setattr(o, target, mutant, raising=False)

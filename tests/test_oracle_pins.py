@@ -494,6 +494,48 @@ def test_temperature_closed_form_on_the_worked_example():
         np.testing.assert_allclose(r["probs"][0], z / z.sum(), rtol=1e-6)
 
 
+def test_soft_topk_closed_form_on_the_worked_example():
+    """Soft top-K ([OPS] "坑3") on the worked example, k = 2 (experts 0 and 6): the
+    weights are the temperature softmax over all eight scores taken at the two selected
+    experts, not renormalised -- w_j = exp(s_j / tau) / sum_e exp(s_e / tau), written
+    out with math.exp and math.fsum.  The unselected experts keep the rest of the mass."""
+    g = _gold("ops_top2_example.json")
+    s32 = [float(np.float32(v)) for v in g["scores"]]
+    l = np.array([g["scores"]], dtype=np.float32)
+    for tau in (1.0, 0.5, 2.0, 0.1):
+        r = o.route(l, 2, temperature=tau, soft=True)
+        assert r["topk_idx"].tolist() == [g["topk_idx"]]   # the selection is the hard top-k's
+        den = math.fsum(math.exp(v / tau) for v in s32)
+        want = [math.exp(s32[e] / tau) / den for e in g["topk_idx"]]
+        np.testing.assert_allclose(r["topk_w"][0], want, rtol=3e-7)
+        rest = math.fsum(math.exp(s32[e] / tau) / den for e in range(8) if e not in g["topk_idx"])
+        assert abs(math.fsum(map(float, r["topk_w"][0])) + rest - 1.0) < 1e-6
+        assert float(r["topk_w"][0].sum()) < 1.0 - 0.5 * rest        # mass left to the other six
+    # tau = 1: exactly the plain softmax probabilities of the selected pair
+    w1 = o.route(l, 2, soft=True)["topk_w"][0]
+    p = o.softmax(l)[0]
+    assert w1.tolist() == [np.float32(p[0]), np.float32(p[6])]
+
+
+def test_soft_topk_limits_and_special_cases():
+    rng = np.random.default_rng(16)
+    l = (rng.permutation(64).reshape(8, 8) / 8.0).astype(np.float32)  # distinct logits, gaps >= 1/8
+    cold = o.route(l, 3, temperature=1e-3, soft=True)["topk_w"]
+    np.testing.assert_allclose(cold[:, 0], 1.0, atol=1e-30)             # all mass on the best expert
+    assert np.abs(cold[:, 1:]).max() < 1e-30
+    hot = o.route(l, 3, temperature=1e9, soft=True)["topk_w"]
+    np.testing.assert_allclose(hot, 1.0 / 8.0, rtol=1e-6)               # spread over all E experts
+    # k = E: nothing is left unselected, so the soft weights are the renormalised ones
+    full_s = o.route(l, 8, temperature=0.7, soft=True)["topk_w"]
+    full_r = o.route(l, 8, temperature=0.7)["topk_w"]
+    np.testing.assert_allclose(full_s, full_r, rtol=1e-6)
+    # the ratios between the selected weights do not depend on the renormalisation
+    ws = o.route(l, 3, temperature=0.7, soft=True)["topk_w"].astype(np.float64)
+    wr = o.route(l, 3, temperature=0.7)["topk_w"].astype(np.float64)
+    np.testing.assert_allclose(ws / ws.sum(1, keepdims=True), wr, rtol=1e-6)
+    assert (ws.sum(1) < 1.0).all()
+
+
 def test_temperature_limits():
     rng = np.random.default_rng(6)
     l = (rng.permutation(64).reshape(8, 8) / 8.0).astype(np.float32)  # distinct logits, gaps >= 1/8
@@ -566,8 +608,8 @@ def test_jitter_input_vs_torch_and_identity():
 
 
 def test_layer_router_variants_vs_brute_force():
-    """The layer with jitter, noise, a temperature and the uniform assignment against the
-    pure-Python brute force fed the same variant routing."""
+    """The layer with jitter, noise, a temperature, the uniform assignment and the soft
+    top-K against a brute force fed the same variant routing."""
     rng = np.random.default_rng(11)
     T, h, f, E, k = 12, 16, 24, 5, 2
     x = rng.standard_normal((T, h)).astype(np.float32)
@@ -576,9 +618,9 @@ def test_layer_router_variants_vs_brute_force():
     W2 = (rng.standard_normal((E, f, h)) / 5).astype(np.float32)
     u = rng.uniform(0.9, 1.1, (T, h)).astype(np.float32)
     noise = (rng.standard_normal((T, E)) / E).astype(np.float32)
-    for uniform in (False, True):
+    for uniform, soft in ((False, False), (True, False), (False, True)):
         ref = o.layer_forward(x, Wg, None, W1, None, W2, k=k, capacity_factor=0.0, act="gelu", dtype="f32",
-                              jitter=u, noise=noise, temperature=0.7, uniform=uniform)
+                              jitter=u, noise=noise, temperature=0.7, uniform=uniform, soft=soft)
         # routing of the variant, recomputed step by step from its definitions
         xr = x * u
         lg = (xr.astype(np.float64) @ Wg.astype(np.float64)).astype(np.float32)
@@ -586,7 +628,7 @@ def test_layer_router_variants_vs_brute_force():
         idx = np.argsort(-ln.astype(np.float64), axis=1, kind="stable")[:, :k]
         p = np.exp((ln.astype(np.float64) - ln.max(1, keepdims=True)) / 0.7)
         ps = np.take_along_axis(p, idx, 1)
-        w = ps / ps.sum(1, keepdims=True)
+        w = ps / (p.sum(1, keepdims=True) if soft else ps.sum(1, keepdims=True))
         if uniform:
             idx = (np.arange(T * k) % E).reshape(T, k)
         y = np.zeros((T, h))
