@@ -494,14 +494,14 @@ def router_logit_grad_scale(l: np.ndarray, idx: np.ndarray, w: np.ndarray, dw_m:
 
 
 def expert_grad_scale(X: np.ndarray, dy_rows: np.ndarray, w_rows: np.ndarray, a: np.ndarray, g, hm_r: np.ndarray,
-                      O: np.ndarray, W1e: np.ndarray, W3e, W2e: np.ndarray, act: str) -> dict:
+                      W1e: np.ndarray, W3e, W2e: np.ndarray, act: str) -> dict:
     """Magnitude scales of one expert's gradients (rows X of that expert, fp64): the
     chain of products of :func:`layer_backward` taken over absolute values,
 
       ``|dO| = |w| |dy|``, ``dHm_m = |dO| |W2|^T``; SwiGLU ``da_m = dHm_m |g silu'(a)|``,
       ``dg_m = dHm_m |silu(a)|``; GELU ``da_m = dHm_m |gelu'(a)|``;
       ``dW2_m = |Hm|^T |dO|``, ``dW1_m = |X|^T da_m``, ``dW3_m = |X|^T dg_m``,
-      ``dX_m = da_m |W1|^T (+ dg_m |W3|^T)``, ``dw_m = sum |dy| |O|`` per row.
+      ``dX_m = da_m |W1|^T (+ dg_m |W3|^T)``.
 
     Each is at least the magnitude of the matching gradient (triangle inequality), and
     equals it when no sum has terms of both signs.  A computation that rounds its
@@ -510,7 +510,7 @@ def expert_grad_scale(X: np.ndarray, dy_rows: np.ndarray, w_rows: np.ndarray, a:
     reduced-precision implementation."""
     dO_m = np.abs(w_rows)[:, None] * np.abs(dy_rows)
     dHm_m = dO_m @ np.abs(W2e).T
-    out = dict(dw=np.sum(np.abs(dy_rows) * np.abs(O), axis=1), dW2=np.abs(hm_r).T @ dO_m)
+    out = dict(dW2=np.abs(hm_r).T @ dO_m)
     if act == "swiglu":
         da_m = dHm_m * np.abs(g * silu_grad(a))
         dg_m = dHm_m * np.abs(silu(a))
@@ -584,10 +584,8 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
     kept = slot_pos.reshape(T, k) >= 0
     wk = w.astype(np.float64)
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    need_tok = np.zeros(T, dtype=bool)
-    need_tok[tok] = True
-    if with_w_gate:
-        need_tok[:] = True           # dl of every token enters dW_gate
+    want_dx = np.zeros(T, dtype=bool)
+    want_dx[tok] = True
     want_e = set(range(E)) if experts is None else set(int(e) for e in experts)
 
     dx = np.zeros((T, h))
@@ -602,11 +600,11 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
         dw_m = np.zeros((T, k))
     for e in range(E):
         rows, slots = np.nonzero((idx == e) & kept)
-        if e in want_e:
-            sel = np.ones(rows.shape, dtype=bool)      # all rows of e: the weight gradients need them
-        else:
-            sel = need_tok[rows]                       # only the rows whose token is asked for
-        rows, slots = rows[sel], slots[sel]
+        # the expert's forward for the rows whose dw is needed: every row when dW_gate (which
+        # takes dl of every token) or this expert's weight gradients are asked for, else the
+        # rows of the tokens whose dx is (dl of a token needs the dw of all its slots)
+        fwd = np.ones(rows.shape, dtype=bool) if (e in want_e or with_w_gate) else want_dx[rows]
+        rows, slots = rows[fwd], slots[fwd]
         if rows.size == 0:
             continue
         X = x64[rows]
@@ -623,6 +621,15 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
         hm_r = bf16_to_f64(round_to_bf16(hm)) if dtype == "bf16" else hm
         O = hm_r @ W2e
         dw[rows, slots] = np.sum(dy64[rows] * O, axis=1)
+        if with_scale:
+            dw_m[rows, slots] = np.sum(np.abs(dy64[rows]) * np.abs(O), axis=1)
+        # the chain through the expert for every row of a wanted expert, else for the rows
+        # of the tokens whose dx is asked for
+        back = np.ones(rows.shape, dtype=bool) if e in want_e else want_dx[rows]
+        if not back.any():
+            continue
+        rows, slots, X, a, hm_r = rows[back], slots[back], X[back], a[back], hm_r[back]
+        g = None if g is None else g[back]
         dO = wk[rows, slots][:, None] * dy64[rows]
         dHm = dO @ W2e.T
         if act == "swiglu":
@@ -638,8 +645,7 @@ def layer_backward(x, W_gate, logit_bias, W1, W3, W2, dy, d_aux: float, *, k: in
             if act == "swiglu":
                 dW3[e] = X.T @ dg
         if with_scale:
-            m = expert_grad_scale(X, dy64[rows], wk[rows, slots], a, g, hm_r, O, W1e, W3e, W2e, act)
-            dw_m[rows, slots] = m["dw"]
+            m = expert_grad_scale(X, dy64[rows], wk[rows, slots], a, g, hm_r, W1e, W3e, W2e, act)
             if e in want_e:
                 sc["dW2"][e] = m["dW2"]
                 sc["dW1"][e] = m["dW1"]

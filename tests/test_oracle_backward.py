@@ -346,3 +346,25 @@ def test_grad_scale_vs_brute_force_chain():
     sg = [[math.fsum(abs(F(x[t, i])) * dl_m[t][e] for t in range(T)) for e in range(E)] for i in range(h)]
     for key, want in (("dx", sx), ("dW1", s1), ("dW3", s3), ("dW2", s2), ("dW_gate", sg)):
         np.testing.assert_allclose(g["scale"][key], np.array(want), rtol=1e-10, atol=1e-300, err_msg=key)
+
+
+@pytest.mark.parametrize("with_w_gate", [True, False])
+def test_restricted_backward_equals_the_full_one(with_w_gate):
+    """Asking for some tokens' dx and some experts' weight gradients gives the full
+    backward's values there (the oracle only skips the work nobody asked for; a matrix
+    product over fewer rows may sum in another order, so to fp64 rounding)."""
+    x, Wg, b, W1, W3, W2, dy = _case(T=40, E=6, k=2, seed=50)
+    kw = dict(k=2, capacity_factor=0.7, act="swiglu", dtype="f32", with_scale=True, soft=True, temperature=0.8)
+    full = o.layer_backward(x, Wg, b, W1, W3, W2, dy, 0.4, **kw)
+    tokens, experts = [0, 7, 31, 39], [1, 4]
+    part = o.layer_backward(x, Wg, b, W1, W3, W2, dy, 0.4, tokens=tokens, experts=experts, with_w_gate=with_w_gate,
+                            **kw)
+    same = lambda a, b_: np.testing.assert_allclose(a, b_, rtol=1e-12, atol=1e-15)
+    same(part["dx"][tokens], full["dx"][tokens])
+    same(part["scale"]["dx"][tokens], full["scale"]["dx"][tokens])
+    for name in ("dW1", "dW3", "dW2"):
+        same(part[name][experts], full[name][experts])
+        same(part["scale"][name][experts], full["scale"][name][experts])
+    if with_w_gate:
+        same(part["dW_gate"], full["dW_gate"])
+        same(part["scale"]["dW_gate"], full["scale"]["dW_gate"])

@@ -97,9 +97,9 @@ def _gelu_grad_cdf_only(z):
     return 0.5 * (1.0 + om._erf(z / math.sqrt(2.0)))
 
 
-def _scale_no_abs_on_W2(X, dy_rows, w_rows, a, g, hm_r, O, W1e, W3e, W2e, act):
+def _scale_no_abs_on_W2(X, dy_rows, w_rows, a, g, hm_r, W1e, W3e, W2e, act):
     # the magnitude chain with |W2| replaced by W2 (a dropped abs)
-    return _orig["expert_grad_scale"](X, dy_rows, w_rows, a, g, hm_r, O, W1e, W3e, W2e, act) | dict(
+    return _orig["expert_grad_scale"](X, dy_rows, w_rows, a, g, hm_r, W1e, W3e, W2e, act) | dict(
         dX=_scale_chain_dx(X, dy_rows, w_rows, a, g, W1e, W3e, W2e, act, abs_w2=False))
 
 
@@ -111,9 +111,9 @@ def _scale_chain_dx(X, dy_rows, w_rows, a, g, W1e, W3e, W2e, act, abs_w2):
     return (dHm_m * np.abs(om.gelu_grad(a))) @ np.abs(W1e).T
 
 
-def _scale_dg_term_doubled(X, dy_rows, w_rows, a, g, hm_r, O, W1e, W3e, W2e, act):
+def _scale_dg_term_doubled(X, dy_rows, w_rows, a, g, hm_r, W1e, W3e, W2e, act):
     # |W3| enters only the dX chain's dg term: doubling it doubles that term
-    return _orig["expert_grad_scale"](X, dy_rows, w_rows, a, g, hm_r, O, W1e, None if W3e is None else 2 * W3e,
+    return _orig["expert_grad_scale"](X, dy_rows, w_rows, a, g, hm_r, W1e, None if W3e is None else 2 * W3e,
                                       W2e, act)
 
 
