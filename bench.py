@@ -110,6 +110,114 @@ def traffic_entry(workload: str):
     return e.get("bytes_per_launch")
 
 
+# the other configurations whose fractions the default run also records (timed in the same
+# process after the headline workload)
+OTHER_WORKLOADS = ("decode-mixtral", "capacity-e64", "finegrained-e256")
+
+
+def measure_other(name: str, steps: int, warmup: int) -> dict:
+    """One more workload's layer forward, timed like the headline: an instrumented pass for the
+    stage times, then `steps` calls with events only around the up projection.  Returns the
+    figures the roofline needs (ms per layer, the layer's roofline fraction, the up and down
+    projections' HBM or MFMA fractions)."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as mw
+    import top_routing_expert_moe_amd as moe
+
+    dev = torch.device("cuda:0")
+    w = mw.by_name(name)
+    t = time.time()
+    host = mw.make_inputs(w)
+    bf = w.dtype == "bf16"
+
+    def to_dev(a, low):
+        if a is None:
+            return None
+        if low and bf:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = {k: to_dev(v, k in ("x", "W1", "W3", "W2")) for k, v in host.items()}
+    del host
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: inputs drawn and resident in {time.time() - t:.1f}s")
+    T, h, f, E, k = w.T, w.h, w.f, w.E, w.k
+    act = moe.SWIGLU if w.act == "swiglu" else moe.GELU
+    dt = moe.BF16 if bf else moe.F32
+    y = torch.empty((T, h), dtype=d["x"].dtype, device=dev)
+    aux = torch.empty((), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    ws = torch.empty(moe.workspace_bytes(T, h, f, E, k, w.cf, dt, act), dtype=torch.uint8, device=dev)
+
+    def step(events=None):
+        moe.layer_forward(d["x"], d["W_gate"], d["logit_bias"], d["W1"], d["W3"], d["W2"], k=k,
+                          capacity_factor=w.cf, act=w.act, ws=ws, y=y, aux=aux, counts=counts, events=events)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    hip = Hip()
+    stages = moe.LAYER_STAGES
+    nst = len(stages)
+    n_inst = max(1, min(steps, 10))
+    ev = [hip.events(nst + 1) for _ in range(n_inst)]
+    for i in range(n_inst):
+        step(ev[i])
+    torch.cuda.synchronize()
+    stage_ms = {s: sum(hip.elapsed_ms(ev[i][j], ev[i][j + 1]) for i in range(n_inst)) / n_inst
+                for j, s in enumerate(stages)}
+    for e_ in ev:
+        hip.destroy(e_)
+    jd = stages.index("expert_up")
+    live = [hip.events(2) for _ in range(steps)]
+    arrs = []
+    for i in range(steps):
+        a_ = (ctypes.c_void_p * (nst + 1))()
+        a_[jd], a_[jd + 1] = live[i][0], live[i][1]
+        arrs.append(a_)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(arrs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    up_ms = sum(hip.elapsed_ms(live[i][0], live[i][1]) for i in range(steps)) / steps
+    for e_ in live:
+        hip.destroy(e_)
+    cnt = counts.cpu().numpy().astype(np.int64)
+    C = moe.capacity(T, E, k, w.cf)
+    kept = cnt if C is None else np.minimum(cnt, C)
+    R = int(kept.sum())
+    active = int((kept > 0).sum())
+    es = 2 if bf else 4
+    n_up = 2 if w.act == "swiglu" else 1
+    ms = wall / steps * 1e3
+    flops_up, flops_down = 2.0 * n_up * R * h * f, 2.0 * R * f * h
+    bytes_up = active * n_up * h * f * es + R * h * es + R * f * es
+    bytes_down = active * f * h * es + R * f * es + R * h * 4
+    layer_bytes = T * h * es + h * E * 4 + active * (n_up + 1) * h * f * es + T * h * es + T * k * 12
+    t_roof = max((flops_up + flops_down) / (PEAK_BF16_TFLOPS * 1e12), layer_bytes / (PEAK_HBM_GBS * 1e9))
+    route_bytes = T * h * es + h * E * 4 + T * E * 4 + T * k * 16
+    route_ms = sum(stage_ms[s] for s in ("logits", "select", "scan", "scatter"))
+    down_s = stage_ms["expert_down"] / 1e3
+    out = {"ms_per_layer": round(ms, 5), "tokens_per_s": round(T / (ms / 1e3), 1),
+           "layer_roofline_frac": round(t_roof / (ms / 1e3), 4),
+           "layer_bound": "mfma" if (flops_up + flops_down) / PEAK_BF16_TFLOPS / 1e12 >= layer_bytes / PEAK_HBM_GBS / 1e9
+           else "hbm",
+           "up_ms": round(up_ms, 5), "up_hbm_frac": round(bytes_up / (up_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+           "up_mfma_frac": round(flops_up / (up_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "down_ms": round(stage_ms["expert_down"], 5),
+           "down_hbm_frac": round(bytes_down / down_s / 1e9 / PEAK_HBM_GBS, 4),
+           "down_mfma_frac": round(flops_down / down_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "route_permute_ms": round(route_ms, 5), "route_gbps": round(route_bytes / (route_ms / 1e3) / 1e9, 1),
+           "combine_ms": round(stage_ms["combine"], 5), "rows_kept": R, "active_experts": active,
+           "steps": steps, "stage_ms": {s_: round(v, 5) for s_, v in stage_ms.items()}}
+    del d, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +234,9 @@ def main():
                     help="time a training step: the training forward (which saves the up projection's "
                          "pre-activations), then the backward pass (dy ~ N(0,1), aux weight 0.01), with per-stage "
                          "times of both")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other configurations (decode-mixtral, capacity-e64, finegrained-e256) that the "
+                         "default prefill run also times, in the same process, for extra.others")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run a plain elementwise copy (y = x + 1, fp32) over this many MiB three "
                          "times: a kernel of known traffic for calibrating rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -457,6 +568,17 @@ def main():
         extra["parity_vs_oracle"] = {"tokens": int(same.sum()), "routing_differs": int((~same).sum()),
                                      "max_abs_over_rms": round(float(np.abs(got - ry).max()) / rms, 5),
                                      "aux_rel_err": abs(extra["aux_loss"] - ref["aux"]) / abs(ref["aux"])}
+
+    if not args.no_others and not args.backward and not binned and args.capacity_factor is None and \
+            w.name == "prefill-mixtral":
+        del d, ws
+        torch.cuda.empty_cache()
+        others = {}
+        for name in OTHER_WORKLOADS:
+            others[name] = measure_other(name, steps=max(args.steps, 20) if name == "decode-mixtral" else
+                                         max(args.steps // 2, 10), warmup=3)
+            log(f"[bench] {name}: {json.dumps(others[name])}")
+        extra["others"] = others
 
     out = {
         "metric": METRIC if not args.backward else "MoE layer training step (forward + backward) tokens/s",

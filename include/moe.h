@@ -36,7 +36,10 @@
  *     16-bit patterns); the router (W_gate, logit_bias, logits, weights) is
  *     always fp32.  MOE_F32: everything fp32.
  *   - Limits: 1 <= k <= E; E <= 256 (MOE_ERR_UNSUPPORTED beyond: one 8-bit
- *     digit for the sort by expert id); k <= 16; h and f multiples of 64.
+ *     digit for the sort by expert id); k <= 16; h and f multiples of 64.  The
+ *     expert GEMMs address their left operand with 32-bit element offsets, so the
+ *     entry points that run them return MOE_ERR_UNSUPPORTED when T*h, R*h or R*f
+ *     reaches 2^32 (R: the rows the GEMMs may get, min(T*k, E*C), or R_max).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -104,12 +107,20 @@ moe_status_t moe_route(const void* x, const float* W_gate, const float* logit_bi
  *   logit_noise [T,E] fp32 or NULL: added (in fp32) to the logits before the softmax and
  *               the top-k ([CAI] Top2Router with a NormalNoiseGenerator); the logits
  *               returned by moe_route_ex are the router's own, without the noise.
- *   temperature > 0: probabilities = softmax(logits / temperature), used for the weights
- *               and the aux loss; the selection still ranks the (noisy) logits ([OPS]
- *               "坑3": a softmax with a temperature as the soft top-K remedy).  1 = plain.
+ *   temperature > 0: probabilities p = softmax(logits / temperature), used for the
+ *               weights and the aux loss; the selection still ranks the (noisy) logits,
+ *               the same order for any temperature.  1 = plain.
  *   uniform_assignment nonzero: the expert id of slot j of token t is replaced by
  *               (t*k + j) % E; the weights stay those of the real top-k ([MB] section 5,
  *               the benchmark-only uniform assignment).
+ *   soft_topk nonzero: soft top-K ([OPS] "坑3：数值稳定性": instead of a hard top-K, a
+ *               softmax with a temperature over all experts, so that the experts that are
+ *               not selected keep a little probability and receive gradient).  The k best
+ *               experts still run, weighted by p at the selection WITHOUT renormalising
+ *               over the k: topk_w[t,j] = p[t, topk_idx[t,j]], summing to less than 1; the
+ *               rest of the mass belongs to the unselected experts, whose logits get
+ *               gradient through the softmax's denominator (moe_layer_backward_ex).
+ *               0 = renormalised weights (the plain router).
  * Errors: MOE_ERR_ARG for a temperature that is not finite and > 0, or jitter together
  * with MOE_ROUTE_LOGITS_IN; MOE_ERR_UNSUPPORTED for a jitter buffer or x not 16-byte
  * aligned.  With jitter the entry points need moe_router_opts_workspace_bytes(...) bytes
@@ -119,6 +130,7 @@ typedef struct {
   const float* logit_noise;
   float temperature;
   int32_t uniform_assignment;
+  int32_t soft_topk;
 } moe_router_opts_t;
 size_t moe_router_opts_workspace_bytes(int32_t T, int32_t h, moe_dtype_t dt, const moe_router_opts_t* opts);
 moe_status_t moe_route_ex(const void* x, const float* W_gate, const float* logit_bias,
@@ -138,7 +150,9 @@ moe_status_t moe_route_ex(const void* x, const float* W_gate, const float* logit
  *   prob_sum [E] fp32 or NULL (from moe_route), aux_loss: device fp32 scalar or NULL --
  *            when both are given, aux = E * sum_e (counts_e/(T*k)) * (prob_sum_e/T),
  *            unscaled ([OPS] 坑1; [RTR] load-balancing passage; [CAI] MoeLoss).
- *   ws: needs about 8*ceil(T/64)*E + 4*T*k bytes (see moe_workspace_bytes). */
+ *   ws: at least moe_permute_workspace_bytes(T,E,k) bytes (per-block expert counts and
+ *       scatter bases, and the row -> token map). */
+size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k);  /* 0 for invalid sizes */
 moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int32_t h, int32_t E,
                          int32_t k, float capacity_factor, moe_dtype_t dt,
                          int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
@@ -185,6 +199,29 @@ moe_status_t moe_layer_forward(const void* x, const float* W_gate, const float* 
                                void* y, float* aux_loss, int32_t* counts,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Where a moe_layer_forward (or _ex, _train) call left its routing in its workspace:
+ * device pointers into `ws`, valid until the workspace is reused.  The pieces are the
+ * router's and the permutation's results ([OPS] Steps 2-4; [MB] sections 4.1-4.6):
+ *   logits [T,E] fp32 (the router's own, without gate noise), topk_idx [T,k] int32,
+ *   topk_w [T,k] fp32, counts [E] int32 pre-drop (only when the call's `counts` argument
+ *   was NULL; otherwise the counts went there), offsets [E+1] int32 over the kept rows,
+ *   slot_pos [T*k] int32 (-1 = dropped), sorted_slot [>= offsets[E]] int32 (row -> s).
+ * Host only: pointer arithmetic on `ws`, nothing is read or launched.  Errors as for
+ * moe_layer_forward's size checks; MOE_ERR_WORKSPACE when ws_bytes is smaller than
+ * moe_workspace_bytes(...); MOE_ERR_ARG for a NULL ws or out. */
+typedef struct {
+  const float* logits;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* slot_pos;
+  const int32_t* sorted_slot;
+} moe_layer_routing_t;
+moe_status_t moe_layer_routing(const void* ws, size_t ws_bytes, int32_t T, int32_t h, int32_t f, int32_t E,
+                               int32_t k, float capacity_factor, moe_dtype_t dt, moe_act_t act,
+                               moe_layer_routing_t* out);
+
 /* moe_layer_forward with the router variants of moe_router_opts_t (NULL = plain).  ws:
  * moe_workspace_bytes(...) + moe_router_opts_workspace_bytes(T,h,dt,opts) bytes. */
 moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const float* logit_bias,
@@ -205,8 +242,8 @@ moe_status_t moe_layer_forward_ex(const void* x, const float* W_gate, const floa
  *   dl[t,S_j] = w_j (dw_j - sum_j' w_j' dw_j') + d_aux (E/T) p (f - <f, p>) (p the full
  *   softmax, f_e = counts_e / (T k)).
  * Selection and capacity are piecewise constant (no gradient); in bf16 the rounding of
- * Hm passes gradients unchanged, while dW2 uses the rounded Hm.  The plain router only:
- * not the variants of moe_router_opts_t.
+ * Hm passes gradients unchanged, while dW2 uses the rounded Hm.  The plain router; for
+ * the variants of moe_router_opts_t see moe_layer_backward_ex.
  *   fwd_ws / fwd_ws_bytes: the workspace of the moe_layer_forward (or
  *     moe_layer_forward_train) call being differentiated, untouched since (it holds the
  *     routing, Hm and the expert outputs); the other inputs must be that call's.
@@ -227,6 +264,30 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
                                 const float* preact, size_t preact_bytes, void* dx,
                                 float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_backward for a moe_layer_forward_ex call with router variants: the gradients
+ * of the same L through the variant router ([OPS] "坑3" soft top-K and temperature; [CAI]
+ * gate noise; [MB] section 5 jitter).  With p = softmax((logits + noise) / tau):
+ *   renormalised weights: dl[t,S_j] = w_j (dw_j - sum_j' w_j' dw_j') / tau, 0 elsewhere;
+ *   soft top-K: dl[t,b] = p_b (dw_b - sum_j w_j dw_j) / tau for every expert b (dw_b = 0
+ *     when b was not selected, so unselected experts get -p_b sum_j w_j dw_j / tau);
+ *   aux: + d_aux (E/T) p_b (f_b - <f, p>) / tau.
+ * Gate noise is an input: the gradient with respect to the noisy logits is the one with
+ * respect to the logits.  Jitter u: dW_gate = (x u)^T dl and the router's share of dx is
+ * (dl W_gate^T) * u (the rounding of the product passes gradients unchanged).
+ *   opts: the options of that forward call (the same noise and jitter buffers), or NULL
+ *         (= moe_layer_backward).  fwd_ws must be that call's workspace: with jitter it
+ *         holds the router's input after the layer's pieces.
+ *   preact must be NULL when opts is not (MOE_ERR_ARG): the training forward has no
+ *   router variants.  uniform_assignment: MOE_ERR_UNSUPPORTED (a benchmarking mode whose
+ *   ids are not the router's choice).  Other arguments as moe_layer_backward. */
+moe_status_t moe_layer_backward_ex(const void* x, const float* W_gate, const void* W1, const void* W3,
+                                   const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                   float capacity_factor, moe_act_t act, moe_dtype_t dt,
+                                   const moe_router_opts_t* opts, const void* dy, float d_aux, const void* fwd_ws,
+                                   size_t fwd_ws_bytes, const float* preact, size_t preact_bytes, void* dx,
+                                   float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* Training forward: moe_layer_forward (same arguments and results) that also writes the
  * up projection's fp32 pre-activations a (| g) of every kept assignment to `preact`, so

@@ -100,3 +100,23 @@ def check_bf16_out(got, ref, what: str, frac: float = 2e-2):
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond {frac}*RMS + half-ulp; "
                            f"max|d|/RMS {raw:.4f}, beyond-rounding {beyond:.4f}")
     return raw, beyond
+
+
+# ---------------------------------------------------------------- sentinels
+
+SENTINEL = {"bf16": 0x5A5A, "f32": 0x5A5A5A5A}   # finite bit patterns no kernel writes by chance
+
+
+def sentinel_like(shape, dtype: str):
+    """A device tensor of ``shape`` filled with the sentinel bit pattern of ``dtype``."""
+    t = torch()
+    if dtype == "bf16":
+        return t.full(shape, SENTINEL["bf16"], dtype=t.int16, device=dev()).view(t.bfloat16)
+    return t.full(shape, SENTINEL["f32"], dtype=t.int32, device=dev()).view(t.float32)
+
+
+def is_sentinel(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Elementwise: does the host copy (bf16 bits or fp32 values) still hold the sentinel?"""
+    if dtype == "bf16":
+        return np.asarray(a).view(np.uint16) == SENTINEL["bf16"]
+    return np.asarray(a, dtype=np.float32).view(np.uint32) == SENTINEL["f32"]

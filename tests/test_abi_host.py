@@ -42,7 +42,8 @@ def test_exports_every_declared_symbol(L):
                           "moe_layer_forward_binned", "moe_layer_forward_binned_timed",
                           "moe_router_opts_workspace_bytes", "moe_route_ex", "moe_layer_forward_ex",
                           "moe_layer_backward_workspace_bytes", "moe_layer_backward", "moe_layer_backward_timed",
-                          "moe_layer_preact_bytes", "moe_layer_forward_train"}
+                          "moe_layer_preact_bytes", "moe_layer_forward_train", "moe_permute_workspace_bytes",
+                          "moe_layer_backward_ex", "moe_layer_routing"}
     for n in names:
         assert hasattr(L, n), n
     out = os.popen(f"nm -D --defined-only {moe.lib_path}").read()
@@ -184,6 +185,10 @@ def test_permute_host_errors(L):
     assert call(h=32) == UNSUP
     assert call(xp=MIS) == UNSUP
     assert call(wsb=8) == WS
+    need = L.moe_permute_workspace_bytes(16, 8, 2)
+    assert need >= 2 * 4 * 8 + 4 * 16 * 2        # per-block counts and bases, row -> token map
+    assert call(wsb=need - 1) == WS
+    assert L.moe_permute_workspace_bytes(16, 8, 9) == 0 and L.moe_permute_workspace_bytes(-1, 8, 2) == 0
     assert call(T=0) == OK
 
 
@@ -291,8 +296,8 @@ def test_layer_forward_binned_workspace_boundary(L):
     assert _binned(L, ws_bytes=need - 1) == WS
 
 
-def _ropts(jitter=None, noise=None, temperature=1.0, uniform=0):
-    return ctypes.byref(moe.RouterOpts(jitter, noise, temperature, uniform))
+def _ropts(jitter=None, noise=None, temperature=1.0, uniform=0, soft=0):
+    return ctypes.byref(moe.RouterOpts(jitter, noise, temperature, uniform, soft))
 
 
 def test_router_opts_workspace_bytes(L):
@@ -419,3 +424,68 @@ def test_bench_refuses_several_gpus():
                        text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stdout
+
+
+def test_32bit_operand_offsets_are_refused(L):
+    """The expert GEMMs address their left operand with 32-bit element offsets (x for the
+    gathered up projection, x_perm and the hidden activation Hm): sizes where T*h, R*h or
+    R*f reach 2^32 return MOE_ERR_UNSUPPORTED on the host instead of wrapping."""
+    # T*k*f = 262144 * 2 * 14336 ~ 7.5e9: the hidden activation's offsets would wrap
+    assert _layer(L, T=262144, h=4096, f=14336, E=8, k=2) == UNSUP
+    # a capacity that keeps R = E*C rows small enough passes the check (then: workspace)
+    assert _layer(L, T=262144, h=4096, f=14336, E=8, k=2, cf=0.25, ws_bytes=1000) == WS
+    # T*h = 2^32 exactly (x of the gathered up projection), R*f below it
+    assert _layer(L, T=1 << 20, h=4096, f=64, E=256, k=1, cf=0.001, ws_bytes=1000) == UNSUP
+    assert _layer(L, T=(1 << 20) - 1, h=4096, f=64, E=256, k=1, cf=0.001, ws_bytes=1000) == WS
+    f = L.moe_expert_ffn
+    # (x_perm, offsets, R_max, h, f, E, W1, W3, W2, act, dt, out, ws, ws_bytes, stream)
+    assert f(FAKE, FAKE, 1 << 19, 64, 8192, 8, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, 100, None) == UNSUP
+    assert f(FAKE, FAKE, (1 << 19) - 1, 64, 8192, 8, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, 100, None) == WS
+    assert f(FAKE, FAKE, 1 << 20, 4096, 64, 8, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, 100, None) == UNSUP
+    # the backward runs the same GEMMs
+    bw = L.moe_layer_backward
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 262144, 4096, 14336, 8, 2, 0.0, 1, 1, FAKE, 0.0, FAKE, 1 << 45, None, 0, FAKE,
+         None, FAKE, FAKE, FAKE, FAKE, 1 << 45, None]
+    assert bw(*a) == UNSUP
+    a[10] = 0.25   # capacity 16384 per expert: R*f < 2^32
+    a[16] = 1000   # then the forward's workspace is too small
+    assert bw(*a) == WS
+
+
+def test_layer_backward_ex_host_errors(L):
+    T, h, f, E, k = 64, 128, 256, 8, 2
+    fwd = moe.workspace_bytes(T, h, f, E, k, 0.0, 1, 1)
+    bws = L.moe_layer_backward_workspace_bytes(T, h, f, E, k, 0.0, 1, 1)
+
+    def call(opts, pre=None, preb=0, fwsb=fwd, x=FAKE, T_=T):
+        return L.moe_layer_backward_ex(x, FAKE, FAKE, FAKE, FAKE, T_, h, f, E, k, 0.0, 1, 1, opts, FAKE, 0.0, FAKE,
+                                       fwsb, pre, preb, FAKE, None, FAKE, FAKE, FAKE, FAKE, bws, None)
+    assert call(_ropts(temperature=0.0)) == ARG
+    assert call(_ropts(temperature=float("nan"), soft=1)) == ARG
+    assert call(_ropts(uniform=1)) == UNSUP             # benchmarking mode: not differentiated
+    assert call(_ropts(soft=1), pre=FAKE, preb=1 << 30) == ARG   # the training forward has no variants
+    assert call(_ropts(jitter=MIS)) == UNSUP
+    # with jitter the forward's workspace also holds the router's input x * u
+    extra = L.moe_router_opts_workspace_bytes(T, h, 1, _ropts(FAKE))
+    assert call(_ropts(jitter=FAKE), fwsb=fwd + extra - 1) == WS
+    assert call(_ropts(soft=1), fwsb=fwd - 1) == WS
+    assert call(_ropts(soft=1, temperature=0.5), T_=0) == OK
+
+
+def test_layer_routing_host_errors(L):
+    T, h, f, E, k = 64, 128, 256, 8, 2
+    need = moe.workspace_bytes(T, h, f, E, k, 0.0, 1, 1)
+    r = moe.LayerRouting()
+    # (ws, ws_bytes, T, h, f, E, k, cf, dt, act, out)
+    assert L.moe_layer_routing(FAKE, need, T, h, f, E, k, 0.0, 1, 1, None) == ARG
+    assert L.moe_layer_routing(None, need, T, h, f, E, k, 0.0, 1, 1, ctypes.byref(r)) == ARG
+    assert L.moe_layer_routing(FAKE, need - 1, T, h, f, E, k, 0.0, 1, 1, ctypes.byref(r)) == WS
+    assert L.moe_layer_routing(FAKE, need, T, 96, f, E, k, 0.0, 1, 1, ctypes.byref(r)) == UNSUP
+    assert L.moe_layer_routing(FAKE, need, T, h, f, E, k, 0.0, 1, 1, ctypes.byref(r)) == OK
+    # the pieces lie inside the workspace, in its documented order, without overlaps
+    ptrs = [r.logits, r.topk_idx, r.topk_w, r.counts, r.offsets, r.slot_pos, r.sorted_slot]
+    sizes = [T * E * 4, T * k * 4, T * k * 4, E * 4, (E + 1) * 4, T * k * 4, T * k * 4]
+    assert all(FAKE <= p and p + n <= FAKE + need for p, n in zip(ptrs, sizes))
+    assert ptrs == sorted(ptrs)
+    assert all(a + n <= b for a, b, n in zip(ptrs, ptrs[1:], sizes))
+

@@ -71,10 +71,11 @@ def _cmp(got, ref, dtype, what, scale=None, bf16_out=False):
         gu.check_rel_rms(got, ref, 1e-4, what)
 
 
-def _check_all(w, host, g, gl, dy_host, tokens=None, experts=None, with_w_gate=True):
+def _check_all(w, host, g, gl, dy_host, tokens=None, experts=None, with_w_gate=True, variants=None):
     ref = o.layer_backward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"],
                            dy_host, D_AUX, k=w.k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, logits=gl,
-                           tokens=tokens, experts=experts, with_w_gate=with_w_gate, with_scale=True)
+                           tokens=tokens, experts=experts, with_w_gate=with_w_gate, with_scale=True,
+                           **(variants or {}))
     sc = ref["scale"]
     tok = np.arange(w.T) if tokens is None else np.asarray(tokens)
     dx = gu.as_f64(gu.from_dev(g["dx"])[tok], w.dtype)
@@ -134,6 +135,8 @@ def test_backward_full_size(name):
 
 @pytest.mark.parametrize("name", ["prefill-mixtral", "finegrained-e256"])
 def test_backward_full_size_sampled(name):
+    """dx on sampled tokens, dW_gate in full (it takes every token's logit gradient), and
+    the weight gradients of the experts with the fewest and the most rows."""
     _say(f"backward {name} (sampled)")
     w, host, dd = gu.workload(name)
     dy = _dy(w.T, w.h, w.dtype)
@@ -141,9 +144,11 @@ def test_backward_full_size_sampled(name):
     counts = o.histogram(o.select_topk(gl, w.k), w.E)
     live = np.nonzero(counts > 0)[0]
     e_small = int(live[np.argmin(counts[live])])
+    e_big = int(np.argmax(counts))
     tokens = np.sort(np.random.default_rng(5).choice(w.T, 48, replace=False))
-    _say(f"  experts checked: {e_small} ({int(counts[e_small])} rows); tokens: {len(tokens)}")
-    _check_all(w, host, g, gl, dy, tokens=tokens, experts=[e_small], with_w_gate=False)
+    _say(f"  experts checked: {e_small} ({int(counts[e_small])} rows), {e_big} ({int(counts[e_big])} rows); "
+         f"tokens: {len(tokens)}; dW_gate in full")
+    _check_all(w, host, g, gl, dy, tokens=tokens, experts=[e_small, e_big], with_w_gate=True)
 
 
 def test_backward_deterministic():
@@ -221,3 +226,73 @@ def test_saved_preactivations_parity(T, h, f, E, k, cf, act, dtype):
                            capacity_factor=cf, act=act, fwd_ws=fws, d_aux=D_AUX, preact=pre)
     torch.cuda.synchronize()
     _check_all(w, host, g, gu.from_dev(logits), dy)
+
+
+VARIANTS = {
+    "soft": dict(soft=True),
+    "soft-temperature-0.6-noise": dict(soft=True, temperature=0.6, noise=True),
+    "temperature-1.5-jitter": dict(temperature=1.5, jitter=True),
+    "soft-noise-jitter": dict(soft=True, noise=True, jitter=True, temperature=0.8),
+}
+
+
+def _variant_case(w, host, dd, spec):
+    vi = mw.router_variant_inputs(w)
+    h_kw = dict(temperature=spec.get("temperature", 1.0), soft=spec.get("soft", False),
+                noise=vi["noise"] if spec.get("noise") else None, jitter=vi["jitter"] if spec.get("jitter") else None)
+    d_kw = dict(h_kw, noise=gu.to_dev(h_kw["noise"], "f32") if h_kw["noise"] is not None else None,
+                jitter=gu.to_dev(h_kw["jitter"], w.dtype) if h_kw["jitter"] is not None else None)
+    return h_kw, d_kw
+
+
+def _run_variant(w, dd, dy_host, d_kw):
+    torch = gu.torch()
+    dt = moe.BF16 if w.dtype == "bf16" else moe.F32
+    a = moe.SWIGLU if w.act == "swiglu" else moe.GELU
+    opts = moe._opts(d_kw["jitter"], d_kw["noise"], d_kw["temperature"], False, dd["x"], w.T, w.E, d_kw["soft"])
+    extra = moe.lib().moe_router_opts_workspace_bytes(w.T, w.h, dt, moe.ctypes.byref(opts))
+    fws = moe._ws(moe.workspace_bytes(w.T, w.h, w.f, w.E, w.k, w.cf, dt, a) + extra, dd["x"].device)
+    args = (dd["x"], dd["W_gate"], dd["logit_bias"], dd["W1"], dd["W3"], dd["W2"])
+    moe.layer_forward(*args, k=w.k, capacity_factor=w.cf, act=w.act, ws=fws, **d_kw)
+    logits, _, _, _ = moe.route(dd["x"], dd["W_gate"], dd["logit_bias"], w.k, jitter=d_kw["jitter"])
+    g = moe.layer_backward(dd["x"], dd["W_gate"], dd["W1"], dd["W3"], dd["W2"], gu.to_dev(dy_host, w.dtype), k=w.k,
+                           capacity_factor=w.cf, act=w.act, fwd_ws=fws, d_aux=D_AUX, **d_kw)
+    torch.cuda.synchronize()
+    return g, gu.from_dev(logits)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("T,h,f,E,k,cf,act,dtype", [
+    (200, 256, 512, 8, 2, 0.0, "swiglu", "bf16"),
+    (130, 192, 256, 16, 3, 1.0, "gelu", "f32"),
+    (64, 512, 1024, 8, 2, 0.6, "swiglu", "bf16"),      # one block of tokens, drops
+])
+def test_backward_router_variants(variant, T, h, f, E, k, cf, act, dtype):
+    """moe_layer_backward_ex against the oracle's backward through the same variant router:
+    soft top-K and temperature (the logit gradient reaches unselected experts, and with it
+    every column of dW_gate), gate noise, jitter of the router input."""
+    _say(f"backward variant {variant} T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")
+    rng = np.random.default_rng(T + 5 * E)
+    conv = (lambda a: mw.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32),
+                logit_bias=rng.standard_normal(E).astype(np.float32),
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)) if act == "swiglu" else None,
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("variant", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
+    h_kw, d_kw = _variant_case(w, host, dd, VARIANTS[variant])
+    dy = _dy(T, h, dtype)
+    g, gl = _run_variant(w, dd, dy, d_kw)
+    _check_all(w, host, g, gl, dy, variants=h_kw)
+
+
+@pytest.mark.parametrize("name,variant", [("decode-mixtral", "soft"), ("capacity-e64", "soft-noise-jitter")])
+def test_backward_router_variants_full_size(name, variant):
+    _say(f"backward variant {variant} {name}")
+    w, host, dd = gu.workload(name)
+    h_kw, d_kw = _variant_case(w, host, dd, VARIANTS[variant])
+    dy = _dy(w.T, w.h, w.dtype)
+    g, gl = _run_variant(w, dd, dy, d_kw)
+    _check_all(w, host, g, gl, dy, variants=h_kw)

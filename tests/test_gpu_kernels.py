@@ -139,8 +139,9 @@ def test_permute_parity(case):
     x = mw.f32_to_bf16_bits(np.random.default_rng(T).standard_normal((T, h)).astype(np.float32))
     probs = np.random.default_rng(1).dirichlet(np.ones(E), size=T).astype(np.float32)
     ps = probs.astype(np.float64).sum(0).astype(np.float32)
+    xps = gu.sentinel_like((T * k, h), "bf16")
     r = moe.permute(torch.from_numpy(idx).to(gu.dev()), gu.to_dev(x, "bf16"), E, cf,
-                    prob_sum=gu.to_dev(ps, "f32"))
+                    prob_sum=gu.to_dev(ps, "f32"), x_perm=xps)
     torch.cuda.synchronize()
     C = o.expert_capacity(T, E, k, cf)
     counts, offsets, sorted_slot, slot_pos = o.permute(idx, E, C)
@@ -149,8 +150,10 @@ def test_permute_parity(case):
     assert np.array_equal(gu.from_dev(r["offsets"]), offsets)
     assert np.array_equal(gu.from_dev(r["slot_pos"]), slot_pos)
     assert np.array_equal(gu.from_dev(r["sorted_slot"])[:R], sorted_slot[:R])
-    xp = gu.from_dev(r["x_perm"])[:R]
+    xp_all = gu.from_dev(r["x_perm"])
+    xp = xp_all[:R]
     assert np.array_equal(xp, x[sorted_slot[:R] // k])
+    assert gu.is_sentinel(xp_all[R:], "bf16").all()   # only the kept rows are written
     aux = float(gu.from_dev(r["aux"]))
     ref = E * float(np.sum(counts / (T * k) * (ps.astype(np.float64) / T)))
     assert abs(aux - ref) <= 1e-5 * abs(ref)
@@ -196,7 +199,7 @@ def _rand(shape, scale, rng, dtype):
 def _ffn_case(E, h, f, seg, act, dtype, seed):
     rng = np.random.default_rng(seed)
     R = int(sum(seg))
-    R_max = R + 7  # rows beyond offsets[E] must stay untouched
+    R_max = R + 7  # rows beyond offsets[E] must stay untouched (checked with a sentinel)
     xp = _rand((R_max, h), 1.0, rng, dtype)
     W1 = _rand((E, h, f), 1 / math.sqrt(h), rng, dtype)
     W3 = _rand((E, h, f), 1 / math.sqrt(h), rng, dtype) if act == "swiglu" else None
@@ -223,9 +226,12 @@ def test_expert_ffn_parity(act, dtype, E, h, f, seg):
     xp, W1, W3, W2, offsets, R = _ffn_case(E, h, f, seg, act, dtype, seed=E * 7 + h)
     dx = gu.to_dev(xp, dtype)
     out = moe.expert_ffn(dx, torch.from_numpy(offsets).to(gu.dev()), gu.to_dev(W1, dtype), gu.to_dev(W3, dtype),
-                         gu.to_dev(W2, dtype), act)
+                         gu.to_dev(W2, dtype), act, out=gu.sentinel_like(tuple(dx.shape), dtype))
     torch.cuda.synchronize()
-    got = gu.as_f64(gu.from_dev(out), dtype)
+    raw = gu.from_dev(out)
+    assert gu.is_sentinel(raw[R:], dtype).all(), "rows past offsets[E] were written"
+    assert not gu.is_sentinel(raw[:R], dtype).any(), "a kept row was not written"
+    got = gu.as_f64(raw[:R], dtype)
     a64 = gu.as_f64(xp, dtype)
     for e in range(E):
         lo, hi = offsets[e], offsets[e + 1]

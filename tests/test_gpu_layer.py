@@ -26,19 +26,39 @@ def _say(*a):
 
 
 def _run_layer(w, d_host, d_dev):
+    """The layer on a sentinel-filled y, with its workspace kept: returns y, aux, counts,
+    the router's logits (from moe_route, the same kernel) and the routing the layer left
+    in its workspace (moe_layer_routing)."""
     torch = gu.torch()
+    dt = moe.BF16 if w.dtype == "bf16" else moe.F32
+    ws = moe._ws(moe.workspace_bytes(w.T, w.h, w.f, w.E, w.k, w.cf, dt, moe.SWIGLU if w.act == "swiglu" else moe.GELU),
+                 d_dev["x"].device)
+    y = gu.sentinel_like(tuple(d_dev["x"].shape), w.dtype)
     y, aux, counts = moe.layer_forward(d_dev["x"], d_dev["W_gate"], d_dev["logit_bias"], d_dev["W1"], d_dev["W3"],
-                                       d_dev["W2"], k=w.k, capacity_factor=w.cf, act=w.act)
+                                       d_dev["W2"], k=w.k, capacity_factor=w.cf, act=w.act, ws=ws, y=y)
     logits, idx, _, _ = moe.route(d_dev["x"], d_dev["W_gate"], d_dev["logit_bias"], w.k)
     torch.cuda.synchronize()
-    return y, aux, counts, logits
+    routing = moe.layer_routing(ws, T=w.T, h=w.h, f=w.f, E=w.E, k=w.k, capacity_factor=w.cf, dtype=dt, act=w.act)
+    routing = {kk: gu.from_dev(v).copy() for kk, v in routing.items()}
+    return y, aux, counts, logits, routing
 
 
-def _check_layer(w, host, y, aux, counts, logits, tokens):
+def _check_layer(w, host, y, aux, counts, logits, tokens, routing=None):
     gl = gu.from_dev(logits)
     ref = o.layer_forward(host["x"], host["W_gate"], host["logit_bias"], host["W1"], host["W3"], host["W2"],
                           k=w.k, capacity_factor=w.cf, act=w.act, dtype=w.dtype, logits=gl, tokens=tokens)
     assert np.array_equal(gu.from_dev(counts), ref["counts"])
+    assert not gu.is_sentinel(gu.from_dev(y), w.dtype).any(), "a row of y was not written"
+    if routing is not None:
+        # the layer's own routing, bit for bit: the same logits, selection, permutation and drops
+        R = int(ref["offsets"][-1])
+        assert np.array_equal(routing["logits"], gl)
+        assert np.array_equal(routing["topk_idx"], ref["topk_idx"])
+        assert np.array_equal(routing["offsets"], ref["offsets"])
+        assert np.array_equal(routing["slot_pos"], ref["slot_pos"])
+        assert np.array_equal(routing["slot_pos"] < 0, ref["slot_pos"] < 0)      # the drop mask
+        assert np.array_equal(routing["sorted_slot"][:R], ref["sorted_slot"][:R])
+        gu.check_rel_rms(routing["topk_w"], ref["topk_w"], 1e-5, "topk_w")
     R = int(ref["offsets"][-1])
     _say(f"  rows kept {R} of {w.T * w.k}; active experts {int((ref['counts'] > 0).sum())}; C={ref['C']}")
     a = float(gu.from_dev(aux))
@@ -56,13 +76,13 @@ def _check_layer(w, host, y, aux, counts, logits, tokens):
 def test_layer_forward_parity(name):
     _say(f"layer {name}")
     w, host, dd = gu.workload(name)
-    y, aux, counts, logits = _run_layer(w, host, dd)
+    y, aux, counts, logits, routing = _run_layer(w, host, dd)
     if w.T <= 64:
         tokens = np.arange(w.T)
     else:
         tokens = np.sort(np.random.default_rng(123).choice(w.T, SAMPLE, replace=False))
         tokens[0], tokens[-1] = 0, w.T - 1  # include both ends of the batch
-    _check_layer(w, host, y, aux, counts, logits, tokens)
+    _check_layer(w, host, y, aux, counts, logits, tokens, routing)
 
 
 def test_layer_forward_deterministic():
@@ -91,6 +111,9 @@ def test_layer_forward_deterministic():
     (40, 2048, 1024, 6, 2, 0.5, "gelu", "bf16"),     # K-split GEMMs with drops
     (64, 128, 128, 256, 16, 0.0, "swiglu", "bf16"),  # the largest E and k the library takes
     (96, 64, 128, 256, 16, 1.0, "gelu", "f32"),      # ... in fp32, with drops
+    (64, 256, 512, 8, 2, 0.5, "swiglu", "bf16"),     # one block of tokens (fused scan and scatter), drops
+    (50, 128, 256, 16, 3, 0.4, "gelu", "bf16"),      # ... ragged, heavy drops
+    (64, 128, 128, 64, 4, 0.7, "swiglu", "f32"),     # ... 64 experts, fp32
 ])
 def test_layer_edge_cases(T, h, f, E, k, cf, act, dtype):
     import math
@@ -105,8 +128,8 @@ def test_layer_edge_cases(T, h, f, E, k, cf, act, dtype):
                 W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
     dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
     w = mw.Workload("edge", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
-    y, aux, counts, logits = _run_layer(w, host, dd)
-    ref = _check_layer(w, host, y, aux, counts, logits, np.arange(T))
+    y, aux, counts, logits, routing = _run_layer(w, host, dd)
+    ref = _check_layer(w, host, y, aux, counts, logits, np.arange(T), routing)
     if cf > 0:
         dropped = (ref["slot_pos"].reshape(T, k) < 0).all(1)
         if dropped.any():

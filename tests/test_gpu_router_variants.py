@@ -22,6 +22,9 @@ VARIANTS = {
     "uniform": dict(uniform=True),
     "jitter": dict(jitter=True),
     "all": dict(jitter=True, noise=True, temperature=0.7, uniform=True),
+    "soft": dict(soft=True),
+    "soft-temperature-0.5": dict(soft=True, temperature=0.5),
+    "soft-noise-jitter-1.5": dict(soft=True, noise=True, jitter=True, temperature=1.5),
 }
 
 
@@ -33,10 +36,11 @@ def _variant_args(w, spec, dev_dtype):
     vi = mw.router_variant_inputs(w)
     host = dict(jitter=vi["jitter"] if spec.get("jitter") else None,
                 noise=vi["noise"] if spec.get("noise") else None,
-                temperature=spec.get("temperature", 1.0), uniform=spec.get("uniform", False))
+                temperature=spec.get("temperature", 1.0), uniform=spec.get("uniform", False),
+                soft=spec.get("soft", False))
     dev = dict(jitter=gu.to_dev(host["jitter"], dev_dtype) if host["jitter"] is not None else None,
                noise=gu.to_dev(host["noise"], "f32") if host["noise"] is not None else None,
-               temperature=host["temperature"], uniform=host["uniform"])
+               temperature=host["temperature"], uniform=host["uniform"], soft=host["soft"])
     return host, dev
 
 
@@ -57,15 +61,20 @@ def test_route_variant_parity(name, variant):
     gl = gu.from_dev(logits)
     xr = d["x"] if host["jitter"] is None else o.jitter_input(d["x"], host["jitter"], w.dtype)
     gu.check_rel_rms(gl, o.router_logits(xr, d["W_gate"], d["logit_bias"], w.dtype), 1e-5, "logits")
-    ref = o.route(gl, w.k, noise=host["noise"], temperature=host["temperature"], uniform=host["uniform"])
+    ref = o.route(gl, w.k, noise=host["noise"], temperature=host["temperature"], uniform=host["uniform"],
+                  soft=host["soft"])
     assert np.array_equal(gu.from_dev(idx), ref["topk_idx"])
     gu.check_rel_rms(gu.from_dev(wt), ref["topk_w"], 1e-5, "topk_w")
+    if host["soft"] and w.k < w.E:
+        assert (gu.from_dev(wt).astype(np.float64).sum(1) < 1.0).all()   # mass left to unselected experts
     gu.check_rel_rms(gu.from_dev(ps), ref["probs"].sum(0), 1e-5, "prob_sum")
 
 
 @pytest.mark.parametrize("name,variant", [("tiny-fp32", "all"), ("capacity-e64", "noise-temperature-2"),
                                           ("capacity-e64", "jitter"), ("prefill-mixtral", "uniform"),
-                                          ("decode-mixtral", "all")])
+                                          ("decode-mixtral", "all"), ("decode-mixtral", "soft"),
+                                          ("prefill-mixtral", "soft-temperature-0.5"),
+                                          ("capacity-e64", "soft-noise-jitter-1.5"), ("tiny-fp32", "soft")])
 def test_layer_forward_variant_parity(name, variant):
     torch = gu.torch()
     _say(f"layer {name} {variant}")
@@ -82,7 +91,7 @@ def test_layer_forward_variant_parity(name, variant):
     ref = o.layer_forward(host_in["x"], host_in["W_gate"], host_in["logit_bias"], host_in["W1"], host_in["W3"],
                           host_in["W2"], k=w.k, capacity_factor=w.cf, act=w.act, dtype=w.dtype,
                           logits=gu.from_dev(logits), tokens=tokens, noise=host["noise"],
-                          temperature=host["temperature"], uniform=host["uniform"])
+                          temperature=host["temperature"], uniform=host["uniform"], soft=host["soft"])
     assert np.array_equal(gu.from_dev(counts), ref["counts"])
     if host["uniform"]:
         assert len(set(ref["counts"].tolist())) <= 2   # balanced up to one when E does not divide T*k

@@ -18,7 +18,8 @@ import os
 __all__ = ["MoEError", "lib", "lib_path", "capacity", "workspace_bytes", "status_string", "route",
            "permute", "expert_ffn", "unpermute", "layer_forward", "LAYER_STAGES", "F32", "BF16", "GELU", "SWIGLU",
            "ROUTE_LOGITS_IN", "layer_backward", "layer_forward_binned", "preact_bytes", "BACKWARD_STAGES",
-           "BINNED_STAGES", "binned_capacity_max", "binned_workspace_bytes", "CapacityConfig", "RouterOpts"]
+           "BINNED_STAGES", "binned_capacity_max", "binned_workspace_bytes", "CapacityConfig", "RouterOpts",
+           "layer_routing", "LayerRouting"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoe_mi355x.so")
@@ -35,12 +36,18 @@ _sz = ctypes.c_size_t
 
 class RouterOpts(ctypes.Structure):
     """moe_router_opts_t: router-input jitter, gate noise, softmax temperature, uniform
-    expert assignment (device pointers as integers, or None)."""
+    expert assignment, soft top-K weights (device pointers as integers, or None)."""
     _fields_ = [("jitter", ctypes.c_void_p), ("logit_noise", ctypes.c_void_p), ("temperature", ctypes.c_float),
-                ("uniform_assignment", ctypes.c_int32)]
+                ("uniform_assignment", ctypes.c_int32), ("soft_topk", ctypes.c_int32)]
 
 
 _opts_p = ctypes.POINTER(RouterOpts)
+
+
+class LayerRouting(ctypes.Structure):
+    """moe_layer_routing_t: device pointers into a layer call's workspace."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("logits", "topk_idx", "topk_w", "counts", "offsets", "slot_pos",
+                                              "sorted_slot")]
 
 _SIGS = {
     "moe_capacity": (_i32, [_i32, _i32, _i32, _f32]),
@@ -51,6 +58,7 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, ctypes.c_int,
                                  ctypes.c_uint32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz,
                                  _c_void_p]),
+    "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _f32, ctypes.c_int,
                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p, _c_void_p, _sz, _c_void_p]),
@@ -66,6 +74,8 @@ _SIGS = {
                                                _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
                                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p,
                                                _c_void_p]),
+    "moe_layer_routing": (ctypes.c_int, [_c_void_p, _sz, _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int,
+                                         ctypes.c_int, ctypes.POINTER(LayerRouting)]),
     "moe_router_opts_workspace_bytes": (_sz, [_i32, _i32, ctypes.c_int, _opts_p]),
     "moe_route_ex": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, ctypes.c_int,
                                     ctypes.c_uint32, _opts_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -79,6 +89,10 @@ _SIGS = {
                                           _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _c_void_p, _f32, _c_void_p,
                                           _sz, _c_void_p, _sz, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                           _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_layer_backward_ex": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                                             _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _opts_p, _c_void_p,
+                                             _f32, _c_void_p, _sz, _c_void_p, _sz, _c_void_p, _c_void_p, _c_void_p,
+                                             _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
     "moe_layer_backward_timed": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                                 _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _c_void_p, _f32,
                                                 _c_void_p, _sz, _c_void_p, _sz, _c_void_p, _c_void_p, _c_void_p,
@@ -214,23 +228,23 @@ def _ws(nbytes: int, dev):
     return _torch().empty(max(int(nbytes), 1), dtype=_torch().uint8, device=dev)
 
 
-def _opts(jitter, noise, temperature, uniform, x=None, T=None, E=None):
+def _opts(jitter, noise, temperature, uniform, x=None, T=None, E=None, soft=False):
     """A RouterOpts for the given variants, or None when all are at their defaults."""
-    if jitter is None and noise is None and float(temperature) == 1.0 and not uniform:
+    if jitter is None and noise is None and float(temperature) == 1.0 and not uniform and not soft:
         return None
     torch = _torch()
     if jitter is not None and (x is None or jitter.shape != x.shape or jitter.dtype != x.dtype):
         raise ValueError("jitter must have x's shape and dtype")
     if noise is not None and (tuple(noise.shape) != (T, E) or noise.dtype != torch.float32):
         raise ValueError("noise must be fp32 [T, E]")
-    return RouterOpts(_p(jitter), _p(noise), float(temperature), 1 if uniform else 0)
+    return RouterOpts(_p(jitter), _p(noise), float(temperature), 1 if uniform else 0, 1 if soft else 0)
 
 
 def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = False, jitter=None, noise=None,
-          temperature: float = 1.0, uniform: bool = False):
+          temperature: float = 1.0, uniform: bool = False, soft: bool = False):
     """Router on ``x[T,h]`` (or on given fp32 ``logits[T,E]``), optionally with the
     router variants (``jitter`` [T,h] in x's dtype, gate ``noise`` [T,E] fp32, softmax
-    ``temperature``, ``uniform`` expert assignment).
+    ``temperature``, ``uniform`` expert assignment, ``soft`` top-K weights).
 
     Returns ``(logits, topk_idx, topk_w, prob_sum)`` (prob_sum is None unless
     requested)."""
@@ -239,7 +253,7 @@ def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = F
     dev = ref.device
     T = ref.shape[0]
     E = (logits if logits is not None else W_gate).shape[-1]
-    opts = _opts(jitter, noise, temperature, uniform, x, T, E)
+    opts = _opts(jitter, noise, temperature, uniform, x, T, E, soft)
     h = 0 if x is None else x.shape[1]
     dt = F32 if x is None else _dt(x)
     flags = ROUTE_LOGITS_IN if logits is not None else 0
@@ -261,11 +275,14 @@ def route(x, W_gate, logit_bias, k: int, *, logits=None, with_prob_sum: bool = F
     return out_logits, idx, w, ps
 
 
-def permute(topk_idx, x, E: int, capacity_factor: float, *, with_x_perm: bool = True, prob_sum=None):
+def permute(topk_idx, x, E: int, capacity_factor: float, *, with_x_perm: bool = True, prob_sum=None,
+            x_perm=None):
     """Histogram, capacity, stable sort by expert id and gather.
 
     Returns a dict with ``counts``, ``offsets``, ``sorted_slot``, ``slot_pos``,
-    ``x_perm`` (or None) and ``aux`` (0-d tensor, or None without prob_sum)."""
+    ``x_perm`` (or None) and ``aux`` (0-d tensor, or None without prob_sum).
+    ``x_perm``: a preallocated ``[T*k, h]`` output (rows past the kept count are left
+    as they are)."""
     torch = _torch()
     dev = topk_idx.device
     T, k = topk_idx.shape
@@ -276,10 +293,10 @@ def permute(topk_idx, x, E: int, capacity_factor: float, *, with_x_perm: bool = 
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     sorted_slot = torch.full((n,), -1, dtype=torch.int32, device=dev)
     slot_pos = torch.empty(n, dtype=torch.int32, device=dev)
-    x_perm = torch.empty((n, h), dtype=x.dtype, device=dev) if (with_x_perm and x is not None) else None
+    if x_perm is None and with_x_perm and x is not None:
+        x_perm = torch.empty((n, h), dtype=x.dtype, device=dev)
     aux = torch.empty((), dtype=torch.float32, device=dev) if prob_sum is not None else None
-    nhb = -(-T // 64)
-    ws = _ws(8 * nhb * E + 4 * n + 4096, dev)
+    ws = _ws(lib().moe_permute_workspace_bytes(T, E, k), dev)
     st = lib().moe_permute(_p(topk_idx), _p(x) if x_perm is not None else None, T, h, E, k,
                            float(capacity_factor), dt, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_pos),
                            _p(x_perm), _p(prob_sum), _p(aux), _p(ws), ws.numel(), _stream(dev))
@@ -288,14 +305,18 @@ def permute(topk_idx, x, E: int, capacity_factor: float, *, with_x_perm: bool = 
                 aux=aux)
 
 
-def expert_ffn(x_perm, offsets, W1, W3, W2, act: str):
-    """Grouped expert MLP over the segments of ``x_perm``; returns ``out_perm[R_max,h]``."""
+def expert_ffn(x_perm, offsets, W1, W3, W2, act: str, out=None):
+    """Grouped expert MLP over the segments of ``x_perm``; returns ``out_perm[R_max,h]``
+    (``out``: a preallocated one; rows from ``offsets[E]`` on are not written)."""
     torch = _torch()
     dev = x_perm.device
     R_max, h = x_perm.shape
     E, _, f = W1.shape
     dt = _dt(x_perm)
-    out = torch.empty_like(x_perm)
+    if out is None:
+        out = torch.empty_like(x_perm)
+    elif out.shape != x_perm.shape or out.dtype != x_perm.dtype:
+        raise ValueError("out must have x_perm's shape and dtype")
     ws = _ws(lib().moe_expert_ffn_workspace_bytes(R_max, h, f, E, dt, _ACT[act]), dev)
     st = lib().moe_expert_ffn(_p(x_perm), _p(offsets), R_max, h, f, E, _p(W1), _p(W3), _p(W2), _ACT[act], dt,
                               _p(out), _p(ws), ws.numel(), _stream(dev))
@@ -322,19 +343,19 @@ def preact_bytes(T: int, h: int, f: int, E: int, k: int, capacity_factor: float,
 
 def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float, act: str,
                   ws=None, y=None, aux=None, counts=None, events=None, jitter=None, noise=None,
-                  temperature: float = 1.0, uniform: bool = False, preact=None):
+                  temperature: float = 1.0, uniform: bool = False, soft: bool = False, preact=None):
     """The whole layer.  Returns ``(y, aux_loss, counts)``.  Pass preallocated
     ``ws``/``y``/``aux``/``counts`` to avoid allocations in a timed loop.
     ``events``: a ctypes array of ``len(LAYER_STAGES) + 1`` hipEvent_t handles to
     record between the stages (the measurement variant of the entry point).
-    ``jitter``/``noise``/``temperature``/``uniform``: the router variants (see route).
+    ``jitter``/``noise``/``temperature``/``uniform``/``soft``: the router variants (see route).
     ``preact``: a uint8 device tensor of ``preact_bytes(...)`` bytes: the training forward,
     which also saves the up projection's pre-activations there for layer_backward."""
     torch = _torch()
     dev = x.device
     T, h = x.shape
     E, _, f = W1.shape
-    opts = _opts(jitter, noise, temperature, uniform, x, T, E)
+    opts = _opts(jitter, noise, temperature, uniform, x, T, E, soft)
     if opts is not None and events is not None:
         raise ValueError("the measurement entry point takes no router variants")
     if opts is not None and preact is not None:
@@ -366,6 +387,30 @@ def layer_forward(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor:
     else:
         _check(lib().moe_layer_forward_timed(*args, ctypes.cast(events, _c_void_p)), "moe_layer_forward_timed")
     return y, aux, counts
+
+
+def layer_routing(ws, *, T: int, h: int, f: int, E: int, k: int, capacity_factor: float, dtype, act: str) -> dict:
+    """The routing that the layer call using workspace ``ws`` left there (moe_layer_routing):
+    torch views (no copies) of ``logits``, ``topk_idx``, ``topk_w``, ``counts`` (valid when
+    the call got no counts buffer of its own), ``offsets``, ``slot_pos`` and
+    ``sorted_slot`` (first ``offsets[E]`` valid)."""
+    torch = _torch()
+    dt = dtype if isinstance(dtype, int) else _dt(torch.empty(0, dtype=dtype))
+    r = LayerRouting()
+    _check(lib().moe_layer_routing(_p(ws), ws.numel(), T, h, f, E, k, float(capacity_factor), dt, _ACT[act],
+                                   ctypes.byref(r)), "moe_layer_routing")
+    base = ws.data_ptr()
+
+    def view(name, n, tdtype):
+        off = getattr(r, name) - base
+        esz = torch.empty(0, dtype=tdtype).element_size()
+        return ws[off:off + n * esz].view(tdtype)
+    n = T * k
+    return dict(logits=view("logits", T * E, torch.float32).view(T, E),
+                topk_idx=view("topk_idx", n, torch.int32).view(T, k),
+                topk_w=view("topk_w", n, torch.float32).view(T, k), counts=view("counts", E, torch.int32),
+                offsets=view("offsets", E + 1, torch.int32), slot_pos=view("slot_pos", n, torch.int32),
+                sorted_slot=view("sorted_slot", n, torch.int32))
 
 
 def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_factor: float,
@@ -408,13 +453,16 @@ def layer_forward_binned(x, W_gate, logit_bias, W1, W3, W2, *, k: int, capacity_
 
 
 def layer_backward(x, W_gate, W1, W3, W2, dy, *, k: int, capacity_factor: float, act: str, fwd_ws,
-                   d_aux: float = 0.0, with_w_gate: bool = True, ws=None, out=None, events=None, preact=None):
+                   d_aux: float = 0.0, with_w_gate: bool = True, ws=None, out=None, events=None, preact=None,
+                   jitter=None, noise=None, temperature: float = 1.0, soft: bool = False):
     """Gradients of ``<dy, y> + d_aux * aux`` for the layer_forward call that used the
     workspace ``fwd_ws`` (pass the same inputs).  Returns a dict with ``dx`` (x's dtype)
     and fp32 ``dW_gate`` (or None), ``dW1``, ``dW3`` (None for GELU), ``dW2``.  ``out``:
     preallocated tensors under those names.  ``events``: ``len(BACKWARD_STAGES) + 1``
     hipEvent_t handles recorded between the stages.  ``preact``: the pre-activations that
-    the training forward (layer_forward with ``preact``) saved; None = recompute them."""
+    the training forward (layer_forward with ``preact``) saved; None = recompute them.
+    ``jitter``/``noise``/``temperature``/``soft``: the router variants of the forward call
+    (the same tensors), differentiated through ``moe_layer_backward_ex``."""
     torch = _torch()
     dev = x.device
     T, h = x.shape
@@ -433,7 +481,12 @@ def layer_backward(x, W_gate, W1, W3, W2, dy, *, k: int, capacity_factor: float,
             float(d_aux), _p(fwd_ws), fwd_ws.numel(), _p(preact), 0 if preact is None else _nbytes(preact),
             _p(o["dx"]), _p(o["dW_gate"]), _p(o["dW1"]), _p(o["dW3"]), _p(o["dW2"]), _p(ws), ws.numel(),
             _stream(dev))
-    if events is None:
+    opts = _opts(jitter, noise, temperature, False, x, T, E, soft)
+    if opts is not None:
+        if events is not None:
+            raise ValueError("the measurement entry point takes no router variants")
+        _check(lib().moe_layer_backward_ex(*args[:13], ctypes.byref(opts), *args[13:]), "moe_layer_backward_ex")
+    elif events is None:
         _check(lib().moe_layer_backward(*args), "moe_layer_backward")
     else:
         _check(lib().moe_layer_backward_timed(*args, ctypes.cast(events, _c_void_p)), "moe_layer_backward_timed")

@@ -20,11 +20,11 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed-fp32 VALU forms anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+BUILD_DIR = os.path.join(PKG, "_build")
 
 
 def hipcc() -> str:
@@ -38,19 +38,41 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+# hipcc's host pass does not know the packed-fp32 feature name; that warning is harmless
+_NOISE = "'-packed-fp32-ops' is not a recognized feature"
+
+
+def _run(cmd: list[str], verbose: bool) -> subprocess.CompletedProcess:
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature name; that warning is harmless
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared library.
+    Every call compiles; the objects live in a scratch folder beside the sources."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    objs, jobs = [], []
+    for src in sources():
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [hipcc(), *HIPCC_FLAGS, *inc, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    errors = []
+    for src, job in zip(sources(), jobs):
+        _, err = job.communicate()
+        err = "\n".join(l for l in err.splitlines() if _NOISE not in l)
+        if job.returncode != 0:
+            errors.append(f"{os.path.basename(src)} ({job.returncode}):\n{err}")
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+    tmp = LIB + ".tmp"
+    res = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -90,10 +90,24 @@ moe_status_t common_sizes(int32_t T, int32_t E, int32_t k) {
   return MOE_OK;
 }
 
+// The expert GEMMs address their left operand with 32-bit element offsets (row * K):
+// x (T rows of h) in the gathered up projection, x_perm (R_max rows of h) and Hm (R_max
+// rows of f).  Sizes where one of those products reaches 2^32 are refused.
+moe_status_t rows_ok(int64_t rows, int32_t h, int32_t f) {
+  if (rows * (int64_t)(h > f ? h : f) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 moe_status_t dim_ok(int32_t d) {
   if (d <= 0) return MOE_ERR_ARG;
   if (d % 64 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// rows_ok for the layer: the larger of T and R_max rows
+moe_status_t size_ok(int32_t T, int32_t h, int32_t f, int32_t E, int32_t k, float cf) {
+  const int64_t R_max = rows_max(T, E, k, capacity_of(T, E, k, cf));
+  return rows_ok(R_max > T ? R_max : (int64_t)T, h, f);
 }
 
 // --- workspace layouts (the same carve is used to size and to place)
@@ -343,6 +357,7 @@ static void apply_opts(RouteArgs& a, const moe_router_opts_t* o) {
   a.noise = o->logit_noise;
   a.inv_temp = 1.0f / o->temperature;
   a.uniform = o->uniform_assignment != 0;
+  a.soft = o->soft_topk != 0;
 }
 
 static moe_status_t route_impl(const void* x, const float* W_gate, const float* logit_bias, int32_t T, int32_t h,
@@ -412,6 +427,13 @@ size_t moe_router_opts_workspace_bytes(int32_t T, int32_t h, moe_dtype_t dt, con
   return align_up((size_t)T * h * elem_bytes(dt));
 }
 
+size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k) {
+  if (common_sizes(T, E, k) != MOE_OK) return 0;
+  Carve c(nullptr);
+  carve_perm(c, T, E, k);
+  return c.bytes();
+}
+
 moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int32_t h, int32_t E, int32_t k,
                          float capacity_factor, moe_dtype_t dt, int32_t* counts, int32_t* offsets,
                          int32_t* sorted_slot, int32_t* slot_pos, void* x_perm, const float* prob_sum,
@@ -478,6 +500,7 @@ moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t 
   if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_ARG;
   if (!aligned16(x_perm) || !aligned16(W1) || !aligned16(W2) || (W3 && !aligned16(W3)) || !aligned16(out_perm))
     return MOE_ERR_UNSUPPORTED;
+  if ((s = rows_ok(R_max, h, f)) != MOE_OK) return s;
   if (R_max == 0) return MOE_OK;
   const bool bf = dt == MOE_BF16;
   const FfnPlan pl = plan_ffn(bf, (double)R_max / E, E, R_max, h, f);
@@ -520,6 +543,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || (W3 && !aligned16(W3)) || !aligned16(y))
     return MOE_ERR_UNSUPPORTED;
   if ((s = opts_ok(opts, x, false)) != MOE_OK) return s;
+  if ((s = size_ok(T, h, f, E, k, capacity_factor)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   const int64_t C = capacity_of(T, E, k, capacity_factor);
   const int R_max = rows_max(T, E, k, C);
@@ -611,6 +635,29 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   }
   MOE_TRY(launch_combine(w.o, true, pl.s_down, (size_t)R_max * h, w.slot_pos, w.topk_w, T, h, k, bf, y, stream));
   if (!mark()) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_routing(const void* ws, size_t ws_bytes, int32_t T, int32_t h, int32_t f, int32_t E,
+                               int32_t k, float capacity_factor, moe_dtype_t dt, moe_act_t act,
+                               moe_layer_routing_t* out) {
+  moe_status_t s = common_sizes(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor) || !ws || !out) return MOE_ERR_ARG;
+  if ((s = dim_ok(h)) != MOE_OK) return s;
+  if ((s = dim_ok(f)) != MOE_OK) return s;
+  const int64_t C = capacity_of(T, E, k, capacity_factor);
+  Carve c(const_cast<void*>(ws));
+  const LayerWs w = carve_layer(c, T, h, f, E, k, rows_max(T, E, k, C), layer_plan(dt == MOE_BF16, T, h, f, E, k, C),
+                                dt, act);
+  if (ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
+  out->logits = w.logits;
+  out->topk_idx = w.topk_idx;
+  out->topk_w = w.topk_w;
+  out->counts = w.counts;
+  out->offsets = w.offsets;
+  out->slot_pos = w.slot_pos;
+  out->sorted_slot = w.sorted_slot;
   return MOE_OK;
 }
 
@@ -846,7 +893,8 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
                                         float d_aux, const void* fwd_ws, size_t fwd_ws_bytes,
                                         const float* preact, size_t preact_len, void* dx, float* dW_gate,
                                         float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
-                                        hipStream_t stream, hipEvent_t* ev) {
+                                        hipStream_t stream, hipEvent_t* ev,
+                                        const moe_router_opts_t* opts = nullptr) {
   moe_status_t s = common_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (!dtype_ok(dt) || !act_ok(act) || !isfinite(capacity_factor) || !isfinite(d_aux)) return MOE_ERR_ARG;
@@ -854,14 +902,22 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   if ((s = dim_ok(f)) != MOE_OK) return s;
   if (!x || !W_gate || !W1 || !W2 || !dy || !dx || !dW1 || !dW2) return MOE_ERR_ARG;
   if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr) || (act == MOE_ACT_SWIGLU) != (dW3 != nullptr)) return MOE_ERR_ARG;
+  if ((s = opts_ok(opts, x, false)) != MOE_OK) return s;
+  // the training forward takes no router variants, so its pre-activations belong to the plain routing
+  if (opts != nullptr && preact != nullptr) return MOE_ERR_ARG;
+  // the uniform assignment is a benchmarking mode: its ids are not the router's choice
+  if (opts != nullptr && opts->uniform_assignment != 0) return MOE_ERR_UNSUPPORTED;
+  if ((s = size_ok(T, h, f, E, k, capacity_factor)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   const int64_t C = capacity_of(T, E, k, capacity_factor);
   const int R_max = rows_max(T, E, k, C);
   const bool bf = dt == MOE_BF16;
   const FfnPlan pl = layer_plan(bf, T, h, f, E, k, C);
-  // the forward's workspace, carved as the forward carved it
+  // the forward's workspace, carved as the forward carved it (with jitter: the router's
+  // input x * u follows the layer's pieces)
   Carve cf(const_cast<void*>(fwd_ws));
   LayerWs w = carve_layer(cf, T, h, f, E, k, R_max, pl, dt, act);
+  const void* xr = has_jitter(opts) ? (const void*)cf.take<char>((size_t)T * h * elem_bytes(dt)) : x;
   if (!fwd_ws || fwd_ws_bytes < cf.bytes()) return MOE_ERR_WORKSPACE;
   Carve c(ws);
   const int parts = dx_parts(bf, pl, T, h, f, E, k, C, act == MOE_ACT_SWIGLU ? 2 : 1);
@@ -889,7 +945,9 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
                              stream));
   if (!mark()) return MOE_ERR_DEVICE;
   // router: logit gradient of the renormalised selection and of the aux loss
-  MOE_TRY(launch_router_bwd(w.logits, w.topk_idx, w.topk_w, b.dw, b.counts, T, E, k, d_aux, b.dl, stream));
+  MOE_TRY(launch_router_bwd(w.logits, opts ? opts->logit_noise : nullptr, w.topk_idx, w.topk_w, b.dw, b.counts, T,
+                            E, k, d_aux, opts ? 1.0f / opts->temperature : 1.0f, opts && opts->soft_topk != 0, b.dl,
+                            stream));
   if (!mark()) return MOE_ERR_DEVICE;
   // the up projection's pre-activations a (| g): saved by the training forward, else
   // recomputed with the same GEMM
@@ -1023,7 +1081,7 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   MOE_TRY(launch_gemm_nt(nt, stream));
   if (dW_gate) {
     tn = BwdTN{};
-    tn.A = x;
+    tn.A = xr;  // the router's input
     tn.lda = h;
     tn.a_bf16 = bf;
     tn.B = b.dl;
@@ -1044,7 +1102,8 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
     MOE_TRY(launch_gemm_tn(tn, stream));
   }
   if (!mark()) return MOE_ERR_DEVICE;
-  MOE_TRY(launch_dx_final(b.dx_r, b.dXp, parts, (size_t)R_max * h, w.slot_pos, T, h, k, bf, dx, stream));
+  MOE_TRY(launch_dx_final(b.dx_r, has_jitter(opts) ? opts->jitter : nullptr, b.dXp, parts, (size_t)R_max * h,
+                          w.slot_pos, T, h, k, bf, dx, stream));
   if (!mark()) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
@@ -1058,6 +1117,18 @@ moe_status_t moe_layer_backward(const void* x, const float* W_gate, const void* 
   return layer_backward_impl(x, W_gate, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, dy, d_aux, fwd_ws,
                              fwd_ws_bytes, preact, preact_bytes_, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream,
                              nullptr);
+}
+
+moe_status_t moe_layer_backward_ex(const void* x, const float* W_gate, const void* W1, const void* W3,
+                                   const void* W2, int32_t T, int32_t h, int32_t f, int32_t E, int32_t k,
+                                   float capacity_factor, moe_act_t act, moe_dtype_t dt,
+                                   const moe_router_opts_t* opts, const void* dy, float d_aux, const void* fwd_ws,
+                                   size_t fwd_ws_bytes, const float* preact, size_t preact_bytes_, void* dx,
+                                   float* dW_gate, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return layer_backward_impl(x, W_gate, W1, W3, W2, T, h, f, E, k, capacity_factor, act, dt, dy, d_aux, fwd_ws,
+                             fwd_ws_bytes, preact, preact_bytes_, dx, dW_gate, dW1, dW3, dW2, ws, ws_bytes, stream,
+                             nullptr, opts);
 }
 
 moe_status_t moe_layer_backward_timed(const void* x, const float* W_gate, const void* W1, const void* W3,

@@ -102,11 +102,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TD* __restrict__
 // One wave per token: the logit gradient of the renormalised selection and of the aux
 // loss.  Lane l holds experts l, l + 64, ...
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ logits,
+                                                         const float* __restrict__ noise,
                                                          const int* __restrict__ topk_idx,
                                                          const float* __restrict__ topk_w,
                                                          const float* __restrict__ dw,
                                                          const int* __restrict__ counts, int T, int E, int k,
-                                                         float d_aux, float* __restrict__ dl) {
+                                                         float d_aux, float inv_temp, int soft,
+                                                         float* __restrict__ dl) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int e = lane + 64 * q;
-    l[q] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    l[q] = e < E ? logits[(size_t)t * E + e] + (noise != nullptr ? noise[(size_t)t * E + e] : 0.f) : -INFINITY;
     m = fmaxf(m, l[q]);
   }
   m = wave_max(m);
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int e = lane + 64 * q;
-    p[q] = e < E ? expf(l[q] - m) : 0.f;
+    p[q] = e < E ? expf((l[q] - m) * inv_temp) : 0.f;
     s += p[q];
   }
   s = wave_sum(s);
@@ -139,19 +141,36 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     fp += fe[q] * p[q];
   }
   fp = wave_sum(fp);
-  const float ca = d_aux * (float)E / (float)T;
+  // softmax(l / tau) has the Jacobian p_a (delta_ab - p_b) / tau
+  const float ca = d_aux * (float)E / (float)T * inv_temp;
   float g[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) g[q] = ca * p[q] * (fe[q] - fp);
-  // the renormalised softmax over the selection
   float swd = 0.f;
   for (int j = 0; j < k; ++j) swd += topk_w[(size_t)t * k + j] * dw[(size_t)t * k + j];
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[(size_t)t * k + j];
-    const float v = topk_w[(size_t)t * k + j] * (dw[(size_t)t * k + j] - swd);
+  if (soft) {
+    // weights p[S_j] (not renormalised): p_b (dw_b - sum_j w_j dw_j) / tau for every expert b
+    float own[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      if (lane + 64 * q == e) g[q] += v;
+    for (int q = 0; q < NQ; ++q) own[q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(size_t)t * k + j];
+      const float d = dw[(size_t)t * k + j];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (lane + 64 * q == e) own[q] = d;
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) g[q] += p[q] * (own[q] - swd) * inv_temp;
+  } else {
+    // the renormalised softmax over the selection: w_j (dw_j - sum_j' w_j' dw_j') / tau
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(size_t)t * k + j];
+      const float v = topk_w[(size_t)t * k + j] * (dw[(size_t)t * k + j] - swd) * inv_temp;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (lane + 64 * q == e) g[q] += v;
+    }
   }
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -882,12 +901,15 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 // dX is the sum of the `parts` K parts of dXp (part p at dXp + p * part_stride), in order
 template <typename TD>
 __global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__ dx_router,
+                                                       const TD* __restrict__ jitter,
                                                        const float* __restrict__ dXp, int parts, size_t part_stride,
                                                        const int* __restrict__ slot_pos, int T, int h, int k,
                                                        TD* __restrict__ dx) {
   const int t = blockIdx.x;
   for (int i = threadIdx.x; i < h; i += 256) {
+    // the router read x * u: its share of the gradient is multiplied by u
     float v = dx_router[(size_t)t * h + i];
+    if (jitter != nullptr) v *= ld(jitter, (size_t)t * h + i);
     for (int j = 0; j < k; ++j) {
       const int r = slot_pos[(size_t)t * k + j];
       if (r < 0) continue;
@@ -939,12 +961,13 @@ hipError_t launch_combine_bwd(const void* dy, const float* O, int n_parts, size_
   return hipGetLastError();
 }
 
-hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const float* topk_w, const float* dw,
-                             const int* counts, int T, int E, int k, float d_aux, float* dl, hipStream_t st) {
+hipError_t launch_router_bwd(const float* logits, const float* noise, const int* topk_idx, const float* topk_w,
+                             const float* dw, const int* counts, int T, int E, int k, float d_aux, float inv_temp,
+                             bool soft, float* dl, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (E > 256) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, topk_idx, topk_w, dw, counts,
-                     T, E, k, d_aux, dl);
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, noise, topk_idx, topk_w, dw,
+                     counts, T, E, k, d_aux, inv_temp, soft ? 1 : 0, dl);
   return hipGetLastError();
 }
 
@@ -1101,16 +1124,17 @@ hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_dx_final(const float* dx_router, const float* dXp, int parts, size_t part_stride,
-                           const int* slot_pos, int T, int h, int k, bool bf16, void* dx, hipStream_t st) {
+hipError_t launch_dx_final(const float* dx_router, const void* jitter, const float* dXp, int parts,
+                           size_t part_stride, const int* slot_pos, int T, int h, int k, bool bf16, void* dx,
+                           hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (parts < 1) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(dx_final_kernel<bf16_t>, dim3(T), dim3(256), 0, st, dx_router, dXp, parts, part_stride,
-                       slot_pos, T, h, k, (bf16_t*)dx);
+    hipLaunchKernelGGL(dx_final_kernel<bf16_t>, dim3(T), dim3(256), 0, st, dx_router, (const bf16_t*)jitter, dXp,
+                       parts, part_stride, slot_pos, T, h, k, (bf16_t*)dx);
   else
-    hipLaunchKernelGGL(dx_final_kernel<float>, dim3(T), dim3(256), 0, st, dx_router, dXp, parts, part_stride,
-                       slot_pos, T, h, k, (float*)dx);
+    hipLaunchKernelGGL(dx_final_kernel<float>, dim3(T), dim3(256), 0, st, dx_router, (const float*)jitter, dXp,
+                       parts, part_stride, slot_pos, T, h, k, (float*)dx);
   return hipGetLastError();
 }
 

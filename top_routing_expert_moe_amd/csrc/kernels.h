@@ -41,10 +41,12 @@ struct RouteArgs {
                           // bf16 split router weights, then (few tokens) [SH][T][E] fp32 partial
                           // logits
   // router variants (selection kernel): gate noise [T,E] added to the logits, softmax of
-  // logits * inv_temp, ids replaced by (t*k + j) % E
+  // logits * inv_temp, ids replaced by (t*k + j) % E, soft top-K weights (the full
+  // softmax at the selection, not renormalised)
   const float* noise = nullptr;
   float inv_temp = 1.0f;
   bool uniform = false;
+  bool soft = false;
   // not null and T <= kSelTokens: the selection kernel also does the scan and the scatter
   const SmallPermute* permute = nullptr;
 };
@@ -192,12 +194,17 @@ hipError_t launch_tile_scan(const int* offsets, int E, int BM, int* tile_off, hi
 hipError_t launch_combine_bwd(const void* dy, const float* O, int n_parts, size_t part_stride, const int* slot_pos,
                               const float* topk_w, int T, int h, int k, bool bf16, float* dw, void* dO,
                               hipStream_t st);
-hipError_t launch_router_bwd(const float* logits, const int* topk_idx, const float* topk_w, const float* dw,
-                             const int* counts, int T, int E, int k, float d_aux, float* dl, hipStream_t st);
+// logit gradient of the weights and the aux loss; noise (or null) as in the forward's selection,
+// p = softmax((logits + noise) * inv_temp); soft: the weights are p at the selection (soft top-K)
+hipError_t launch_router_bwd(const float* logits, const float* noise, const int* topk_idx, const float* topk_w,
+                             const float* dw, const int* counts, int T, int E, int k, float d_aux, float inv_temp,
+                             bool soft, float* dl, hipStream_t st);
 hipError_t launch_gemm_nt(const BwdNT& a, hipStream_t st);
 hipError_t launch_gemm_tn(const BwdTN& a, hipStream_t st);
-hipError_t launch_dx_final(const float* dx_router, const float* dXp, int parts, size_t part_stride,
-                           const int* slot_pos, int T, int h, int k, bool bf16, void* dx, hipStream_t st);
+// dx[t] = dx_router[t] (* jitter[t], x's dtype, when not null) + sum over kept slots of the dX parts
+hipError_t launch_dx_final(const float* dx_router, const void* jitter, const float* dXp, int parts,
+                           size_t part_stride, const int* slot_pos, int T, int h, int k, bool bf16, void* dx,
+                           hipStream_t st);
 // xp[r] = x[rows[r]] (row_bytes each) for r < offsets[E]
 hipError_t launch_gather_rows(const void* x, const int* rows, const int* offsets, int E, int R_max, int row_bytes,
                               void* xp, hipStream_t st);

@@ -172,7 +172,19 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       for (int e = wave; e < E; e += kScanThreads / 64) {
         double ps = 0.0;
         if (a.prob_part != nullptr) {
-          for (int b = lane; b < a.nrb; b += 64) ps += (double)a.prob_part[(size_t)b * E + e];
+          constexpr int kCache = 8;
+          if (a.nrb <= kCache * 64) {
+            float c[kCache];
+#pragma unroll
+            for (int i = 0; i < kCache; ++i) {
+              const int b = lane + 64 * i;
+              c[i] = b < a.nrb ? a.prob_part[(size_t)b * E + e] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < kCache; ++i) ps += (double)c[i];
+          } else {
+            for (int b = lane; b < a.nrb; b += 64) ps += (double)a.prob_part[(size_t)b * E + e];
+          }
         } else if (lane == 0) {
           ps = (double)a.prob_sum[e];
         }
@@ -186,7 +198,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       double ps = 0.0;
       if (e < E) {
         if (a.prob_part != nullptr) {
-          for (int b = part; b < a.nrb; b += P) ps += (double)a.prob_part[(size_t)b * E + e];
+          // up to 16 blocks per thread: all loads issued before the first add (the adds keep
+          // ascending block order)
+          constexpr int kCache = 16;
+          if (a.nrb <= kCache * P) {
+            float c[kCache];
+#pragma unroll
+            for (int i = 0; i < kCache; ++i) {
+              const int b = part + i * P;
+              c[i] = b < a.nrb ? a.prob_part[(size_t)b * E + e] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < kCache; ++i) ps += (double)c[i];
+          } else {
+            for (int b = part; b < a.nrb; b += P) ps += (double)a.prob_part[(size_t)b * E + e];
+          }
         } else if (part == 0) {
           ps = (double)a.prob_sum[e];
         }

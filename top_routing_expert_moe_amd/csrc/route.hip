@@ -282,8 +282,10 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // Router variants: `noise` [T,E] (or null) is added to the logits before anything else
 // uses them (the stored logits stay the router's own); the softmax and the weights use
 // logits * inv_temp (selection ranks the logits themselves, the same order for any
-// positive temperature); with `uniform` the ids written (and counted) are (t*k + j) % E
-// while the weights stay those of the real top-k.
+// positive temperature); `vflags` bit 0 (uniform assignment): the ids written (and
+// counted) are (t*k + j) % E while the weights stay those of the real top-k; bit 1
+// (soft top-K): the weights are the full softmax at the selected experts, not
+// renormalised over them.
 // FUSE (T <= kSelTokens, one workgroup): the workgroup then also does the scan and the
 // scatter (single_block_permute) into the outputs named by sp.
 template <int NV, int G, bool HSPLIT, int NWS = 4, bool FUSE = false>
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
                                                      int SH, int T, int E, int k,
                                                      int* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                      float* __restrict__ prob_part, int* __restrict__ blk_counts,
-                                                     const float* __restrict__ noise, float inv_temp, int uniform,
+                                                     const float* __restrict__ noise, float inv_temp, int vflags,
                                                      SmallPermute sp) {
   static_assert(G == 64 || NV == 1, "several values per lane only with whole-wave groups");
   constexpr int TPW = 64 / G;                  // tokens per wave and pass
@@ -389,9 +391,11 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
       if (gl == j) { my_l = l_sel; my_e = e_sel; }
     }
     if (tv && gl < k) {
-      const int e_out = uniform ? (int)(((int64_t)t * k + gl) % E) : my_e;
+      const int e_out = (vflags & 1) ? (int)(((int64_t)t * k + gl) % E) : my_e;
       topk_idx[(size_t)t * k + gl] = e_out;
-      topk_w[(size_t)t * k + gl] = expf((my_l - lmax) * inv_temp) / wsum;
+      // lmax is the token's largest logit, m: the same value
+      const float ew = expf((my_l - lmax) * inv_temp);
+      topk_w[(size_t)t * k + gl] = (vflags & 2) ? ew * inv : ew / wsum;
       if (blk_counts != nullptr) atomicAdd(&cnt[e_out], 1);
     }
   }
@@ -553,7 +557,7 @@ hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
 #define MOE_SELECT_F(NV, G, HS, NWS, F)                                                                          \
   hipLaunchKernelGGL((select_kernel<NV, G, HS, NWS, F>), grid, dim3(NWS * 64), 0, st, a.logits, lpart, SH, a.T, \
                      a.E, a.k, a.topk_idx, a.topk_w, a.prob_part, a.blk_counts, a.noise, a.inv_temp,       \
-                     a.uniform ? 1 : 0, sp)
+                     (a.uniform ? 1 : 0) | (a.soft ? 2 : 0), sp)
 #define MOE_SELECT_W(NV, G, HS, NWS)              \
   do {                                            \
     if (fuse) MOE_SELECT_F(NV, G, HS, NWS, true); \
