@@ -124,6 +124,31 @@ def test_backward_edge_cases(T, h, f, E, k, cf, act, dtype):
     _check_all(w, host, g, gl, dy)
 
 
+@pytest.mark.parametrize("h", [256, 2048])
+def test_backward_skewed_experts(h):
+    """The recomputing backward walks the forward's tile list, where a dominant expert in a
+    launch of 128-row tiles takes 256-row tiles (with h >= 2048 every expert past 128 rows)."""
+    T, f, E, k, cf, act, dtype = 1500, 512, 8, 1, 0.0, "swiglu", "bf16"
+    _say(f"backward skewed T={T} h={h} f={f} E={E} k={k}")
+    rng = np.random.default_rng(99)
+    conv = mw.f32_to_bf16_bits
+    bias = np.zeros(E, np.float32)
+    bias[2] = 3.0
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32), logit_bias=bias,
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("skewed", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
+    dy = _dy(T, h, dtype)
+    g, gl = _run(w, dd, dy)
+    counts = o.histogram(o.select_topk(gl, k), E)
+    _say(f"  rows per expert: {counts.tolist()}")
+    assert counts.max() >= 512
+    _check_all(w, host, g, gl, dy)
+
+
 @pytest.mark.parametrize("name", ["tiny-fp32", "decode-mixtral", "capacity-e64"])
 def test_backward_full_size(name):
     _say(f"backward {name}")

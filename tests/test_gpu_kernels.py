@@ -217,6 +217,9 @@ def _ffn_case(E, h, f, seg, act, dtype, seed):
     ("swiglu", "bf16", 2, 192, 320, [300, 530]),                   # 256-row tiles with k and N tails
     ("swiglu", "bf16", 4, 1024, 2048, [5, 20, 0, 9]),              # 32-row tiles, K split 2 (up) and 4 (down)
     ("gelu", "bf16", 3, 2048, 1024, [12, 3, 30]),                  # K split 4 (up) and 2 (down), GELU parts
+    ("swiglu", "bf16", 8, 256, 512, [700, 20, 5, 40, 60, 0, 100, 90]),  # 128-row launch, one big expert: 256-row tiles
+    ("gelu", "bf16", 6, 192, 320, [512, 511, 3, 0, 40, 33]),           # ... at the threshold (512 rows) and just below
+    ("swiglu", "bf16", 4, 2048, 256, [200, 129, 0, 60]),               # h >= 2048: 256-row tiles from 129 rows
     ("swiglu", "f32", 5, 128, 256, [0, 1, 70, 129, 37]),
     ("gelu", "f32", 3, 192, 320, [65, 0, 64]),
 ])

@@ -136,6 +136,40 @@ def test_layer_edge_cases(T, h, f, E, k, cf, act, dtype):
             assert (gu.from_dev(y)[dropped] == 0).all()
 
 
+@pytest.mark.parametrize("T,h,f,E,k,cf,act,dtype", [
+    (1500, 256, 512, 8, 1, 0.0, "swiglu", "bf16"),   # 128-row tiles; the dominant expert takes 256-row tiles
+    (2000, 192, 320, 16, 2, 0.0, "gelu", "bf16"),    # ... two big experts, the rest small
+    (3000, 128, 256, 8, 1, 0.8, "swiglu", "bf16"),   # capacity 300 keeps every expert below the threshold
+    (600, 2048, 256, 8, 2, 0.0, "gelu", "bf16"),     # h >= 2048: every expert past 128 rows takes 256-row tiles
+])
+def test_layer_skewed_experts(T, h, f, E, k, cf, act, dtype):
+    """Launches of 128-row tiles in which some experts have 512 rows or more: those experts'
+    m-tiles are 256 rows high (the tile list and the GEMMs agree on the height)."""
+    import math
+    _say(f"layer skewed T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")
+    rng = np.random.default_rng(T + 7 * E)
+    conv = (lambda a: mw.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    bias = np.zeros(E, np.float32)
+    bias[0] = 3.0
+    if E > 8:
+        bias[5] = 2.5
+    if h >= 2048:
+        bias[1] = 1.5    # an expert between 129 and 511 rows as well
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32), logit_bias=bias,
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)) if act == "swiglu" else None,
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, dtype if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("skewed", T=T, h=h, f=f, E=E, k=k, act=act, dtype=dtype, cf=cf)
+    y, aux, counts, logits, routing = _run_layer(w, host, dd)
+    ref = _check_layer(w, host, y, aux, counts, logits, np.arange(T), routing)
+    kept = np.diff(ref["offsets"])
+    _say(f"  rows per expert: {kept.tolist()}")
+    if cf <= 0:
+        assert kept.max() >= 512       # the case this test is for
+
+
 def test_layer_forward_timed_matches_untimed():
     """The measurement entry point runs the same kernels: identical outputs, and the
     stage events are ordered and add up to the whole layer."""

@@ -231,6 +231,7 @@ moe_status_t run_ffn(const void* A, const int* a_rows, const int* offsets, const
   up.E = E;
   up.R_max = R_max;
   up.bm = pl.bm;
+  up.big = pl.big;
   up.ksplit = pl.s_up;
   up.act = gact;
   up.save = bf && pl.s_up <= 1 && !sep ? save : nullptr;  // bf16 only (fp32: the caller runs preact_gemms)
@@ -277,6 +278,7 @@ moe_status_t preact_gemms(const void* A, const int* a_rows, const int* offsets, 
   up.E = E;
   up.R_max = R_max;
   up.bm = pl.bm;
+  up.big = pl.big;
   up.ksplit = 1;
   up.W = W1;
   up.out = ag;
@@ -507,7 +509,7 @@ moe_status_t moe_expert_ffn(const void* x_perm, const int32_t* offsets, int32_t 
   Carve c(ws);
   FfnWs w = carve_ffn(c, pl, R_max, h, f, E, dt, act);
   if (!ws || ws_bytes < c.bytes()) return MOE_ERR_WORKSPACE;
-  MOE_TRY(launch_tiles(offsets, E, pl.bm, w.tile_off, stream));
+  MOE_TRY(launch_tiles(offsets, E, pl.bm, pl.big, w.tile_off, stream));
   return run_ffn(x_perm, nullptr, offsets, w.tile_off, pl, R_max, h, f, E, W1, W3, W2, act, dt, w.hm, w.part_up,
                  out_perm, false, w.part_down, false, stream);
 }
@@ -589,6 +591,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   if (one_block) {
     sp.C = (int)C;
     sp.BM = pl.bm;
+    sp.big = pl.big;
     sp.nbits = expert_bits(E);
     sp.counts = counts ? counts : w.counts;
     sp.offsets = w.offsets;
@@ -611,6 +614,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.k = k;
   sa.C = (int)C;
   sa.BM = pl.bm;
+  sa.big = pl.big;
   sa.prob_part = w.prob_part;
   sa.nrb = route_blocks(T);
   sa.prob_sum = nullptr;
@@ -755,6 +759,7 @@ static moe_status_t layer_forward_binned_impl(const void* x, const float* W_gate
   sa.k = k;
   sa.C = (int)cfix;
   sa.BM = pl.bm;
+  sa.big = pl.big;
   sa.prob_part = w.prob_part;
   sa.nrb = route_blocks(T);
   sa.counts = counts ? counts : w.counts;

@@ -76,6 +76,14 @@ __device__ __forceinline__ float silu_fast(float z) {
 }
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
+// Height of an expert's m-tiles in the grouped GEMMs, given the launch's tile height fh, the
+// launch's threshold `big` and the expert's row count: fh, except that in a launch of
+// 128-row tiles an expert with at least `big` rows takes 256-row tiles.  Every builder of
+// a tile list and every GEMM that walks one uses this same function with the same big.
+__host__ __device__ __forceinline__ int m_tile_rows(int rows, int fh, int big) {
+  return (fh == 128 && rows >= big) ? 256 : fh;
+}
+
 // Binary search: the expert e with tile_off[e] <= mt < tile_off[e+1] (E >= 1).
 __device__ __forceinline__ int find_expert(const int* __restrict__ tile_off, int E, int mt) {
   int lo = 0, hi = E;  // invariant: tile_off[lo] <= mt < tile_off[hi]

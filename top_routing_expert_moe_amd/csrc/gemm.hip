@@ -36,6 +36,7 @@
 //    (m-tile, n-tile) inside each expert, so the workgroups running together in
 //    one XCD share activation and weight tiles in its L2.
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -58,7 +59,13 @@ __device__ __forceinline__ void store4(float* p, const float* v) { *(floatx4*)p 
 // then the next n-group, then the next m-group.  Consecutive tiles -- which run at the
 // same time on one XCD -- therefore share both their activation rows (across the GN
 // n-tiles) and their weight columns (across the GM m-tiles) in that XCD's L2.
-constexpr int GM = 4, GN = 8;
+#ifndef MOE_GM
+#define MOE_GM 4
+#endif
+#ifndef MOE_GN
+#define MOE_GN 8
+#endif
+constexpr int GM = MOE_GM, GN = MOE_GN;
 
 __device__ __forceinline__ void tile_of(int L, const int* __restrict__ tile_off, int E, int NT, int& e,
                                         int& mt_local, int& nt) {
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
-    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, float* __restrict__ save) {
+    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, int big, float* __restrict__ save) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
   // ---- tile schedule (XCD-aware), exits for surplus workgroups
@@ -495,8 +502,9 @@ gemm_bf16_kernel(
   }
   tile_of(Lt, tile_off, E, NT, e, mt_local, nt);
   const int Kc = SPLIT ? K / S : K;  // this workgroup's k range: [ks * Kc, ks * Kc + Kc)
-  const int row0 = offsets[e] + mt_local * fh;
-  const int rows = min(fh, offsets[e + 1] - row0);
+  const int fe = m_tile_rows(offsets[e + 1] - offsets[e], fh, big);  // this expert's tile height
+  const int row0 = offsets[e] + mt_local * fe;
+  const int rows = min(fe, offsets[e + 1] - row0);
   const int n0 = nt * NO;
   if (rows > 128)
     gemm_tile<256, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc,
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 gemm_bf16_wide_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
-    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, float* __restrict__ save) {
+    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, int big, float* __restrict__ save) {
   // K parts: spread copies and the XCD-aware order; one part (the up projection, also
   // its separated raw form): copies after the barrier and launch order
   constexpr bool KP = SPLIT && ACT != ACT_SWIGLU_SEP;
@@ -543,8 +551,9 @@ gemm_bf16_wide_kernel(
   }
   tile_of(Lt, tile_off, E, NT, e, mt_local, nt);
   const int Kc = SPLIT ? K / S : K;
-  const int row0 = offsets[e] + mt_local * fh;
-  const int rows = min(fh, offsets[e + 1] - row0);
+  const int fe = m_tile_rows(offsets[e + 1] - offsets[e], fh, big);  // 32 here: fh is 32
+  const int row0 = offsets[e] + mt_local * fe;
+  const int rows = min(fe, offsets[e + 1] - row0);
   gemm_tile<32, ACT, GATHER, OT, SPLIT, BNW, CFG>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows,
                                                   nt * NO, ks, Kc, save);
 }
@@ -648,13 +657,13 @@ hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   if (wide)
     hipLaunchKernelGGL((gemm_bf16_wide_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                        (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, save);
+                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, a.big, save);
   else if constexpr (ACT == ACT_SWIGLU_SEP)
     return hipErrorInvalidValue;  // wide tiles only
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                        (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, save);
+                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, a.big, save);
   return hipGetLastError();
 }
 
@@ -755,8 +764,19 @@ hipError_t launch_ffn_finish(const float* part, int S, int R_max, int N, int act
 }
 
 FfnPlan plan_ffn(bool bf16, double rows_per_expert, int E, int R_max, int h, int f) {
-  FfnPlan p{gemm_bm(bf16, rows_per_expert), 1, 1};
+  FfnPlan p{gemm_bm(bf16, rows_per_expert), 1, 1, INT_MAX};
   if (!bf16) return p;
+  if (p.bm == 128) {
+    // Experts with many rows take 256-row tiles.  Four 128-row m-tiles of an expert run
+    // together on one XCD and share its weight panels in L2, so an expert with more rows
+    // streams its weights from HBM once per group of four: from 512 rows, 256-row tiles halve
+    // those re-reads.  With a long up-projection contraction (h >= 2048) every expert past
+    // one 128-row tile is better off with 256-row tiles (fewer tiles, one weight stream per
+    // expert; measured at T = 4096, h = 4096, f = 2048, E = 256, k = 8: the up projection
+    // 1.86 -> 1.73 ms); with h = 1024 (T = 8192, f = 4096, E = 64, k = 2, capacity 320)
+    // 256-row tiles for its 320-row experts made the up projection 0.148 -> 0.194 ms.
+    p.big = h >= 2048 ? 129 : 512;
+  }
   constexpr double kCUs = 256.0;
   const double mt_max = ceil((double)R_max / p.bm) + E;
   if (p.bm == 32) {

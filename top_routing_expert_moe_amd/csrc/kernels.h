@@ -15,6 +15,7 @@ constexpr int kSelTokens = 64;  // tokens per selection / histogram / scatter bl
 struct SmallPermute {
   int C;                   // capacity, INT32_MAX = none
   int BM;                  // rows per GEMM tile for tile_off; 0 = no tile list
+  int big;                 // m_tile_rows threshold of the tile list (FfnPlan::big)
   int nbits;               // bits of an expert id (expert_bits)
   int* counts;             // [E] pre-drop
   int* offsets;            // [E+1] over kept
@@ -69,6 +70,7 @@ struct ScanArgs {
   int nhb, E, T, k;
   int C;                   // capacity, INT32_MAX = none
   int BM;                  // rows per GEMM tile for tile_off; 0 = no tile schedule
+  int big;                 // m_tile_rows threshold of the tile list (FfnPlan::big)
   const float* prob_part;  // [nrb,E] or null
   int nrb;
   const float* prob_sum;   // [E] or null (used when prob_part is null)
@@ -99,7 +101,7 @@ hipError_t launch_scatter(const int* topk_idx, int T, int E, int k, int C, const
                           hipStream_t st);
 hipError_t launch_gather(const void* x, const int* perm_token, const int* offsets, int E, int R_max,
                          int h, int elem_bytes, void* x_perm, hipStream_t st);
-hipError_t launch_tiles(const int* offsets, int E, int BM, int* tile_off, hipStream_t st);
+hipError_t launch_tiles(const int* offsets, int E, int BM, int big, int* tile_off, hipStream_t st);
 
 // ---- expert GEMMs
 // ACT_SWIGLU_SEP is a kernel mode, not an activation: the raw SwiGLU pre-activations
@@ -120,6 +122,7 @@ struct GemmArgs {
   int act;
   bool out_f32;         // bf16 GEMM writing fp32 output (down projection inside the layer)
   int bm;               // rows per m-tile (gemm_bm); tile_off must be built with it
+  int big;              // m_tile_rows threshold the tile list was built with
   // K split into ksplit equal parts (K / ksplit a multiple of 64).  With ksplit > 1
   // the kernel writes raw fp32 partial products, part s at out + s * R_max * NW
   // (row stride NW = 2N for SwiGLU -- W1 columns then W3 columns -- else N), and
@@ -142,6 +145,7 @@ struct FfnPlan {
   int bm;       // rows per m-tile
   int s_up;     // K splits of the up projection (1 = none)
   int s_down;   // K splits of the down projection
+  int big;      // with bm = 128: experts with at least this many rows take 256-row tiles (m_tile_rows)
 };
 FfnPlan plan_ffn(bool bf16, double rows_per_expert, int E, int R_max, int h, int f);
 // rows per m-tile of the expert GEMMs, from the expected rows per expert

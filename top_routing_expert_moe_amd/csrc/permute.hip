@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     kept = tid < E ? cb : 0;
     if (tid == 0 && a.cap_out != nullptr) *a.cap_out = cb;
   }
-  const int mt = (tid < E && a.BM > 0) ? (kept + a.BM - 1) / a.BM : 0;
+  const int bm = a.BM > 0 ? m_tile_rows(kept, a.BM, a.big) : 1;
+  const int mt = (tid < E && a.BM > 0) ? (kept + bm - 1) / bm : 0;
   int ik = wave_incl_scan(kept, lane, 64), im = wave_incl_scan(mt, lane, 64);
   if (wave < 4 && lane == 63) {
     wsum[0][wave] = ik;
@@ -172,19 +173,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       for (int e = wave; e < E; e += kScanThreads / 64) {
         double ps = 0.0;
         if (a.prob_part != nullptr) {
-          constexpr int kCache = 8;
-          if (a.nrb <= kCache * 64) {
-            float c[kCache];
-#pragma unroll
-            for (int i = 0; i < kCache; ++i) {
-              const int b = lane + 64 * i;
-              c[i] = b < a.nrb ? a.prob_part[(size_t)b * E + e] : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < kCache; ++i) ps += (double)c[i];
-          } else {
-            for (int b = lane; b < a.nrb; b += 64) ps += (double)a.prob_part[(size_t)b * E + e];
-          }
+          for (int b = lane; b < a.nrb; b += 64) ps += (double)a.prob_part[(size_t)b * E + e];
         } else if (lane == 0) {
           ps = (double)a.prob_sum[e];
         }
@@ -198,21 +187,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       double ps = 0.0;
       if (e < E) {
         if (a.prob_part != nullptr) {
-          // up to 16 blocks per thread: all loads issued before the first add (the adds keep
-          // ascending block order)
-          constexpr int kCache = 16;
-          if (a.nrb <= kCache * P) {
-            float c[kCache];
-#pragma unroll
-            for (int i = 0; i < kCache; ++i) {
-              const int b = part + i * P;
-              c[i] = b < a.nrb ? a.prob_part[(size_t)b * E + e] : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < kCache; ++i) ps += (double)c[i];
-          } else {
-            for (int b = part; b < a.nrb; b += P) ps += (double)a.prob_part[(size_t)b * E + e];
-          }
+          for (int b = part; b < a.nrb; b += P) ps += (double)a.prob_part[(size_t)b * E + e];
         } else if (part == 0) {
           ps = (double)a.prob_sum[e];
         }
@@ -235,12 +210,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void tiles_kernel(const int* __restrict__ offsets, int E, int BM,
+__global__ __launch_bounds__(256) void tiles_kernel(const int* __restrict__ offsets, int E, int BM, int big,
                                                     int* __restrict__ tile_off) {
   __shared__ int sh[256];
   const int tid = threadIdx.x;
   const int rows = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
-  const int mt = (rows + BM - 1) / BM;
+  const int bm = m_tile_rows(rows, BM, big);
+  const int mt = (rows + bm - 1) / bm;
   const int incl = block_inclusive_scan256(mt, sh);
   if (tid < E) {
     tile_off[tid] = incl - mt;
@@ -312,8 +288,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_tiles(const int* offsets, int E, int BM, int* tile_off, hipStream_t st) {
-  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(256), 0, st, offsets, E, BM, tile_off);
+hipError_t launch_tiles(const int* offsets, int E, int BM, int big, int* tile_off, hipStream_t st) {
+  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(256), 0, st, offsets, E, BM, big, tile_off);
   return hipGetLastError();
 }
 

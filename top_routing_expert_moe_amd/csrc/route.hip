@@ -117,11 +117,13 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
   }
   const size_t plane = (size_t)E16 * h;
   const bf16_t* wrow[NB];
-  const float* wcol[NB];  // WF32: W_gate[8 * (lane >> 4)][e], or null past E
+  const float* wcol[NB];  // WF32: W_gate[8 * (lane >> 4)][e], clamped to expert E-1 past E (masked by wok)
+  bool wok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int e = e0 + nb * 16 + (lane & 15);
-    if (WF32) wcol[nb] = e < E ? W_gate + (size_t)(8 * (lane >> 4)) * E + e : nullptr;
+    wok[nb] = e < E;
+    if (WF32) wcol[nb] = W_gate + (size_t)(8 * (lane >> 4)) * E + min(e, E - 1);
     else wrow[nb] = planes + (size_t)e * h + 8 * (lane >> 4);
   }
 
@@ -139,14 +141,17 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
     for (int u = 0; u < UU; ++u) {
       if (u < steps) {
         const int kk = k0 + 32 * u;
+        // (xrow points at a valid row for every lane; the invalid tokens' results are not stored)
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) xb[u][tg] = tvalid[tg] ? *(const bf16x8*)(xrow[tg] + kk) : bf16x8{};
+        for (int tg = 0; tg < TG; ++tg) xb[u][tg] = *(const bf16x8*)(xrow[tg] + kk);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           if (WF32) {
             float wv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wv[j] = wcol[nb] ? wcol[nb][(size_t)(kk + j) * E] : 0.f;
+            for (int j = 0; j < 8; ++j) wv[j] = wcol[nb][(size_t)(kk + j) * E];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wv[j] = wok[nb] ? wv[j] : 0.f;
             uint32_t pk[3][4];
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
@@ -307,29 +312,32 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
   if (tid < 256) cnt[tid] = 0;
   __syncthreads();
 
+  // Every load is unconditional, at an index clamped into the arrays (token T-1, expert
+  // E-1, part SH-1), so all of a wave's loads are in flight together; the values of
+  // tokens, experts and parts past the ends are masked afterwards.
   float v[NQ][NV];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int t = t0 + q * TPW + sub;
+    const size_t tc = (size_t)min(t, T - 1);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = gl + 64 * i;
+      const size_t at = tc * E + min(e, E - 1);
       float l = 0.f;
-      if (e < E && t < T) {
-        if (HSPLIT) {
-          // SH <= 8: issue all the loads, then add in ascending z
-          float pz[8];
+      if (HSPLIT) {
+        // SH <= 8 parts, added in ascending z
+        float pz[8];
 #pragma unroll
-          for (int z = 0; z < 8; ++z) pz[z] = z < SH ? lpart[((size_t)z * T + t) * E + e] : 0.f;
+        for (int z = 0; z < 8; ++z) pz[z] = lpart[(size_t)min(z, SH - 1) * T * E + at];
 #pragma unroll
-          for (int z = 0; z < 8; ++z) l += pz[z];
-          logits[(size_t)t * E + e] = l;
-        } else {
-          l = logits[(size_t)t * E + e];
-        }
-        if (noise != nullptr) l += noise[(size_t)t * E + e];
+        for (int z = 0; z < 8; ++z) l += z < SH ? pz[z] : 0.f;
+      } else {
+        l = logits[at];
       }
-      v[q][i] = e < E ? l : -INFINITY;
+      const float nz = noise != nullptr ? noise[at] : 0.f;
+      if (HSPLIT && e < E && t < T) logits[at] = l;
+      v[q][i] = (e < E && t < T) ? (noise != nullptr ? l + nz : l) : (e < E ? 0.f : -INFINITY);
     }
   }
   float psum[NV];
