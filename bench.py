@@ -170,10 +170,13 @@ def measure_other(name: str, steps: int, warmup: int) -> dict:
     for e_ in ev:
         hip.destroy(e_)
     jd = stages.index("expert_up")
-    live = [hip.events(2) for _ in range(steps)]
+    # events before the router and around the up projection (the one before it closes the
+    # routing + permutation region, which so carries no event gaps inside)
+    live = [hip.events(3) for _ in range(steps)]
     arrs = []
     for i in range(steps):
         a_ = (ctypes.c_void_p * (nst + 1))()
+        a_[0] = live[i][2]
         a_[jd], a_[jd + 1] = live[i][0], live[i][1]
         arrs.append(a_)
     torch.cuda.synchronize()
@@ -183,6 +186,7 @@ def measure_other(name: str, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     up_ms = sum(hip.elapsed_ms(live[i][0], live[i][1]) for i in range(steps)) / steps
+    route_ms = sum(hip.elapsed_ms(live[i][2], live[i][0]) for i in range(steps)) / steps
     for e_ in live:
         hip.destroy(e_)
     cnt = counts.cpu().numpy().astype(np.int64)
@@ -199,7 +203,6 @@ def measure_other(name: str, steps: int, warmup: int) -> dict:
     layer_bytes = T * h * es + h * E * 4 + active * (n_up + 1) * h * f * es + T * h * es + T * k * 12
     t_roof = max((flops_up + flops_down) / (PEAK_BF16_TFLOPS * 1e12), layer_bytes / (PEAK_HBM_GBS * 1e9))
     route_bytes = T * h * es + h * E * 4 + T * E * 4 + T * k * 16
-    route_ms = sum(stage_ms[s] for s in ("logits", "select", "scan", "scatter"))
     down_s = stage_ms["expert_down"] / 1e3
     out = {"ms_per_layer": round(ms, 5), "tokens_per_s": round(T / (ms / 1e3), 1),
            "layer_roofline_frac": round(t_roof / (ms / 1e3), 4),
@@ -372,11 +375,18 @@ def main():
     else:
         dom_stage = "expert_up"
     jd = stages.index(dom_stage)
-    live = [hip.events(2) for _ in range(args.steps)]
+    # one more pair of events brackets routing + permutation (before the router, after the
+    # scatter), with no event inside it; where the scatter's end is the dominant kernel's
+    # start the same event serves both
+    ir = stages.index("scatter") + 1
+    live = [hip.events(4) for _ in range(args.steps)]
     arrs = []
     for i in range(args.steps):
         a_ = (ctypes.c_void_p * (nst + 1))()
         a_[jd], a_[jd + 1] = live[i][0], live[i][1]
+        a_[0] = live[i][2]
+        if ir != jd:
+            a_[ir] = live[i][3]
         arrs.append(a_)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -386,6 +396,8 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
     dom_ms = sum(hip.elapsed_ms(live[i][0], live[i][1]) for i in range(args.steps)) / args.steps
+    route_ms = sum(hip.elapsed_ms(live[i][2], live[i][0] if ir == jd else live[i][3])
+                   for i in range(args.steps)) / args.steps
     for e_ in live:
         hip.destroy(e_)
     log("[bench] stage ms: " + ", ".join(f"{s}={v:.4f}" for s, v in stage_ms.items()))
@@ -445,7 +457,7 @@ def main():
     # compulsory bytes of routing + permutation metadata: x and W_gate read once, logits written,
     # topk idx/w, slot_pos and the sorted order (4 B each per assignment)
     route_bytes = T * h * es + h * E * 4 + T * E * 4 + T * k * 16
-    route_ms = sum(stage_ms[s] for s in ("logits", "select", "scan", "scatter"))
+    route_stage_ms = sum(stage_ms[s] for s in ("logits", "select", "scan", "scatter"))
     # the layer's own roof: compulsory bytes (x, W_gate, active weights, y, routing metadata) against
     # its MFMA work
     layer_bytes = T * h * es + h * E * 4 + active * (n_up + 1) * h * f * es + T * h * es + T * k * 12
@@ -467,7 +479,9 @@ def main():
         "expert_down_frac": round(flops_down / (stage_ms["expert_down"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "expert_up_hbm_gbs": round(bytes_up / up_s / 1e9, 1),
         "expert_down_hbm_gbs": round(bytes_down / (stage_ms["expert_down"] / 1e3) / 1e9, 1),
+        "route_permute_ms": round(route_ms, 5),
         "route_gbps": round(route_bytes / (route_ms / 1e3) / 1e9, 1),
+        "route_stage_sum_ms": round(route_stage_ms, 5),
         "router_flops": flops_router,
         "aux_loss": float(aux.cpu()),
     }

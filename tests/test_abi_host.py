@@ -379,6 +379,10 @@ def test_layer_backward_host_errors(L):
     assert pb == T * k * 2 * f * 4 and L.moe_layer_preact_bytes(T, h, f, E, k, 0.0, 0) == pb // 2
     assert L.moe_layer_preact_bytes(T, 96, f, E, k, 0.0, 1) == 0
     assert call(pre=FAKE, preb=pb - 1) == WS
+    # every tensor 16-byte aligned, as for the forward entry points
+    for name in ("x", "Wg", "W1", "W3", "W2", "dy", "dx", "dWg", "dW1", "dW3", "dW2"):
+        assert call(**{name: FAKE + 8}) == UNSUP, name
+    assert call(pre=FAKE + 4, preb=pb) == UNSUP
     assert call(T=0) == OK
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, T, h, f, E, k, 0.0, 1, 1, FAKE, 0.0, FAKE, fwd, None, 0, FAKE, None, FAKE,
          FAKE, FAKE, FAKE, bws, None]

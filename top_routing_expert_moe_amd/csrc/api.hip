@@ -471,9 +471,13 @@ moe_status_t moe_permute(const int32_t* topk_idx, const void* x, int32_t T, int3
   sa.blk_base = w.blk_base;
   sa.tile_off = nullptr;
   sa.aux = (prob_sum && aux_loss) ? aux_loss : nullptr;
-  MOE_TRY(launch_scan(sa, stream));
-  MOE_TRY(launch_scatter(topk_idx, T, E, k, (int)C, offsets, w.blk_base, slot_pos, sorted_slot, w.perm_token,
-                         stream));
+  if (scan_scatter_fusable(sa.nhb, 0, E)) {
+    MOE_TRY(launch_scan_scatter(sa, topk_idx, slot_pos, sorted_slot, w.perm_token, stream));
+  } else {
+    MOE_TRY(launch_scan(sa, stream));
+    MOE_TRY(launch_scatter(topk_idx, T, E, k, (int)C, offsets, w.blk_base, slot_pos, sorted_slot, w.perm_token,
+                           stream));
+  }
   if (x_perm)
     MOE_TRY(launch_gather(x, w.perm_token, offsets, E, rows_max(T, E, k, C), h, (int)elem_bytes(dt), x_perm,
                           stream));
@@ -623,9 +627,12 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.blk_base = w.blk_base;
   sa.tile_off = w.tile_off;
   sa.aux = aux_loss ? aux_loss : w.aux;
-  if (!one_block) MOE_TRY(launch_scan(sa, stream));
+  // (fused scan + scatter: the scan stage holds both and the scatter stage is empty)
+  const bool fused = !one_block && scan_scatter_fusable(sa.nhb, sa.nrb, E);
+  if (fused) MOE_TRY(launch_scan_scatter(sa, w.topk_idx, w.slot_pos, w.sorted_slot, w.perm_token, stream));
+  else if (!one_block) MOE_TRY(launch_scan(sa, stream));
   if (!mark()) return MOE_ERR_DEVICE;
-  if (!one_block)
+  if (!one_block && !fused)
     MOE_TRY(launch_scatter(w.topk_idx, T, E, k, (int)C, w.offsets, w.blk_base, w.slot_pos, w.sorted_slot,
                            w.perm_token, stream));
   if (!mark()) return MOE_ERR_DEVICE;
@@ -907,6 +914,9 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   if ((s = dim_ok(f)) != MOE_OK) return s;
   if (!x || !W_gate || !W1 || !W2 || !dy || !dx || !dW1 || !dW2) return MOE_ERR_ARG;
   if ((act == MOE_ACT_SWIGLU) != (W3 != nullptr) || (act == MOE_ACT_SWIGLU) != (dW3 != nullptr)) return MOE_ERR_ARG;
+  for (const void* p : {x, (const void*)W_gate, W1, W3, W2, dy, (const void*)dx, (const void*)dW_gate,
+                        (const void*)dW1, (const void*)dW3, (const void*)dW2, (const void*)preact})
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;  // (null passes: the optional ones)
   if ((s = opts_ok(opts, x, false)) != MOE_OK) return s;
   // the training forward takes no router variants, so its pre-activations belong to the plain routing
   if (opts != nullptr && preact != nullptr) return MOE_ERR_ARG;

@@ -65,8 +65,22 @@ __global__ void tile_scan_kernel(const int* __restrict__ offsets, int E, int BM,
   tile_off[E] = acc;
 }
 
+// Four consecutive elements at p + i (i a multiple of 4; rows of h, h a multiple of 64, keep
+// them 16-byte aligned for fp32 and 8-byte aligned for bf16).
+__device__ __forceinline__ floatx4 ld4(const float* p, size_t i) { return *(const floatx4*)(p + i); }
+__device__ __forceinline__ floatx4 ld4(const bf16_t* p, size_t i) {
+  const u32x2 v = *(const u32x2*)(p + i);
+  return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                 __uint_as_float(v[1] & 0xFFFF0000u)};
+}
+__device__ __forceinline__ void st4(float* p, size_t i, floatx4 v) { *(floatx4*)(p + i) = v; }
+__device__ __forceinline__ void st4(bf16_t* p, size_t i, floatx4 v) {
+  *(u32x2*)(p + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
 // One workgroup per token: dw[t,j] = <dy[t], O[r]> (O = sum of the down projection's
-// K parts) and dO[r] = w[t,j] dy[t]; dropped slots get dw = 0 and write nothing.
+// K parts) and dO[r] = w[t,j] dy[t]; dropped slots get dw = 0 and write nothing.  Each
+// thread takes four consecutive columns at a time.
 template <typename TD>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const TD* __restrict__ dy, const float* __restrict__ O,
                                                           int n_parts, size_t part_stride,
@@ -76,6 +90,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TD* __restrict__
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int h4 = h >> 2;
   for (int j = 0; j < k; ++j) {
     const int r = slot_pos[(size_t)t * k + j];
     if (r < 0) {
@@ -84,12 +99,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TD* __restrict__
     }
     const float wj = topk_w[(size_t)t * k + j];
     float part = 0.f;
-    for (int i = tid; i < h; i += 256) {
-      const float g = ld(dy, (size_t)t * h + i);
-      float o = 0.f;
-      for (int p = 0; p < n_parts; ++p) o += O[p * part_stride + (size_t)r * h + i];
-      part += g * o;
-      st(dO, (size_t)r * h + i, wj * g);
+    for (int i4 = tid; i4 < h4; i4 += 256) {
+      const floatx4 g = ld4(dy, (size_t)t * h + 4 * i4);
+      floatx4 o = ld4(O, (size_t)r * h + 4 * i4);
+      for (int p = 1; p < n_parts; ++p) o += ld4(O + p * part_stride, (size_t)r * h + 4 * i4);
+      part += (g[0] * o[0] + g[1] * o[1]) + (g[2] * o[2] + g[3] * o[3]);
+      st4(dO, (size_t)r * h + 4 * i4, floatx4{wj * g[0], wj * g[1], wj * g[2], wj * g[3]});
     }
     part = wave_sum(part);
     if ((tid & 63) == 0) red[tid >> 6] = part;
@@ -898,7 +913,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 }
 
 // dx[t] = dx_router[t] + sum over kept slots j (ascending) of dX[slot of (t, j)], where
-// dX is the sum of the `parts` K parts of dXp (part p at dXp + p * part_stride), in order
+// dX is the sum of the `parts` K parts of dXp (part p at dXp + p * part_stride), in order;
+// four consecutive columns per thread at a time
 template <typename TD>
 __global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__ dx_router,
                                                        const TD* __restrict__ jitter,
@@ -906,18 +922,20 @@ __global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__
                                                        const int* __restrict__ slot_pos, int T, int h, int k,
                                                        TD* __restrict__ dx) {
   const int t = blockIdx.x;
-  for (int i = threadIdx.x; i < h; i += 256) {
+  const int h4 = h >> 2;
+  for (int i4 = threadIdx.x; i4 < h4; i4 += 256) {
+    const size_t at = (size_t)t * h + 4 * i4;
     // the router read x * u: its share of the gradient is multiplied by u
-    float v = dx_router[(size_t)t * h + i];
-    if (jitter != nullptr) v *= ld(jitter, (size_t)t * h + i);
+    floatx4 v = ld4(dx_router, at);
+    if (jitter != nullptr) v *= ld4(jitter, at);
     for (int j = 0; j < k; ++j) {
       const int r = slot_pos[(size_t)t * k + j];
       if (r < 0) continue;
-      float d = dXp[(size_t)r * h + i];
-      for (int p = 1; p < parts; ++p) d += dXp[p * part_stride + (size_t)r * h + i];
+      floatx4 d = ld4(dXp, (size_t)r * h + 4 * i4);
+      for (int p = 1; p < parts; ++p) d += ld4(dXp + p * part_stride, (size_t)r * h + 4 * i4);
       v += d;
     }
-    st(dx, (size_t)t * h + i, v);
+    st4(dx, at, v);
   }
 }
 

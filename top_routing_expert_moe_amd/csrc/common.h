@@ -83,6 +83,11 @@ __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + e
 __host__ __device__ __forceinline__ int m_tile_rows(int rows, int fh, int big) {
   return (fh == 128 && rows >= big) ? 256 : fh;
 }
+// an expert's m-tiles: ceil(rows / m_tile_rows(rows, fh, big)); the last may be partial
+__host__ __device__ __forceinline__ int m_tile_count(int rows, int fh, int big) {
+  const int fe = m_tile_rows(rows, fh, big);
+  return (rows + fe - 1) / fe;
+}
 
 // Binary search: the expert e with tile_off[e] <= mt < tile_off[e+1] (E >= 1).
 __device__ __forceinline__ int find_expert(const int* __restrict__ tile_off, int E, int mt) {

@@ -85,6 +85,11 @@ struct ScanArgs {
   int* cap_out;            // scalar or null
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+// the scan and the scatter in one launch (not for fixed-capacity buckets); fusable: whether
+// every block can read all nhb histograms (and the nrb softmax partial sums, nrb <= nhb)
+bool scan_scatter_fusable(int nhb, int nrb, int E);
+hipError_t launch_scan_scatter(const ScanArgs& a, const int* topk_idx, int* slot_pos, int* sorted_slot,
+                               int* perm_token, hipStream_t st);
 // bits of an expert id (at least 1): the scatter's match by ballots
 inline int expert_bits(int E) {
   int nbits = 1;

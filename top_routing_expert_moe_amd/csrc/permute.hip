@@ -25,6 +25,8 @@
 // scatter itself (single_block_permute in permute_dev.h).
 #include <limits.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "permute_dev.h"
@@ -142,8 +144,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     kept = tid < E ? cb : 0;
     if (tid == 0 && a.cap_out != nullptr) *a.cap_out = cb;
   }
-  const int bm = a.BM > 0 ? m_tile_rows(kept, a.BM, a.big) : 1;
-  const int mt = (tid < E && a.BM > 0) ? (kept + bm - 1) / bm : 0;
+  const int mt = (tid < E && a.BM > 0) ? m_tile_count(kept, a.BM, a.big) : 0;
   int ik = wave_incl_scan(kept, lane, 64), im = wave_incl_scan(mt, lane, 64);
   if (wave < 4 && lane == 63) {
     wsum[0][wave] = ik;
@@ -210,13 +211,117 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
 }
 
+// The scan and the scatter in one launch (one workgroup of 256 per token block), for when
+// every block can afford to read all the block histograms: block b sums each expert's
+// column of blk_counts over all blocks (the counts) and over the blocks before b (its rank
+// origins), P threads per expert, each over a contiguous range of at most PER blocks with
+// all its loads in flight at once.  Every block then has the same counts, so the same
+// offsets; block 0 also writes counts, offsets, the m-tile list and the aux loss.  Integer
+// sums are exact, and the aux loss is summed in a fixed order, so the results are those of
+// the separate scan and scatter kernels (the aux loss up to the order of its fp64 sum).
+template <int PER>
+__global__ __launch_bounds__(256) void scan_scatter_kernel(ScanArgs a, const int* __restrict__ topk_idx, int nbits,
+                                                           int* __restrict__ slot_pos, int* __restrict__ sorted_slot,
+                                                           int* __restrict__ perm_token) {
+  __shared__ int cnt_sh[256], base_sh[256], off_sh[256];
+  __shared__ int wsum[2][4];
+  __shared__ double dterm[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, blk = blockIdx.x;
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int P = min(64, 256 / ep);  // threads per expert (a power of two dividing 64)
+  const int e = tid / P, part = tid % P;
+  const bool act = e < E;
+  const int ec = min(e, E - 1);
+  const int per = (a.nhb + P - 1) / P;  // <= PER (checked by the launcher)
+  const int b0 = part * per;
+  int tot = 0, pre = 0;
+  {
+    int c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) c[i] = a.blk_counts[(size_t)min(b0 + i, a.nhb - 1) * E + ec];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int bi = b0 + i;
+      const int v = (act && i < per && bi < a.nhb) ? c[i] : 0;
+      tot += v;
+      pre += bi < blk ? v : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    if (o < P) {
+      tot += __shfl_xor(tot, o, kWave);
+      pre += __shfl_xor(pre, o, kWave);
+    }
+  }
+  if (act && part == 0) {
+    cnt_sh[e] = tot;
+    base_sh[e] = pre;
+  }
+  __syncthreads();
+  // kept counts -> offsets, m-tiles -> tile list: exclusive scans over the experts (4 waves)
+  const int cnt = tid < E ? cnt_sh[tid] : 0;
+  const int kept = tid < E ? min(cnt, a.C) : 0;
+  const int mt = (tid < E && a.BM > 0) ? m_tile_count(kept, a.BM, a.big) : 0;
+  int ik = wave_incl_scan(kept, lane, 64), im = wave_incl_scan(mt, lane, 64);
+  if (lane == 63) {
+    wsum[0][wave] = ik;
+    wsum[1][wave] = im;
+  }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    ik += wsum[0][w];
+    im += wsum[1][w];
+  }
+  if (tid < E) off_sh[tid] = ik - kept;
+  if (blk == 0 && tid < E) {
+    a.counts[tid] = cnt;
+    a.offsets[tid] = ik - kept;
+    if (tid == E - 1) a.offsets[E] = ik;
+    if (a.BM > 0 && a.tile_off != nullptr) {
+      a.tile_off[tid] = im - mt;
+      if (tid == E - 1) a.tile_off[E] = im;
+    }
+  }
+  if (blk == 0 && a.aux != nullptr && (a.prob_part != nullptr || a.prob_sum != nullptr)) {
+    // sum_t p[t,e] in fp64: the same P-thread ranges over the blocks' softmax sums, then a
+    // butterfly over the parts (each step adds the same two values on both lanes, so every
+    // lane of a group holds the same sum)
+    double ps = 0.0;
+    if (a.prob_part != nullptr) {
+      float q[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) q[i] = a.prob_part[(size_t)min(b0 + i, a.nrb - 1) * E + ec];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ps += (act && i < per && b0 + i < a.nrb) ? (double)q[i] : 0.0;
+    } else if (act && part == 0) {
+      ps = (double)a.prob_sum[e];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+      if (o < P) ps += __shfl_xor(ps, o, kWave);
+    const double n = (double)a.T * (double)a.k;
+    if (act && part == 0) dterm[e] = ((double)cnt_sh[e] / n) * (ps / (double)a.T);
+    __syncthreads();
+    if (wave == 0) {
+      double t = 0.0;
+      for (int x = lane; x < E; x += 64) t += dterm[x];
+      t = wave_sum_f64(t);
+      if (lane == 0) *a.aux = (float)((double)E * t);
+    }
+  }
+  __syncthreads();
+  scatter_block(blk, topk_idx, a.T, E, a.k, nbits, a.C, off_sh, base_sh, slot_pos, sorted_slot, perm_token);
+}
+
 __global__ __launch_bounds__(256) void tiles_kernel(const int* __restrict__ offsets, int E, int BM, int big,
                                                     int* __restrict__ tile_off) {
   __shared__ int sh[256];
   const int tid = threadIdx.x;
   const int rows = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
-  const int bm = m_tile_rows(rows, BM, big);
-  const int mt = (rows + bm - 1) / bm;
+  const int mt = tid < E ? m_tile_count(rows, BM, big) : 0;
   const int incl = block_inclusive_scan256(mt, sh);
   if (tid < E) {
     tile_off[tid] = incl - mt;
@@ -285,6 +390,40 @@ hipError_t launch_hist(const int* topk_idx, int T, int k, int E, int* blk_counts
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+namespace {
+// blocks each thread of the fused scan + scatter sums (P threads per expert), 0 = not fusable
+int scan_scatter_per(int nhb, int nrb, int E) {
+  if (E <= 0 || E > 256 || nrb > nhb) return 0;
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int P = std::min(64, 256 / ep);
+  const int per = (nhb + P - 1) / P;
+  return per <= 64 ? per : 0;
+}
+}  // namespace
+
+bool scan_scatter_fusable(int nhb, int nrb, int E) { return scan_scatter_per(nhb, nrb, E) > 0; }
+
+hipError_t launch_scan_scatter(const ScanArgs& a, const int* topk_idx, int* slot_pos, int* sorted_slot,
+                               int* perm_token, hipStream_t st) {
+  const int per = scan_scatter_per(a.nhb, a.prob_part != nullptr ? a.nrb : 0, a.E);
+  if (per == 0 || a.binned) return hipErrorInvalidValue;
+  const int nbits = expert_bits(a.E);
+  const dim3 grid(a.nhb), block(256);
+#define MOE_SCAN_SCATTER(PER_)                                                                                    \
+  hipLaunchKernelGGL(scan_scatter_kernel<PER_>, grid, block, 0, st, a, topk_idx, nbits, slot_pos, sorted_slot, \
+                     perm_token)
+  if (per <= 1) MOE_SCAN_SCATTER(1);
+  else if (per <= 2) MOE_SCAN_SCATTER(2);
+  else if (per <= 4) MOE_SCAN_SCATTER(4);
+  else if (per <= 8) MOE_SCAN_SCATTER(8);
+  else if (per <= 16) MOE_SCAN_SCATTER(16);
+  else if (per <= 32) MOE_SCAN_SCATTER(32);
+  else MOE_SCAN_SCATTER(64);
+#undef MOE_SCAN_SCATTER
   return hipGetLastError();
 }
 

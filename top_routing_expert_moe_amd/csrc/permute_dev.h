@@ -99,8 +99,7 @@ __device__ __forceinline__ void single_block_permute(const int* cnt, const float
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid < E ? cnt[tid] : 0;
   const int kept = tid < E ? min(c, sp.C) : 0;
-  const int bm = sp.BM > 0 ? m_tile_rows(kept, sp.BM, sp.big) : 1;
-  const int mt = (tid < E && sp.BM > 0) ? (kept + bm - 1) / bm : 0;
+  const int mt = (tid < E && sp.BM > 0) ? m_tile_count(kept, sp.BM, sp.big) : 0;
   int ik = wave_incl_scan(kept, lane, 64), im = wave_incl_scan(mt, lane, 64);
   if (wave < 4 && lane == 63) {
     wsum[0][wave] = ik;

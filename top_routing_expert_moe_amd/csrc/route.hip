@@ -10,17 +10,21 @@
 // gfx950 design, two kernels:
 //  * logits.  For bf16 activations the contraction runs on the matrix cores
 //    at fp32 accuracy: W_gate (fp32) is split exactly into three bf16 planes
-//    hi + mid + lo (each the bf16 rounding of what the previous ones left, 24
+//    hi + mid + lo (each the top 16 bits of what the previous ones left, 24
 //    significant bits in total), a bf16 x times a bf16 plane is exact in fp32,
 //    and v_mfma_f32_16x16x32_bf16 accumulates the three products in fp32.  Each
 //    wave streams 16 token rows straight from HBM into MFMA operands (no LDS).
-//    Up to 16 experts each wave splits the fp32 weights it loads in registers;
-//    from 32 experts up (where that split would cost as much as the MFMAs) a
-//    first kernel writes the planes ([3][E16][h], k-contiguous; small, they stay
-//    in L2).  For fp32 activations a plain fp32 FMA kernel is used instead.
-//  * select.  A group of lanes per token (a whole wave from 64 experts up): lane
-//    e holds the logits of experts e, e+64, ...; softmax sums and k rounds of a
-//    64-bit group arg-max pick the experts.
+//    Up to 16 experts, and 64 experts over many tokens, each wave splits the fp32
+//    weights it loads in registers (a mask, a subtraction, a mask, a subtraction and
+//    a byte permute per pair); otherwise a first kernel writes the planes
+//    ([3][E16][h], k-contiguous; small, they stay in L2), and with several expert
+//    groups the workgroups on one XCD share a group, so its planes stay in that
+//    XCD's L2.  Each wave keeps the loads of its next k-steps in flight while it
+//    multiplies the current ones.  For fp32 activations a plain fp32 FMA kernel is
+//    used instead.
+//  * select.  G lanes per token (4 up to 64 experts, 8, 16 beyond), each lane
+//    holding a contiguous chunk of E/G experts: softmax sums and k rounds of a 64-bit
+//    group arg-max, exchanged between the G lanes with DPP and swizzles, pick the experts.
 //    The key orders by logit (IEEE order, -0 == +0) then by the lower expert
 //    index, so ties are deterministic.  The same kernel counts its block's
 //    assignments per expert (the histogram) and sums the softmax per expert.
@@ -46,16 +50,19 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ float bf16_round(float v) { return __uint_as_float(f32_to_bf16_bits(v) << 16); }
-
-// w == hi + mid + lo exactly (fp32 w: 24 significant bits, 8 per bf16 part), each part
-// the bf16 rounding of what the previous parts leave
-__device__ __forceinline__ void split3(float w, float& hi, float& mid, float& lo) {
-  hi = bf16_round(w);
-  const float r1 = w - hi;  // exact
-  mid = bf16_round(r1);
-  lo = bf16_round(r1 - mid);
+// w == hi + mid + lo exactly, each part a bf16 value: hi is w with its low 16 bits cleared
+// (same sign and exponent, so w - hi is exact and holds the 16 low significand bits), mid
+// is that remainder with its low 16 bits cleared, and lo = remainder - mid, exact and of at
+// most 8 significant bits, so a bf16 too.  Returned as fp32 bit patterns with zero low halves.
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = __float_as_uint(w) & 0xFFFF0000u;
+  const float r1 = w - __uint_as_float(hi);  // exact
+  mid = __float_as_uint(r1) & 0xFFFF0000u;
+  lo = __float_as_uint(r1 - __uint_as_float(mid));  // exact; low 16 bits zero
 }
+
+// the bf16 pair (lo16 = upper half of a, hi16 = upper half of b) in one v_perm_b32
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 // ---------------------------------------------------------------------------
 // W_gate [h,E] fp32 -> planes [3][E16][h] bf16 with hi + mid + lo == W (to fp32 precision)
@@ -65,12 +72,12 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
   if (idx >= (int64_t)E16 * h) return;
   const int e = (int)(idx / h), i = (int)(idx % h);
   const float w = e < E ? W_gate[(size_t)i * E + e] : 0.f;
-  float hi, mid, lo;
+  uint32_t hi, mid, lo;
   split3(w, hi, mid, lo);
   const size_t plane = (size_t)E16 * h;
-  planes[idx] = (bf16_t)(__float_as_uint(hi) >> 16);
-  planes[plane + idx] = (bf16_t)(__float_as_uint(mid) >> 16);
-  planes[2 * plane + idx] = (bf16_t)(__float_as_uint(lo) >> 16);
+  planes[idx] = (bf16_t)(hi >> 16);
+  planes[plane + idx] = (bf16_t)(mid >> 16);
+  planes[2 * plane + idx] = (bf16_t)(lo >> 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -85,21 +92,45 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
 // WF32: the weights come as W_gate itself ([h][E] fp32) and each lane splits the eight
 // k-values of its expert column that it loads (exactly what the split kernel writes);
 // otherwise they come as the bf16 planes.
+// One batch of a wave's operands: UU k-steps of x (TG groups of 16 tokens) and of the
+// router weights (NB groups of 16 experts), as loaded: the three bf16 planes, or (WF32)
+// eight fp32 k-values of the lane's expert column.
+template <int UU, int TG, int NB, bool WF32>
+struct LogitBatch {
+  bf16x8 x[UU][TG];
+  bf16x8 p[WF32 ? 1 : UU][WF32 ? 1 : NB][3];
+  float w[WF32 ? UU : 1][WF32 ? NB : 1][8];
+};
+
 template <int NB, int TW, int NW, int TG = 1, bool WF32 = false>
 __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ planes,
                                                           const float* __restrict__ W_gate,
                                                           const float* __restrict__ bias, int T, int h, int E,
-                                                          int E16, float* __restrict__ logits) {
+                                                          int E16, float* __restrict__ logits, int gx, int gy) {
   constexpr int KS = NW / TW;
-  // k-steps of 32 per batch of loads (bounded by registers: 128 per lane at 16 waves)
-  constexpr int U = NB >= 4 ? 2 : (NB == 2 ? 4 : (NW > 4 ? 4 : 8));
+  // k-steps of 32 per batch of loads; two batches are live (the next one is in flight while
+  // this one is multiplied), so the batch shrinks as the fragments per step grow
+  constexpr int FR = NB * TG;
+  constexpr int UU = FR >= 4 ? 1 : (FR >= 2 ? 2 : (NW > 4 ? 2 : 4));
+  using Batch = LogitBatch<UU, TG, NB, WF32>;
   __shared__ floatx4 red[KS > 1 ? KS - 1 : 1][TW][TG][NB][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tw = wave % TW, ks = wave / TW;
-  const int t0 = blockIdx.x * (16 * TW * TG) + tw * 16 * TG;
-  const int e0 = blockIdx.y * (16 * NB);
+  int bx = blockIdx.x, by = 0;
+  if (gy > 1) {
+    // gx token tiles x gy expert groups on a 1-D grid (a multiple of 8): workgroups are
+    // dispatched round-robin over the 8 XCDs, and the ones on one XCD take consecutive
+    // tiles of one expert group, so that group's weight planes stay in that XCD's L2
+    const int n = gx * gy, per = (n + 7) >> 3;
+    const int L = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (L >= n) return;
+    by = L / gx;
+    bx = L - by * gx;
+  }
+  const int t0 = bx * (16 * TW * TG) + tw * 16 * TG;
+  const int e0 = by * (16 * NB);
   const int kspan = h / (KS * gridDim.z);
   const int kb = (blockIdx.z * KS + ks) * kspan, ke = kb + kspan;
   if (gridDim.z > 1) {
@@ -127,64 +158,100 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
     else wrow[nb] = planes + (size_t)e * h + 8 * (lane >> 4);
   }
 
-  floatx4 acc[TG][NB];
+  // few fragments per step: one accumulator per plane, so no MFMA waits on the one before
+  constexpr int PA = NB * TG >= 4 ? 1 : 3;
+  floatx4 acc[TG][NB], accp[PA][TG][NB];
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg)
+  for (int q = 0; q < PA; ++q)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[tg][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) accp[q][tg][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int UU = TG > 1 ? 1 : U;
-  for (int k0 = kb; k0 < ke; k0 += 32 * UU) {
-    const int steps = min(UU, (ke - k0) / 32);
-    bf16x8 xb[UU][TG], wa[UU][NB][3];
+  // Loads of the batch at k0; every step's k is clamped into [kb, ke) so that all loads
+  // are unconditional (steps past ke re-read the last one and are not multiplied).
+  auto load = [&](int k0, Batch& b) {
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-      if (u < steps) {
-        const int kk = k0 + 32 * u;
-        // (xrow points at a valid row for every lane; the invalid tokens' results are not stored)
+      const int kk = min(k0 + 32 * u, ke - 32);
+      // (xrow points at a valid row for every lane; the invalid tokens' results are not stored)
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) xb[u][tg] = *(const bf16x8*)(xrow[tg] + kk);
+      for (int tg = 0; tg < TG; ++tg) b.x[u][tg] = *(const bf16x8*)(xrow[tg] + kk);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          if (WF32) {
-            float wv[8];
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (WF32) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wv[j] = wcol[nb][(size_t)(kk + j) * E];
+          for (int j = 0; j < 8; ++j) b.w[u][nb][j] = wcol[nb][(size_t)(kk + j) * E];
+        } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wv[j] = wok[nb] ? wv[j] : 0.f;
-            uint32_t pk[3][4];
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-              float p0[3], p1[3];
-              split3(wv[j], p0[0], p0[1], p0[2]);
-              split3(wv[j + 1], p1[0], p1[1], p1[2]);
-#pragma unroll
-              for (int p = 0; p < 3; ++p)
-                pk[p][j / 2] = (__float_as_uint(p0[p]) >> 16) | (__float_as_uint(p1[p]) & 0xFFFF0000u);
-            }
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-              wa[u][nb][p] = __builtin_bit_cast(bf16x8, u32x4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]});
-          } else {
-#pragma unroll
-            for (int p = 0; p < 3; ++p) wa[u][nb][p] = *(const bf16x8*)(wrow[nb] + p * plane + kk);
-          }
+          for (int p = 0; p < 3; ++p) b.p[u][nb][p] = *(const bf16x8*)(wrow[nb] + p * plane + kk);
         }
       }
     }
+  };
+  // Per k-step: the weight fragments of every expert group first, then the MFMAs with the
+  // plane outermost, so consecutive MFMAs update different accumulators (NB*TG of them)
+  // rather than one accumulator three times in a row.
+  auto multiply = [&](int steps, const Batch& b) {
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
       if (u < steps) {
+        bf16x8 wp[NB][3];
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg)
+        for (int nb = 0; nb < NB; ++nb) {
+          if constexpr (WF32) {
+            uint32_t pk[3][4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+              uint32_t p0[3], p1[3];
+              split3(wok[nb] ? b.w[u][nb][j] : 0.f, p0[0], p0[1], p0[2]);
+              split3(wok[nb] ? b.w[u][nb][j + 1] : 0.f, p1[0], p1[1], p1[2]);
+#pragma unroll
+              for (int p = 0; p < 3; ++p) pk[p][j / 2] = pack_hi16(p0[p], p1[p]);
+            }
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              wp[nb][p] = __builtin_bit_cast(bf16x8, u32x4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]});
+          } else {
+#pragma unroll
+            for (int p = 0; p < 3; ++p) wp[nb][p] = b.p[u][nb][p];
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-              acc[tg][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[u][nb][p], xb[u][tg], acc[tg][nb], 0, 0, 0);
+            for (int tg = 0; tg < TG; ++tg)
+              accp[p % PA][tg][nb] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp[nb][p], b.x[u][tg], accp[p % PA][tg][nb], 0, 0, 0);
       }
     }
+  };
+  {
+    // two batches in ping-pong: the loads of one are in flight while the other is multiplied
+    Batch b0, b1;
+    int k0 = kb;
+    load(k0, b0);
+    while (true) {
+      load(k0 + 32 * UU, b1);
+      multiply(min(UU, (ke - k0) / 32), b0);
+      k0 += 32 * UU;
+      if (k0 >= ke) break;
+      load(k0 + 32 * UU, b0);
+      multiply(min(UU, (ke - k0) / 32), b1);
+      k0 += 32 * UU;
+      if (k0 >= ke) break;
+    }
   }
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc[tg][nb] = accp[0][tg][nb];
+#pragma unroll
+      for (int q = 1; q < PA; ++q) acc[tg][nb] += accp[q][tg][nb];
+    }
   // lane holds token (lane & 15) of each group, experts 4*(lane>>4) + 0..3 of each 16-block
   if (KS > 1) {
     if (ks > 0) {
@@ -293,6 +360,51 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // renormalised over them.
 // FUSE (T <= kSelTokens, one workgroup): the workgroup then also does the scan and the
 // scatter (single_block_permute) into the outputs named by sp.
+// Layout: G lanes per token (a power of two, at most 16), lane gl of a token holding the
+// NV experts gl*NV .. gl*NV + NV - 1 (E <= G*NV), so the reductions over a token (max,
+// sum, arg-max) take log2(G) lane exchanges (DPP within quads, swizzles beyond).
+
+// v from lane (lane ^ O): quad permutes for O = 1, 2; ds_swizzle (bit mode, xor mask O) up to
+// 16; every lane of the wave takes part
+template <int O>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "xor distance");
+  if constexpr (O == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  else if constexpr (O == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  else if constexpr (O < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (O << 10) | 0x1F);
+  else return (uint32_t)__shfl_xor((int)v, O, kWave);
+}
+template <int O>
+__device__ __forceinline__ float lane_xor_f(float v) { return __uint_as_float(lane_xor<O>(__float_as_uint(v))); }
+
+// reductions over the aligned groups of G lanes, exchanges at distance 1, 2, ..., G/2 (each
+// step combines the same two values on both lanes, so every lane ends with the same result)
+template <int G, int O = 1>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (O < G) return group_max<G, 2 * O>(fmaxf(v, lane_xor_f<O>(v)));
+  else return v;
+}
+template <int G, int O = 1>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (O < G) return group_sum<G, 2 * O>(v + lane_xor_f<O>(v));
+  else return v;
+}
+template <int G, int O = 1>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  if constexpr (O < G) {
+    const uint64_t o = ((uint64_t)lane_xor<O>((uint32_t)(v >> 32)) << 32) | lane_xor<O>((uint32_t)v);
+    return group_max_u64<G, 2 * O>(o > v ? o : v);
+  } else {
+    return v;
+  }
+}
+// sum over the lanes that share lane % G (the token groups of a wave), distances G .. 32
+template <int G, int O = G>
+__device__ __forceinline__ float across_groups_sum(float v) {
+  if constexpr (O < 64) return across_groups_sum<G, 2 * O>(v + lane_xor_f<O>(v));
+  else return v;
+}
+
 template <int NV, int G, bool HSPLIT, int NWS = 4, bool FUSE = false>
 __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ logits, const float* __restrict__ lpart,
                                                      int SH, int T, int E, int k,
@@ -300,44 +412,69 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
                                                      float* __restrict__ prob_part, int* __restrict__ blk_counts,
                                                      const float* __restrict__ noise, float inv_temp, int vflags,
                                                      SmallPermute sp) {
-  static_assert(G == 64 || NV == 1, "several values per lane only with whole-wave groups");
+  static_assert(G >= 1 && G <= 16 && (G & (G - 1)) == 0 && G * NV <= 256, "lanes per token");
   constexpr int TPW = 64 / G;                  // tokens per wave and pass
   constexpr int NQ = kSelTokens / NWS / TPW;   // passes per wave
-  static_assert(NQ >= 1, "tokens per wave");
-  __shared__ float pp[NWS][64 * NV];
+  static_assert(NQ >= 1 && NWS * 64 >= 256, "tokens per wave; 256 threads for the histogram");
+  constexpr int KR = (16 + G - 1) / G;         // selections a lane stores (k <= 16)
+  __shared__ float pp[NWS][256];
   __shared__ int cnt[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int sub = lane / G, gl = lane % G;
+  const int eb = gl * NV;  // this lane's first expert
   const int t0 = blockIdx.x * kSelTokens + w * (kSelTokens / NWS);
   if (tid < 256) cnt[tid] = 0;
   __syncthreads();
 
   // Every load is unconditional, at an index clamped into the arrays (token T-1, expert
   // E-1, part SH-1), so all of a wave's loads are in flight together; the values of
-  // tokens, experts and parts past the ends are masked afterwards.
+  // tokens, experts and parts past the ends are masked afterwards.  Rows whose lanes'
+  // chunks all lie inside (E == G*NV) on 16-byte aligned arrays take 16-byte loads.
+  const bool vec4 = NV % 4 == 0 && E == G * NV && ((uintptr_t)logits & 15) == 0 &&
+                    ((uintptr_t)noise & 15) == 0;
   float v[NQ][NV];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int t = t0 + q * TPW + sub;
-    const size_t tc = (size_t)min(t, T - 1);
+    const size_t row = (size_t)min(t, T - 1) * E;
+    float l[NV], nz[NV];
+    if (HSPLIT) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = gl + 64 * i;
-      const size_t at = tc * E + min(e, E - 1);
-      float l = 0.f;
-      if (HSPLIT) {
+      for (int i = 0; i < NV; ++i) {
+        const size_t at = row + min(eb + i, E - 1);
         // SH <= 8 parts, added in ascending z
         float pz[8];
 #pragma unroll
         for (int z = 0; z < 8; ++z) pz[z] = lpart[(size_t)min(z, SH - 1) * T * E + at];
+        l[i] = 0.f;
 #pragma unroll
-        for (int z = 0; z < 8; ++z) l += z < SH ? pz[z] : 0.f;
-      } else {
-        l = logits[at];
+        for (int z = 0; z < 8; ++z) l[i] += z < SH ? pz[z] : 0.f;
+        nz[i] = noise != nullptr ? noise[at] : 0.f;
+        if (eb + i < E && t < T) logits[at] = l[i];
       }
-      const float nz = noise != nullptr ? noise[at] : 0.f;
-      if (HSPLIT && e < E && t < T) logits[at] = l;
-      v[q][i] = (e < E && t < T) ? (noise != nullptr ? l + nz : l) : (e < E ? 0.f : -INFINITY);
+    } else if (vec4) {
+#pragma unroll
+      for (int i = 0; i < NV; i += 4) {
+        const floatx4 lv = *(const floatx4*)(logits + row + eb + i);
+        const floatx4 nv = noise != nullptr ? *(const floatx4*)(noise + row + eb + i) : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          l[i + j] = lv[j];
+          nz[i + j] = nv[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const size_t at = row + min(eb + i, E - 1);
+        l[i] = logits[at];
+        nz[i] = noise != nullptr ? noise[at] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool ev = eb + i < E;
+      v[q][i] = (ev && t < T) ? (noise != nullptr ? l[i] + nz[i] : l[i]) : (ev ? 0.f : -INFINITY);
     }
   }
   float psum[NV];
@@ -351,16 +488,14 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NV; ++i) m = fmaxf(m, v[q][i]);
-#pragma unroll
-    for (int o = G / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    m = group_max<G>(m);
     float ex[NV], s = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      ex[i] = gl + 64 * i < E ? expf((v[q][i] - m) * inv_temp) : 0.f;
+      ex[i] = eb + i < E ? expf((v[q][i] - m) * inv_temp) : 0.f;
       s += ex[i];
     }
-#pragma unroll
-    for (int o = G / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+    s = group_sum<G>(s);
     const float inv = 1.0f / s;
     if (tv) {
 #pragma unroll
@@ -370,51 +505,61 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
     bool taken[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) taken[i] = false;
-    float lmax = 0.f, wsum = 0.f, my_l = 0.f;
-    int my_e = 0;
+    float lmax = 0.f, wsum = 0.f;
+    float my_l[KR];
+    int my_e[KR];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      my_l[r] = 0.f;
+      my_e[r] = 0;
+    }
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int e = gl + 64 * i;
+        const int e = eb + i;
         if (e < E && !taken[i]) {
           const uint64_t key = ((uint64_t)ordered_bits(v[q][i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
           best = key > best ? key : best;
         }
       }
-#pragma unroll
-      for (int o = G / 2; o >= 1; o >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)best, o, kWave);
-        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, kWave);
-        const uint64_t b2 = ((uint64_t)hi << 32) | lo;
-        best = b2 > best ? b2 : best;
-      }
+      best = group_max_u64<G>(best);
       const int e_sel = (int)(0xFFFFFFFFu - (uint32_t)best);
       const float l_sel = from_ordered((uint32_t)(best >> 32));
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        if (gl + 64 * i == e_sel) taken[i] = true;
+        if (eb + i == e_sel) taken[i] = true;
       if (j == 0) lmax = l_sel;
       wsum += expf((l_sel - lmax) * inv_temp);
-      if (gl == j) { my_l = l_sel; my_e = e_sel; }
+#pragma unroll
+      for (int r = 0; r < KR; ++r)
+        if (j == gl + G * r) {
+          my_l[r] = l_sel;
+          my_e[r] = e_sel;
+        }
     }
-    if (tv && gl < k) {
-      const int e_out = (vflags & 1) ? (int)(((int64_t)t * k + gl) % E) : my_e;
-      topk_idx[(size_t)t * k + gl] = e_out;
-      // lmax is the token's largest logit, m: the same value
-      const float ew = expf((my_l - lmax) * inv_temp);
-      topk_w[(size_t)t * k + gl] = (vflags & 2) ? ew * inv : ew / wsum;
-      if (blk_counts != nullptr) atomicAdd(&cnt[e_out], 1);
+    if (tv) {
+#pragma unroll
+      for (int r = 0; r < KR; ++r) {
+        const int j = gl + G * r;
+        if (j < k) {
+          const int e_out = (vflags & 1) ? (int)(((int64_t)t * k + j) % E) : my_e[r];
+          topk_idx[(size_t)t * k + j] = e_out;
+          // lmax is the token's largest logit, m: the same value
+          const float ew = expf((my_l[r] - lmax) * inv_temp);
+          topk_w[(size_t)t * k + j] = (vflags & 2) ? ew * inv : ew / wsum;
+          if (blk_counts != nullptr) atomicAdd(&cnt[e_out], 1);
+        }
+      }
     }
   }
   // the token groups of a wave hold partial sums of the same experts: add them (fixed tree)
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int o = G; o < 64; o <<= 1) psum[i] += __shfl_xor(psum[i], o, kWave);
+  for (int i = 0; i < NV; ++i) psum[i] = across_groups_sum<G>(psum[i]);
   if (prob_part != nullptr && sub == 0) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) pp[w][gl + 64 * i] = psum[i];
+    for (int i = 0; i < NV; ++i)
+      if (eb + i < 256) pp[w][eb + i] = psum[i];
   }
   __syncthreads();
   if (prob_part != nullptr)
@@ -449,18 +594,24 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
 }
 
 template <int NB, int TW, int NW = 4, int TG = 1>
-void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr) {
-  const dim3 grid((a.T + 16 * TW * TG - 1) / (16 * TW * TG), E16 / (16 * NB), SH);
-  if constexpr (NB == 1) {
-    if (E16 <= 16) {  // weights split in registers
-      hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true>), grid, dim3(NW * 64), 0, st,
-                         (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
-                     (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits);
+void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr,
+                        bool wf32 = false) {
+  const int gx = (a.T + 16 * TW * TG - 1) / (16 * TW * TG), gy = E16 / (16 * NB);
+  // one expert group: gx x SH grid; several: a 1-D grid, XCD-aware (SH is then 1)
+  const dim3 grid = gy > 1 ? dim3((unsigned)((gx * gy + 7) / 8 * 8)) : dim3(gx, 1, SH);
+  if (wf32 || E16 <= 16)  // weights split in registers
+    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true>), grid, dim3(NW * 64), 0, st,
+                       (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx,
+                       gy);
+  else
+    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
+                       (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx, gy);
 }
+
+// 64 experts, many tokens: the kernel splits the fp32 weights itself (no planes kernel)
+// (measured at T = 8192, h = 1024: the logits 22.3 -> 17.8 us, and the 4.4 us planes kernel
+// is gone)
+bool logits_wf32_e64(int T, int h, int E16) { return E16 == 64 && h % 256 == 0 && T >= 1024; }
 
 }  // namespace
 
@@ -474,7 +625,10 @@ int route_hsplit(int T, int h, int E, bool bf16) {
   // few tokens: too few workgroups to stream the router weights and x at full rate, so the
   // contraction over h is split across workgroups (partial logits added in the selection)
   const int E16 = (E + 15) / 16 * 16;
-  if (!bf16 || E16 > 16 || T > 1024) return 1;
+  if (!bf16 || E16 > 16) return 1;
+  // (many tokens: none; a 2- or 4-way split with 32 or 64 tokens per workgroup measured
+  // slower at T = 4096, h = 4096, E = 8)
+  if (T > 1024) return 1;
   const int nwg = (T + 15) / 16;
   int SH = 1;
   // (8-way at most: the selection adds the parts; measured best at T = 64, h = 4096)
@@ -501,7 +655,8 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
     if (a.bf16) {
       const int E16 = (a.E + 15) / 16 * 16;
       const int64_t n = (int64_t)E16 * a.h;
-      if (E16 > 16)
+      const bool wf64 = logits_wf32_e64(a.T, a.h, E16);
+      if (E16 > 16 && !wf64)
         hipLaunchKernelGGL(wsplit_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.W_gate, a.h, a.E,
                            E16, (bf16_t*)a.planes);
       // k split across waves needs h/KS to be a multiple of 32
@@ -522,7 +677,8 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
         // h = 1024).  More experts: 64 tokens per wave and a 4-way k split (the weight
         // planes, 4x larger, are then read half as often; 8 waves of 32 tokens measured
         // 94 -> 139 us at T = 4096, h = 4096, E = 256).  h / KS must be a multiple of 32.
-        if (E16 == 64 && a.h % 256 == 0 && a.T >= 1024) launch_logits_mfma<4, 1, 8, 2>(a, E16, st);
+        if (E16 == 64 && a.h % 256 == 0 && a.T >= 1024)
+          launch_logits_mfma<4, 1, 8, 2>(a, E16, st, 1, nullptr, wf64);
         else if (a.h % 128 == 0 && a.T >= 1024) launch_logits_mfma<4, 1, 4, 4>(a, E16, st);
         else launch_logits_mfma<4, 4>(a, E16, st);
       } else if (E16 % 32 == 0) {
@@ -573,14 +729,20 @@ hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
   } while (0)
 #define MOE_SELECT(NV, G, HS) MOE_SELECT_W(NV, G, HS, 4)
   if (SH > 1 && a.E > 16) return hipErrorInvalidValue;  // the h split is for few experts only
+  // four lanes per token (sixteen tokens per wave) up to 32 experts, then 16, 8 and 16
+  // lanes, one pass per wave
   if (a.E <= 4) { if (SH > 1) MOE_SELECT(1, 4, true); else MOE_SELECT(1, 4, false); }
-  else if (a.E <= 8) { if (SH > 1) MOE_SELECT(1, 8, true); else MOE_SELECT(1, 8, false); }
-  else if (a.E <= 16) { if (SH > 1) MOE_SELECT(1, 16, true); else MOE_SELECT(1, 16, false); }
-  else if (a.E <= 32) MOE_SELECT(1, 32, false);
-  // a whole wave per token: 16 waves, 4 tokens each, to keep enough selections in flight
-  else if (a.E <= 64) MOE_SELECT_W(1, 64, false, 16);
-  else if (a.E <= 128) MOE_SELECT_W(2, 64, false, 16);
-  else MOE_SELECT_W(4, 64, false, 16);
+  else if (a.E <= 8) { if (SH > 1) MOE_SELECT(2, 4, true); else MOE_SELECT(2, 4, false); }
+  else if (a.E <= 16) { if (SH > 1) MOE_SELECT(4, 4, true); else MOE_SELECT(4, 4, false); }
+  else if (a.E <= 32) MOE_SELECT(8, 4, false);
+  else if (a.E <= 64) {
+    // 16 lanes per token, 16 waves of 4 tokens (measured at T = 8192: 6.8 us with 4 lanes
+    // per token and 4 waves of 16 tokens, 4.7 us so)
+    MOE_SELECT_W(4, 16, false, 16);
+  }
+  else if (a.E <= 128) MOE_SELECT_W(16, 8, false, 8);
+  // (T = 4096, E = 256: 36 us with 4 waves of 4 passes, 18.6 us with 16 waves of one)
+  else MOE_SELECT_W(16, 16, false, 16);
 #undef MOE_SELECT
 #undef MOE_SELECT_W
 #undef MOE_SELECT_F
