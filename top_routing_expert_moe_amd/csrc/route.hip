@@ -64,6 +64,12 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
 // the bf16 pair (lo16 = upper half of a, hi16 = upper half of b) in one v_perm_b32
 __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
+// Row stride of the weight planes (elements): h + 32, so that consecutive expert rows start
+// 64 bytes apart modulo 128.  A wave's 16-row fragment loads then fall half in each 64-byte
+// half of their 128-byte lines instead of all in one (measured at T = 4096, h = 4096,
+// E = 256: the logits 79 -> 64 us; 16- or 128-byte shifts gave 70 and 79 us).
+__host__ __device__ __forceinline__ int plane_ld(int h) { return h + 32; }
+
 // ---------------------------------------------------------------------------
 // W_gate [h,E] fp32 -> planes [3][E16][h] bf16 with hi + mid + lo == W (to fp32 precision)
 __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W_gate, int h, int E, int E16,
@@ -71,13 +77,14 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)E16 * h) return;
   const int e = (int)(idx / h), i = (int)(idx % h);
+  const int64_t at = (int64_t)e * plane_ld(h) + i;
   const float w = e < E ? W_gate[(size_t)i * E + e] : 0.f;
   uint32_t hi, mid, lo;
   split3(w, hi, mid, lo);
-  const size_t plane = (size_t)E16 * h;
-  planes[idx] = (bf16_t)(hi >> 16);
-  planes[plane + idx] = (bf16_t)(mid >> 16);
-  planes[2 * plane + idx] = (bf16_t)(lo >> 16);
+  const size_t plane = (size_t)E16 * plane_ld(h);
+  planes[at] = (bf16_t)(hi >> 16);
+  planes[plane + at] = (bf16_t)(mid >> 16);
+  planes[2 * plane + at] = (bf16_t)(lo >> 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -102,7 +109,8 @@ struct LogitBatch {
   float w[WF32 ? UU : 1][WF32 ? NB : 1][8];
 };
 
-template <int NB, int TW, int NW, int TG = 1, bool WF32 = false>
+// EC > 0: E is EC (the fp32 weights' row stride then folds into the loads' offsets).
+template <int NB, int TW, int NW, int TG = 1, bool WF32 = false, int EC = 0>
 __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ planes,
                                                           const float* __restrict__ W_gate,
@@ -114,7 +122,8 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
   constexpr int FR = NB * TG;
   constexpr int UU = FR >= 4 ? 1 : (FR >= 2 ? 2 : (NW > 4 ? 2 : 4));
   using Batch = LogitBatch<UU, TG, NB, WF32>;
-  __shared__ floatx4 red[KS > 1 ? KS - 1 : 1][TW][TG][NB][64];
+  __shared__ floatx4 red[KS > 1 ? KS : 1][TW][TG][NB][64];
+  if (EC > 0) E = EC;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tw = wave % TW, ks = wave / TW;
@@ -144,18 +153,21 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
   for (int tg = 0; tg < TG; ++tg) {
     const int tok = t0 + 16 * tg + (lane & 15);
     tvalid[tg] = tok < T;
-    xrow[tg] = x + (size_t)(tvalid[tg] ? tok : 0) * h + 8 * (lane >> 4);
+    xrow[tg] = x + (size_t)(tvalid[tg] ? tok : 0) * h;
   }
-  const size_t plane = (size_t)E16 * h;
+  // lane group g = lane >> 4 takes k 8g .. 8g + 7 of each step of 32
+  const int goff = 8 * (lane >> 4);
+  auto step_k = [&](int st) { return kb + st * 32 + goff; };
+  const size_t plane = (size_t)E16 * plane_ld(h);
   const bf16_t* wrow[NB];
-  const float* wcol[NB];  // WF32: W_gate[8 * (lane >> 4)][e], clamped to expert E-1 past E (masked by wok)
+  const float* wcol[NB];  // WF32: W_gate[0][e], clamped to expert E-1 past E (masked by wok)
   bool wok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int e = e0 + nb * 16 + (lane & 15);
     wok[nb] = e < E;
-    if (WF32) wcol[nb] = W_gate + (size_t)(8 * (lane >> 4)) * E + min(e, E - 1);
-    else wrow[nb] = planes + (size_t)e * h + 8 * (lane >> 4);
+    if (WF32) wcol[nb] = W_gate + min(e, E - 1);
+    else wrow[nb] = planes + (size_t)e * plane_ld(h);
   }
 
   // few fragments per step: one accumulator per plane, so no MFMA waits on the one before
@@ -168,12 +180,13 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) accp[q][tg][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads of the batch at k0; every step's k is clamped into [kb, ke) so that all loads
-  // are unconditional (steps past ke re-read the last one and are not multiplied).
+  // Loads of the batch at k0; every step is clamped to the wave's last one so that all
+  // loads are unconditional (steps past ke re-read the last one and are not multiplied).
+  const int nsteps = kspan / 32;
   auto load = [&](int k0, Batch& b) {
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-      const int kk = min(k0 + 32 * u, ke - 32);
+      const int kk = step_k(min((k0 - kb) / 32 + u, nsteps - 1));  // this lane's first k
       // (xrow points at a valid row for every lane; the invalid tokens' results are not stored)
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) b.x[u][tg] = *(const bf16x8*)(xrow[tg] + kk);
@@ -253,33 +266,35 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
       for (int q = 1; q < PA; ++q) acc[tg][nb] += accp[q][tg][nb];
     }
   // lane holds token (lane & 15) of each group, experts 4*(lane>>4) + 0..3 of each 16-block
-  if (KS > 1) {
-    if (ks > 0) {
+  auto store = [&](int tg, int nb, const floatx4& v) {
+    const int tok = t0 + 16 * tg + (lane & 15);
+    if (tok >= T) return;
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) red[ks - 1][tw][tg][nb][lane] = acc[tg][nb];
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + nb * 16 + 4 * (lane >> 4) + r;
+      if (e < E) logits[(size_t)tok * E + e] = v[r] + (bias ? bias[e] : 0.f);
     }
-    __syncthreads();
-    if (ks > 0) return;
+  };
+  if constexpr (KS > 1) {
+    // every wave parks its partial sums; the TG*NB fragments of a token-wave are then
+    // shared out over its KS k-waves, each adding the KS parts of its own in k order
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) red[ks][tw][tg][nb][lane] = acc[tg][nb];
+    __syncthreads();
+    for (int q = ks; q < TG * NB; q += KS) {
+      const int tg = q / NB, nb = q - (q / NB) * NB;
+      floatx4 v = red[0][tw][tg][nb][lane];
 #pragma unroll
-        for (int s = 0; s < KS - 1; ++s) acc[tg][nb] += red[s][tw][tg][nb][lane];
-  }
+      for (int z = 1; z < KS; ++z) v += red[z][tw][tg][nb][lane];
+      store(tg, nb, v);
+    }
+  } else {
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg) {
-    if (!tvalid[tg]) continue;
-    const int tok = t0 + 16 * tg + (lane & 15);
+    for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = e0 + nb * 16 + 4 * (lane >> 4) + r;
-        if (e < E) logits[(size_t)tok * E + e] = acc[tg][nb][r] + (bias ? bias[e] : 0.f);
-      }
+      for (int nb = 0; nb < NB; ++nb) store(tg, nb, acc[tg][nb]);
   }
 }
 
@@ -593,18 +608,18 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
   prob_sum[e] = s;
 }
 
-template <int NB, int TW, int NW = 4, int TG = 1>
+template <int NB, int TW, int NW = 4, int TG = 1, int EC = 0>
 void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr,
                         bool wf32 = false) {
   const int gx = (a.T + 16 * TW * TG - 1) / (16 * TW * TG), gy = E16 / (16 * NB);
   // one expert group: gx x SH grid; several: a 1-D grid, XCD-aware (SH is then 1)
   const dim3 grid = gy > 1 ? dim3((unsigned)((gx * gy + 7) / 8 * 8)) : dim3(gx, 1, SH);
   if (wf32 || E16 <= 16)  // weights split in registers
-    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true>), grid, dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true, EC>), grid, dim3(NW * 64), 0, st,
                        (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx,
                        gy);
   else
-    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
+    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false, 0>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
                        (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx, gy);
 }
 
@@ -618,7 +633,7 @@ bool logits_wf32_e64(int T, int h, int E16) { return E16 == 64 && h % 256 == 0 &
 // the bf16 planes of the router weights (from 32 experts up; fewer are split in registers)
 int route_planes_elems(int h, int E) {
   const int E16 = (E + 15) / 16 * 16;
-  return E16 > 16 ? 3 * E16 * h : 0;
+  return E16 > 16 ? 3 * E16 * plane_ld(h) : 0;
 }
 
 int route_hsplit(int T, int h, int E, bool bf16) {
@@ -661,10 +676,13 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
                            E16, (bf16_t*)a.planes);
       // k split across waves needs h/KS to be a multiple of 32
       const int SH = route_hsplit(a.T, a.h, a.E, true);
-      if (SH > 1) {
+      if (SH > 1 && E16 <= 16) {
         launch_logits_mfma<1, 1>(a, E16, st, SH, route_lpart(a));
       } else if (E16 <= 16) {
-        if (a.h % 512 == 0) launch_logits_mfma<1, 1, 16>(a, E16, st);
+        if (a.h % 512 == 0) {
+          if (a.E == 8) launch_logits_mfma<1, 1, 16, 1, 8>(a, E16, st);
+          else launch_logits_mfma<1, 1, 16>(a, E16, st);
+        }
         else if (a.h % 128 == 0) launch_logits_mfma<1, 1>(a, E16, st);
         else launch_logits_mfma<1, 2>(a, E16, st);
       } else if (E16 == 32) {
@@ -678,7 +696,8 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
         // planes, 4x larger, are then read half as often; 8 waves of 32 tokens measured
         // 94 -> 139 us at T = 4096, h = 4096, E = 256).  h / KS must be a multiple of 32.
         if (E16 == 64 && a.h % 256 == 0 && a.T >= 1024)
-          launch_logits_mfma<4, 1, 8, 2>(a, E16, st, 1, nullptr, wf64);
+          if (a.E == 64) launch_logits_mfma<4, 1, 8, 2, 64>(a, E16, st, 1, nullptr, wf64);
+          else launch_logits_mfma<4, 1, 8, 2>(a, E16, st, 1, nullptr, wf64);
         else if (a.h % 128 == 0 && a.T >= 1024) launch_logits_mfma<4, 1, 4, 4>(a, E16, st);
         else launch_logits_mfma<4, 4>(a, E16, st);
       } else if (E16 % 32 == 0) {
