@@ -614,7 +614,8 @@ void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1,
   const int gx = (a.T + 16 * TW * TG - 1) / (16 * TW * TG), gy = E16 / (16 * NB);
   // one expert group: gx x SH grid; several: a 1-D grid, XCD-aware (SH is then 1)
   const dim3 grid = gy > 1 ? dim3((unsigned)((gx * gy + 7) / 8 * 8)) : dim3(gx, 1, SH);
-  if (wf32 || E16 <= 16)  // weights split in registers
+  if (wf32 || E16 <= 16)  // weights split in registers (planes at 16 experts measured 22.8 + 4.4 us
+                          // against 13.6 at T = 4096, h = 4096)
     hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true, EC>), grid, dim3(NW * 64), 0, st,
                        (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx,
                        gy);
