@@ -170,6 +170,35 @@ def test_layer_skewed_experts(T, h, f, E, k, cf, act, dtype):
         assert kept.max() >= 512       # the case this test is for
 
 
+@pytest.mark.parametrize("T,E,k,cf", [
+    (1024, 64, 2, 1.25),    # the fused scan + scatter: 16 blocks
+    (1500, 64, 4, 0.0),     # ... with a ragged last block (24 blocks, 28 tokens in the last)
+    (8256, 64, 2, 1.0),     # 129 blocks: the largest fused scan at 64 experts (64 blocks per thread)
+    (16448, 64, 1, 1.0),    # 257 blocks are too many for it: the separate scan and scatter kernels
+    (8256, 256, 1, 2.0),    # ... and 129 blocks of 256 experts too
+])
+def test_layer_many_tokens_routing_paths(T, E, k, cf):
+    """Many tokens, many experts: the fused scan + scatter up to the sizes whose histograms
+    one workgroup reads, the separate scan and scatter kernels past them.  Everything the
+    layer decides is bit-exact against the oracle, as for the other shapes."""
+    import math
+    h, f = 256, 256 if E == 64 else 128
+    _say(f"layer E={E} T={T} k={k} cf={cf}")
+    rng = np.random.default_rng(T + k)
+    conv = mw.f32_to_bf16_bits
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32),
+                logit_bias=(0.5 * rng.standard_normal(E)).astype(np.float32),
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)), W3=None,
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, "bf16" if kk in ("x", "W1", "W2") else "f32") for kk, v in host.items()
+          if v is not None}
+    dd["W3"] = None
+    w = mw.Workload("many-tokens", T=T, h=h, f=f, E=E, k=k, act="gelu", dtype="bf16", cf=cf)
+    y, aux, counts, logits, routing = _run_layer(w, host, dd)
+    _check_layer(w, host, y, aux, counts, logits, np.sort(rng.choice(T, 300, replace=False)), routing)
+
+
 def test_layer_forward_timed_matches_untimed():
     """The measurement entry point runs the same kernels: identical outputs, and the
     stage events are ordered and add up to the whole layer."""

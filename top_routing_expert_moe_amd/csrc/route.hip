@@ -88,6 +88,130 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
 }
 
 // ---------------------------------------------------------------------------
+// Lane exchanges and the per-token selection.
+
+// v from lane (lane ^ O): quad permutes for O = 1, 2; ds_swizzle (bit mode, xor mask O) up to
+// 16; every lane of the wave takes part
+template <int O>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "xor distance");
+  if constexpr (O == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  else if constexpr (O == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  else if constexpr (O < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (O << 10) | 0x1F);
+  else return (uint32_t)__shfl_xor((int)v, O, kWave);
+}
+template <int O>
+__device__ __forceinline__ float lane_xor_f(float v) { return __uint_as_float(lane_xor<O>(__float_as_uint(v))); }
+
+// reductions over the aligned groups of G lanes, exchanges at distance 1, 2, ..., G/2 (each
+// step combines the same two values on both lanes, so every lane ends with the same result)
+template <int G, int O = 1>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (O < G) return group_max<G, 2 * O>(fmaxf(v, lane_xor_f<O>(v)));
+  else return v;
+}
+template <int G, int O = 1>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (O < G) return group_sum<G, 2 * O>(v + lane_xor_f<O>(v));
+  else return v;
+}
+template <int G, int O = 1>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  if constexpr (O < G) {
+    const uint64_t o = ((uint64_t)lane_xor<O>((uint32_t)(v >> 32)) << 32) | lane_xor<O>((uint32_t)v);
+    return group_max_u64<G, 2 * O>(o > v ? o : v);
+  } else {
+    return v;
+  }
+}
+// sum over the lanes that share lane % G (the token groups of a wave), distances G .. 32
+template <int G, int O = G>
+__device__ __forceinline__ float across_groups_sum(float v) {
+  if constexpr (O < 64) return across_groups_sum<G, 2 * O>(v + lane_xor_f<O>(v));
+  else return v;
+}
+
+// The selection for one token t: the G lanes of the token (lane gl holding experts gl*NV ..
+// gl*NV + NV - 1 in v, -INF past E) compute the softmax sums and k rounds of the group
+// arg-max, and write the token's topk_idx and topk_w (t < T); cnt (LDS, or null) counts the
+// ids written, and psum gains the token's softmax (t < T).
+template <int NV, int G>
+__device__ __forceinline__ void select_token(const float (&v)[NV], int t, int T, int E, int k, int gl,
+                                             float inv_temp, int vflags, int* __restrict__ topk_idx,
+                                             float* __restrict__ topk_w, int* cnt, float (&psum)[NV]) {
+  constexpr int KR = (16 + G - 1) / G;  // selections a lane stores (k <= 16)
+  const int eb = gl * NV;
+  const bool tv = t < T;
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) m = fmaxf(m, v[i]);
+  m = group_max<G>(m);
+  float ex[NV], s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    ex[i] = eb + i < E ? expf((v[i] - m) * inv_temp) : 0.f;
+    s += ex[i];
+  }
+  s = group_sum<G>(s);
+  const float inv = 1.0f / s;
+  if (tv) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) psum[i] += ex[i] * inv;
+  }
+
+  bool taken[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) taken[i] = false;
+  float lmax = 0.f, wsum = 0.f;
+  float my_l[KR];
+  int my_e[KR];
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+    my_l[r] = 0.f;
+    my_e[r] = 0;
+  }
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = eb + i;
+      if (e < E && !taken[i]) {
+        const uint64_t key = ((uint64_t)ordered_bits(v[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+        best = key > best ? key : best;
+      }
+    }
+    best = group_max_u64<G>(best);
+    const int e_sel = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const float l_sel = from_ordered((uint32_t)(best >> 32));
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (eb + i == e_sel) taken[i] = true;
+    if (j == 0) lmax = l_sel;
+    wsum += expf((l_sel - lmax) * inv_temp);
+#pragma unroll
+    for (int r = 0; r < KR; ++r)
+      if (j == gl + G * r) {
+        my_l[r] = l_sel;
+        my_e[r] = e_sel;
+      }
+  }
+  if (tv) {
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int j = gl + G * r;
+      if (j < k) {
+        const int e_out = (vflags & 1) ? (int)(((int64_t)t * k + j) % E) : my_e[r];
+        topk_idx[(size_t)t * k + j] = e_out;
+        // lmax is the token's largest logit, m: the same value
+        const float ew = expf((my_l[r] - lmax) * inv_temp);
+        topk_w[(size_t)t * k + j] = (vflags & 2) ? ew * inv : ew / wsum;
+        if (cnt != nullptr) atomicAdd(&cnt[e_out], 1);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // logits for bf16 x on MFMA.  Workgroup = NW waves = TW token-waves x KS k-splits;
 // each wave: TG groups of 16 tokens x NB*16 experts over h/KS (the weight fragments
 // loaded for one k-step serve all TG token groups).  Few experts: 16 waves split h 16
@@ -360,10 +484,8 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// selection: 64 tokens per workgroup, 16 per wave.  A token is handled by a group of G
-// lanes (G = E rounded up to a power of two, at most 64; lane gl of the group holds
-// experts gl, gl + 64, ...), so a wave works on 64/G tokens at once.  All of a wave's
-// logits are loaded before any is used: the kernel costs one memory round trip.
+// selection: 64 tokens per workgroup of NWS waves.  All of a wave's logits are loaded
+// before any is used: the kernel costs one memory round trip.
 // With SH > 1 the logits arrive as SH partial sums (lpart[z][t][e]); they are added in
 // ascending z and the sums written to `logits`.
 // Router variants: `noise` [T,E] (or null) is added to the logits before anything else
@@ -379,47 +501,6 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // NV experts gl*NV .. gl*NV + NV - 1 (E <= G*NV), so the reductions over a token (max,
 // sum, arg-max) take log2(G) lane exchanges (DPP within quads, swizzles beyond).
 
-// v from lane (lane ^ O): quad permutes for O = 1, 2; ds_swizzle (bit mode, xor mask O) up to
-// 16; every lane of the wave takes part
-template <int O>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "xor distance");
-  if constexpr (O == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
-  else if constexpr (O == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
-  else if constexpr (O < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (O << 10) | 0x1F);
-  else return (uint32_t)__shfl_xor((int)v, O, kWave);
-}
-template <int O>
-__device__ __forceinline__ float lane_xor_f(float v) { return __uint_as_float(lane_xor<O>(__float_as_uint(v))); }
-
-// reductions over the aligned groups of G lanes, exchanges at distance 1, 2, ..., G/2 (each
-// step combines the same two values on both lanes, so every lane ends with the same result)
-template <int G, int O = 1>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (O < G) return group_max<G, 2 * O>(fmaxf(v, lane_xor_f<O>(v)));
-  else return v;
-}
-template <int G, int O = 1>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (O < G) return group_sum<G, 2 * O>(v + lane_xor_f<O>(v));
-  else return v;
-}
-template <int G, int O = 1>
-__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-  if constexpr (O < G) {
-    const uint64_t o = ((uint64_t)lane_xor<O>((uint32_t)(v >> 32)) << 32) | lane_xor<O>((uint32_t)v);
-    return group_max_u64<G, 2 * O>(o > v ? o : v);
-  } else {
-    return v;
-  }
-}
-// sum over the lanes that share lane % G (the token groups of a wave), distances G .. 32
-template <int G, int O = G>
-__device__ __forceinline__ float across_groups_sum(float v) {
-  if constexpr (O < 64) return across_groups_sum<G, 2 * O>(v + lane_xor_f<O>(v));
-  else return v;
-}
-
 template <int NV, int G, bool HSPLIT, int NWS = 4, bool FUSE = false>
 __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ logits, const float* __restrict__ lpart,
                                                      int SH, int T, int E, int k,
@@ -431,7 +512,6 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
   constexpr int TPW = 64 / G;                  // tokens per wave and pass
   constexpr int NQ = kSelTokens / NWS / TPW;   // passes per wave
   static_assert(NQ >= 1 && NWS * 64 >= 256, "tokens per wave; 256 threads for the histogram");
-  constexpr int KR = (16 + G - 1) / G;         // selections a lane stores (k <= 16)
   __shared__ float pp[NWS][256];
   __shared__ int cnt[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -497,77 +577,9 @@ __global__ __launch_bounds__(NWS * 64) void select_kernel(float* __restrict__ lo
   for (int i = 0; i < NV; ++i) psum[i] = 0.f;
 
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int t = t0 + q * TPW + sub;
-    const bool tv = t < T;
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) m = fmaxf(m, v[q][i]);
-    m = group_max<G>(m);
-    float ex[NV], s = 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      ex[i] = eb + i < E ? expf((v[q][i] - m) * inv_temp) : 0.f;
-      s += ex[i];
-    }
-    s = group_sum<G>(s);
-    const float inv = 1.0f / s;
-    if (tv) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) psum[i] += ex[i] * inv;
-    }
-
-    bool taken[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) taken[i] = false;
-    float lmax = 0.f, wsum = 0.f;
-    float my_l[KR];
-    int my_e[KR];
-#pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      my_l[r] = 0.f;
-      my_e[r] = 0;
-    }
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int e = eb + i;
-        if (e < E && !taken[i]) {
-          const uint64_t key = ((uint64_t)ordered_bits(v[q][i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-          best = key > best ? key : best;
-        }
-      }
-      best = group_max_u64<G>(best);
-      const int e_sel = (int)(0xFFFFFFFFu - (uint32_t)best);
-      const float l_sel = from_ordered((uint32_t)(best >> 32));
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (eb + i == e_sel) taken[i] = true;
-      if (j == 0) lmax = l_sel;
-      wsum += expf((l_sel - lmax) * inv_temp);
-#pragma unroll
-      for (int r = 0; r < KR; ++r)
-        if (j == gl + G * r) {
-          my_l[r] = l_sel;
-          my_e[r] = e_sel;
-        }
-    }
-    if (tv) {
-#pragma unroll
-      for (int r = 0; r < KR; ++r) {
-        const int j = gl + G * r;
-        if (j < k) {
-          const int e_out = (vflags & 1) ? (int)(((int64_t)t * k + j) % E) : my_e[r];
-          topk_idx[(size_t)t * k + j] = e_out;
-          // lmax is the token's largest logit, m: the same value
-          const float ew = expf((my_l[r] - lmax) * inv_temp);
-          topk_w[(size_t)t * k + j] = (vflags & 2) ? ew * inv : ew / wsum;
-          if (blk_counts != nullptr) atomicAdd(&cnt[e_out], 1);
-        }
-      }
-    }
-  }
+  for (int q = 0; q < NQ; ++q)
+    select_token<NV, G>(v[q], t0 + q * TPW + sub, T, E, k, gl, inv_temp, vflags, topk_idx, topk_w,
+                        blk_counts != nullptr ? cnt : nullptr, psum);
   // the token groups of a wave hold partial sums of the same experts: add them (fixed tree)
 #pragma unroll
   for (int i = 0; i < NV; ++i) psum[i] = across_groups_sum<G>(psum[i]);
@@ -620,15 +632,15 @@ void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1,
                        (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx,
                        gy);
   else
-    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false, 0>), grid, dim3(NW * 64), 0, st, (const bf16_t*)a.x,
-                       (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx, gy);
+    hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false, 0>), grid, dim3(NW * 64), 0, st,
+                       (const bf16_t*)a.x, (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16,
+                       out ? out : a.logits, gx, gy);
 }
 
 // 64 experts, many tokens: the kernel splits the fp32 weights itself (no planes kernel)
 // (measured at T = 8192, h = 1024: the logits 22.3 -> 17.8 us, and the 4.4 us planes kernel
 // is gone)
 bool logits_wf32_e64(int T, int h, int E16) { return E16 == 64 && h % 256 == 0 && T >= 1024; }
-
 }  // namespace
 
 // the bf16 planes of the router weights (from 32 experts up; fewer are split in registers)
