@@ -695,9 +695,11 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
         if (a.h % 512 == 0) {
           if (a.E == 8) launch_logits_mfma<1, 1, 16, 1, 8>(a, E16, st);
           else launch_logits_mfma<1, 1, 16>(a, E16, st);
+        } else if (a.h % 128 == 0) {
+          launch_logits_mfma<1, 1>(a, E16, st);
+        } else {
+          launch_logits_mfma<1, 2>(a, E16, st);
         }
-        else if (a.h % 128 == 0) launch_logits_mfma<1, 1>(a, E16, st);
-        else launch_logits_mfma<1, 2>(a, E16, st);
       } else if (E16 == 32) {
         if (a.h % 128 == 0) launch_logits_mfma<2, 1>(a, E16, st);
         else launch_logits_mfma<2, 2>(a, E16, st);
@@ -708,11 +710,14 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
         // h = 1024).  More experts: 64 tokens per wave and a 4-way k split (the weight
         // planes, 4x larger, are then read half as often; 8 waves of 32 tokens measured
         // 94 -> 139 us at T = 4096, h = 4096, E = 256).  h / KS must be a multiple of 32.
-        if (E16 == 64 && a.h % 256 == 0 && a.T >= 1024)
+        if (E16 == 64 && a.h % 256 == 0 && a.T >= 1024) {
           if (a.E == 64) launch_logits_mfma<4, 1, 8, 2, 64>(a, E16, st, 1, nullptr, wf64);
           else launch_logits_mfma<4, 1, 8, 2>(a, E16, st, 1, nullptr, wf64);
-        else if (a.h % 128 == 0 && a.T >= 1024) launch_logits_mfma<4, 1, 4, 4>(a, E16, st);
-        else launch_logits_mfma<4, 4>(a, E16, st);
+        } else if (a.h % 128 == 0 && a.T >= 1024) {
+          launch_logits_mfma<4, 1, 4, 4>(a, E16, st);
+        } else {
+          launch_logits_mfma<4, 4>(a, E16, st);
+        }
       } else if (E16 % 32 == 0) {
         launch_logits_mfma<2, 4>(a, E16, st);
       } else {
