@@ -37,6 +37,7 @@
 //    one XCD share activation and weight tiles in its L2.
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -67,24 +68,54 @@ __device__ __forceinline__ void store4(float* p, const float* v) { *(floatx4*)p 
 #endif
 constexpr int GM = MOE_GM, GN = MOE_GN;
 
-__device__ __forceinline__ void tile_of(int L, const int* __restrict__ tile_off, int E, int NT, int& e,
-                                        int& mt_local, int& nt) {
-  // expert: tile_off[e]*NT <= L < tile_off[e+1]*NT
-  int lo = 0, hi = E;
+// Reads of the tile list and the expert offsets: uniform addresses, loaded through the
+// constant address space so that they are scalar loads (the GEMM counts its vector-memory
+// operations by hand, and a vector load here would make the compiler wait for them all).
+__device__ __forceinline__ int ldc(const int* p, int i) {
+  return ((const __attribute__((address_space(4))) int*)p)[i];
+}
+
+struct TileInfo {
+  int e, ks, row0, rows, n0;
+};
+
+// The tile at position L of the launch's list: K part ks = L / n_tiles, then position Lt
+// in the tile list.  Expert e: tile_off[e] * NT <= Lt < tile_off[e + 1] * NT, searched from
+// e_from (an expert at or before it; 0 for none) -- a few steps forward, then bisection.
+// fh, big: the tile heights (m_tile_rows); NO: output columns per n-tile.
+__device__ __forceinline__ TileInfo tile_at(int L, const int* __restrict__ tile_off, const int* __restrict__ offsets,
+                                            int E, int NT, int n_tiles, bool split, int fh, int big, int NO,
+                                            int e_from) {
+  TileInfo t;
+  t.ks = split ? L / n_tiles : 0;
+  const int Lt = L - t.ks * n_tiles;
+  int lo = e_from, hi = E;  // tile_off[lo] * NT <= Lt < tile_off[hi] * NT
+  for (int st = 0; st < 4 && hi - lo > 1; ++st) {
+    if (ldc(tile_off, lo + 1) * NT <= Lt) ++lo;
+    else hi = lo + 1;
+  }
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (tile_off[mid] * NT <= L) lo = mid; else hi = mid;
+    if (ldc(tile_off, mid) * NT <= Lt) lo = mid; else hi = mid;
   }
-  e = lo;
-  const int me = tile_off[e + 1] - tile_off[e];
-  const int l = L - tile_off[e] * NT;
+  const int e = lo;
+  t.e = e;
+  const int t0 = ldc(tile_off, e);
+  const int me = ldc(tile_off, e + 1) - t0;
+  const int l = Lt - t0 * NT;
   const int mg = l / (GM * NT);
   const int gm = min(GM, me - mg * GM);
   const int r = l - mg * GM * NT;
   const int ng = r / (gm * GN);
   const int r2 = r - ng * gm * GN;
-  mt_local = mg * GM + r2 % gm;
-  nt = ng * GN + r2 / gm;
+  const int mt_local = mg * GM + r2 % gm;
+  const int nt = ng * GN + r2 / gm;
+  const int o0 = ldc(offsets, e), o1 = ldc(offsets, e + 1);
+  const int fe = m_tile_rows(o1 - o0, fh, big);  // this expert's tile height
+  t.row0 = o0 + mt_local * fe;
+  t.rows = min(fe, o1 - t.row0);
+  t.n0 = nt * NO;
+  return t;
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -160,17 +191,42 @@ __device__ __forceinline__ void copy_to_lds16(const void* gptr, uint32_t lds_blo
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_block) : "memory", "m0");
 }
 
+// The same for one 4-byte word per lane (lane l writes LDS bytes [4l, 4l+4) of the block).
+__device__ __forceinline__ void copy_to_lds4(const void* gptr, uint32_t lds_block) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_block) : "memory", "m0");
+}
+
 constexpr int kSmemBytes = 160 * 1024;  // LDS of the largest tile shape
+constexpr int kRowsBytes = kWaves * 256;  // per wave, 64 row indices of the next tile (see gemm_tile)
+
+// The tile a workgroup runs after this one, when it has the same shape: its first stages
+// can then be copied during this tile's last ones (ok), into the buffers it will read them
+// from.
+struct NextTile {
+  bool ok;
+  int e, row0, row_end, n0, ks;
+};
+// The activation copy offsets of a tile whose first stages a previous tile issued (its
+// gather indices were read then, so the tile itself issues no load it must wait for).
+struct XCarry {
+  uint32_t v[4];
+};
 
 // One tile of BMT rows (row0 .. row_end-1 of expert e) x BNT weight columns from n0, over
 // k in [ks * Kc, ks * Kc + Kc).  SPLIT: the raw fp32 accumulators go to K part ks of
 // `out` (row stride NW = 2N for SwiGLU, else N; parts R_max rows apart) and the
 // activation is applied when the parts are added.
+// pre: the copies of this tile's first NSW - 1 stages are already in flight (issued by the
+// previous tile of the workgroup).  nx: the next tile; returns whether its first stages
+// were issued here (then the next call gets pre = true).  That happens when the stage
+// buffers are one cycle (NSW == NSTAGE) that this tile's stage count fills exactly, so
+// the next tile's stage q lands in buffer q % NSW, where its own prologue would put it.
 template <int BMT, int ACT, bool GATHER, typename OT, bool SPLIT, int BNT = BN, typename CFG = TileCfg<BMT>>
-__device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__ A, const int* __restrict__ a_rows,
+__device__ __forceinline__ bool gemm_tile(char* smem, const bf16_t* __restrict__ A, const int* __restrict__ a_rows,
                                           const bf16_t* __restrict__ W, const bf16_t* __restrict__ W3, int K,
                                           int N, OT* __restrict__ out, int R_max, int e, int row0, int row_end,
-                                          int n0, int ks, int Kc, float* __restrict__ save) {
+                                          int n0, int ks, int Kc, float* __restrict__ save, bool pre,
+                                          const NextTile& nx, XCarry& carry) {
   static_assert(!SPLIT || std::is_same<OT, float>::value, "K-split parts are fp32");
   constexpr int NSTAGE = CFG::NSTAGE, NSW = CFG::NSW, SPREAD = CFG::SPREAD;
   static_assert(NSW == NSTAGE || (NSW == 3 && NSTAGE == 2), "stage counts");
@@ -187,11 +243,18 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   constexpr int XI = BMT / 8;                     // activation copies (1 KiB each) per stage
   constexpr int NIX = (XI + kWaves - 1) / kWaves; // ... per wave (waves past XI / NIX have none)
   static_assert(XI % NIX == 0, "activation copies");
-  static_assert((NSW * WSTT + NSTAGE * XST) * 2 <= kSmemBytes, "LDS");
+  constexpr int ROWS_OFF = (NSW * WSTT + NSTAGE * XST) * 2;  // LDS bytes: the next tile's row indices
+  static_assert(ROWS_OFF <= kSmemBytes && (NSW != NSTAGE || ROWS_OFF + kRowsBytes <= kSmemBytes), "LDS");
+  static_assert(NIX <= 4, "XCarry");
   bf16_t(*Ws)[WSTT] = reinterpret_cast<bf16_t(*)[WSTT]>(smem);
   bf16_t(*Xs)[XST] = reinterpret_cast<bf16_t(*)[XST]>(smem + NSW * WSTT * 2);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // An opaque copy of the thread index: the lane-dependent offsets below are then computed
+  // per tile instead of being hoisted out of a workgroup's tile loop, where the offsets of
+  // every tile shape would hold registers at once.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const bool has_x = XI % kWaves == 0 || NIX * uwave < XI;  // this wave copies activations
 
@@ -202,37 +265,55 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   // a valid neighbour instead (their results are never stored).
   // Weight columns: each wave's WTN LDS columns hold, for SwiGLU, WTN/2 columns of W1
   // followed by the same WTN/2 columns of W3.
+  auto plan_w = [&](int e_, int n0_, int ks_, const bf16_t* (&wsrc_)[NIWT]) {
+#pragma unroll
+    for (int i = 0; i < NIWT; ++i) {
+      const int r = RPI * (NIWT * wave + i) + lane / CPR;  // weight stage row (k)
+      const int c = (lane % CPR) ^ wswz(r);                // 16-byte chunk of 8 columns
+      int col;
+      const bf16_t* Wm;
+      if (ACT == ACT_SWIGLU) {
+        constexpr int CPW = WTN / 8;  // chunks per wave's columns
+        const int wg = c / CPW, cc = c % CPW;
+        col = n0_ + wg * (WTN / 2) + (cc % (CPW / 2)) * 8;
+        Wm = cc < CPW / 2 ? W : W3;
+      } else if (ACT == ACT_SWIGLU_SEP) {
+        // column n0 + 8c of [W1 | W3] (N a multiple of 8: no chunk straddles the two)
+        const int gc = n0_ + c * 8;
+        col = gc < N ? gc : gc - N;
+        Wm = gc < N ? W : W3;
+      } else {
+        col = n0_ + c * 8;
+        Wm = W;
+      }
+      wsrc_[i] = Wm + (size_t)e_ * K * N + (size_t)(ks_ * Kc + r) * N + min(col, N - 8);
+    }
+  };
+  // activation row xr of the stage (m) comes from source row src_row
+  auto x_off = [&](int i, int src_row, int ks_) -> uint32_t {
+    const int xr = 8 * (NIX * wave + i) + lane / XCH;
+    return (uint32_t)src_row * (uint32_t)K + (uint32_t)(ks_ * Kc) + (uint32_t)((((lane % XCH) ^ xswz(xr))) << 3);
+  };
   const bf16_t* wsrc[NIWT];
   uint32_t xsrc[NIX];
-#pragma unroll
-  for (int i = 0; i < NIWT; ++i) {
-    const int r = RPI * (NIWT * wave + i) + lane / CPR;  // weight stage row (k)
-    const int c = (lane % CPR) ^ wswz(r);                // 16-byte chunk of 8 columns
-    int col;
-    const bf16_t* Wm;
-    if (ACT == ACT_SWIGLU) {
-      constexpr int CPW = WTN / 8;  // chunks per wave's columns
-      const int wg = c / CPW, cc = c % CPW;
-      col = n0 + wg * (WTN / 2) + (cc % (CPW / 2)) * 8;
-      Wm = cc < CPW / 2 ? W : W3;
-    } else if (ACT == ACT_SWIGLU_SEP) {
-      // column n0 + 8c of [W1 | W3] (N a multiple of 8: no chunk straddles the two)
-      const int gc = n0 + c * 8;
-      col = gc < N ? gc : gc - N;
-      Wm = gc < N ? W : W3;
-    } else {
-      col = n0 + c * 8;
-      Wm = W;
-    }
-    wsrc[i] = Wm + (size_t)e * K * N + (size_t)(ks * Kc + r) * N + min(col, N - 8);
-  }
+  const bf16_t* wsrc_n[NIWT];  // the next tile's (see below)
+  uint32_t xsrc_n[NIX];
+  plan_w(e, n0, ks, wsrc);
 #pragma unroll
   for (int i = 0; i < NIX; ++i) {
-    const int xr = 8 * (NIX * wave + i) + lane / XCH;  // activation stage row (m)
-    const int rr = min(row0 + xr, row_end - 1);
-    const int src_row = GATHER ? a_rows[rr] : rr;
-    xsrc[i] = (uint32_t)src_row * (uint32_t)K + (uint32_t)(ks * Kc) + (uint32_t)((((lane % XCH) ^ xswz(xr))) << 3);
+    if (pre) {
+      xsrc[i] = carry.v[i];
+    } else {
+      const int rr = min(row0 + 8 * (NIX * wave + i) + lane / XCH, row_end - 1);
+      xsrc[i] = x_off(i, GATHER ? a_rows[rr] : rr, ks);
+    }
   }
+  // The next tile's first NSW - 1 stages follow this tile's last ones in the same buffers
+  // (one cycle of NSW buffers, a whole number of cycles per tile).  At least 2 NSW stages:
+  // then the gather indices copied below have landed when the next tile's copies start.
+  const int nk = Kc / KB;
+  const bool cont = NSW == NSTAGE && nx.ok && nk % NSW == 0 && nk >= 2 * NSW;
+  const uint32_t rows_lds = (uint32_t)(uintptr_t)(lds_void_t*)(smem + ROWS_OFF) + 256u * (uint32_t)uwave;
   const uint32_t ws_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Ws[0][0];
   const uint32_t xs_lds = (uint32_t)(uintptr_t)(lds_void_t*)&Xs[0][0];
   // The copies that belong to MFMA group `part` of `parts` (parts == 1: all of them):
@@ -242,17 +323,19 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   // with a deeper weight pipeline the activation copies (needed first) take the first
   // sp/2 groups and the weight copies the next sp.
   // (ALL: both stages are known to exist, no checks)
-  auto issue_part = [&](int xkt, int xst, int wkt, int wst, int part, int parts, bool all = false) {
+  // (nxp: the stages xkt / wkt are the next tile's)
+  auto issue_part = [&](int xkt, int xst, int wkt, int wst, int part, int parts, bool all = false, bool nxp = false) {
     const int sp = parts < SPREAD ? parts : (SPREAD > 0 ? SPREAD : 1);
     const bool split = NSW != NSTAGE && parts > 1;
 #pragma unroll
     for (int i = 0; i < NIX; ++i)
       if ((all || xkt >= 0) && has_x && (split ? i * (sp / 2) / NIX : i * sp / NIX) == part)
-        copy_to_lds16(A + xsrc[i] + xkt * KB, xs_lds + 2u * (uint32_t)(xst * XST + 8 * (NIX * uwave + i) * KB));
+        copy_to_lds16(A + (nxp ? xsrc_n[i] : xsrc[i]) + xkt * KB,
+                      xs_lds + 2u * (uint32_t)(xst * XST + 8 * (NIX * uwave + i) * KB));
 #pragma unroll
     for (int i = 0; i < NIWT; ++i)
       if ((all || wkt >= 0) && (split ? sp / 2 + i * sp / NIWT : i * sp / NIWT) == part)
-        copy_to_lds16(wsrc[i] + (size_t)wkt * KB * N,
+        copy_to_lds16((nxp ? wsrc_n[i] : wsrc[i]) + (size_t)wkt * KB * N,
                       ws_lds + 2u * (uint32_t)(wst * WSTT + RPI * (NIWT * uwave + i) * BNT));
   };
 
@@ -295,7 +378,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   // MFMAs of stage kt; the copies of later stages (see issue_part) are issued in
   // between, one share after each group of JB MFMAs.
   // (xkt, xnb) / (wkt, wnb): the stage whose copies are issued, and its buffer
-  auto compute = [&](int xbuf, int wbuf, int xkt, int xnb, int wkt, int wnb, bool all) {
+  auto compute = [&](int xbuf, int wbuf, int xkt, int xnb, int wkt, int wnb, bool all, bool nxp = false) {
     const bf16_t* Wb = Ws[wbuf];
     const bf16_t* Xb = Xs[xbuf];
     constexpr int PARTS = (KB / 16) * IB;
@@ -306,7 +389,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
                                       : (NIWT - 1) * SP / NIWT < PARTS && (NIX - 1) * SP / NIX < PARTS),
                   "copy groups");
     const bool mf = NCW == kWaves || uwave < NCW;  // waves past the grid only copy
-    if (SPREAD == 0) issue_part(xkt, xnb, wkt, wnb, 0, 1, all);  // all copies before the first LDS read
+    if (SPREAD == 0) issue_part(xkt, xnb, wkt, wnb, 0, 1, all, nxp);  // all copies before the first LDS read
 #pragma unroll
     for (int kh = 0; kh < KB / 16; ++kh) {
       bf16x8 a[IB], b[JB];
@@ -327,7 +410,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
           for (int jb = 0; jb < JB; ++jb)
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib], b[jb], acc[ib][jb], 0, 0, 0);
         }
-        if (SPREAD > 0) issue_part(xkt, xnb, wkt, wnb, kh * IB + ib, PARTS, all);
+        if (SPREAD > 0) issue_part(xkt, xnb, wkt, wnb, kh * IB + ib, PARTS, all, nxp);
       }
     }
   };
@@ -337,34 +420,73 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
   // stage kt + NSW - 1 are copied, into the buffers that the barrier of step kt has
   // released.  Each thread waits for its own copies of stage kt -- newer copies, issued
   // after them, may stay in flight -- then the barrier makes every thread's copies visible.
-  const int nk = Kc / KB;
+  if (!pre) {
 #pragma unroll
-  for (int p = 0; p < NSW - 1; ++p)
-    if (p < nk) issue_part(p < NSTAGE - 1 ? p : -1, p, p, p, 0, 1);
+    for (int p = 0; p < NSW - 1; ++p)
+      if (p < nk) issue_part(p < NSTAGE - 1 ? p : -1, p, p, p, 0, 1);
+  }
+  // the next tile's gather indices: lane l copies row index 8 NIX uwave + min(l, 8 NIX - 1)
+  // of the next tile (clamped to its last row) into this wave's 256 LDS bytes
+  if (GATHER && cont && has_x) {
+    const int rr = min(nx.row0 + 8 * NIX * uwave + min(lane, 8 * NIX - 1), nx.row_end - 1);
+    copy_to_lds4(a_rows + rr, rows_lds);
+  }
   // Steady state: U = lcm(NSTAGE, NSW) stages per iteration, so every buffer index is a
   // constant, and every copy of these stages exists.
   constexpr int U = NSW == NSTAGE ? NSW : NSW * NSTAGE;
+  // stage kt's copies have landed when at most the newer stages' copies are in flight
+  auto wait_steady = [&]() {
+    if (NSW == NSTAGE) {
+      if (NSTAGE >= 4) {
+        if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIWT + NIX)) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIWT) : "memory");
+      } else if (NSTAGE == 3) {
+        if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT + NIX) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    } else {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
+    }
+  };
   int kt = 0;
   for (; kt + U + NSW - 2 < nk; kt += U) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      if (NSW == NSTAGE) {
-        if (NSTAGE >= 4) {
-          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NIWT + NIX)) : "memory");
-          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NIWT) : "memory");
-        } else if (NSTAGE == 3) {
-          if (has_x) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT + NIX) : "memory");
-          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
-        } else {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-      } else {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIWT) : "memory");
-      }
+      wait_steady();
       __syncthreads();
       compute(j % NSTAGE, j % NSW, kt + j + NSTAGE - 1, (j + NSTAGE - 1) % NSTAGE, kt + j + NSW - 1,
               (j + NSW - 1) % NSW, true);
     }
+  }
+  if (NSW == NSTAGE && cont) {
+    // The last NSW stages (kt = nk - NSW + j, buffer j): the first issues this tile's last
+    // stage, the others the next tile's stages 0 .. NSW - 2, into buffers 0 .. NSW - 2.
+    // The wait stays the steady one: NSW - 2 stages, of either tile, stay in flight.
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+      wait_steady();
+      __syncthreads();
+      if (j == 0) {
+        compute(0, 0, nk - 1, NSW - 1, nk - 1, NSW - 1, true);
+      } else {
+        if (j == 1) {
+          plan_w(nx.e, nx.n0, nx.ks, wsrc_n);
+          const int* rw = reinterpret_cast<const int*>(smem + ROWS_OFF + 256 * uwave);
+#pragma unroll
+          for (int i = 0; i < NIX; ++i) {
+            int src;
+            if (GATHER) src = rw[8 * i + lane / XCH];
+            else src = min(nx.row0 + 8 * (NIX * wave + i) + lane / XCH, nx.row_end - 1);
+            xsrc_n[i] = x_off(i, src, nx.ks);
+            carry.v[i] = xsrc_n[i];
+          }
+        }
+        compute(j, j, j - 1, j - 1, j - 1, j - 1, true, true);
+      }
+    }
+    kt = nk;
   }
   // the remaining stages (the pipeline drains)
   for (; kt < nk; ++kt) {
@@ -394,7 +516,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
 
   // ---- epilogue: lane holds token row 32*jb + (lane & 31) and, for acc element
   // 4q+p, weight column 32*ib + 8q + 4*(lane >> 5) + p of its wave's columns.
-  if (NCW < kWaves && uwave >= NCW) return;
+  if (NCW < kWaves && uwave >= NCW) return cont;
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb) {
     const int r = row0 + wm * WTM + jb * 32 + l31;
@@ -469,6 +591,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, const bf16_t* __restrict__
         }
     }
   }
+  return cont;
 }
 
 // The grouped GEMM over all experts in one launch.  The tile list (device-side
@@ -484,37 +607,48 @@ gemm_bf16_kernel(
     const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, int big, float* __restrict__ save) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
-  // ---- tile schedule (XCD-aware), exits for surplus workgroups
-  const int MT = tile_off[E];
-  const int n_tiles = MT * NT;
+  // ---- tile schedule (XCD-aware): XCD x takes list positions [x per, x per + per); its
+  // workgroups take every nslot-th of them
+  const int n_tiles = ldc(tile_off, E) * NT;
   const int n_real = n_tiles * (SPLIT ? S : 1);
   const int per = (n_real + 7) >> 3;
+  const int nslot = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  if (slot >= per) return;
-  const int L = xcd * per + slot;
-  if (L >= n_real) return;
-  int e, mt_local, nt;
-  int ks = 0;  // K part
-  int Lt = L;
-  if (SPLIT) {
-    ks = L / n_tiles;
-    Lt = L - ks * n_tiles;
+  const int Lend = min((xcd + 1) * per, n_real);
+  int L = xcd * per + slot;
+  if (L >= Lend) return;
+  const int Kc = SPLIT ? K / S : K;  // each tile's k range: [ks * Kc, ks * Kc + Kc)
+  // the tile's code path is chosen by the rows it really has
+  auto shape = [](int rows) { return rows > 128 ? 2 : (rows > 32 ? 1 : 0); };
+  TileInfo cur = tile_at(L, tile_off, offsets, E, NT, n_tiles, SPLIT, fh, big, NO, 0);
+  bool pre = false, first = true;
+  XCarry carry;
+  for (;;) {
+    const int Ln = L + nslot;
+    const bool more = Ln < Lend;
+    TileInfo nxt = cur;
+    if (more) {
+      const bool same_part = !SPLIT || Ln / n_tiles == cur.ks;  // list positions only grow inside a part
+      nxt = tile_at(Ln, tile_off, offsets, E, NT, n_tiles, SPLIT, fh, big, NO, same_part ? cur.e : 0);
+    }
+    const int sh = shape(cur.rows);
+    const NextTile nx{more && shape(nxt.rows) == sh, nxt.e, nxt.row0, nxt.row0 + nxt.rows, nxt.n0, nxt.ks};
+    // a tile that starts its own copies waits until every wave is done with the buffers
+    if (!pre && !first) __syncthreads();
+    if (sh == 2)
+      pre = gemm_tile<256, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, cur.e, cur.row0,
+                                                   cur.row0 + cur.rows, cur.n0, cur.ks, Kc, save, pre, nx, carry);
+    else if (sh == 1)
+      pre = gemm_tile<128, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, cur.e, cur.row0,
+                                                   cur.row0 + cur.rows, cur.n0, cur.ks, Kc, save, pre, nx, carry);
+    else
+      pre = gemm_tile<32, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, cur.e, cur.row0,
+                                                  cur.row0 + cur.rows, cur.n0, cur.ks, Kc, save, pre, nx, carry);
+    if (!more) break;
+    first = false;
+    L = Ln;
+    cur = nxt;
   }
-  tile_of(Lt, tile_off, E, NT, e, mt_local, nt);
-  const int Kc = SPLIT ? K / S : K;  // this workgroup's k range: [ks * Kc, ks * Kc + Kc)
-  const int fe = m_tile_rows(offsets[e + 1] - offsets[e], fh, big);  // this expert's tile height
-  const int row0 = offsets[e] + mt_local * fe;
-  const int rows = min(fe, offsets[e + 1] - row0);
-  const int n0 = nt * NO;
-  if (rows > 128)
-    gemm_tile<256, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc,
-                                           save);
-  else if (rows > 32)
-    gemm_tile<128, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc,
-                                           save);
-  else
-    gemm_tile<32, ACT, GATHER, OT, SPLIT>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows, n0, ks, Kc,
-                                          save);
 }
 
 // The same grouped GEMM when every m-tile has at most 32 rows (fh = 32): wide tiles.
@@ -528,34 +662,47 @@ gemm_bf16_wide_kernel(
   // its separated raw form): copies after the barrier and launch order
   constexpr bool KP = SPLIT && ACT != ACT_SWIGLU_SEP;
   using CFG = TileCfgWide32<KP>;
-  constexpr int LDS = (CFG::NSW * KB * BNW + CFG::NSTAGE * 32 * KB) * 2;
+  constexpr int LDS = (CFG::NSW * KB * BNW + CFG::NSTAGE * 32 * KB) * 2 + kRowsBytes;
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   constexpr int NO = ACT == ACT_SWIGLU ? BNW / 2 : BNW;  // output columns per tile
-  const int MT = tile_off[E];
-  const int n_tiles = MT * NT;
+  const int n_tiles = ldc(tile_off, E) * NT;
   const int n_real = n_tiles * (SPLIT ? S : 1);
-  int L = blockIdx.x;
+  int L, Lend, step;
   if (KP) {
     const int per = (n_real + 7) >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    if (slot >= per) return;
     L = xcd * per + slot;
+    Lend = min((xcd + 1) * per, n_real);
+    step = gridDim.x >> 3;
+  } else {
+    L = blockIdx.x;
+    Lend = n_real;
+    step = gridDim.x;
   }
-  if (L >= n_real) return;
-  int e, mt_local, nt;
-  int ks = 0;
-  int Lt = L;
-  if (SPLIT) {
-    ks = L / n_tiles;
-    Lt = L - ks * n_tiles;
-  }
-  tile_of(Lt, tile_off, E, NT, e, mt_local, nt);
+  if (L >= Lend) return;
   const int Kc = SPLIT ? K / S : K;
-  const int fe = m_tile_rows(offsets[e + 1] - offsets[e], fh, big);  // 32 here: fh is 32
-  const int row0 = offsets[e] + mt_local * fe;
-  const int rows = min(fe, offsets[e + 1] - row0);
-  gemm_tile<32, ACT, GATHER, OT, SPLIT, BNW, CFG>(smem, A, a_rows, W, W3, K, N, out, R_max, e, row0, row0 + rows,
-                                                  nt * NO, ks, Kc, save);
+  // fh is 32 here: every tile is 32 rows
+  TileInfo cur = tile_at(L, tile_off, offsets, E, NT, n_tiles, SPLIT, fh, big, NO, 0);
+  bool pre = false, first = true;
+  XCarry carry;
+  for (;;) {
+    const int Ln = L + step;
+    const bool more = Ln < Lend;
+    TileInfo nxt = cur;
+    if (more) {
+      const bool same_part = !SPLIT || Ln / n_tiles == cur.ks;
+      nxt = tile_at(Ln, tile_off, offsets, E, NT, n_tiles, SPLIT, fh, big, NO, same_part ? cur.e : 0);
+    }
+    const NextTile nx{more, nxt.e, nxt.row0, nxt.row0 + nxt.rows, nxt.n0, nxt.ks};
+    if (!pre && !first) __syncthreads();
+    pre = gemm_tile<32, ACT, GATHER, OT, SPLIT, BNW, CFG>(smem, A, a_rows, W, W3, K, N, out, R_max, cur.e, cur.row0,
+                                                          cur.row0 + cur.rows, cur.n0, cur.ks, Kc, save, pre, nx,
+                                                          carry);
+    if (!more) break;
+    first = false;
+    L = Ln;
+    cur = nxt;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -644,6 +791,33 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   }
 }
 
+// Workgroups of a bf16 GEMM launch.  By default one per tile slot, and the hardware hands
+// tiles to CUs as they free up.  Launches of short tiles (a contraction of at most
+// kPersistStages LDS stages per tile) instead start only as many workgroups as run at once
+// (one per CU: each takes most of its LDS), rounded up to a multiple of 8 for the XCD-aware
+// order; each runs its share of the tile list in turn and copies a tile's first stages
+// during the previous tile's last ones.  (Measured at T = 8192, h = 1024, f = 4096,
+// E = 64, k = 2, capacity 320: the up projection, 16 stages per tile, 143.5 -> 137.9 us;
+// with 64 stages per tile -- T = 4096, h = 4096, f = 2048, E = 256, k = 8 -- the fixed
+// schedule was slower than the hardware's, 1816 -> 1926 us, and it gained nothing on
+// 256-row tiles.)  MOE_GEMM_WORKGROUPS (environment) sets the count for every launch;
+// the results do not depend on it.
+constexpr int kPersistStages = 16;
+long long gemm_workgroups(long long slots, int stages) {
+  if (const char* v = getenv("MOE_GEMM_WORKGROUPS")) {
+    const long n = strtol(v, nullptr, 10);
+    if (n > 0 && n <= (1L << 20)) return std::min(slots, (long long)(n + 7) / 8 * 8);
+  }
+  if (stages > kPersistStages) return slots;
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 256;
+    return n > 0 ? n : 256;
+  }();
+  return std::min(slots, (long long)(cus + 7) / 8 * 8);
+}
+
 template <int ACT, bool G, typename OT, bool SPLIT>
 hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   const bool wide = a.bm == 32;
@@ -651,7 +825,7 @@ hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   const int NT = ((ACT == ACT_SWIGLU_SEP ? 2 * a.N : a.N) + NO - 1) / NO;
   const int S = SPLIT ? std::max(a.ksplit, 1) : 1;
   const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
-  const long long grid = (slots + 7) / 8 * 8;
+  const long long grid = gemm_workgroups((slots + 7) / 8 * 8, a.K / S / KB);
   if (grid <= 0) return hipSuccess;
   float* save = SPLIT ? nullptr : a.save;
   if (wide)
