@@ -34,10 +34,7 @@
 //  * XCD-aware order: hardware workgroup i runs on XCD i%8; each XCD takes a
 //    contiguous range of the tile list, which is ordered in 4 x 8 groups of
 //    (m-tile, n-tile) inside each expert, so the workgroups running together in
-//    one XCD share activation and weight tiles in its L2;
-//  * launches of short tiles (at most 16 stages of k) start one workgroup per CU,
-//    and each workgroup runs its share of the tile list in turn, copying the next
-//    tile's first stages during the current tile's last ones.
+//    one XCD share activation and weight tiles in its L2.
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
