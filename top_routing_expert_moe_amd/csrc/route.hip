@@ -621,8 +621,11 @@ __global__ void reduce_prob_kernel(const float* __restrict__ prob_part, int nblk
 }
 
 template <int NB, int TW, int NW = 4, int TG = 1, int EC = 0>
-void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr,
-                        bool wf32 = false) {
+hipError_t launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1, float* out = nullptr,
+                              bool wf32 = false) {
+  // every wave's share of the contraction is whole steps of 32 (else a wave would read
+  // before its range)
+  if (a.h % (32 * (NW / TW) * SH) != 0) return hipErrorInvalidValue;
   const int gx = (a.T + 16 * TW * TG - 1) / (16 * TW * TG), gy = E16 / (16 * NB);
   // one expert group: gx x SH grid; several: a 1-D grid, XCD-aware (SH is then 1)
   const dim3 grid = gy > 1 ? dim3((unsigned)((gx * gy + 7) / 8 * 8)) : dim3(gx, 1, SH);
@@ -635,6 +638,7 @@ void launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int SH = 1,
     hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false, 0>), grid, dim3(NW * 64), 0, st,
                        (const bf16_t*)a.x, (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16,
                        out ? out : a.logits, gx, gy);
+  return hipSuccess;
 }
 
 // 64 experts, many tokens: the kernel splits the fp32 weights itself (no planes kernel)
@@ -679,6 +683,7 @@ float* route_lpart(const RouteArgs& a) {
 int route_blocks(int T) { return (T + kSelTokens - 1) / kSelTokens; }
 
 hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
+  hipError_t err = hipSuccess;
   {
     if (a.bf16) {
       const int E16 = (a.E + 15) / 16 * 16;
@@ -690,19 +695,19 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
       // k split across waves needs h/KS to be a multiple of 32
       const int SH = route_hsplit(a.T, a.h, a.E, true);
       if (SH > 1 && E16 <= 16) {
-        launch_logits_mfma<1, 1>(a, E16, st, SH, route_lpart(a));
+        err = launch_logits_mfma<1, 1>(a, E16, st, SH, route_lpart(a));
       } else if (E16 <= 16) {
         if (a.h % 512 == 0) {
-          if (a.E == 8) launch_logits_mfma<1, 1, 16, 1, 8>(a, E16, st);
-          else launch_logits_mfma<1, 1, 16>(a, E16, st);
+          if (a.E == 8) err = launch_logits_mfma<1, 1, 16, 1, 8>(a, E16, st);
+          else err = launch_logits_mfma<1, 1, 16>(a, E16, st);
         } else if (a.h % 128 == 0) {
-          launch_logits_mfma<1, 1>(a, E16, st);
+          err = launch_logits_mfma<1, 1>(a, E16, st);
         } else {
-          launch_logits_mfma<1, 2>(a, E16, st);
+          err = launch_logits_mfma<1, 2>(a, E16, st);
         }
       } else if (E16 == 32) {
-        if (a.h % 128 == 0) launch_logits_mfma<2, 1>(a, E16, st);
-        else launch_logits_mfma<2, 2>(a, E16, st);
+        if (a.h % 128 == 0) err = launch_logits_mfma<2, 1>(a, E16, st);
+        else err = launch_logits_mfma<2, 2>(a, E16, st);
       } else if (E16 % 64 == 0) {
         // Many tokens: each wave takes several 16-token groups, so the router weights are
         // read once per group of groups.  64 experts: 32 tokens per wave and an 8-way k
@@ -710,18 +715,21 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
         // h = 1024).  More experts: 64 tokens per wave and a 4-way k split (the weight
         // planes, 4x larger, are then read half as often; 8 waves of 32 tokens measured
         // 94 -> 139 us at T = 4096, h = 4096, E = 256).  h / KS must be a multiple of 32.
+        // (At T = 8192, h = 1024, E = 64 the eight waves of 32 tokens took 14.5 us; 16 waves
+        // of 16 tokens 29.8, 32 experts per workgroup 15.6, 64 tokens per workgroup 19.6,
+        // 16 tokens per workgroup 20.7, four waves 15.1.)
         if (E16 == 64 && a.h % 256 == 0 && a.T >= 1024) {
-          if (a.E == 64) launch_logits_mfma<4, 1, 8, 2, 64>(a, E16, st, 1, nullptr, wf64);
-          else launch_logits_mfma<4, 1, 8, 2>(a, E16, st, 1, nullptr, wf64);
+          if (a.E == 64) err = launch_logits_mfma<4, 1, 8, 2, 64>(a, E16, st, 1, nullptr, wf64);
+          else err = launch_logits_mfma<4, 1, 8, 2>(a, E16, st, 1, nullptr, wf64);
         } else if (a.h % 128 == 0 && a.T >= 1024) {
-          launch_logits_mfma<4, 1, 4, 4>(a, E16, st);
+          err = launch_logits_mfma<4, 1, 4, 4>(a, E16, st);
         } else {
-          launch_logits_mfma<4, 4>(a, E16, st);
+          err = launch_logits_mfma<4, 4>(a, E16, st);
         }
       } else if (E16 % 32 == 0) {
-        launch_logits_mfma<2, 4>(a, E16, st);
+        err = launch_logits_mfma<2, 4>(a, E16, st);
       } else {
-        launch_logits_mfma<1, 4>(a, E16, st);
+        err = launch_logits_mfma<1, 4>(a, E16, st);
       }
     } else {
       const dim3 grid((a.T + 31) / 32);
@@ -744,6 +752,7 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
 #undef MOE_LOGITS_F32
     }
   }
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 
