@@ -61,6 +61,8 @@ def _rand(shape, scale, rng, dtype):
     ("swiglu", 4, 1024, 2048, [5, 20, 0, 9]),                      # 32-row tiles, K parts
     ("gelu", 3, 2048, 1024, [12, 3, 30]),                          # K parts in both projections
     ("swiglu", 4, 2048, 768, [200, 129, 0, 60]),                   # h >= 2048: 256-row tiles from 129 rows
+    ("gelu", 4, 384, 768, [100, 90, 120, 70]),                     # 128-row tiles, stage counts 6 and 12:
+                                                                   # multiples of their three buffers
 ])
 @pytest.mark.parametrize("wgs", [8, 24])
 def test_expert_ffn_schedule_invariant(act, E, h, f, seg, wgs):
@@ -99,6 +101,8 @@ def test_expert_ffn_schedule_invariant(act, E, h, f, seg, wgs):
     (2000, 192, 320, 16, 2, 0.0, "gelu"),     # N tails, mixed tile heights
     (3000, 128, 256, 64, 2, 1.25, "gelu"),    # many experts, capacity drops
     (40, 1024, 2048, 8, 2, 0.0, "swiglu"),    # wide tiles, K parts
+    (1600, 384, 768, 16, 1, 0.0, "swiglu"),   # gathered 128-row tiles whose stage count (6) fills
+                                              # the three buffers: handed over with their row indices
 ])
 def test_layer_schedule_invariant(T, h, f, E, k, cf, act):
     torch = gu.torch()
