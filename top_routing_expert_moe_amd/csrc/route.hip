@@ -140,6 +140,7 @@ __device__ __forceinline__ void select_token(const float (&v)[NV], int t, int T,
                                              float inv_temp, int vflags, int* __restrict__ topk_idx,
                                              float* __restrict__ topk_w, int* cnt, float (&psum)[NV]) {
   constexpr int KR = (16 + G - 1) / G;  // selections a lane stores (k <= 16)
+  static_assert((NV & (NV - 1)) == 0, "experts per lane: a power of two");
   const int eb = gl * NV;
   const bool tv = t < T;
   float m = -INFINITY;
@@ -159,9 +160,13 @@ __device__ __forceinline__ void select_token(const float (&v)[NV], int t, int T,
     for (int i = 0; i < NV; ++i) psum[i] += ex[i] * inv;
   }
 
-  bool taken[NV];
+  // The 64-bit keys (ordered logit bits, then ~e): unique, and the larger is selected first.
+  // 0 stands for an expert past E and, once it is selected, for that expert (every real
+  // key is above 0).  Built once; each round takes the largest and clears it.
+  uint64_t key[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) taken[i] = false;
+  for (int i = 0; i < NV; ++i)
+    key[i] = eb + i < E ? ((uint64_t)ordered_bits(v[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(eb + i)) : 0;
   float lmax = 0.f, wsum = 0.f;
   float my_l[KR];
   int my_e[KR];
@@ -171,21 +176,20 @@ __device__ __forceinline__ void select_token(const float (&v)[NV], int t, int T,
     my_e[r] = 0;
   }
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    // the lane's largest key, as a tree (independent compares)
+    uint64_t mx[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = eb + i;
-      if (e < E && !taken[i]) {
-        const uint64_t key = ((uint64_t)ordered_bits(v[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-        best = key > best ? key : best;
-      }
-    }
-    best = group_max_u64<G>(best);
+    for (int i = 0; i < NV; ++i) mx[i] = key[i];
+#pragma unroll
+    for (int w = NV / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) mx[i] = mx[i + w] > mx[i] ? mx[i + w] : mx[i];
+    const uint64_t best = group_max_u64<G>(mx[0]);
     const int e_sel = (int)(0xFFFFFFFFu - (uint32_t)best);
     const float l_sel = from_ordered((uint32_t)(best >> 32));
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (eb + i == e_sel) taken[i] = true;
+    for (int i = 0; i < NV; ++i)  // the low words (~e) tell the experts apart
+      if ((uint32_t)key[i] == (uint32_t)best) key[i] = 0;
     if (j == 0) lmax = l_sel;
     wsum += expf((l_sel - lmax) * inv_temp);
 #pragma unroll
