@@ -76,7 +76,8 @@ def test_route_ties_signed_zero_and_k_equals_E():
 
 @pytest.mark.parametrize("T,h,E,k", [(65, 192, 8, 2), (100, 64, 40, 3), (1, 256, 256, 8), (130, 320, 96, 4),
                                      (70, 128, 32, 1), (3, 192, 16, 16), (257, 512, 64, 2), (64, 1024, 200, 6),
-                                     (1100, 256, 64, 2), (1030, 384, 256, 8)])  # 64 tokens per router wave
+                                     (1100, 256, 64, 2), (1030, 384, 256, 8),  # 64 tokens per router wave
+                                     (1030, 512, 128, 4), (1100, 768, 192, 3)])  # ... eight waves, 8-way k split
 def test_route_bf16_shapes(T, h, E, k):
     """The MFMA router's code paths: k split across waves (h % 128), 1/2/4 expert blocks, ragged T and E."""
     torch = gu.torch()

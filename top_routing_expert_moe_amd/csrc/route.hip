@@ -720,15 +720,21 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
         // Many tokens: each wave takes several 16-token groups, so the router weights are
         // read once per group of groups.  64 experts: 32 tokens per wave and an 8-way k
         // split, eight waves (more loads in flight; measured 36 -> 28 us at T = 8192,
-        // h = 1024).  More experts: 64 tokens per wave and a 4-way k split (the weight
-        // planes, 4x larger, are then read half as often; 8 waves of 32 tokens measured
-        // 94 -> 139 us at T = 4096, h = 4096, E = 256).  h / KS must be a multiple of 32.
+        // h = 1024).  More experts: 64 tokens per wave (the weights, 4x larger, are then
+        // read half as often; 8 waves of 32 tokens measured 94 -> 139 us at T = 4096,
+        // h = 4096, E = 256), eight waves with an 8-way k split where h allows it, else
+        // four with a 4-way split.  h / KS must be a multiple of 32.
         // (At T = 8192, h = 1024, E = 64 the eight waves of 32 tokens took 14.5 us; 16 waves
         // of 16 tokens 29.8, 32 experts per workgroup 15.6, 64 tokens per workgroup 19.6,
         // 16 tokens per workgroup 20.7, four waves 15.1.)
         if (E16 == 64 && a.h % 256 == 0 && a.T >= 1024) {
           if (a.E == 64) err = launch_logits_mfma<4, 1, 8, 2, 64>(a, E16, st, 1, nullptr, wf32);
           else err = launch_logits_mfma<4, 1, 8, 2>(a, E16, st, 1, nullptr, wf32);
+        } else if (a.h % 256 == 0 && a.T >= 1024) {
+          // eight waves, an 8-way k split (at T = 4096, h = 4096, E = 256: 58.2 us with four
+          // waves and a 4-way split, 51.3 so; 16-token pairs per wave 72.7, 32 experts per
+          // workgroup 65.9)
+          err = launch_logits_mfma<4, 1, 8, 4>(a, E16, st, 1, nullptr, wf32);
         } else if (a.h % 128 == 0 && a.T >= 1024) {
           err = launch_logits_mfma<4, 1, 4, 4>(a, E16, st, 1, nullptr, wf32);
         } else {
