@@ -8,8 +8,9 @@
 //
 // gfx950 design: one thread per (token, 8 consecutive columns); it reads the
 // k expert-output rows through slot_pos with 16-byte (bf16) or 32-byte (fp32)
-// loads and sums w_j * O in fp32, j ascending, in registers -- the
-// [tokens, k, h] temporary of the page's scatter-then-sum is never formed.
+// loads, all of them in flight together, and sums w_j * O in fp32, j ascending,
+// in registers -- the [tokens, k, h] temporary of the page's scatter-then-sum is
+// never formed.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,7 +18,7 @@ namespace moe {
 
 namespace {
 
-template <typename OT, typename YT>
+template <typename OT, typename YT, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, int parts, size_t part_stride,
                                                       const int* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w, int T, int h, int k,
@@ -27,32 +28,53 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ O, 
   if (gid >= (int64_t)T * groups) return;
   const int t = (int)(gid / groups);
   const int c = (int)(gid % groups) * 8;
+  // k <= KM slots: their rows and weights first, then the first part of every kept row, so
+  // that all the row loads are in flight together; the sums then go in ascending j (and s)
+  int pos[KM];
+  float w[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
+    w[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+  }
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int pos = slot_pos[(size_t)t * k + j];
-    if (pos < 0) continue;
-    const float wj = topk_w[(size_t)t * k + j];
-    const OT* src = O + (size_t)pos * h + c;
-    if constexpr (sizeof(OT) == 2) {
-      const u32x4 v = *(const u32x4*)src;
+  if constexpr (sizeof(OT) == 2) {
+    u32x4 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (pos[j] >= 0) v[j] = *(const u32x4*)(O + (size_t)pos[j] * h + c);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (pos[j] < 0) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wj * __uint_as_float(v[i] << 16);
-        acc[2 * i + 1] += wj * __uint_as_float(v[i] & 0xFFFF0000u);
+        acc[2 * i] += w[j] * __uint_as_float(v[j][i] << 16);
+        acc[2 * i + 1] += w[j] * __uint_as_float(v[j][i] & 0xFFFF0000u);
       }
-    } else {
-      floatx4 v0 = *(const floatx4*)src, v1 = *(const floatx4*)(src + 4);
-#pragma unroll 8
+    }
+  } else {
+    floatx4 v0[KM], v1[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (pos[j] >= 0) {
+        const OT* src = O + (size_t)pos[j] * h + c;
+        v0[j] = *(const floatx4*)src;
+        v1[j] = *(const floatx4*)(src + 4);
+      }
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (pos[j] < 0) continue;
+      const OT* src = O + (size_t)pos[j] * h + c;
       for (int s = 1; s < parts; ++s) {  // K parts of a split down projection, ascending
-        v0 += *(const floatx4*)(src + s * part_stride);
-        v1 += *(const floatx4*)(src + s * part_stride + 4);
+        v0[j] += *(const floatx4*)(src + s * part_stride);
+        v1[j] += *(const floatx4*)(src + s * part_stride + 4);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i] += wj * v0[i];
-        acc[4 + i] += wj * v1[i];
+        acc[i] += w[j] * v0[j][i];
+        acc[4 + i] += w[j] * v1[j][i];
       }
     }
   }
@@ -74,15 +96,24 @@ hipError_t launch_combine(const void* O, bool o_f32, int o_parts, size_t o_part_
   const int64_t n = (int64_t)T * (h / 8);
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (grid == 0) return hipSuccess;
-  if (bf16 && o_f32)
-    hipLaunchKernelGGL((combine_kernel<float, bf16_t>), dim3(grid), dim3(256), 0, st, (const float*)O, o_parts, o_part_stride, slot_pos,
-                       topk_w, T, h, k, (bf16_t*)y);
-  else if (bf16)
-    hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), dim3(grid), dim3(256), 0, st, (const bf16_t*)O, 1, (size_t)0, slot_pos,
-                       topk_w, T, h, k, (bf16_t*)y);
-  else
-    hipLaunchKernelGGL((combine_kernel<float, float>), dim3(grid), dim3(256), 0, st, (const float*)O, o_parts, o_part_stride, slot_pos,
-                       topk_w, T, h, k, (float*)y);
+  if (k < 1 || k > 16) return hipErrorInvalidValue;
+#define MOE_COMBINE(KM)                                                                                        \
+  do {                                                                                                         \
+    if (bf16 && o_f32)                                                                                         \
+      hipLaunchKernelGGL((combine_kernel<float, bf16_t, KM>), dim3(grid), dim3(256), 0, st, (const float*)O,  \
+                         o_parts, o_part_stride, slot_pos, topk_w, T, h, k, (bf16_t*)y);                      \
+    else if (bf16)                                                                                             \
+      hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t, KM>), dim3(grid), dim3(256), 0, st, (const bf16_t*)O, \
+                         1, (size_t)0, slot_pos, topk_w, T, h, k, (bf16_t*)y);                                \
+    else                                                                                                       \
+      hipLaunchKernelGGL((combine_kernel<float, float, KM>), dim3(grid), dim3(256), 0, st, (const float*)O,   \
+                         o_parts, o_part_stride, slot_pos, topk_w, T, h, k, (float*)y);                       \
+  } while (0)
+  if (k <= 2) MOE_COMBINE(2);
+  else if (k <= 4) MOE_COMBINE(4);
+  else if (k <= 8) MOE_COMBINE(8);
+  else MOE_COMBINE(16);
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
