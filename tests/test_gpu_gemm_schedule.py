@@ -1,9 +1,11 @@
 """The grouped GEMMs' workgroup schedule does not change their results.
 
-A bf16 GEMM launch has at most one workgroup per CU; each runs its share of the tile
-list in turn, and a tile followed by one of the same shape copies that tile's first
-stages during its own last ones.  The environment variable MOE_GEMM_WORKGROUPS sets
-the number of workgroups: with few of them every workgroup runs many tiles in a row,
+The schedule has two knobs, environment variables read at each launch:
+MOE_GEMM_ORDER picks which workgroup runs which tile, and MOE_GEMM_WORKGROUPS sets
+the number of workgroups.  A bf16 GEMM launch of short tiles has at most one
+workgroup per CU; each runs its share of the tile list in turn, and a tile followed by
+one of the same shape copies that tile's first stages during its own last ones.  With
+few workgroups every workgroup runs many tiles in a row,
 so the hand-over between tiles (including the gathered activation rows of the up
 projection) runs at every tile boundary.  Every tile's arithmetic is the same whoever
 runs it, so the outputs must be bit-identical to the default schedule's, and they are
@@ -29,24 +31,29 @@ def _say(*a):
     print(*a, flush=True)
 
 
-class _Workgroups:
-    """MOE_GEMM_WORKGROUPS set to n (None: unset) inside the block."""
+class _Env:
+    """Environment variable `var` set to n (None: unset) inside the block."""
 
-    def __init__(self, n):
-        self.n = n
+    def __init__(self, var, n):
+        self.var, self.n = var, n
 
     def __enter__(self):
-        self.old = os.environ.get(ENV)
+        self.old = os.environ.get(self.var)
         if self.n is None:
-            os.environ.pop(ENV, None)
+            os.environ.pop(self.var, None)
         else:
-            os.environ[ENV] = str(self.n)
+            os.environ[self.var] = str(self.n)
 
     def __exit__(self, *exc):
         if self.old is None:
-            os.environ.pop(ENV, None)
+            os.environ.pop(self.var, None)
         else:
-            os.environ[ENV] = self.old
+            os.environ[self.var] = self.old
+
+
+def _Workgroups(n):
+    """MOE_GEMM_WORKGROUPS set to n (None: unset) inside the block."""
+    return _Env(ENV, n)
 
 
 def _rand(shape, scale, rng, dtype):
@@ -133,3 +140,48 @@ def test_layer_schedule_invariant(T, h, f, E, k, cf, act):
                           k=k, capacity_factor=cf, act=act, dtype="bf16", logits=gu.from_dev(logits), tokens=tokens)
     assert np.array_equal(outs[1][2], ref["counts"])
     gu.check_bf16_out(gu.as_f64(outs[1][0][tokens], "bf16"), ref["y64"], "y")
+
+
+@pytest.mark.parametrize("act,E,h,f,seg", [
+    ("swiglu", 4, 256, 512, [1100, 20, 700, 300]),                  # 256-row launches: 256-, 128- and
+                                                                     # 32-row tiles, NT a multiple of 8
+    ("gelu", 8, 512, 768, [104, 1300, 557, 0, 800, 734, 699, 134]),  # skewed, one expert empty, NT = 3 / 2
+    ("swiglu", 16, 256, 256, [400] * 3 + [33] * 5 + [2000, 0, 257, 5, 1900, 128, 129, 700]),
+    ("gelu", 6, 512, 1024, [700, 20, 5, 300, 60, 0]),               # 128-row launches
+    ("swiglu", 3, 2048, 512, [12, 3, 30]),                           # K parts (down projection)
+])
+@pytest.mark.parametrize("order", [0, 1, 2])
+@pytest.mark.parametrize("wgs", [None, 16])
+def test_expert_ffn_tile_order_invariant(act, E, h, f, seg, order, wgs):
+    """MOE_GEMM_ORDER picks which workgroup runs which tile (XCD ranges of the list, launch
+    order, or n-tile ranges per XCD): the outputs are bit-identical to the default
+    schedule's, with one workgroup per tile slot and with few workgroups running many
+    tiles each."""
+    torch = gu.torch()
+    _say(f"expert_ffn tile order {order} {act} E={E} h={h} f={f} seg={seg} workgroups={wgs}")
+    rng = np.random.default_rng(E * 7 + h + f)
+    R = int(sum(seg))
+    R_max = R + 3
+    xp = _rand((R_max, h), 1.0, rng, "bf16")
+    W1 = _rand((E, h, f), 1 / math.sqrt(h), rng, "bf16")
+    W3 = _rand((E, h, f), 1 / math.sqrt(h), rng, "bf16") if act == "swiglu" else None
+    W2 = _rand((E, f, h), 1 / math.sqrt(f), rng, "bf16")
+    offsets = np.concatenate([[0], np.cumsum(seg)]).astype(np.int32)
+    d = dict(x=gu.to_dev(xp, "bf16"), off=torch.from_numpy(offsets).to(gu.dev()), W1=gu.to_dev(W1, "bf16"),
+             W3=None if W3 is None else gu.to_dev(W3, "bf16"), W2=gu.to_dev(W2, "bf16"))
+    outs = []
+    for ordr, n in ((None, None), (order, wgs)):
+        with _Env("MOE_GEMM_ORDER", ordr), _Workgroups(n):
+            out = moe.expert_ffn(d["x"], d["off"], d["W1"], d["W3"], d["W2"], act,
+                                 out=gu.sentinel_like((R_max, h), "bf16"))
+            torch.cuda.synchronize()
+        outs.append(gu.from_dev(out).copy())
+    assert gu.is_sentinel(outs[1][R:], "bf16").all(), "rows past offsets[E] were written"
+    assert np.array_equal(outs[0], outs[1]), "the tile order changed the result"
+    got = gu.as_f64(outs[1][:R], "bf16")
+    a64 = gu.as_f64(xp, "bf16")
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            ref = o.expert_ffn(a64[lo:hi], W1[e], None if W3 is None else W3[e], W2[e], act, "bf16")
+            gu.check_bf16_out(got[lo:hi], ref, f"expert {e}")

@@ -68,6 +68,31 @@ __device__ __forceinline__ void store4(float* p, const float* v) { *(floatx4*)p 
 #endif
 constexpr int GM = MOE_GM, GN = MOE_GN;
 
+// Which workgroup runs which tile.  The hardware hands workgroup i to XCD i % 8, in launch
+// order: workgroup i waits until XCD i % 8 has a free CU, even while other XCDs idle.  So
+// the eight XCDs move through their workgroups in step, and a schedule is fast when, at
+// each step, the eight get tiles of the same cost.
+//  * kOrderRanges: XCD x runs the x-th eighth of the list (its workgroups take every
+//    nslot-th tile of it).  Equal counts, but not equal costs when tile heights differ:
+//    at T = 4096, E = 8, k = 2 three XCDs get only full 256-row tiles.
+//  * kOrderNRange: XCD x runs n-tiles [x NT / 8, (x + 1) NT / 8) of every m-tile, in the
+//    grouped order of a launch that narrow.  With NT a multiple of 8 every XCD then has the
+//    same sequence of tile heights, and its weight columns stay in its own L2.  It reads
+//    every activation row once per XCD.
+//  * kOrderLaunch: tile i runs on workgroup i, one m-tile at a time (n fastest), so the
+//    tiles the eight XCDs take together are of one m-tile.
+// Measured (one MI355X, A/B in one session): at T = 4096, h = 4096, f = 14336, E = 8,
+// k = 2 the up projection takes 1.770 ms with ranges, 1.716 ms with n-ranges and
+// 1.736 ms in launch order, and the down projection 0.942 / 0.934 / 0.947 ms; at
+// T = 8192, h = 1024, f = 4096, E = 64, k = 2 (capacity 320) the down projection takes
+// 0.125 ms with ranges, 0.118 ms in launch order and 0.156 ms with n-ranges (NT = 4: half
+// the XCDs idle); at T = 4096, h = 4096, f = 2048, E = 256, k = 8 the up projection takes
+// 1.733 / 1.737 / 1.751 ms and the down projection 0.985 / 0.999 / 0.972 ms.  Ranges
+// balanced by tile cost instead of count (256-row tile 4, 128-row 2, 32-row 1) made the
+// prefill-shaped up projection slower (1.80 -> 1.98 ms): their counts differ, so the XCDs
+// fall out of step.
+enum TileOrder { kOrderRanges = 0, kOrderLaunch = 1, kOrderNRange = 2 };
+
 // Reads of the tile list and the expert offsets: uniform addresses, loaded through the
 // constant address space so that they are scalar loads (the GEMM counts its vector-memory
 // operations by hand, and a vector load here would make the compiler wait for them all).
@@ -85,7 +110,7 @@ struct TileInfo {
 // fh, big: the tile heights (m_tile_rows); NO: output columns per n-tile.
 __device__ __forceinline__ TileInfo tile_at(int L, const int* __restrict__ tile_off, const int* __restrict__ offsets,
                                             int E, int NT, int n_tiles, bool split, int fh, int big, int NO,
-                                            int e_from) {
+                                            int e_from, int gmx = GM) {
   TileInfo t;
   t.ks = split ? L / n_tiles : 0;
   const int Lt = L - t.ks * n_tiles;
@@ -103,12 +128,12 @@ __device__ __forceinline__ TileInfo tile_at(int L, const int* __restrict__ tile_
   const int t0 = ldc(tile_off, e);
   const int me = ldc(tile_off, e + 1) - t0;
   const int l = Lt - t0 * NT;
-  const int mg = l / (GM * NT);
-  const int gm = min(GM, me - mg * GM);
-  const int r = l - mg * GM * NT;
+  const int mg = l / (gmx * NT);
+  const int gm = min(gmx, me - mg * gmx);
+  const int r = l - mg * gmx * NT;
   const int ng = r / (gm * GN);
   const int r2 = r - ng * gm * GN;
-  const int mt_local = mg * GM + r2 % gm;
+  const int mt_local = mg * gmx + r2 % gm;
   const int nt = ng * GN + r2 / gm;
   const int o0 = ldc(offsets, e), o1 = ldc(offsets, e + 1);
   const int fe = m_tile_rows(o1 - o0, fh, big);  // this expert's tile height
@@ -604,32 +629,50 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int* __restrict__ a_rows, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ W3, int K, int N, OT* __restrict__ out, const int* __restrict__ offsets,
-    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, int big, float* __restrict__ save) {
+    const int* __restrict__ tile_off, int E, int NT, int S, int R_max, int fh, int big, float* __restrict__ save,
+    int order) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   constexpr int NO = ACT == ACT_SWIGLU ? BN / 2 : BN;  // output columns per tile
-  // ---- tile schedule (XCD-aware): XCD x takes list positions [x per, x per + per); its
-  // workgroups take every nslot-th of them
-  const int n_tiles = ldc(tile_off, E) * NT;
-  const int n_real = n_tiles * (SPLIT ? S : 1);
-  const int per = (n_real + 7) >> 3;
+  // ---- tile schedule (see TileOrder)
   const int nslot = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int Lend = min((xcd + 1) * per, n_real);
-  int L = xcd * per + slot;
+  // kOrderNRange: XCD x's list is that of a launch of its NTl n-tiles, shifted by nb
+  const int nb = order == kOrderNRange ? xcd * NT / 8 : 0;
+  const int NTl = order == kOrderNRange ? (xcd + 1) * NT / 8 - nb : NT;
+  const int n_tiles = ldc(tile_off, E) * NTl;
+  const int n_real = n_tiles * (SPLIT ? S : 1);
+  int L, Lend, step, gmx = GM;
+  if (order == kOrderLaunch) {
+    L = blockIdx.x;
+    Lend = n_real;
+    step = gridDim.x;
+    gmx = 1;
+  } else if (order == kOrderNRange) {
+    L = slot;
+    Lend = n_real;
+    step = nslot;
+  } else {
+    const int per = (n_real + 7) >> 3;
+    L = xcd * per + slot;
+    Lend = min((xcd + 1) * per, n_real);
+    step = nslot;
+  }
   if (L >= Lend) return;
   const int Kc = SPLIT ? K / S : K;  // each tile's k range: [ks * Kc, ks * Kc + Kc)
   // the tile's code path is chosen by the rows it really has
   auto shape = [](int rows) { return rows > 128 ? 2 : (rows > 32 ? 1 : 0); };
-  TileInfo cur = tile_at(L, tile_off, offsets, E, NT, n_tiles, SPLIT, fh, big, NO, 0);
+  TileInfo cur = tile_at(L, tile_off, offsets, E, NTl, n_tiles, SPLIT, fh, big, NO, 0, gmx);
+  cur.n0 += nb * NO;
   bool pre = false, first = true;
   XCarry carry;
   for (;;) {
-    const int Ln = L + nslot;
+    const int Ln = L + step;
     const bool more = Ln < Lend;
     TileInfo nxt = cur;
     if (more) {
       const bool same_part = !SPLIT || Ln / n_tiles == cur.ks;  // list positions only grow inside a part
-      nxt = tile_at(Ln, tile_off, offsets, E, NT, n_tiles, SPLIT, fh, big, NO, same_part ? cur.e : 0);
+      nxt = tile_at(Ln, tile_off, offsets, E, NTl, n_tiles, SPLIT, fh, big, NO, same_part ? cur.e : 0, gmx);
+      nxt.n0 += nb * NO;
     }
     const int sh = shape(cur.rows);
     const NextTile nx{more && shape(nxt.rows) == sh, nxt.e, nxt.row0, nxt.row0 + nxt.rows, nxt.n0, nxt.ks};
@@ -818,13 +861,30 @@ long long gemm_workgroups(long long slots, int stages) {
   return std::min(slots, (long long)(cus + 7) / 8 * 8);
 }
 
+// The tile order of a launch of m-tiles bm rows high and NT n-tiles (down: the output is
+// the raw product): n-ranges for 256-row tiles over a multiple of 8 n-tiles, launch order
+// for the down projections of 128-row tiles, else ranges.  MOE_GEMM_ORDER (environment:
+// 0, 1 or 2) sets it for every launch; the results do not depend on it.
+int tile_order(int bm, int NT, bool down) {
+  if (const char* v = getenv("MOE_GEMM_ORDER")) {
+    const long m = strtol(v, nullptr, 10);
+    if (m >= kOrderRanges && m <= kOrderNRange) return (int)m;
+  }
+  if (bm == 256 && NT % 8 == 0) return kOrderNRange;
+  if (bm == 128 && down) return kOrderLaunch;
+  return kOrderRanges;
+}
+
 template <int ACT, bool G, typename OT, bool SPLIT>
 hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   const bool wide = a.bm == 32;
   const int NO = ACT == ACT_SWIGLU ? (wide ? BNW : BN) / 2 : (wide ? BNW : BN);
   const int NT = ((ACT == ACT_SWIGLU_SEP ? 2 * a.N : a.N) + NO - 1) / NO;
   const int S = SPLIT ? std::max(a.ksplit, 1) : 1;
-  const long long slots = ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * NT * S;
+  const int order = wide ? kOrderRanges : tile_order(a.bm, NT, ACT == ACT_NONE);
+  // (kOrderNRange: every XCD has slots for its ceil(NT / 8) n-tiles of every m-tile)
+  const long long slots =
+      ((long long)(a.R_max + a.bm - 1) / a.bm + a.E) * (order == kOrderNRange ? (NT + 7) / 8 * 8 : NT) * S;
   const long long grid = gemm_workgroups((slots + 7) / 8 * 8, a.K / S / KB);
   if (grid <= 0) return hipSuccess;
   float* save = SPLIT ? nullptr : a.save;
@@ -837,7 +897,7 @@ hipError_t launch_bf16_k(const GemmArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<ACT, G, OT, SPLIT>), dim3((unsigned)grid), dim3(kWaves * 64), 0, st,
                        (const bf16_t*)a.A, a.a_rows, (const bf16_t*)a.W, (const bf16_t*)a.W3, a.K, a.N,
-                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, a.big, save);
+                       (OT*)a.out, a.offsets, a.tile_off, a.E, NT, S, a.R_max, a.bm, a.big, save, order);
   return hipGetLastError();
 }
 
