@@ -106,6 +106,8 @@ def _check_all(w, host, g, gl, dy_host, tokens=None, experts=None, with_w_gate=T
     (150, 320, 448, 4, 2, 0.0, "swiglu", "bf16"),    # pipelined TN with partial tiles in both weight dimensions
     (600, 320, 576, 3, 2, 0.5, "gelu", "bf16"),      # ... GELU with drops; 128-row NT tiles, partial in N
     (1400, 320, 576, 2, 1, 0.9, "gelu", "bf16"),     # 256-row NT tiles, partial in N, with drops
+    (1090, 512, 256, 8, 2, 0.7, "swiglu", "bf16"),   # the forward's histogram in 16-token blocks (the
+                                                     # logits kernel selects), ragged T, drops
 ])
 def test_backward_edge_cases(T, h, f, E, k, cf, act, dtype):
     _say(f"backward edge T={T} h={h} f={f} E={E} k={k} cf={cf} {act} {dtype}")

@@ -171,6 +171,36 @@ def test_layer_skewed_experts(T, h, f, E, k, cf, act, dtype):
 
 
 @pytest.mark.parametrize("T,E,k,cf", [
+    (1025, 8, 2, 0.0),      # 64 blocks of 16 tokens + 1 token
+    (2001, 5, 3, 0.6),      # five experts (four per lane group), ragged, drops
+    (1100, 16, 16, 0.0),    # k = E = 16: every expert
+    (1040, 16, 1, 1.0),     # k = 1, drops
+    (4097, 8, 2, 1.25),     # 257 blocks of 16 tokens, 65 scatter blocks
+])
+def test_layer_selection_in_logits_kernel(T, E, k, cf):
+    """bf16, at most 16 experts, h a multiple of 512 and many tokens: the logits kernel
+    selects each 16-token group's experts itself and counts the histogram per 16 tokens,
+    and the fused scan + scatter reads four histogram blocks per 64-token block.  Everything
+    the layer decides is bit-exact against the oracle."""
+    import math
+    h, f = 512, 256
+    _say(f"layer selection in the logits kernel E={E} T={T} k={k} cf={cf}")
+    rng = np.random.default_rng(T + 5 * k)
+    conv = mw.f32_to_bf16_bits
+    host = dict(x=conv(rng.standard_normal((T, h)).astype(np.float32)),
+                W_gate=(rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32),
+                logit_bias=(0.5 * rng.standard_normal(E)).astype(np.float32),
+                W1=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W3=conv((rng.standard_normal((E, h, f)) / math.sqrt(h)).astype(np.float32)),
+                W2=conv((rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)))
+    dd = {kk: gu.to_dev(v, "bf16" if kk in ("x", "W1", "W3", "W2") else "f32") for kk, v in host.items()}
+    w = mw.Workload("select-in-logits", T=T, h=h, f=f, E=E, k=k, act="swiglu", dtype="bf16", cf=cf)
+    y, aux, counts, logits, routing = _run_layer(w, host, dd)
+    tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 300, replace=False)]))
+    _check_layer(w, host, y, aux, counts, logits, tokens, routing)
+
+
+@pytest.mark.parametrize("T,E,k,cf", [
     (1024, 64, 2, 1.25),    # the fused scan + scatter: 16 blocks
     (1500, 64, 4, 0.0),     # ... with a ragged last block (24 blocks, 28 tokens in the last)
     (8256, 64, 2, 1.0),     # 129 blocks: the largest fused scan at 64 experts (64 blocks per thread)

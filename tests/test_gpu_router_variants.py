@@ -74,7 +74,8 @@ def test_route_variant_parity(name, variant):
                                           ("capacity-e64", "jitter"), ("prefill-mixtral", "uniform"),
                                           ("decode-mixtral", "all"), ("decode-mixtral", "soft"),
                                           ("prefill-mixtral", "soft-temperature-0.5"),
-                                          ("capacity-e64", "soft-noise-jitter-1.5"), ("tiny-fp32", "soft")])
+                                          ("capacity-e64", "soft-noise-jitter-1.5"), ("tiny-fp32", "soft"),
+                                          ("prefill-mixtral", "all"), ("prefill-mixtral", "noise-temperature-2")])
 def test_layer_forward_variant_parity(name, variant):
     torch = gu.torch()
     _say(f"layer {name} {variant}")

@@ -171,8 +171,10 @@ LayerWs carve_layer(Carve& c, int32_t T, int32_t h, int32_t f, int32_t E, int32_
   w.logits = c.take<float>((size_t)T * E);
   w.topk_idx = c.take<int>(n);
   w.topk_w = c.take<float>(n);
-  w.prob_part = c.take<float>((size_t)route_blocks(T) * E);
-  w.blk_counts = c.take<int>(nhb * E);
+  // per histogram block (16 or kSelTokens tokens: route_hist_tokens)
+  const size_t nhist = (size_t)route_hist_blocks(T, h, E, dt == MOE_BF16);
+  w.prob_part = c.take<float>(nhist * E);
+  w.blk_counts = c.take<int>(nhist * E);
   w.blk_base = c.take<int>(nhb * E);
   w.counts = c.take<int>(E);
   w.offsets = c.take<int>((size_t)E + 1);
@@ -582,8 +584,9 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   ra.topk_idx = w.topk_idx;
   ra.topk_w = w.topk_w;
   ra.prob_part = w.prob_part;
-  ra.blk_counts = w.blk_counts;  // the histogram is counted by the selection kernel
+  ra.blk_counts = w.blk_counts;  // the histogram is counted by the selection (or logits) kernel
   ra.planes = w.planes;
+  ra.hist_tokens = route_hist_tokens(T, h, E, bf);
   apply_opts(ra, opts);
   if (xj != nullptr) {  // only the router sees the jittered input
     MOE_TRY(launch_jitter(x, opts->jitter, (int64_t)T * h, bf, xj, stream));
@@ -612,7 +615,8 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   if (!mark()) return MOE_ERR_DEVICE;
   ScanArgs sa{};
   sa.blk_counts = w.blk_counts;
-  sa.nhb = route_blocks(T);
+  sa.nhb = route_hist_blocks(T, h, E, bf);
+  sa.hpb = kSelTokens / ra.hist_tokens;
   sa.E = E;
   sa.T = T;
   sa.k = k;
@@ -620,7 +624,7 @@ static moe_status_t layer_forward_impl(const void* x, const float* W_gate, const
   sa.BM = pl.bm;
   sa.big = pl.big;
   sa.prob_part = w.prob_part;
-  sa.nrb = route_blocks(T);
+  sa.nrb = sa.nhb;
   sa.prob_sum = nullptr;
   sa.counts = counts ? counts : w.counts;
   sa.offsets = w.offsets;
@@ -949,7 +953,7 @@ static moe_status_t layer_backward_impl(const void* x, const float* W_gate, cons
   };
   if (!mark()) return MOE_ERR_DEVICE;
 
-  MOE_TRY(launch_counts(w.blk_counts, route_blocks(T), E, b.counts, stream));
+  MOE_TRY(launch_counts(w.blk_counts, route_hist_blocks(T, h, E, bf), E, b.counts, stream));
   MOE_TRY(launch_tile_scan(w.offsets, E, 64, b.tile64, stream));
   // data-gradient tile height: 256 rows when the forward's GEMMs take 256-row tiles
   const int ts = pl.bm == 256 ? 256 : 128;

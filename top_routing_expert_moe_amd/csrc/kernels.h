@@ -50,6 +50,9 @@ struct RouteArgs {
   bool soft = false;
   // not null and T <= kSelTokens: the selection kernel also does the scan and the scatter
   const SmallPermute* permute = nullptr;
+  // tokens per histogram block (prob_part and blk_counts rows): kSelTokens, or 16 when the
+  // logits kernel also selects (route_hist_tokens); launch_select then launches nothing
+  int hist_tokens = kSelTokens;
 };
 // router-input jitter: out = x * u elementwise in the storage dtype (n_elems * elem size % 16 == 0)
 hipError_t launch_jitter(const void* x, const void* u, int64_t n_elems, bool bf16, void* out, hipStream_t st);
@@ -57,6 +60,12 @@ int route_planes_elems(int h, int E);
 int route_hsplit(int T, int h, int E, bool bf16);              // h-split of the logits (1 = none)
 size_t route_scratch_bytes(int T, int h, int E, bool bf16);   // bytes behind RouteArgs::planes
 int route_blocks(int T);
+// Tokens per histogram block of a layer's routing: 16 when the logits kernel selects the
+// experts itself (bf16, at most 16 experts, h a multiple of 512, more than one 64-token
+// block, no split of h and a fusable scan + scatter over the 16-token blocks), else
+// kSelTokens.  A function of the sizes only, so that the backward finds the forward's blocks.
+int route_hist_tokens(int T, int h, int E, bool bf16);
+int route_hist_blocks(int T, int h, int E, bool bf16);  // ceil(T / route_hist_tokens)
 hipError_t launch_logits(const RouteArgs& a, hipStream_t st);  // logits only (ignores logits_in)
 hipError_t launch_select(const RouteArgs& a, hipStream_t st);  // softmax, top-k, weights, histogram
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);   // both (logits skipped when logits_in)
@@ -68,6 +77,7 @@ hipError_t launch_hist(const int* topk_idx, int T, int k, int E, int* blk_counts
 struct ScanArgs {
   const int* blk_counts;   // [nhb,E]
   int nhb, E, T, k;
+  int hpb = 1;             // histogram blocks per kSelTokens-token scatter block (fused scan only)
   int C;                   // capacity, INT32_MAX = none
   int BM;                  // rows per GEMM tile for tile_off; 0 = no tile schedule
   int big;                 // m_tile_rows threshold of the tile list (FfnPlan::big)

@@ -211,10 +211,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
 }
 
-// The scan and the scatter in one launch (one workgroup of 256 per token block), for when
-// every block can afford to read all the block histograms: block b sums each expert's
-// column of blk_counts over all blocks (the counts) and over the blocks before b (its rank
-// origins), P threads per expert, each over a contiguous range of at most PER blocks with
+// The scan and the scatter in one launch (one workgroup of 256 per kSelTokens-token block),
+// for when every block can afford to read all the block histograms: block b sums each
+// expert's column of blk_counts over all histogram blocks (the counts) and over those of
+// the tokens before its own (its rank origins; hpb histogram blocks per token block when
+// the histogram was counted per fewer tokens), P threads per expert, each over a contiguous range of at most PER blocks with
 // all its loads in flight at once.  Every block then has the same counts, so the same
 // offsets; block 0 also writes counts, offsets, the m-tile list and the aux loss.  Integer
 // sums are exact, and the aux loss is summed in a fixed order, so the results are those of
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScanArgs a, const int
       const int bi = b0 + i;
       const int v = (act && i < per && bi < a.nhb) ? c[i] : 0;
       tot += v;
-      pre += bi < blk ? v : 0;
+      pre += bi < blk * a.hpb ? v : 0;
     }
   }
 #pragma unroll
@@ -412,7 +413,8 @@ hipError_t launch_scan_scatter(const ScanArgs& a, const int* topk_idx, int* slot
   const int per = scan_scatter_per(a.nhb, a.prob_part != nullptr ? a.nrb : 0, a.E);
   if (per == 0 || a.binned) return hipErrorInvalidValue;
   const int nbits = expert_bits(a.E);
-  const dim3 grid(a.nhb), block(256);
+  if (a.hpb < 1 || (size_t)route_blocks(a.T) * a.hpb < (size_t)a.nhb) return hipErrorInvalidValue;
+  const dim3 grid(route_blocks(a.T)), block(256);  // one workgroup per scatter block
 #define MOE_SCAN_SCATTER(PER_)                                                                                    \
   hipLaunchKernelGGL(scan_scatter_kernel<PER_>, grid, block, 0, st, a, topk_idx, nbits, slot_pos, sorted_slot, \
                      perm_token)

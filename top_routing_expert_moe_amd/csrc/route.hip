@@ -237,14 +237,30 @@ struct LogitBatch {
   float w[WF32 ? UU : 1][WF32 ? NB : 1][8];
 };
 
+// The selection's outputs and variant arguments, for a logits kernel that also selects.
+struct SelOut {
+  int* topk_idx;
+  float* topk_w;
+  float* prob_part;   // [T / 16][E] or null
+  int* blk_counts;    // [T / 16][E] or null
+  const float* noise;
+  float inv_temp;
+  int vflags, k;
+};
+
 // EC > 0: E is EC (the fp32 weights' row stride then folds into the loads' offsets).
-template <int NB, int TW, int NW, int TG = 1, bool WF32 = false, int EC = 0>
+// SEL (one group of 16 tokens per workgroup, at most 16 experts): the workgroup then also
+// selects its tokens' experts, as select_kernel does for 64, and writes its 16-token
+// block's histogram and softmax sums (row blockIdx.x of so.blk_counts / so.prob_part).
+template <int NB, int TW, int NW, int TG = 1, bool WF32 = false, int EC = 0, bool SEL = false>
 __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ planes,
                                                           const float* __restrict__ W_gate,
                                                           const float* __restrict__ bias, int T, int h, int E,
-                                                          int E16, float* __restrict__ logits, int gx, int gy) {
+                                                          int E16, float* __restrict__ logits, int gx, int gy,
+                                                          SelOut so) {
   constexpr int KS = NW / TW;
+  static_assert(!SEL || (NB == 1 && TW == 1 && TG == 1 && KS > 1), "selection: one 16 x 16 fragment");
   // k-steps of 32 per batch of loads; two batches are live (the next one is in flight while
   // this one is multiplied), so the batch shrinks as the fragments per step grow
   constexpr int FR = NB * TG;
@@ -393,14 +409,19 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
 #pragma unroll
       for (int q = 1; q < PA; ++q) acc[tg][nb] += accp[q][tg][nb];
     }
+  // the workgroup's logits for the selection: [token][expert], 17 words per row
+  __shared__ float lsel[SEL ? 16 : 1][17];
+  __shared__ int cnt[16];
+  if (SEL && threadIdx.x < 16) cnt[threadIdx.x] = 0;
   // lane holds token (lane & 15) of each group, experts 4*(lane>>4) + 0..3 of each 16-block
   auto store = [&](int tg, int nb, const floatx4& v) {
     const int tok = t0 + 16 * tg + (lane & 15);
-    if (tok >= T) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int e = e0 + nb * 16 + 4 * (lane >> 4) + r;
-      if (e < E) logits[(size_t)tok * E + e] = v[r] + (bias ? bias[e] : 0.f);
+      const float l = v[r] + (bias && e < E ? bias[e] : 0.f);
+      if (SEL) lsel[lane & 15][4 * (lane >> 4) + r] = l;
+      if (e < E && tok < T) logits[(size_t)tok * E + e] = l;
     }
   };
   if constexpr (KS > 1) {
@@ -417,6 +438,38 @@ __global__ __launch_bounds__(NW * 64) void logits_mfma_kernel(const bf16_t* __re
 #pragma unroll
       for (int z = 1; z < KS; ++z) v += red[z][tw][tg][nb][lane];
       store(tg, nb, v);
+    }
+    if constexpr (SEL) {
+      // Wave 0 selects for the 16 tokens, G = 4 lanes per token (lane = 4 * token + gl,
+      // lane gl holding experts gl * NV .. gl * NV + NV - 1), with the selection kernel's
+      // per-token function; the block's histogram is counted in LDS.
+      constexpr int NV = EC > 0 && EC <= 8 ? 2 : 4;
+      __syncthreads();
+      if (wave == 0) {
+        const int sub = lane >> 2, gl = lane & 3, t = t0 + sub;
+        float v[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int e = gl * NV + i;
+          const float nz = so.noise != nullptr ? so.noise[(size_t)min(t, T - 1) * E + min(e, E - 1)] : 0.f;
+          v[i] = e < E ? (t < T ? lsel[sub][e] + nz : 0.f) : -INFINITY;
+        }
+        float psum[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) psum[i] = 0.f;
+        select_token<NV, 4>(v, t, T, E, so.k, gl, so.inv_temp, so.vflags, so.topk_idx, so.topk_w,
+                            so.blk_counts != nullptr ? cnt : nullptr, psum);
+        // the 16 token groups' softmax sums, added by a fixed tree; lanes 0..3 then hold them
+#pragma unroll
+        for (int i = 0; i < NV; ++i) psum[i] = across_groups_sum<4>(psum[i]);
+        if (so.prob_part != nullptr && sub == 0) {
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+            if (gl * NV + i < E) so.prob_part[(size_t)blockIdx.x * E + gl * NV + i] = psum[i];
+        }
+      }
+      __syncthreads();
+      if (so.blk_counts != nullptr && threadIdx.x < E) so.blk_counts[(size_t)blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
     }
   } else {
 #pragma unroll
@@ -633,15 +686,27 @@ hipError_t launch_logits_mfma(const RouteArgs& a, int E16, hipStream_t st, int S
   const int gx = (a.T + 16 * TW * TG - 1) / (16 * TW * TG), gy = E16 / (16 * NB);
   // one expert group: gx x SH grid; several: a 1-D grid, XCD-aware (SH is then 1)
   const dim3 grid = gy > 1 ? dim3((unsigned)((gx * gy + 7) / 8 * 8)) : dim3(gx, 1, SH);
+  if (a.hist_tokens == 16) {
+    // the selection in the same kernel: one 16-token group per workgroup, no split of h
+    if constexpr (NB == 1 && TW == 1 && TG == 1 && NW / TW > 1) {
+      if (E16 != 16 || SH != 1 || out != nullptr || a.logits_in || a.permute != nullptr) return hipErrorInvalidValue;
+      const SelOut so{a.topk_idx, a.topk_w, a.prob_part, a.blk_counts, a.noise, a.inv_temp,
+                      (a.uniform ? 1 : 0) | (a.soft ? 2 : 0), a.k};
+      hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true, EC, true>), grid, dim3(NW * 64), 0, st,
+                         (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, a.logits, gx, gy, so);
+      return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+  }
   if (wf32 || E16 <= 16)  // weights split in registers (planes at 16 experts measured 22.8 + 4.4 us
                           // against 13.6 at T = 4096, h = 4096)
     hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, true, EC>), grid, dim3(NW * 64), 0, st,
                        (const bf16_t*)a.x, nullptr, a.W_gate, a.bias, a.T, a.h, a.E, E16, out ? out : a.logits, gx,
-                       gy);
+                       gy, SelOut{});
   else
     hipLaunchKernelGGL((logits_mfma_kernel<NB, TW, NW, TG, false, 0>), grid, dim3(NW * 64), 0, st,
                        (const bf16_t*)a.x, (const bf16_t*)a.planes, nullptr, a.bias, a.T, a.h, a.E, E16,
-                       out ? out : a.logits, gx, gy);
+                       out ? out : a.logits, gx, gy, SelOut{});
   return hipSuccess;
 }
 
@@ -689,6 +754,21 @@ float* route_lpart(const RouteArgs& a) {
 }
 
 int route_blocks(int T) { return (T + kSelTokens - 1) / kSelTokens; }
+
+// (At T = 4096, h = 4096, E = 8 the selection kernel took 4.3-4.9 us after a 13.8 us logits
+// kernel.)
+int route_hist_tokens(int T, int h, int E, bool bf16) {
+  const int E16 = (E + 15) / 16 * 16;
+  if (!bf16 || E16 != 16 || h % 512 != 0 || route_blocks(T) <= 1 || route_hsplit(T, h, E, bf16) != 1)
+    return kSelTokens;
+  const int nhb = (T + 15) / 16;
+  return scan_scatter_fusable(nhb, nhb, E) ? 16 : kSelTokens;
+}
+
+int route_hist_blocks(int T, int h, int E, bool bf16) {
+  const int ht = route_hist_tokens(T, h, E, bf16);
+  return (T + ht - 1) / ht;
+}
 
 hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
   hipError_t err = hipSuccess;
@@ -771,6 +851,8 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_select(const RouteArgs& a, hipStream_t st) {
+  if (a.hist_tokens == 16) return a.logits_in ? hipErrorInvalidValue : hipSuccess;  // done by the logits kernel
+  if (a.hist_tokens != kSelTokens) return hipErrorInvalidValue;
   const dim3 grid(route_blocks(a.T));
   // partial logits from a split contraction (never with logits given as input)
   const int SH = a.logits_in ? 1 : route_hsplit(a.T, a.h, a.E, a.bf16);
