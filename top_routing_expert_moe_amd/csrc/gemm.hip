@@ -82,9 +82,10 @@ constexpr int GM = MOE_GM, GN = MOE_GN;
 //    more bytes into L2 and were 0.5 % slower.)
 //  * kOrderLaunch: tile i runs on workgroup i, one m-tile at a time (n fastest), so the
 //    tiles the eight XCDs take together are of one m-tile.
-// Measured (one MI355X, A/B in one session): at T = 4096, h = 4096, f = 14336, E = 8,
-// k = 2 the up projection takes 1.770 ms with ranges, 1.716 ms with n-ranges and
-// 1.736 ms in launch order, and the down projection 0.942 / 0.934 / 0.947 ms; at
+// Measured (one MI355X, A/B in one session, n-ranges then contiguous per XCD): at
+// T = 4096, h = 4096, f = 14336, E = 8, k = 2 the up projection takes 1.770 ms with
+// ranges, 1.716 ms with n-ranges and 1.736 ms in launch order, and the down projection
+// 0.942 / 0.934 / 0.947 ms; at
 // T = 8192, h = 1024, f = 4096, E = 64, k = 2 (capacity 320) the down projection takes
 // 0.125 ms with ranges, 0.118 ms in launch order and 0.156 ms with n-ranges (NT = 4: half
 // the XCDs idle); at T = 4096, h = 4096, f = 2048, E = 256, k = 8 the up projection takes
